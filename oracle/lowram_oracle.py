@@ -1,0 +1,469 @@
+"""CPU oracle for LowRAM compressed-KV decode attention (numpy, float64).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+the benchmark's CPU-baseline leg may import this module.  It shares no code
+with the HIP library and imports nothing from it.
+
+What it computes, by source:
+
+* M_KV = 2 L H_kv d_h N s -- zicq.com English summary, "Core Mechanism".
+* Values are predicted from keys, V_hat = f(K), and the cache keeps
+  delta = V - V_hat only for the tokens the predictor reconstructs worst --
+  same section, and the abstract of arXiv 2611.07025 (mlinfo.pages.dev).
+* Keys of a group of adjacent layers are stored as low-dimensional per-token
+  coefficients on a shared basis ("Cross-Layer Low-Rank Key Compression" on
+  the zicq.com English summary; xKV on the rit.work page).
+* At decode the context is split into chunks, the chunks suited to the current
+  query are picked, only those are rebuilt, and post-prefill tokens stay
+  uncompressed (rit.work page, section on generation).
+* Attention A = softmax(Q K^T / sqrt(d_h)), O = A V -- OjaKV page, section 3.
+* Quantisation and eviction compose with the pipeline (abstract; zicq.com
+  "Composition with Quantization and Eviction").
+
+Where the pages leave a step open, the reading taken here is stated in the
+docstring of the function that takes it (scorer = group-summed query against
+the chunk's mean coefficient; predictor input = reconstructed key; squared L2
+error per (layer, head); lowest index wins ties; symmetric per-channel int8
+with fp16 scales; eviction by the group-summed score of observation queries).
+
+Stored tensors are passed as numpy arrays in their storage dtype: float64,
+float32, float16, int8, or uint16 holding bfloat16 bit patterns.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F64, F32, BF16, F16, I8 = "f64", "f32", "bf16", "f16", "i8"
+
+
+# ============================================================================
+# number formats (round to nearest, ties to even)
+# ============================================================================
+def _round_sig(x: np.ndarray, sig_bits: int, min_exp: int) -> np.ndarray:
+    """Round float64 values to `sig_bits` significant bits, RNE.
+
+    The grid spacing at x is 2**(e - sig_bits) with x = m 2**e, 0.5 <= |m| < 1,
+    and never below 2**min_exp (gradual underflow).  x / spacing is an exact
+    power-of-two scaling, so np.rint applies round-half-even exactly.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    spacing_exp = np.maximum(e - sig_bits, min_exp)
+    return np.ldexp(np.rint(np.ldexp(x, -spacing_exp)), spacing_exp)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> bfloat16 (8 significant bits) bit patterns, single rounding."""
+    y = _round_sig(x, 8, -133)
+    with np.errstate(over="ignore"):
+        y32 = y.astype(np.float32)  # exact: y is on the bf16 grid (inf if too large)
+    return (y32.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def from_bf16_bits(u: np.ndarray) -> np.ndarray:
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def to_f16(x: np.ndarray) -> np.ndarray:
+    """float64 -> float16, single rounding (11 significant bits)."""
+    y = _round_sig(x, 11, -24)
+    with np.errstate(over="ignore"):
+        return y.astype(np.float16)
+
+
+def decode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values -> float64."""
+    if dtype == BF16:
+        return from_bf16_bits(x)
+    return np.asarray(x, dtype=np.float64)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 -> stored representation in `dtype` (not for i8: see quantise)."""
+    if dtype == F64:
+        return np.asarray(x, dtype=np.float64).copy()
+    if dtype == F32:
+        return np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == BF16:
+        return to_bf16_bits(x)
+    if dtype == F16:
+        return to_f16(x)
+    raise ValueError(dtype)
+
+
+def quantise(x: np.ndarray, axis: int):
+    """Symmetric per-channel int8 with fp16 scales (composition with quantisation,
+    zicq.com "Composition with Quantization and Eviction").
+
+    Reading: the channel is every index of the axes other than `axis`;
+    s = fp16(max |x| / 127) over `axis`; q = clamp(rne(x / s), -127, 127);
+    a channel whose scale is zero stores zeros.  Returns (q int8, s float16).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if x.shape[axis] == 0:
+        amax = np.zeros_like(x.sum(axis=axis, keepdims=True))
+    else:
+        amax = np.max(np.abs(x), axis=axis, keepdims=True)
+    s16 = to_f16(amax / 127.0)
+    s = s16.astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint(x / np.where(s > 0, s, 1.0)), 0.0)
+    q = np.clip(q, -127, 127).astype(np.int8)
+    return q, np.squeeze(s16, axis=axis)
+
+
+def dequantise(q: np.ndarray, s: np.ndarray, axis: int) -> np.ndarray:
+    return q.astype(np.float64) * np.expand_dims(s.astype(np.float64), axis)
+
+
+# ============================================================================
+# compress side
+# ============================================================================
+def basis_slice(U: np.ndarray, l: int, h: int, Hkv: int, dh: int) -> np.ndarray:
+    """U_{l,h}: rows (l, h, 0..dh-1) of the D x r group basis (D ordered (l, h, d))."""
+    r0 = (l * Hkv + h) * dh
+    return U[r0:r0 + dh, :]
+
+
+def project(k_cat: np.ndarray, U: np.ndarray) -> np.ndarray:
+    """Per-token group coefficients c_t = U^T k_t^cat (N x r), float64.
+
+    Cross-layer key compression stores low-dimensional coefficients on a basis
+    shared by the group (zicq.com English summary, "Cross-Layer Low-Rank Key
+    Compression").  Reading: the coefficients are per token and shared by
+    every layer and head of the group; the basis rows are sliced per (l, h).
+    """
+    return k_cat @ U
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def predict(khat: np.ndarray, w1, b1, w2, b2) -> np.ndarray:
+    """V_hat = f(K): per-head 2-layer MLP with SiLU (abstract: "lightweight
+    per-head predictor"; zicq.com "Core Mechanism": V_hat = f(K)).
+
+    Reading: f(k) = W2 SiLU(W1 k + b1) + b2 applied to the reconstructed key,
+    the only key available at decode.
+    """
+    return silu(khat @ w1.T + b1) @ w2.T + b2
+
+
+def l2_errors(v: np.ndarray, vhat: np.ndarray) -> np.ndarray:
+    """Squared L2 reconstruction error per token (ranking key for residuals)."""
+    d = v - vhat
+    return np.sum(d * d, axis=-1)
+
+
+def topk_indices(key: np.ndarray, k: int) -> np.ndarray:
+    """The k indices with the largest key, lowest index first among equal keys,
+    returned in ascending index order."""
+    n = key.shape[0]
+    k = max(0, min(k, n))
+    order = np.lexsort((np.arange(n), -key))  # primary: key desc, secondary: index asc
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def landmarks(cdeq: np.ndarray, C: int) -> np.ndarray:
+    """Chunk landmark = mean coefficient of the chunk's C tokens, rounded to fp32.
+
+    Reading of "picks the fragments suited to the current query" (rit.work,
+    generation section): each chunk is summarised by its mean coefficient.
+    """
+    N, r = cdeq.shape
+    return cdeq.reshape(N // C, C, r).mean(axis=1).astype(np.float32)
+
+
+def compress(inp: dict, s) -> dict:
+    """Compress a prefill: project keys, predict values, keep residuals for the
+    worst tokens, summarise chunks.  `inp` holds stored arrays (see synth.gen);
+    `s` carries sizes and dtypes.  Returns the stored cache and fp64 side data.
+
+    Steps (per sequence b):
+      1. c_t = U^T k_t^cat; store c~ = round(c) (or int8 + fp16 scales per
+         coefficient channel).
+      2. k_hat_{t,l,h} = U_{l,h} deq(c~_t).
+      3. v_hat = f_{l,h}(k_hat).
+      4. e_t = ||v_t - v_hat_t||^2 per (l, h).
+      5. R_{l,h} = top ceil(rho N) tokens by (e desc, t asc); store
+         delta_t = round(v_t - v_hat_t) for t in R, CSR by chunk, sorted by t
+         (or int8 + fp16 scales per (l, h, dim) over R).
+      6. landmark_j = mean of deq(c~_t) over chunk j, fp32.
+    """
+    B, G, Hkv, dh, N, C, r = s.B, s.G, s.Hkv, s.dh, s.N, s.C, s.r
+    n_c, n_res = N // C, s.n_res
+    act, cdt, rdt = s.act, s.coeff, s.resid
+    U_all = decode(inp["basis"], act)
+    out = {
+        "coeff": [], "coeff_scale": [], "landmark": [], "res_ptr": [], "res_idx": [],
+        "res_val": [], "res_scale": [], "errors": [], "c_exact": [],
+    }
+    for b in range(B):
+        U = U_all[b]
+        k = decode(inp["k"][b], act)                     # [G][Hkv][N][dh]
+        v = decode(inp["v"][b], act)
+        k_cat = k.transpose(2, 0, 1, 3).reshape(N, -1)   # token-major, (l, h, d)
+        c = project(k_cat, U)
+        out["c_exact"].append(c)
+        if cdt == I8:
+            cq, cs = quantise(c, axis=0)
+            cdeq = dequantise(cq, cs, axis=0)
+            out["coeff"].append(cq)
+            out["coeff_scale"].append(cs)
+        else:
+            cst = round_to(c, cdt)
+            out["coeff"].append(cst)
+            cdeq = decode(cst, cdt)
+        out["landmark"].append(landmarks(cdeq, C))
+        ptr_b, idx_b, val_b, sc_b, err_b = [], [], [], [], []
+        for l in range(G):
+            for h in range(Hkv):
+                Ulh = basis_slice(U, l, h, Hkv, dh)
+                khat = cdeq @ Ulh.T
+                w1, b1 = decode(inp["w1"][b, l, h], act), decode(inp["b1"][b, l, h], act)
+                w2, b2 = decode(inp["w2"][b, l, h], act), decode(inp["b2"][b, l, h], act)
+                vhat = predict(khat, w1, b1, w2, b2)
+                e = l2_errors(v[l, h], vhat)
+                err_b.append(e)
+                R = topk_indices(e, n_res)
+                delta = v[l, h][R] - vhat[R]
+                if rdt == I8:
+                    dq, ds = quantise(delta, axis=0)
+                    val_b.append(dq)
+                    sc_b.append(ds)
+                else:
+                    val_b.append(round_to(delta, rdt))
+                idx_b.append(R.astype(np.int32))
+                ptr_b.append(csr_pointers(R, C, n_c))
+        out["res_ptr"].append(np.stack(ptr_b).reshape(G, Hkv, n_c + 1))
+        out["res_idx"].append(np.stack(idx_b).reshape(G, Hkv, n_res))
+        out["res_val"].append(np.stack(val_b).reshape(G, Hkv, n_res, dh))
+        if rdt == I8:
+            out["res_scale"].append(np.stack(sc_b).reshape(G, Hkv, dh))
+        out["errors"].append(np.stack(err_b).reshape(G, Hkv, N))
+    cache = {k2: (np.stack(v2) if v2 else None) for k2, v2 in out.items()}
+    return cache
+
+
+def csr_pointers(R: np.ndarray, C: int, n_c: int) -> np.ndarray:
+    """ptr[j] = number of residual tokens with index < j*C (R sorted ascending)."""
+    ptr = np.zeros(n_c + 1, dtype=np.int32)
+    for j in range(n_c + 1):
+        ptr[j] = int(np.sum(R < j * C))
+    return ptr
+
+
+def coeff_deq(cache: dict, b: int, cdt: str) -> np.ndarray:
+    if cdt == I8:
+        return dequantise(cache["coeff"][b], cache["coeff_scale"][b], axis=0)
+    return decode(cache["coeff"][b], cdt)
+
+
+def resid_deq(cache: dict, b: int, l: int, h: int, rdt: str) -> np.ndarray:
+    if rdt == I8:
+        return dequantise(cache["res_val"][b, l, h], cache["res_scale"][b, l, h], axis=0)
+    return decode(cache["res_val"][b, l, h], rdt)
+
+
+# ============================================================================
+# decode side
+# ============================================================================
+def kv_head_of(g: int, Hq: int, Hkv: int) -> int:
+    """GQA: contiguous groups of Hq/Hkv query heads share a KV head."""
+    return (g * Hkv) // Hq
+
+
+def chunk_scores(landmark: np.ndarray, U: np.ndarray, q: np.ndarray, l: int, h: int,
+                 Hq: int, Hkv: int, dh: int) -> np.ndarray:
+    """s_j = q~ . landmark_j with q~ = U_{l,h}^T sum_{g in grp(h)} q_g (fp64).
+
+    Reading of the query-driven chunk choice (rit.work, generation section):
+    the group-summed query mapped into coefficient space, scored against each
+    chunk's mean coefficient.  Each score is an independent row-wise sum, so
+    equal landmark rows give equal scores.
+    """
+    grp = [g for g in range(Hq) if kv_head_of(g, Hq, Hkv) == h]
+    qsum = np.sum(q[grp], axis=0)
+    qt = basis_slice(U, l, h, Hkv, dh).T @ qsum
+    return np.sum(landmark.astype(np.float64) * qt[None, :], axis=1)
+
+
+def select_chunks(scores: np.ndarray, k: int) -> np.ndarray:
+    """top-min(k, n_c) chunks by (score desc, index asc), ascending."""
+    return topk_indices(scores, k)
+
+
+def softmax_attend(qg: np.ndarray, keys: np.ndarray, vals: np.ndarray) -> np.ndarray:
+    """o = softmax(keys q / sqrt(d_h)) vals, two-pass with the max subtracted
+    (OjaKV page, section 3, attention definition)."""
+    a = keys @ qg / math.sqrt(qg.shape[-1])
+    p = np.exp(a - np.max(a))
+    p = p / np.sum(p)
+    return p @ vals
+
+
+def decode_layer(cache: dict, inp: dict, s, l: int, q: np.ndarray, top_k: int,
+                 N: int | None = None, return_parts: bool = False):
+    """One decode step of attention at layer l of the group for B sequences.
+
+    q: [B][Hq][dh] stored.  Uses the stored cache (coeff, landmarks, residuals),
+    the stored basis and predictor, and the stored tail of layer l.
+    Returns (out [B][Hq][dh] float64, sel [B][Hkv][k'] int64).
+
+    For each (b, h): score chunks, pick the top k, rebuild the keys
+    k_hat = U_{l,h} deq(c~) and values v_hat + [t in R] delta of the picked
+    chunks only, append the uncompressed tail, and attend each query head of
+    the group over that set.
+    """
+    B, Hq, Hkv, dh, C = s.B, s.Hq, s.Hkv, s.dh, s.C
+    act, cdt, rdt = s.act, s.coeff, s.resid
+    N = s.N if N is None else N
+    n_c = N // C
+    kk = max(0, min(top_k, n_c))
+    out = np.zeros((B, Hq, dh))
+    sel = np.zeros((B, Hkv, kk), dtype=np.int64)
+    parts = {}
+    U_all = decode(inp["basis"], act)
+    for b in range(B):
+        U = U_all[b]
+        qb = decode(q[b], act)
+        cdeq = coeff_deq(cache, b, cdt) if n_c else np.zeros((0, s.r))
+        for h in range(Hkv):
+            if n_c and kk:
+                sc = chunk_scores(cache["landmark"][b], U, qb, l, h, Hq, Hkv, dh)
+                S = select_chunks(sc, kk)
+            else:
+                S = np.zeros(0, dtype=np.int64)
+            sel[b, h] = S
+            toks = (S[:, None] * C + np.arange(C)[None, :]).reshape(-1)
+            Ulh = basis_slice(U, l, h, Hkv, dh)
+            khat = cdeq[toks] @ Ulh.T
+            w1, b1 = decode(inp["w1"][b, l, h], act), decode(inp["b1"][b, l, h], act)
+            w2, b2 = decode(inp["w2"][b, l, h], act), decode(inp["b2"][b, l, h], act)
+            vals = predict(khat, w1, b1, w2, b2) if len(toks) else np.zeros((0, dh))
+            # residuals of the picked chunks: CSR slice per chunk
+            ptr = cache["res_ptr"][b, l, h]
+            R = cache["res_idx"][b, l, h]
+            dv = resid_deq(cache, b, l, h, rdt) if R.shape[0] else np.zeros((0, dh))
+            pos = {int(t): i for i, t in enumerate(toks)}
+            for j in S:
+                for e in range(int(ptr[j]), int(ptr[j + 1])):
+                    vals[pos[int(R[e])]] += dv[e]
+            kt = decode(inp["k_tail"][b, l, h], act)
+            vt = decode(inp["v_tail"][b, l, h], act)
+            keys = np.concatenate([khat, kt], axis=0)
+            allv = np.concatenate([vals, vt], axis=0)
+            if keys.shape[0] == 0:
+                raise ValueError("nothing to attend: no chunks selected and no tail")
+            for g in range(Hq):
+                if kv_head_of(g, Hq, Hkv) == h:
+                    out[b, g] = softmax_attend(qb[g], keys, allv)
+            if return_parts:
+                parts[(b, h)] = (keys, allv)
+    if return_parts:
+        return out, sel, parts
+    return out, sel
+
+
+def dense_decode_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, Hq: int, Hkv: int) -> np.ndarray:
+    """Uncompressed decode attention: q [B][Hq][dh], k/v [B][Hkv][n][dh] float64."""
+    B, _, dh = q.shape
+    out = np.zeros((B, Hq, dh))
+    for b in range(B):
+        for g in range(Hq):
+            h = kv_head_of(g, Hq, Hkv)
+            out[b, g] = softmax_attend(q[b, g], k[b, h], v[b, h])
+    return out
+
+
+# ============================================================================
+# eviction (composition with eviction)
+# ============================================================================
+def eviction_scores(cache: dict, inp: dict, s, obs_q: np.ndarray) -> np.ndarray:
+    """acc[b][j] = sum over observation queries w, layers l and KV heads h of the
+    chunk score s^{(w)}_{l,h,j} (fp64).
+
+    Reading of "eviction removes low-value tokens" (zicq.com Chinese summary,
+    composition section): since coefficients are shared by the whole group, a
+    chunk's value is its score summed over the group's layers and heads and
+    over a window of observation queries.
+    """
+    B, G, Hq, Hkv, dh = s.B, s.G, s.Hq, s.Hkv, s.dh
+    n_c = cache["landmark"].shape[1]
+    acc = np.zeros((B, n_c))
+    U_all = decode(inp["basis"], s.act)
+    for b in range(B):
+        for w in range(obs_q.shape[0]):
+            for l in range(G):
+                qb = decode(obs_q[w, b, l], s.act)
+                for h in range(Hkv):
+                    acc[b] += chunk_scores(cache["landmark"][b], U_all[b], qb, l, h, Hq, Hkv, dh)
+    return acc
+
+
+def evict(cache: dict, inp: dict, s, obs_q: np.ndarray, keep: int) -> dict:
+    """Keep the top `keep` chunks by (acc desc, j asc) per sequence and compact
+    them in ascending chunk order.  Residuals of evicted chunks are dropped;
+    kept residual tokens are renumbered to their new positions.  Residual
+    arrays keep their capacity; res_ptr[n_c'] gives the live count."""
+    B, G, Hkv, C = s.B, s.G, s.Hkv, s.C
+    acc = eviction_scores(cache, inp, s, obs_q)
+    n_res = cache["res_idx"].shape[-1]
+    dh = cache["res_val"].shape[-1]
+    new = {k: None for k in cache}
+    new["keep"] = np.stack([topk_indices(acc[b], keep) for b in range(B)])
+    new["acc"] = acc
+    new["coeff"] = np.stack([
+        cache["coeff"][b].reshape(-1, C, cache["coeff"].shape[-1])[new["keep"][b]].reshape(-1, cache["coeff"].shape[-1])
+        for b in range(B)])
+    new["coeff_scale"] = cache.get("coeff_scale")
+    new["landmark"] = np.stack([cache["landmark"][b][new["keep"][b]] for b in range(B)])
+    new["res_scale"] = cache.get("res_scale")
+    ptr = np.zeros((B, G, Hkv, keep + 1), dtype=np.int32)
+    idx = np.zeros((B, G, Hkv, n_res), dtype=np.int32)
+    val = np.zeros((B, G, Hkv, n_res, dh), dtype=cache["res_val"].dtype)
+    for b in range(B):
+        for l in range(G):
+            for h in range(Hkv):
+                op, oi, ov = cache["res_ptr"][b, l, h], cache["res_idx"][b, l, h], cache["res_val"][b, l, h]
+                n = 0
+                for jn, jo in enumerate(new["keep"][b]):
+                    ptr[b, l, h, jn] = n
+                    for e in range(int(op[jo]), int(op[jo + 1])):
+                        idx[b, l, h, n] = int(oi[e]) - jo * C + jn * C
+                        val[b, l, h, n] = ov[e]
+                        n += 1
+                ptr[b, l, h, keep] = n
+    new["res_ptr"], new["res_idx"], new["res_val"] = ptr, idx, val
+    return new
+
+
+# ============================================================================
+# storage accounting
+# ============================================================================
+DTYPE_BYTES = {F64: 8, F32: 4, BF16: 2, F16: 2, I8: 1}
+
+
+def m_kv(L: int, Hkv: int, dh: int, N: int, s_bytes: int) -> int:
+    """M_KV = 2 L H_kv d_h N s (zicq.com English summary, "Core Mechanism")."""
+    return 2 * L * Hkv * dh * N * s_bytes
+
+
+def compressed_bytes(G, Hkv, dh, N, C, r, F, n_res, act, coeff, resid) -> int:
+    """Bytes of one sequence's compressed group: coefficients, basis, predictor,
+    residual rows with their int32 token index, CSR pointers, fp32 landmarks
+    and fp16 scales.  The uncompressed tail is identical on both sides and is
+    not counted."""
+    D = G * Hkv * dh
+    n_c = N // C
+    s, sc, sr = DTYPE_BYTES[act], DTYPE_BYTES[coeff], DTYPE_BYTES[resid]
+    total = N * r * sc + D * r * s + G * Hkv * (2 * F * dh + F + dh) * s
+    total += G * Hkv * n_res * (dh * sr + 4) + G * Hkv * (n_c + 1) * 4 + n_c * r * 4
+    if coeff == I8:
+        total += r * 2
+    if resid == I8:
+        total += G * Hkv * dh * 2
+    return total

@@ -1,0 +1,449 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: printed
+values (tests/golden), closed forms, textbook identities, brute force on tiny
+inputs, or a library routine a special case reduces to.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lowram_oracle as O
+from synth import gen
+from synth.configs import F64, BF16, I8, QWEN4B_64K, Shape, small
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny64(**kw) -> Shape:
+    base = dict(name="pin", cfg_id=90, B=1, G=2, Hq=4, Hkv=2, dh=8, r=8, F=16, N=64, C=8,
+                k=2, T=4, rho=0.25, act=F64, coeff=F64, resid=F64, steps=2)
+    base.update(kw)
+    return Shape(**base)
+
+
+def kcat_of(inp, s, b):
+    k = O.decode(inp["k"][b], s.act)
+    return k.transpose(2, 0, 1, 3).reshape(s.N, -1)
+
+
+def recon_keys(cache, inp, s, b, l, h):
+    """k_hat rows written out with einsum, independent of the oracle's matmul path."""
+    U = O.decode(inp["basis"][b], s.act)
+    r0 = (l * s.Hkv + h) * s.dh
+    c = O.coeff_deq(cache, b, s.coeff)
+    return np.einsum("tr,dr->td", c, U[r0:r0 + s.dh])
+
+
+def mlp_explicit(x, w1, b1, w2, b2):
+    out = np.zeros((x.shape[0], w2.shape[0]))
+    for t in range(x.shape[0]):
+        pre = np.array([sum(w1[f, d] * x[t, d] for d in range(x.shape[1])) + b1[f] for f in range(w1.shape[0])])
+        hid = pre * (1.0 / (1.0 + np.exp(-pre)))
+        out[t] = w2 @ hid + b2
+    return out
+
+
+def sdpa64(q, k, v):
+    """torch's scaled_dot_product_attention in float64 on the CPU (library routine)."""
+    qt = torch.from_numpy(np.ascontiguousarray(q))[None, None, None, :]
+    kt = torch.from_numpy(np.ascontiguousarray(k))[None, None]
+    vt = torch.from_numpy(np.ascontiguousarray(v))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, 0, 0].numpy()
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+def test_bf16_rounding_golden():
+    with open(os.path.join(GOLDEN, "bf16_rounding.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    xs = np.array([float.fromhex(a) for a, _ in rows])
+    want = np.array([int(b, 16) for _, b in rows], dtype=np.uint16)
+    got = O.to_bf16_bits(xs)
+    assert np.array_equal(got, want), list(zip(rows, [hex(g) for g in got]))
+
+
+def test_bf16_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(1)
+    x32 = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.to_bf16_bits(x32.astype(np.float64))
+    assert np.array_equal(got, want)
+    back = O.from_bf16_bits(got)
+    assert np.array_equal(back, torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy())
+
+
+def test_f16_matches_numpy():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(200000) * np.exp(rng.uniform(-18, 11, 200000))
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16)
+    assert np.array_equal(O.to_f16(x).view(np.uint16), ref.view(np.uint16))
+    # ties to even at 11 significant bits, single rounding from float64
+    assert O.to_f16(np.array([1 + 2.0 ** -11]))[0] == np.float16(1.0)
+    assert O.to_f16(np.array([1 + 2.0 ** -11 + 2.0 ** -40]))[0] == np.float16(1 + 2.0 ** -10)
+
+
+# ---------------------------------------------------------------------------
+# keys: projection and reconstruction
+# ---------------------------------------------------------------------------
+def test_basis_is_orthonormal():
+    s = tiny64(r=20)
+    inp = gen.make(s)
+    U = O.decode(inp["basis"][0], s.act)
+    assert np.max(np.abs(U.T @ U - np.eye(s.r))) < 1e-12
+
+
+def test_full_rank_reconstructs_keys_exactly():
+    s = tiny64(r=32)  # r = D
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    for l in range(s.G):
+        for h in range(s.Hkv):
+            k = O.decode(inp["k"][0, l, h], s.act)
+            kh = recon_keys(cache, inp, s, 0, l, h)
+            assert np.max(np.abs(kh - k)) <= 1e-12 * np.max(np.abs(k))
+
+
+@pytest.mark.parametrize("r", [1, 5, 13])
+def test_eckart_young(r):
+    s = tiny64(r=r, N=96, C=8)
+    inp = gen.make(s)
+    K = kcat_of(inp, s, 0)
+    _, sig, vt = np.linalg.svd(K, full_matrices=False)
+    inp["basis"] = vt[:r].T[None].copy()
+    cache = O.compress(inp, s)
+    err = 0.0
+    for l in range(s.G):
+        for h in range(s.Hkv):
+            k = O.decode(inp["k"][0, l, h], s.act)
+            err += np.sum((recon_keys(cache, inp, s, 0, l, h) - k) ** 2)
+    assert err == pytest.approx(np.sum(sig[r:] ** 2), rel=1e-9, abs=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# values: predictor and residuals
+# ---------------------------------------------------------------------------
+def test_predictor_matches_explicit_mlp():
+    s = tiny64(N=16, C=8)
+    inp = gen.make(s)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, s.dh))
+    w1, b1, w2, b2 = (O.decode(inp[n][0, 1, 0], s.act) for n in ("w1", "b1", "w2", "b2"))
+    assert np.allclose(O.predict(x, w1, b1, w2, b2), mlp_explicit(x, w1, b1, w2, b2), rtol=1e-13, atol=1e-13)
+
+
+def test_zero_first_layer_gives_b2():
+    s = tiny64()
+    inp = gen.make(s)
+    inp["w1"][:] = 0.0
+    inp["b1"][:] = 0.0
+    cache = O.compress(inp, s)
+    for l in range(s.G):
+        for h in range(s.Hkv):
+            v = O.decode(inp["v"][0, l, h], s.act)
+            b2 = O.decode(inp["b2"][0, l, h], s.act)
+            assert np.allclose(cache["errors"][0, l, h], np.sum((v - b2) ** 2, axis=1), rtol=1e-13)
+
+
+def test_noise_free_full_rank_needs_no_residual():
+    s = tiny64(r=32)
+    inp = gen.make(s, noise_scale=0.0)
+    cache = O.compress(inp, s)
+    assert np.max(cache["errors"]) < 1e-20
+    assert np.max(np.abs(cache["res_val"])) < 1e-10
+
+
+def test_all_residuals_give_exact_values():
+    s = tiny64(r=32, rho=1.0)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    for l in range(s.G):
+        for h in range(s.Hkv):
+            k = recon_keys(cache, inp, s, 0, l, h)
+            w = [O.decode(inp[n][0, l, h], s.act) for n in ("w1", "b1", "w2", "b2")]
+            vhat = mlp_explicit(k, *w)
+            idx = cache["res_idx"][0, l, h]
+            assert np.array_equal(idx, np.arange(s.N))
+            v = O.decode(inp["v"][0, l, h], s.act)
+            assert np.max(np.abs(vhat + O.decode(cache["res_val"][0, l, h], s.resid) - v)) < 1e-12
+
+
+def test_residual_set_is_brute_force_topk():
+    s = tiny64(N=48, C=8, rho=0.3)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    for l in range(s.G):
+        for h in range(s.Hkv):
+            e = cache["errors"][0, l, h]
+            want = sorted(sorted(range(s.N), key=lambda t: (-e[t], t))[:s.n_res])
+            assert list(cache["res_idx"][0, l, h]) == want
+            ptr = cache["res_ptr"][0, l, h]
+            for j in range(s.n_c + 1):
+                assert ptr[j] == sum(1 for t in want if t < j * s.C)
+
+
+def test_topk_ties_go_to_lower_index():
+    key = np.array([1.0, 5.0, 3.0, 5.0, 2.0, 5.0])
+    assert list(O.topk_indices(key, 1)) == [1]
+    assert list(O.topk_indices(key, 2)) == [1, 3]
+    assert list(O.topk_indices(key, 4)) == [1, 2, 3, 5]
+    assert list(O.topk_indices(key, 99)) == [0, 1, 2, 3, 4, 5]
+    rng = np.random.default_rng(4)
+    for trial in range(200):
+        n = int(rng.integers(1, 40))
+        key = rng.integers(0, 5, n).astype(np.float64)
+        k = int(rng.integers(0, n + 2))
+        want = sorted(sorted(range(n), key=lambda t: (-key[t], t))[:k])
+        assert list(O.topk_indices(key, k)) == want
+
+
+def test_duplicated_tokens_tie_to_lower_index():
+    s = tiny64(N=32, C=8, rho=0.125)  # n_res = 4
+    inp = gen.make(s)
+    # token 20 becomes an exact copy of token 3 in every layer and head
+    for name in ("k", "v"):
+        inp[name][:, :, :, 20] = inp[name][:, :, :, 3]
+    # make their error the largest: push their value far off
+    inp["v"][:, :, :, 3] += 50.0
+    inp["v"][:, :, :, 20] = inp["v"][:, :, :, 3]
+    s1 = s.replace(rho=1.0 / 32)  # n_res = 1: exactly one of the two tied tokens
+    cache = O.compress(inp, s1)
+    assert cache["errors"][0, 0, 0, 3] == cache["errors"][0, 0, 0, 20]
+    assert np.all(cache["res_idx"][..., 0] == 3)
+
+
+def test_outlier_tokens_all_get_residuals():
+    s = small(QWEN4B_64K, B=1, N=16 * 256)
+    inp = gen.make(s)
+    assert inp["outliers"].shape[1] == round(0.01 * s.N)
+    cache = O.compress(inp, s)
+    for l in range(s.G):
+        for h in range(s.Hkv):
+            assert set(inp["outliers"][0].tolist()) <= set(cache["res_idx"][0, l, h].tolist())
+
+
+# ---------------------------------------------------------------------------
+# chunk scorer and selection
+# ---------------------------------------------------------------------------
+def test_chunk_score_equals_mean_token_score():
+    s = tiny64(N=64, C=8, r=12)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    q = O.decode(inp["q"][0, 1, 0], s.act)  # step 0, layer 1, b 0
+    for h in range(s.Hkv):
+        kh = recon_keys(cache, inp, s, 0, 1, h)
+        grp = [g for g in range(s.Hq) if g * s.Hkv // s.Hq == h]
+        per_tok = sum(kh @ q[g] for g in grp)
+        want = per_tok.reshape(s.n_c, s.C).mean(axis=1)
+        got = O.chunk_scores(cache["landmark"][0], O.decode(inp["basis"][0], s.act), q, 1, h,
+                             s.Hq, s.Hkv, s.dh)
+        assert np.allclose(got, want, rtol=1e-6, atol=1e-6 * np.max(np.abs(want)))
+
+
+def test_selection_is_brute_force_and_ties_lower_chunk():
+    s = tiny64(N=64, C=8, r=12, k=3)
+    inp = gen.make(s)
+    # chunk 6 becomes a copy of chunk 2, so their landmarks (and scores) are equal
+    inp["k"][:, :, :, 48:56] = inp["k"][:, :, :, 16:24]
+    cache = O.compress(inp, s)
+    assert np.array_equal(cache["landmark"][0, 6], cache["landmark"][0, 2])
+    U = O.decode(inp["basis"][0], s.act)
+    for step in range(2):
+        q = O.decode(inp["q"][step, 0, 0], s.act)
+        for h in range(s.Hkv):
+            sc = O.chunk_scores(cache["landmark"][0], U, q, 0, h, s.Hq, s.Hkv, s.dh)
+            assert sc[6] == sc[2]
+            for k in range(0, s.n_c + 2):
+                want = sorted(sorted(range(s.n_c), key=lambda j: (-sc[j], j))[:k])
+                assert list(O.select_chunks(sc, k)) == want
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+def _independent_decode(cache, inp, s, l, q, sel):
+    """Brute force: rebuild the selected keys/values with einsum and explicit
+    loops, append the tail, attend with torch's SDPA in float64."""
+    out = np.zeros((s.B, s.Hq, s.dh))
+    for b in range(s.B):
+        qb = O.decode(q[b], s.act)
+        for h in range(s.Hkv):
+            kh = recon_keys(cache, inp, s, b, l, h)
+            w = [O.decode(inp[n][b, l, h], s.act) for n in ("w1", "b1", "w2", "b2")]
+            toks = [j * s.C + i for j in sel[b, h] for i in range(s.C)]
+            vh = mlp_explicit(kh[toks], *w) if toks else np.zeros((0, s.dh))
+            resid = dict(zip(cache["res_idx"][b, l, h][: cache["res_ptr"][b, l, h][-1]].tolist(),
+                             O.resid_deq(cache, b, l, h, s.resid)))
+            for i, t in enumerate(toks):
+                if t in resid:
+                    vh[i] = vh[i] + resid[t]
+            keys = np.concatenate([kh[toks], O.decode(inp["k_tail"][b, l, h], s.act)])
+            vals = np.concatenate([vh, O.decode(inp["v_tail"][b, l, h], s.act)])
+            for g in range(s.Hq):
+                if g * s.Hkv // s.Hq == h:
+                    out[b, g] = sdpa64(qb[g], keys, vals)
+    return out
+
+
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_decode_matches_brute_force(k):
+    s = tiny64(N=64, C=8, r=12, k=k, B=2)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    for l in range(s.G):
+        out, sel = O.decode_layer(cache, inp, s, l, inp["q"][0, l], k)
+        assert sel.shape == (s.B, s.Hkv, min(k, s.n_c))
+        want = _independent_decode(cache, inp, s, l, inp["q"][0, l], sel)
+        assert np.allclose(out, want, rtol=1e-11, atol=1e-12)
+
+
+def test_exact_cache_all_chunks_equals_dense_attention():
+    s = tiny64(r=32, rho=1.0, B=2)  # r = D and residuals on every token: exact K/V
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    for l in range(s.G):
+        q = inp["q"][1, l]
+        out, sel = O.decode_layer(cache, inp, s, l, q, s.n_c)
+        assert np.array_equal(sel[0, 0], np.arange(s.n_c))
+        for b in range(s.B):
+            for g in range(s.Hq):
+                h = g * s.Hkv // s.Hq
+                K = np.concatenate([inp["k"][b, l, h], inp["k_tail"][b, l, h]])
+                V = np.concatenate([inp["v"][b, l, h], inp["v_tail"][b, l, h]])
+                assert np.allclose(out[b, g], sdpa64(q[b, g], K, V), rtol=1e-10, atol=1e-11)
+
+
+def test_mha_reduces_to_per_head_attention():
+    s = tiny64(Hq=2, Hkv=2, r=32, rho=1.0)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    q = inp["q"][0, 0]
+    out, _ = O.decode_layer(cache, inp, s, 0, q, s.n_c)
+    for g in range(2):
+        K = np.concatenate([inp["k"][0, 0, g], inp["k_tail"][0, 0, g]])
+        V = np.concatenate([inp["v"][0, 0, g], inp["v_tail"][0, 0, g]])
+        assert np.allclose(out[0, g], sdpa64(q[0, g], K, V), rtol=1e-10, atol=1e-11)
+
+
+def test_tail_only_and_no_tail():
+    s = tiny64(B=1)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    q = inp["q"][0, 0]
+    out, sel = O.decode_layer(cache, inp, s, 0, q, 0)  # k = 0: the tail alone
+    assert sel.shape[-1] == 0
+    for g in range(s.Hq):
+        h = g * s.Hkv // s.Hq
+        assert np.allclose(out[0, g], sdpa64(q[0, g], inp["k_tail"][0, 0, h], inp["v_tail"][0, 0, h]))
+    s0 = s.replace(T=0)
+    inp0 = gen.make(s0)
+    cache0 = O.compress(inp0, s0)
+    out0, sel0 = O.decode_layer(cache0, inp0, s0, 1, inp0["q"][0, 1], 2)
+    want = _independent_decode(cache0, inp0, s0, 1, inp0["q"][0, 1], sel0)
+    assert np.allclose(out0, want, rtol=1e-11, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.decode_layer(cache0, inp0, s0, 0, inp0["q"][0, 0], 0)
+
+
+# ---------------------------------------------------------------------------
+# storage accounting
+# ---------------------------------------------------------------------------
+def test_mkv_golden_llama8b():
+    with open(os.path.join(GOLDEN, "mkv_llama8b_32k.json")) as f:
+        g = json.load(f)
+    total = g["B"] * O.m_kv(g["L"], g["Hkv"], g["dh"], g["N"], g["s_bytes"])
+    assert total == g["expected_bytes"] == 16 * 2 ** 30
+    assert abs(total / 1e9 - g["printed_GB"]) / g["printed_GB"] < 0.08
+
+
+def test_value_side_ratio_near_printed_4x():
+    with open(os.path.join(GOLDEN, "value_ratio_4x.json")) as f:
+        g = json.load(f)
+    N = 4096
+    dense_v = N * g["dh"] * g["s_bytes"]
+    resid = math.ceil(g["rho"] * N) * (g["dh"] * g["s_bytes"] + 4)
+    assert abs(dense_v / resid / g["printed_ratio"] - 1) < g["tolerance_rel"]
+
+
+def test_compressed_bytes_counts_each_stored_tensor():
+    s = tiny64(coeff=F64, resid=F64)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    stored = (cache["coeff"][0].nbytes + inp["basis"][0].nbytes
+              + sum(inp[n][0].nbytes for n in ("w1", "b1", "w2", "b2"))
+              + cache["res_val"][0].nbytes + cache["res_idx"][0].nbytes
+              + cache["res_ptr"][0].nbytes + cache["landmark"][0].nbytes)
+    assert O.compressed_bytes(s.G, s.Hkv, s.dh, s.N, s.C, s.r, s.F, s.n_res, s.act, s.coeff, s.resid) == stored
+
+
+# ---------------------------------------------------------------------------
+# quantisation
+# ---------------------------------------------------------------------------
+def test_int8_quantisation_bounds():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((500, 7)) * np.array([1e-3, 0.1, 1, 10, 100, 3e3, 0.0])
+    q, s16 = O.quantise(x, axis=0)
+    s = s16.astype(np.float64)
+    assert q.dtype == np.int8 and s16.dtype == np.float16
+    assert np.all(np.abs(q) <= 127)
+    deq = O.dequantise(q, s16, axis=0)
+    amax = np.max(np.abs(x), axis=0)
+    bound = s / 2 + np.maximum(amax - 127 * s, 0) + 1e-300
+    assert np.all(np.abs(deq - x) <= bound[None, :] * (1 + 1e-12))
+    assert np.all(q[:, 6] == 0) and s[6] == 0
+    grid = np.arange(-127, 128)[:, None] * s[None, :5]
+    q2, s2 = O.quantise(grid, axis=0)
+    assert np.array_equal(s2, s16[:5])
+    assert np.array_equal(O.dequantise(q2, s2, axis=0), grid)
+
+
+# ---------------------------------------------------------------------------
+# eviction
+# ---------------------------------------------------------------------------
+def test_eviction_keeps_top_chunks_by_group_score():
+    s = tiny64(N=128, C=8, r=12, coeff=F64, n_obs=3, B=2)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    keep = 4
+    new = O.evict(cache, inp, s, inp["obs_q"], keep)
+    for b in range(s.B):
+        acc = np.zeros(s.n_c)
+        for w in range(s.n_obs):
+            for l in range(s.G):
+                q = O.decode(inp["obs_q"][w, b, l], s.act)
+                for h in range(s.Hkv):
+                    kh = recon_keys(cache, inp, s, b, l, h)
+                    grp = [g for g in range(s.Hq) if g * s.Hkv // s.Hq == h]
+                    acc += sum(kh @ q[g] for g in grp).reshape(s.n_c, s.C).mean(axis=1)
+        assert np.allclose(new["acc"][b], acc, rtol=1e-6, atol=1e-6 * np.max(np.abs(acc)))
+        order = sorted(range(s.n_c), key=lambda j: (-acc[j], j))
+        gap = acc[order[keep - 1]] - acc[order[keep]]
+        assert gap > 1e-4 * np.max(np.abs(acc))
+        assert list(new["keep"][b]) == sorted(order[:keep])
+        # kept coefficients and residuals map back to the original tokens
+        for jn, jo in enumerate(new["keep"][b]):
+            assert np.array_equal(new["coeff"][b, jn * s.C:(jn + 1) * s.C], cache["coeff"][b, jo * s.C:(jo + 1) * s.C])
+        for l in range(s.G):
+            for h in range(s.Hkv):
+                n = new["res_ptr"][b, l, h, keep]
+                old = dict(zip(cache["res_idx"][b, l, h].tolist(), cache["res_val"][b, l, h]))
+                for e in range(n):
+                    t = int(new["res_idx"][b, l, h, e])
+                    jo = new["keep"][b][t // s.C]
+                    assert np.array_equal(new["res_val"][b, l, h, e], old[jo * s.C + t % s.C])
+                assert n == sum(1 for t in old if t // s.C in set(new["keep"][b].tolist()))
+
+
+def test_eviction_keep_all_is_identity():
+    s = tiny64(N=64, C=8, n_obs=2)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    new = O.evict(cache, inp, s, inp["obs_q"], s.n_c)
+    for name in ("coeff", "landmark", "res_ptr", "res_idx", "res_val"):
+        assert np.array_equal(new[name], cache[name]), name
