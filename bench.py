@@ -1,0 +1,309 @@
+"""Benchmark of the compressed-KV decode step on one MI355X.
+
+One step = one new query per sequence through every layer of an xKV group
+(G lowram_decode_attn calls: chunk select, rebuild-and-attend, combine) on the
+Llama-3.1-8B-shaped workload: B=4, 32 q / 8 kv heads, d_h=128, 4-layer group,
+rank 512, predictor 128-256-128, residuals on 12.5% of tokens, 32K context,
+chunks of 128, top-32 chunks, 128-token uncompressed tail, bf16.  Inputs are
+seeded synthetic data resident in HBM before the timed region.
+
+Prints one JSON line: seq-steps/s, the roofline of the rebuild-and-attend
+kernel (HIP events on its stream), the dense bf16 comparator on the same
+queries (x vs dense), and the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic_llama8b_32k.json")
+ATTEND_SRC = os.path.join(ROOT, "decode_attention_compressed_amd", "csrc", "k_attend_mfma.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama8b-32k")
+    ap.add_argument("--batch", type=int, default=0, help="override the batch (e.g. 16/32/64 for mistral7b-16k)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def attend_accounting(s, sel, res_ptr, layer):
+    """Algorithmic HBM bytes and FLOPs of one rebuild-and-attend launch.
+
+    bytes: the union over kv heads of the selected coefficient tiles (each
+    read once per sequence), the layer's basis slice and first predictor
+    layer, residual rows (+int32 index) and CSR pointers of the selected
+    chunks, the layer's tail K/V and the queries.
+    flops: per selected token-head 2(d_h r + F d_h + g d_h + g F) (rebuilt key,
+    hidden layer, logits, p-weighted hidden sum), plus the tail's 4 T d_h per
+    query head."""
+    B, Hkv, C, r, dh, F, T = s.B, s.Hkv, s.C, s.r, s.dh, s.F, s.T
+    sa, sc, sr = 2, (1 if s.coeff == "i8" else 2), (1 if s.resid == "i8" else 2)
+    union = sum(len(np.unique(sel[b])) for b in range(B))
+    nbytes = union * C * r * sc
+    if s.coeff == "i8":
+        nbytes += B * r * 2
+    nbytes += B * Hkv * dh * r * sa + B * Hkv * (F * dh + F) * sa
+    rows = 0
+    for b in range(B):
+        for h in range(Hkv):
+            p = res_ptr[b, layer, h]
+            rows += int(np.sum(p[sel[b, h] + 1] - p[sel[b, h]]))
+    nbytes += rows * (dh * sr + 4) + B * Hkv * sel.shape[-1] * 8
+    if s.resid == "i8":
+        nbytes += B * Hkv * dh * 2
+    nbytes += 2 * B * Hkv * T * dh * sa + B * s.Hq * dh * sa
+    g = s.Hq // Hkv
+    flops = B * Hkv * sel.shape[-1] * C * 2 * (dh * r + F * dh + g * dh + g * F) + B * s.Hq * T * dh * 4
+    return nbytes, flops, union
+
+
+def step_bytes(s, attend_b):
+    """Whole-step extras beyond the attend kernel: landmarks read by the
+    scorer, basis slice read by the scorer, W2/b2 and partial-free output."""
+    B, Hkv, dh, r, F = s.B, s.Hkv, s.dh, s.r, s.F
+    n_c = s.N_after // s.C
+    return attend_b + B * n_c * r * 4 + B * Hkv * dh * r * 2 + B * Hkv * (dh * F + dh) * 2 + B * s.Hq * dh * 2
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per attend launch measured by rocprofv3 counters, if they were
+    taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    src = hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()
+    if t.get("kernel_sha256") != src:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(s, host, inp, budget_s):
+    from oracle import lowram_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        for layer in range(s.G):
+            O.decode_layer(host, inp, s, layer, inp["q"][steps % inp["q"].shape[0], layer], s.k, N=s.N_after)
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s or steps >= 8:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": s.B * steps / dt, "unit": "seq-steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} full decode step(s) ({s.G} layers x B={s.B}) of the {s.name} workload, "
+                      f"float64 numpy oracle, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards over "
+              "sequences with no exchange, so N GPUs run N independent copies).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import decode_attention_compressed_amd as P
+    from synth import gen
+    from synth.configs import BY_NAME
+    from tests.harness import cache_to_host, dims_of, model_of, to_dev, to_host, upload
+
+    s = BY_NAME[args.workload]
+    if args.batch:
+        s = s.replace(B=args.batch)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev_name = torch.cuda.get_device_name(0)
+    log(f"workload {s.name}: {s}")
+    t0 = time.perf_counter()
+    n_q = min(64, max(args.steps, 1))
+    inp = gen.make(s, steps=n_q)
+    log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
+    dev = upload(inp)
+    d = dims_of(s)
+    model = model_of(dev)
+    cache = P.alloc_cache(d)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    P.compress(d, model, dev["k"], dev["v"], cache)
+    ev[1].record()
+    torch.cuda.synchronize()
+    compress_ms = ev[0].elapsed_time(ev[1])
+    log(f"compress {compress_ms:.1f} ms")
+    if s.evict_keep < 1.0:
+        cache, d, _ = P.evict(d, model, cache, to_dev(inp["obs_q"]), s.keep_chunks)
+        torch.cuda.synchronize()
+    comp_bytes, dense_bytes = P.cache_bytes(dims_of(s))
+
+    # per (query set, layer) pre-marshalled calls
+    kk = P.k_eff(d)
+    ws = P.workspace(d, P._lib.OP_DECODE)
+    out = torch.empty((s.B, s.Hq, s.dh), dtype=torch.bfloat16, device="cuda")
+    sels = [[torch.empty((s.B, s.Hkv, kk), dtype=torch.int32, device="cuda") for _ in range(s.G)] for _ in range(n_q)]
+    calls = [[P.DecodeCall(d, l, model, cache, dev["q"][i, l], dev["k_tail"], dev["v_tail"], out, ws, sels[i][l])
+              for l in range(s.G)] for i in range(n_q)]
+
+    def step(i):
+        for c in calls[i % n_q]:
+            c()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps captured in one HIP graph -------------------
+    graph = None
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+    except Exception as e:  # capture unsupported: time eager launches instead
+        log(f"graph capture failed ({e}); timing eager launches")
+        graph = None
+    torch.cuda.synchronize()
+    ev[0].record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms_total = ev[0].elapsed_time(ev[1])
+    ms_step = ms_total / args.steps
+    log(f"{args.steps} steps in {ms_total:.3f} ms -> {ms_step * 1e3:.1f} us/step (graph={graph is not None})")
+
+    # ---- attend-kernel timing with events on its stream ------------------------
+    stream = torch.cuda.current_stream()
+    n_time = min(args.steps, n_q)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_time * s.G)]
+    k = 0
+    for i in range(n_time):
+        for c in calls[i]:
+            c.select()
+            evs[k][0].record(stream)
+            c.attend()
+            evs[k][1].record(stream)
+            c.combine()
+            k += 1
+    torch.cuda.synchronize()
+    attend_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    host_ptr = to_host(cache["res_ptr"])
+    acc = [attend_accounting(s, to_host(sels[i][l]), host_ptr, l) for i in range(n_time) for l in range(s.G)]
+    a_bytes = np.mean([a[0] for a in acc])
+    a_flops = np.mean([a[1] for a in acc])
+    union = np.mean([a[2] for a in acc]) / s.B
+    t_attend = attend_ms.mean() * 1e-3
+    gbps = a_bytes / t_attend / 1e9
+    tflops = a_flops / t_attend / 1e12
+    t_hbm, t_mfma = a_bytes / (HBM_PEAK_GBPS * 1e9), a_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = traffic_for_current_kernel()
+    roof.update({"kernel": "k_attend_mfma (rebuild-and-attend)", "avg_launch_us": round(t_attend * 1e6, 2),
+                 "algorithmic_bytes_per_launch": int(a_bytes), "algorithmic_flops_per_launch": int(a_flops),
+                 "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                 "hbm_gbps": round(gbps, 1), "roof_time_us": round(max(t_hbm, t_mfma) * 1e6, 2),
+                 "frac_of_binding_roof": round(max(t_hbm, t_mfma) / t_attend, 4)})
+    log(f"attend {t_attend * 1e6:.1f} us/launch, {gbps:.0f} GB/s, {tflops:.1f} TF/s, union {union:.1f} chunks/seq")
+
+    # ---- dense comparator on the same queries ---------------------------------
+    dense = None
+    if not args.no_dense:
+        kd = torch.cat([dev["k"], dev["k_tail"]], dim=3).contiguous()
+        vd = torch.cat([dev["v"], dev["v_tail"]], dim=3).contiguous()
+        dws = P.dense_workspace(d, kd.shape[3])
+        dout = torch.empty_like(out)
+        for i in range(2):
+            for l in range(s.G):
+                P.dense_decode_attn(d, dev["q"][i, l], kd, vd, l, out=dout, ws=dws)
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(args.steps):
+            for l in range(s.G):
+                P.dense_decode_attn(d, dev["q"][i % n_q, l], kd, vd, l, out=dout, ws=dws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        dense_ms = ev[0].elapsed_time(ev[1]) / args.steps
+        dense_bytes_step = 2 * s.B * s.G * s.Hkv * kd.shape[3] * s.dh * 2
+        dense = {"ms_per_step": round(dense_ms, 4), "hbm_gbps": round(dense_bytes_step / (dense_ms * 1e-3) / 1e9, 1),
+                 "kernel": "k_dense (bf16 split-K, eager launches)"}
+        log(f"dense {dense_ms * 1e3:.1f} us/step, {dense['hbm_gbps']} GB/s")
+        del kd, vd
+
+    # ---- CPU oracle on a bounded sample ---------------------------------------
+    cpu = None
+    if not args.no_cpu:
+        host = cache_to_host(cache)
+        cpu = cpu_baseline(s, host, inp, args.cpu_seconds)
+        log(f"cpu oracle {cpu['value']:.3f} seq-steps/s on {cpu['cores']} threads")
+
+    step_b = step_bytes(s, a_bytes) * s.G
+    result = {
+        "metric": "decode-attn seq-steps/s and HBM GB/s (% peak) at Llama-8B shape 32K; x vs dense",
+        "value": round(s.B / (ms_step * 1e-3), 1),
+        "unit": "seq-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded spectrum-decayed keys, MLP+Student-t values, N(0,1) queries)",
+        "config": {"workload": s.name, "B": s.B, "G": s.G, "Hq": s.Hq, "Hkv": s.Hkv, "dh": s.dh,
+                   "r": s.r, "F": s.F, "N": s.N_after, "C": s.C, "top_k": s.k, "T": s.T,
+                   "rho": s.rho, "coeff": s.coeff, "resid": s.resid, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "step_hbm_gbps": round(step_b / (ms_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_b / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "x_vs_dense": round(dense["ms_per_step"] / ms_step, 3) if dense else None,
+        "dense": dense,
+        "compression_ratio": round(dense_bytes / comp_bytes, 3),
+        "selected_chunk_union_per_seq": round(float(union), 1),
+        "compress_ms": round(compress_ms, 2),
+        "graph": graph is not None,
+        "device": dev_name,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

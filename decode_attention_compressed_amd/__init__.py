@@ -1,0 +1,13 @@
+"""MI355X (gfx950) compressed-KV decode attention: LowRAM's decode-step hot path.
+
+The HIP library (liblowram.so, C ABI in include/lowram.h) does all the work;
+this package marshals torch tensors into it.
+"""
+from . import _lib
+from ._lib import LowramError
+from .api import (DecodeCall, alloc_cache, cache_bytes, compress, decode_attn, dense_decode_attn,
+                  dense_workspace, evict, k_eff, make_dims, with_, workspace, workspace_bytes)
+
+__all__ = ["DecodeCall", "LowramError", "alloc_cache", "cache_bytes", "compress", "decode_attn",
+           "dense_decode_attn", "dense_workspace", "evict", "k_eff", "make_dims", "with_",
+           "workspace", "workspace_bytes", "_lib"]

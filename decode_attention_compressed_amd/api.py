@@ -1,0 +1,242 @@
+"""Torch-facing binding of the lowram C ABI (argument marshalling only).
+
+Every computation runs in the HIP library; torch provides device memory and
+the current stream.  Shapes and dtypes are checked here so that mistakes
+surface as Python exceptions, and the library re-validates everything.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+from ._lib import LowramError  # noqa: F401  (re-export)
+
+TORCH_DT = {L.F32: torch.float32, L.BF16: torch.bfloat16, L.I8: torch.int8}
+NAME_DT = {"f32": L.F32, "bf16": L.BF16, "i8": L.I8, "f16": L.F16}
+
+
+def make_dims(batch, layers, heads_q, heads_kv, head_dim, rank, hidden, n_ctx, chunk, top_k,
+              n_tail, n_res, act="bf16", coeff="bf16", resid="bf16") -> L.Dims:
+    d = L.Dims()
+    vals = dict(batch=batch, layers=layers, heads_q=heads_q, heads_kv=heads_kv, head_dim=head_dim,
+                rank=rank, hidden=hidden, n_ctx=n_ctx, chunk=chunk, top_k=top_k, n_tail=n_tail,
+                n_res=n_res, act=NAME_DT.get(act, act), coeff=NAME_DT.get(coeff, coeff),
+                resid=NAME_DT.get(resid, resid))
+    for k, v in vals.items():
+        setattr(d, k, int(v))
+    return d
+
+
+def with_(d: L.Dims, **kw) -> L.Dims:
+    vals = d.as_dict()
+    vals.update(kw)
+    out = L.Dims()
+    for k, v in vals.items():
+        setattr(out, k, int(v))
+    return out
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def n_chunks(d: L.Dims) -> int:
+    return d.n_ctx // d.chunk
+
+
+def k_eff(d: L.Dims) -> int:
+    return min(d.top_k, n_chunks(d))
+
+
+def workspace_bytes(d: L.Dims, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    L.check(L.lib().lowram_workspace_bytes(ctypes.byref(d), op, ctypes.byref(n)))
+    return n.value
+
+
+def workspace(d: L.Dims, op: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(1, workspace_bytes(d, op)), dtype=torch.uint8, device=device)
+
+
+def cache_bytes(d: L.Dims):
+    c, dn = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    L.check(L.lib().lowram_cache_bytes(ctypes.byref(d), ctypes.byref(c), ctypes.byref(dn)))
+    return c.value, dn.value
+
+
+def cache_shapes(d: L.Dims) -> dict:
+    B, G, H, dh, r, N, C = d.batch, d.layers, d.heads_kv, d.head_dim, d.rank, d.n_ctx, d.chunk
+    n_c = N // C
+    shapes = {
+        "coeff": ((B, N, r), TORCH_DT[d.coeff]),
+        "landmark": ((B, n_c, r), torch.float32),
+        "res_ptr": ((B, G, H, n_c + 1), torch.int32),
+        "res_idx": ((B, G, H, max(d.n_res, 0)), torch.int32),
+        "res_val": ((B, G, H, max(d.n_res, 0), dh), TORCH_DT[d.resid]),
+    }
+    if d.coeff == L.I8:
+        shapes["coeff_scale"] = ((B, r), torch.float16)
+    if d.resid == L.I8:
+        shapes["res_scale"] = ((B, G, H, dh), torch.float16)
+    return shapes
+
+
+def alloc_cache(d: L.Dims, device="cuda") -> dict:
+    return {k: torch.zeros(s, dtype=t, device=device) for k, (s, t) in cache_shapes(d).items()}
+
+
+def cache_struct(d: L.Dims, c: dict) -> L.Cache:
+    s = L.Cache()
+    for k, (shape, dt) in cache_shapes(d).items():
+        setattr(s, k, _ptr(c[k], dt, shape, k).value if c.get(k) is not None else None)
+    return s
+
+
+def model_shapes(d: L.Dims) -> dict:
+    B, G, H, dh, r, F = d.batch, d.layers, d.heads_kv, d.head_dim, d.rank, d.hidden
+    D = G * H * dh
+    return {"basis": (B, D, r), "w1": (B, G, H, F, dh), "b1": (B, G, H, F),
+            "w2": (B, G, H, dh, F), "b2": (B, G, H, dh)}
+
+
+def model_struct(d: L.Dims, m: dict) -> L.Model:
+    s = L.Model()
+    dt = TORCH_DT[d.act]
+    for k, shape in model_shapes(d).items():
+        setattr(s, k, _ptr(m[k], dt, shape, k).value)
+    return s
+
+
+# ---------------------------------------------------------------------------
+def compress(d: L.Dims, model: dict, k, v, cache: dict, ws=None, stream=None):
+    dt = TORCH_DT[d.act]
+    kv_shape = (d.batch, d.layers, d.heads_kv, d.n_ctx, d.head_dim)
+    ws = workspace(d, L.OP_COMPRESS, k.device) if ws is None else ws
+    L.check(L.lib().lowram_compress(ctypes.byref(d), ctypes.byref(model_struct(d, model)),
+                                    _ptr(k, dt, kv_shape, "k"), _ptr(v, dt, kv_shape, "v"),
+                                    ctypes.byref(cache_struct(d, cache)), _ptr(ws, torch.uint8),
+                                    ws.numel(), _stream(stream)))
+    return cache
+
+
+def _decode_common(d, q, k_tail, v_tail):
+    dt = TORCH_DT[d.act]
+    qp = _ptr(q, dt, (d.batch, d.heads_q, d.head_dim), "q")
+    tail_shape = (d.batch, d.layers, d.heads_kv, d.n_tail, d.head_dim)
+    kt = _ptr(k_tail, dt, tail_shape, "k_tail") if d.n_tail else None
+    vt = _ptr(v_tail, dt, tail_shape, "v_tail") if d.n_tail else None
+    return qp, kt, vt
+
+
+def decode_attn(d: L.Dims, layer: int, model: dict, cache: dict, q, k_tail, v_tail, out=None,
+                sel_out=None, ws=None, stream=None):
+    qp, kt, vt = _decode_common(d, q, k_tail, v_tail)
+    out = torch.empty_like(q) if out is None else out
+    ws = workspace(d, L.OP_DECODE, q.device) if ws is None else ws
+    sp = _ptr(sel_out, torch.int32, (d.batch, d.heads_kv, k_eff(d)), "sel_out")
+    L.check(L.lib().lowram_decode_attn(ctypes.byref(d), layer, ctypes.byref(model_struct(d, model)),
+                                       ctypes.byref(cache_struct(d, cache)), qp, kt, vt,
+                                       _ptr(out, TORCH_DT[d.act], tuple(q.shape), "out"), sp,
+                                       _ptr(ws, torch.uint8), ws.numel(), _stream(stream)))
+    return out
+
+
+class DecodeCall:
+    """Pre-marshalled arguments of one decode call, for tight loops and timing:
+    the three stages can be issued separately on the current stream."""
+
+    def __init__(self, d, layer, model, cache, q, k_tail, v_tail, out, ws, sel_out=None):
+        self.d = d
+        self.layer = layer
+        self.qp, self.kt, self.vt = _decode_common(d, q, k_tail, v_tail)
+        self.mp = model_struct(d, model)
+        self.cp = cache_struct(d, cache)
+        self.op = _ptr(out, TORCH_DT[d.act], tuple(q.shape), "out")
+        self.sp = _ptr(sel_out, torch.int32, (d.batch, d.heads_kv, k_eff(d)), "sel_out")
+        self.wp = _ptr(ws, torch.uint8)
+        self.wn = ws.numel()
+        self._keep = (q, k_tail, v_tail, out, ws, sel_out, model, cache)
+
+    def select(self, stream=None):
+        L.check(L.lib().lowram_decode_select(ctypes.byref(self.d), self.layer, ctypes.byref(self.mp),
+                                             ctypes.byref(self.cp), self.qp, self.sp, self.wp, self.wn,
+                                             _stream(stream)))
+
+    def attend(self, stream=None):
+        L.check(L.lib().lowram_decode_attend(ctypes.byref(self.d), self.layer, ctypes.byref(self.mp),
+                                             ctypes.byref(self.cp), self.qp, self.kt, self.vt, self.wp,
+                                             self.wn, _stream(stream)))
+
+    def combine(self, stream=None):
+        L.check(L.lib().lowram_decode_combine(ctypes.byref(self.d), self.layer, ctypes.byref(self.mp),
+                                              self.op, self.wp, self.wn, _stream(stream)))
+
+    def __call__(self, stream=None):
+        L.check(L.lib().lowram_decode_attn(ctypes.byref(self.d), self.layer, ctypes.byref(self.mp),
+                                           ctypes.byref(self.cp), self.qp, self.kt, self.vt, self.op,
+                                           self.sp, self.wp, self.wn, _stream(stream)))
+
+
+def evict(d: L.Dims, model: dict, src: dict, obs_q, keep: int, dst=None, keep_out=None, ws=None,
+          stream=None):
+    """Returns (dst cache, dims of the evicted cache, keep indices)."""
+    dt = TORCH_DT[d.act]
+    n_obs = 0 if obs_q is None else obs_q.shape[0]
+    d2 = with_(d, n_ctx=keep * d.chunk)
+    dev = src["coeff"].device
+    if dst is None:
+        dst = alloc_cache(d2, dev)
+        if d.coeff == L.I8:
+            dst["coeff_scale"] = src["coeff_scale"]
+        if d.resid == L.I8:
+            dst["res_scale"] = src["res_scale"]
+    keep_out = torch.empty((d.batch, keep), dtype=torch.int32, device=dev) if keep_out is None else keep_out
+    ws = workspace(d, L.OP_EVICT, dev) if ws is None else ws
+    qp = _ptr(obs_q, dt, (n_obs, d.batch, d.layers, d.heads_q, d.head_dim), "obs_q") if n_obs else None
+    L.check(L.lib().lowram_evict(ctypes.byref(d), ctypes.byref(model_struct(d, model)),
+                                 ctypes.byref(cache_struct(d, src)), qp, n_obs, keep,
+                                 ctypes.byref(cache_struct(d2, dst)),
+                                 _ptr(keep_out, torch.int32, (d.batch, keep), "keep_out"),
+                                 _ptr(ws, torch.uint8), ws.numel(), _stream(stream)))
+    return dst, d2, keep_out
+
+
+def dense_workspace(d: L.Dims, n_tokens: int, device="cuda") -> torch.Tensor:
+    return workspace(with_(d, n_ctx=n_tokens), L.OP_DENSE, device)
+
+
+def dense_decode_attn(d: L.Dims, q, k_all, v_all, layer: int, out=None, ws=None, stream=None):
+    """Uncompressed decode attention at `layer` over a dense cache k_all / v_all
+    of shape [B][G][Hkv][n][dh] (n tokens per sequence)."""
+    dt = TORCH_DT[d.act]
+    B, G, H, n, dh = k_all.shape
+    if (B, H, dh) != (d.batch, d.heads_kv, d.head_dim) or not 0 <= layer < G:
+        raise ValueError("dense cache shape does not match dims / layer")
+    for name, t in (("k_all", k_all), ("v_all", v_all)):
+        _ptr(t, dt, (B, G, H, n, dh), name)
+    off = layer * H * n * dh * k_all.element_size()
+    out = torch.empty_like(q) if out is None else out
+    ws = dense_workspace(d, n, q.device) if ws is None else ws
+    L.check(L.lib().lowram_dense_decode_attn(ctypes.byref(d), _ptr(q, dt, (B, d.heads_q, dh), "q"),
+                                             ctypes.c_void_p(k_all.data_ptr() + off),
+                                             ctypes.c_void_p(v_all.data_ptr() + off), n, G * H * n * dh,
+                                             _ptr(out, dt, tuple(q.shape), "out"),
+                                             _ptr(ws, torch.uint8), ws.numel(), _stream(stream)))
+    return out

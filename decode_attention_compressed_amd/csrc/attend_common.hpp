@@ -1,0 +1,96 @@
+// Pieces shared by the two rebuild-and-attend kernels: loaders, the online
+// softmax tile update, the uncompressed tail split and the partial writer.
+#pragma once
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace lowram {
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+template <typename T> __device__ __forceinline__ float ldf(const T *p, long i) { return to_f32(p[i]); }
+__device__ __forceinline__ float ld_coeff(const float *c, long i, const uint16_t *, int) { return c[i]; }
+__device__ __forceinline__ float ld_coeff(const bf16 *c, long i, const uint16_t *, int) { return to_f32(c[i]); }
+__device__ __forceinline__ float ld_coeff(const int8_t *c, long i, const uint16_t *sc, int ch) {
+  return (float)c[i] * f16_bits_to_f32(sc[ch]);
+}
+
+// ---------------------------------------------------------------------------
+// Online-softmax update of one tile: lg[gi*ld + t] holds scaled logits (log2
+// units) for t < nt; replaced by p = 2^(lg - m_new).  Updates m, l and writes
+// the rescale factor alpha = 2^(m_old - m_new).  Whole block calls; each wave
+// owns query heads gi = wave, wave + 4, ...
+// ---------------------------------------------------------------------------
+__device__ inline void softmax_tile(float *lg, int ld, int nt, int g, float *ms, float *ls,
+                                    float *al) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  for (int gi = wave; gi < g; gi += 256 / WAVE) {
+    float mx = -INFINITY;
+    for (int t = lane; t < nt; t += WAVE) mx = fmaxf(mx, lg[gi * ld + t]);
+    mx = wave_max(mx);
+    const float m_old = ms[gi];
+    const float m_new = fmaxf(m_old, mx);
+    float sum = 0.f;
+    for (int t = lane; t < nt; t += WAVE) {
+      const float p = exp2f(lg[gi * ld + t] - m_new);
+      lg[gi * ld + t] = p;
+      sum += p;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) {
+      const float alpha = (m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new);
+      al[gi] = alpha;
+      ls[gi] = ls[gi] * alpha + sum;
+      ms[gi] = m_new;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Uncompressed tail of one (b, h): dense softmax over T tokens (shared by the
+// VALU and MFMA kernels).  smem: qs[g][dh] floats already loaded; lg scratch
+// [g][TT]; accV [g][dh]; ms/ls/al [g].
+// ---------------------------------------------------------------------------
+template <typename TA>
+__device__ void tail_split(const AttendArgs &a, const float *qs, float *lg, int TT, float *accV,
+                           float *ms, float *ls, float *al) {
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int g = a.g, dh = a.dh;
+  const long base = ((((long)b * a.G + a.layer) * a.Hkv + h) * a.T) * dh;
+  const TA *kt = reinterpret_cast<const TA *>(a.k_tail) + base;
+  const TA *vt = reinterpret_cast<const TA *>(a.v_tail) + base;
+  for (int t0 = 0; t0 < a.T; t0 += TT) {
+    const int nt = min(TT, a.T - t0);
+    for (int idx = tid; idx < g * nt; idx += 256) {
+      const int gi = idx / nt, t = idx % nt;
+      const TA *kr = kt + (long)(t0 + t) * dh;
+      float s = 0.f;
+      for (int d = 0; d < dh; ++d) s = fmaf(qs[gi * dh + d], ldf(kr, d), s);
+      lg[gi * TT + t] = s * a.scale_log2;
+    }
+    __syncthreads();
+    softmax_tile(lg, TT, nt, g, ms, ls, al);
+    __syncthreads();
+    for (int idx = tid; idx < g * dh; idx += 256) {
+      const int gi = idx / dh, d = idx % dh;
+      float acc = accV[idx] * al[gi];
+      for (int t = 0; t < nt; ++t) acc = fmaf(lg[gi * TT + t], ldf(vt, (long)(t0 + t) * dh + d), acc);
+      accV[idx] = acc;
+    }
+    __syncthreads();
+  }
+}
+
+__device__ inline void write_partial(const AttendArgs &a, int split, const float *ms,
+                                     const float *ls, const float *accH, const float *accV) {
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  float *p = a.part + (((long)b * a.Hkv + h) * (a.n_split + 1) + split) * a.g * a.PW;
+  for (int gi = 0; gi < a.g; ++gi) {
+    float *pg = p + (long)gi * a.PW;
+    if (tid == 0) { pg[0] = ms[gi]; pg[1] = ls[gi]; pg[2] = 0.f; pg[3] = 0.f; }
+    for (int f = tid; f < a.F; f += 256) pg[4 + f] = accH ? accH[gi * a.F + f] : 0.f;
+    for (int d = tid; d < a.dh; d += 256) pg[4 + a.F + d] = accV[gi * a.dh + d];
+  }
+}
+
+}  // namespace lowram

@@ -1,0 +1,91 @@
+// Internal declarations shared by the host layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lowram.h"
+
+namespace lowram {
+
+// Kernel-side view of one decode call (device pointers, sizes).
+struct AttendArgs {
+  const void *q;          // [B][Hq][dh] act
+  const void *basis;      // [B][D][r] act
+  const void *w1, *b1;    // [B][G][Hkv][F][dh], [B][G][Hkv][F] act
+  const void *coeff;      // [B][N][r] coeff
+  const uint16_t *coeff_scale;  // [B][r] f16 or null
+  const int32_t *res_ptr;       // [B][G][Hkv][n_c+1]
+  const int32_t *res_idx;       // [B][G][Hkv][n_res]
+  const void *res_val;          // [B][G][Hkv][n_res][dh] resid
+  const uint16_t *res_scale;    // [B][G][Hkv][dh] f16 or null
+  const void *k_tail, *v_tail;  // [B][G][Hkv][T][dh] act
+  const int32_t *sel;           // [B][Hkv][k_eff]
+  float *part;                  // [B][Hkv][n_split+1][g][PW]
+  int B, G, Hq, Hkv, dh, r, F, N, C, T, k_eff, n_res, layer;
+  int g, cps, n_split, PW;
+  float scale_log2;             // log2(e) / sqrt(dh)
+};
+
+struct CombineArgs {
+  const float *part;    // [B][Hkv][n_total][g][PW]
+  const void *w2, *b2;  // [B][G][Hkv][dh][F], [B][G][Hkv][dh] act (null when F == 0)
+  void *out;            // [B][Hq][dh] act
+  int B, G, Hq, Hkv, dh, F, layer, g, n_comp, n_total, PW;
+};
+
+// launchers (return hipSuccess or the launch error)
+// sel (if k_eff > 0) receives the selection; sel_out (optional) a copy of it;
+// scores (optional) the float64 chunk scores [B][Hkv][n_c].
+hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
+                         const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
+                         int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
+                         double *scores, hipStream_t st);
+hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st);
+hipError_t launch_combine(int act, const CombineArgs &a, hipStream_t st);
+hipError_t launch_dense(int act, const void *q, const void *k, const void *v, long batch_stride,
+                        int B, int Hq, int Hkv, int dh, int n, int tps, int n_split, float *part,
+                        int PW, hipStream_t st);
+
+struct CompressArgs {
+  const void *k, *v;            // [B][G][Hkv][N][dh] act
+  const void *basis, *w1, *b1, *w2, *b2;
+  void *coeff;                  // [B][N][r] coeff
+  uint16_t *coeff_scale;        // [B][r]
+  float *landmark;              // [B][n_c][r]
+  int32_t *res_ptr, *res_idx;
+  void *res_val;
+  uint16_t *res_scale;
+  double *c64;                  // workspace [B][N][r] (int8 coefficients only)
+  double *err;                  // workspace [B][G][Hkv][N]
+  double *d64;                  // workspace [B][G][Hkv][n_res][dh] (int8 residuals only)
+  int B, G, Hq, Hkv, dh, r, F, N, C, n_res, act, coeff_dt, resid_dt;
+};
+hipError_t run_compress(const CompressArgs &a, hipStream_t st);
+
+struct EvictArgs {
+  const void *basis;
+  const void *obs_q;            // [n_obs][B][G][Hq][dh]
+  int n_obs, keep;
+  const void *coeff; const float *landmark;
+  const int32_t *res_ptr, *res_idx; const void *res_val;
+  void *d_coeff; float *d_landmark; int32_t *d_res_ptr, *d_res_idx; void *d_res_val;
+  int32_t *keep_out;            // [B][keep]
+  double *scores;               // workspace [B][Hkv][n_c]
+  double *acc;                  // workspace [B][n_c]
+  int B, G, Hq, Hkv, dh, r, N, C, n_res, act, coeff_dt, resid_dt;
+};
+hipError_t run_evict(const EvictArgs &a, hipStream_t st);
+
+// Kernels with more than 64 KiB of dynamic LDS declare it once per instantiation.
+template <typename K>
+inline void allow_dynamic_lds(K kernel, size_t bytes) {
+  if (bytes > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+inline int dtype_bytes(int dt) {
+  return dt == LOWRAM_F32 ? 4 : (dt == LOWRAM_I8 ? 1 : 2);
+}
+
+}  // namespace lowram

@@ -1,0 +1,511 @@
+// Compress-side kernels for gfx950 (run once per context, before decoding):
+//   k_project     c_t = U^T k_t^cat in float64, rounded once to the storage type
+//   k_colmax      per-channel max |x| -> fp16 scale = fp16(max / 127)
+//   k_quant       q = clamp(rne(x / s), -127, 127)
+//   k_landmark    mean dequantised coefficient of each chunk, float64 -> float32
+//   k_pred        float64 predictor: k_hat = U_{l,h} c~, v_hat = W2 SiLU(W1 k_hat + b1) + b2,
+//                 emitting either e_t = ||v_t - v_hat_t||^2 or delta = v - v_hat
+//   k_err_topk    residual set: top n_res tokens by (e desc, t asc), ascending,
+//                 with chunk CSR pointers
+//   eviction      group score accumulation, top chunks, compaction
+//
+// Keys of a layer group are stored as per-token coefficients on a shared basis
+// (zicq.com English summary, "Cross-Layer Low-Rank Key Compression"); values
+// are predicted from keys and only the worst-reconstructed tokens keep their
+// residual (same page, "Core Mechanism"; abstract of arXiv 2611.07025).  The
+// ranking key is computed in float64 so that the chosen set does not depend
+// on summation order.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace lowram {
+
+__device__ __forceinline__ double ldd(const float *p, long i) { return (double)p[i]; }
+__device__ __forceinline__ double ldd(const bf16 *p, long i) { return to_f64(p[i]); }
+__device__ __forceinline__ double ld_cdeq(const float *c, long i, const uint16_t *, int) { return (double)c[i]; }
+__device__ __forceinline__ double ld_cdeq(const bf16 *c, long i, const uint16_t *, int) { return to_f64(c[i]); }
+__device__ __forceinline__ double ld_cdeq(const int8_t *c, long i, const uint16_t *sc, int ch) {
+  return (double)c[i] * (double)f16_bits_to_f32(sc[ch]);
+}
+__device__ __forceinline__ void st_round(float *p, double x) { *p = (float)x; }
+__device__ __forceinline__ void st_round(bf16 *p, double x) { p->u = f64_to_bf16_bits(x); }
+__device__ __forceinline__ void st_round(double *p, double x) { *p = x; }
+
+// ---------------------------------------------------------------------------
+// C1: out[b][t][i] = sum_kk K(b, t, kk) U[b][kk][i], float64 accumulate.
+// K(b, t, kk) = k[b][l][h][t][d] with kk = (l*Hkv + h)*dh + d.
+// grid (ceil(r/64), ceil(N/64), B), 256 threads, 4x4 outputs per thread.
+// ---------------------------------------------------------------------------
+template <typename TA, typename TO>
+__global__ __launch_bounds__(256) void k_project(const TA *__restrict__ k, const TA *__restrict__ U,
+                                                 TO *__restrict__ out, int N, int D, int dh, int r) {
+  __shared__ double As[16][64 + 1];
+  __shared__ double Bs[16][64];
+  const int b = blockIdx.z, t0 = blockIdx.y * 64, i0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  const TA *kb = k + (long)b * D * N;  // [G*Hkv][N][dh] blocks
+  const TA *Ub = U + (long)b * D * r;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < D; k0 += 16) {
+    for (int idx = tid; idx < 16 * 64; idx += 256) {
+      const int kk = idx % 16, t = idx / 16;  // consecutive threads walk d (contiguous)
+      const int gk = k0 + kk, tt = t0 + t;
+      As[kk][t] = (tt < N && gk < D) ? ldd(kb, (long)(gk / dh) * N * dh + (long)tt * dh + gk % dh) : 0.0;
+    }
+    for (int idx = tid; idx < 16 * 64; idx += 256) {
+      const int kk = idx / 64, i = idx % 64;
+      const int gk = k0 + kk, ii = i0 + i;
+      Bs[kk][i] = (gk < D && ii < r) ? ldd(Ub, (long)gk * r + ii) : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) av[a] = As[kk][ty + 16 * a];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bv[c] = Bs[kk][tx + 16 * c];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int tt = t0 + ty + 16 * a;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ii = i0 + tx + 16 * c;
+      if (tt < N && ii < r) st_round(out + ((long)b * N + tt) * r + ii, acc[a][c]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-channel fp16 scale over rows: x[batch][rows][cols] -> s[batch][cols].
+// grid (ceil(cols/64), batch), 256 threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_colmax(const double *__restrict__ x, uint16_t *__restrict__ s,
+                                                int rows, int cols) {
+  __shared__ double red[4][64];
+  const int bt = blockIdx.y, c = blockIdx.x * 64 + threadIdx.x % 64, rg = threadIdx.x / 64;
+  double m = 0.0;
+  if (c < cols)
+    for (int t = rg; t < rows; t += 4) m = fmax(m, fabs(x[((long)bt * rows + t) * cols + c]));
+  red[rg][threadIdx.x % 64] = m;
+  __syncthreads();
+  if (rg == 0 && c < cols) {
+    const double mx = fmax(fmax(red[0][threadIdx.x], red[1][threadIdx.x]),
+                           fmax(red[2][threadIdx.x], red[3][threadIdx.x]));
+    s[(long)bt * cols + c] = f64_to_f16_bits(mx / 127.0);
+  }
+}
+
+// q = clamp(rne(x / s), -127, 127); zero where the scale is zero.
+__global__ __launch_bounds__(256) void k_quant(const double *__restrict__ x,
+                                               const uint16_t *__restrict__ s,
+                                               int8_t *__restrict__ q, long rows, int cols,
+                                               long total) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long bt = i / (rows * cols);
+  const int c = (int)(i % cols);
+  const double sc = (double)f16_bits_to_f32(s[bt * cols + c]);
+  double v = 0.0;
+  if (sc > 0.0) v = fmin(127.0, fmax(-127.0, rint(x[i] / sc)));
+  q[i] = (int8_t)v;
+}
+
+// C2: landmark[b][j][i] = float32(mean_t deq(coeff[b][jC + t][i])).  grid (n_c, B).
+template <typename TC>
+__global__ __launch_bounds__(256) void k_landmark(const TC *__restrict__ coeff,
+                                                  const uint16_t *__restrict__ cscale,
+                                                  float *__restrict__ lm, int N, int C, int r) {
+  const int j = blockIdx.x, b = blockIdx.y;
+  const TC *cb = coeff + ((long)b * N + (long)j * C) * r;
+  const uint16_t *sc = cscale ? cscale + (long)b * r : nullptr;
+  for (int i = threadIdx.x; i < r; i += 256) {
+    double s = 0.0;
+    for (int t = 0; t < C; ++t) s += ld_cdeq(cb, (long)t * r + i, sc, i);
+    lm[((long)b * (N / C) + j) * r + i] = (float)(s / (double)C);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// C3 / C5: float64 predictor over a tile of TM rows of one (b, l, h).
+// MODE 0: rows are tokens t, writes err[b][l][h][t] = ||v_t - v_hat_t||^2.
+// MODE 1: rows are residual entries e, token res_idx[e]; writes delta rows
+//         (rounded to TD) to dout[b][l][h][e][:].
+// grid (ceil(rows/TM), G*Hkv, B), 256 threads (16 x 16).
+// ---------------------------------------------------------------------------
+template <int DH, int TM, int MODE, typename TA, typename TC, typename TD>
+__global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
+                                              const uint16_t *__restrict__ cscale,
+                                              const TA *__restrict__ basis, const TA *__restrict__ w1,
+                                              const TA *__restrict__ b1, const TA *__restrict__ w2,
+                                              const TA *__restrict__ b2, const TA *__restrict__ v,
+                                              const int32_t *__restrict__ res_idx,
+                                              double *__restrict__ err, TD *__restrict__ dout,
+                                              int Hkv, int N, int r, int F, int n_rows, int n_res) {
+  constexpr int NA = TM / 16, NC = DH / 16;
+  constexpr int KS = DH + 1, HS = 64 + 1;
+  extern __shared__ __align__(16) double psm[];
+  double *Ks = psm;              // [TM][DH+1]
+  double *Hs = Ks + TM * KS;     // [TM][65]
+  double *As = Hs + TM * HS;     // [16][TM]   (GEMM1 A slab)
+  double *Bs = As + 16 * TM;     // [16][DH]   (B slabs: U, W1 block, W2 block)
+  __shared__ int tok[TM];
+  const int lh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  const int l = lh / Hkv, h = lh % Hkv;
+  const int G = gridDim.y / Hkv;
+  const long bh = ((long)b * G + l) * Hkv + h;
+  const int row0 = blockIdx.x * TM;
+  const int D = G * Hkv * DH;
+  const TA *Ul = basis + ((long)b * D + (long)lh * DH) * r;
+  const TA *W1 = w1 + bh * F * DH;
+  const TA *B1 = b1 + bh * F;
+  const TA *W2 = w2 + bh * DH * F;
+  const TA *B2 = b2 + bh * DH;
+  const TA *V = v + bh * N * DH;
+  const TC *cb = coeff + (long)b * N * r;
+  const uint16_t *sc = cscale ? cscale + (long)b * r : nullptr;
+  for (int i = tid; i < TM; i += 256) {
+    const int rr = row0 + i;
+    int t = -1;
+    if (rr < n_rows) t = MODE == 0 ? rr : res_idx[bh * n_res + rr];
+    tok[i] = t;
+  }
+  __syncthreads();
+
+  // GEMM1: k_hat[TM][DH] = deq(c)[TM][r] . U_{l,h}^T
+  double acc[NA][NC] = {};
+  for (int k0 = 0; k0 < r; k0 += 16) {
+    for (int idx = tid; idx < 16 * TM; idx += 256) {
+      const int kk = idx % 16, m = idx / 16;
+      const int t = tok[m];
+      As[kk * TM + m] = t >= 0 ? ld_cdeq(cb, (long)t * r + k0 + kk, sc, k0 + kk) : 0.0;
+    }
+    for (int idx = tid; idx < 16 * DH; idx += 256) {
+      const int kk = idx % 16, d = idx / 16;
+      Bs[kk * DH + d] = ldd(Ul, (long)d * r + k0 + kk);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < 16; ++kk) {
+      double av[NA], bv[NC];
+#pragma unroll
+      for (int a = 0; a < NA; ++a) av[a] = As[kk * TM + ty + 16 * a];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) bv[c] = Bs[kk * DH + tx + 16 * c];
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) Ks[(ty + 16 * a) * KS + tx + 16 * c] = acc[a][c];
+  __syncthreads();
+
+  // GEMM2 + SiLU per 64-wide hidden block, GEMM3 accumulated: v_hat = H . W2^T
+  double vacc[NA][NC] = {};
+  for (int f0 = 0; f0 < F; f0 += 64) {
+    double hacc[NA][4] = {};
+    for (int k0 = 0; k0 < DH; k0 += 16) {
+      for (int idx = tid; idx < 16 * 64; idx += 256) {
+        const int kk = idx % 16, f = idx / 16;
+        Bs[kk * 64 + f] = ldd(W1, (long)(f0 + f) * DH + k0 + kk);
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int kk = 0; kk < 16; ++kk) {
+        double av[NA], bv[4];
+#pragma unroll
+        for (int a = 0; a < NA; ++a) av[a] = Ks[(ty + 16 * a) * KS + k0 + kk];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bv[c] = Bs[kk * 64 + tx + 16 * c];
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) hacc[a][c] = fma(av[a], bv[c], hacc[a][c]);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double x = hacc[a][c] + ldd(B1, f0 + tx + 16 * c);
+        Hs[(ty + 16 * a) * HS + tx + 16 * c] = x / (1.0 + exp(-x));
+      }
+    __syncthreads();
+    for (int k0 = 0; k0 < 64; k0 += 16) {
+      for (int idx = tid; idx < 16 * DH; idx += 256) {
+        const int kk = idx % 16, d = idx / 16;
+        Bs[kk * DH + d] = ldd(W2, (long)d * F + f0 + k0 + kk);
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int kk = 0; kk < 16; ++kk) {
+        double av[NA], bv[NC];
+#pragma unroll
+        for (int a = 0; a < NA; ++a) av[a] = Hs[(ty + 16 * a) * HS + k0 + kk];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) bv[c] = Bs[kk * DH + tx + 16 * c];
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) vacc[a][c] = fma(av[a], bv[c], vacc[a][c]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // epilogue
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const int m = ty + 16 * a;
+    const int t = tok[m];
+    if (MODE == 0) {
+      double e = 0.0;
+      if (t >= 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int d = tx + 16 * c;
+          const double dv = ldd(V, (long)t * DH + d) - (vacc[a][c] + ldd(B2, d));
+          e = fma(dv, dv, e);
+        }
+      }
+      // sum over the 16 threads of this row (lanes tx = 0..15 of one wave quarter)
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) e += __shfl_xor(e, o, WAVE);
+      if (tx == 0 && t >= 0) err[bh * N + t] = e;
+    } else if (t >= 0) {
+      const int rr = row0 + m;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int d = tx + 16 * c;
+        const double dv = ldd(V, (long)t * DH + d) - (vacc[a][c] + ldd(B2, d));
+        st_round(dout + (bh * n_res + rr) * DH + d, dv);
+      }
+    }
+  }
+}
+
+// C4: residual set and CSR pointers per (b, l, h).  grid (G*Hkv, B), 1024 threads.
+__global__ __launch_bounds__(1024) void k_err_topk(const double *__restrict__ err, int N, int C,
+                                                   int n_res, int32_t *__restrict__ res_idx,
+                                                   int32_t *__restrict__ res_ptr) {
+  __shared__ TopkSmem tk;
+  const long bh = (long)blockIdx.y * gridDim.x + blockIdx.x;
+  const double *e = err + bh * N;
+  block_topk<1024>([&](int i) { return f64_order_key(e[i]); }, N, n_res, res_idx + bh * n_res, tk,
+                   C, res_ptr + bh * (N / C + 1));
+}
+
+// ---------------------------------------------------------------------------
+// eviction
+// ---------------------------------------------------------------------------
+// acc[b][j] += sum_h s[b][h][j], heads in ascending order (so over all calls
+// acc = sum over w, then l, then h, in that order).  grid (ceil(n_c/256), B).
+__global__ __launch_bounds__(256) void k_evict_accum(const double *__restrict__ s, double *__restrict__ acc,
+                                                     int Hkv, int n_c, int first) {
+  const int j = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
+  if (j >= n_c) return;
+  double v = first ? 0.0 : acc[(long)b * n_c + j];
+  for (int h = 0; h < Hkv; ++h) v += s[((long)b * Hkv + h) * n_c + j];
+  acc[(long)b * n_c + j] = v;
+}
+
+// keep the top `keep` chunks by accumulated score.  grid (B), 1024 threads.
+__global__ __launch_bounds__(1024) void k_evict_select(const double *__restrict__ acc, int n_c,
+                                                       int keep, int32_t *__restrict__ keep_idx) {
+  __shared__ TopkSmem tk;
+  const int b = blockIdx.x;
+  const double *ab = acc + (long)b * n_c;
+  block_topk<1024>([&](int i) { return f64_order_key(ab[i]); }, n_c, keep,
+                   keep_idx + (long)b * keep, tk, 0, nullptr);
+}
+
+// copy the kept chunks' coefficient rows and landmarks.  grid (keep, B).
+__global__ __launch_bounds__(256) void k_evict_copy(const unsigned char *__restrict__ coeff,
+                                                    const float *__restrict__ lm,
+                                                    const int32_t *__restrict__ keep_idx,
+                                                    unsigned char *__restrict__ d_coeff,
+                                                    float *__restrict__ d_lm, int keep, int n_c,
+                                                    long chunk_bytes, int r) {
+  const int jn = blockIdx.x, b = blockIdx.y;
+  const int jo = keep_idx[(long)b * keep + jn];
+  const uint4 *src = reinterpret_cast<const uint4 *>(coeff + ((long)b * n_c + jo) * chunk_bytes);
+  uint4 *dst = reinterpret_cast<uint4 *>(d_coeff + ((long)b * keep + jn) * chunk_bytes);
+  for (long i = threadIdx.x; i < chunk_bytes / 16; i += 256) dst[i] = src[i];
+  for (int i = threadIdx.x; i < r; i += 256)
+    d_lm[((long)b * keep + jn) * r + i] = lm[((long)b * n_c + jo) * r + i];
+}
+
+// rebuild the residual CSR of the kept chunks.  grid (G*Hkv, B), 256 threads.
+__global__ __launch_bounds__(256) void k_evict_resid(const int32_t *__restrict__ ptr,
+                                                     const int32_t *__restrict__ idx,
+                                                     const unsigned char *__restrict__ val,
+                                                     const int32_t *__restrict__ keep_idx,
+                                                     int32_t *__restrict__ d_ptr,
+                                                     int32_t *__restrict__ d_idx,
+                                                     unsigned char *__restrict__ d_val, int n_c,
+                                                     int keep, int C, int n_res, int row_bytes) {
+  __shared__ int32_t part[257];
+  const long bh = (long)blockIdx.y * gridDim.x + blockIdx.x;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int32_t *p = ptr + bh * (n_c + 1);
+  const int32_t *kp = keep_idx + (long)b * keep;
+  int32_t *dp = d_ptr + bh * (keep + 1);
+  // each thread sums a contiguous run of kept chunks, then a serial scan of the runs
+  const int per = (keep + 255) / 256;
+  const int j0 = min(keep, tid * per), j1 = min(keep, j0 + per);
+  int32_t s = 0;
+  for (int jn = j0; jn < j1; ++jn) s += p[kp[jn] + 1] - p[kp[jn]];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int i = 0; i < 256; ++i) { const int32_t c = part[i]; part[i] = run; run += c; }
+    part[256] = run;
+  }
+  __syncthreads();
+  int32_t run = part[tid];
+  for (int jn = j0; jn < j1; ++jn) {
+    dp[jn] = run;
+    const int jo = kp[jn];
+    for (int e = p[jo]; e < p[jo + 1]; ++e, ++run) {
+      d_idx[bh * n_res + run] = idx[bh * n_res + e] - jo * C + jn * C;
+      const unsigned char *sr = val + (bh * n_res + e) * (long)row_bytes;
+      unsigned char *dr = d_val + (bh * n_res + run) * (long)row_bytes;
+      for (int i = 0; i < row_bytes; i += 16)
+        *reinterpret_cast<uint4 *>(dr + i) = *reinterpret_cast<const uint4 *>(sr + i);
+    }
+  }
+  if (tid == 0) dp[keep] = part[256];
+}
+
+// ---------------------------------------------------------------------------
+// host sequencing
+// ---------------------------------------------------------------------------
+template <int DH, int TM, int MODE, typename TA, typename TC, typename TD>
+static void launch_pred(const CompressArgs &a, int n_rows, TD *dout, hipStream_t st) {
+  const size_t smem = sizeof(double) * ((size_t)TM * (DH + 1) + (size_t)TM * 65 + 16 * TM + 16 * DH);
+  dim3 grid((n_rows + TM - 1) / TM, a.G * a.Hkv, a.B);
+  static const bool lds_ok = (allow_dynamic_lds(k_pred<DH, TM, MODE, TA, TC, TD>, smem), true);
+  (void)lds_ok;
+  hipLaunchKernelGGL((k_pred<DH, TM, MODE, TA, TC, TD>), grid, dim3(256), smem, st,
+                     (const TC *)a.coeff, a.coeff_scale, (const TA *)a.basis, (const TA *)a.w1,
+                     (const TA *)a.b1, (const TA *)a.w2, (const TA *)a.b2, (const TA *)a.v,
+                     a.res_idx, a.err, dout, a.Hkv, a.N, a.r, a.F, n_rows, a.n_res);
+}
+
+template <int DH, int TM, typename TA, typename TC, typename TR>
+static void pred_both(const CompressArgs &a, hipStream_t st) {
+  launch_pred<DH, TM, 0, TA, TC, double>(a, a.N, nullptr, st);
+  hipLaunchKernelGGL(k_err_topk, dim3(a.G * a.Hkv, a.B), dim3(1024), 0, st, a.err, a.N, a.C,
+                     a.n_res, a.res_idx, a.res_ptr);
+  if (a.n_res > 0) {
+    if (a.resid_dt == LOWRAM_I8)
+      launch_pred<DH, TM, 1, TA, TC, double>(a, a.n_res, a.d64, st);
+    else
+      launch_pred<DH, TM, 1, TA, TC, TR>(a, a.n_res, (TR *)a.res_val, st);
+  }
+}
+
+template <typename TA, typename TC, typename TR>
+static void pred_dispatch(const CompressArgs &a, hipStream_t st) {
+  if (a.dh == 64) pred_both<64, 128, TA, TC, TR>(a, st);
+  else if (a.dh == 128) pred_both<128, 64, TA, TC, TR>(a, st);
+  else pred_both<256, 32, TA, TC, TR>(a, st);
+}
+
+hipError_t run_compress(const CompressArgs &a, hipStream_t st) {
+  const int D = a.G * a.Hkv * a.dh, n_c = a.N / a.C;
+  dim3 pgrid((a.r + 63) / 64, (a.N + 63) / 64, a.B);
+  // C1 (+ Q1 for int8 coefficients)
+  if (a.act == LOWRAM_F32) {
+    hipLaunchKernelGGL((k_project<float, float>), pgrid, dim3(256), 0, st, (const float *)a.k,
+                       (const float *)a.basis, (float *)a.coeff, a.N, D, a.dh, a.r);
+  } else if (a.coeff_dt == LOWRAM_BF16) {
+    hipLaunchKernelGGL((k_project<bf16, bf16>), pgrid, dim3(256), 0, st, (const bf16 *)a.k,
+                       (const bf16 *)a.basis, (bf16 *)a.coeff, a.N, D, a.dh, a.r);
+  } else {
+    double *c64 = a.c64;
+    hipLaunchKernelGGL((k_project<bf16, double>), pgrid, dim3(256), 0, st, (const bf16 *)a.k,
+                       (const bf16 *)a.basis, c64, a.N, D, a.dh, a.r);
+    hipLaunchKernelGGL(k_colmax, dim3((a.r + 63) / 64, a.B), dim3(256), 0, st, c64,
+                       a.coeff_scale, a.N, a.r);
+    const long total = (long)a.B * a.N * a.r;
+    hipLaunchKernelGGL(k_quant, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, c64,
+                       a.coeff_scale, (int8_t *)a.coeff, (long)a.N, a.r, total);
+  }
+  // C2
+  if (a.act == LOWRAM_F32)
+    hipLaunchKernelGGL(k_landmark<float>, dim3(n_c, a.B), dim3(256), 0, st, (const float *)a.coeff,
+                       nullptr, a.landmark, a.N, a.C, a.r);
+  else if (a.coeff_dt == LOWRAM_BF16)
+    hipLaunchKernelGGL(k_landmark<bf16>, dim3(n_c, a.B), dim3(256), 0, st, (const bf16 *)a.coeff,
+                       nullptr, a.landmark, a.N, a.C, a.r);
+  else
+    hipLaunchKernelGGL(k_landmark<int8_t>, dim3(n_c, a.B), dim3(256), 0, st,
+                       (const int8_t *)a.coeff, a.coeff_scale, a.landmark, a.N, a.C, a.r);
+  // C3, C4, C5
+  if (a.act == LOWRAM_F32) pred_dispatch<float, float, float>(a, st);
+  else if (a.coeff_dt == LOWRAM_BF16 && a.resid_dt == LOWRAM_BF16) pred_dispatch<bf16, bf16, bf16>(a, st);
+  else if (a.coeff_dt == LOWRAM_I8 && a.resid_dt == LOWRAM_BF16) pred_dispatch<bf16, int8_t, bf16>(a, st);
+  else if (a.coeff_dt == LOWRAM_BF16) pred_dispatch<bf16, bf16, bf16>(a, st);
+  else pred_dispatch<bf16, int8_t, bf16>(a, st);
+  // Q1 on residual rows
+  if (a.resid_dt == LOWRAM_I8 && a.n_res > 0) {
+    const int bl = a.B * a.G * a.Hkv;
+    hipLaunchKernelGGL(k_colmax, dim3((a.dh + 63) / 64, bl), dim3(256), 0, st, a.d64, a.res_scale,
+                       a.n_res, a.dh);
+    const long total = (long)bl * a.n_res * a.dh;
+    hipLaunchKernelGGL(k_quant, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a.d64,
+                       a.res_scale, (int8_t *)a.res_val, (long)a.n_res, a.dh, total);
+  } else if (a.resid_dt == LOWRAM_I8) {
+    const int bl = a.B * a.G * a.Hkv;
+    hipLaunchKernelGGL(k_colmax, dim3((a.dh + 63) / 64, bl), dim3(256), 0, st, a.d64, a.res_scale,
+                       0, a.dh);
+  }
+  return hipGetLastError();
+}
+
+hipError_t run_evict(const EvictArgs &a, hipStream_t st) {
+  const int n_c = a.N / a.C, D = a.G * a.Hkv * a.dh;
+  const int esz = dtype_bytes(a.act);
+  for (int w = 0; w < a.n_obs; ++w)
+    for (int l = 0; l < a.G; ++l) {
+      const unsigned char *qb = reinterpret_cast<const unsigned char *>(a.obs_q) +
+                                ((long)w * a.B * a.G + l) * a.Hq * a.dh * esz;
+      hipError_t e = launch_select(a.act, qb, (long)a.G * a.Hq * a.dh, a.basis, a.landmark, a.B,
+                                   a.Hq, a.Hkv, a.dh, a.r, n_c, D, l, 0, nullptr, nullptr,
+                                   a.scores, st);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_evict_accum, dim3((n_c + 255) / 256, a.B), dim3(256), 0, st, a.scores,
+                         a.acc, a.Hkv, n_c, (w == 0 && l == 0) ? 1 : 0);
+    }
+  if (a.n_obs == 0)
+    hipLaunchKernelGGL(k_evict_accum, dim3((n_c + 255) / 256, a.B), dim3(256), 0, st, a.scores,
+                       a.acc, 0, n_c, 1);
+  hipLaunchKernelGGL(k_evict_select, dim3(a.B), dim3(1024), 0, st, a.acc, n_c, a.keep, a.keep_out);
+  const long chunk_bytes = (long)a.C * a.r * dtype_bytes(a.coeff_dt);
+  hipLaunchKernelGGL(k_evict_copy, dim3(a.keep, a.B), dim3(256), 0, st,
+                     (const unsigned char *)a.coeff, a.landmark, a.keep_out,
+                     (unsigned char *)a.d_coeff, a.d_landmark, a.keep, n_c, chunk_bytes, a.r);
+  hipLaunchKernelGGL(k_evict_resid, dim3(a.G * a.Hkv, a.B), dim3(256), 0, st, a.res_ptr, a.res_idx,
+                     (const unsigned char *)a.res_val, a.keep_out, a.d_res_ptr, a.d_res_idx,
+                     (unsigned char *)a.d_res_val, n_c, a.keep, a.C, a.n_res,
+                     a.dh * dtype_bytes(a.resid_dt));
+  return hipGetLastError();
+}
+
+}  // namespace lowram

@@ -1,0 +1,430 @@
+// Host side of the C ABI: argument validation, workspace plans and launch
+// sequencing on the caller's stream.  Nothing here allocates device memory or
+// synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "internal.hpp"
+
+using namespace lowram;
+
+namespace {
+
+thread_local std::string g_err;
+
+lowram_status fail(lowram_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+lowram_status hip_status(hipError_t e, const char *where) {
+  if (e == hipSuccess) return LOWRAM_OK;
+  return fail(LOWRAM_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t WS_ALIGN = 256;
+size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int n_chunks(const lowram_dims *d) { return d->chunk > 0 ? d->n_ctx / d->chunk : 0; }
+
+lowram_status check_dims(const lowram_dims *d) {
+  if (!d) return fail(LOWRAM_E_INVALID, "dims is NULL");
+  if (d->batch < 1 || d->layers < 1 || d->heads_kv < 1 || d->heads_q < 1)
+    return fail(LOWRAM_E_INVALID, "batch, layers, heads_q and heads_kv must be >= 1");
+  if (d->heads_q % d->heads_kv != 0)
+    return fail(LOWRAM_E_INVALID, "heads_q (%d) must be a multiple of heads_kv (%d)", d->heads_q, d->heads_kv);
+  if (d->heads_q / d->heads_kv > 16)
+    return fail(LOWRAM_E_UNSUPPORTED, "at most 16 query heads per kv head");
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
+    return fail(LOWRAM_E_UNSUPPORTED, "head_dim %d: supported 64, 128, 256", d->head_dim);
+  const long D = (long)d->layers * d->heads_kv * d->head_dim;
+  if (d->rank < 16 || d->rank % 16 != 0 || d->rank > 2048)
+    return fail(LOWRAM_E_UNSUPPORTED, "rank %d: must be a multiple of 16 in [16, 2048]", d->rank);
+  if (d->rank > D) return fail(LOWRAM_E_INVALID, "rank %d exceeds the group key dim %ld", d->rank, D);
+  if (d->hidden < 64 || d->hidden % 64 != 0)
+    return fail(LOWRAM_E_UNSUPPORTED, "hidden %d: must be a positive multiple of 64", d->hidden);
+  if (d->chunk < 1) return fail(LOWRAM_E_INVALID, "chunk must be >= 1");
+  if (d->n_ctx < 0 || d->n_ctx % d->chunk != 0)
+    return fail(LOWRAM_E_INVALID, "n_ctx %d must be a non-negative multiple of chunk %d", d->n_ctx, d->chunk);
+  if (d->n_ctx > (1 << 22)) return fail(LOWRAM_E_UNSUPPORTED, "n_ctx above 4M tokens");
+  if (n_chunks(d) > 8192) return fail(LOWRAM_E_UNSUPPORTED, "more than 8192 chunks");
+  if (d->top_k < 0 || d->n_tail < 0) return fail(LOWRAM_E_INVALID, "top_k and n_tail must be >= 0");
+  if (d->n_res < 0 || d->n_res > d->n_ctx)
+    return fail(LOWRAM_E_INVALID, "n_res %d must lie in [0, n_ctx]", d->n_res);
+  if (d->act == LOWRAM_F32) {
+    if (d->coeff != LOWRAM_F32 || d->resid != LOWRAM_F32)
+      return fail(LOWRAM_E_UNSUPPORTED, "float32 caches store coefficients and residuals in float32");
+  } else if (d->act == LOWRAM_BF16) {
+    if ((d->coeff != LOWRAM_BF16 && d->coeff != LOWRAM_I8) || (d->resid != LOWRAM_BF16 && d->resid != LOWRAM_I8))
+      return fail(LOWRAM_E_UNSUPPORTED, "bfloat16 caches store coefficients/residuals in bf16 or int8");
+  } else {
+    return fail(LOWRAM_E_UNSUPPORTED, "act dtype must be F32 or BF16");
+  }
+  return LOWRAM_OK;
+}
+
+struct DecodePlan {
+  int k_eff, cps, n_split, PW;
+  size_t sel_off, part_off, bytes;
+};
+
+DecodePlan decode_plan(const lowram_dims *d) {
+  DecodePlan p;
+  const int n_c = n_chunks(d);
+  p.k_eff = d->top_k < n_c ? d->top_k : n_c;
+  p.cps = 1;
+  p.n_split = p.k_eff > 0 ? (p.k_eff + p.cps - 1) / p.cps : 0;
+  p.PW = 4 + d->hidden + d->head_dim;
+  const int g = d->heads_q / d->heads_kv;
+  p.sel_off = 0;
+  p.part_off = align_up(sizeof(int32_t) * (size_t)d->batch * d->heads_kv * (p.k_eff > 0 ? p.k_eff : 1));
+  p.bytes = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * (p.n_split + 1) * g * p.PW);
+  return p;
+}
+
+struct CompressPlan {
+  size_t err_off, c64_off, d64_off, bytes;
+};
+
+CompressPlan compress_plan(const lowram_dims *d) {
+  CompressPlan p;
+  const size_t bl = (size_t)d->batch * d->layers * d->heads_kv;
+  p.err_off = 0;
+  p.c64_off = align_up(sizeof(double) * bl * d->n_ctx);
+  p.d64_off = p.c64_off + (d->coeff == LOWRAM_I8 ? align_up(sizeof(double) * (size_t)d->batch * d->n_ctx * d->rank) : 0);
+  p.bytes = p.d64_off + (d->resid == LOWRAM_I8 ? align_up(sizeof(double) * bl * d->n_res * d->head_dim) : 0);
+  return p;
+}
+
+struct EvictPlan {
+  size_t scores_off, acc_off, keep_off, bytes;
+};
+
+EvictPlan evict_plan(const lowram_dims *d) {
+  EvictPlan p;
+  const size_t n_c = (size_t)(n_chunks(d) > 0 ? n_chunks(d) : 1);
+  p.scores_off = 0;
+  p.acc_off = align_up(sizeof(double) * d->batch * d->heads_kv * n_c);
+  p.keep_off = p.acc_off + align_up(sizeof(double) * d->batch * n_c);
+  p.bytes = p.keep_off + align_up(sizeof(int32_t) * d->batch * n_c);
+  return p;
+}
+
+struct DensePlan {
+  int tps, n_split, PW;
+  size_t bytes;
+};
+
+DensePlan dense_plan(const lowram_dims *d, int n_tokens) {
+  DensePlan p;
+  const long work = (long)n_tokens * d->batch * d->heads_kv;
+  long tps = (work + 2047) / 2048;
+  tps = ((tps + 63) / 64) * 64;
+  if (tps < 64) tps = 64;
+  p.tps = (int)tps;
+  p.n_split = n_tokens > 0 ? (int)((n_tokens + tps - 1) / tps) : 1;
+  p.PW = 4 + d->head_dim;
+  p.bytes = align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * p.n_split *
+                     (d->heads_q / d->heads_kv) * p.PW);
+  return p;
+}
+
+// The dense comparator only reads batch, heads, head_dim and act.
+lowram_status check_dense_dims(const lowram_dims *d) {
+  if (!d) return fail(LOWRAM_E_INVALID, "dims is NULL");
+  if (d->batch < 1 || d->heads_kv < 1 || d->heads_q < 1 || d->heads_q % d->heads_kv != 0)
+    return fail(LOWRAM_E_INVALID, "bad batch or head counts");
+  if (d->heads_q / d->heads_kv > 16) return fail(LOWRAM_E_UNSUPPORTED, "at most 16 query heads per kv head");
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
+    return fail(LOWRAM_E_UNSUPPORTED, "head_dim %d: supported 64, 128, 256", d->head_dim);
+  if (d->act != LOWRAM_F32 && d->act != LOWRAM_BF16) return fail(LOWRAM_E_UNSUPPORTED, "act must be F32 or BF16");
+  if (d->n_ctx < 0) return fail(LOWRAM_E_INVALID, "n_ctx must be >= 0");
+  return LOWRAM_OK;
+}
+
+lowram_status check_ws(void *ws, size_t have, size_t need) {
+  if (need > have) return fail(LOWRAM_E_WORKSPACE, "workspace of %zu bytes, %zu needed", have, need);
+  if (need && !ws) return fail(LOWRAM_E_INVALID, "workspace is NULL");
+  if (((uintptr_t)ws & (WS_ALIGN - 1)) != 0) return fail(LOWRAM_E_INVALID, "workspace must be 256-byte aligned");
+  return LOWRAM_OK;
+}
+
+#define REQUIRE_PTR(p)                                                             \
+  do {                                                                             \
+    if (!(p)) return fail(LOWRAM_E_INVALID, "%s is NULL", #p);                     \
+    if (!aligned16(p)) return fail(LOWRAM_E_INVALID, "%s is not 16-byte aligned", #p); \
+  } while (0)
+#define OPTIONAL_PTR(p)                                                            \
+  do {                                                                             \
+    if ((p) && !aligned16(p)) return fail(LOWRAM_E_INVALID, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+lowram_status check_decode_inputs(const lowram_dims *d, int32_t layer, const lowram_model *m,
+                                  const lowram_cache *c, const DecodePlan &p) {
+  if (layer < 0 || layer >= d->layers)
+    return fail(LOWRAM_E_INVALID, "layer %d outside [0, %d)", layer, d->layers);
+  if (p.k_eff == 0 && d->n_tail == 0)
+    return fail(LOWRAM_E_INVALID, "nothing to attend: no chunk selected and no tail");
+  if (!m) return fail(LOWRAM_E_INVALID, "model is NULL");
+  if (p.k_eff > 0) {
+    if (!c) return fail(LOWRAM_E_INVALID, "cache is NULL");
+    REQUIRE_PTR(m->basis); REQUIRE_PTR(m->w1); REQUIRE_PTR(m->b1);
+    REQUIRE_PTR(c->coeff); REQUIRE_PTR(c->landmark); REQUIRE_PTR(c->res_ptr);
+    if (d->n_res > 0) { REQUIRE_PTR(c->res_idx); REQUIRE_PTR(c->res_val); }
+    if (d->coeff == LOWRAM_I8) REQUIRE_PTR(c->coeff_scale);
+    if (d->resid == LOWRAM_I8 && d->n_res > 0) REQUIRE_PTR(c->res_scale);
+  }
+  return LOWRAM_OK;
+}
+
+AttendArgs make_attend(const lowram_dims *d, int32_t layer, const lowram_model *m,
+                       const lowram_cache *c, const void *q, const void *kt, const void *vt,
+                       void *ws, const DecodePlan &p) {
+  AttendArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q; a.k_tail = kt; a.v_tail = vt;
+  if (m) { a.basis = m->basis; a.w1 = m->w1; a.b1 = m->b1; }
+  if (c) {
+    a.coeff = c->coeff; a.coeff_scale = (const uint16_t *)c->coeff_scale;
+    a.res_ptr = c->res_ptr; a.res_idx = c->res_idx; a.res_val = c->res_val;
+    a.res_scale = (const uint16_t *)c->res_scale;
+  }
+  a.sel = reinterpret_cast<const int32_t *>((char *)ws + p.sel_off);
+  a.part = reinterpret_cast<float *>((char *)ws + p.part_off);
+  a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
+  a.r = d->rank; a.F = d->hidden; a.N = d->n_ctx; a.C = d->chunk; a.T = d->n_tail;
+  a.k_eff = p.k_eff; a.n_res = d->n_res; a.layer = layer;
+  a.g = d->heads_q / d->heads_kv; a.cps = p.cps; a.n_split = p.n_split; a.PW = p.PW;
+  a.scale_log2 = 1.4426950408889634f / sqrtf((float)d->head_dim);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lowram_status_string(lowram_status s) {
+  switch (s) {
+    case LOWRAM_OK: return "ok";
+    case LOWRAM_E_INVALID: return "invalid argument";
+    case LOWRAM_E_UNSUPPORTED: return "unsupported";
+    case LOWRAM_E_WORKSPACE: return "workspace too small";
+    case LOWRAM_E_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *lowram_last_error(void) { return g_err.c_str(); }
+
+lowram_status lowram_workspace_bytes(const lowram_dims *d, int32_t op, size_t *bytes) {
+  lowram_status st = op == LOWRAM_OP_DENSE ? check_dense_dims(d) : check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  if (!bytes) return fail(LOWRAM_E_INVALID, "bytes is NULL");
+  switch (op) {
+    case LOWRAM_OP_COMPRESS: *bytes = compress_plan(d).bytes; return LOWRAM_OK;
+    case LOWRAM_OP_DECODE: *bytes = decode_plan(d).bytes; return LOWRAM_OK;
+    case LOWRAM_OP_EVICT: *bytes = evict_plan(d).bytes; return LOWRAM_OK;
+    case LOWRAM_OP_DENSE: *bytes = dense_plan(d, d->n_ctx).bytes; return LOWRAM_OK;
+  }
+  return fail(LOWRAM_E_INVALID, "unknown op %d", op);
+}
+
+lowram_status lowram_cache_bytes(const lowram_dims *d, uint64_t *compressed, uint64_t *dense) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  const uint64_t G = d->layers, H = d->heads_kv, dh = d->head_dim, N = d->n_ctx, r = d->rank;
+  const uint64_t F = d->hidden, n_c = (uint64_t)n_chunks(d), D = G * H * dh;
+  const uint64_t s = dtype_bytes(d->act), sc = dtype_bytes(d->coeff), sr = dtype_bytes(d->resid);
+  if (dense) *dense = 2 * G * H * dh * N * s;
+  if (compressed) {
+    uint64_t t = N * r * sc + D * r * s + G * H * (2 * F * dh + F + dh) * s;
+    t += G * H * (uint64_t)d->n_res * (dh * sr + 4) + G * H * (n_c + 1) * 4 + n_c * r * 4;
+    if (d->coeff == LOWRAM_I8) t += r * 2;
+    if (d->resid == LOWRAM_I8) t += G * H * dh * 2;
+    *compressed = t;
+  }
+  return LOWRAM_OK;
+}
+
+lowram_status lowram_compress(const lowram_dims *d, const lowram_model *m, const void *k,
+                              const void *v, const lowram_cache *out, void *ws, size_t ws_bytes,
+                              void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  if (d->n_ctx < d->chunk) return fail(LOWRAM_E_INVALID, "compress needs at least one chunk");
+  if (!m || !out) return fail(LOWRAM_E_INVALID, "model and out must not be NULL");
+  REQUIRE_PTR(k); REQUIRE_PTR(v);
+  REQUIRE_PTR(m->basis); REQUIRE_PTR(m->w1); REQUIRE_PTR(m->b1); REQUIRE_PTR(m->w2); REQUIRE_PTR(m->b2);
+  REQUIRE_PTR(out->coeff); REQUIRE_PTR(out->landmark); REQUIRE_PTR(out->res_ptr);
+  if (d->n_res > 0) { REQUIRE_PTR(out->res_idx); REQUIRE_PTR(out->res_val); }
+  if (d->coeff == LOWRAM_I8) REQUIRE_PTR(out->coeff_scale);
+  if (d->resid == LOWRAM_I8) REQUIRE_PTR(out->res_scale);
+  const CompressPlan p = compress_plan(d);
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  CompressArgs a;
+  memset(&a, 0, sizeof a);
+  a.k = k; a.v = v; a.basis = m->basis; a.w1 = m->w1; a.b1 = m->b1; a.w2 = m->w2; a.b2 = m->b2;
+  a.coeff = out->coeff; a.coeff_scale = (uint16_t *)out->coeff_scale; a.landmark = out->landmark;
+  a.res_ptr = out->res_ptr; a.res_idx = out->res_idx; a.res_val = out->res_val;
+  a.res_scale = (uint16_t *)out->res_scale;
+  a.err = reinterpret_cast<double *>((char *)ws + p.err_off);
+  a.c64 = reinterpret_cast<double *>((char *)ws + p.c64_off);
+  a.d64 = reinterpret_cast<double *>((char *)ws + p.d64_off);
+  a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
+  a.r = d->rank; a.F = d->hidden; a.N = d->n_ctx; a.C = d->chunk; a.n_res = d->n_res;
+  a.act = d->act; a.coeff_dt = d->coeff; a.resid_dt = d->resid;
+  return hip_status(run_compress(a, (hipStream_t)stream), "lowram_compress");
+}
+
+lowram_status lowram_decode_select(const lowram_dims *d, int32_t layer, const lowram_model *m,
+                                   const lowram_cache *c, const void *q, int32_t *sel_out,
+                                   void *ws, size_t ws_bytes, void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  const DecodePlan p = decode_plan(d);
+  if ((st = check_decode_inputs(d, layer, m, c, p)) != LOWRAM_OK) return st;
+  REQUIRE_PTR(q);
+  OPTIONAL_PTR(sel_out);
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  if (p.k_eff == 0) return LOWRAM_OK;
+  const long D = (long)d->layers * d->heads_kv * d->head_dim;
+  int32_t *sel = reinterpret_cast<int32_t *>((char *)ws + p.sel_off);
+  return hip_status(launch_select(d->act, q, (long)d->heads_q * d->head_dim, m->basis, c->landmark,
+                                  d->batch, d->heads_q, d->heads_kv, d->head_dim, d->rank,
+                                  n_chunks(d), (int)D, layer, p.k_eff, sel, sel_out, nullptr,
+                                  (hipStream_t)stream),
+                    "lowram_decode_select");
+}
+
+lowram_status lowram_decode_attend(const lowram_dims *d, int32_t layer, const lowram_model *m,
+                                   const lowram_cache *c, const void *q, const void *k_tail,
+                                   const void *v_tail, void *ws, size_t ws_bytes, void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  const DecodePlan p = decode_plan(d);
+  if ((st = check_decode_inputs(d, layer, m, c, p)) != LOWRAM_OK) return st;
+  REQUIRE_PTR(q);
+  if (d->n_tail > 0) { REQUIRE_PTR(k_tail); REQUIRE_PTR(v_tail); }
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  const AttendArgs a = make_attend(d, layer, m, c, q, k_tail, v_tail, ws, p);
+  return hip_status(launch_attend(d->act, d->coeff, d->resid, a, (hipStream_t)stream),
+                    "lowram_decode_attend");
+}
+
+lowram_status lowram_decode_combine(const lowram_dims *d, int32_t layer, const lowram_model *m,
+                                    void *out, void *ws, size_t ws_bytes, void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  const DecodePlan p = decode_plan(d);
+  if (layer < 0 || layer >= d->layers)
+    return fail(LOWRAM_E_INVALID, "layer %d outside [0, %d)", layer, d->layers);
+  if (p.k_eff == 0 && d->n_tail == 0)
+    return fail(LOWRAM_E_INVALID, "nothing to attend: no chunk selected and no tail");
+  REQUIRE_PTR(out);
+  if (p.k_eff > 0) {
+    if (!m) return fail(LOWRAM_E_INVALID, "model is NULL");
+    REQUIRE_PTR(m->w2); REQUIRE_PTR(m->b2);
+  }
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  CombineArgs a;
+  memset(&a, 0, sizeof a);
+  a.part = reinterpret_cast<const float *>((char *)ws + p.part_off);
+  a.w2 = m ? m->w2 : nullptr; a.b2 = m ? m->b2 : nullptr; a.out = out;
+  a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
+  a.F = d->hidden; a.layer = layer; a.g = d->heads_q / d->heads_kv;
+  a.n_comp = p.n_split; a.n_total = p.n_split + 1; a.PW = p.PW;
+  return hip_status(launch_combine(d->act, a, (hipStream_t)stream), "lowram_decode_combine");
+}
+
+lowram_status lowram_decode_attn(const lowram_dims *d, int32_t layer, const lowram_model *m,
+                                 const lowram_cache *c, const void *q, const void *k_tail,
+                                 const void *v_tail, void *out, int32_t *sel_out, void *ws,
+                                 size_t ws_bytes, void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  const DecodePlan p = decode_plan(d);
+  if ((st = check_decode_inputs(d, layer, m, c, p)) != LOWRAM_OK) return st;
+  REQUIRE_PTR(q); REQUIRE_PTR(out); OPTIONAL_PTR(sel_out);
+  if (d->n_tail > 0) { REQUIRE_PTR(k_tail); REQUIRE_PTR(v_tail); }
+  if (p.k_eff > 0) { REQUIRE_PTR(m->w2); REQUIRE_PTR(m->b2); }
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  if ((st = lowram_decode_select(d, layer, m, c, q, sel_out, ws, ws_bytes, stream)) != LOWRAM_OK) return st;
+  if ((st = lowram_decode_attend(d, layer, m, c, q, k_tail, v_tail, ws, ws_bytes, stream)) != LOWRAM_OK) return st;
+  return lowram_decode_combine(d, layer, m, out, ws, ws_bytes, stream);
+}
+
+lowram_status lowram_evict(const lowram_dims *d, const lowram_model *m, const lowram_cache *src,
+                           const void *obs_q, int32_t n_obs, int32_t keep_chunks,
+                           const lowram_cache *dst, int32_t *keep_out, void *ws, size_t ws_bytes,
+                           void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  const int n_c = n_chunks(d);
+  if (n_c < 1) return fail(LOWRAM_E_INVALID, "evict needs at least one chunk");
+  if (keep_chunks < 1 || keep_chunks > n_c)
+    return fail(LOWRAM_E_INVALID, "keep_chunks %d outside [1, %d]", keep_chunks, n_c);
+  if (n_obs < 0) return fail(LOWRAM_E_INVALID, "n_obs must be >= 0");
+  if (!m || !src || !dst) return fail(LOWRAM_E_INVALID, "model, src and dst must not be NULL");
+  if (n_obs > 0) REQUIRE_PTR(obs_q);
+  REQUIRE_PTR(m->basis);
+  REQUIRE_PTR(src->coeff); REQUIRE_PTR(src->landmark); REQUIRE_PTR(src->res_ptr);
+  REQUIRE_PTR(dst->coeff); REQUIRE_PTR(dst->landmark); REQUIRE_PTR(dst->res_ptr);
+  if (d->n_res > 0) {
+    REQUIRE_PTR(src->res_idx); REQUIRE_PTR(src->res_val);
+    REQUIRE_PTR(dst->res_idx); REQUIRE_PTR(dst->res_val);
+  }
+  OPTIONAL_PTR(keep_out);
+  if (src->coeff == dst->coeff || src->res_val == dst->res_val || src->res_ptr == dst->res_ptr)
+    return fail(LOWRAM_E_INVALID, "src and dst must not share coefficient or residual storage");
+  const EvictPlan p = evict_plan(d);
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  EvictArgs a;
+  memset(&a, 0, sizeof a);
+  a.basis = m->basis; a.obs_q = obs_q; a.n_obs = n_obs; a.keep = keep_chunks;
+  a.coeff = src->coeff; a.landmark = src->landmark; a.res_ptr = src->res_ptr;
+  a.res_idx = src->res_idx; a.res_val = src->res_val;
+  a.d_coeff = dst->coeff; a.d_landmark = dst->landmark; a.d_res_ptr = dst->res_ptr;
+  a.d_res_idx = dst->res_idx; a.d_res_val = dst->res_val;
+  a.keep_out = keep_out ? keep_out : reinterpret_cast<int32_t *>((char *)ws + p.keep_off);
+  a.scores = reinterpret_cast<double *>((char *)ws + p.scores_off);
+  a.acc = reinterpret_cast<double *>((char *)ws + p.acc_off);
+  a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
+  a.r = d->rank; a.N = d->n_ctx; a.C = d->chunk; a.n_res = d->n_res;
+  a.act = d->act; a.coeff_dt = d->coeff; a.resid_dt = d->resid;
+  return hip_status(run_evict(a, (hipStream_t)stream), "lowram_evict");
+}
+
+lowram_status lowram_dense_decode_attn(const lowram_dims *d, const void *q, const void *k,
+                                       const void *v, int32_t n_tokens, int64_t batch_stride,
+                                       void *out, void *ws, size_t ws_bytes, void *stream) {
+  lowram_status st = check_dense_dims(d);
+  if (st != LOWRAM_OK) return st;
+  if (n_tokens < 1) return fail(LOWRAM_E_INVALID, "n_tokens must be >= 1");
+  if (batch_stride < (int64_t)d->heads_kv * n_tokens * d->head_dim && d->batch > 1)
+    return fail(LOWRAM_E_INVALID, "batch_stride smaller than one sequence's keys");
+  REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(out);
+  const DensePlan p = dense_plan(d, n_tokens);
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  float *part = reinterpret_cast<float *>(ws);
+  hipError_t e = launch_dense(d->act, q, k, v, (long)batch_stride, d->batch, d->heads_q,
+                              d->heads_kv, d->head_dim, n_tokens, p.tps, p.n_split, part, p.PW,
+                              (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "lowram_dense_decode_attn");
+  CombineArgs a;
+  memset(&a, 0, sizeof a);
+  a.part = part; a.out = out;
+  a.B = d->batch; a.G = 1; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
+  a.F = 0; a.layer = 0; a.g = d->heads_q / d->heads_kv; a.n_comp = 0; a.n_total = p.n_split; a.PW = p.PW;
+  return hip_status(launch_combine(d->act, a, (hipStream_t)stream), "lowram_dense_decode_attn");
+}
+
+}  // extern "C"

@@ -1,0 +1,205 @@
+/*
+ * lowram.h -- C ABI of the MI355X (gfx950) compressed-KV decode-attention library.
+ *
+ * The method (LowRAM: "Low-Rank Keys and Amortised Values for Composable KV
+ * Cache Compression at Test-Time", abstract on mlinfo.pages.dev; summaries on
+ * zicq.com and rit.work) stores
+ *   - keys of a group of adjacent layers as per-token coefficients on a shared
+ *     low-rank basis (zicq.com English summary, "Cross-Layer Low-Rank Key
+ *     Compression"; xKV on the rit.work page),
+ *   - values as a per-head predictor V_hat = f(K) plus residuals
+ *     delta = V - V_hat for the tokens it reconstructs worst (zicq.com English
+ *     summary, "Core Mechanism"; abstract),
+ * and at each decode step rebuilds only the query-selected context chunks,
+ * while tokens produced after prefill stay uncompressed (rit.work page,
+ * generation section).  Attention is softmax(q K^T / sqrt(d_h)) V (OjaKV page,
+ * section 3).
+ *
+ * Conventions for every entry point
+ *   Ownership   The caller owns every buffer.  All tensor pointers are DEVICE
+ *               pointers unless a comment says "host".  The library never
+ *               allocates or frees memory, keeps no pointer after return and
+ *               never synchronises the stream.
+ *   Ordering    Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *               stream) in call order; outputs are valid once that work ends.
+ *   Errors      Arguments are validated on the host before anything is
+ *               enqueued; on error nothing is enqueued and a status is
+ *               returned.  LOWRAM_E_HIP means a launch failed (the stream may
+ *               then hold part of the work).  lowram_last_error() returns a
+ *               thread-local message for the last failing call on the thread.
+ *   Alignment   Every tensor pointer must be 16-byte aligned; the workspace
+ *               256-byte aligned.
+ *   Threads     Functions are re-entrant; calls that share output buffers or a
+ *               workspace must not overlap.
+ *   Layouts     Row-major, innermost index last.  D = layers * heads_kv *
+ *               head_dim, ordered (layer, kv head, dim).  n_c = n_ctx / chunk.
+ *               GQA: query head g reads kv head (g * heads_kv) / heads_q.
+ *   Dtypes      act = F32: everything float32.  act = BF16: q, out, K, V, tail,
+ *               basis and predictor in bfloat16; coeff and resid BF16 or I8
+ *               (int8 with float16 per-channel scales).  Landmarks are always
+ *               float32, indices int32.
+ */
+#ifndef LOWRAM_H
+#define LOWRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOWRAM_OK = 0,
+  LOWRAM_E_INVALID = 1,      /* bad sizes, pointers, alignment or layer index    */
+  LOWRAM_E_UNSUPPORTED = 2,  /* valid request outside what the kernels implement */
+  LOWRAM_E_WORKSPACE = 3,    /* workspace too small                               */
+  LOWRAM_E_HIP = 4           /* a HIP launch failed                               */
+} lowram_status;
+
+typedef enum { LOWRAM_F32 = 0, LOWRAM_BF16 = 1, LOWRAM_F16 = 2, LOWRAM_I8 = 3 } lowram_dtype;
+
+typedef enum {
+  LOWRAM_OP_COMPRESS = 0,
+  LOWRAM_OP_DECODE = 1,
+  LOWRAM_OP_EVICT = 2,
+  LOWRAM_OP_DENSE = 3
+} lowram_op;
+
+/* Sizes of one xKV group over a batch.  All counts are per sequence. */
+typedef struct {
+  int32_t batch;      /* B: sequences                                      */
+  int32_t layers;     /* G: layers in the group                            */
+  int32_t heads_q;    /* H_q                                               */
+  int32_t heads_kv;   /* H_kv, divides H_q, H_q / H_kv <= 16               */
+  int32_t head_dim;   /* d_h, multiple of 8, <= 256                        */
+  int32_t rank;       /* r, multiple of 8, <= D                            */
+  int32_t hidden;     /* F: predictor hidden width, multiple of 8          */
+  int32_t n_ctx;      /* N: compressed tokens, multiple of chunk (may be 0)*/
+  int32_t chunk;      /* C: tokens per chunk                               */
+  int32_t top_k;      /* chunks selected per kv head; clamped to n_c       */
+  int32_t n_tail;     /* T: uncompressed tail tokens (may be 0)            */
+  int32_t n_res;      /* residual capacity per (b, layer, kv head), <= N   */
+  int32_t act;        /* lowram_dtype of q/out/K/V/tail/basis/predictor    */
+  int32_t coeff;      /* lowram_dtype of the coefficients                  */
+  int32_t resid;      /* lowram_dtype of the residual rows                 */
+} lowram_dims;
+
+/* Per-context state that is not per token: the group basis and the per-head
+ * value predictor f(k) = W2 SiLU(W1 k + b1) + b2 (act dtype). */
+typedef struct {
+  const void *basis;  /* [B][D][r]          */
+  const void *w1;     /* [B][G][Hkv][F][dh] */
+  const void *b1;     /* [B][G][Hkv][F]     */
+  const void *w2;     /* [B][G][Hkv][dh][F] */
+  const void *b2;     /* [B][G][Hkv][dh]    */
+} lowram_model;
+
+/* The compressed cache of one group. */
+typedef struct {
+  void *coeff;        /* [B][N][r] coeff dtype: per-token coefficients shared by the group */
+  void *coeff_scale;  /* [B][r] float16 when coeff is I8, else NULL                        */
+  float *landmark;    /* [B][n_c][r] float32: mean dequantised coefficient of each chunk   */
+  int32_t *res_ptr;   /* [B][G][Hkv][n_c+1]: residual rows of chunk j are [ptr[j], ptr[j+1]) */
+  int32_t *res_idx;   /* [B][G][Hkv][n_res]: token index of each residual row, ascending   */
+  void *res_val;      /* [B][G][Hkv][n_res][dh] resid dtype: delta = v - v_hat              */
+  void *res_scale;    /* [B][G][Hkv][dh] float16 when resid is I8, else NULL                */
+} lowram_cache;
+
+/* Workspace bytes `op` needs for these dims (host only, enqueues nothing). */
+lowram_status lowram_workspace_bytes(const lowram_dims *dims, int32_t op, size_t *bytes);
+
+/* Storage accounting (host only).  *dense = M_KV = 2 L H_kv d_h N s for the
+ * group with s = 2 (bf16) or 4 (f32 act) -- the M_KV formula of the zicq.com
+ * English summary, "Core Mechanism" -- and *compressed = coefficients + basis
+ * + predictor + residual rows with int32 indices (n_res of them) + CSR
+ * pointers + float32 landmarks + fp16 scales, per sequence.  The tail is
+ * identical on both sides and counted in neither.  Either pointer may be NULL. */
+lowram_status lowram_cache_bytes(const lowram_dims *dims, uint64_t *compressed, uint64_t *dense);
+
+/* Compress a prefill of N tokens (zicq.com "Core Mechanism" and "Cross-Layer
+ * Low-Rank Key Compression"; abstract).  For each sequence:
+ *   c_t = U^T k_t^cat, stored rounded to coeff dtype (I8: per-channel scales
+ *   over the N tokens, s = fp16(max|c|/127), q = clamp(rne(c/s), +-127));
+ *   e_t = ||v_t - f_{l,h}(U_{l,h} deq(c_t))||^2 in float64 per (layer, head);
+ *   the n_res tokens with the largest e (lowest index wins ties) keep
+ *   delta = v - v_hat rounded to resid dtype (I8: per-dim scales over those
+ *   rows), stored in ascending token order with chunk CSR pointers;
+ *   landmark_j = mean of deq(c_t) over chunk j, float64 rounded to float32.
+ * k, v: [B][G][Hkv][N][dh] act dtype.  out: every cache pointer the dtypes
+ * need.  Workspace: lowram_workspace_bytes(LOWRAM_OP_COMPRESS). */
+lowram_status lowram_compress(const lowram_dims *dims, const lowram_model *model, const void *k,
+                              const void *v, const lowram_cache *out, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* One decode step of attention at `layer` of the group for one new query per
+ * sequence (rit.work generation section; OjaKV section 3).  For each (b, kv
+ * head h):
+ *   q~ = U_{l,h}^T sum_{g in group(h)} q_g and s_j = q~ . landmark_j in
+ *   float64; the top min(top_k, n_c) chunks by (s desc, j asc) are selected;
+ *   their keys U_{l,h} deq(c_t) and values f(k_hat) + delta (residual rows)
+ *   are rebuilt in registers/LDS; each query head attends over them plus the
+ *   layer's T tail tokens with scale 1/sqrt(d_h).
+ * q: [B][Hq][dh]; k_tail, v_tail: [B][G][Hkv][T][dh] (the whole group; the
+ * layer is selected here); out: [B][Hq][dh], act dtype.  sel_out: optional
+ * [B][Hkv][min(top_k, n_c)] int32, chunk indices ascending.  Error if no chunk
+ * is selected and T = 0.  Workspace: lowram_workspace_bytes(LOWRAM_OP_DECODE). */
+lowram_status lowram_decode_attn(const lowram_dims *dims, int32_t layer, const lowram_model *model,
+                                 const lowram_cache *cache, const void *q, const void *k_tail,
+                                 const void *v_tail, void *out, int32_t *sel_out, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* The three stages lowram_decode_attn runs, for callers that schedule or time
+ * them separately.  They communicate through the workspace, which must be the
+ * same buffer with the same dims and layer for all three.
+ *   select:  chunk scores and top-k (writes the selection into the workspace
+ *            and, if sel_out != NULL, into sel_out);
+ *   attend:  rebuild-and-attend over the selected chunks and the tail, writing
+ *            per-split softmax partials into the workspace;
+ *   combine: merges the partials and applies the hoisted second predictor
+ *            layer, writing out. */
+lowram_status lowram_decode_select(const lowram_dims *dims, int32_t layer, const lowram_model *model,
+                                   const lowram_cache *cache, const void *q, int32_t *sel_out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+lowram_status lowram_decode_attend(const lowram_dims *dims, int32_t layer, const lowram_model *model,
+                                   const lowram_cache *cache, const void *q, const void *k_tail,
+                                   const void *v_tail, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+lowram_status lowram_decode_combine(const lowram_dims *dims, int32_t layer, const lowram_model *model,
+                                    void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Eviction composed on top of the compressed cache (zicq.com Chinese summary,
+ * composition with quantisation and eviction).  acc_j = sum over the n_obs
+ * observation queries, the G layers and the Hkv heads of the chunk score s_j
+ * (as in decode) in float64; the keep_chunks chunks with the largest acc
+ * (lowest index wins ties) are copied to dst in ascending chunk order:
+ * coefficients, landmarks and residual rows, with residual token indices
+ * renumbered to the new positions.  dst has n_ctx' = keep_chunks * chunk and
+ * the same residual capacity n_res (dst res_ptr[n_c'] rows are live); scales
+ * are unchanged (dst coeff_scale / res_scale may alias src's).
+ * obs_q: [n_obs][B][G][Hq][dh] act dtype.  keep_out: optional [B][keep_chunks]
+ * int32 kept source chunk indices.  Workspace: LOWRAM_OP_EVICT. */
+lowram_status lowram_evict(const lowram_dims *dims, const lowram_model *model,
+                           const lowram_cache *src, const void *obs_q, int32_t n_obs,
+                           int32_t keep_chunks, const lowram_cache *dst, int32_t *keep_out,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Uncompressed decode attention, the comparator for the compressed path:
+ * out[b][g] = softmax(k_b,h q_g / sqrt(d_h)) v_b,h over n_tokens tokens
+ * (OjaKV section 3).  Uses batch, heads_q, heads_kv, head_dim and act of dims.
+ * q: [B][Hq][dh]; k, v: element (b, h, t, d) at b*batch_stride +
+ * (h*n_tokens + t)*dh + d (so one layer of a [B][G][Hkv][n][dh] cache can be
+ * passed with batch_stride = G*Hkv*n*dh); out: [B][Hq][dh].
+ * Workspace: LOWRAM_OP_DENSE with dims.n_ctx = n_tokens. */
+lowram_status lowram_dense_decode_attn(const lowram_dims *dims, const void *q, const void *k,
+                                       const void *v, int32_t n_tokens, int64_t batch_stride,
+                                       void *out, void *workspace, size_t workspace_bytes,
+                                       void *stream);
+
+const char *lowram_status_string(lowram_status status);
+const char *lowram_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOWRAM_H */

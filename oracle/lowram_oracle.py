@@ -177,10 +177,14 @@ def landmarks(cdeq: np.ndarray, C: int) -> np.ndarray:
     return cdeq.reshape(N // C, C, r).mean(axis=1).astype(np.float32)
 
 
-def compress(inp: dict, s) -> dict:
+def compress(inp: dict, s, stored: dict | None = None) -> dict:
     """Compress a prefill: project keys, predict values, keep residuals for the
     worst tokens, summarise chunks.  `inp` holds stored arrays (see synth.gen);
     `s` carries sizes and dtypes.  Returns the stored cache and fp64 side data.
+
+    `stored` (optional) supplies already-stored coefficients ("coeff", and
+    "coeff_scale" for int8) that replace step 1's rounding, so the later steps
+    can be checked on exactly the bits another implementation stored.
 
     Steps (per sequence b):
       1. c_t = U^T k_t^cat; store c~ = round(c) (or int8 + fp16 scales per
@@ -208,7 +212,16 @@ def compress(inp: dict, s) -> dict:
         k_cat = k.transpose(2, 0, 1, 3).reshape(N, -1)   # token-major, (l, h, d)
         c = project(k_cat, U)
         out["c_exact"].append(c)
-        if cdt == I8:
+        if stored is not None:
+            cst = np.asarray(stored["coeff"][b])
+            out["coeff"].append(cst)
+            if cdt == I8:
+                cs = np.asarray(stored["coeff_scale"][b])
+                out["coeff_scale"].append(cs)
+                cdeq = dequantise(cst, cs, axis=0)
+            else:
+                cdeq = decode(cst, cdt)
+        elif cdt == I8:
             cq, cs = quantise(c, axis=0)
             cdeq = dequantise(cq, cs, axis=0)
             out["coeff"].append(cq)

@@ -1,0 +1,168 @@
+"""The C ABI on the host: exported symbols, storage accounting, workspace
+sizing and every validation path.  No call here reaches a kernel launch, so
+these run without a GPU (fake device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import lowram_oracle as O
+from synth.configs import ALL, COMPOSED_128K, LLAMA8B_32K, TINY
+from tests.harness import dims_of
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+P = pytest.importorskip("decode_attention_compressed_amd")
+L = P._lib
+
+FAKE = 1 << 20  # a 256-byte aligned fake device address; never dereferenced
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "lowram.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(lowram_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.lib()
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(L.SIGNATURES) == set(names)
+
+
+@pytest.mark.parametrize("s", ALL, ids=lambda s: s.name)
+def test_cache_bytes_match_accounting(s):
+    d = dims_of(s)
+    comp, dense = P.cache_bytes(d)
+    assert dense == O.m_kv(s.G, s.Hkv, s.dh, s.N, O.DTYPE_BYTES[s.act])
+    assert comp == O.compressed_bytes(s.G, s.Hkv, s.dh, s.N, s.C, s.r, s.F, s.n_res, s.act, s.coeff, s.resid)
+
+
+def test_llama_ratio_and_composed_ratio():
+    c, dn = P.cache_bytes(dims_of(LLAMA8B_32K))
+    assert dn / c == pytest.approx(7.008, abs=1e-3)
+    c, dn = P.cache_bytes(dims_of(TINY))
+    assert dn / c == pytest.approx(3.006, abs=1e-3)
+
+
+@pytest.mark.parametrize("s", ALL, ids=lambda s: s.name)
+def test_workspace_sizes_are_positive_and_aligned(s):
+    d = dims_of(s)
+    for op in (L.OP_COMPRESS, L.OP_DECODE, L.OP_EVICT, L.OP_DENSE):
+        n = P.workspace_bytes(d, op)
+        assert n > 0 and n % 256 == 0
+
+
+def call_decode(d, layer=0, ws_bytes=None, q=FAKE, out=FAKE, sel=None, ws=FAKE, model=None, cache=None):
+    lib = L.lib()
+    m = model or L.Model(FAKE, FAKE, FAKE, FAKE, FAKE)
+    c = cache or L.Cache(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    need = P.workspace_bytes(d, L.OP_DECODE) if ws_bytes is None else ws_bytes
+    return lib.lowram_decode_attn(ctypes.byref(d), layer, ctypes.byref(m), ctypes.byref(c), q, FAKE,
+                                  FAKE, out, sel, ws, need, None)
+
+
+def status_of(fn):
+    try:
+        fn()
+    except P.LowramError as e:
+        return e.status
+    return L.OK
+
+
+def base_dims(**kw):
+    d = dims_of(LLAMA8B_32K.replace(B=1, N=1024))
+    return P.with_(d, **kw)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), L.E_UNSUPPORTED),
+    (dict(n_ctx=1000), L.E_INVALID),            # not a multiple of the chunk
+    (dict(n_res=5000), L.E_INVALID),            # more residuals than tokens
+    (dict(heads_q=30), L.E_INVALID),            # not a multiple of heads_kv
+    (dict(heads_q=8 * 17), L.E_UNSUPPORTED),    # more than 16 query heads per kv head
+    (dict(rank=520), L.E_UNSUPPORTED),          # not a multiple of 16
+    (dict(rank=8192), L.E_UNSUPPORTED),
+    (dict(hidden=100), L.E_UNSUPPORTED),
+    (dict(batch=0), L.E_INVALID),
+    (dict(chunk=0), L.E_INVALID),
+    (dict(top_k=-1), L.E_INVALID),
+    (dict(act=L.F32), L.E_UNSUPPORTED),         # f32 act with bf16 coefficients
+    (dict(coeff=L.F16), L.E_UNSUPPORTED),
+    (dict(act=7), L.E_UNSUPPORTED),
+])
+def test_bad_dims_rejected_before_launch(kw, status):
+    d = base_dims(**kw)
+    assert status_of(lambda: P.workspace_bytes(d, L.OP_DECODE)) == status
+    assert call_decode(d, ws_bytes=1 << 30) == status
+    assert L.lib().lowram_last_error()
+
+
+def test_decode_argument_errors():
+    d = base_dims()
+    assert call_decode(d, layer=4) == L.E_INVALID
+    assert call_decode(d, layer=-1) == L.E_INVALID
+    assert call_decode(d, ws_bytes=P.workspace_bytes(d, L.OP_DECODE) - 256) == L.E_WORKSPACE
+    assert call_decode(d, ws=FAKE + 16) == L.E_INVALID    # workspace not 256-byte aligned
+    assert call_decode(d, q=FAKE + 2) == L.E_INVALID      # q not 16-byte aligned
+    assert call_decode(d, q=None) == L.E_INVALID
+    assert call_decode(d, out=None) == L.E_INVALID
+    assert call_decode(d, sel=FAKE + 4) == L.E_INVALID
+    nothing = P.with_(d, top_k=0, n_tail=0)
+    assert call_decode(nothing) == L.E_INVALID
+    no_cache = L.Cache(None, None, None, None, None, None, None)
+    assert call_decode(d, cache=no_cache) == L.E_INVALID
+    i8 = P.with_(d, coeff=L.I8)
+    assert call_decode(i8, cache=L.Cache(FAKE, None, FAKE, FAKE, FAKE, FAKE, None)) == L.E_INVALID
+
+
+def test_compress_and_evict_argument_errors():
+    lib = L.lib()
+    d = base_dims()
+    m = L.Model(FAKE, FAKE, FAKE, FAKE, FAKE)
+    c = L.Cache(FAKE, None, FAKE, FAKE, FAKE, FAKE, None)
+    need = P.workspace_bytes(d, L.OP_COMPRESS)
+    assert lib.lowram_compress(ctypes.byref(d), ctypes.byref(m), None, FAKE, ctypes.byref(c), FAKE, need, None) == L.E_INVALID
+    assert lib.lowram_compress(ctypes.byref(d), ctypes.byref(m), FAKE, FAKE, ctypes.byref(c), FAKE, need - 1, None) == L.E_WORKSPACE
+    empty = P.with_(d, n_ctx=0, n_res=0)
+    assert lib.lowram_compress(ctypes.byref(empty), ctypes.byref(m), FAKE, FAKE, ctypes.byref(c), FAKE, need, None) == L.E_INVALID
+    dst = L.Cache(FAKE * 2, None, FAKE * 2, FAKE * 2, FAKE * 2, FAKE * 2, None)
+    ne = P.workspace_bytes(d, L.OP_EVICT)
+    n_c = d.n_ctx // d.chunk
+    ev = lambda keep, dst_=dst, n_obs=1: lib.lowram_evict(ctypes.byref(d), ctypes.byref(m), ctypes.byref(c), FAKE, n_obs, keep, ctypes.byref(dst_), None, FAKE, ne, None)
+    assert ev(0) == L.E_INVALID
+    assert ev(n_c + 1) == L.E_INVALID
+    assert ev(2, n_obs=-1) == L.E_INVALID
+    assert ev(2, dst_=c) == L.E_INVALID        # in-place eviction is refused
+
+
+def test_dense_argument_errors():
+    lib = L.lib()
+    d = P.with_(base_dims(), n_ctx=1000, chunk=7)   # the comparator ignores chunking
+    need = P.workspace_bytes(d, L.OP_DENSE)
+    assert need > 0
+    ok_stride = d.heads_kv * 1000 * d.head_dim
+    assert lib.lowram_dense_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, 0, ok_stride, FAKE, FAKE, need, None) == L.E_INVALID
+    assert lib.lowram_dense_decode_attn(ctypes.byref(P.with_(d, batch=2)), FAKE, FAKE, FAKE, 1000, 10, FAKE, FAKE, need, None) == L.E_INVALID
+
+
+def test_status_strings():
+    lib = L.lib()
+    for s in range(5):
+        assert lib.lowram_status_string(s)
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "decode_attention_compressed_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+(oracle|synth)\b", text, re.M), f
+    ora = open(os.path.join(ROOT, "oracle", "lowram_oracle.py")).read()
+    assert not re.search(r"^\s*(from|import)\s+(decode_attention_compressed_amd|synth|torch)\b", ora, re.M)

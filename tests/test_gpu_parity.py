@@ -1,0 +1,252 @@
+"""GPU parity of the HIP library against the CPU oracle, through the C ABI.
+
+Sizes: every workload shape with a reduced batch and context so that the
+oracle finishes in seconds, while each case still spans several 128-token
+tiles, several chunks per split and ragged tails.  Stage isolation: the oracle
+continues from the bits the GPU stored (coefficients, then the whole cache),
+so selections must be bit-exact; float outputs must satisfy
+|gpu - oracle| <= 2e-3 + 1e-2 |oracle| elementwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import lowram_oracle as O
+from synth import gen
+from synth.configs import (BF16, COMPOSED_128K, F32, I8, LLAMA8B_32K, MISTRAL7B_16K, QWEN4B_64K,
+                           TINY, small)
+from tests.harness import (bf16_ulp_diff, cache_to_host, dims_of, f32_of, model_of, to_dev,
+                           to_host, upload, within_tol)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny-fp32": TINY,
+    "llama8b-small": small(LLAMA8B_32K, k=6, T=100),
+    "mistral7b-small": small(MISTRAL7B_16K, k=5, T=64),
+    "qwen4b-small": small(QWEN4B_64K, k=3, T=200),
+    "composed-small": small(COMPOSED_128K, k=3, T=72),
+}
+
+
+def P():
+    import decode_attention_compressed_amd as pkg
+    return pkg
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def run(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    s = CASES[request.param]
+    print(f"\n[case] {request.param}: {s}", flush=True)
+    inp = gen.make(s)
+    dev = upload(inp)
+    d = dims_of(s)
+    cache = P().alloc_cache(d)
+    P().compress(d, model_of(dev), dev["k"], dev["v"], cache)
+    sync()
+    return dict(name=request.param, s=s, inp=inp, dev=dev, d=d, cache=cache, host=cache_to_host(cache))
+
+
+def test_coefficients_match_oracle_rounding(run):
+    s, inp, host = run["s"], run["inp"], run["host"]
+    ref = O.compress(inp, s)
+    if s.coeff == I8:
+        assert np.array_equal(host["coeff_scale"].view(np.uint16), ref["coeff_scale"].view(np.uint16))
+        diff = np.abs(host["coeff"].astype(np.int32) - ref["coeff"].astype(np.int32))
+        assert diff.max() <= 1 and np.mean(diff > 0) < 1e-4
+    elif s.coeff == BF16:
+        ulp = bf16_ulp_diff(host["coeff"], ref["coeff"])
+        assert ulp.max() <= 1 and np.mean(ulp > 0) < 1e-4, (ulp.max(), np.mean(ulp > 0))
+    else:
+        g, o = host["coeff"].astype(np.float64), ref["coeff"].astype(np.float64)
+        assert np.max(np.abs(g - o) / np.maximum(np.abs(o), 1e-30)) <= 2 ** -23
+
+
+def test_compress_stages_bit_exact(run):
+    """Landmarks, residual sets, CSR pointers and residual rows from the GPU's
+    stored coefficients."""
+    s, inp, host = run["s"], run["inp"], run["host"]
+    ref = O.compress(inp, s, stored={"coeff": host["coeff"], "coeff_scale": host.get("coeff_scale")})
+    assert np.array_equal(host["landmark"], ref["landmark"])
+    assert np.array_equal(host["res_idx"], ref["res_idx"])
+    assert np.array_equal(host["res_ptr"], ref["res_ptr"])
+    if s.resid == I8:
+        assert np.array_equal(host["res_scale"].view(np.uint16), ref["res_scale"].view(np.uint16))
+        diff = np.abs(host["res_val"].astype(np.int32) - ref["res_val"].astype(np.int32))
+        assert diff.max() <= 1 and np.mean(diff > 0) < 1e-4
+    elif s.resid == BF16:
+        ulp = bf16_ulp_diff(host["res_val"], ref["res_val"])
+        assert ulp.max() <= 1 and np.mean(ulp > 0) < 1e-4
+    else:
+        assert np.allclose(host["res_val"], ref["res_val"], rtol=2 ** -23, atol=0)
+
+
+def test_residual_sets_end_to_end(run):
+    """Oracle from raw K/V with its own rounding: the residual sets agree."""
+    s, inp, host = run["s"], run["inp"], run["host"]
+    ref = O.compress(inp, s)
+    inter = sum(len(np.intersect1d(host["res_idx"][i], ref["res_idx"][i]))
+                for i in np.ndindex(host["res_idx"].shape[:3]))
+    total = host["res_idx"].size
+    assert inter / max(total, 1) > 0.999
+
+
+def evicted(run):
+    """(dims, device cache, host cache, token count) the decode steps run on."""
+    s, d = run["s"], run["d"]
+    if s.evict_keep >= 1.0:
+        return d, run["cache"], run["host"], s.N
+    if "evicted" not in run:
+        dev = run["dev"]
+        obs = to_dev(run["inp"]["obs_q"])
+        dst, d2, keep = P().evict(d, model_of(dev), run["cache"], obs, s.keep_chunks)
+        sync()
+        run["evicted"] = (d2, dst, cache_to_host(dst), to_host(keep))
+    d2, dst, hdst, keep = run["evicted"]
+    return d2, dst, hdst, d2.n_ctx
+
+
+def test_eviction_matches_oracle(run):
+    s = run["s"]
+    if s.evict_keep >= 1.0:
+        pytest.skip("no eviction in this workload")
+    d2, dst, hdst, N2 = evicted(run)
+    keep = run["evicted"][3]
+    ref = O.evict(run["host"], run["inp"], s, run["inp"]["obs_q"], s.keep_chunks)
+    assert np.array_equal(keep, ref["keep"])
+    assert np.array_equal(hdst["coeff"], ref["coeff"])
+    assert np.array_equal(hdst["landmark"], ref["landmark"])
+    assert np.array_equal(hdst["res_ptr"], ref["res_ptr"])
+    for i in np.ndindex(hdst["res_ptr"].shape[:3]):
+        n = hdst["res_ptr"][i][-1]
+        assert np.array_equal(hdst["res_idx"][i][:n], ref["res_idx"][i][:n])
+        assert np.array_equal(hdst["res_val"][i][:n], ref["res_val"][i][:n])
+
+
+def decode_both(run, step, layer, top_k=None, tail=True):
+    s = run["s"]
+    d, cache, hcache, N = evicted(run)
+    if top_k is not None:
+        d = P().with_(d, top_k=top_k)
+    if not tail:
+        d = P().with_(d, n_tail=0)
+    dev = run["dev"]
+    q = dev["q"][step, layer].contiguous()
+    kk = P().k_eff(d)
+    sel = torch.full((s.B, s.Hkv, kk), -1, dtype=torch.int32, device="cuda")
+    kt = dev["k_tail"] if tail else None
+    vt = dev["v_tail"] if tail else None
+    out = P().decode_attn(d, layer, model_of(dev), cache, q, kt, vt, sel_out=sel)
+    sync()
+    inp = run["inp"] if tail else dict(run["inp"], k_tail=run["inp"]["k_tail"][:, :, :, :0],
+                                        v_tail=run["inp"]["v_tail"][:, :, :, :0])
+    ref, rsel = O.decode_layer(hcache, inp, s, layer, run["inp"]["q"][step, layer], d.top_k, N=N)
+    return f32_of(out), to_host(sel), ref, rsel
+
+
+def test_decode_matches_oracle(run):
+    s = run["s"]
+    for step in range(2):
+        for layer in range(s.G):
+            out, sel, ref, rsel = decode_both(run, step, layer)
+            assert np.array_equal(sel, rsel), (step, layer)
+            ok, worst = within_tol(out, ref)
+            assert ok, f"step {step} layer {layer}: worst excess {worst}"
+
+
+@pytest.mark.parametrize("which", ["all", "clamp", "tail-only", "no-tail", "one"])
+def test_decode_edge_cases(run, which):
+    s = run["s"]
+    n_c = evicted(run)[0].n_ctx // s.C
+    kw = {"all": dict(top_k=n_c), "clamp": dict(top_k=n_c + 7), "tail-only": dict(top_k=0),
+          "no-tail": dict(tail=False), "one": dict(top_k=1)}[which]
+    out, sel, ref, rsel = decode_both(run, 1, s.G - 1, **kw)
+    assert np.array_equal(sel, rsel)
+    if which in ("all", "clamp"):
+        assert np.array_equal(sel[0, 0], np.arange(n_c))
+    ok, worst = within_tol(out, ref)
+    assert ok, worst
+
+
+def test_decode_is_deterministic(run):
+    s = run["s"]
+    d, cache, _, _ = evicted(run)
+    dev = run["dev"]
+    q = dev["q"][0, 0].contiguous()
+    outs = [P().decode_attn(d, 0, model_of(dev), cache, q, dev["k_tail"], dev["v_tail"]).clone() for _ in range(2)]
+    sync()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_staged_calls_equal_fused_call(run):
+    s = run["s"]
+    d, cache, _, _ = evicted(run)
+    dev = run["dev"]
+    q = dev["q"][1, 0].contiguous()
+    ws = P().workspace(d, P()._lib.OP_DECODE)
+    out1 = torch.empty_like(q)
+    call = P().DecodeCall(d, 0, model_of(dev), cache, q, dev["k_tail"], dev["v_tail"], out1, ws)
+    call.select(); call.attend(); call.combine()
+    out2 = P().decode_attn(d, 0, model_of(dev), cache, q, dev["k_tail"], dev["v_tail"])
+    sync()
+    assert torch.equal(out1, out2)
+
+
+def test_dense_comparator_matches_oracle(run):
+    s = run["s"]
+    dev, inp = run["dev"], run["inp"]
+    kd = torch.cat([dev["k"], dev["k_tail"]], dim=3).contiguous()
+    vd = torch.cat([dev["v"], dev["v_tail"]], dim=3).contiguous()
+    d = run["d"]
+    for layer in (0, s.G - 1):
+        q = dev["q"][0, layer].contiguous()
+        out = P().dense_decode_attn(d, q, kd, vd, layer)
+        sync()
+        K = np.concatenate([O.decode(inp["k"][:, layer], s.act), O.decode(inp["k_tail"][:, layer], s.act)], axis=2)
+        V = np.concatenate([O.decode(inp["v"][:, layer], s.act), O.decode(inp["v_tail"][:, layer], s.act)], axis=2)
+        ref = O.dense_decode_layer(O.decode(inp["q"][0, layer], s.act), K, V, s.Hq, s.Hkv)
+        ok, worst = within_tol(f32_of(out), ref)
+        assert ok, worst
+
+
+# ---------------------------------------------------------------------------
+# special shapes
+# ---------------------------------------------------------------------------
+def _roundtrip(s, top_k):
+    inp = gen.make(s)
+    dev = upload(inp)
+    d = dims_of(s, top_k=top_k)
+    cache = P().alloc_cache(d)
+    P().compress(d, model_of(dev), dev["k"], dev["v"], cache)
+    q = dev["q"][0, 1].contiguous()
+    sel = torch.empty((s.B, s.Hkv, P().k_eff(d)), dtype=torch.int32, device="cuda")
+    out = P().decode_attn(d, 1, model_of(dev), cache, q, dev["k_tail"], dev["v_tail"], sel_out=sel)
+    sync()
+    host = cache_to_host(cache)
+    ref, rsel = O.decode_layer(host, inp, s, 1, inp["q"][0, 1], top_k)
+    return f32_of(out), to_host(sel), ref, rsel, host, inp
+
+
+@pytest.mark.parametrize("name,shape,top_k", [
+    ("mha", small(LLAMA8B_32K, Hq=8, Hkv=8, B=1, N=1024, T=32), 3),
+    ("no-residuals", small(LLAMA8B_32K, B=1, N=1024, rho=0.0, T=16), 4),
+    ("all-residuals", small(LLAMA8B_32K, B=1, N=1024, rho=1.0, T=16), 4),
+    ("fp32-g8", TINY.replace(Hq=16, N=512, rho=0.5, T=1), 3),
+    ("int8-ragged", small(COMPOSED_128K, B=1, N=2048, evict_keep=1.0, n_obs=0, T=5), 7),
+])
+def test_special_shapes(name, shape, top_k):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"\n[case] {name}: {shape}", flush=True)
+    out, sel, ref, rsel, host, inp = _roundtrip(shape, top_k)
+    assert np.array_equal(sel, rsel)
+    ok, worst = within_tol(out, ref)
+    assert ok, worst
+    if shape.rho == 1.0:
+        assert np.array_equal(host["res_idx"][0, 0, 0], np.arange(shape.N))
