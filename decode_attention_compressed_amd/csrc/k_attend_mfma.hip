@@ -1,12 +1,13 @@
-// Fused rebuild-and-attend on gfx950 matrix cores (bf16 MFMA, fp32 accumulate).
+// Fused rebuild-and-attend on gfx950 matrix cores (bf16/fp16 MFMA, fp32 accumulate).
 //
 // One workgroup (4 waves) owns one (sequence b, kv head h) and a run of the
 // chunks selected for it.  For each 128-token tile of a selected chunk:
 //   1. K_hat[128][dh] = deq(coeff tile)[128][r] . U_{l,h}^T   (32x32x16 MFMA,
-//      coefficient and basis slabs staged through LDS; int8 coefficients are
-//      exact in bf16 and their per-channel scale is folded into the basis slab)
+//      coefficient and basis slabs staged through LDS; bf16 operands as
+//      stored; int8 coefficients are exact in fp16 and their per-channel
+//      scale is folded into an fp16 basis slab)
 //   2. logits = K_hat . q^T for the g query heads of h (16x16x32 MFMA, g padded
-//      to 16), online softmax in log2 units, p rounded to bf16 in LDS
+//      to 16), online softmax in log2 units, p rounded to fp16 in LDS
 //   3. H = SiLU(K_hat . W1^T + b1) in 64-wide hidden blocks (32x32x16 MFMA)
 //   4. accH += p . H (16x16x32 MFMA), kept in registers across tiles
 //   5. accV += p . delta for the residual rows of the tile (CSR of the chunk)
@@ -23,6 +24,7 @@
 namespace lowram {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
@@ -31,18 +33,32 @@ constexpr int RS = 32;    // rank slab of step 1
 constexpr int PAD = 8;    // bf16 pad per LDS row (keeps 16-byte rows, spreads banks)
 constexpr int CS_LD = RS + PAD, HS_LD = TM + PAD, PS_LD = TM + PAD;
 
-__device__ __forceinline__ bf16x8 lds8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+// 16-byte LDS fragment loads
+__device__ __forceinline__ bf16x8 ldb8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ f16x8 ldh8(const uint16_t *p) { return *reinterpret_cast<const f16x8 *>(p); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Operands produced inside the kernel (rebuilt keys, hidden activations,
+// softmax weights, queries, first-layer weights) are fp16: 11 significant
+// bits instead of bf16's 8 at the same MFMA rate.  The stored bf16
+// coefficients and basis feed step 1 exactly as stored.
+__device__ __forceinline__ uint16_t h16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+__device__ __forceinline__ float f16f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  return (uint32_t)h16(lo) | ((uint32_t)h16(hi) << 16);
 }
+
+template <typename TC> struct Step1 { typedef bf16x8 frag; static __device__ frag ld(const uint16_t *p) { return ldb8(p); } };
+template <> struct Step1<int8_t> { typedef f16x8 frag; static __device__ frag ld(const uint16_t *p) { return ldh8(p); } };
 
 template <int DH>
 struct MfmaSmem {
@@ -81,7 +97,7 @@ template <int DH>
 __device__ __forceinline__ void stage_slab(const int8_t *cf, const uint16_t *csc, const bf16 *U,
                                            long row0, int r, int r0, uint16_t *Cs, uint16_t *Us) {
   const int tid = threadIdx.x;
-  // int8 coefficient rows: 32 bytes per row, two 16-byte pieces; |q| <= 127 is exact in bf16
+  // int8 coefficient rows: 32 bytes per row, two 16-byte pieces; |q| <= 127 is exact in fp16
   {
     const int row = tid / 2, part = tid % 2;
     const uint4 v = *reinterpret_cast<const uint4 *>(cf + (row0 + row) * r + r0 + part * 16);
@@ -92,7 +108,7 @@ __device__ __forceinline__ void stage_slab(const int8_t *cf, const uint16_t *csc
     *reinterpret_cast<uint4 *>(Cs + row * CS_LD + part * 16) = make_uint4(w[0], w[1], w[2], w[3]);
     *reinterpret_cast<uint4 *>(Cs + row * CS_LD + part * 16 + 8) = make_uint4(w[4], w[5], w[6], w[7]);
   }
-  // basis rows scaled by the coefficient channel scales, rounded to bf16
+  // basis rows scaled by the coefficient channel scales, rounded once to fp16
 #pragma unroll
   for (int u = 0; u < (DH * RS / 8) / 256; ++u) {
     const int c = tid + 256 * u, row = c / (RS / 8), part = c % (RS / 8);
@@ -162,7 +178,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + ((long)b * a.Hq + (long)h * g) * DH;
     for (int i = tid; i < 16 * DH; i += 256) {
       const int gi = i / DH, d = i % DH;
-      Qs[gi * KS_LD + d] = gi < g ? qb[gi * DH + d] : (uint16_t)0;
+      Qs[gi * KS_LD + d] = gi < g ? h16(bf16_bits_to_f32(qb[gi * DH + d])) : (uint16_t)0;
     }
   }
   if (tid < 16) { ms[tid] = -INFINITY; ls[tid] = 0.f; al[tid] = 0.f; }
@@ -195,12 +211,12 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
 #pragma unroll
         for (int ks = 0; ks < RS / 16; ++ks) {
           const int kof = 16 * ks + 8 * (lane >> 5);
-          bf16x8 af[2];
+          typename Step1<TC>::frag af[2];
 #pragma unroll
-          for (int mi = 0; mi < 2; ++mi) af[mi] = lds8(Cs + (64 * wm + 32 * mi + (lane & 31)) * CS_LD + kof);
+          for (int mi = 0; mi < 2; ++mi) af[mi] = Step1<TC>::ld(Cs + (64 * wm + 32 * mi + (lane & 31)) * CS_LD + kof);
 #pragma unroll
           for (int ni = 0; ni < NT1; ++ni) {
-            const bf16x8 bfr = lds8(Us + (wn * (DH / 2) + 32 * ni + (lane & 31)) * CS_LD + kof);
+            const typename Step1<TC>::frag bfr = Step1<TC>::ld(Us + (wn * (DH / 2) + 32 * ni + (lane & 31)) * CS_LD + kof);
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi) acc1[mi][ni] = mfma32(af[mi], bfr, acc1[mi][ni]);
           }
@@ -215,7 +231,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
           for (int i = 0; i < 16; ++i) {
             const int row = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
             const int col = wn * (DH / 2) + 32 * ni + (lane & 31);
-            Ks[row * KS_LD + col] = f32_to_bf16_bits(acc1[mi][ni][i]);
+            Ks[row * KS_LD + col] = h16(acc1[mi][ni][i]);
           }
       __syncthreads();
 
@@ -224,10 +240,10 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
 #pragma unroll
       for (int ks = 0; ks < DH / 32; ++ks) {
         const int kof = 32 * ks + 8 * (lane >> 4);
-        const bf16x8 bq = lds8(Qs + (lane & 15) * KS_LD + kof);
+        const f16x8 bq = ldh8(Qs + (lane & 15) * KS_LD + kof);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
-          acc2[mi] = mfma16(lds8(Ks + (32 * w + 16 * mi + (lane & 15)) * KS_LD + kof), bq, acc2[mi]);
+          acc2[mi] = mfma16(ldh8(Ks + (32 * w + 16 * mi + (lane & 15)) * KS_LD + kof), bq, acc2[mi]);
       }
       const int gi = lane & 15;
       float mx = -INFINITY;
@@ -251,7 +267,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = gi < g ? exp2f(acc2[mi][i] - m_new) : 0.f;
-          pv[i] = bf16_bits_to_f32(f32_to_bf16_bits(p));
+          pv[i] = f16f(h16(p));
           psum += pv[i];
         }
         const int t = 32 * w + 16 * mi + 4 * (lane >> 4);
@@ -279,7 +295,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
           for (int e = e0; e < e1; ++e) {
             const int t = ridx[e] - (int)row0;
             if (t >= 0 && t < TM)
-              acc = fmaf(bf16_bits_to_f32(Ps[gq * PS_LD + t]), ld_res(rval, (long)e * DH + d, rsc, d), acc);
+              acc = fmaf(f16f(Ps[gq * PS_LD + t]), ld_res(rval, (long)e * DH + d, rsc, d), acc);
           }
           accV[p] = acc;
         }
@@ -294,8 +310,12 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
       for (int fb = 0; fb < NF64; ++fb) {
         for (int c = tid; c < 64 * DH / 8; c += 256) {
           const int f = c / (DH / 8), part = c % (DH / 8);
-          *reinterpret_cast<uint4 *>(W1s + f * W1S_LD + part * 8) =
-              *reinterpret_cast<const uint4 *>(W1 + (long)(fb * 64 + f) * DH + part * 8);
+          const uint4 v = *reinterpret_cast<const uint4 *>(W1 + (long)(fb * 64 + f) * DH + part * 8);
+          const uint32_t *u = reinterpret_cast<const uint32_t *>(&v);
+          uint32_t o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = pack2(bf16_bits_to_f32(u[i] & 0xFFFFu), bf16_bits_to_f32(u[i] >> 16));
+          *reinterpret_cast<uint4 *>(W1s + f * W1S_LD + part * 8) = make_uint4(o[0], o[1], o[2], o[3]);
         }
         __syncthreads();
         f32x16 acc3[2];
@@ -306,10 +326,10 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
 #pragma unroll
         for (int ks = 0; ks < DH / 16; ++ks) {
           const int kof = 16 * ks + 8 * (lane >> 5);
-          const bf16x8 bw = lds8(W1s + (32 * wn + (lane & 31)) * W1S_LD + kof);
+          const f16x8 bw = ldh8(W1s + (32 * wn + (lane & 31)) * W1S_LD + kof);
 #pragma unroll
           for (int mi = 0; mi < 2; ++mi)
-            acc3[mi] = mfma32(lds8(Ks + (64 * wm + 32 * mi + (lane & 31)) * KS_LD + kof), bw, acc3[mi]);
+            acc3[mi] = mfma32(ldh8(Ks + (64 * wm + 32 * mi + (lane & 31)) * KS_LD + kof), bw, acc3[mi]);
         }
         const int fl_ = 32 * wn + (lane & 31);
         const float bias = to_f32(B1[fb * 64 + fl_]);
@@ -327,8 +347,8 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
 #pragma unroll
         for (int ks = 0; ks < TM / 32; ++ks) {
           const int kof = 32 * ks + 8 * (lane >> 4);
-          accH[fb] = mfma16(lds8(Ps + (lane & 15) * PS_LD + kof),
-                            lds8(Hs + (16 * w + (lane & 15)) * HS_LD + kof), accH[fb]);
+          accH[fb] = mfma16(ldh8(Ps + (lane & 15) * PS_LD + kof),
+                            ldh8(Hs + (16 * w + (lane & 15)) * HS_LD + kof), accH[fb]);
         }
       }
       __syncthreads();
