@@ -6,7 +6,9 @@
 
 namespace lowram {
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU with the hardware reciprocal (about 1 ulp); callers round the result
+// to 11 or fewer significant bits
+__device__ __forceinline__ float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 template <typename T> __device__ __forceinline__ float ldf(const T *p, long i) { return to_f32(p[i]); }
 __device__ __forceinline__ float ld_coeff(const float *c, long i, const uint16_t *, int) { return c[i]; }
@@ -48,24 +50,35 @@ __device__ inline void softmax_tile(float *lg, int ld, int nt, int g, float *ms,
 
 // ---------------------------------------------------------------------------
 // Uncompressed tail of one (b, h): dense softmax over T tokens (shared by the
-// VALU and MFMA kernels).  smem: qs[g][dh] floats already loaded; lg scratch
-// [g][TT]; accV [g][dh]; ms/ls/al [g].
+// VALU and MFMA kernels).  qs[g][dh] floats already loaded; lg scratch
+// [g][TT]; accV [g][dh]; ms/ls/al [g]; kv scratch of 2*TT*(dh+1) floats where
+// each tile's keys and values are staged with 16-byte loads.
 // ---------------------------------------------------------------------------
 template <typename TA>
-__device__ void tail_split(const AttendArgs &a, const float *qs, float *lg, int TT, float *accV,
-                           float *ms, float *ls, float *al) {
-  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int g = a.g, dh = a.dh;
+__device__ void tail_split(const AttendArgs &a, int h, int b, const float *qs, float *lg, int TT,
+                           float *accV, float *ms, float *ls, float *al, float *kv) {
+  const int tid = threadIdx.x;
+  const int g = a.g, dh = a.dh, ld = dh + 1;
   const long base = ((((long)b * a.G + a.layer) * a.Hkv + h) * a.T) * dh;
   const TA *kt = reinterpret_cast<const TA *>(a.k_tail) + base;
   const TA *vt = reinterpret_cast<const TA *>(a.v_tail) + base;
+  float *ks = kv, *vs = kv + TT * ld;
+  constexpr int PER = 16 / sizeof(TA);  // elements per 16-byte piece
   for (int t0 = 0; t0 < a.T; t0 += TT) {
     const int nt = min(TT, a.T - t0);
+    for (int pc = tid; pc < nt * dh / PER; pc += 256) {
+      const int t = pc / (dh / PER), d0 = (pc % (dh / PER)) * PER;
+      const u32x4 kr = gld16(kt + (long)(t0 + t) * dh + d0);
+      const u32x4 vr = gld16(vt + (long)(t0 + t) * dh + d0);
+      const TA *ke = reinterpret_cast<const TA *>(&kr), *ve = reinterpret_cast<const TA *>(&vr);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) { ks[t * ld + d0 + j] = to_f32(ke[j]); vs[t * ld + d0 + j] = to_f32(ve[j]); }
+    }
+    __syncthreads();
     for (int idx = tid; idx < g * nt; idx += 256) {
       const int gi = idx / nt, t = idx % nt;
-      const TA *kr = kt + (long)(t0 + t) * dh;
       float s = 0.f;
-      for (int d = 0; d < dh; ++d) s = fmaf(qs[gi * dh + d], ldf(kr, d), s);
+      for (int d = 0; d < dh; ++d) s = fmaf(qs[gi * dh + d], ks[t * ld + d], s);
       lg[gi * TT + t] = s * a.scale_log2;
     }
     __syncthreads();
@@ -74,16 +87,16 @@ __device__ void tail_split(const AttendArgs &a, const float *qs, float *lg, int 
     for (int idx = tid; idx < g * dh; idx += 256) {
       const int gi = idx / dh, d = idx % dh;
       float acc = accV[idx] * al[gi];
-      for (int t = 0; t < nt; ++t) acc = fmaf(lg[gi * TT + t], ldf(vt, (long)(t0 + t) * dh + d), acc);
+      for (int t = 0; t < nt; ++t) acc = fmaf(lg[gi * TT + t], vs[t * ld + d], acc);
       accV[idx] = acc;
     }
     __syncthreads();
   }
 }
 
-__device__ inline void write_partial(const AttendArgs &a, int split, const float *ms,
+__device__ inline void write_partial(const AttendArgs &a, int h, int b, int split, const float *ms,
                                      const float *ls, const float *accH, const float *accV) {
-  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   float *p = a.part + (((long)b * a.Hkv + h) * (a.n_split + 1) + split) * a.g * a.PW;
   for (int gi = 0; gi < a.g; ++gi) {
     float *pg = p + (long)gi * a.PW;

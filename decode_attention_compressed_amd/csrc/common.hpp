@@ -64,6 +64,21 @@ __device__ __forceinline__ void store_f32(float *p, float x) { *p = x; }
 __device__ __forceinline__ void store_f32(bf16 *p, float x) { p->u = f32_to_bf16_bits(x); }
 
 // ---------------------------------------------------------------------------
+// 16-byte payloads as native vectors.  (HIP's uint4/float4 are classes; whole
+// copies of them out of register arrays are lowered through stack memory and
+// serialise the loads.)
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32v4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 gld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void lst16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+__device__ __forceinline__ u32x4 v4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 r;
+  r.x = a; r.y = b; r.z = c; r.w = d;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
 // reductions
 // ---------------------------------------------------------------------------
 template <typename T>

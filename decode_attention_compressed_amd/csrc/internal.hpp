@@ -34,12 +34,13 @@ struct CombineArgs {
 };
 
 // launchers (return hipSuccess or the launch error)
-// sel (if k_eff > 0) receives the selection; sel_out (optional) a copy of it;
-// scores (optional) the float64 chunk scores [B][Hkv][n_c].
+// Chunk scores (float64) into scores [B][Hkv][n_c] (workspace), through the
+// q~ workspace qt [B][Hkv][r]; if k_eff > 0 the selection into sel and,
+// optionally, a copy into sel_out.
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
-                         double *scores, hipStream_t st);
+                         double *scores, double *qt, hipStream_t st);
 hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st);
 hipError_t launch_combine(int act, const CombineArgs &a, hipStream_t st);
 hipError_t launch_dense(int act, const void *q, const void *k, const void *v, long batch_stride,
@@ -71,6 +72,7 @@ struct EvictArgs {
   void *d_coeff; float *d_landmark; int32_t *d_res_ptr, *d_res_idx; void *d_res_val;
   int32_t *keep_out;            // [B][keep]
   double *scores;               // workspace [B][Hkv][n_c]
+  double *qt;                   // workspace [B][Hkv][r]
   double *acc;                  // workspace [B][n_c]
   int B, G, Hq, Hkv, dh, r, N, C, n_res, act, coeff_dt, resid_dt;
 };

@@ -342,8 +342,8 @@ __global__ __launch_bounds__(256) void k_evict_copy(const unsigned char *__restr
                                                     long chunk_bytes, int r) {
   const int jn = blockIdx.x, b = blockIdx.y;
   const int jo = keep_idx[(long)b * keep + jn];
-  const uint4 *src = reinterpret_cast<const uint4 *>(coeff + ((long)b * n_c + jo) * chunk_bytes);
-  uint4 *dst = reinterpret_cast<uint4 *>(d_coeff + ((long)b * keep + jn) * chunk_bytes);
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(coeff + ((long)b * n_c + jo) * chunk_bytes);
+  u32x4 *dst = reinterpret_cast<u32x4 *>(d_coeff + ((long)b * keep + jn) * chunk_bytes);
   for (long i = threadIdx.x; i < chunk_bytes / 16; i += 256) dst[i] = src[i];
   for (int i = threadIdx.x; i < r; i += 256)
     d_lm[((long)b * keep + jn) * r + i] = lm[((long)b * n_c + jo) * r + i];
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256) void k_evict_resid(const int32_t *__restrict__
       const unsigned char *sr = val + (bh * n_res + e) * (long)row_bytes;
       unsigned char *dr = d_val + (bh * n_res + run) * (long)row_bytes;
       for (int i = 0; i < row_bytes; i += 16)
-        *reinterpret_cast<uint4 *>(dr + i) = *reinterpret_cast<const uint4 *>(sr + i);
+        lst16(dr + i, gld16(sr + i));
     }
   }
   if (tid == 0) dp[keep] = part[256];
@@ -488,7 +488,7 @@ hipError_t run_evict(const EvictArgs &a, hipStream_t st) {
                                 ((long)w * a.B * a.G + l) * a.Hq * a.dh * esz;
       hipError_t e = launch_select(a.act, qb, (long)a.G * a.Hq * a.dh, a.basis, a.landmark, a.B,
                                    a.Hq, a.Hkv, a.dh, a.r, n_c, D, l, 0, nullptr, nullptr,
-                                   a.scores, st);
+                                   a.scores, a.qt, st);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(k_evict_accum, dim3((n_c + 255) / 256, a.B), dim3(256), 0, st, a.scores,
                          a.acc, a.Hkv, n_c, (w == 0 && l == 0) ? 1 : 0);

@@ -22,57 +22,131 @@
 namespace lowram {
 
 // ---------------------------------------------------------------------------
-// D1-D3: q~ = U_{l,h}^T sum_g q_g; s_j = q~ . landmark_j (float64); top-k.
-// grid (Hkv, B), 256 threads.  scores (optional) receives s[b][h][n_c].
+// D1-D3 in three wide kernels (the scorer reads the basis slices of all heads
+// and every landmark; spreading it over hundreds of workgroups keeps those
+// reads in flight together):
+//   k_qtilde  q~_{b,h} = U_{l,h}^T sum_{g in group(h)} q_g     (float64)
+//   k_scores  s_{b,h,j} = q~_{b,h} . landmark_{b,j}             (float64)
+//   k_topk    top min(k, n_c) chunks per (b, h) by (s desc, j asc), ascending
+// Each score is one wave's fixed-order reduction of one landmark row, so equal
+// rows give equal scores.
 // ---------------------------------------------------------------------------
+constexpr int QT_I = 64;  // ranks per q~ workgroup
+
+// grid (ceil(r / 64), Hkv, B), 256 threads: 64 ranks x 4 slices of d
 template <typename TA>
-__global__ __launch_bounds__(256) void k_select(const TA *__restrict__ q, long q_bstride,
-                                                const TA *__restrict__ basis,
-                                                const float *__restrict__ landmark, int Hq,
-                                                int Hkv, int dh, int r, int n_c, int D, int layer,
-                                                int k_eff, int32_t *__restrict__ sel,
-                                                int32_t *__restrict__ sel_out,
-                                                double *__restrict__ scores) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  TopkSmem &tk = *reinterpret_cast<TopkSmem *>(smem);
-  double *qsum = reinterpret_cast<double *>(smem + ((sizeof(TopkSmem) + 15) & ~15));
-  double *qt = qsum + dh;
-  double *sc = qt + r;
-  int32_t *sl = reinterpret_cast<int32_t *>(sc + n_c);
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+__global__ __launch_bounds__(256) void k_qtilde(const TA *__restrict__ q, long q_bstride,
+                                                const TA *__restrict__ basis, int Hq, int Hkv,
+                                                int dh, int r, int D, int layer,
+                                                double *__restrict__ qt) {
+  __shared__ double qsum[256];
+  __shared__ double part[4][QT_I];
+  const int i0 = blockIdx.x * QT_I, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int grp = Hq / Hkv;
   const TA *qb = q + (long)b * q_bstride + (long)h * grp * dh;
   for (int d = tid; d < dh; d += 256) {
-    double s = 0.0;
-    for (int gi = 0; gi < grp; ++gi) s += to_f64(qb[gi * dh + d]);
-    qsum[d] = s;
+    double sq = 0.0;
+    for (int gi = 0; gi < grp; ++gi) sq += to_f64(qb[gi * dh + d]);
+    qsum[d] = sq;
   }
   __syncthreads();
   const TA *U = basis + ((long)b * D + (long)(layer * Hkv + h) * dh) * r;
-  for (int i = tid; i < r; i += 256) {
-    double s = 0.0;
-    for (int d = 0; d < dh; ++d) s = fma(to_f64(U[(long)d * r + i]), qsum[d], s);
-    qt[i] = s;
+  const int i = min(i0 + (tid % QT_I), r - 1), sl = tid / QT_I, dps = dh / 4;
+  double acc = 0.0;
+  for (int d0 = 0; d0 < dps; d0 += 16) {
+    float uv[16];  // 16 independent loads in flight
+#pragma unroll
+    for (int u = 0; u < 16; ++u) uv[u] = to_f32(U[(long)(sl * dps + d0 + u) * r + i]);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc = fma((double)uv[u], qsum[sl * dps + d0 + u], acc);
   }
+  part[sl][tid % QT_I] = acc;
+  __syncthreads();
+  if (tid < QT_I && i0 + tid < r)
+    qt[((long)b * Hkv + h) * r + i0 + tid] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+}
+
+constexpr int SC_J = 8;  // chunks per score workgroup
+
+// grid (ceil(n_c / 8), B), 256 threads.  dynamic LDS: q~ of all heads [Hkv][r].
+__global__ __launch_bounds__(256) void k_scores(const double *__restrict__ qt,
+                                                const float *__restrict__ landmark, int Hkv, int r,
+                                                int n_c, double *__restrict__ scores) {
+  extern __shared__ __align__(16) double qs_all[];
+  const int j0 = blockIdx.x * SC_J, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+  for (int e = tid; e < Hkv * r; e += 256) qs_all[e] = qt[(long)b * Hkv * r + e];
   __syncthreads();
   const float *L = landmark + (long)b * n_c * r;
-  for (int j = wave; j < n_c; j += 256 / WAVE) {
-    double s = 0.0;
-    for (int i = lane; i < r; i += WAVE) s = fma((double)L[(long)j * r + i], qt[i], s);
-    s = wave_sum(s);
-    if (lane == 0) sc[j] = s;
+  // wave w handles chunks j0 + w and j0 + w + 4 for every head; landmark
+  // values are loaded eight per lane at a time, unconditionally (clamped)
+  for (int jj = wave; jj < SC_J; jj += 4) {
+    const int j = min(j0 + jj, n_c - 1);
+    double sacc[16];
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) sacc[hh] = 0.0;
+    for (int i0 = 0; i0 < r; i0 += 8 * WAVE) {
+      float lv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) lv[u] = L[(long)j * r + min(i0 + u * WAVE + lane, r - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * WAVE + lane;
+        if (i < r)
+          for (int hh = 0; hh < Hkv; ++hh) sacc[hh] = fma((double)lv[u], qs_all[hh * r + i], sacc[hh]);
+      }
+    }
+    for (int hh = 0; hh < Hkv; ++hh) {
+      const double v = wave_sum(sacc[hh]);
+      if (lane == 0 && j0 + jj < n_c) scores[((long)b * Hkv + hh) * n_c + j0 + jj] = v;
+    }
+  }
+}
+
+constexpr int TK_NT = 1024;
+
+// grid (Hkv, B), 1024 threads.  dynamic LDS: keys [n_c] u64, counts [4][n_c], sel [k].
+__global__ __launch_bounds__(TK_NT) void k_topk(const double *__restrict__ scores, int Hkv, int n_c,
+                                                int k_eff, int32_t *__restrict__ sel,
+                                                int32_t *__restrict__ sel_out) {
+  extern __shared__ __align__(16) unsigned char tsm[];
+  __shared__ TopkSmem tk;
+  uint64_t *key = reinterpret_cast<uint64_t *>(tsm);
+  int32_t *cnt = reinterpret_cast<int32_t *>(key + n_c);
+  int32_t *sl = cnt + 4 * n_c;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const double *sc = scores + ((long)b * Hkv + h) * n_c;
+  for (int j = tid; j < n_c; j += TK_NT) key[j] = f64_order_key(sc[j]);
+  __syncthreads();
+  if (n_c <= TK_NT / 4) {
+    // rank under (score desc, index asc), counted by four threads over
+    // quarters of the chunks; selected iff rank < k
+    {
+      const int j = tid % n_c, qp = tid / n_c;
+      if (qp < 4) {
+        const uint64_t kj = key[j];
+        const int q0 = qp * n_c / 4, q1 = (qp + 1) * n_c / 4;
+        int rank = 0;
+        for (int jj = q0; jj < q1; ++jj) {
+          const uint64_t o = key[jj];
+          rank += (o > kj) || (o == kj && jj < j);
+        }
+        cnt[qp * n_c + j] = rank;
+      }
+    }
+    __syncthreads();
+    bool take = false;
+    if (tid < n_c) take = (cnt[tid] + cnt[n_c + tid] + cnt[2 * n_c + tid] + cnt[3 * n_c + tid]) < k_eff;
+    uint32_t pos, p2, tot, t2;
+    block_exclusive_counts<TK_NT>(take, false, pos, p2, tot, t2, tk);
+    if (take) sl[pos] = tid;
+  } else {
+    block_topk<TK_NT>([&](int i) { return key[i]; }, n_c, k_eff, sl, tk, 0, nullptr);
   }
   __syncthreads();
-  if (scores)
-    for (int j = tid; j < n_c; j += 256) scores[((long)b * Hkv + h) * n_c + j] = sc[j];
-  if (k_eff > 0) {
-    block_topk<256>([&](int i) { return f64_order_key(sc[i]); }, n_c, k_eff, sl, tk, 0, nullptr);
-    __syncthreads();
-    for (int i = tid; i < k_eff; i += 256) {
-      sel[((long)b * Hkv + h) * k_eff + i] = sl[i];
-      if (sel_out) sel_out[((long)b * Hkv + h) * k_eff + i] = sl[i];
-    }
+  for (int i = tid; i < k_eff; i += TK_NT) {
+    sel[((long)b * Hkv + h) * k_eff + i] = sl[i];
+    if (sel_out) sel_out[((long)b * Hkv + h) * k_eff + i] = sl[i];
   }
 }
 
@@ -102,8 +176,8 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
   __syncthreads();
 
   if (split == a.n_split) {
-    tail_split<TA>(a, qs, lg, TT, accV, ms, ls, al);
-    write_partial(a, split, ms, ls, nullptr, accV);
+    tail_split<TA>(a, h, b, qs, lg, TT, accV, ms, ls, al, cb);
+    write_partial(a, h, b, split, ms, ls, nullptr, accV);
     return;
   }
 
@@ -175,67 +249,117 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
       __syncthreads();
     }
   }
-  write_partial(a, split, ms, ls, accH, accV);
+  write_partial(a, h, b, split, ms, ls, accH, accV);
 }
 
 // ---------------------------------------------------------------------------
 // D7: merge the splits of each query head and apply W2 / b2 once.
-// grid (Hq, B), 256 threads.
+// grid (Hq, B), 256 threads.  Split partials pass through LDS in batches of
+// CB splits, every load of a batch issued before any is used; all sums run in
+// a fixed order.
 // ---------------------------------------------------------------------------
+constexpr int CB = 16;
+
 template <typename TA>
 __global__ __launch_bounds__(256) void k_combine(const CombineArgs a) {
   extern __shared__ __align__(16) float csm[];
   const int gq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int h = (gq * a.Hkv) / a.Hq, gi = gq - h * a.g;
-  float *wts = csm;                   // [n_total]
-  float *accH = wts + a.n_total;      // [F]
-  float *red = accH + a.F;            // [8]
+  const int n_out = a.F + a.dh;
+  float *wts = csm;                      // [n_total]
+  float *ls = wts + a.n_total;           // [n_total]
+  float *acc = ls + a.n_total;           // [F + dh]: accH then accV
+  float *red = acc + n_out;              // [8]
+  float *stage = red + 8;                // [CB][n_out]
   const float *p = a.part + ((long)b * a.Hkv + h) * a.n_total * a.g * a.PW + (long)gi * a.PW;
   const long sstride = (long)a.g * a.PW;
-  // global max over splits (exact, order independent)
   float mx = -INFINITY;
-  for (int s = tid; s < a.n_total; s += 256) mx = fmaxf(mx, p[s * sstride]);
+  for (int s = tid; s < a.n_total; s += 256) {
+    const float m = p[s * sstride];
+    wts[s] = m;
+    ls[s] = p[s * sstride + 1];
+    mx = fmaxf(mx, m);
+  }
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  for (int s = tid; s < a.n_total; s += 256) {
-    const float m = p[s * sstride];
-    wts[s] = (m == -INFINITY) ? 0.f : exp2f(m - M);
+  for (int s = tid; s < a.n_total; s += 256) wts[s] = (wts[s] == -INFINITY) ? 0.f : exp2f(wts[s] - M);
+  for (int o = tid; o < n_out; o += 256) acc[o] = 0.f;
+  // 16-byte pieces of one split's [accH | accV] row; threads are laid out as
+  // (split offset, piece) with a power-of-two piece stride (no divisions)
+  const int per_split = n_out / 4;
+  const int pstride = per_split <= 64 ? 64 : (per_split <= 128 ? 128 : 256);
+  const int sub = 256 / pstride, pc = tid % pstride, so = tid / pstride;
+  const int bsz = CB * sub;  // splits per batch: each thread loads CB pieces
+  for (int s0 = 0; s0 < a.n_total; s0 += bsz) {
+    const int nb = min(bsz, a.n_total - s0);
+    __syncthreads();
+    u32x4 v[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {  // all of this thread's loads of the batch in flight together
+      const int sl = min(s0 + so + u * sub, a.n_total - 1);
+      v[u] = gld16(p + sl * sstride + 4 + 4 * min(pc, per_split - 1));
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      if (so + u * sub < nb && pc < per_split) lst16(stage + (so + u * sub) * n_out + 4 * pc, v[u]);
+    __syncthreads();
+    for (int o = tid; o < n_out; o += 256) {
+      const int n_s = o < a.F ? a.n_comp : a.n_total;  // accH only from rebuilt splits
+      float vv = acc[o];
+      for (int u = 0; u < nb; ++u)
+        if (s0 + u < n_s) vv = fmaf(wts[s0 + u], stage[u * n_out + o], vv);
+      acc[o] = vv;
+    }
   }
   __syncthreads();
-  float L = 0.f, mass = 0.f;  // same order in every thread: deterministic
+  float L = 0.f, mass = 0.f;  // same order in every thread
   for (int s = 0; s < a.n_total; ++s) {
-    const float wl = wts[s] * p[s * sstride + 1];
+    const float wl = wts[s] * ls[s];
     L += wl;
     if (s < a.n_comp) mass += wl;
   }
-  for (int f = tid; f < a.F; f += 256) {
-    float acc = 0.f;
-    for (int s = 0; s < a.n_comp; ++s) acc = fmaf(wts[s], p[s * sstride + 4 + f], acc);
-    accH[f] = acc;
-  }
-  __syncthreads();
   const long bh = ((long)b * a.G + a.layer) * a.Hkv + h;
   const bool hoisted = a.F > 0 && a.n_comp > 0;  // W2/b2 only when rebuilt chunks contributed
   const TA *W2 = hoisted ? reinterpret_cast<const TA *>(a.w2) + bh * a.dh * a.F : nullptr;
   const TA *B2 = hoisted ? reinterpret_cast<const TA *>(a.b2) + bh * a.dh : nullptr;
   TA *out = reinterpret_cast<TA *>(a.out) + ((long)b * a.Hq + gq) * a.dh;
   const float invL = 1.0f / L;
-  for (int d = wave; d < a.dh; d += 256 / WAVE) {
-    float s = 0.f;
-    if (hoisted) {
-      for (int f = lane; f < a.F; f += WAVE) s = fmaf(ldf(W2, (long)d * a.F + f), accH[f], s);
-      s = wave_sum(s);
+  // out[d] = (W2[d] . accH + b2[d] mass + accV[d]) / L.  The block splits each
+  // W2 row into tpr contiguous segments; a thread dots its segment with accH
+  // (16-byte loads, eight in flight), the segment sums of a row are added in a
+  // fixed order through LDS.
+  float *rs = stage;  // [256] partial row sums (stage is free now)
+  const int tpr = 256 / a.dh;  // 1, 2 or 4 threads per row
+  const int d = tid / tpr, sg = tid % tpr;
+  float sv = 0.f;
+  if (hoisted) {
+    constexpr int PER = 16 / sizeof(TA);
+    const int seg = a.F / tpr;  // a multiple of 16
+    const TA *wr = W2 + (long)d * a.F + sg * seg;
+    const float *hv = acc + sg * seg;
+    for (int f0 = 0; f0 < seg; f0 += 8 * PER) {
+      u32x4 raw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) raw[u] = gld16(wr + min(f0 + u * PER, seg - PER));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const TA *e = reinterpret_cast<const TA *>(&raw[u]);
+        if (f0 + u * PER < seg)
+#pragma unroll
+          for (int j = 0; j < PER; ++j) sv = fmaf(to_f32(e[j]), hv[f0 + u * PER + j], sv);
+      }
     }
-    if (lane == 0) {
-      float v = s;
-      if (hoisted) v = fmaf(ldf(B2, d), mass, v);
-      for (int sp = 0; sp < a.n_total; ++sp) v = fmaf(wts[sp], p[sp * sstride + 4 + a.F + d], v);
-      store_f32(out + d, v * invL);
-    }
+  }
+  rs[tid] = sv;
+  __syncthreads();
+  if (sg == 0) {
+    float v = 0.f;
+    for (int k = 0; k < tpr; ++k) v += rs[tid + k];
+    if (hoisted) v = fmaf(ldf(B2, d), mass, v);
+    store_f32(out + d, (v + acc[a.F + d]) * invL);
   }
 }
 
@@ -296,30 +420,167 @@ __global__ __launch_bounds__(256) void k_dense(const TA *__restrict__ q, const T
 }
 
 // ---------------------------------------------------------------------------
+// Dense split-K decode attention for bf16 caches on the matrix cores.
+// grid (n_split, Hkv, B), 256 threads; 64-token tiles.  Logits: each wave
+// feeds its 16 tokens' key rows straight from global memory as the A operand
+// of a 16x16x32 bf16 MFMA against the zero-padded queries; values are staged
+// in LDS and reduced on the vector ALUs.  The next tile's keys and values are
+// in flight in registers while the current tile is reduced.
+// ---------------------------------------------------------------------------
+typedef __bf16 dbf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float df32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef u32x4 dvec4;
+
+template <int DH>
+__global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__ q,
+                                                    const uint16_t *__restrict__ k,
+                                                    const uint16_t *__restrict__ v, long bstride,
+                                                    int Hq, int Hkv, int n, int tps, int n_split,
+                                                    float *__restrict__ part, int PW, float scale_log2) {
+  constexpr int TT = 64, VS_LD = DH + 8, NK = DH / 32, NV = TT * DH / 8 / 256;
+  __shared__ __align__(16) uint16_t Vs[TT * VS_LD];
+  __shared__ __align__(16) float Ps[16][TT + 4];
+  __shared__ float red[64], red2[64], ms[16], ls[16], al[16];
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, gi = lane & 15;
+  const int g = Hq / Hkv;
+  const uint16_t *kb = k + (long)b * bstride + (long)h * n * DH;
+  const uint16_t *vb = v + (long)b * bstride + (long)h * n * DH;
+  dbf16x8 qf[NK];
+  {
+    const uint16_t *qr = q + ((long)b * Hq + (long)h * g + gi) * DH;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      u32x4 u = v4(0, 0, 0, 0);
+      if (gi < g) u = gld16(qr + 32 * ks + 8 * (lane >> 4));
+      qf[ks] = __builtin_bit_cast(dbf16x8, u);
+    }
+  }
+  if (tid < 16) { ms[tid] = -INFINITY; ls[tid] = 0.f; al[tid] = 0.f; }
+  // (query head, dim pair) items of the value reduction
+  constexpr int ITEMS = 16 * DH / 2 / 256;
+  float acc0[ITEMS], acc1[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) { acc0[it] = 0.f; acc1[it] = 0.f; }
+  const int t_beg = split * tps, t_end = min(n, t_beg + tps);
+  dvec4 kr[NK], vr[NV];
+  auto fetch = [&](int t0) {
+    // rows past the split's end are clamped to its last row: the loads stay
+    // unconditional, and those rows get p = 0
+    const int t = min(t0 + 16 * w + (lane & 15), t_end - 1);
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+      kr[ks] = *reinterpret_cast<const dvec4 *>(kb + (long)t * DH + 32 * ks + 8 * (lane >> 4));
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int pc = tid + 256 * u, row = pc / (DH / 8), part = pc % (DH / 8);
+      vr[u] = *reinterpret_cast<const dvec4 *>(vb + (long)min(t0 + row, t_end - 1) * DH + part * 8);
+    }
+  };
+  if (t_beg < t_end) fetch(t_beg);
+  __syncthreads();
+  for (int t0 = t_beg; t0 < t_end; t0 += TT) {
+    df32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8, kr[ks]), qf[ks], acc, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int pc = tid + 256 * u, row = pc / (DH / 8), part = pc % (DH / 8);
+      *reinterpret_cast<dvec4 *>(Vs + row * VS_LD + part * 8) = vr[u];
+    }
+    if (t0 + TT < t_end) fetch(t0 + TT);
+    float mx = -INFINITY;
+    float lg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * w + 4 * (lane >> 4) + i;
+      lg[i] = t < t_end ? acc[i] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, lg[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (lane < 16) red[w * 16 + gi] = mx;
+    __syncthreads();
+    const float m_old = ms[gi];
+    const float m_new = fmaxf(m_old, fmaxf(fmaxf(red[gi], red[16 + gi]), fmaxf(red[32 + gi], red[48 + gi])));
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = (gi < g && lg[i] != -INFINITY) ? exp2f(lg[i] - m_new) : 0.f;
+      Ps[gi][16 * w + 4 * (lane >> 4) + i] = p;
+      psum += p;
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    if (lane < 16) red2[w * 16 + gi] = psum;
+    __syncthreads();
+    if (tid < 16) {
+      const float alpha = (m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new);
+      al[tid] = alpha;
+      ls[tid] = ls[tid] * alpha + ((red2[tid] + red2[16 + tid]) + (red2[32 + tid] + red2[48 + tid]));
+      ms[tid] = m_new;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int item = tid + 256 * it, gq = item / (DH / 2), d2 = item % (DH / 2);
+      if (gq < g) {
+        float s0 = acc0[it] * al[gq], s1 = acc1[it] * al[gq];
+#pragma unroll 8
+        for (int t = 0; t < TT; ++t) {
+          const uint32_t vv = *reinterpret_cast<const uint32_t *>(Vs + t * VS_LD + 2 * d2);
+          const float p = Ps[gq][t];
+          s0 = fmaf(p, bf16_bits_to_f32(vv & 0xFFFFu), s0);
+          s1 = fmaf(p, bf16_bits_to_f32(vv >> 16), s1);
+        }
+        acc0[it] = s0;
+        acc1[it] = s1;
+      }
+    }
+    __syncthreads();
+  }
+  float *pp = part + (((long)b * Hkv + h) * n_split + split) * g * PW;
+  if (tid < g) { pp[tid * PW] = ms[tid]; pp[tid * PW + 1] = ls[tid]; pp[tid * PW + 2] = 0.f; pp[tid * PW + 3] = 0.f; }
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int item = tid + 256 * it, gq = item / (DH / 2), d2 = item % (DH / 2);
+    if (gq < g) { pp[gq * PW + 4 + 2 * d2] = acc0[it]; pp[gq * PW + 4 + 2 * d2 + 1] = acc1[it]; }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
-                         double *scores, hipStream_t st) {
-  const size_t smem = ((sizeof(TopkSmem) + 15) & ~size_t(15)) + sizeof(double) * (dh + r + n_c) +
-                      sizeof(int32_t) * (k_eff > 0 ? k_eff : 0);
-  dim3 grid(Hkv, B);
-  allow_dynamic_lds(act == LOWRAM_F32 ? (const void *)k_select<float> : (const void *)k_select<bf16>, smem);
+                         double *scores, double *qt, hipStream_t st) {
+  dim3 g1((r + QT_I - 1) / QT_I, Hkv, B);
   if (act == LOWRAM_F32)
-    hipLaunchKernelGGL(k_select<float>, grid, dim3(256), smem, st, (const float *)q, q_bstride,
-                       (const float *)basis, landmark, Hq, Hkv, dh, r, n_c, D, layer, k_eff, sel,
-                       sel_out, scores);
+    hipLaunchKernelGGL(k_qtilde<float>, g1, dim3(256), 0, st, (const float *)q, q_bstride,
+                       (const float *)basis, Hq, Hkv, dh, r, D, layer, qt);
   else
-    hipLaunchKernelGGL(k_select<bf16>, grid, dim3(256), smem, st, (const bf16 *)q, q_bstride,
-                       (const bf16 *)basis, landmark, Hq, Hkv, dh, r, n_c, D, layer, k_eff, sel,
-                       sel_out, scores);
+    hipLaunchKernelGGL(k_qtilde<bf16>, g1, dim3(256), 0, st, (const bf16 *)q, q_bstride,
+                       (const bf16 *)basis, Hq, Hkv, dh, r, D, layer, qt);
+  const size_t sm2 = sizeof(double) * (size_t)Hkv * r;
+  allow_dynamic_lds(k_scores, sm2);
+  hipLaunchKernelGGL(k_scores, dim3((n_c + SC_J - 1) / SC_J, B), dim3(256), sm2, st, qt, landmark,
+                     Hkv, r, n_c, scores);
+  if (k_eff > 0) {
+    const size_t sm3 = (size_t)n_c * (8 + 16) + sizeof(int32_t) * (size_t)k_eff;
+    allow_dynamic_lds(k_topk, sm3);
+    hipLaunchKernelGGL(k_topk, dim3(Hkv, B), dim3(TK_NT), sm3, st, scores, Hkv, n_c, k_eff, sel,
+                       sel_out);
+  }
   return hipGetLastError();
 }
 
 size_t valu_smem_bytes(int g, int dh, int r, int F, int TT) {
+  // the tail split reuses the tile region for 2*TT*(dh+1) floats of keys/values
+  const size_t tile = (size_t)TT * (r + dh + F), tail = (size_t)2 * TT * (dh + 1);
   return sizeof(float) * ((size_t)2 * g * dh + (size_t)g * F + 48 + (size_t)g * TT +
-                          (size_t)TT * (r + dh + F));
+                          (tile > tail ? tile : tail));
 }
 
 int valu_tile(int g, int dh, int r, int F) {
@@ -347,8 +608,13 @@ hipError_t launch_attend_valu(int act, int coeff, int resid, const AttendArgs &a
 }
 
 hipError_t launch_combine(int act, const CombineArgs &a, hipStream_t st) {
-  const size_t smem = sizeof(float) * ((size_t)a.n_total + a.F + 8);
+  // stage: CB * sub splits of (F + dh) floats, sub = 256 / (piece stride) <= 1024 / (F + dh)
+  const int n_out = a.F + a.dh, per = n_out / 4;
+  const int sub = 256 / (per <= 64 ? 64 : (per <= 128 ? 128 : 256));
+  const size_t stage = (size_t)CB * sub * n_out > 256 ? (size_t)CB * sub * n_out : 256;
+  const size_t smem = sizeof(float) * ((size_t)2 * a.n_total + n_out + 8 + stage);
   dim3 grid(a.Hq, a.B);
+  allow_dynamic_lds(act == LOWRAM_F32 ? (const void *)k_combine<float> : (const void *)k_combine<bf16>, smem);
   if (act == LOWRAM_F32)
     hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), smem, st, a);
   else
@@ -366,6 +632,14 @@ hipError_t launch_dense(int act, const void *q, const void *k, const void *v, lo
   if (act == LOWRAM_F32)
     hipLaunchKernelGGL(k_dense<float>, grid, dim3(256), smem, st, (const float *)q,
                        (const float *)k, (const float *)v, batch_stride, Hq, Hkv, dh, n, tps,
+                       n_split, part, PW, sl);
+  else if (dh == 128)
+    hipLaunchKernelGGL(k_dense_mfma<128>, grid, dim3(256), 0, st, (const uint16_t *)q,
+                       (const uint16_t *)k, (const uint16_t *)v, batch_stride, Hq, Hkv, n, tps,
+                       n_split, part, PW, sl);
+  else if (dh == 256)
+    hipLaunchKernelGGL(k_dense_mfma<256>, grid, dim3(256), 0, st, (const uint16_t *)q,
+                       (const uint16_t *)k, (const uint16_t *)v, batch_stride, Hq, Hkv, n, tps,
                        n_split, part, PW, sl);
   else
     hipLaunchKernelGGL(k_dense<bf16>, grid, dim3(256), smem, st, (const bf16 *)q, (const bf16 *)k,

@@ -44,6 +44,7 @@ lowram_status check_dims(const lowram_dims *d) {
     return fail(LOWRAM_E_INVALID, "heads_q (%d) must be a multiple of heads_kv (%d)", d->heads_q, d->heads_kv);
   if (d->heads_q / d->heads_kv > 16)
     return fail(LOWRAM_E_UNSUPPORTED, "at most 16 query heads per kv head");
+  if (d->heads_kv > 16) return fail(LOWRAM_E_UNSUPPORTED, "at most 16 kv heads per layer");
   if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
     return fail(LOWRAM_E_UNSUPPORTED, "head_dim %d: supported 64, 128, 256", d->head_dim);
   const long D = (long)d->layers * d->heads_kv * d->head_dim;
@@ -74,7 +75,7 @@ lowram_status check_dims(const lowram_dims *d) {
 
 struct DecodePlan {
   int k_eff, cps, n_split, PW;
-  size_t sel_off, part_off, bytes;
+  size_t sel_off, qt_off, sc_off, part_off, bytes;
 };
 
 DecodePlan decode_plan(const lowram_dims *d) {
@@ -86,7 +87,9 @@ DecodePlan decode_plan(const lowram_dims *d) {
   p.PW = 4 + d->hidden + d->head_dim;
   const int g = d->heads_q / d->heads_kv;
   p.sel_off = 0;
-  p.part_off = align_up(sizeof(int32_t) * (size_t)d->batch * d->heads_kv * (p.k_eff > 0 ? p.k_eff : 1));
+  p.qt_off = align_up(sizeof(int32_t) * (size_t)d->batch * d->heads_kv * (p.k_eff > 0 ? p.k_eff : 1));
+  p.sc_off = p.qt_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * d->rank);
+  p.part_off = p.sc_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * (n_c > 0 ? n_c : 1));
   p.bytes = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * (p.n_split + 1) * g * p.PW);
   return p;
 }
@@ -106,14 +109,15 @@ CompressPlan compress_plan(const lowram_dims *d) {
 }
 
 struct EvictPlan {
-  size_t scores_off, acc_off, keep_off, bytes;
+  size_t scores_off, qt_off, acc_off, keep_off, bytes;
 };
 
 EvictPlan evict_plan(const lowram_dims *d) {
   EvictPlan p;
   const size_t n_c = (size_t)(n_chunks(d) > 0 ? n_chunks(d) : 1);
   p.scores_off = 0;
-  p.acc_off = align_up(sizeof(double) * d->batch * d->heads_kv * n_c);
+  p.qt_off = align_up(sizeof(double) * d->batch * d->heads_kv * n_c);
+  p.acc_off = p.qt_off + align_up(sizeof(double) * d->batch * d->heads_kv * d->rank);
   p.keep_off = p.acc_off + align_up(sizeof(double) * d->batch * n_c);
   p.bytes = p.keep_off + align_up(sizeof(int32_t) * d->batch * n_c);
   return p;
@@ -298,9 +302,11 @@ lowram_status lowram_decode_select(const lowram_dims *d, int32_t layer, const lo
   if (p.k_eff == 0) return LOWRAM_OK;
   const long D = (long)d->layers * d->heads_kv * d->head_dim;
   int32_t *sel = reinterpret_cast<int32_t *>((char *)ws + p.sel_off);
+  double *qt = reinterpret_cast<double *>((char *)ws + p.qt_off);
+  double *sc = reinterpret_cast<double *>((char *)ws + p.sc_off);
   return hip_status(launch_select(d->act, q, (long)d->heads_q * d->head_dim, m->basis, c->landmark,
                                   d->batch, d->heads_q, d->heads_kv, d->head_dim, d->rank,
-                                  n_chunks(d), (int)D, layer, p.k_eff, sel, sel_out, nullptr,
+                                  n_chunks(d), (int)D, layer, p.k_eff, sel, sel_out, sc, qt,
                                   (hipStream_t)stream),
                     "lowram_decode_select");
 }
@@ -396,6 +402,7 @@ lowram_status lowram_evict(const lowram_dims *d, const lowram_model *m, const lo
   a.d_res_idx = dst->res_idx; a.d_res_val = dst->res_val;
   a.keep_out = keep_out ? keep_out : reinterpret_cast<int32_t *>((char *)ws + p.keep_off);
   a.scores = reinterpret_cast<double *>((char *)ws + p.scores_off);
+  a.qt = reinterpret_cast<double *>((char *)ws + p.qt_off);
   a.acc = reinterpret_cast<double *>((char *)ws + p.acc_off);
   a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
   a.r = d->rank; a.N = d->n_ctx; a.C = d->chunk; a.n_res = d->n_res;
