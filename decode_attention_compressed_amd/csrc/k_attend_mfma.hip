@@ -42,6 +42,11 @@ constexpr int PAD = 8;    // fp16/bf16 pad per LDS row (16-byte rows, spread ban
 constexpr int PF = 3;     // rank slabs in flight in registers (at most)
 constexpr int CS_LD = RS + PAD, HS_LD = TM + PAD, PS_LD = TM + PAD;
 
+// Two workgroups share a CU when the (head dim, hidden) pair leaves room in
+// 256 registers per lane: one group's loads then run under the other's matrix
+// work.  Larger shapes keep one group per CU, deeper register rings instead.
+template <int DH, int NF64> constexpr bool dual_occupancy() { return DH == 128 && NF64 <= 4; }
+
 // compile-time loop: f(std::integral_constant<int, I>) for I = 0..N-1
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for_impl(F &f) {
@@ -239,7 +244,8 @@ __device__ __forceinline__ void block_coords(const AttendArgs &a, int &h, int &b
 }
 
 template <int DH, int NF64, int NSLAB, typename TC, typename TR>
-__global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
+__global__ __launch_bounds__(256, (dual_occupancy<DH, NF64>() ? 2 : 1)) void k_attend_mfma(const AttendArgs a) {
+  constexpr bool OCC2 = dual_occupancy<DH, NF64>();
   using S = MfmaSmem<DH>;
   constexpr int KS_LD = S::KS_LD;
   constexpr int NT1 = DH / 64;        // 32-row d tiles per wave in step 1
@@ -321,22 +327,25 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
       // ring of PFD slabs in flight, PFD-1 ahead of the one being multiplied
       int e0, e1, rt = -1;
       u32x4 rv = v4(0, 0, 0, 0);
+      auto res_head = [&]() {
+        e0 = rptr[j];
+        e1 = rptr[j + 1];
+        const int e = e0 + tid / RPR;
+        if (e < e1) {
+          rt = ridx[e] - (int)row0;
+          rv = gld16(rval + (long)e * DH + (tid % RPR) * ResRow<TR>::VALS);
+        }
+      };
       {
         using ST = SlabT<DH, TC>;
-        constexpr int PFD = NSLAB < (DH > 128 ? 2 : PF) ? NSLAB : (DH > 128 ? 2 : PF);
+        constexpr int PFD_MAX = OCC2 ? 2 : (DH > 128 ? 2 : PF);
+        constexpr int PFD = NSLAB < PFD_MAX ? NSLAB : PFD_MAX;
         u32x4 rc[PFD][ST::NC], ru[PFD][ST::NU], rs[PFD][ST::NS > 0 ? ST::NS : 1];
 #pragma unroll
         for (int u = 0; u < PFD - 1; ++u) slab_fetch<DH>(cf, csc, U, row0, r, u * RS, rc[u], ru[u], rs[u]);
         // this chunk's residual rows: CSR range, then the first round of pieces
-        e0 = rptr[j];
-        e1 = rptr[j + 1];
-        {
-          const int e = e0 + tid / RPR;
-          if (e < e1) {
-            rt = ridx[e] - (int)row0;
-            rv = gld16(rval + (long)e * DH + (tid % RPR) * ResRow<TR>::VALS);
-          }
-        }
+        // (after step 1 instead when registers are tight)
+        if constexpr (!OCC2) res_head();
         static_for<NSLAB>([&](auto sc_) {
           constexpr int s = decltype(sc_)::value;
           constexpr int cur_slot = s % PFD, next_slot = (s + PFD - 1) % PFD;
@@ -344,31 +353,49 @@ __global__ __launch_bounds__(256) void k_attend_mfma(const AttendArgs a) {
           __syncthreads();
           if constexpr (s + PFD - 1 < NSLAB)
             slab_fetch<DH>(cf, csc, U, row0, r, (s + PFD - 1) * RS, rc[next_slot], ru[next_slot], rs[next_slot]);
-          typename ST::frag bc[2][2], au[2][NT1];
+          if constexpr (OCC2) {  // the other workgroup covers LDS latency
 #pragma unroll
-          for (int ni = 0; ni < 2; ++ni) bc[0][ni] = ST::ld(Cs + (64 * wn + 32 * ni + (lane & 31)) * CS_LD + 8 * (lane >> 5));
+            for (int ks = 0; ks < RS / 16; ++ks) {
+              const int kof = 16 * ks + 8 * (lane >> 5);
+              typename ST::frag bc[2], au[NT1];
 #pragma unroll
-          for (int mi = 0; mi < NT1; ++mi) au[0][mi] = ST::ld(Us + (wm * (DH / 2) + 32 * mi + (lane & 31)) * CS_LD + 8 * (lane >> 5));
+              for (int ni = 0; ni < 2; ++ni) bc[ni] = ST::ld(Cs + (64 * wn + 32 * ni + (lane & 31)) * CS_LD + kof);
 #pragma unroll
-          for (int ks = 0; ks < RS / 16; ++ks) {
-            const int cur = ks & 1, nxt = cur ^ 1;
-            if (ks + 1 < RS / 16) {  // next k-step's fragments in flight under this k-step's MFMAs
-              const int kof = 16 * (ks + 1) + 8 * (lane >> 5);
+              for (int mi = 0; mi < NT1; ++mi) au[mi] = ST::ld(Us + (wm * (DH / 2) + 32 * mi + (lane & 31)) * CS_LD + kof);
 #pragma unroll
-              for (int ni = 0; ni < 2; ++ni) bc[nxt][ni] = ST::ld(Cs + (64 * wn + 32 * ni + (lane & 31)) * CS_LD + kof);
+              for (int mi = 0; mi < NT1; ++mi)
 #pragma unroll
-              for (int mi = 0; mi < NT1; ++mi) au[nxt][mi] = ST::ld(Us + (wm * (DH / 2) + 32 * mi + (lane & 31)) * CS_LD + kof);
+                for (int ni = 0; ni < 2; ++ni) acc1[mi][ni] = mfma32(au[mi], bc[ni], acc1[mi][ni]);
             }
-#pragma unroll
-            for (int mi = 0; mi < NT1; ++mi)
-#pragma unroll
-              for (int ni = 0; ni < 2; ++ni) acc1[mi][ni] = mfma32(au[cur][mi], bc[cur][ni], acc1[mi][ni]);
+          } else {
+            typename ST::frag bc[2][2], au[2][NT1];
+  #pragma unroll
+            for (int ni = 0; ni < 2; ++ni) bc[0][ni] = ST::ld(Cs + (64 * wn + 32 * ni + (lane & 31)) * CS_LD + 8 * (lane >> 5));
+  #pragma unroll
+            for (int mi = 0; mi < NT1; ++mi) au[0][mi] = ST::ld(Us + (wm * (DH / 2) + 32 * mi + (lane & 31)) * CS_LD + 8 * (lane >> 5));
+  #pragma unroll
+            for (int ks = 0; ks < RS / 16; ++ks) {
+              const int cur = ks & 1, nxt = cur ^ 1;
+              if (ks + 1 < RS / 16) {  // next k-step's fragments in flight under this k-step's MFMAs
+                const int kof = 16 * (ks + 1) + 8 * (lane >> 5);
+  #pragma unroll
+                for (int ni = 0; ni < 2; ++ni) bc[nxt][ni] = ST::ld(Cs + (64 * wn + 32 * ni + (lane & 31)) * CS_LD + kof);
+  #pragma unroll
+                for (int mi = 0; mi < NT1; ++mi) au[nxt][mi] = ST::ld(Us + (wm * (DH / 2) + 32 * mi + (lane & 31)) * CS_LD + kof);
+              }
+  #pragma unroll
+              for (int mi = 0; mi < NT1; ++mi)
+  #pragma unroll
+                for (int ni = 0; ni < 2; ++ni) acc1[mi][ni] = mfma32(au[cur][mi], bc[cur][ni], acc1[mi][ni]);
+            }
           }
           __syncthreads();
         });
       }
+      if constexpr (OCC2) res_head();
       // the first WD blocks of W1 go in flight behind steps 2 and 5
-      constexpr int WD = (16 / W1P) < NF64 ? (16 / W1P) : NF64;
+      constexpr int WD_MAX = OCC2 ? 1 : 16 / W1P;
+      constexpr int WD = WD_MAX < NF64 ? WD_MAX : NF64;
       u32x4 w1r[WD][W1P];
       static_for<WD>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
