@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches (for counter runs)")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB three times: a kernel of known "
+                         "traffic that scales hardware byte counters")
     return ap.parse_args()
 
 
@@ -180,6 +184,8 @@ def main():
     # ---- timed region: K steps captured in one HIP graph -------------------
     graph = None
     try:
+        if args.no_graph:
+            raise RuntimeError("disabled by --no-graph")
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(args.steps):
@@ -272,6 +278,15 @@ def main():
         host = cache_to_host(cache)
         cpu = cpu_baseline(s, host, inp, args.cpu_seconds)
         log(f"cpu oracle {cpu['value']:.3f} seq-steps/s on {cpu['cores']} threads")
+
+    if args.copy_ref_mib:
+        src = torch.ones((args.copy_ref_mib << 20) // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):  # an elementwise kernel: reads and writes the buffer once each
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy reference: 3 x {args.copy_ref_mib} MiB")
+        del src, dst
 
     step_b = step_bytes(s, a_bytes) * s.G
     result = {

@@ -95,8 +95,9 @@ __device__ __forceinline__ T wave_max(T v) {
 }
 
 // order-preserving map of a float64 to uint64 (larger double -> larger key)
+// (-0.0 is mapped to +0.0 first, so the two compare equal as doubles do)
 __device__ __forceinline__ uint64_t f64_order_key(double x) {
-  uint64_t u = (uint64_t)__double_as_longlong(x);
+  uint64_t u = (uint64_t)__double_as_longlong(x + 0.0);
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 

@@ -28,125 +28,203 @@ namespace lowram {
 //   k_qtilde  q~_{b,h} = U_{l,h}^T sum_{g in group(h)} q_g     (float64)
 //   k_scores  s_{b,h,j} = q~_{b,h} . landmark_{b,j}             (float64)
 //   k_topk    top min(k, n_c) chunks per (b, h) by (s desc, j asc), ascending
-// Each score is one wave's fixed-order reduction of one landmark row, so equal
-// rows give equal scores.
+// Every score is reduced in the same fixed order (lane partials, then a
+// butterfly), so equal landmark rows give equal scores.
 // ---------------------------------------------------------------------------
 constexpr int QT_I = 64;  // ranks per q~ workgroup
 
-// grid (ceil(r / 64), Hkv, B), 256 threads: 64 ranks x 4 slices of d
-template <typename TA>
+// grid (ceil(r / 64), Hkv, B), 256 threads: 8 groups of 8 ranks x 32 row
+// slices; slice s sums rows s, s + 32, ... in order, then the slices are added
+// in slice order.
+template <typename TA> struct Load8;
+template <> struct Load8<bf16> {
+  typedef u32x4 raw;
+  static constexpr int N = 1;
+  __device__ static void ld(const bf16 *p, raw *v) { v[0] = gld16(p); }
+  __device__ static void f64(const raw *v, double *o) {
+    const uint32_t w[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = (double)bf16_bits_to_f32(w[i] & 0xFFFFu);
+      o[2 * i + 1] = (double)bf16_bits_to_f32(w[i] >> 16);
+    }
+  }
+};
+template <> struct Load8<float> {
+  typedef u32x4 raw;
+  static constexpr int N = 2;
+  __device__ static void ld(const float *p, raw *v) { v[0] = gld16(p); v[1] = gld16(p + 4); }
+  __device__ static void f64(const raw *v, double *o) {
+    const uint32_t w[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (double)__uint_as_float(w[i]);
+  }
+};
+
+template <typename TA, int DH>
 __global__ __launch_bounds__(256) void k_qtilde(const TA *__restrict__ q, long q_bstride,
-                                                const TA *__restrict__ basis, int Hq, int Hkv,
-                                                int dh, int r, int D, int layer,
-                                                double *__restrict__ qt) {
-  __shared__ double qsum[256];
-  __shared__ double part[4][QT_I];
+                                                const TA *__restrict__ basis, int Hq, int Hkv, int r,
+                                                int D, int layer, double *__restrict__ qt) {
+  constexpr int RPS = DH / 32;  // rows per slice
+  __shared__ double qsum[DH];
+  __shared__ double part[32][QT_I];
   const int i0 = blockIdx.x * QT_I, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int grp = Hq / Hkv;
-  const TA *qb = q + (long)b * q_bstride + (long)h * grp * dh;
-  for (int d = tid; d < dh; d += 256) {
+  const int rg = tid % 8, slc = tid / 8;
+  const int ib = i0 + 8 * rg;             // first rank of this thread
+  const int ic = ib < r ? ib : r - 8;     // clamped (r is a multiple of 16)
+  const TA *U = basis + ((long)b * D + (long)(layer * Hkv + h) * DH) * r;
+  typename Load8<TA>::raw raw[RPS][Load8<TA>::N];
+#pragma unroll
+  for (int k = 0; k < RPS; ++k) Load8<TA>::ld(U + (long)(slc + 32 * k) * r + ic, raw[k]);
+  if (tid < DH) {
+    const int grp = Hq / Hkv;
+    const TA *qb = q + (long)b * q_bstride + (long)h * grp * DH;
     double sq = 0.0;
-    for (int gi = 0; gi < grp; ++gi) sq += to_f64(qb[gi * dh + d]);
-    qsum[d] = sq;
+    for (int gi = 0; gi < grp; ++gi) sq += to_f64(qb[gi * DH + tid]);
+    qsum[tid] = sq;
   }
   __syncthreads();
-  const TA *U = basis + ((long)b * D + (long)(layer * Hkv + h) * dh) * r;
-  const int i = min(i0 + (tid % QT_I), r - 1), sl = tid / QT_I, dps = dh / 4;
-  double acc = 0.0;
-  for (int d0 = 0; d0 < dps; d0 += 16) {
-    float uv[16];  // 16 independent loads in flight
+  double acc[8];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) uv[u] = to_f32(U[(long)(sl * dps + d0 + u) * r + i]);
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) acc = fma((double)uv[u], qsum[sl * dps + d0 + u], acc);
+  for (int k = 0; k < RPS; ++k) {
+    double u[8];
+    Load8<TA>::f64(raw[k], u);
+    const double w = qsum[slc + 32 * k];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fma(u[e], w, acc[e]);
   }
-  part[sl][tid % QT_I] = acc;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[slc][8 * rg + e] = acc[e];
   __syncthreads();
-  if (tid < QT_I && i0 + tid < r)
-    qt[((long)b * Hkv + h) * r + i0 + tid] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+  if (tid < QT_I && i0 + tid < r) {
+    double v = 0.0;
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) v += part[k][tid];
+    qt[((long)b * Hkv + h) * r + i0 + tid] = v;
+  }
 }
 
-constexpr int SC_J = 8;  // chunks per score workgroup
+constexpr int SC_J = 32;  // chunks per score workgroup (8 per wave)
 
-// grid (ceil(n_c / 8), B), 256 threads.  dynamic LDS: q~ of all heads [Hkv][r].
+// grid (ceil(n_c / 32), Hkv, B), 256 threads.  Lane l of a wave holds ranks
+// 256u + 4l .. +3 (u < NSEG) of q~; a wave scores one landmark row at a time
+// with RF rows in flight.  The blocks are regrouped so that every head of one
+// (sequence, chunk block) runs on the same XCD and shares its L2 copy of
+// those landmark rows.
+template <int NSEG>
 __global__ __launch_bounds__(256) void k_scores(const double *__restrict__ qt,
                                                 const float *__restrict__ landmark, int Hkv, int r,
                                                 int n_c, double *__restrict__ scores) {
-  extern __shared__ __align__(16) double qs_all[];
-  const int j0 = blockIdx.x * SC_J, b = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
-  for (int e = tid; e < Hkv * r; e += 256) qs_all[e] = qt[(long)b * Hkv * r + e];
-  __syncthreads();
-  const float *L = landmark + (long)b * n_c * r;
-  // wave w handles chunks j0 + w and j0 + w + 4 for every head; landmark
-  // values are loaded eight per lane at a time, unconditionally (clamped)
-  for (int jj = wave; jj < SC_J; jj += 4) {
-    const int j = min(j0 + jj, n_c - 1);
-    double sacc[16];
-#pragma unroll
-    for (int hh = 0; hh < 16; ++hh) sacc[hh] = 0.0;
-    for (int i0 = 0; i0 < r; i0 += 8 * WAVE) {
-      float lv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) lv[u] = L[(long)j * r + min(i0 + u * WAVE + lane, r - 1)];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * WAVE + lane;
-        if (i < r)
-          for (int hh = 0; hh < Hkv; ++hh) sacc[hh] = fma((double)lv[u], qs_all[hh * r + i], sacc[hh]);
-      }
+  constexpr int RF = NSEG <= 2 ? 8 : (NSEG == 4 ? 4 : 2);
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
+  int blk, h, b;
+  {
+    const int NB = gridDim.x, P = NB * gridDim.z;  // (sequence, chunk block) pairs
+    const int lin = blockIdx.x + NB * (blockIdx.y + Hkv * blockIdx.z);
+    if (P % 8 == 0) {
+      const int xcd = lin % 8, i = lin / 8, pr = xcd * (P / 8) + i / Hkv;
+      h = i % Hkv; b = pr / NB; blk = pr % NB;
+    } else {
+      blk = blockIdx.x; h = blockIdx.y; b = blockIdx.z;
     }
-    for (int hh = 0; hh < Hkv; ++hh) {
-      const double v = wave_sum(sacc[hh]);
-      if (lane == 0 && j0 + jj < n_c) scores[((long)b * Hkv + hh) * n_c + j0 + jj] = v;
+  }
+  double qv[NSEG][4];
+  int ioff[NSEG];
+  const double *qb = qt + ((long)b * Hkv + h) * r;
+#pragma unroll
+  for (int u = 0; u < NSEG; ++u) {
+    const int i = 256 * u + 4 * lane;
+    ioff[u] = i < r ? i : r - 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qv[u][e] = i < r ? qb[i + e] : 0.0;
+  }
+  const float *L = landmark + (long)b * n_c * r;
+  const int j0 = blk * SC_J + wv;
+#pragma unroll
+  for (int t0 = 0; t0 < SC_J / 4; t0 += RF) {
+    u32x4 lv[RF][NSEG];
+#pragma unroll
+    for (int t = 0; t < RF; ++t) {
+      const int j = min(j0 + 4 * (t0 + t), n_c - 1);
+#pragma unroll
+      for (int u = 0; u < NSEG; ++u) lv[t][u] = gld16(L + (long)j * r + ioff[u]);
+    }
+#pragma unroll
+    for (int t = 0; t < RF; ++t) {
+      double sacc = 0.0;
+#pragma unroll
+      for (int u = 0; u < NSEG; ++u) {
+        const uint32_t w4[4] = {lv[t][u].x, lv[t][u].y, lv[t][u].z, lv[t][u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc = fma((double)__uint_as_float(w4[e]), qv[u][e], sacc);
+      }
+      sacc = wave_sum(sacc);
+      const int j = j0 + 4 * (t0 + t);
+      if (lane == 0 && j < n_c) scores[((long)b * Hkv + h) * n_c + j] = sacc;
     }
   }
 }
 
 constexpr int TK_NT = 1024;
 
-// grid (Hkv, B), 1024 threads.  dynamic LDS: keys [n_c] u64, counts [4][n_c], sel [k].
+// grid (Hkv, B), 1024 threads, any n_c.  dynamic LDS: keys [n_c] u64, sel [k].
 __global__ __launch_bounds__(TK_NT) void k_topk(const double *__restrict__ scores, int Hkv, int n_c,
                                                 int k_eff, int32_t *__restrict__ sel,
                                                 int32_t *__restrict__ sel_out) {
   extern __shared__ __align__(16) unsigned char tsm[];
   __shared__ TopkSmem tk;
   uint64_t *key = reinterpret_cast<uint64_t *>(tsm);
-  int32_t *cnt = reinterpret_cast<int32_t *>(key + n_c);
-  int32_t *sl = cnt + 4 * n_c;
+  int32_t *sl = reinterpret_cast<int32_t *>(key + n_c);
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const double *sc = scores + ((long)b * Hkv + h) * n_c;
   for (int j = tid; j < n_c; j += TK_NT) key[j] = f64_order_key(sc[j]);
   __syncthreads();
-  if (n_c <= TK_NT / 4) {
-    // rank under (score desc, index asc), counted by four threads over
-    // quarters of the chunks; selected iff rank < k
-    {
-      const int j = tid % n_c, qp = tid / n_c;
-      if (qp < 4) {
-        const uint64_t kj = key[j];
-        const int q0 = qp * n_c / 4, q1 = (qp + 1) * n_c / 4;
-        int rank = 0;
-        for (int jj = q0; jj < q1; ++jj) {
-          const uint64_t o = key[jj];
-          rank += (o > kj) || (o == kj && jj < j);
-        }
-        cnt[qp * n_c + j] = rank;
-      }
-    }
-    __syncthreads();
-    bool take = false;
-    if (tid < n_c) take = (cnt[tid] + cnt[n_c + tid] + cnt[2 * n_c + tid] + cnt[3 * n_c + tid]) < k_eff;
-    uint32_t pos, p2, tot, t2;
-    block_exclusive_counts<TK_NT>(take, false, pos, p2, tot, t2, tk);
-    if (take) sl[pos] = tid;
-  } else {
-    block_topk<TK_NT>([&](int i) { return key[i]; }, n_c, k_eff, sl, tk, 0, nullptr);
-  }
+  block_topk<TK_NT>([&](int i) { return key[i]; }, n_c, k_eff, sl, tk, 0, nullptr);
   __syncthreads();
   for (int i = tid; i < k_eff; i += TK_NT) {
     sel[((long)b * Hkv + h) * k_eff + i] = sl[i];
     if (sel_out) sel_out[((long)b * Hkv + h) * k_eff + i] = sl[i];
+  }
+}
+
+// grid (Hkv, B), 1024 threads, n_c <= 256: four threads per chunk j each
+// count, over a quarter of the chunks, those ranked above j (higher score, or
+// equal score and lower index); j is kept iff fewer than k are in total.
+// Positions in the output follow chunk order.
+constexpr int TK_SMALL = 256;
+__global__ __launch_bounds__(TK_NT) void k_topk_small(const double *__restrict__ scores, int Hkv,
+                                                      int n_c, int k_eff, int32_t *__restrict__ sel,
+                                                      int32_t *__restrict__ sel_out) {
+  __shared__ __align__(16) double s[TK_SMALL];
+  __shared__ int32_t cnt[4][TK_SMALL];
+  __shared__ TopkSmem tk;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int j = tid % TK_SMALL, qp = tid / TK_SMALL;
+  if (tid < TK_SMALL) s[tid] = tid < n_c ? scores[((long)b * Hkv + h) * n_c + tid] : -INFINITY;
+  __syncthreads();
+  const double mine = s[j];
+  int above = 0;
+#pragma unroll
+  for (int i0 = 0; i0 < TK_SMALL / 4; i0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = s[qp * (TK_SMALL / 4) + i0 + e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = qp * (TK_SMALL / 4) + i0 + e;
+      above += (i < j) ? (v[e] >= mine) : (v[e] > mine);
+    }
+  }
+  cnt[qp][j] = above;
+  __syncthreads();
+  const bool take = tid < n_c && (cnt[0][tid] + cnt[1][tid]) + (cnt[2][tid] + cnt[3][tid]) < k_eff;
+  uint32_t pos, p2, tot, t2;
+  block_exclusive_counts<TK_NT>(take, false, pos, p2, tot, t2, tk);
+  if (take) {
+    sel[((long)b * Hkv + h) * k_eff + pos] = tid;
+    if (sel_out) sel_out[((long)b * Hkv + h) * k_eff + pos] = tid;
   }
 }
 
@@ -552,26 +630,45 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+template <typename TA>
+static void launch_qtilde(const TA *q, long q_bstride, const TA *basis, int B, int Hq, int Hkv, int dh,
+                          int r, int D, int layer, double *qt, hipStream_t st) {
+  const dim3 g((r + QT_I - 1) / QT_I, Hkv, B);
+  if (dh == 64)
+    hipLaunchKernelGGL((k_qtilde<TA, 64>), g, dim3(256), 0, st, q, q_bstride, basis, Hq, Hkv, r, D, layer, qt);
+  else if (dh == 128)
+    hipLaunchKernelGGL((k_qtilde<TA, 128>), g, dim3(256), 0, st, q, q_bstride, basis, Hq, Hkv, r, D, layer, qt);
+  else
+    hipLaunchKernelGGL((k_qtilde<TA, 256>), g, dim3(256), 0, st, q, q_bstride, basis, Hq, Hkv, r, D, layer, qt);
+}
+
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
                          double *scores, double *qt, hipStream_t st) {
-  dim3 g1((r + QT_I - 1) / QT_I, Hkv, B);
   if (act == LOWRAM_F32)
-    hipLaunchKernelGGL(k_qtilde<float>, g1, dim3(256), 0, st, (const float *)q, q_bstride,
-                       (const float *)basis, Hq, Hkv, dh, r, D, layer, qt);
+    launch_qtilde<float>((const float *)q, q_bstride, (const float *)basis, B, Hq, Hkv, dh, r, D, layer, qt, st);
   else
-    hipLaunchKernelGGL(k_qtilde<bf16>, g1, dim3(256), 0, st, (const bf16 *)q, q_bstride,
-                       (const bf16 *)basis, Hq, Hkv, dh, r, D, layer, qt);
-  const size_t sm2 = sizeof(double) * (size_t)Hkv * r;
-  allow_dynamic_lds(k_scores, sm2);
-  hipLaunchKernelGGL(k_scores, dim3((n_c + SC_J - 1) / SC_J, B), dim3(256), sm2, st, qt, landmark,
-                     Hkv, r, n_c, scores);
+    launch_qtilde<bf16>((const bf16 *)q, q_bstride, (const bf16 *)basis, B, Hq, Hkv, dh, r, D, layer, qt, st);
+  const dim3 g2((n_c + SC_J - 1) / SC_J, Hkv, B);
+  if (r <= 256)
+    hipLaunchKernelGGL(k_scores<1>, g2, dim3(256), 0, st, qt, landmark, Hkv, r, n_c, scores);
+  else if (r <= 512)
+    hipLaunchKernelGGL(k_scores<2>, g2, dim3(256), 0, st, qt, landmark, Hkv, r, n_c, scores);
+  else if (r <= 1024)
+    hipLaunchKernelGGL(k_scores<4>, g2, dim3(256), 0, st, qt, landmark, Hkv, r, n_c, scores);
+  else
+    hipLaunchKernelGGL(k_scores<8>, g2, dim3(256), 0, st, qt, landmark, Hkv, r, n_c, scores);
   if (k_eff > 0) {
-    const size_t sm3 = (size_t)n_c * (8 + 16) + sizeof(int32_t) * (size_t)k_eff;
-    allow_dynamic_lds(k_topk, sm3);
-    hipLaunchKernelGGL(k_topk, dim3(Hkv, B), dim3(TK_NT), sm3, st, scores, Hkv, n_c, k_eff, sel,
-                       sel_out);
+    if (n_c <= TK_SMALL) {
+      hipLaunchKernelGGL(k_topk_small, dim3(Hkv, B), dim3(TK_NT), 0, st, scores, Hkv, n_c, k_eff,
+                         sel, sel_out);
+    } else {
+      const size_t sm3 = (size_t)n_c * 8 + sizeof(int32_t) * (size_t)k_eff;
+      allow_dynamic_lds(k_topk, sm3);
+      hipLaunchKernelGGL(k_topk, dim3(Hkv, B), dim3(TK_NT), sm3, st, scores, Hkv, n_c, k_eff, sel,
+                         sel_out);
+    }
   }
   return hipGetLastError();
 }

@@ -239,6 +239,12 @@ def _roundtrip(s, top_k):
     ("all-residuals", small(LLAMA8B_32K, B=1, N=1024, rho=1.0, T=16), 4),
     ("fp32-g8", TINY.replace(Hq=16, N=512, rho=0.5, T=1), 3),
     ("int8-ragged", small(COMPOSED_128K, B=1, N=2048, evict_keep=1.0, n_obs=0, T=5), 7),
+    # selection paths: radix top-k inside the fused scorer (256 < n_c <= 1024),
+    # the three-kernel scorer (n_c > 1024), two and four rank segments per lane
+    ("nc-512", TINY.replace(N=32768, T=8), 9),
+    ("nc-2048-unfused", TINY.replace(N=131072, T=8), 11),
+    ("rank-1024", small(LLAMA8B_32K, B=1, N=1024, r=1024, T=16), 3),
+    ("rank-2048", small(LLAMA8B_32K, B=1, N=1024, r=2048, T=16), 3),
 ])
 def test_special_shapes(name, shape, top_k):
     if not torch.cuda.is_available():
