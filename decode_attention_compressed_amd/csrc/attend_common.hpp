@@ -94,13 +94,16 @@ __device__ void tail_split(const AttendArgs &a, int h, int b, const float *qs, f
   }
 }
 
+// Partial of one split for each query head: m, l, the part of l from rebuilt
+// tokens (all of it for a rebuilt split, none for the tail), 0, then accH[F]
+// (zero for the tail) and accV[dh].
 __device__ inline void write_partial(const AttendArgs &a, int h, int b, int split, const float *ms,
                                      const float *ls, const float *accH, const float *accV) {
   const int tid = threadIdx.x;
   float *p = a.part + (((long)b * a.Hkv + h) * (a.n_split + 1) + split) * a.g * a.PW;
   for (int gi = 0; gi < a.g; ++gi) {
     float *pg = p + (long)gi * a.PW;
-    if (tid == 0) { pg[0] = ms[gi]; pg[1] = ls[gi]; pg[2] = 0.f; pg[3] = 0.f; }
+    if (tid == 0) { pg[0] = ms[gi]; pg[1] = ls[gi]; pg[2] = accH ? ls[gi] : 0.f; pg[3] = 0.f; }
     for (int f = tid; f < a.F; f += 256) pg[4 + f] = accH ? accH[gi * a.F + f] : 0.f;
     for (int d = tid; d < a.dh; d += 256) pg[4 + a.F + d] = accV[gi * a.dh + d];
   }

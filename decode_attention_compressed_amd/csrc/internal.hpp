@@ -23,6 +23,7 @@ struct AttendArgs {
   float *part;                  // [B][Hkv][n_split+1][g][PW]
   int B, G, Hq, Hkv, dh, r, F, N, C, T, k_eff, n_res, layer;
   int g, cps, n_split, PW;
+  int tps, tail_per_split;      // register-chained kernel: tiles and tail tokens per split
   float scale_log2;             // log2(e) / sqrt(dh)
 };
 
@@ -42,6 +43,12 @@ hipError_t launch_select(int act, const void *q, long q_bstride, const void *bas
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
                          double *scores, double *qt, hipStream_t st);
 hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st);
+// Register-chained rebuild-and-attend: the shapes it covers, its split plan
+// (splits per (b, h), 64-token tiles per split, tail tokens per split) and the
+// launcher.  Its partials fold the tail in: n_split of them per (b, h).
+bool chain_supported(int act, int coeff, int resid, int dh, int F, int r, int C, int g, int k_eff);
+void chain_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps, int &tail_per_split);
+hipError_t launch_attend_chain(int coeff, const AttendArgs &a, hipStream_t st);
 hipError_t launch_combine(int act, const CombineArgs &a, hipStream_t st);
 hipError_t launch_dense(int act, const void *q, const void *k, const void *v, long batch_stride,
                         int B, int Hq, int Hkv, int dh, int n, int tps, int n_split, float *part,

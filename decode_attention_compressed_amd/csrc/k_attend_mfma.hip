@@ -581,7 +581,7 @@ __global__ __launch_bounds__(256, (dual_occupancy<DH, NF64>() ? 2 : 1)) void k_a
 
   // ---- partials ---------------------------------------------------------------
   float *p = a.part + (((long)b * a.Hkv + h) * (a.n_split + 1) + split) * g * a.PW;
-  if (tid < g) { p[tid * a.PW] = ms[tid]; p[tid * a.PW + 1] = ls[tid]; p[tid * a.PW + 2] = 0.f; p[tid * a.PW + 3] = 0.f; }
+  if (tid < g) { p[tid * a.PW] = ms[tid]; p[tid * a.PW + 1] = ls[tid]; p[tid * a.PW + 2] = ls[tid]; p[tid * a.PW + 3] = 0.f; }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int gq = 4 * (lane >> 4) + i;
@@ -630,6 +630,7 @@ bool mfma_supported(const AttendArgs &a, int act, int coeff, int resid) {
 }
 
 hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st) {
+  if (a.tps > 0) return launch_attend_chain(coeff, a, st);  // planned for the chained kernel
   if (!mfma_supported(a, act, coeff, resid)) return launch_attend_valu(act, coeff, resid, a, st);
   const bool i8 = coeff == LOWRAM_I8;
 #define X(dh_, f_, r_, t_) \

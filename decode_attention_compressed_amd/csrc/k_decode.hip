@@ -347,7 +347,8 @@ __global__ __launch_bounds__(256) void k_combine(const CombineArgs a) {
   const int n_out = a.F + a.dh;
   float *wts = csm;                      // [n_total]
   float *ls = wts + a.n_total;           // [n_total]
-  float *acc = ls + a.n_total;           // [F + dh]: accH then accV
+  float *mc = ls + a.n_total;            // [n_total] part of l from rebuilt tokens
+  float *acc = mc + a.n_total;           // [F + dh]: accH then accV
   float *red = acc + n_out;              // [8]
   float *stage = red + 8;                // [CB][n_out]
   const float *p = a.part + ((long)b * a.Hkv + h) * a.n_total * a.g * a.PW + (long)gi * a.PW;
@@ -357,6 +358,7 @@ __global__ __launch_bounds__(256) void k_combine(const CombineArgs a) {
     const float m = p[s * sstride];
     wts[s] = m;
     ls[s] = p[s * sstride + 1];
+    mc[s] = p[s * sstride + 2];
     mx = fmaxf(mx, m);
   }
   mx = wave_max(mx);
@@ -385,19 +387,16 @@ __global__ __launch_bounds__(256) void k_combine(const CombineArgs a) {
       if (so + u * sub < nb && pc < per_split) lst16(stage + (so + u * sub) * n_out + 4 * pc, v[u]);
     __syncthreads();
     for (int o = tid; o < n_out; o += 256) {
-      const int n_s = o < a.F ? a.n_comp : a.n_total;  // accH only from rebuilt splits
-      float vv = acc[o];
-      for (int u = 0; u < nb; ++u)
-        if (s0 + u < n_s) vv = fmaf(wts[s0 + u], stage[u * n_out + o], vv);
+      float vv = acc[o];  // (a tail split's accH is zero)
+      for (int u = 0; u < nb; ++u) vv = fmaf(wts[s0 + u], stage[u * n_out + o], vv);
       acc[o] = vv;
     }
   }
   __syncthreads();
   float L = 0.f, mass = 0.f;  // same order in every thread
   for (int s = 0; s < a.n_total; ++s) {
-    const float wl = wts[s] * ls[s];
-    L += wl;
-    if (s < a.n_comp) mass += wl;
+    L += wts[s] * ls[s];
+    mass += wts[s] * mc[s];
   }
   const long bh = ((long)b * a.G + a.layer) * a.Hkv + h;
   const bool hoisted = a.F > 0 && a.n_comp > 0;  // W2/b2 only when rebuilt chunks contributed
@@ -709,7 +708,7 @@ hipError_t launch_combine(int act, const CombineArgs &a, hipStream_t st) {
   const int n_out = a.F + a.dh, per = n_out / 4;
   const int sub = 256 / (per <= 64 ? 64 : (per <= 128 ? 128 : 256));
   const size_t stage = (size_t)CB * sub * n_out > 256 ? (size_t)CB * sub * n_out : 256;
-  const size_t smem = sizeof(float) * ((size_t)2 * a.n_total + n_out + 8 + stage);
+  const size_t smem = sizeof(float) * ((size_t)3 * a.n_total + n_out + 8 + stage);
   dim3 grid(a.Hq, a.B);
   allow_dynamic_lds(act == LOWRAM_F32 ? (const void *)k_combine<float> : (const void *)k_combine<bf16>, smem);
   if (act == LOWRAM_F32)

@@ -73,24 +73,35 @@ lowram_status check_dims(const lowram_dims *d) {
   return LOWRAM_OK;
 }
 
+// Decode workspace plan.  The register-chained attend kernel folds the tail
+// into its n_split partials per (b, h); the other attend kernels write one
+// partial per selected chunk plus one for the tail.
 struct DecodePlan {
-  int k_eff, cps, n_split, PW;
+  int k_eff, cps, n_split, n_part, PW, tps, tail_per_split;
   size_t sel_off, qt_off, sc_off, part_off, bytes;
 };
 
 DecodePlan decode_plan(const lowram_dims *d) {
   DecodePlan p;
   const int n_c = n_chunks(d);
+  const int g = d->heads_q / d->heads_kv;
   p.k_eff = d->top_k < n_c ? d->top_k : n_c;
   p.cps = 1;
-  p.n_split = p.k_eff > 0 ? (p.k_eff + p.cps - 1) / p.cps : 0;
+  p.tps = 0;
+  p.tail_per_split = 0;
+  if (chain_supported(d->act, d->coeff, d->resid, d->head_dim, d->hidden, d->rank, d->chunk, g, p.k_eff)) {
+    chain_plan(d->batch, d->heads_kv, p.k_eff, d->chunk, d->n_tail, p.n_split, p.tps, p.tail_per_split);
+    p.n_part = p.n_split;
+  } else {
+    p.n_split = p.k_eff > 0 ? (p.k_eff + p.cps - 1) / p.cps : 0;
+    p.n_part = p.n_split + 1;
+  }
   p.PW = 4 + d->hidden + d->head_dim;
-  const int g = d->heads_q / d->heads_kv;
   p.sel_off = 0;
   p.qt_off = align_up(sizeof(int32_t) * (size_t)d->batch * d->heads_kv * (p.k_eff > 0 ? p.k_eff : 1));
   p.sc_off = p.qt_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * d->rank);
   p.part_off = p.sc_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * (n_c > 0 ? n_c : 1));
-  p.bytes = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * (p.n_split + 1) * g * p.PW);
+  p.bytes = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * p.n_part * g * p.PW);
   return p;
 }
 
@@ -208,6 +219,7 @@ AttendArgs make_attend(const lowram_dims *d, int32_t layer, const lowram_model *
   a.r = d->rank; a.F = d->hidden; a.N = d->n_ctx; a.C = d->chunk; a.T = d->n_tail;
   a.k_eff = p.k_eff; a.n_res = d->n_res; a.layer = layer;
   a.g = d->heads_q / d->heads_kv; a.cps = p.cps; a.n_split = p.n_split; a.PW = p.PW;
+  a.tps = p.tps; a.tail_per_split = p.tail_per_split;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)d->head_dim);
   return a;
 }
@@ -347,7 +359,7 @@ lowram_status lowram_decode_combine(const lowram_dims *d, int32_t layer, const l
   a.w2 = m ? m->w2 : nullptr; a.b2 = m ? m->b2 : nullptr; a.out = out;
   a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
   a.F = d->hidden; a.layer = layer; a.g = d->heads_q / d->heads_kv;
-  a.n_comp = p.n_split; a.n_total = p.n_split + 1; a.PW = p.PW;
+  a.n_comp = p.k_eff > 0 ? p.n_split : 0; a.n_total = p.n_part; a.PW = p.PW;
   return hip_status(launch_combine(d->act, a, (hipStream_t)stream), "lowram_decode_combine");
 }
 
