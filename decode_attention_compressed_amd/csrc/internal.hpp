@@ -20,6 +20,8 @@ struct AttendArgs {
   const uint16_t *res_scale;    // [B][G][Hkv][dh] f16 or null
   const void *k_tail, *v_tail;  // [B][G][Hkv][T][dh] act
   const int32_t *sel;           // [B][Hkv][k_eff]
+  const double *scores;         // [B][Hkv][n_c] fp64 when the attend kernel selects itself, else null
+  int32_t *sel_out;             // [B][Hkv][k_eff] copy of the selection (in-kernel selection only) or null
   float *part;                  // [B][Hkv][n_split+1][g][PW]
   int B, G, Hq, Hkv, dh, r, F, N, C, T, k_eff, n_res, layer;
   int g, cps, n_split, PW;
@@ -37,7 +39,7 @@ struct CombineArgs {
 // launchers (return hipSuccess or the launch error)
 // Chunk scores (float64) into scores [B][Hkv][n_c] (workspace), through the
 // q~ workspace qt [B][Hkv][r]; if k_eff > 0 the selection into sel and,
-// optionally, a copy into sel_out.
+// optionally, a copy into sel_out (k_eff = 0: scores only).
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
@@ -47,6 +49,9 @@ hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hip
 // (splits per (b, h), 64-token tiles per split, tail tokens per split) and the
 // launcher.  Its partials fold the tail in: n_split of them per (b, h).
 bool chain_supported(int act, int coeff, int resid, int dh, int F, int r, int C, int g, int k_eff);
+// Largest chunk count for which the chained kernel ranks the fp64 chunk scores
+// itself (each workgroup, in its prologue) instead of reading a selection.
+constexpr int CHAIN_SELECT_MAX_NC = 512;
 void chain_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps, int &tail_per_split);
 hipError_t launch_attend_chain(int coeff, const AttendArgs &a, hipStream_t st);
 hipError_t launch_combine(int act, const CombineArgs &a, hipStream_t st);

@@ -7,7 +7,8 @@
 //      in 32-wide steps.  The basis slab of a step is shared by the 8 waves
 //      through LDS (double-buffered, one barrier per step, loaded two steps
 //      ahead); every lane loads its coefficient fragments straight from global
-//      memory into the MFMA operand, two steps ahead.
+//      memory into the MFMA operand, two steps ahead, after an L2 prefetch of
+//      the same lines (one word per token row) two steps before that.
 //   2. logits[t][g] = K_hat[t] . q_g: the key accumulators rounded to fp16 are
 //      the A operand exactly as the step-1 output leaves them; online softmax
 //      per wave; p rounded to fp16.
@@ -23,9 +24,10 @@
 // follow the step-1 output layout (W1 and q are stored permuted), the tokens
 // in step 4 follow the step-3 output layout.
 //
-// The workgroup also attends its share of the uncompressed tail (staged in LDS
-// at the start, vector ALUs), then merges the 8 waves and the tail into one
-// partial: (m, l, mass of rebuilt tokens, accH[F], accV[d_h]) per query head.
+// The workgroup's last wave also attends the split's share of the uncompressed
+// tail (staged in LDS at the start; logits on the matrix cores, p . v on the
+// vector ALUs); the 8 waves then merge into one partial per query head:
+// (m, l, mass of rebuilt tokens, accH[F], accV[d_h]).
 // The second predictor layer is linear and is applied once per query head in
 // the combine: sum_t p_t v_t = W2 accH + b2 mass + accV.
 //
@@ -46,7 +48,7 @@ typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
 constexpr int DH = 128;           // head dim handled here
-constexpr int NW = 8;             // waves per workgroup
+constexpr int NW = 8;             // waves per workgroup (two per SIMD)
 constexpr int NTH = NW * WAVE;
 constexpr int TT = 64;            // tokens per wave tile
 constexpr int NTT = TT / 16;      // 16-token tiles
@@ -59,9 +61,13 @@ constexpr int GQ = 4;             // query heads per kv head (at most)
 constexpr int RP = 16;            // residual rows of a tile held in registers
 constexpr int DC = 3;             // coefficient k-steps in registers (2 ahead)
 constexpr int LU = 2;             // basis slabs are loaded LU steps before use
-constexpr int NU = 4;             // basis register ring (divides the step count)
-constexpr int TP = 32;            // tail tokens staged per piece
+constexpr int NU = 2;             // basis register ring (divides the step count)
+constexpr int SP = DH * KS / 8 / NTH;  // 16-byte basis pieces per thread and slab
+constexpr int TP = 32;            // tail tokens staged in LDS per split
+constexpr int PD = 99;            // coefficient k-steps prefetched into L2 ahead (>= NR: none)
 constexpr int CPT = 2;            // tiles per chunk: 128-token chunks
+constexpr int MAXIT = 8;          // tiles per wave and split (at most)
+constexpr int MAXSLOT = MAXIT * NW / CPT;  // selected chunks per split (at most)
 
 template <int I, int N, typename Fn>
 __device__ __forceinline__ void sfor_impl(Fn &f) {
@@ -100,18 +106,20 @@ struct Smem {
   static constexpr int W1S = 0;                          // [F][WLD] fp16, dims permuted
   static constexpr int US = W1S + F * WLD * 2;           // 2 x [DH][ULD] basis slabs
   static constexpr int QS = US + 2 * DH * ULD * 2;       // [16][WLD] fp16 q, dims permuted
-  static constexpr int QF = QS + 16 * WLD * 2;           // [GQ][DH] fp32 q (tail)
-  static constexpr int B1 = QF + GQ * DH * 4;            // [F] fp32 b1
-  static constexpr int PS = B1 + F * 4;                  // [NW][GQ][TT] fp32 p
+  static constexpr int B1 = QS + 16 * WLD * 2;           // [F] fp32 b1
+  static constexpr int PS = B1 + F * 4;                  // [NW][TT][GQ] fp32 p
   static constexpr int TK = PS + NW * GQ * TT * 4;       // [TP][DH] bf16 tail keys
   static constexpr int TV = TK + TP * DH * 2;            // [TP][DH] bf16 tail values
-  static constexpr int TL = TV + TP * DH * 2;            // [GQ][TP] fp32 tail logits / p
-  static constexpr int TS = TL + GQ * TP * 4;            // [4][GQ] fp32 tail m, l, alpha
-  static constexpr int AH = TS + 4 * GQ * 4;             // [NW][GQ][F] fp32 running accH per wave
-  static constexpr int BYTES = AH + NW * GQ * F * 4;
-  // merge area (after the last tile): m, l [NW+1][GQ], accV [NW+1][GQ][DH]
-  static constexpr int MM = 0, ML = MM + (NW + 1) * GQ * 4, MV = ML + (NW + 1) * GQ * 4;
-  static_assert(MV + (NW + 1) * GQ * DH * 4 <= QS, "merge area does not fit");
+  static constexpr int AH = TV + TP * DH * 2;            // [NW][GQ][F] fp32 running accH per wave
+  static constexpr int SEL = AH + NW * GQ * F * 4;       // [MAXSLOT] chunks of this split, [NW] counts
+  static constexpr int BYTES = SEL + (MAXSLOT + NW) * 4;
+  // the chunk scores of the in-kernel selection use the p area (free until the first softmax)
+  static_assert(CHAIN_SELECT_MAX_NC * 12 <= NW * GQ * TT * 4, "score staging does not fit");
+  // merge area (after the last tile): per wave and query head m, l of rebuilt
+  // tokens, l of tail tokens, accH rescale owed, merge weights; then accV
+  static constexpr int MM = 0, MLC = MM + NW * GQ * 4, MLT = MLC + NW * GQ * 4, MHS = MLT + NW * GQ * 4;
+  static constexpr int MWT = MHS + NW * GQ * 4, MWH = MWT + NW * GQ * 4, MV = MWH + NW * GQ * 4;
+  static_assert(MV + NW * GQ * DH * 4 <= QS, "merge area does not fit");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -169,36 +177,43 @@ template <> struct Coef<int8_t> {
   }
 };
 
-// basis slab pieces: thread tid stages 8 ranks of head-dim row tid / 4
-// (lane offset ((tid / 4) * r + 8 (tid % 4)) * 2 bytes, k-step in the scalar offset)
+// basis slab pieces: thread tid stages 8 ranks of head-dim rows tid / 4 + 64 i
+// (lane offset ((tid / 4) * r + 8 (tid % 4)) * 2 bytes; piece and k-step in the
+// scalar offset)
 template <typename TC> struct Slab;
 template <> struct Slab<bf16> {
   typedef bf16x8 op;
-  __device__ static void ld(rsrc_t U, const uint16_t *, uint32_t voff, int k0, u32x4 &u, u32x4 &) {
-    u = bld16(U, voff, 2u * k0);
+  __device__ static void ld(rsrc_t U, const uint16_t *, uint32_t voff, int r, int k0, u32x4 *u, u32x4 &) {
+#pragma unroll
+    for (int i = 0; i < SP; ++i) u[i] = bld16(U, voff, 2u * (k0 + i * (NTH / 4) * r));
   }
-  __device__ static void st(uint16_t *Ub, const u32x4 &u, const u32x4 &) {
+  __device__ static void st(uint16_t *Ub, const u32x4 *u, const u32x4 &) {
     const int tid = threadIdx.x;
-    lst16(Ub + (tid >> 2) * ULD + 8 * (tid & 3), u);
+#pragma unroll
+    for (int i = 0; i < SP; ++i) lst16(Ub + ((tid >> 2) + i * (NTH / 4)) * ULD + 8 * (tid & 3), u[i]);
   }
   __device__ static op get(const uint16_t *p) { return ldb8(p); }
 };
 template <> struct Slab<int8_t> {  // fp16 slab with the coefficient scale folded in
   typedef f16x8 op;
-  __device__ static void ld(rsrc_t U, const uint16_t *csc, uint32_t voff, int k0, u32x4 &u, u32x4 &sc) {
-    u = bld16(U, voff, 2u * k0);
+  __device__ static void ld(rsrc_t U, const uint16_t *csc, uint32_t voff, int r, int k0, u32x4 *u, u32x4 &sc) {
+#pragma unroll
+    for (int i = 0; i < SP; ++i) u[i] = bld16(U, voff, 2u * (k0 + i * (NTH / 4) * r));
     sc = gld16(csc + k0 + 8 * (threadIdx.x & 3));
   }
-  __device__ static void st(uint16_t *Ub, const u32x4 &u, const u32x4 &sc) {
+  __device__ static void st(uint16_t *Ub, const u32x4 *u, const u32x4 &sc) {
     const int tid = threadIdx.x;
-    const uint16_t *u16 = reinterpret_cast<const uint16_t *>(&u);
     const uint16_t *s16 = reinterpret_cast<const uint16_t *>(&sc);
-    uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = pack2(bf16_bits_to_f32(u16[2 * i]) * f16_bits_to_f32(s16[2 * i]),
-                   bf16_bits_to_f32(u16[2 * i + 1]) * f16_bits_to_f32(s16[2 * i + 1]));
-    lst16(Ub + (tid >> 2) * ULD + 8 * (tid & 3), v4(w[0], w[1], w[2], w[3]));
+    for (int i = 0; i < SP; ++i) {
+      const uint16_t *u16 = reinterpret_cast<const uint16_t *>(&u[i]);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack2(bf16_bits_to_f32(u16[2 * e]) * f16_bits_to_f32(s16[2 * e]),
+                     bf16_bits_to_f32(u16[2 * e + 1]) * f16_bits_to_f32(s16[2 * e + 1]));
+      lst16(Ub + ((tid >> 2) + i * (NTH / 4)) * ULD + 8 * (tid & 3), v4(w[0], w[1], w[2], w[3]));
+    }
   }
   __device__ static op get(const uint16_t *p) { return ldh8(p); }
 };
@@ -231,6 +246,7 @@ template <> struct Res<int8_t> {
 template <typename TC, int NR, int NF>
 __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   static_assert(NR % NU == 0, "the basis register ring must divide the k-step count");
+  static_assert(NR >= 4, "step 1 needs at least four k-steps");
   constexpr int F = NF * 16;
   using S = Smem<F>;
   using CT = Coef<TC>;
@@ -239,13 +255,10 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   uint16_t *W1s = reinterpret_cast<uint16_t *>(sm + S::W1S);
   uint16_t *Us = reinterpret_cast<uint16_t *>(sm + S::US);
   uint16_t *Qs = reinterpret_cast<uint16_t *>(sm + S::QS);
-  float *Qf = reinterpret_cast<float *>(sm + S::QF);
   float *B1s = reinterpret_cast<float *>(sm + S::B1);
   float *Ps = reinterpret_cast<float *>(sm + S::PS);
   uint16_t *Tk = reinterpret_cast<uint16_t *>(sm + S::TK);
   uint16_t *Tv = reinterpret_cast<uint16_t *>(sm + S::TV);
-  float *Tl = reinterpret_cast<float *>(sm + S::TL);
-  float *Ts = reinterpret_cast<float *>(sm + S::TS);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile offsets stay scalar
@@ -265,9 +278,11 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   const TC *cf = reinterpret_cast<const TC *>(a.coeff) + (long)b * a.N * r;
   const rsrc_t Cr = make_rsrc(cf, (uint32_t)((long)a.N * r * CT::ES));
   const uint32_t c_voff = (uint32_t)((l16 * r + 8 * kg) * CT::ES);  // + (row0 + 16 tt) r + 32 ks
+  const uint32_t pf_voff = (uint32_t)(lane * r * CT::ES);           // token row lane of a tile
   const uint16_t *csc = a.coeff_scale ? a.coeff_scale + (long)b * r : nullptr;
   const int32_t *rptr = a.res_ptr + bh * (a.N / C + 1);
   const int32_t *ridx = a.res_idx + bh * a.n_res;
+  const rsrc_t Ir = make_rsrc(ridx, (uint32_t)a.n_res * 4u);
   const TC *rval = reinterpret_cast<const TC *>(a.res_val) + bh * (long)a.n_res * DH;
   const rsrc_t Rr = make_rsrc(rval, (uint32_t)((long)a.n_res * DH * Res<TC>::ES));
   const int32_t *selp = a.sel + ((long)b * a.Hkv + h) * a.k_eff;
@@ -278,7 +293,50 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   const int t_end = min(n_tiles, t_begin + a.tps);
   const int iters = (a.tps + NW - 1) / NW;
 
-  // ---- prologue: W1 (in flight first), basis slabs, q, b1, tail piece ------
+  // ---- prologue -------------------------------------------------------------
+  int32_t *selL = reinterpret_cast<int32_t *>(sm + S::SEL);   // chunks of this split's slots
+  const int q0 = t_begin / cpt;                                 // first slot of this split
+  auto tile_row = [&](int tau) -> long {
+    const int j = selL[tau / cpt - q0];
+    return (long)j * C + (long)(tau % cpt) * TT;
+  };
+  const int tau0 = t_begin + w;
+  long row0 = (long)a.N;  // set once the selection is known; a wave without a tile reads out of range
+  auto c_soff = [&](int tt, int q) -> uint32_t {  // scalar offset of k-step q of token tile tt
+    return (uint32_t)(((row0 + 16 * tt) * r + q * KS) * CT::ES);
+  };
+  // L2 prefetch of k-step q of the wave's tile: one 4-byte read per token row
+  // brings the row's k-step sector into L2 ahead of the register loads.  The
+  // word read is folded into pf_acc PD steps later (by then the register load
+  // of the same k-step has been waited for anyway), which keeps the read live.
+  constexpr int PFN = TT / WAVE;  // prefetch reads per k-step
+  auto prefetch = [&](int q, int i) -> uint32_t {
+    return __builtin_amdgcn_raw_buffer_load_b32(Cr, pf_voff, (uint32_t)(((row0 + WAVE * i) * r + q * KS) * CT::ES), 0);
+  };
+  // the selection inputs are read first: everything below waits on them
+  static_assert(CHAIN_SELECT_MAX_NC <= NTH, "one chunk score per thread");
+  const int n_c = a.N / C;
+  double scv = 0.0;
+  int selv = 0;
+  if (a.scores) {
+    if (tid < n_c) scv = a.scores[((long)b * a.Hkv + h) * n_c + tid];
+  } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
+    selv = selp[q0 + tid];
+  }
+  uint32_t pf_acc = 0u, pfr[PD][PFN];
+#pragma unroll
+  for (int k = 0; k < PD; ++k)
+#pragma unroll
+    for (int i = 0; i < PFN; ++i) pfr[k][i] = 0u;
+  u32x4 ur[NU][SP], us_[NU];
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+#pragma unroll
+    for (int i = 0; i < SP; ++i) ur[k][i] = v4(0, 0, 0, 0);
+    us_[k] = v4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < LU; ++q) ST::ld(Ur, csc, u_voff, r, q * KS, ur[q % NU], us_[q % NU]);
   constexpr int W1P = F * DH / 8 / NTH;        // 16-byte W1 pieces per thread
   u32x4 w1r[W1P];
 #pragma unroll
@@ -286,48 +344,106 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     const int p = tid + NTH * k;
     w1r[k] = gld16(W1 + (long)(p / (DH / 8)) * DH + 8 * (p % (DH / 8)));
   }
-  u32x4 ur[NU], us_[NU];
-#pragma unroll
-  for (int k = 0; k < NU; ++k) { ur[k] = v4(0, 0, 0, 0); us_[k] = v4(0, 0, 0, 0); }
-  // slabs 0..LU-1: slab 0 goes straight to LDS, 1..LU-1 stay in the ring
-#pragma unroll
-  for (int q = 0; q < LU; ++q) ST::ld(Ur, csc, u_voff, q * KS, ur[q % NU], us_[q % NU]);
-
-  // the first tile's coordinates and coefficient fragments
-  const int tau0 = t_begin + w;
-  auto tile_row = [&](int tau) -> long {
-    const int j = selp[tau / cpt];
-    return (long)j * C + (long)(tau % cpt) * TT;
-  };
-  typename CT::raw cr[DC][NTT];
-  long row0 = tau0 < t_end ? tile_row(tau0) : 0;
-  // scalar offset of k-step q of token tile tt
-  auto c_soff = [&](int tt, int q) -> uint32_t {
-    return (uint32_t)(((row0 + 16 * tt) * r + q * KS) * CT::ES);
-  };
-  if (tau0 < t_end) {
-#pragma unroll
-    for (int q = 0; q < DC - 1; ++q)
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) cr[q][tt] = CT::ld(Cr, c_voff, c_soff(tt, q));
-  }
-
-  // tail share of this split: tokens [tb, te), first piece staged now
+  const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + ((long)b * a.Hq + (long)h * g) * DH;
+  const u32x4 qraw = tid < g * (DH / 8) ? gld16(qb + 8 * tid) : v4(0, 0, 0, 0);
+  const u32x4 braw = tid < F / 8 ? gld16(B1 + 8 * tid) : v4(0, 0, 0, 0);
+  // tail share of this split: tokens [tb, te); its first TP rows are staged now
   const int tb = min(a.T, s * a.tail_per_split), te = min(a.T, tb + a.tail_per_split);
   const long tail_base = ((((long)b * a.G + a.layer) * a.Hkv + h) * a.T) * DH;
   const uint16_t *kt = reinterpret_cast<const uint16_t *>(a.k_tail) + tail_base;
   const uint16_t *vt = reinterpret_cast<const uint16_t *>(a.v_tail) + tail_base;
-  auto stage_tail = [&](int t0) {  // one piece: TP rows of keys and values, 16 bytes per thread each
-    const int nt = min(TP, te - t0);
-    const int row = tid >> 4, c8 = (tid & 15) * 8;
-    u32x4 kv = v4(0, 0, 0, 0), vv = v4(0, 0, 0, 0);
-    if (row < nt) {
-      kv = gld16(kt + (long)(t0 + row) * DH + c8);
-      vv = gld16(vt + (long)(t0 + row) * DH + c8);
+  constexpr int TPP = TP * (DH / 8) / NTH;   // tail pieces per thread
+  u32x4 tkr[TPP], tvr[TPP];
+#pragma unroll
+  for (int i = 0; i < TPP; ++i) {
+    const int p = tid + NTH * i, row = p >> 4, c8 = (p & 15) * 8;
+    tkr[i] = v4(0, 0, 0, 0);
+    tvr[i] = v4(0, 0, 0, 0);
+    if (tb + row < te) {
+      tkr[i] = gld16(kt + (long)(tb + row) * DH + c8);
+      tvr[i] = gld16(vt + (long)(tb + row) * DH + c8);
     }
-    return std::make_pair(kv, vv);
-  };
-  auto tail0 = stage_tail(tb);
+  }
+
+  // ---- chunk selection of (b, h): the top k_eff chunks by (score desc, index
+  // asc), in ascending index order.  With the scores at hand every workgroup
+  // ranks them itself (two threads per chunk compare against half of the
+  // chunks each); split 0 also writes the whole selection to sel_out.
+  if (a.scores) {
+    // Ranks use the top 32 bits of the order key of each fp64 score: a larger
+    // top half means a larger score, a smaller one a smaller score.  Only
+    // chunks whose top half ties another chunk's are ranked again on the
+    // exact fp64 values (a uniform branch, rare outside crafted ties).
+    double *scL = reinterpret_cast<double *>(sm + S::PS);
+    uint32_t *khL = reinterpret_cast<uint32_t *>(scL + CHAIN_SELECT_MAX_NC);
+    int *wcnt = selL + MAXSLOT;
+    if (tid < n_c) {
+      scL[tid] = scv;
+      khL[tid] = (uint32_t)(f64_order_key(scv) >> 32);
+    }
+    __syncthreads();
+    const int tpc = n_c <= NTH / 2 ? 2 : 1;
+    const int c = tid / tpc, half = tid % tpc;
+    const int i0 = tpc == 2 ? half * ((n_c + 1) / 2) : 0;
+    const int i1 = tpc == 2 && half == 0 ? (n_c + 1) / 2 : n_c;
+    int gt = 0, ge = 0;
+    if (c < n_c) {  // the reads of one index are the same in every lane: LDS broadcasts
+      const uint32_t kc = khL[c];
+      int i = i0;
+      for (; i + 16 <= i1; i += 16) {
+        uint32_t u[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) u[k] = khL[i + k];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          gt += (int)(u[k] > kc);
+          ge += (int)(u[k] >= kc);
+        }
+      }
+      for (; i < i1; ++i) {
+        gt += (int)(khL[i] > kc);
+        ge += (int)(khL[i] >= kc);
+      }
+    }
+    if (tpc == 2) {
+      gt += __shfl_xor(gt, 1, 64);
+      ge += __shfl_xor(ge, 1, 64);
+    }
+    int rank = gt;
+    const bool tie = c < n_c && ge - gt > 1;  // another chunk shares the top half
+    if (__any(tie)) {
+      int extra = 0;
+      if (tie) {
+        const double v = scL[c];
+        const uint32_t kc = khL[c];
+        for (int i = i0; i < i1; ++i) {
+          const double u = scL[i];
+          extra += (int)((khL[i] == kc) & ((u > v) | ((u == v) & (i < c))));
+        }
+      }
+      if (tpc == 2) extra += __shfl_xor(extra, 1, 64);
+      rank += extra;
+    }
+    const bool chosen = c < n_c && half == 0 && rank < a.k_eff;
+    const uint64_t bal = __ballot(chosen);
+    if (lane == 0) wcnt[w] = __popcll(bal);
+    __syncthreads();
+    int pos = __popcll(bal & lanemask_lt());
+    for (int k = 0; k < w; ++k) pos += wcnt[k];
+    if (chosen) {
+      if (pos >= q0 && pos < q0 + MAXSLOT) selL[pos - q0] = c;
+      if (s == 0 && a.sel_out) a.sel_out[((long)b * a.Hkv + h) * a.k_eff + pos] = c;
+    }
+  } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
+    selL[tid] = selv;
+  }
+  __syncthreads();
+  if (tau0 < t_end) row0 = tile_row(tau0);
+  typename CT::raw cr[DC][NTT];
+#pragma unroll
+  for (int q = 0; q < DC - 1; ++q)
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) cr[q][tt] = CT::ld(Cr, c_voff, c_soff(tt, q));
 
   // W1 -> fp16, head dims permuted (two 4-dim runs per piece)
 #pragma unroll
@@ -341,20 +457,30 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     *reinterpret_cast<uint2 *>(W1s + f * WLD + dpos(d0)) = lo;
     *reinterpret_cast<uint2 *>(W1s + f * WLD + dpos(d0 + 4)) = hi;
   }
-  {  // q rows of this kv head: fp16 permuted (zero rows up to 16) and fp32 natural
-    const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + ((long)b * a.Hq + (long)h * g) * DH;
-    for (int i = tid; i < 16 * DH; i += NTH) {
-      const int gi = i / DH, d = i % DH;
-      const float x = gi < g ? bf16_bits_to_f32(qb[gi * DH + d]) : 0.f;
-      Qs[gi * WLD + dpos(d)] = h16(x);
-      if (gi < GQ) Qf[gi * DH + d] = x;
-    }
-    for (int f = tid; f < F; f += NTH) B1s[f] = bf16_bits_to_f32(B1[f]);
+  // q rows of this kv head as fp16 with permuted dims; rows g..15 are zero
+  for (int i = tid; i < (16 - g) * (DH / 2); i += NTH)
+    reinterpret_cast<uint32_t *>(Qs)[(g + i / (DH / 2)) * (WLD / 2) + i % (DH / 2)] = 0u;
+  if (tid < g * (DH / 8)) {
+    const int gi = tid / (DH / 8), d0 = 8 * (tid % (DH / 8));
+    const uint2 lo = make_uint2(pack2(bf16_bits_to_f32(qraw.x & 0xFFFFu), bf16_bits_to_f32(qraw.x >> 16)),
+                                pack2(bf16_bits_to_f32(qraw.y & 0xFFFFu), bf16_bits_to_f32(qraw.y >> 16)));
+    const uint2 hi = make_uint2(pack2(bf16_bits_to_f32(qraw.z & 0xFFFFu), bf16_bits_to_f32(qraw.z >> 16)),
+                                pack2(bf16_bits_to_f32(qraw.w & 0xFFFFu), bf16_bits_to_f32(qraw.w >> 16)));
+    *reinterpret_cast<uint2 *>(Qs + gi * WLD + dpos(d0)) = lo;
+    *reinterpret_cast<uint2 *>(Qs + gi * WLD + dpos(d0 + 4)) = hi;
   }
-  {
-    const int row = tid >> 4, c8 = (tid & 15) * 8;
-    lst16(Tk + row * DH + c8, tail0.first);
-    lst16(Tv + row * DH + c8, tail0.second);
+  if (tid < F / 8) {
+    float *bo = B1s + 8 * tid;
+    *reinterpret_cast<f32x4 *>(bo) = f32x4{bf16_bits_to_f32(braw.x & 0xFFFFu), bf16_bits_to_f32(braw.x >> 16),
+                                           bf16_bits_to_f32(braw.y & 0xFFFFu), bf16_bits_to_f32(braw.y >> 16)};
+    *reinterpret_cast<f32x4 *>(bo + 4) = f32x4{bf16_bits_to_f32(braw.z & 0xFFFFu), bf16_bits_to_f32(braw.z >> 16),
+                                               bf16_bits_to_f32(braw.w & 0xFFFFu), bf16_bits_to_f32(braw.w >> 16)};
+  }
+#pragma unroll
+  for (int i = 0; i < TPP; ++i) {
+    const int p = tid + NTH * i, row = p >> 4, c8 = (p & 15) * 8;
+    lst16(Tk + row * DH + c8, tkr[i]);
+    lst16(Tv + row * DH + c8, tvr[i]);
   }
   ST::st(Us, ur[0], us_[0]);   // slab 0 -> buffer 0
   __syncthreads();
@@ -371,29 +497,51 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     rs0 = f16_bits_to_f32(rsc[2 * lane]);
     rs1 = f16_bits_to_f32(rsc[2 * lane + 1]);
   }
+  // accV += p[g][t] row[t] for this wave's p in Ps and rows of d_h values
+  // (lane: dims 2 lane, 2 lane + 1)
+  static_assert(GQ == 4, "p rows are read as one 16-byte vector");
+  auto add_row = [&](int t, float d0, float d1) {
+    const f32x4 pv = *reinterpret_cast<const f32x4 *>(Ps + (w * TT + t) * GQ);
+#pragma unroll
+    for (int gi = 0; gi < GQ; ++gi) {
+      accV[gi][0] = fmaf(pv[gi], d0, accV[gi][0]);
+      accV[gi][1] = fmaf(pv[gi], d1, accV[gi][1]);
+    }
+  };
+  auto wave_lds_sync = []() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
   for (int it = 0; it < iters; ++it) {
     const int tau = t_begin + w + NW * it;
     const bool has = tau < t_end;
-    if (it > 0 && has) {
-      row0 = tile_row(tau);
+    if (it > 0) {  // restart the coefficient and basis pipelines for the next tile
+      row0 = has ? tile_row(tau) : (long)a.N;
 #pragma unroll
       for (int q = 0; q < DC - 1; ++q)
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) cr[q][tt] = CT::ld(Cr, c_voff, c_soff(tt, q));
+#pragma unroll
+      for (int q = 0; q < LU; ++q) ST::ld(Ur, csc, u_voff, r, q * KS, ur[q % NU], us_[q % NU]);
+      ST::st(Us, ur[0], us_[0]);   // slab 0 -> buffer 0 (last read two barriers ago)
+      __syncthreads();
     }
-    // this tile's residual rows: CSR range of the chunk, then the tile's part
+    // this tile's residual rows: CSR range of the chunk (loads issued here, read
+    // late in step 1), then the tile's part of it
+    const int jc = has ? (int)(row0 / C) : 0;
+    const int e0r = rptr[jc], e1r = rptr[jc + 1];
     int e0 = 0, e1 = 0;
-    if (has) {
-      const int j = (int)(row0 / C);
-      e0 = rptr[j];
-      e1 = rptr[j + 1];
-    }
-    int rtok[CPT] = {-1, -1};                  // token - row0 of entries e0 + lane + 64m
+    constexpr int RM = CPT * TT / WAVE;         // chunk entries per lane (C <= 64 RM)
+    int rtok[RM];                              // token of entries e0 + lane + 64m (raw)
+#pragma unroll
+    for (int m = 0; m < RM; ++m) rtok[m] = 0;
     int r_lo = 0, r_n = 0;                     // first row and count of this tile's rows
     typename Res<TC>::raw dr[RP];
 
     // ---- step 1: K_hat^T = U . C^T over NR k-steps ------------------------
+    const uint16_t *u_rd = Us + l16 * ULD + 8 * kg;  // lane's basis fragment, head-dim tile 0
     f32x4 acc[NDT][NTT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -402,63 +550,73 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
 
     sfor<NR>([&](auto ksc) {
       constexpr int ks = decltype(ksc)::value;
-      // basis slab ks + LU into the ring (wraps to the next tile's first slabs);
-      // issued before this step's coefficient loads so that waiting for it
-      // LU - 1 steps later waits for nothing newer than the coefficients then due
-      if (it + 1 < iters || ks + LU < NR)
-        ST::ld(Ur, csc, u_voff, ((ks + LU) % NR) * KS, ur[(ks + LU) % NU], us_[(ks + LU) % NU]);
-      // coefficients DC - 1 steps ahead
+      __builtin_amdgcn_sched_barrier(0);  // keep each k-step's loads and MFMAs in place
+      // basis slab ks + LU into the ring; issued before this step's coefficient
+      // loads so that waiting for it LU - 1 steps later waits for nothing newer
+      // than the coefficients then due
+      if constexpr (ks + LU < NR)
+        ST::ld(Ur, csc, u_voff, r, (ks + LU) * KS, ur[(ks + LU) % NU], us_[(ks + LU) % NU]);
+      // coefficients DC - 1 steps ahead, then the L2 prefetch PD steps ahead.
+      // Every load here is unconditional (a wave without a tile reads out of
+      // range), so the wait counts stay exact across steps.
       if constexpr (ks + DC - 1 < NR) {
-        if (has) {
 #pragma unroll
-          for (int tt = 0; tt < NTT; ++tt) cr[(ks + DC - 1) % DC][tt] = CT::ld(Cr, c_voff, c_soff(tt, ks + DC - 1));
+        for (int tt = 0; tt < NTT; ++tt) cr[(ks + DC - 1) % DC][tt] = CT::ld(Cr, c_voff, c_soff(tt, ks + DC - 1));
+      }
+      if constexpr (ks >= PD) {  // the prefetch of this k-step
+#pragma unroll
+        for (int i = 0; i < PFN; ++i) pf_acc ^= pfr[ks % PD][i];
+      }
+      if constexpr (ks + PD < NR) {
+#pragma unroll
+        for (int i = 0; i < PFN; ++i) pfr[ks % PD][i] = prefetch(ks + PD, i);
+      }
+      // residual entries of the chunk: their tokens two steps before the end,
+      // the tile's rows in the last step (read after the softmax)
+      if constexpr (ks == NR - 3) {
+        e0 = has ? e0r : 0;
+        e1 = has ? e1r : 0;
+        const int cnt = e1 - e0;
+#pragma unroll
+        for (int m = 0; m < RM; ++m) {
+          const int i = lane + 64 * m;
+          rtok[m] = (int)__builtin_amdgcn_raw_buffer_load_b32(Ir, 4u * (uint32_t)(i < cnt ? e0 + i : a.n_res), 0u, 0);
         }
       }
-      // residual entries of the chunk (their CSR range arrived by now)
-      if constexpr (ks == 1) {
-        if (has) {
-          const int cnt = e1 - e0;
+      if constexpr (ks == NR - 1) {  // this tile's rows: a contiguous run of the chunk's
+        const int cnt = e1 - e0;
+        int below = 0, inside = 0;
 #pragma unroll
-          for (int m = 0; m < CPT; ++m)
-            if (lane + 64 * m < cnt) rtok[m] = ridx[e0 + lane + 64 * m] - (int)row0;
+        for (int m = 0; m < RM; ++m) {
+          const bool valid = lane + 64 * m < cnt;
+          rtok[m] -= (int)row0;  // token within the tile
+          below += __popcll(__ballot(valid && rtok[m] < 0));
+          inside += __popcll(__ballot(valid && rtok[m] >= 0 && rtok[m] < TT));
         }
-      }
-      if constexpr (ks == 3 || (NR <= 3 && ks == NR - 1)) {
-        if (has) {
-          const int cnt = e1 - e0;
-          int below = 0, inside = 0;
+        r_lo = e0 + below;
+        r_n = inside;
 #pragma unroll
-          for (int m = 0; m < CPT; ++m) {
-            const bool valid = lane + 64 * m < cnt;
-            below += __popcll(__ballot(valid && rtok[m] < 0));
-            inside += __popcll(__ballot(valid && rtok[m] >= 0 && rtok[m] < TT));
-          }
-          r_lo = e0 + below;
-          r_n = inside;
-#pragma unroll
-          for (int k = 0; k < RP; ++k)
-            if (k < r_n) dr[k] = Res<TC>::ld(Rr, r_lo + k, lane);
-        }
+        for (int k = 0; k < RP; ++k) dr[k] = Res<TC>::ld(Rr, k < r_n ? r_lo + k : a.n_res, lane);
       }
+      __builtin_amdgcn_sched_barrier(0);  // this step's loads go out before its MFMAs
       // basis slab ks + 1 -> LDS (its load was issued LU - 1 steps ago)
-      if constexpr (ks + 1 < NR) {
-        ST::st(Us + ((ks + 1) & 1) * DH * ULD, ur[(ks + 1) % NU], us_[(ks + 1) % NU]);
-      } else {
-        if (it + 1 < iters) ST::st(Us, ur[0], us_[0]);  // the next tile's slab 0
-      }
-      if (has) {
-        const uint16_t *ub = Us + (ks & 1) * DH * ULD + l16 * ULD + 8 * kg;
+      if constexpr (ks + 1 < NR) ST::st(Us + ((ks + 1) & 1) * DH * ULD, ur[(ks + 1) % NU], us_[(ks + 1) % NU]);
+      {  // basis fragments one head-dim tile ahead of the MFMAs that use them
+        const uint16_t *ub = u_rd + (ks & 1) * DH * ULD;
         typename CT::op bc[NTT];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) bc[tt] = CT::get(cr[ks % DC][tt]);
+        typename ST::op au[2];
+        au[0] = ST::get(ub);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const typename ST::op au = ST::get(ub + 16 * dt * ULD);
+          if (dt + 1 < NDT) au[(dt + 1) & 1] = ST::get(ub + 16 * (dt + 1) * ULD);
 #pragma unroll
-          for (int tt = 0; tt < NTT; ++tt) acc[dt][tt] = mfma(au, bc[tt], acc[dt][tt]);
+          for (int tt = 0; tt < NTT; ++tt) acc[dt][tt] = mfma(au[dt & 1], bc[tt], acc[dt][tt]);
         }
       }
       __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     });
     if (!has) continue;
 
@@ -475,12 +633,13 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
         }
 
     // ---- step 2: logits and online softmax ------------------------------------
+    const uint16_t *q_rd = Qs + l16 * WLD + 8 * kg;
     f32x4 lg[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) lg[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
-      const f16x8 qf = ldh8(Qs + l16 * WLD + 32 * jj + 8 * kg);
+      const f16x8 qf = ldh8(q_rd + 32 * jj);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) lg[tt] = mfma(KA[jj][tt], qf, lg[tt]);
     }
@@ -509,65 +668,66 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    // p of this tile for the residual pass: Ps[w][g][t]
+    // p of this tile for the residual pass: Ps[w][t][g]
     if (l16 < GQ) {
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
-        *reinterpret_cast<f32x4 *>(Ps + (w * GQ + l16) * TT + 16 * tt + 4 * kg) = lg[tt];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Ps[(w * TT + 16 * tt + 4 * kg + v) * GQ + l16] = lg[tt][v];
     }
     // rescale the running sums: accV here, accH (rows g = v of lanes 0..15)
     // when this tile's hidden sums are folded into LDS
     float ah[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) ah[v] = __shfl(alpha, v, 64);
-    {
 #pragma unroll
-      for (int gi = 0; gi < GQ; ++gi) {
-        const float av = __shfl(alpha, gi, 64);
-        accV[gi][0] *= av;
-        accV[gi][1] *= av;
-      }
+    for (int gi = 0; gi < GQ; ++gi) {
+      const float av = __shfl(alpha, gi, 64);
+      accV[gi][0] *= av;
+      accV[gi][1] *= av;
     }
 
     // ---- step 5: residual rows (vector ALUs) -------------------------------------
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Branch-free over the RP rows held in registers: rows past r_n were read
+    // out of range as zeros and add nothing, so every p read can be batched.
+    wave_lds_sync();
     {
       const int below = r_lo - e0;
-      auto row = [&](int k, typename Res<TC>::raw raw) {
+#pragma unroll
+      for (int k = 0; k < RP; ++k) {
+        const int pos = below + k;
+        const int tsel = pos < 64 ? rtok[0] : rtok[1];
+        const int t = min(max(__shfl(tsel, pos & 63, 64), 0), TT - 1);
+        float d0, d1;
+        Res<TC>::get(dr[k], rs0, rs1, d0, d1);
+        add_row(t, d0, d1);
+      }
+      for (int k = RP; k < r_n; ++k) {  // rare: more than RP rows in the tile
         const int pos = below + k;
         const int tsel = pos < 64 ? rtok[0] : rtok[1];
         const int t = __shfl(tsel, pos & 63, 64);
         float d0, d1;
-        Res<TC>::get(raw, rs0, rs1, d0, d1);
-        const float *pt = Ps + w * GQ * TT + t;
-#pragma unroll
-        for (int gi = 0; gi < GQ; ++gi) {
-          const float p = pt[gi * TT];
-          accV[gi][0] = fmaf(p, d0, accV[gi][0]);
-          accV[gi][1] = fmaf(p, d1, accV[gi][1]);
-        }
-      };
-#pragma unroll
-      for (int k = 0; k < RP; ++k)
-        if (k < r_n) row(k, dr[k]);
-      for (int k = RP; k < r_n; ++k) row(k, Res<TC>::ld(Rr, r_lo + k, lane));
+        Res<TC>::get(Res<TC>::ld(Rr, r_lo + k, lane), rs0, rs1, d0, d1);
+        add_row(t, d0, d1);
+      }
     }
 
     // ---- steps 3 and 4 per 16-wide hidden tile ------------------------------------
     // accH[g][f] of this tile: lane holds column f = 16 fi + l16, rows g = 4 kg + v;
     // each hidden tile is folded into the wave's running accH in LDS right away
     // (the real rows g < GQ live in lanes 0..15)
-#pragma unroll
+    const uint16_t *w1_rd = W1s + l16 * WLD + 8 * kg;   // + 16 fi WLD + 32 jj
+    const float *b1_rd = B1s + l16;
+    float *ah_rw = AHw + l16;
+#pragma unroll 2
     for (int fi = 0; fi < NF; ++fi) {
-      const float bias = B1s[16 * fi + l16];
+      const float bias = b1_rd[16 * fi];
       f32x4 hc[NTT];
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) hc[tt] = f32x4{bias, bias, bias, bias};
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
-        const f16x8 bw = ldh8(W1s + (16 * fi + l16) * WLD + 32 * jj + 8 * kg);
+        const f16x8 bw = ldh8(w1_rd + 16 * fi * WLD + 32 * jj);
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) hc[tt] = mfma(KA[jj][tt], bw, hc[tt]);
       }
@@ -585,7 +745,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       if (kg == 0) {
 #pragma unroll
         for (int v = 0; v < GQ; ++v) {
-          float *pa = AHw + v * F + 16 * fi + l16;
+          float *pa = ah_rw + v * F + 16 * fi;
           *pa = first ? ahc[v] : fmaf(*pa, ah[v], ahc[v]);
         }
       }
@@ -599,109 +759,144 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       for (int v = 0; v < GQ; ++v) AHw[v * F + 16 * fi + l16] = 0.f;
   }
 
-  // ---- the split's share of the uncompressed tail (vector ALUs) ---------------
-  __syncthreads();
-  float *mm = reinterpret_cast<float *>(sm + S::MM), *ml = reinterpret_cast<float *>(sm + S::ML);
-  float *mv = reinterpret_cast<float *>(sm + S::MV);
-  const float *AH = reinterpret_cast<const float *>(sm + S::AH);
-  if (tid < GQ) { Ts[tid] = -INFINITY; Ts[GQ + tid] = 0.f; }
-  float tacc = 0.f;   // thread (gi, d) = (tid / DH, tid % DH) of the tail's p . V
-  for (int t0 = tb; t0 < te; t0 += TP) {
-    const int nt = min(TP, te - t0);
-    if (t0 > tb) {
-      __syncthreads();
-      auto piece = stage_tail(t0);
-      const int row = tid >> 4, c8 = (tid & 15) * 8;
-      lst16(Tk + row * DH + c8, piece.first);
-      lst16(Tv + row * DH + c8, piece.second);
-      __syncthreads();
-    }
-    if (tid < GQ * TP) {  // logits: thread (gi, t)
-      const int gi = tid / TP, t = tid % TP;
-      if (gi < g && t < nt) {
-        float sdot = 0.f;
-        for (int d = 0; d < DH; ++d) sdot = fmaf(Qf[gi * DH + d], bf16_bits_to_f32(Tk[t * DH + d]), sdot);
-        Tl[gi * TP + t] = sdot * a.scale_log2;
+  // ---- the split's share of the uncompressed tail: the last wave, 16 tokens at
+  // a time, logits on the matrix cores, p . v on the vector ALUs ---------------------
+  float l_t = 0.f;   // tail part of l
+  float hsc = 1.f;   // rescale still owed by the running accH (applied in the merge)
+  if (w == NW - 1 && tb < te) {
+    f16x8 qf[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) qf[jj] = ldh8(Qs + l16 * WLD + 32 * jj + 8 * kg);
+    for (int t0 = tb; t0 < te; t0 += 16) {
+      const int nt = min(16, te - t0), tl = t0 - tb;
+      const bool staged = tl + 16 <= TP;
+      f16x8 kf[NJ];
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+        if (l16 < nt) {
+          const int dlo = 32 * jj + 4 * kg;
+          const uint16_t *src = staged ? Tk + (tl + l16) * DH : kt + (long)(t0 + l16) * DH;
+          lo = *reinterpret_cast<const uint2 *>(src + dlo);
+          hi = *reinterpret_cast<const uint2 *>(src + dlo + 16);
+        }
+        const uint32_t wv[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kf[jj][2 * i] = (_Float16)bf16_bits_to_f32(wv[i] & 0xFFFFu);
+          kf[jj][2 * i + 1] = (_Float16)bf16_bits_to_f32(wv[i] >> 16);
+        }
       }
-    }
-    __syncthreads();
-    if (tid < g) {  // online softmax of the piece
-      float mx = -INFINITY;
-      for (int t = 0; t < nt; ++t) mx = fmaxf(mx, Tl[tid * TP + t]);
-      const float m_old = Ts[tid], mn = fmaxf(m_old, mx);
-      const float al = (m_old == -INFINITY) ? 0.f : exp2f(m_old - mn);
-      float sum = 0.f;
-      for (int t = 0; t < nt; ++t) {
-        const float p = exp2f(Tl[tid * TP + t] - mn);
-        Tl[tid * TP + t] = p;
-        sum += p;
+      f32x4 lt4 = f32x4{0.f, 0.f, 0.f, 0.f};  // lane (g = l16, kg): tokens 4 kg + v
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) lt4 = mfma(kf[jj], qf[jj], lt4);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        lt4[v] = 4 * kg + v < nt ? lt4[v] * a.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, lt4[v]);
       }
-      Ts[tid] = mn;
-      Ts[GQ + tid] = Ts[GQ + tid] * al + sum;
-      Ts[2 * GQ + tid] = al;
-    }
-    __syncthreads();
-    {
-      const int gi = tid / DH, d = tid % DH;
-      if (gi < g) {
-        float v = tacc * Ts[2 * GQ + gi];
-        for (int t = 0; t < nt; ++t) v = fmaf(Tl[gi * TP + t], bf16_bits_to_f32(Tv[t * DH + d]), v);
-        tacc = v;
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = 4 * kg + v < nt ? (float)(_Float16)exp2f(lt4[v] - m_new) : 0.f;
+        lt4[v] = p;
+        ps += p;
       }
+      l_run *= alpha;
+      l_t = l_t * alpha + ps;
+      hsc *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int gi = 0; gi < GQ; ++gi) {
+        const float av = __shfl(alpha, gi, 64);
+        accV[gi][0] *= av;
+        accV[gi][1] *= av;
+      }
+      if (l16 < GQ) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Ps[(w * TT + 4 * kg + v) * GQ + l16] = lt4[v];
+      }
+      wave_lds_sync();
+      if (staged) {  // all 16 rows, branch-free: p is zero past nt
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const uint32_t v2 = *reinterpret_cast<const uint32_t *>(Tv + (tl + t) * DH + 2 * lane);
+          add_row(t, bf16_bits_to_f32(v2 & 0xFFFFu), bf16_bits_to_f32(v2 >> 16));
+        }
+      } else {
+        for (int t = 0; t < nt; ++t) {
+          const uint32_t v2 = *reinterpret_cast<const uint32_t *>(vt + (long)(t0 + t) * DH + 2 * lane);
+          add_row(t, bf16_bits_to_f32(v2 & 0xFFFFu), bf16_bits_to_f32(v2 >> 16));
+        }
+      }
+      wave_lds_sync();
     }
   }
-  __syncthreads();  // W1, the basis slabs and the tail scratch are free from here
 
-  // ---- merge the waves and the tail into one partial ------------------------------
+  // ---- merge the waves into one partial --------------------------------------------
+  __syncthreads();  // W1 and the basis slabs are free from here
+  float *mm = reinterpret_cast<float *>(sm + S::MM), *mlc = reinterpret_cast<float *>(sm + S::MLC);
+  float *mlt = reinterpret_cast<float *>(sm + S::MLT), *mhs = reinterpret_cast<float *>(sm + S::MHS);
+  float *mwt = reinterpret_cast<float *>(sm + S::MWT), *mwh = reinterpret_cast<float *>(sm + S::MWH);
+  float *mv = reinterpret_cast<float *>(sm + S::MV);
+  const float *AH = reinterpret_cast<const float *>(sm + S::AH);
   {
-    float lt = l_run;
+    float lc = l_run, lt = l_t;
+    lc += __shfl_xor(lc, 16, 64);
+    lc += __shfl_xor(lc, 32, 64);
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    if (lane < GQ) { mm[w * GQ + lane] = m_run; ml[w * GQ + lane] = lt; }
+    if (lane < GQ) {
+      mm[w * GQ + lane] = m_run;
+      mlc[w * GQ + lane] = lc;
+      mlt[w * GQ + lane] = lt;
+      mhs[w * GQ + lane] = hsc;
+    }
     float *aw = mv + w * GQ * DH;
 #pragma unroll
-    for (int gi = 0; gi < GQ; ++gi) {
-      aw[gi * DH + 2 * lane] = accV[gi][0];
-      aw[gi * DH + 2 * lane + 1] = accV[gi][1];
-    }
-    // the tail as a ninth contributor (no hidden sums)
-    float *at = mv + NW * GQ * DH;
-    if (tid < GQ) {
-      mm[NW * GQ + tid] = tb < te && tid < g ? Ts[tid] : -INFINITY;
-      ml[NW * GQ + tid] = tb < te && tid < g ? Ts[GQ + tid] : 0.f;
-    }
-    {
-      const int gi = tid / DH, d = tid % DH;
-      if (gi < GQ) at[gi * DH + d] = (tb < te && gi < g) ? tacc : 0.f;
-    }
+    for (int gi = 0; gi < GQ; ++gi)
+      *reinterpret_cast<float2 *>(aw + gi * DH + 2 * lane) = make_float2(accV[gi][0], accV[gi][1]);
   }
   __syncthreads();
   float *part = a.part + (((long)b * a.Hkv + h) * a.n_split + s) * g * a.PW;
-  constexpr int PWC = 4 + F + DH;
-  for (int i = tid; i < g * PWC; i += NTH) {
-    const int gi = i / PWC, c = i % PWC;
+  if (tid < g) {  // per query head: the common maximum and each wave's weights
     float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k <= NW; ++k) M = fmaxf(M, mm[k * GQ + gi]);
-    float wt[NW + 1];
+    for (int k = 0; k < NW; ++k) M = fmaxf(M, mm[k * GQ + tid]);
+    float L = 0.f, mass = 0.f;
 #pragma unroll
-    for (int k = 0; k <= NW; ++k) wt[k] = mm[k * GQ + gi] == -INFINITY ? 0.f : exp2f(mm[k * GQ + gi] - M);
-    float v = 0.f;
-    if (c == 0) {
-      v = M;
-    } else if (c == 1 || c == 2) {  // l over everything, mass over rebuilt tokens
-#pragma unroll
-      for (int k = 0; k < NW; ++k) v = fmaf(wt[k], ml[k * GQ + gi], v);
-      if (c == 1) v = fmaf(wt[NW], ml[NW * GQ + gi], v);
-    } else if (c >= 4 && c < 4 + F) {
-#pragma unroll
-      for (int k = 0; k < NW; ++k) v = fmaf(wt[k], AH[(k * GQ + gi) * F + c - 4], v);
-    } else if (c >= 4 + F) {
-#pragma unroll
-      for (int k = 0; k <= NW; ++k) v = fmaf(wt[k], mv[(k * GQ + gi) * DH + c - 4 - F], v);
+    for (int k = 0; k < NW; ++k) {
+      const float mk = mm[k * GQ + tid];
+      const float wt = mk == -INFINITY ? 0.f : exp2f(mk - M);
+      mwt[k * GQ + tid] = wt;
+      mwh[k * GQ + tid] = wt * mhs[k * GQ + tid];
+      L = fmaf(wt, mlc[k * GQ + tid] + mlt[k * GQ + tid], L);
+      mass = fmaf(wt, mlc[k * GQ + tid], mass);
     }
-    part[(long)gi * a.PW + c] = v;
+    part[(long)tid * a.PW + 0] = M;
+    part[(long)tid * a.PW + 1] = L;
+    part[(long)tid * a.PW + 2] = mass;
+    part[(long)tid * a.PW + 3] = 0.f;
   }
+  __syncthreads();
+  for (int i = tid; i < g * (F + DH); i += NTH) {
+    const int gi = i / (F + DH), c = i % (F + DH);
+    float v = 0.f;
+    if (c < F) {
+#pragma unroll
+      for (int k = 0; k < NW; ++k) v = fmaf(mwh[k * GQ + gi], AH[(k * GQ + gi) * F + c], v);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NW; ++k) v = fmaf(mwt[k * GQ + gi], mv[(k * GQ + gi) * DH + c - F], v);
+    }
+    part[(long)gi * a.PW + 4 + c] = v;
+  }
+  asm volatile("" ::"v"(pf_acc));  // the prefetch reads stay live (no code)
 }
 
 template <typename TC, int NR, int NF>
@@ -747,7 +942,7 @@ void chain_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps,
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
   int iters = (n_tiles + want * chain::NW - 1) / (want * chain::NW);
-  if (iters > 8) iters = 8;
+  if (iters > chain::MAXIT) iters = chain::MAXIT;
   tps = iters * chain::NW;
   n_split = (n_tiles + tps - 1) / tps;
   tail_per_split = (T + n_split - 1) / n_split;

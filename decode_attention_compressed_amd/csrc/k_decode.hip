@@ -703,7 +703,158 @@ hipError_t launch_attend_valu(int act, int coeff, int resid, const AttendArgs &a
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// D7 for d_h = 128, bf16, at most 4 query heads per kv head and F a multiple
+// of 128: one workgroup per (sequence, kv head, quarter of the head dims)
+// merges the splits of all query heads of the kv head and applies the rows of
+// W2 it owns.  Every global read is issued before the first is used (split
+// heads, hidden sums, value sums, W2 rows and b2): one memory round trip.
+// Sums run in split order, so the result is deterministic.
+// grid (4, Hkv, B), 256 threads.
+// ---------------------------------------------------------------------------
+constexpr int KV_DQ = 32;    // head dims per workgroup
+constexpr int KV_SB = 16;    // splits whose loads are in flight together
+
+template <int F>
+__global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
+  constexpr int DH = 128, GM = 4, FP = F / 4;       // float4 pieces of a hidden row
+  constexpr int PPT = (GM * FP + 255) / 256;          // (g, piece) pairs per thread
+  constexpr int WPT = F / 8 / 8;                      // 16-byte W2 pieces per thread (8 threads per row)
+  __shared__ float hd[64][GM][3];                     // split heads m, l, mass
+  __shared__ float wt[64][GM];                        // split weights
+  __shared__ float fin[GM][3];                        // M, 1/L, mass
+  __shared__ __align__(16) float accHm[GM][F];
+  __shared__ float accVm[GM][KV_DQ];
+  const int dq = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int g = a.g, S = a.n_total;
+  const long sstride = (long)g * a.PW;
+  const float *p0 = a.part + ((long)b * a.Hkv + h) * S * sstride;
+  const long bh = ((long)b * a.G + a.layer) * a.Hkv + h;
+  const uint16_t *W2 = reinterpret_cast<const uint16_t *>(a.w2) + (bh * DH + (long)dq * KV_DQ) * F;
+  const uint16_t *B2 = reinterpret_cast<const uint16_t *>(a.b2) + bh * DH + dq * KV_DQ;
+
+  // W2 rows of this quarter and b2 (independent of the partials)
+  const int wr = tid >> 3, ws = tid & 7;             // row, eighth of the row
+  u32x4 w2r[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) w2r[i] = gld16(W2 + (long)wr * F + ws * (F / 8) + 8 * i);
+  const float b2v = bf16_bits_to_f32(B2[wr]);
+  // hidden and value sums of the first KV_SB splits: thread pairs (gi, piece)
+  // and (gi, dd), loads in flight before the split heads are combined
+  const int vg = tid / KV_DQ, vd = tid % KV_DQ;
+  f32v4 hp[PPT][KV_SB];
+  float vv[KV_SB];
+  auto load_batch = [&](int s0, int nb) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int pr = tid + 256 * k, gi = pr / FP, pc = pr % FP;
+#pragma unroll
+      for (int u = 0; u < KV_SB; ++u)
+        if (u < nb && gi < g)
+          hp[k][u] = *reinterpret_cast<const f32v4 *>(p0 + (long)(s0 + u) * sstride + (long)gi * a.PW + 4 + 4 * pc);
+    }
+#pragma unroll
+    for (int u = 0; u < KV_SB; ++u)
+      if (u < nb && vg < g) vv[u] = p0[(long)(s0 + u) * sstride + (long)vg * a.PW + 4 + F + dq * KV_DQ + vd];
+  };
+  load_batch(0, min(KV_SB, S));
+  // split heads
+  for (int i = tid; i < S * g; i += 256) {
+    const u32x4 v = gld16(p0 + (long)(i / g) * sstride + (long)(i % g) * a.PW);
+    hd[i / g][i % g][0] = __uint_as_float(v.x);
+    hd[i / g][i % g][1] = __uint_as_float(v.y);
+    hd[i / g][i % g][2] = __uint_as_float(v.z);
+  }
+  f32v4 hacc[PPT];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) hacc[k] = f32v4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  if (tid < g) {  // common maximum, weights, 1/L and the rebuilt-token mass
+    float M = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, hd[sp][tid][0]);
+    float L = 0.f, mass = 0.f;
+    for (int sp = 0; sp < S; ++sp) {
+      const float m = hd[sp][tid][0];
+      const float w = m == -INFINITY ? 0.f : exp2f(m - M);
+      wt[sp][tid] = w;
+      L = fmaf(w, hd[sp][tid][1], L);
+      mass = fmaf(w, hd[sp][tid][2], mass);
+    }
+    fin[tid][0] = M;
+    fin[tid][1] = 1.0f / L;
+    fin[tid][2] = mass;
+  }
+  __syncthreads();
+  float vsum = 0.f;
+  for (int s0 = 0; s0 < S; s0 += KV_SB) {
+    const int nb = min(KV_SB, S - s0);
+    if (s0 > 0) load_batch(s0, nb);
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int pr = tid + 256 * k, gi = pr / FP;
+      if (gi < g) {
+#pragma unroll
+        for (int u = 0; u < KV_SB; ++u)
+          if (u < nb) {
+            const float w = wt[s0 + u][gi];
+            hacc[k].x = fmaf(w, hp[k][u].x, hacc[k].x);
+            hacc[k].y = fmaf(w, hp[k][u].y, hacc[k].y);
+            hacc[k].z = fmaf(w, hp[k][u].z, hacc[k].z);
+            hacc[k].w = fmaf(w, hp[k][u].w, hacc[k].w);
+          }
+      }
+    }
+    if (vg < g) {
+#pragma unroll
+      for (int u = 0; u < KV_SB; ++u)
+        if (u < nb) vsum = fmaf(wt[s0 + u][vg], vv[u], vsum);
+    }
+  }
+  if (vg < g) accVm[vg][vd] = vsum;
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int pr = tid + 256 * k, gi = pr / FP, pc = pr % FP;
+    if (gi < GM) *reinterpret_cast<f32v4 *>(&accHm[gi][4 * pc]) = hacc[k];
+  }
+  __syncthreads();
+  // out[gi][d] = (W2[d] . accH[gi] + b2[d] mass[gi] + accV[gi][d]) / L[gi]
+  float dot[GM] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int f0 = ws * (F / 8) + 8 * i;
+    const uint32_t wv[4] = {w2r[i].x, w2r[i].y, w2r[i].z, w2r[i].w};
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) {
+      const f32v4 h0 = *reinterpret_cast<const f32v4 *>(&accHm[gi][f0]);
+      const f32v4 h1 = *reinterpret_cast<const f32v4 *>(&accHm[gi][f0 + 4]);
+      const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot[gi] = fmaf(bf16_bits_to_f32(wv[e] & 0xFFFFu), hv[2 * e], dot[gi]);
+        dot[gi] = fmaf(bf16_bits_to_f32(wv[e] >> 16), hv[2 * e + 1], dot[gi]);
+      }
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < GM; ++gi) {  // the eight partial dots of a row, fixed order
+    dot[gi] += __shfl_xor(dot[gi], 1, 64);
+    dot[gi] += __shfl_xor(dot[gi], 2, 64);
+    dot[gi] += __shfl_xor(dot[gi], 4, 64);
+  }
+  if (ws == 0) {
+    bf16 *out = reinterpret_cast<bf16 *>(a.out) + ((long)b * a.Hq + (long)h * g) * DH + dq * KV_DQ + wr;
+    for (int gi = 0; gi < g; ++gi)
+      store_f32(out + (long)gi * DH, (dot[gi] + fmaf(b2v, fin[gi][2], accVm[gi][wr])) * fin[gi][1]);
+  }
+}
+
 hipError_t launch_combine(int act, const CombineArgs &a, hipStream_t st) {
+  if (act == LOWRAM_BF16 && a.F > 0 && a.n_comp > 0 && a.dh == 128 && a.g <= 4 && a.n_total <= 64) {
+    const dim3 grid(128 / KV_DQ, a.Hkv, a.B);
+    if (a.F == 128) { hipLaunchKernelGGL(k_combine_kv<128>, grid, dim3(256), 0, st, a); return hipGetLastError(); }
+    if (a.F == 256) { hipLaunchKernelGGL(k_combine_kv<256>, grid, dim3(256), 0, st, a); return hipGetLastError(); }
+    if (a.F == 512) { hipLaunchKernelGGL(k_combine_kv<512>, grid, dim3(256), 0, st, a); return hipGetLastError(); }
+  }
   // stage: CB * sub splits of (F + dh) floats, sub = 256 / (piece stride) <= 1024 / (F + dh)
   const int n_out = a.F + a.dh, per = n_out / 4;
   const int sub = 256 / (per <= 64 ? 64 : (per <= 128 ? 128 : 256));

@@ -201,9 +201,14 @@ lowram_status check_decode_inputs(const lowram_dims *d, int32_t layer, const low
   return LOWRAM_OK;
 }
 
+// True when the chained attend kernel ranks the chunk scores itself.
+bool attend_selects(const lowram_dims *d, const DecodePlan &p) {
+  return p.tps > 0 && n_chunks(d) <= CHAIN_SELECT_MAX_NC;
+}
+
 AttendArgs make_attend(const lowram_dims *d, int32_t layer, const lowram_model *m,
                        const lowram_cache *c, const void *q, const void *kt, const void *vt,
-                       void *ws, const DecodePlan &p) {
+                       void *ws, const DecodePlan &p, int32_t *sel_out) {
   AttendArgs a;
   memset(&a, 0, sizeof a);
   a.q = q; a.k_tail = kt; a.v_tail = vt;
@@ -214,6 +219,8 @@ AttendArgs make_attend(const lowram_dims *d, int32_t layer, const lowram_model *
     a.res_scale = (const uint16_t *)c->res_scale;
   }
   a.sel = reinterpret_cast<const int32_t *>((char *)ws + p.sel_off);
+  a.scores = attend_selects(d, p) ? reinterpret_cast<const double *>((char *)ws + p.sc_off) : nullptr;
+  a.sel_out = attend_selects(d, p) ? sel_out : nullptr;
   a.part = reinterpret_cast<float *>((char *)ws + p.part_off);
   a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
   a.r = d->rank; a.F = d->hidden; a.N = d->n_ctx; a.C = d->chunk; a.T = d->n_tail;
@@ -301,6 +308,31 @@ lowram_status lowram_compress(const lowram_dims *d, const lowram_model *m, const
   return hip_status(run_compress(a, (hipStream_t)stream), "lowram_compress");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scores, and the selection itself unless the attend kernel will rank the
+// scores (with_topk false); arguments already validated.
+lowram_status run_select(const lowram_dims *d, int32_t layer, const lowram_model *m,
+                         const lowram_cache *c, const void *q, int32_t *sel_out, void *ws,
+                         const DecodePlan &p, bool with_topk, void *stream) {
+  if (p.k_eff == 0) return LOWRAM_OK;
+  const long D = (long)d->layers * d->heads_kv * d->head_dim;
+  int32_t *sel = reinterpret_cast<int32_t *>((char *)ws + p.sel_off);
+  double *qt = reinterpret_cast<double *>((char *)ws + p.qt_off);
+  double *sc = reinterpret_cast<double *>((char *)ws + p.sc_off);
+  return hip_status(launch_select(d->act, q, (long)d->heads_q * d->head_dim, m->basis, c->landmark,
+                                  d->batch, d->heads_q, d->heads_kv, d->head_dim, d->rank,
+                                  n_chunks(d), (int)D, layer, with_topk ? p.k_eff : 0, sel, sel_out,
+                                  sc, qt, (hipStream_t)stream),
+                    "lowram_decode_select");
+}
+
+}  // namespace
+
+extern "C" {
+
 lowram_status lowram_decode_select(const lowram_dims *d, int32_t layer, const lowram_model *m,
                                    const lowram_cache *c, const void *q, int32_t *sel_out,
                                    void *ws, size_t ws_bytes, void *stream) {
@@ -311,16 +343,7 @@ lowram_status lowram_decode_select(const lowram_dims *d, int32_t layer, const lo
   REQUIRE_PTR(q);
   OPTIONAL_PTR(sel_out);
   if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
-  if (p.k_eff == 0) return LOWRAM_OK;
-  const long D = (long)d->layers * d->heads_kv * d->head_dim;
-  int32_t *sel = reinterpret_cast<int32_t *>((char *)ws + p.sel_off);
-  double *qt = reinterpret_cast<double *>((char *)ws + p.qt_off);
-  double *sc = reinterpret_cast<double *>((char *)ws + p.sc_off);
-  return hip_status(launch_select(d->act, q, (long)d->heads_q * d->head_dim, m->basis, c->landmark,
-                                  d->batch, d->heads_q, d->heads_kv, d->head_dim, d->rank,
-                                  n_chunks(d), (int)D, layer, p.k_eff, sel, sel_out, sc, qt,
-                                  (hipStream_t)stream),
-                    "lowram_decode_select");
+  return run_select(d, layer, m, c, q, sel_out, ws, p, true, stream);
 }
 
 lowram_status lowram_decode_attend(const lowram_dims *d, int32_t layer, const lowram_model *m,
@@ -333,7 +356,7 @@ lowram_status lowram_decode_attend(const lowram_dims *d, int32_t layer, const lo
   REQUIRE_PTR(q);
   if (d->n_tail > 0) { REQUIRE_PTR(k_tail); REQUIRE_PTR(v_tail); }
   if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
-  const AttendArgs a = make_attend(d, layer, m, c, q, k_tail, v_tail, ws, p);
+  const AttendArgs a = make_attend(d, layer, m, c, q, k_tail, v_tail, ws, p, nullptr);
   return hip_status(launch_attend(d->act, d->coeff, d->resid, a, (hipStream_t)stream),
                     "lowram_decode_attend");
 }
@@ -375,8 +398,14 @@ lowram_status lowram_decode_attn(const lowram_dims *d, int32_t layer, const lowr
   if (d->n_tail > 0) { REQUIRE_PTR(k_tail); REQUIRE_PTR(v_tail); }
   if (p.k_eff > 0) { REQUIRE_PTR(m->w2); REQUIRE_PTR(m->b2); }
   if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
-  if ((st = lowram_decode_select(d, layer, m, c, q, sel_out, ws, ws_bytes, stream)) != LOWRAM_OK) return st;
-  if ((st = lowram_decode_attend(d, layer, m, c, q, k_tail, v_tail, ws, ws_bytes, stream)) != LOWRAM_OK) return st;
+  // When the attend kernel ranks the scores itself, the top-k kernel is skipped
+  // and the attend kernel writes sel_out; the results are the same bits.
+  const bool in_attend = attend_selects(d, p);
+  if ((st = run_select(d, layer, m, c, q, in_attend ? nullptr : sel_out, ws, p, !in_attend, stream)) != LOWRAM_OK)
+    return st;
+  const AttendArgs a = make_attend(d, layer, m, c, q, k_tail, v_tail, ws, p, sel_out);
+  if ((st = hip_status(launch_attend(d->act, d->coeff, d->resid, a, (hipStream_t)stream), "lowram_decode_attend")) != LOWRAM_OK)
+    return st;
   return lowram_decode_combine(d, layer, m, out, ws, ws_bytes, stream);
 }
 
