@@ -92,6 +92,16 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 __device__ __forceinline__ f16x8 ldh8(const uint16_t *p) { return *reinterpret_cast<const f16x8 *>(p); }
 __device__ __forceinline__ bf16x8 ldb8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
+// The hidden pre-activation is kept in units of -log2(e): W1 and b1 are scaled
+// by -log2(e) when staged, so with y = -log2(e) x, SiLU(x) = x / (1 + e^-x)
+// becomes -ln(2) * y / (1 + 2^y): one exp2, one reciprocal and one product.
+// The factor -ln(2) is applied once, to the merged hidden sums.
+constexpr float NEG_LOG2E = -1.4426950408889634f;
+constexpr float NEG_LN2 = -0.6931471805599453f;
+__device__ __forceinline__ float silu_scaled(float y) {
+  return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
+}
+
 // Position of head dim d inside the permuted order: within each 32-wide step,
 // lane group kg of the step-1 output holds dims 4kg..4kg+3 and 16+4kg..16+4kg+3,
 // which become its eight consecutive k positions 8kg..8kg+7.
@@ -116,9 +126,9 @@ struct Smem {
   // the chunk scores of the in-kernel selection use the p area (free until the first softmax)
   static_assert(CHAIN_SELECT_MAX_NC * 12 <= NW * GQ * TT * 4, "score staging does not fit");
   // merge area (after the last tile): per wave and query head m, l of rebuilt
-  // tokens, l of tail tokens, accH rescale owed, merge weights; then accV
+  // tokens, l of tail tokens, scale owed by accH; then accV
   static constexpr int MM = 0, MLC = MM + NW * GQ * 4, MLT = MLC + NW * GQ * 4, MHS = MLT + NW * GQ * 4;
-  static constexpr int MWT = MHS + NW * GQ * 4, MWH = MWT + NW * GQ * 4, MV = MWH + NW * GQ * 4;
+  static constexpr int MV = MHS + NW * GQ * 4;
   static_assert(MV + NW * GQ * DH * 4 <= QS, "merge area does not fit");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
@@ -307,8 +317,9 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   };
   // L2 prefetch of k-step q of the wave's tile: one 4-byte read per token row
   // brings the row's k-step sector into L2 ahead of the register loads.  The
-  // word read is folded into pf_acc PD steps later (by then the register load
-  // of the same k-step has been waited for anyway), which keeps the read live.
+  // word read is consumed PD steps later by an empty asm statement (by then the
+  // register load of the same k-step has been waited for anyway); that keeps
+  // the read live without extending its register's lifetime.
   constexpr int PFN = TT / WAVE;  // prefetch reads per k-step
   auto prefetch = [&](int q, int i) -> uint32_t {
     return __builtin_amdgcn_raw_buffer_load_b32(Cr, pf_voff, (uint32_t)(((row0 + WAVE * i) * r + q * KS) * CT::ES), 0);
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
     selv = selp[q0 + tid];
   }
-  uint32_t pf_acc = 0u, pfr[PD][PFN];
+  uint32_t pfr[PD][PFN];
 #pragma unroll
   for (int k = 0; k < PD; ++k)
 #pragma unroll
@@ -450,10 +461,9 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   for (int k = 0; k < W1P; ++k) {
     const int p = tid + NTH * k, f = p / (DH / 8), d0 = 8 * (p % (DH / 8));
     const u32x4 v = w1r[k];
-    const uint2 lo = make_uint2(pack2(bf16_bits_to_f32(v.x & 0xFFFFu), bf16_bits_to_f32(v.x >> 16)),
-                                pack2(bf16_bits_to_f32(v.y & 0xFFFFu), bf16_bits_to_f32(v.y >> 16)));
-    const uint2 hi = make_uint2(pack2(bf16_bits_to_f32(v.z & 0xFFFFu), bf16_bits_to_f32(v.z >> 16)),
-                                pack2(bf16_bits_to_f32(v.w & 0xFFFFu), bf16_bits_to_f32(v.w >> 16)));
+    auto sc = [](uint32_t u) { return bf16_bits_to_f32(u) * NEG_LOG2E; };
+    const uint2 lo = make_uint2(pack2(sc(v.x & 0xFFFFu), sc(v.x >> 16)), pack2(sc(v.y & 0xFFFFu), sc(v.y >> 16)));
+    const uint2 hi = make_uint2(pack2(sc(v.z & 0xFFFFu), sc(v.z >> 16)), pack2(sc(v.w & 0xFFFFu), sc(v.w >> 16)));
     *reinterpret_cast<uint2 *>(W1s + f * WLD + dpos(d0)) = lo;
     *reinterpret_cast<uint2 *>(W1s + f * WLD + dpos(d0 + 4)) = hi;
   }
@@ -471,10 +481,9 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   }
   if (tid < F / 8) {
     float *bo = B1s + 8 * tid;
-    *reinterpret_cast<f32x4 *>(bo) = f32x4{bf16_bits_to_f32(braw.x & 0xFFFFu), bf16_bits_to_f32(braw.x >> 16),
-                                           bf16_bits_to_f32(braw.y & 0xFFFFu), bf16_bits_to_f32(braw.y >> 16)};
-    *reinterpret_cast<f32x4 *>(bo + 4) = f32x4{bf16_bits_to_f32(braw.z & 0xFFFFu), bf16_bits_to_f32(braw.z >> 16),
-                                               bf16_bits_to_f32(braw.w & 0xFFFFu), bf16_bits_to_f32(braw.w >> 16)};
+    auto sc = [](uint32_t u) { return bf16_bits_to_f32(u) * NEG_LOG2E; };
+    *reinterpret_cast<f32x4 *>(bo) = f32x4{sc(braw.x & 0xFFFFu), sc(braw.x >> 16), sc(braw.y & 0xFFFFu), sc(braw.y >> 16)};
+    *reinterpret_cast<f32x4 *>(bo + 4) = f32x4{sc(braw.z & 0xFFFFu), sc(braw.z >> 16), sc(braw.w & 0xFFFFu), sc(braw.w >> 16)};
   }
 #pragma unroll
   for (int i = 0; i < TPP; ++i) {
@@ -530,7 +539,8 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     }
     // this tile's residual rows: CSR range of the chunk (loads issued here, read
     // late in step 1), then the tile's part of it
-    const int jc = has ? (int)(row0 / C) : 0;
+    const int jc = has ? (int)(row0 >> 7) : 0;  // 128-token chunks
+    static_assert(CPT * TT == 128, "chunk index by shift");
     const int e0r = rptr[jc], e1r = rptr[jc + 1];
     int e0 = 0, e1 = 0;
     constexpr int RM = CPT * TT / WAVE;         // chunk entries per lane (C <= 64 RM)
@@ -565,7 +575,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       }
       if constexpr (ks >= PD) {  // the prefetch of this k-step
 #pragma unroll
-        for (int i = 0; i < PFN; ++i) pf_acc ^= pfr[ks % PD][i];
+        for (int i = 0; i < PFN; ++i) asm volatile("" ::"v"(pfr[ks % PD][i]));
       }
       if constexpr (ks + PD < NR) {
 #pragma unroll
@@ -661,7 +671,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const _Float16 p = (_Float16)exp2f(lg[tt][v] - m_new);
+        const _Float16 p = (_Float16)__builtin_amdgcn_exp2f(lg[tt][v] - m_new);
         PA[tt >> 1][4 * (tt & 1) + v] = p;
         lg[tt][v] = (float)p;
         psum += (float)p;
@@ -715,30 +725,37 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     // ---- steps 3 and 4 per 16-wide hidden tile ------------------------------------
     // accH[g][f] of this tile: lane holds column f = 16 fi + l16, rows g = 4 kg + v;
     // each hidden tile is folded into the wave's running accH in LDS right away
-    // (the real rows g < GQ live in lanes 0..15)
+    // (the real rows g < GQ live in lanes 0..15).  Software-pipelined: the W1
+    // products of tile fi + 1 are issued before the SiLU of tile fi, so the
+    // matrix cores work while the vector ALUs evaluate SiLU.
     const uint16_t *w1_rd = W1s + l16 * WLD + 8 * kg;   // + 16 fi WLD + 32 jj
     const float *b1_rd = B1s + l16;
     float *ah_rw = AHw + l16;
-#pragma unroll 2
-    for (int fi = 0; fi < NF; ++fi) {
+    auto hidden_mfma = [&](int fi, f32x4 *hc) {
       const float bias = b1_rd[16 * fi];
-      f32x4 hc[NTT];
+      f16x8 bw[NJ];
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) bw[jj] = ldh8(w1_rd + 16 * fi * WLD + 32 * jj);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) hc[tt] = f32x4{bias, bias, bias, bias};
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        const f16x8 bw = ldh8(w1_rd + 16 * fi * WLD + 32 * jj);
+      for (int jj = 0; jj < NJ; ++jj)  // head-dim step outer: four independent chains
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) hc[tt] = mfma(KA[jj][tt], bw, hc[tt]);
-      }
+        for (int tt = 0; tt < NTT; ++tt) hc[tt] = mfma(KA[jj][tt], bw[jj], hc[tt]);
+    };
+    f32x4 hcur[NTT], hnext[NTT];
+    hidden_mfma(0, hcur);
+#pragma unroll
+    for (int fi = 0; fi < NF; ++fi) {
+      if (fi + 1 < NF) hidden_mfma(fi + 1, hnext);
       f32x4 ahc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NTT / 2; ++i) {
         f16x8 hb;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          hb[v] = (_Float16)silu_f(hc[2 * i][v]);
-          hb[4 + v] = (_Float16)silu_f(hc[2 * i + 1][v]);
+          hb[v] = (_Float16)silu_scaled(hcur[2 * i][v]);
+          hb[4 + v] = (_Float16)silu_scaled(hcur[2 * i + 1][v]);
         }
         ahc = mfma(PA[i], hb, ahc);
       }
@@ -749,6 +766,8 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
           *pa = first ? ahc[v] : fmaf(*pa, ah[v], ahc[v]);
         }
       }
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) hcur[tt] = hnext[tt];
     }
     first = false;
   }
@@ -803,7 +822,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       float ps = 0.f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float p = 4 * kg + v < nt ? (float)(_Float16)exp2f(lt4[v] - m_new) : 0.f;
+        const float p = 4 * kg + v < nt ? (float)(_Float16)__builtin_amdgcn_exp2f(lt4[v] - m_new) : 0.f;
         lt4[v] = p;
         ps += p;
       }
@@ -842,7 +861,6 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   __syncthreads();  // W1 and the basis slabs are free from here
   float *mm = reinterpret_cast<float *>(sm + S::MM), *mlc = reinterpret_cast<float *>(sm + S::MLC);
   float *mlt = reinterpret_cast<float *>(sm + S::MLT), *mhs = reinterpret_cast<float *>(sm + S::MHS);
-  float *mwt = reinterpret_cast<float *>(sm + S::MWT), *mwh = reinterpret_cast<float *>(sm + S::MWH);
   float *mv = reinterpret_cast<float *>(sm + S::MV);
   const float *AH = reinterpret_cast<const float *>(sm + S::AH);
   {
@@ -855,7 +873,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       mm[w * GQ + lane] = m_run;
       mlc[w * GQ + lane] = lc;
       mlt[w * GQ + lane] = lt;
-      mhs[w * GQ + lane] = hsc;
+      mhs[w * GQ + lane] = hsc * NEG_LN2;  // hidden sums were accumulated in -log2(e) units
     }
     float *aw = mv + w * GQ * DH;
 #pragma unroll
@@ -864,39 +882,54 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   }
   __syncthreads();
   float *part = a.part + (((long)b * a.Hkv + h) * a.n_split + s) * g * a.PW;
-  if (tid < g) {  // per query head: the common maximum and each wave's weights
-    float M = -INFINITY;
+  // every thread derives the weights of its query head from the wave maxima
+  auto weights = [&](int gi, float *wt, float &M) {
+    M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) M = fmaxf(M, mm[k * GQ + tid]);
+    for (int k = 0; k < NW; ++k) M = fmaxf(M, mm[k * GQ + gi]);
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float mk = mm[k * GQ + gi];
+      wt[k] = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+    }
+  };
+  if (tid < g) {
+    float wt[NW], M;
+    weights(tid, wt, M);
     float L = 0.f, mass = 0.f;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
-      const float mk = mm[k * GQ + tid];
-      const float wt = mk == -INFINITY ? 0.f : exp2f(mk - M);
-      mwt[k * GQ + tid] = wt;
-      mwh[k * GQ + tid] = wt * mhs[k * GQ + tid];
-      L = fmaf(wt, mlc[k * GQ + tid] + mlt[k * GQ + tid], L);
-      mass = fmaf(wt, mlc[k * GQ + tid], mass);
+      L = fmaf(wt[k], mlc[k * GQ + tid] + mlt[k * GQ + tid], L);
+      mass = fmaf(wt[k], mlc[k * GQ + tid], mass);
     }
     part[(long)tid * a.PW + 0] = M;
     part[(long)tid * a.PW + 1] = L;
     part[(long)tid * a.PW + 2] = mass;
     part[(long)tid * a.PW + 3] = 0.f;
   }
-  __syncthreads();
-  for (int i = tid; i < g * (F + DH); i += NTH) {
-    const int gi = i / (F + DH), c = i % (F + DH);
-    float v = 0.f;
-    if (c < F) {
+  constexpr int PC = (F + DH) / 4;  // float4 outputs per query head
+  for (int i = tid; i < g * PC; i += NTH) {
+    const int gi = i / PC, c4 = 4 * (i % PC);
+    float wt[NW], M;
+    weights(gi, wt, M);
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c4 < F) {
 #pragma unroll
-      for (int k = 0; k < NW; ++k) v = fmaf(mwh[k * GQ + gi], AH[(k * GQ + gi) * F + c], v);
+      for (int k = 0; k < NW; ++k) {
+        const float wh = wt[k] * mhs[k * GQ + gi];
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(AH + (k * GQ + gi) * F + c4);
+        v = f32x4{fmaf(wh, x[0], v[0]), fmaf(wh, x[1], v[1]), fmaf(wh, x[2], v[2]), fmaf(wh, x[3], v[3])};
+      }
     } else {
 #pragma unroll
-      for (int k = 0; k < NW; ++k) v = fmaf(mwt[k * GQ + gi], mv[(k * GQ + gi) * DH + c - F], v);
+      for (int k = 0; k < NW; ++k) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(mv + (k * GQ + gi) * DH + c4 - F);
+        v = f32x4{fmaf(wt[k], x[0], v[0]), fmaf(wt[k], x[1], v[1]), fmaf(wt[k], x[2], v[2]), fmaf(wt[k], x[3], v[3])};
+      }
     }
-    part[(long)gi * a.PW + 4 + c] = v;
+    *reinterpret_cast<f32x4 *>(part + (long)gi * a.PW + 4 + c4) = v;
   }
-  asm volatile("" ::"v"(pf_acc));  // the prefetch reads stay live (no code)
+
 }
 
 template <typename TC, int NR, int NF>
