@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic_llama8b_32k.json")
-ATTEND_SRC = os.path.join(ROOT, "decode_attention_compressed_amd", "csrc", "k_attend_mfma.hip")
+ATTEND_SRC = os.path.join(ROOT, "decode_attention_compressed_amd", "csrc", "k_attend_chain.hip")
 
 
 def log(msg):
@@ -58,7 +58,8 @@ def attend_accounting(s, sel, res_ptr, layer):
     bytes: the union over kv heads of the selected coefficient tiles (each
     read once per sequence), the layer's basis slice and first predictor
     layer, residual rows (+int32 index) and CSR pointers of the selected
-    chunks, the layer's tail K/V and the queries.
+    chunks, the layer's tail K/V, the queries and the chunk scores the kernel
+    ranks for its own top-k.
     flops: per selected token-head 2(d_h r + F d_h + g d_h + g F) (rebuilt key,
     hidden layer, logits, p-weighted hidden sum), plus the tail's 4 T d_h per
     query head."""
@@ -78,6 +79,7 @@ def attend_accounting(s, sel, res_ptr, layer):
     if s.resid == "i8":
         nbytes += B * Hkv * dh * 2
     nbytes += 2 * B * Hkv * T * dh * sa + B * s.Hq * dh * sa
+    nbytes += B * Hkv * (s.N_after // C) * 8
     g = s.Hq // Hkv
     flops = B * Hkv * sel.shape[-1] * C * 2 * (dh * r + F * dh + g * dh + g * F) + B * s.Hq * T * dh * 4
     return nbytes, flops, union
@@ -241,7 +243,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
     roof["traffic"] = traffic_for_current_kernel()
-    roof.update({"kernel": "k_attend_mfma (rebuild-and-attend)", "avg_launch_us": round(t_attend * 1e6, 2),
+    roof.update({"kernel": "k_attend_chain (top-k + rebuild-and-attend)", "avg_launch_us": round(t_attend * 1e6, 2),
                  "algorithmic_bytes_per_launch": int(a_bytes), "algorithmic_flops_per_launch": int(a_flops),
                  "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                  "hbm_gbps": round(gbps, 1), "roof_time_us": round(max(t_hbm, t_mfma) * 1e6, 2),

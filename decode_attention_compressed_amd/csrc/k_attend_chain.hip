@@ -523,17 +523,26 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
+  // Restart of the coefficient and basis pipelines for iteration it_next: issued
+  // on every path at the end of an iteration (also after the last one, where the
+  // coefficient reads fall out of range), so that the registers carried around
+  // the loop always hold fresh loads and nothing of step 1 stays live through
+  // the softmax and hidden phases.
+  auto restart = [&](int it_next) {
+    const int tau_n = t_begin + w + NW * it_next;
+    row0 = tau_n < t_end ? tile_row(tau_n) : (long)a.N;
+#pragma unroll
+    for (int q = 0; q < DC - 1; ++q)
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) cr[q][tt] = CT::ld(Cr, c_voff, c_soff(tt, q));
+#pragma unroll
+    for (int q = 0; q < LU; ++q) ST::ld(Ur, csc, u_voff, r, q * KS, ur[q % NU], us_[q % NU]);
+  };
+
   for (int it = 0; it < iters; ++it) {
     const int tau = t_begin + w + NW * it;
     const bool has = tau < t_end;
-    if (it > 0) {  // restart the coefficient and basis pipelines for the next tile
-      row0 = has ? tile_row(tau) : (long)a.N;
-#pragma unroll
-      for (int q = 0; q < DC - 1; ++q)
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) cr[q][tt] = CT::ld(Cr, c_voff, c_soff(tt, q));
-#pragma unroll
-      for (int q = 0; q < LU; ++q) ST::ld(Ur, csc, u_voff, r, q * KS, ur[q % NU], us_[q % NU]);
+    if (it > 0) {
       ST::st(Us, ur[0], us_[0]);   // slab 0 -> buffer 0 (last read two barriers ago)
       __syncthreads();
     }
@@ -628,7 +637,10 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     });
-    if (!has) continue;
+    if (!has) {
+      restart(it + 1);
+      continue;
+    }
 
     // ---- rebuilt keys as fp16 A operands --------------------------------------
     f16x8 KA[NJ][NTT];
@@ -770,6 +782,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       for (int tt = 0; tt < NTT; ++tt) hcur[tt] = hnext[tt];
     }
     first = false;
+    restart(it + 1);
   }
   if (first && kg == 0) {  // a wave with no tile contributes zeros
 #pragma unroll

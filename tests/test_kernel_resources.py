@@ -1,0 +1,46 @@
+"""Register budget of the fused select-rebuild-attend kernel, checked at
+compile time on the host: every instantiation must fit its registers without
+scratch.  A spill there is written back to HBM once per tile and read again,
+which the kernel's traffic cannot afford, and it is invisible to the parity
+tests."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "decode_attention_compressed_amd", "csrc")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def resource_usage(src):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", os.devnull]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out, cur = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            out[cur] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+)", line)
+        if m and cur:
+            out[cur][m.group(1).strip()] = int(m.group(2))
+    return out
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
+def test_chain_kernel_has_no_scratch():
+    use = resource_usage("k_attend_chain.hip")
+    kernels = {k: v for k, v in use.items() if "k_attend_chain" in k}
+    assert len(kernels) >= 5, sorted(use)
+    for name, v in kernels.items():
+        assert v.get("ScratchSize") == 0, (name, v)
+        assert v.get("VGPRs Spill") == 0, (name, v)
+        assert v.get("VGPRs", 999) <= 256, (name, v)
