@@ -20,7 +20,8 @@ struct AttendArgs {
   const uint16_t *res_scale;    // [B][G][Hkv][dh] f16 or null
   const void *k_tail, *v_tail;  // [B][G][Hkv][T][dh] act
   const int32_t *sel;           // [B][Hkv][k_eff]
-  const double *scores;         // [B][Hkv][n_c] fp64 when the attend kernel selects itself, else null
+  const double *score_part;     // [B][Hkv][select_rank_blocks(r)][n_c] fp64 partial chunk scores
+                                // when the attend kernel selects itself, else null
   int32_t *sel_out;             // [B][Hkv][k_eff] copy of the selection (in-kernel selection only) or null
   float *part;                  // [B][Hkv][n_split+1][g][PW]
   int B, G, Hq, Hkv, dh, r, F, N, C, T, k_eff, n_res, layer;
@@ -37,13 +38,16 @@ struct CombineArgs {
 };
 
 // launchers (return hipSuccess or the launch error)
-// Chunk scores (float64) into scores [B][Hkv][n_c] (workspace), through the
-// q~ workspace qt [B][Hkv][r]; if k_eff > 0 the selection into sel and,
-// optionally, a copy into sel_out (k_eff = 0: scores only).
+// Chunk scores (float64).  Partial scores per block of 64 ranks go to part
+// [B][Hkv][select_rank_blocks(r)][n_c] (workspace); the score of a chunk is the
+// sum of its partials in block order.  If scores is not null the sums are
+// written to scores [B][Hkv][n_c], and if k_eff > 0 (scores required) the
+// selection into sel and, optionally, a copy into sel_out.
+inline int select_rank_blocks(int r) { return (r + 63) / 64; }
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
-                         double *scores, double *qt, hipStream_t st);
+                         double *part, double *scores, hipStream_t st);
 hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st);
 // Register-chained rebuild-and-attend: the shapes it covers, its split plan
 // (splits per (b, h), 64-token tiles per split, tail tokens per split) and the
@@ -83,8 +87,8 @@ struct EvictArgs {
   const int32_t *res_ptr, *res_idx; const void *res_val;
   void *d_coeff; float *d_landmark; int32_t *d_res_ptr, *d_res_idx; void *d_res_val;
   int32_t *keep_out;            // [B][keep]
+  double *spart;                // workspace [B][Hkv][select_rank_blocks(r)][n_c]
   double *scores;               // workspace [B][Hkv][n_c]
-  double *qt;                   // workspace [B][Hkv][r]
   double *acc;                  // workspace [B][n_c]
   int B, G, Hq, Hkv, dh, r, N, C, n_res, act, coeff_dt, resid_dt;
 };

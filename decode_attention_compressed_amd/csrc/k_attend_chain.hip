@@ -120,7 +120,7 @@ struct Smem {
   static constexpr int PS = B1 + F * 4;                  // [NW][TT][GQ] fp32 p
   static constexpr int TK = PS + NW * GQ * TT * 4;       // [TP][DH] bf16 tail keys
   static constexpr int TV = TK + TP * DH * 2;            // [TP][DH] bf16 tail values
-  static constexpr int AH = TV + TP * DH * 2;            // [NW][GQ][F] fp32 running accH per wave
+  static constexpr int AH = TV + TP * DH * 2;            // [NW][F][GQ] fp32 running accH per wave
   static constexpr int SEL = AH + NW * GQ * F * 4;       // [MAXSLOT] chunks of this split, [NW] counts
   static constexpr int BYTES = SEL + (MAXSLOT + NW) * 4;
   // the chunk scores of the in-kernel selection use the p area (free until the first softmax)
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile offsets stay scalar
   const int l16 = lane & 15, kg = lane >> 4;
-  float *AHw = reinterpret_cast<float *>(sm + S::AH) + w * GQ * F;  // this wave's running accH
+  float *AHw = reinterpret_cast<float *>(sm + S::AH) + w * F * GQ;  // this wave's running accH, [f][g]
   int b, h, s;
   coords(a, b, h, s);
   const int g = a.g, r = NR * KS, C = a.C;
@@ -329,8 +329,18 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   const int n_c = a.N / C;
   double scv = 0.0;
   int selv = 0;
-  if (a.scores) {
-    if (tid < n_c) scv = a.scores[((long)b * a.Hkv + h) * n_c + tid];
+  if (a.score_part) {  // a chunk's score: its rank blocks' partials summed in block order
+    constexpr int NRB = NR * KS / 64;
+    static_assert(NR * KS % 64 == 0, "whole rank blocks");
+    if (tid < n_c) {
+      const double *sp = a.score_part + ((long)b * a.Hkv + h) * NRB * n_c + tid;
+      double pv[NRB];
+#pragma unroll
+      for (int k = 0; k < NRB; ++k) pv[k] = sp[(long)k * n_c];
+      scv = pv[0];
+#pragma unroll
+      for (int k = 1; k < NRB; ++k) scv += pv[k];
+    }
   } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
     selv = selp[q0 + tid];
   }
@@ -380,7 +390,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   // asc), in ascending index order.  With the scores at hand every workgroup
   // ranks them itself (two threads per chunk compare against half of the
   // chunks each); split 0 also writes the whole selection to sel_out.
-  if (a.scores) {
+  if (a.score_part) {
     // Ranks use the top 32 bits of the order key of each fp64 score: a larger
     // top half means a larger score, a smaller one a smaller score.  Only
     // chunks whose top half ties another chunk's are ranked again on the
@@ -491,12 +501,15 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     lst16(Tk + row * DH + c8, tkr[i]);
     lst16(Tv + row * DH + c8, tvr[i]);
   }
+  // the wave's running accH starts at zero (a wave without a tile leaves it so)
+#pragma unroll
+  for (int i = 0; i < F * GQ / (4 * WAVE); ++i)
+    *reinterpret_cast<f32x4 *>(AHw + 4 * (lane + WAVE * i)) = f32x4{0.f, 0.f, 0.f, 0.f};
   ST::st(Us, ur[0], us_[0]);   // slab 0 -> buffer 0
   __syncthreads();
 
   // per-wave softmax state: lane holds query head l16 (rows >= g are padding)
   float m_run = -INFINITY, l_run = 0.f;
-  bool first = true;  // no tile attended yet: the running accH in LDS is undefined
   float accV[GQ][2];
 #pragma unroll
   for (int i = 0; i < GQ; ++i) accV[i][0] = accV[i][1] = 0.f;
@@ -737,12 +750,16 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     // ---- steps 3 and 4 per 16-wide hidden tile ------------------------------------
     // accH[g][f] of this tile: lane holds column f = 16 fi + l16, rows g = 4 kg + v;
     // each hidden tile is folded into the wave's running accH in LDS right away
-    // (the real rows g < GQ live in lanes 0..15).  Software-pipelined: the W1
-    // products of tile fi + 1 are issued before the SiLU of tile fi, so the
+    // (the real rows g < GQ live in lanes 0..15, whose four values are one
+    // 16-byte word of the [f][g] layout, read before the products that update
+    // it).  The running accH starts at zero and the first tile's rescale factor
+    // is zero, so the fold needs no first-tile case.  Software-pipelined: the
+    // W1 products of tile fi + 1 are issued before the SiLU of tile fi, so the
     // matrix cores work while the vector ALUs evaluate SiLU.
     const uint16_t *w1_rd = W1s + l16 * WLD + 8 * kg;   // + 16 fi WLD + 32 jj
     const float *b1_rd = B1s + l16;
-    float *ah_rw = AHw + l16;
+    f32x4 *ah_rw = reinterpret_cast<f32x4 *>(AHw) + l16;  // + 16 fi
+    const f32x4 ahv = f32x4{ah[0], ah[1], ah[2], ah[3]};
     auto hidden_mfma = [&](int fi, f32x4 *hc) {
       const float bias = b1_rd[16 * fi];
       f16x8 bw[NJ];
@@ -759,6 +776,8 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     hidden_mfma(0, hcur);
 #pragma unroll
     for (int fi = 0; fi < NF; ++fi) {
+      f32x4 prev = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (kg == 0) prev = ah_rw[16 * fi];
       if (fi + 1 < NF) hidden_mfma(fi + 1, hnext);
       f32x4 ahc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -771,24 +790,13 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
         }
         ahc = mfma(PA[i], hb, ahc);
       }
-      if (kg == 0) {
-#pragma unroll
-        for (int v = 0; v < GQ; ++v) {
-          float *pa = ah_rw + v * F + 16 * fi;
-          *pa = first ? ahc[v] : fmaf(*pa, ah[v], ahc[v]);
-        }
-      }
+      if (kg == 0)
+        ah_rw[16 * fi] = f32x4{fmaf(prev[0], ahv[0], ahc[0]), fmaf(prev[1], ahv[1], ahc[1]),
+                               fmaf(prev[2], ahv[2], ahc[2]), fmaf(prev[3], ahv[3], ahc[3])};
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) hcur[tt] = hnext[tt];
     }
-    first = false;
     restart(it + 1);
-  }
-  if (first && kg == 0) {  // a wave with no tile contributes zeros
-#pragma unroll
-    for (int fi = 0; fi < NF; ++fi)
-#pragma unroll
-      for (int v = 0; v < GQ; ++v) AHw[v * F + 16 * fi + l16] = 0.f;
   }
 
   // ---- the split's share of the uncompressed tail: the last wave, 16 tokens at
@@ -920,27 +928,40 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     part[(long)tid * a.PW + 2] = mass;
     part[(long)tid * a.PW + 3] = 0.f;
   }
-  constexpr int PC = (F + DH) / 4;  // float4 outputs per query head
-  for (int i = tid; i < g * PC; i += NTH) {
-    const int gi = i / PC, c4 = 4 * (i % PC);
-    float wt[NW], M;
-    weights(gi, wt, M);
-    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (c4 < F) {
+  // items [0, F): hidden column f for every query head (one 16-byte [f][g] word
+  // per wave); items [F, F + g DH / 4): four value dims of one query head
+  for (int i = tid; i < F + g * (DH / 4); i += NTH) {
+    if (i < F) {
+      float wh[GQ][NW];  // wave weights times the owed rescale; zero for padded heads
 #pragma unroll
-      for (int k = 0; k < NW; ++k) {
-        const float wh = wt[k] * mhs[k * GQ + gi];
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(AH + (k * GQ + gi) * F + c4);
-        v = f32x4{fmaf(wh, x[0], v[0]), fmaf(wh, x[1], v[1]), fmaf(wh, x[2], v[2]), fmaf(wh, x[3], v[3])};
+      for (int gi = 0; gi < GQ; ++gi) {
+        float M;
+        weights(gi, wh[gi], M);
+#pragma unroll
+        for (int k = 0; k < NW; ++k) wh[gi][k] = gi < g ? wh[gi][k] * mhs[k * GQ + gi] : 0.f;
       }
-    } else {
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NW; ++k) {
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(mv + (k * GQ + gi) * DH + c4 - F);
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(AH + (k * F + i) * GQ);
+#pragma unroll
+        for (int gi = 0; gi < GQ; ++gi) v[gi] = fmaf(wh[gi][k], x[gi], v[gi]);
+      }
+#pragma unroll
+      for (int gi = 0; gi < GQ; ++gi)
+        if (gi < g) part[(long)gi * a.PW + 4 + i] = v[gi];
+    } else {
+      const int gi = (i - F) / (DH / 4), c4 = 4 * ((i - F) % (DH / 4));
+      float wt[NW], M;
+      weights(gi, wt, M);
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NW; ++k) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(mv + (k * GQ + gi) * DH + c4);
         v = f32x4{fmaf(wt[k], x[0], v[0]), fmaf(wt[k], x[1], v[1]), fmaf(wt[k], x[2], v[2]), fmaf(wt[k], x[3], v[3])};
       }
+      *reinterpret_cast<f32x4 *>(part + (long)gi * a.PW + 4 + F + c4) = v;
     }
-    *reinterpret_cast<f32x4 *>(part + (long)gi * a.PW + 4 + c4) = v;
   }
 
 }

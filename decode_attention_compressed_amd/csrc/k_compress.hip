@@ -488,7 +488,7 @@ hipError_t run_evict(const EvictArgs &a, hipStream_t st) {
                                 ((long)w * a.B * a.G + l) * a.Hq * a.dh * esz;
       hipError_t e = launch_select(a.act, qb, (long)a.G * a.Hq * a.dh, a.basis, a.landmark, a.B,
                                    a.Hq, a.Hkv, a.dh, a.r, n_c, D, l, 0, nullptr, nullptr,
-                                   a.scores, a.qt, st);
+                                   a.spart, a.scores, st);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(k_evict_accum, dim3((n_c + 255) / 256, a.B), dim3(256), 0, st, a.scores,
                          a.acc, a.Hkv, n_c, (w == 0 && l == 0) ? 1 : 0);

@@ -22,20 +22,17 @@
 namespace lowram {
 
 // ---------------------------------------------------------------------------
-// D1-D3 in three wide kernels (the scorer reads the basis slices of all heads
+// D1-D3 in two wide kernels (the scorer reads the basis slices of all heads
 // and every landmark; spreading it over hundreds of workgroups keeps those
 // reads in flight together):
-//   k_qtilde  q~_{b,h} = U_{l,h}^T sum_{g in group(h)} q_g     (float64)
-//   k_scores  s_{b,h,j} = q~_{b,h} . landmark_{b,j}             (float64)
-//   k_topk    top min(k, n_c) chunks per (b, h) by (s desc, j asc), ascending
+//   k_select_partial q~_{b,h} = U_{l,h}^T sum_{g in group(h)} q_g, and the
+//                    partial scores q~ . landmark_{b,j} of one rank block  (float64)
+//   k_select_sum     s_{b,h,j}: the blocks' partials summed in block order
+//   k_topk           top min(k, n_c) chunks per (b, h) by (s desc, j asc), ascending
 // Every score is reduced in the same fixed order (lane partials, then a
 // butterfly), so equal landmark rows give equal scores.
 // ---------------------------------------------------------------------------
-constexpr int QT_I = 64;  // ranks per q~ workgroup
-
-// grid (ceil(r / 64), Hkv, B), 256 threads: 8 groups of 8 ranks x 32 row
-// slices; slice s sums rows s, s + 32, ... in order, then the slices are added
-// in slice order.
+// 8 consecutive basis values of one row as float64
 template <typename TA> struct Load8;
 template <> struct Load8<bf16> {
   typedef u32x4 raw;
@@ -61,21 +58,94 @@ template <> struct Load8<float> {
   }
 };
 
+// Sums R rows of per-lane partials over the lanes that differ in the log2 R
+// lane bits OFF0, OFF0 / 2, ... (R a power of two).  Each step also
+// transposes: over lane bit k a lane keeps the half of its rows that its bit
+// selects and adds the partner's partials of those rows, so one value per
+// lane remains.  Every row is summed by the same pairwise tree whatever its
+// position, so equal inputs give equal sums.  On return a lane holds the row
+// whose index has the lane's bits OFF0, OFF0 / 2, ... as its binary digits,
+// most significant first.
+template <int N, int OFF>
+__device__ __forceinline__ void xpose_step(double *v, int lane) {
+  if constexpr (N > 1) {
+    const bool hi = (lane & OFF) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const double keep = hi ? v[N / 2 + i] : v[i];
+      const double send = hi ? v[i] : v[N / 2 + i];
+      v[i] = keep + __shfl_xor(send, OFF, WAVE);
+    }
+    xpose_step<N / 2, OFF / 2>(v, lane);
+  }
+}
+template <int R, int OFF0>
+__device__ __forceinline__ double xpose_sum(double (&v)[R], int lane) {
+  static_assert((R & (R - 1)) == 0 && R <= 2 * OFF0, "R a power of two within the lane bits");
+  xpose_step<R, OFF0>(v, lane);
+  return v[0];
+}
+
+// D1 and D2 per block of 64 ranks.  grid (ceil(r / 64), Hkv, B), 256 threads;
+// block rb of (b, h) writes part[b][h][rb][j] = sum over its ranks i of
+// q~_i landmark_{b,j,i}, with q~ = U_{l,h}^T sum_g q_g restricted to the block.
+// The chunk score is the sum of the blocks' partials in block order (summed by
+// the consumer).  Splitting the rank dimension reads every basis row once and
+// each landmark row once per kv head; a split over chunks would make every
+// workgroup rebuild the whole q~.
+//
+// q~ of the block: lane (rank group lane & 7, slice 8 w + (lane >> 3)) sums
+// eight ranks over head dims slice + 32 k in ascending k; the wave's eight
+// slices are added by a transposing butterfly and the four waves in order.
+// Partials: 16 lanes per chunk, four ranks (one 16-byte landmark piece) each,
+// sixteen chunk rows in flight per lane, then a transposing butterfly over
+// the 16 lanes.  Blocks are regrouped so that the heads of one (sequence,
+// rank block) share an XCD and its L2 copy of those landmark columns.
+constexpr int SEL_RB = 64;
+
 template <typename TA, int DH>
-__global__ __launch_bounds__(256) void k_qtilde(const TA *__restrict__ q, long q_bstride,
-                                                const TA *__restrict__ basis, int Hq, int Hkv, int r,
-                                                int D, int layer, double *__restrict__ qt) {
-  constexpr int RPS = DH / 32;  // rows per slice
+__global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q, long q_bstride,
+                                                        const TA *__restrict__ basis,
+                                                        const float *__restrict__ landmark, int Hq,
+                                                        int Hkv, int r, int n_c, int D, int layer,
+                                                        double *__restrict__ part) {
+  constexpr int RPS = DH / 32;  // basis rows per slice
   __shared__ double qsum[DH];
-  __shared__ double part[32][QT_I];
-  const int i0 = blockIdx.x * QT_I, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int rg = tid % 8, slc = tid / 8;
-  const int ib = i0 + 8 * rg;             // first rank of this thread
-  const int ic = ib < r ? ib : r - 8;     // clamped (r is a multiple of 16)
-  const TA *U = basis + ((long)b * D + (long)(layer * Hkv + h) * DH) * r;
+  __shared__ double qtp[4][SEL_RB];
+  __shared__ double qt[SEL_RB];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int NRB = gridDim.x;
+  int rb, h, b;
+  {
+    const int P = NRB * gridDim.z;  // (sequence, rank block) pairs
+    const int lin = blockIdx.x + NRB * (blockIdx.y + Hkv * blockIdx.z);
+    if (P % 8 == 0) {
+      const int xcd = lin % 8, i = lin / 8, pr = xcd * (P / 8) + i / Hkv;
+      h = i % Hkv; b = pr / NRB; rb = pr % NRB;
+    } else {
+      rb = blockIdx.x; h = blockIdx.y; b = blockIdx.z;
+    }
+  }
+  const int i0 = rb * SEL_RB, nr = min(SEL_RB, r - i0);  // ranks of this block (a multiple of 16)
+
+  // basis rows of this thread: rank group rg, head dims sl + 32 k
+  const int rg = lane & 7, sl = 8 * w + (lane >> 3);
+  const bool rg_ok = 8 * rg < nr;
+  const TA *U = basis + ((long)b * D + (long)(layer * Hkv + h) * DH) * r + i0 + 8 * (rg_ok ? rg : 0);
   typename Load8<TA>::raw raw[RPS][Load8<TA>::N];
 #pragma unroll
-  for (int k = 0; k < RPS; ++k) Load8<TA>::ld(U + (long)(slc + 32 * k) * r + ic, raw[k]);
+  for (int k = 0; k < RPS; ++k) Load8<TA>::ld(U + (long)(sl + 32 * k) * r, raw[k]);
+  // landmark pieces of the first 16 chunk rows (independent of q~)
+  const int gq = lane >> 4, li = lane & 15;
+  const bool li_ok = 4 * li < nr;
+  const float *L = landmark + (long)b * n_c * r + i0 + 4 * (li_ok ? li : 0);
+  constexpr int MB = 16;  // chunk rows per lane in flight
+  u32x4 lv[MB];
+  auto load_rows = [&](int j_base) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m) lv[m] = gld16(L + (long)min(j_base + 16 * m + 4 * w + gq, n_c - 1) * r);
+  };
+  load_rows(0);
   if (tid < DH) {
     const int grp = Hq / Hkv;
     const TA *qb = q + (long)b * q_bstride + (long)h * grp * DH;
@@ -84,87 +154,55 @@ __global__ __launch_bounds__(256) void k_qtilde(const TA *__restrict__ q, long q
     qsum[tid] = sq;
   }
   __syncthreads();
-  double acc[8];
+  {
+    double acc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
 #pragma unroll
-  for (int k = 0; k < RPS; ++k) {
-    double u[8];
-    Load8<TA>::f64(raw[k], u);
-    const double w = qsum[slc + 32 * k];
+    for (int k = 0; k < RPS; ++k) {
+      double u[8];
+      Load8<TA>::f64(raw[k], u);
+      const double wq = qsum[sl + 32 * k];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fma(u[e], w, acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = fma(u[e], wq, acc[e]);
+    }
+    const double v = xpose_sum<8, 32>(acc, lane);  // rank 8 rg + (lane >> 3), this wave's slices
+    qtp[w][8 * rg + (lane >> 3)] = v;
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) part[slc][8 * rg + e] = acc[e];
   __syncthreads();
-  if (tid < QT_I && i0 + tid < r) {
-    double v = 0.0;
-#pragma unroll 8
-    for (int k = 0; k < 32; ++k) v += part[k][tid];
-    qt[((long)b * Hkv + h) * r + i0 + tid] = v;
+  if (tid < SEL_RB) qt[tid] = ((qtp[0][tid] + qtp[1][tid]) + qtp[2][tid]) + qtp[3][tid];
+  __syncthreads();
+
+  double qv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) qv[e] = li_ok ? qt[4 * li + e] : 0.0;
+  double *pb = part + (((long)b * Hkv + h) * NRB + rb) * n_c;
+  for (int j_base = 0; j_base < n_c; j_base += 16 * MB) {
+    if (j_base > 0) load_rows(j_base);
+    double sacc[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const uint32_t w4[4] = {lv[m].x, lv[m].y, lv[m].z, lv[m].w};
+      sacc[m] = 0.0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sacc[m] = fma((double)__uint_as_float(w4[e]), qv[e], sacc[m]);
+    }
+    const double tot = xpose_sum<MB, 8>(sacc, lane);  // chunk row li of lane group gq
+    const int j = j_base + 16 * li + 4 * w + gq;
+    if (j < n_c) pb[j] = tot;
   }
 }
 
-constexpr int SC_J = 32;  // chunks per score workgroup (8 per wave)
-
-// grid (ceil(n_c / 32), Hkv, B), 256 threads.  Lane l of a wave holds ranks
-// 256u + 4l .. +3 (u < NSEG) of q~; a wave scores one landmark row at a time
-// with RF rows in flight.  The blocks are regrouped so that every head of one
-// (sequence, chunk block) runs on the same XCD and shares its L2 copy of
-// those landmark rows.
-template <int NSEG>
-__global__ __launch_bounds__(256) void k_scores(const double *__restrict__ qt,
-                                                const float *__restrict__ landmark, int Hkv, int r,
-                                                int n_c, double *__restrict__ scores) {
-  constexpr int RF = NSEG <= 2 ? 8 : (NSEG == 4 ? 4 : 2);
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
-  int blk, h, b;
-  {
-    const int NB = gridDim.x, P = NB * gridDim.z;  // (sequence, chunk block) pairs
-    const int lin = blockIdx.x + NB * (blockIdx.y + Hkv * blockIdx.z);
-    if (P % 8 == 0) {
-      const int xcd = lin % 8, i = lin / 8, pr = xcd * (P / 8) + i / Hkv;
-      h = i % Hkv; b = pr / NB; blk = pr % NB;
-    } else {
-      blk = blockIdx.x; h = blockIdx.y; b = blockIdx.z;
-    }
-  }
-  double qv[NSEG][4];
-  int ioff[NSEG];
-  const double *qb = qt + ((long)b * Hkv + h) * r;
-#pragma unroll
-  for (int u = 0; u < NSEG; ++u) {
-    const int i = 256 * u + 4 * lane;
-    ioff[u] = i < r ? i : r - 4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) qv[u][e] = i < r ? qb[i + e] : 0.0;
-  }
-  const float *L = landmark + (long)b * n_c * r;
-  const int j0 = blk * SC_J + wv;
-#pragma unroll
-  for (int t0 = 0; t0 < SC_J / 4; t0 += RF) {
-    u32x4 lv[RF][NSEG];
-#pragma unroll
-    for (int t = 0; t < RF; ++t) {
-      const int j = min(j0 + 4 * (t0 + t), n_c - 1);
-#pragma unroll
-      for (int u = 0; u < NSEG; ++u) lv[t][u] = gld16(L + (long)j * r + ioff[u]);
-    }
-#pragma unroll
-    for (int t = 0; t < RF; ++t) {
-      double sacc = 0.0;
-#pragma unroll
-      for (int u = 0; u < NSEG; ++u) {
-        const uint32_t w4[4] = {lv[t][u].x, lv[t][u].y, lv[t][u].z, lv[t][u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sacc = fma((double)__uint_as_float(w4[e]), qv[u][e], sacc);
-      }
-      sacc = wave_sum(sacc);
-      const int j = j0 + 4 * (t0 + t);
-      if (lane == 0 && j < n_c) scores[((long)b * Hkv + h) * n_c + j] = sacc;
-    }
-  }
+// scores[b][h][j] = sum over rank blocks rb (in order) of part[b][h][rb][j].
+// grid (ceil(n_c / 256), Hkv, B), 256 threads.
+__global__ __launch_bounds__(256) void k_select_sum(const double *__restrict__ part, int Hkv, int n_c,
+                                                    int NRB, double *__restrict__ scores) {
+  const int j = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (j >= n_c) return;
+  const double *p = part + ((long)b * Hkv + h) * NRB * n_c + j;
+  double s = p[0];
+  for (int rb = 1; rb < NRB; ++rb) s += p[(long)rb * n_c];
+  scores[((long)b * Hkv + h) * n_c + j] = s;
 }
 
 constexpr int TK_NT = 1024;
@@ -630,34 +668,29 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 // launchers
 // ---------------------------------------------------------------------------
 template <typename TA>
-static void launch_qtilde(const TA *q, long q_bstride, const TA *basis, int B, int Hq, int Hkv, int dh,
-                          int r, int D, int layer, double *qt, hipStream_t st) {
-  const dim3 g((r + QT_I - 1) / QT_I, Hkv, B);
+static void launch_partial(const TA *q, long q_bstride, const TA *basis, const float *landmark, int B,
+                           int Hq, int Hkv, int dh, int r, int n_c, int D, int layer, double *part,
+                           hipStream_t st) {
+  const dim3 g(select_rank_blocks(r), Hkv, B);
   if (dh == 64)
-    hipLaunchKernelGGL((k_qtilde<TA, 64>), g, dim3(256), 0, st, q, q_bstride, basis, Hq, Hkv, r, D, layer, qt);
+    hipLaunchKernelGGL((k_select_partial<TA, 64>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part);
   else if (dh == 128)
-    hipLaunchKernelGGL((k_qtilde<TA, 128>), g, dim3(256), 0, st, q, q_bstride, basis, Hq, Hkv, r, D, layer, qt);
+    hipLaunchKernelGGL((k_select_partial<TA, 128>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part);
   else
-    hipLaunchKernelGGL((k_qtilde<TA, 256>), g, dim3(256), 0, st, q, q_bstride, basis, Hq, Hkv, r, D, layer, qt);
+    hipLaunchKernelGGL((k_select_partial<TA, 256>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part);
 }
 
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
-                         double *scores, double *qt, hipStream_t st) {
+                         double *part, double *scores, hipStream_t st) {
   if (act == LOWRAM_F32)
-    launch_qtilde<float>((const float *)q, q_bstride, (const float *)basis, B, Hq, Hkv, dh, r, D, layer, qt, st);
+    launch_partial<float>((const float *)q, q_bstride, (const float *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, st);
   else
-    launch_qtilde<bf16>((const bf16 *)q, q_bstride, (const bf16 *)basis, B, Hq, Hkv, dh, r, D, layer, qt, st);
-  const dim3 g2((n_c + SC_J - 1) / SC_J, Hkv, B);
-  if (r <= 256)
-    hipLaunchKernelGGL(k_scores<1>, g2, dim3(256), 0, st, qt, landmark, Hkv, r, n_c, scores);
-  else if (r <= 512)
-    hipLaunchKernelGGL(k_scores<2>, g2, dim3(256), 0, st, qt, landmark, Hkv, r, n_c, scores);
-  else if (r <= 1024)
-    hipLaunchKernelGGL(k_scores<4>, g2, dim3(256), 0, st, qt, landmark, Hkv, r, n_c, scores);
-  else
-    hipLaunchKernelGGL(k_scores<8>, g2, dim3(256), 0, st, qt, landmark, Hkv, r, n_c, scores);
+    launch_partial<bf16>((const bf16 *)q, q_bstride, (const bf16 *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, st);
+  if (!scores) return k_eff > 0 ? hipErrorInvalidValue : hipGetLastError();
+  hipLaunchKernelGGL(k_select_sum, dim3((n_c + 255) / 256, Hkv, B), dim3(256), 0, st, part, Hkv, n_c,
+                     select_rank_blocks(r), scores);
   if (k_eff > 0) {
     if (n_c <= TK_SMALL) {
       hipLaunchKernelGGL(k_topk_small, dim3(Hkv, B), dim3(TK_NT), 0, st, scores, Hkv, n_c, k_eff,

@@ -78,7 +78,7 @@ lowram_status check_dims(const lowram_dims *d) {
 // partial per selected chunk plus one for the tail.
 struct DecodePlan {
   int k_eff, cps, n_split, n_part, PW, tps, tail_per_split;
-  size_t sel_off, qt_off, sc_off, part_off, bytes;
+  size_t sel_off, sp_off, sc_off, part_off, bytes;
 };
 
 DecodePlan decode_plan(const lowram_dims *d) {
@@ -98,8 +98,9 @@ DecodePlan decode_plan(const lowram_dims *d) {
   }
   p.PW = 4 + d->hidden + d->head_dim;
   p.sel_off = 0;
-  p.qt_off = align_up(sizeof(int32_t) * (size_t)d->batch * d->heads_kv * (p.k_eff > 0 ? p.k_eff : 1));
-  p.sc_off = p.qt_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * d->rank);
+  p.sp_off = align_up(sizeof(int32_t) * (size_t)d->batch * d->heads_kv * (p.k_eff > 0 ? p.k_eff : 1));
+  p.sc_off = p.sp_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * select_rank_blocks(d->rank) *
+                                 (n_c > 0 ? n_c : 1));
   p.part_off = p.sc_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * (n_c > 0 ? n_c : 1));
   p.bytes = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * p.n_part * g * p.PW);
   return p;
@@ -120,15 +121,15 @@ CompressPlan compress_plan(const lowram_dims *d) {
 }
 
 struct EvictPlan {
-  size_t scores_off, qt_off, acc_off, keep_off, bytes;
+  size_t scores_off, spart_off, acc_off, keep_off, bytes;
 };
 
 EvictPlan evict_plan(const lowram_dims *d) {
   EvictPlan p;
   const size_t n_c = (size_t)(n_chunks(d) > 0 ? n_chunks(d) : 1);
   p.scores_off = 0;
-  p.qt_off = align_up(sizeof(double) * d->batch * d->heads_kv * n_c);
-  p.acc_off = p.qt_off + align_up(sizeof(double) * d->batch * d->heads_kv * d->rank);
+  p.spart_off = align_up(sizeof(double) * d->batch * d->heads_kv * n_c);
+  p.acc_off = p.spart_off + align_up(sizeof(double) * d->batch * d->heads_kv * select_rank_blocks(d->rank) * n_c);
   p.keep_off = p.acc_off + align_up(sizeof(double) * d->batch * n_c);
   p.bytes = p.keep_off + align_up(sizeof(int32_t) * d->batch * n_c);
   return p;
@@ -219,7 +220,7 @@ AttendArgs make_attend(const lowram_dims *d, int32_t layer, const lowram_model *
     a.res_scale = (const uint16_t *)c->res_scale;
   }
   a.sel = reinterpret_cast<const int32_t *>((char *)ws + p.sel_off);
-  a.scores = attend_selects(d, p) ? reinterpret_cast<const double *>((char *)ws + p.sc_off) : nullptr;
+  a.score_part = attend_selects(d, p) ? reinterpret_cast<const double *>((char *)ws + p.sp_off) : nullptr;
   a.sel_out = attend_selects(d, p) ? sel_out : nullptr;
   a.part = reinterpret_cast<float *>((char *)ws + p.part_off);
   a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
@@ -312,20 +313,21 @@ lowram_status lowram_compress(const lowram_dims *d, const lowram_model *m, const
 
 namespace {
 
-// Scores, and the selection itself unless the attend kernel will rank the
-// scores (with_topk false); arguments already validated.
+// Partial chunk scores, and the summed scores and the selection itself unless
+// the attend kernel will rank the scores (with_topk false); arguments already
+// validated.
 lowram_status run_select(const lowram_dims *d, int32_t layer, const lowram_model *m,
                          const lowram_cache *c, const void *q, int32_t *sel_out, void *ws,
                          const DecodePlan &p, bool with_topk, void *stream) {
   if (p.k_eff == 0) return LOWRAM_OK;
   const long D = (long)d->layers * d->heads_kv * d->head_dim;
   int32_t *sel = reinterpret_cast<int32_t *>((char *)ws + p.sel_off);
-  double *qt = reinterpret_cast<double *>((char *)ws + p.qt_off);
+  double *sp = reinterpret_cast<double *>((char *)ws + p.sp_off);
   double *sc = reinterpret_cast<double *>((char *)ws + p.sc_off);
   return hip_status(launch_select(d->act, q, (long)d->heads_q * d->head_dim, m->basis, c->landmark,
                                   d->batch, d->heads_q, d->heads_kv, d->head_dim, d->rank,
                                   n_chunks(d), (int)D, layer, with_topk ? p.k_eff : 0, sel, sel_out,
-                                  sc, qt, (hipStream_t)stream),
+                                  sp, with_topk ? sc : nullptr, (hipStream_t)stream),
                     "lowram_decode_select");
 }
 
@@ -443,7 +445,7 @@ lowram_status lowram_evict(const lowram_dims *d, const lowram_model *m, const lo
   a.d_res_idx = dst->res_idx; a.d_res_val = dst->res_val;
   a.keep_out = keep_out ? keep_out : reinterpret_cast<int32_t *>((char *)ws + p.keep_off);
   a.scores = reinterpret_cast<double *>((char *)ws + p.scores_off);
-  a.qt = reinterpret_cast<double *>((char *)ws + p.qt_off);
+  a.spart = reinterpret_cast<double *>((char *)ws + p.spart_off);
   a.acc = reinterpret_cast<double *>((char *)ws + p.acc_off);
   a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
   a.r = d->rank; a.N = d->n_ctx; a.C = d->chunk; a.n_res = d->n_res;
