@@ -109,6 +109,34 @@ __device__ __forceinline__ int dpos(int d) {
   return (d & ~31) + 8 * ((d & 15) >> 2) + 4 * ((d >> 4) & 1) + (d & 3);
 }
 
+// Sums R rows of per-lane partials over the lanes that differ in the log2 R
+// lane bits OFF0, OFF0 / 2, ..., then over the remaining lower lane bits.
+// Each transposing step keeps the half of a lane's rows that its lane bit
+// selects and adds the partner's values of those rows.  On return every lane
+// holds the wave total of row (lane >> (6 - log2 R)) when OFF0 = 32.
+template <int N, int OFF>
+__device__ __forceinline__ void xpose_step_f(float *v, int lane) {
+  if constexpr (N > 1) {
+    const bool hi = (lane & OFF) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float keep = hi ? v[N / 2 + i] : v[i];
+      const float send = hi ? v[i] : v[N / 2 + i];
+      v[i] = keep + __shfl_xor(send, OFF, 64);
+    }
+    xpose_step_f<N / 2, OFF / 2>(v, lane);
+  } else if constexpr (OFF > 0) {
+    v[0] += __shfl_xor(v[0], OFF, 64);
+    xpose_step_f<1, OFF / 2>(v, lane);
+  }
+}
+template <int R, int OFF0>
+__device__ __forceinline__ float xpose_sum_f(float (&v)[R], int lane) {
+  static_assert((R & (R - 1)) == 0 && R <= 2 * OFF0, "R a power of two within the lane bits");
+  xpose_step_f<R, OFF0>(v, lane);
+  return v[0];
+}
+
 // LDS layout (bytes).  The merge area at the end reuses W1 and the basis slabs;
 // each wave's running accH stays in LDS across its tiles.
 template <int F>
@@ -129,7 +157,8 @@ struct Smem {
   // tokens, l of tail tokens, scale owed by accH; then accV
   static constexpr int MM = 0, MLC = MM + NW * GQ * 4, MLT = MLC + NW * GQ * 4, MHS = MLT + NW * GQ * 4;
   static constexpr int MV = MHS + NW * GQ * 4;
-  static_assert(MV + NW * GQ * DH * 4 <= QS, "merge area does not fit");
+  static constexpr int MWT = MV + NW * GQ * DH * 4, MWH = MWT + NW * GQ * 4;  // merge weights
+  static_assert(MWH + NW * GQ * 4 <= QS, "merge area does not fit");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -799,82 +828,67 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     restart(it + 1);
   }
 
-  // ---- the split's share of the uncompressed tail: the last wave, 16 tokens at
-  // a time, logits on the matrix cores, p . v on the vector ALUs ---------------------
+  // ---- the split's share of the uncompressed tail: every wave takes tokens
+  // tb + w, tb + w + NW, ..., two at a time, logits and p . v on the vector ALUs
+  // (lane: head dims 2 lane, 2 lane + 1).  The eight partial logits of a pair
+  // (token u, head gi) are summed over the wave by a transposing butterfly.
   float l_t = 0.f;   // tail part of l
   float hsc = 1.f;   // rescale still owed by the running accH (applied in the merge)
-  if (w == NW - 1 && tb < te) {
-    f16x8 qf[NJ];
+  {
+    float qd[GQ][2];  // q of the kv head's query heads at the lane's dims (fp16 values)
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) qf[jj] = ldh8(Qs + l16 * WLD + 32 * jj + 8 * kg);
-    for (int t0 = tb; t0 < te; t0 += 16) {
-      const int nt = min(16, te - t0), tl = t0 - tb;
-      const bool staged = tl + 16 <= TP;
-      f16x8 kf[NJ];
+    for (int gi = 0; gi < GQ; ++gi) {
+      const uint32_t qq = *reinterpret_cast<const uint32_t *>(Qs + gi * WLD + dpos(2 * lane));
+      qd[gi][0] = f16_bits_to_f32(qq & 0xFFFFu);
+      qd[gi][1] = f16_bits_to_f32(qq >> 16);
+    }
+    auto row = [&](const uint16_t *lds, const uint16_t *glb, int t, float &x0, float &x1) {
+      const int tl = t - tb;
+      const uint32_t v2 = tl < TP ? *reinterpret_cast<const uint32_t *>(lds + tl * DH + 2 * lane)
+                                  : *reinterpret_cast<const uint32_t *>(glb + (long)t * DH + 2 * lane);
+      x0 = bf16_bits_to_f32(v2 & 0xFFFFu);
+      x1 = bf16_bits_to_f32(v2 >> 16);
+    };
+    for (int t0 = tb + w; t0 < te; t0 += 2 * NW) {
+      const bool two = t0 + NW < te;
+      float k0[2][2], v0[2][2];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
-        if (l16 < nt) {
-          const int dlo = 32 * jj + 4 * kg;
-          const uint16_t *src = staged ? Tk + (tl + l16) * DH : kt + (long)(t0 + l16) * DH;
-          lo = *reinterpret_cast<const uint2 *>(src + dlo);
-          hi = *reinterpret_cast<const uint2 *>(src + dlo + 16);
-        }
-        const uint32_t wv[4] = {lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kf[jj][2 * i] = (_Float16)bf16_bits_to_f32(wv[i] & 0xFFFFu);
-          kf[jj][2 * i + 1] = (_Float16)bf16_bits_to_f32(wv[i] >> 16);
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int t = u == 0 || two ? t0 + NW * u : t0;
+        row(Tk, kt, t, k0[u][0], k0[u][1]);
+        row(Tv, vt, t, v0[u][0], v0[u][1]);
       }
-      f32x4 lt4 = f32x4{0.f, 0.f, 0.f, 0.f};  // lane (g = l16, kg): tokens 4 kg + v
+      float pl[2 * GQ];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) lt4 = mfma(kf[jj], qf[jj], lt4);
-      float mt = -INFINITY;
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        lt4[v] = 4 * kg + v < nt ? lt4[v] * a.scale_log2 : -INFINITY;
-        mt = fmaxf(mt, lt4[v]);
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-      float ps = 0.f;
+        for (int gi = 0; gi < GQ; ++gi) pl[GQ * u + gi] = fmaf(qd[gi][0], k0[u][0], qd[gi][1] * k0[u][1]);
+      // lane l ends with the logit of pair (l >> 3): token (l >> 5), head (l >> 3) & 3
+      const float lsum = xpose_sum_f<2 * GQ, 32>(pl, lane);
+      const int hq = l16 & (GQ - 1);  // this lane's head (lanes past g are padding)
+      float lt2[2];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p = 4 * kg + v < nt ? (float)(_Float16)__builtin_amdgcn_exp2f(lt4[v] - m_new) : 0.f;
-        lt4[v] = p;
-        ps += p;
+      for (int u = 0; u < 2; ++u) lt2[u] = __shfl(lsum, 32 * u + 8 * hq, 64) * a.scale_log2;
+      if (!two) lt2[1] = -INFINITY;
+      const float m_new = fmaxf(m_run, fmaxf(lt2[0], lt2[1]));
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      float p2[2], ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        p2[u] = lt2[u] == -INFINITY ? 0.f : (float)(_Float16)__builtin_amdgcn_exp2f(lt2[u] - m_new);
+        ps += p2[u];
       }
       l_run *= alpha;
-      l_t = l_t * alpha + ps;
+      l_t = l_t * alpha + (kg == 0 ? ps : 0.f);  // l is kept as partials over the lane groups kg
       hsc *= alpha;
       m_run = m_new;
 #pragma unroll
       for (int gi = 0; gi < GQ; ++gi) {
         const float av = __shfl(alpha, gi, 64);
-        accV[gi][0] *= av;
-        accV[gi][1] *= av;
+        const float pa = __shfl(p2[0], gi, 64), pb = __shfl(p2[1], gi, 64);
+        accV[gi][0] = fmaf(pb, v0[1][0], fmaf(pa, v0[0][0], accV[gi][0] * av));
+        accV[gi][1] = fmaf(pb, v0[1][1], fmaf(pa, v0[0][1], accV[gi][1] * av));
       }
-      if (l16 < GQ) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Ps[(w * TT + 4 * kg + v) * GQ + l16] = lt4[v];
-      }
-      wave_lds_sync();
-      if (staged) {  // all 16 rows, branch-free: p is zero past nt
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const uint32_t v2 = *reinterpret_cast<const uint32_t *>(Tv + (tl + t) * DH + 2 * lane);
-          add_row(t, bf16_bits_to_f32(v2 & 0xFFFFu), bf16_bits_to_f32(v2 >> 16));
-        }
-      } else {
-        for (int t = 0; t < nt; ++t) {
-          const uint32_t v2 = *reinterpret_cast<const uint32_t *>(vt + (long)(t0 + t) * DH + 2 * lane);
-          add_row(t, bf16_bits_to_f32(v2 & 0xFFFFu), bf16_bits_to_f32(v2 >> 16));
-        }
-      }
-      wave_lds_sync();
     }
   }
 
@@ -903,27 +917,28 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   }
   __syncthreads();
   float *part = a.part + (((long)b * a.Hkv + h) * a.n_split + s) * g * a.PW;
-  // every thread derives the weights of its query head from the wave maxima
-  auto weights = [&](int gi, float *wt, float &M) {
-    M = -INFINITY;
+  // wave weights exp2(m_k - M) per query head, and the same times the rescale
+  // the wave still owes its hidden sums; zero for padded heads
+  float *mwt = reinterpret_cast<float *>(sm + S::MWT), *mwh = reinterpret_cast<float *>(sm + S::MWH);
+  if (tid < NW * GQ) {
+    const int k = tid / GQ, gi = tid % GQ;
+    float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) M = fmaxf(M, mm[k * GQ + gi]);
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const float mk = mm[k * GQ + gi];
-      wt[k] = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
-    }
-  };
+    for (int kk = 0; kk < NW; ++kk) M = fmaxf(M, mm[kk * GQ + gi]);
+    const float mk = mm[k * GQ + gi];
+    const float wt = (gi >= g || mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+    mwt[k * GQ + gi] = wt;
+    mwh[k * GQ + gi] = wt * mhs[k * GQ + gi];
+    if (k == 0 && gi < g) part[(long)gi * a.PW + 0] = M;
+  }
+  __syncthreads();
   if (tid < g) {
-    float wt[NW], M;
-    weights(tid, wt, M);
     float L = 0.f, mass = 0.f;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
-      L = fmaf(wt[k], mlc[k * GQ + tid] + mlt[k * GQ + tid], L);
-      mass = fmaf(wt[k], mlc[k * GQ + tid], mass);
+      L = fmaf(mwt[k * GQ + tid], mlc[k * GQ + tid] + mlt[k * GQ + tid], L);
+      mass = fmaf(mwt[k * GQ + tid], mlc[k * GQ + tid], mass);
     }
-    part[(long)tid * a.PW + 0] = M;
     part[(long)tid * a.PW + 1] = L;
     part[(long)tid * a.PW + 2] = mass;
     part[(long)tid * a.PW + 3] = 0.f;
@@ -932,38 +947,29 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   // per wave); items [F, F + g DH / 4): four value dims of one query head
   for (int i = tid; i < F + g * (DH / 4); i += NTH) {
     if (i < F) {
-      float wh[GQ][NW];  // wave weights times the owed rescale; zero for padded heads
-#pragma unroll
-      for (int gi = 0; gi < GQ; ++gi) {
-        float M;
-        weights(gi, wh[gi], M);
-#pragma unroll
-        for (int k = 0; k < NW; ++k) wh[gi][k] = gi < g ? wh[gi][k] * mhs[k * GQ + gi] : 0.f;
-      }
       f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NW; ++k) {
         const f32x4 x = *reinterpret_cast<const f32x4 *>(AH + (k * F + i) * GQ);
+        const f32x4 wh = *reinterpret_cast<const f32x4 *>(mwh + k * GQ);
 #pragma unroll
-        for (int gi = 0; gi < GQ; ++gi) v[gi] = fmaf(wh[gi][k], x[gi], v[gi]);
+        for (int gi = 0; gi < GQ; ++gi) v[gi] = fmaf(wh[gi], x[gi], v[gi]);
       }
 #pragma unroll
       for (int gi = 0; gi < GQ; ++gi)
         if (gi < g) part[(long)gi * a.PW + 4 + i] = v[gi];
     } else {
       const int gi = (i - F) / (DH / 4), c4 = 4 * ((i - F) % (DH / 4));
-      float wt[NW], M;
-      weights(gi, wt, M);
       f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NW; ++k) {
+        const float wt = mwt[k * GQ + gi];
         const f32x4 x = *reinterpret_cast<const f32x4 *>(mv + (k * GQ + gi) * DH + c4);
-        v = f32x4{fmaf(wt[k], x[0], v[0]), fmaf(wt[k], x[1], v[1]), fmaf(wt[k], x[2], v[2]), fmaf(wt[k], x[3], v[3])};
+        v = f32x4{fmaf(wt, x[0], v[0]), fmaf(wt, x[1], v[1]), fmaf(wt, x[2], v[2]), fmaf(wt, x[3], v[3])};
       }
       *reinterpret_cast<f32x4 *>(part + (long)gi * a.PW + 4 + F + c4) = v;
     }
   }
-
 }
 
 template <typename TC, int NR, int NF>
