@@ -152,7 +152,7 @@ struct Smem {
   static constexpr int SEL = AH + NW * GQ * F * 4;       // [MAXSLOT] chunks of this split, [NW] counts
   static constexpr int BYTES = SEL + (MAXSLOT + NW) * 4;
   // the chunk scores of the in-kernel selection use the p area (free until the first softmax)
-  static_assert(CHAIN_SELECT_MAX_NC * 12 <= NW * GQ * TT * 4, "score staging does not fit");
+  static_assert(CHAIN_SELECT_MAX_NC * 8 <= NW * GQ * TT * 4, "score staging does not fit");
   // merge area (after the last tile): per wave and query head m, l of rebuilt
   // tokens, l of tail tokens, scale owed by accH; then accV
   static constexpr int MM = 0, MLC = MM + NW * GQ * 4, MLT = MLC + NW * GQ * 4, MHS = MLT + NW * GQ * 4;
@@ -417,72 +417,112 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
 
   // ---- chunk selection of (b, h): the top k_eff chunks by (score desc, index
   // asc), in ascending index order.  With the scores at hand every workgroup
-  // ranks them itself (two threads per chunk compare against half of the
-  // chunks each); split 0 also writes the whole selection to sel_out.
+  // selects them itself: wave 0 holds the order keys of all chunks (chunk
+  // 64 i + lane in slot i) and finds the k-th largest key by a bitwise search
+  // on its top 32 bits, then on the low 32 bits among the chunks that tie
+  // there (a uniform branch, rare outside crafted ties).  Every count is a
+  // 64-lane compare mask and a popcount.  Chunks whose whole key equals the
+  // threshold (equal doubles) are taken lowest index first.  Split 0 also
+  // writes the whole selection to sel_out.
   if (a.score_part) {
-    // Ranks use the top 32 bits of the order key of each fp64 score: a larger
-    // top half means a larger score, a smaller one a smaller score.  Only
-    // chunks whose top half ties another chunk's are ranked again on the
-    // exact fp64 values (a uniform branch, rare outside crafted ties).
     double *scL = reinterpret_cast<double *>(sm + S::PS);
-    uint32_t *khL = reinterpret_cast<uint32_t *>(scL + CHAIN_SELECT_MAX_NC);
-    int *wcnt = selL + MAXSLOT;
-    if (tid < n_c) {
-      scL[tid] = scv;
-      khL[tid] = (uint32_t)(f64_order_key(scv) >> 32);
-    }
+    if (tid < n_c) scL[tid] = scv;
     __syncthreads();
-    const int tpc = n_c <= NTH / 2 ? 2 : 1;
-    const int c = tid / tpc, half = tid % tpc;
-    const int i0 = tpc == 2 ? half * ((n_c + 1) / 2) : 0;
-    const int i1 = tpc == 2 && half == 0 ? (n_c + 1) / 2 : n_c;
-    int gt = 0, ge = 0;
-    if (c < n_c) {  // the reads of one index are the same in every lane: LDS broadcasts
-      const uint32_t kc = khL[c];
-      int i = i0;
-      for (; i + 16 <= i1; i += 16) {
-        uint32_t u[16];
+    if (w == 0) {
+      constexpr int NSL = CHAIN_SELECT_MAX_NC / WAVE;  // key slots per lane
+      uint32_t khi[NSL], klo[NSL];
+      uint64_t valid[NSL];
+      double sv[NSL];  // the staging area holds CHAIN_SELECT_MAX_NC scores: read all, mask later
 #pragma unroll
-        for (int k = 0; k < 16; ++k) u[k] = khL[i + k];
+      for (int i = 0; i < NSL; ++i) sv[i] = scL[WAVE * i + lane];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          gt += (int)(u[k] > kc);
-          ge += (int)(u[k] >= kc);
+      for (int i = 0; i < NSL; ++i) {
+        const int c = WAVE * i + lane;
+        const uint64_t key = c < n_c ? f64_order_key(sv[i]) : 0ull;
+        khi[i] = (uint32_t)(key >> 32);
+        klo[i] = (uint32_t)key;
+        valid[i] = __ballot(c < n_c);
+      }
+      const int k = a.k_eff;
+      // count of chunks with top half >= x (slots past n_c have no valid lanes),
+      // summed as a tree
+      auto count_hi = [&](uint32_t x) {
+        int c8[NSL];
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) c8[i] = __popcll(__ballot(khi[i] >= x) & valid[i]);
+#pragma unroll
+        for (int n = NSL / 2; n > 0; n /= 2)
+#pragma unroll
+          for (int i = 0; i < n; ++i) c8[i] += c8[i + n];
+        return c8[0];
+      };
+      // the k-th largest top half, highest bit first; stops as soon as exactly
+      // k chunks lie at or above the bits fixed so far (further low bits could
+      // only drop chunks below k)
+      uint32_t th = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = th | (1u << bit);
+        const int cnt = count_hi(cand);
+        if (cnt >= k) th = cand;
+        if (cnt == k) break;
+      }
+      uint64_t eq_hi[NSL], sel[NSL];
+      int n_gt = 0, n_eq = 0;
+#pragma unroll
+      for (int i = 0; i < NSL; ++i) {
+        sel[i] = __ballot(khi[i] > th) & valid[i];
+        eq_hi[i] = __ballot(khi[i] == th) & valid[i];
+        n_gt += __popcll(sel[i]);
+        n_eq += __popcll(eq_hi[i]);
+      }
+      if (n_gt + n_eq == k) {  // the threshold's top half is shared by exactly the missing chunks
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) sel[i] |= eq_hi[i];
+      } else {  // more chunks share that top half than are missing: decide on the low halves
+        const int need = k - n_gt;
+        auto count_lo = [&](uint32_t x) {
+          int cnt = 0;
+#pragma unroll
+          for (int i = 0; i < NSL; ++i) cnt += __popcll(__ballot(klo[i] >= x) & eq_hi[i]);
+          return cnt;
+        };
+        uint32_t tl = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = tl | (1u << bit);
+          const int cnt = count_lo(cand);
+          if (cnt >= need) tl = cand;
+          if (cnt == need) break;
+        }
+        int rem = need;
+        uint64_t eq[NSL];
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) {
+          const uint64_t gt = __ballot(klo[i] > tl) & eq_hi[i];
+          sel[i] |= gt;
+          rem -= __popcll(gt);
+          eq[i] = __ballot(klo[i] == tl) & eq_hi[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) {  // equal keys: lowest chunk index first
+          uint64_t e = eq[i];
+          while (rem > 0 && e) {
+            const uint64_t low = e & (~e + 1ull);
+            sel[i] |= low;
+            e ^= low;
+            --rem;
+          }
         }
       }
-      for (; i < i1; ++i) {
-        gt += (int)(khL[i] > kc);
-        ge += (int)(khL[i] >= kc);
-      }
-    }
-    if (tpc == 2) {
-      gt += __shfl_xor(gt, 1, 64);
-      ge += __shfl_xor(ge, 1, 64);
-    }
-    int rank = gt;
-    const bool tie = c < n_c && ge - gt > 1;  // another chunk shares the top half
-    if (__any(tie)) {
-      int extra = 0;
-      if (tie) {
-        const double v = scL[c];
-        const uint32_t kc = khL[c];
-        for (int i = i0; i < i1; ++i) {
-          const double u = scL[i];
-          extra += (int)((khL[i] == kc) & ((u > v) | ((u == v) & (i < c))));
+      int base = 0;
+#pragma unroll
+      for (int i = 0; i < NSL; ++i) {
+        if ((sel[i] >> lane) & 1ull) {
+          const int pos = base + __popcll(sel[i] & lanemask_lt()), c = WAVE * i + lane;
+          if (pos >= q0 && pos < q0 + MAXSLOT) selL[pos - q0] = c;
+          if (s == 0 && a.sel_out) a.sel_out[((long)b * a.Hkv + h) * a.k_eff + pos] = c;
         }
+        base += __popcll(sel[i]);
       }
-      if (tpc == 2) extra += __shfl_xor(extra, 1, 64);
-      rank += extra;
-    }
-    const bool chosen = c < n_c && half == 0 && rank < a.k_eff;
-    const uint64_t bal = __ballot(chosen);
-    if (lane == 0) wcnt[w] = __popcll(bal);
-    __syncthreads();
-    int pos = __popcll(bal & lanemask_lt());
-    for (int k = 0; k < w; ++k) pos += wcnt[k];
-    if (chosen) {
-      if (pos >= q0 && pos < q0 + MAXSLOT) selL[pos - q0] = c;
-      if (s == 0 && a.sel_out) a.sel_out[((long)b * a.Hkv + h) * a.k_eff + pos] = c;
     }
   } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
     selL[tid] = selv;
