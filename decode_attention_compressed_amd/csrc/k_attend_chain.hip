@@ -829,41 +829,49 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     const float *b1_rd = B1s + l16;
     f32x4 *ah_rw = reinterpret_cast<f32x4 *>(AHw) + l16;  // + 16 fi
     const f32x4 ahv = f32x4{ah[0], ah[1], ah[2], ah[3]};
-    auto hidden_mfma = [&](int fi, f32x4 *hc) {
-      const float bias = b1_rd[16 * fi];
-      f16x8 bw[NJ];
+    // W1 fragments and b1 of a hidden tile are read from LDS one tile before
+    // the products that use them; both buffers are indexed by the tile's
+    // parity, a constant in the unrolled loop, so nothing is copied
+    f16x8 bw[2][NJ];
+    float bias[2];
+    auto load_w1 = [&](int fi) {
+      bias[fi & 1] = b1_rd[16 * fi];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) bw[jj] = ldh8(w1_rd + 16 * fi * WLD + 32 * jj);
+      for (int jj = 0; jj < NJ; ++jj) bw[fi & 1][jj] = ldh8(w1_rd + 16 * fi * WLD + 32 * jj);
+    };
+    f32x4 hc[2][NTT];
+    auto hidden_mfma = [&](int fi) {
+      const float bv = bias[fi & 1];
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) hc[tt] = f32x4{bias, bias, bias, bias};
+      for (int tt = 0; tt < NTT; ++tt) hc[fi & 1][tt] = f32x4{bv, bv, bv, bv};
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj)  // head-dim step outer: four independent chains
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) hc[tt] = mfma(KA[jj][tt], bw[jj], hc[tt]);
+        for (int tt = 0; tt < NTT; ++tt) hc[fi & 1][tt] = mfma(KA[jj][tt], bw[fi & 1][jj], hc[fi & 1][tt]);
     };
-    f32x4 hcur[NTT], hnext[NTT];
-    hidden_mfma(0, hcur);
+    load_w1(0);
+    if (NF > 1) load_w1(1);
+    hidden_mfma(0);
 #pragma unroll
     for (int fi = 0; fi < NF; ++fi) {
       f32x4 prev = f32x4{0.f, 0.f, 0.f, 0.f};
       if (kg == 0) prev = ah_rw[16 * fi];
-      if (fi + 1 < NF) hidden_mfma(fi + 1, hnext);
+      if (fi + 1 < NF) hidden_mfma(fi + 1);
+      if (fi + 2 < NF) load_w1(fi + 2);
       f32x4 ahc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NTT / 2; ++i) {
         f16x8 hb;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          hb[v] = (_Float16)silu_scaled(hcur[2 * i][v]);
-          hb[4 + v] = (_Float16)silu_scaled(hcur[2 * i + 1][v]);
+          hb[v] = (_Float16)silu_scaled(hc[fi & 1][2 * i][v]);
+          hb[4 + v] = (_Float16)silu_scaled(hc[fi & 1][2 * i + 1][v]);
         }
         ahc = mfma(PA[i], hb, ahc);
       }
       if (kg == 0)
         ah_rw[16 * fi] = f32x4{fmaf(prev[0], ahv[0], ahc[0]), fmaf(prev[1], ahv[1], ahc[1]),
                                fmaf(prev[2], ahv[2], ahc[2]), fmaf(prev[3], ahv[3], ahc[3])};
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) hcur[tt] = hnext[tt];
     }
     restart(it + 1);
   }
