@@ -7,8 +7,7 @@
 //      in 32-wide steps.  The basis slab of a step is shared by the 8 waves
 //      through LDS (double-buffered, one barrier per step, loaded two steps
 //      ahead); every lane loads its coefficient fragments straight from global
-//      memory into the MFMA operand, two steps ahead, after an L2 prefetch of
-//      the same lines (one word per token row) two steps before that.
+//      memory into the MFMA operand, two steps ahead.
 //   2. logits[t][g] = K_hat[t] . q_g: the key accumulators rounded to fp16 are
 //      the A operand exactly as the step-1 output leaves them; online softmax
 //      per wave; p rounded to fp16.
@@ -24,9 +23,9 @@
 // follow the step-1 output layout (W1 and q are stored permuted), the tokens
 // in step 4 follow the step-3 output layout.
 //
-// The workgroup's last wave also attends the split's share of the uncompressed
-// tail (staged in LDS at the start; logits on the matrix cores, p . v on the
-// vector ALUs); the 8 waves then merge into one partial per query head:
+// While wave 0 selects the chunks, the other waves convert W1 into LDS and
+// attend the split's share of the uncompressed tail on the vector ALUs; after
+// the tiles the 8 waves merge into one partial per query head:
 // (m, l, mass of rebuilt tokens, accH[F], accV[d_h]).
 // The second predictor layer is linear and is applied once per query head in
 // the combine: sum_t p_t v_t = W2 accH + b2 mass + accV.
@@ -64,7 +63,6 @@ constexpr int LU = 2;             // basis slabs are loaded LU steps before use
 constexpr int NU = 2;             // basis register ring (divides the step count)
 constexpr int SP = DH * KS / 8 / NTH;  // 16-byte basis pieces per thread and slab
 constexpr int TP = 32;            // tail tokens staged in LDS per split
-constexpr int PD = 99;            // coefficient k-steps prefetched into L2 ahead (>= NR: none)
 constexpr int CPT = 2;            // tiles per chunk: 128-token chunks
 constexpr int MAXIT = 8;          // tiles per wave and split (at most)
 constexpr int MAXSLOT = MAXIT * NW / CPT;  // selected chunks per split (at most)
@@ -150,13 +148,14 @@ struct Smem {
   static constexpr int TV = TK + TP * DH * 2;            // [TP][DH] bf16 tail values
   static constexpr int AH = TV + TP * DH * 2;            // [NW][F][GQ] fp32 running accH per wave
   static constexpr int SEL = AH + NW * GQ * F * 4;       // [MAXSLOT] chunks of this split, [NW] counts
-  static constexpr int BYTES = SEL + (MAXSLOT + NW) * 4;
+  static constexpr int TLS = SEL + (MAXSLOT + NW) * 4;   // [2][NW][GQ] tail l and the m it is taken at
+  static constexpr int BYTES = TLS + 2 * NW * GQ * 4;
   // the chunk scores of the in-kernel selection use the p area (free until the first softmax)
   static_assert(CHAIN_SELECT_MAX_NC * 8 <= NW * GQ * TT * 4, "score staging does not fit");
   // merge area (after the last tile): per wave and query head m, l of rebuilt
-  // tokens, l of tail tokens, scale owed by accH; then accV
-  static constexpr int MM = 0, MLC = MM + NW * GQ * 4, MLT = MLC + NW * GQ * 4, MHS = MLT + NW * GQ * 4;
-  static constexpr int MV = MHS + NW * GQ * 4;
+  // tokens, l of tail tokens; then accV
+  static constexpr int MM = 0, MLC = MM + NW * GQ * 4, MLT = MLC + NW * GQ * 4;
+  static constexpr int MV = MLT + NW * GQ * 4;
   static constexpr int MWT = MV + NW * GQ * DH * 4, MWH = MWT + NW * GQ * 4;  // merge weights
   static_assert(MWH + NW * GQ * 4 <= QS, "merge area does not fit");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
@@ -317,7 +316,6 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   const TC *cf = reinterpret_cast<const TC *>(a.coeff) + (long)b * a.N * r;
   const rsrc_t Cr = make_rsrc(cf, (uint32_t)((long)a.N * r * CT::ES));
   const uint32_t c_voff = (uint32_t)((l16 * r + 8 * kg) * CT::ES);  // + (row0 + 16 tt) r + 32 ks
-  const uint32_t pf_voff = (uint32_t)(lane * r * CT::ES);           // token row lane of a tile
   const uint16_t *csc = a.coeff_scale ? a.coeff_scale + (long)b * r : nullptr;
   const int32_t *rptr = a.res_ptr + bh * (a.N / C + 1);
   const int32_t *ridx = a.res_idx + bh * a.n_res;
@@ -344,15 +342,6 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   auto c_soff = [&](int tt, int q) -> uint32_t {  // scalar offset of k-step q of token tile tt
     return (uint32_t)(((row0 + 16 * tt) * r + q * KS) * CT::ES);
   };
-  // L2 prefetch of k-step q of the wave's tile: one 4-byte read per token row
-  // brings the row's k-step sector into L2 ahead of the register loads.  The
-  // word read is consumed PD steps later by an empty asm statement (by then the
-  // register load of the same k-step has been waited for anyway); that keeps
-  // the read live without extending its register's lifetime.
-  constexpr int PFN = TT / WAVE;  // prefetch reads per k-step
-  auto prefetch = [&](int q, int i) -> uint32_t {
-    return __builtin_amdgcn_raw_buffer_load_b32(Cr, pf_voff, (uint32_t)(((row0 + WAVE * i) * r + q * KS) * CT::ES), 0);
-  };
   // the selection inputs are read first: everything below waits on them
   static_assert(CHAIN_SELECT_MAX_NC <= NTH, "one chunk score per thread");
   const int n_c = a.N / C;
@@ -373,11 +362,6 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
     selv = selp[q0 + tid];
   }
-  uint32_t pfr[PD][PFN];
-#pragma unroll
-  for (int k = 0; k < PD; ++k)
-#pragma unroll
-    for (int i = 0; i < PFN; ++i) pfr[k][i] = 0u;
   u32x4 ur[NU][SP], us_[NU];
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
@@ -387,12 +371,16 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   }
 #pragma unroll
   for (int q = 0; q < LU; ++q) ST::ld(Ur, csc, u_voff, r, q * KS, ur[q % NU], us_[q % NU]);
-  constexpr int W1P = F * DH / 8 / NTH;        // 16-byte W1 pieces per thread
+  // W1 is read and converted by waves 1..NW-1 while wave 0 selects
+  constexpr int W1N = F * DH / 8;                             // 16-byte W1 pieces
+  constexpr int W1T = NTH - WAVE;                             // threads of waves 1..NW-1
+  constexpr int W1P = (W1N + W1T - 1) / W1T;                  // pieces per such thread
+  const int tw = tid - WAVE;
   u32x4 w1r[W1P];
 #pragma unroll
   for (int k = 0; k < W1P; ++k) {
-    const int p = tid + NTH * k;
-    w1r[k] = gld16(W1 + (long)(p / (DH / 8)) * DH + 8 * (p % (DH / 8)));
+    const int p = tw + W1T * k;
+    w1r[k] = (w != 0 && p < W1N) ? gld16(W1 + (long)(p / (DH / 8)) * DH + 8 * (p % (DH / 8))) : v4(0, 0, 0, 0);
   }
   const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + ((long)b * a.Hq + (long)h * g) * DH;
   const u32x4 qraw = tid < g * (DH / 8) ? gld16(qb + 8 * tid) : v4(0, 0, 0, 0);
@@ -415,6 +403,33 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     }
   }
 
+  // q rows of this kv head as fp16 with permuted dims (rows g..15 zero), and the
+  // tail rows: both are read while wave 0 selects
+  for (int i = tid; i < (16 - g) * (DH / 2); i += NTH)
+    reinterpret_cast<uint32_t *>(Qs)[(g + i / (DH / 2)) * (WLD / 2) + i % (DH / 2)] = 0u;
+  if (tid < g * (DH / 8)) {
+    const int gi = tid / (DH / 8), d0 = 8 * (tid % (DH / 8));
+    const uint2 lo = make_uint2(pack2(bf16_bits_to_f32(qraw.x & 0xFFFFu), bf16_bits_to_f32(qraw.x >> 16)),
+                                pack2(bf16_bits_to_f32(qraw.y & 0xFFFFu), bf16_bits_to_f32(qraw.y >> 16)));
+    const uint2 hi = make_uint2(pack2(bf16_bits_to_f32(qraw.z & 0xFFFFu), bf16_bits_to_f32(qraw.z >> 16)),
+                                pack2(bf16_bits_to_f32(qraw.w & 0xFFFFu), bf16_bits_to_f32(qraw.w >> 16)));
+    *reinterpret_cast<uint2 *>(Qs + gi * WLD + dpos(d0)) = lo;
+    *reinterpret_cast<uint2 *>(Qs + gi * WLD + dpos(d0 + 4)) = hi;
+  }
+#pragma unroll
+  for (int i = 0; i < TPP; ++i) {
+    const int p = tid + NTH * i, row = p >> 4, c8 = (p & 15) * 8;
+    lst16(Tk + row * DH + c8, tkr[i]);
+    lst16(Tv + row * DH + c8, tvr[i]);
+  }
+  // per-wave softmax state: lane holds query head l16 (rows >= g are padding)
+  float m_run = -INFINITY, l_run = 0.f;
+  float accV[GQ][2];
+#pragma unroll
+  for (int i = 0; i < GQ; ++i) accV[i][0] = accV[i][1] = 0.f;
+  // tail part of l per wave and query head, with the running maximum it is
+  // relative to; the merge brings it to the wave's final maximum
+  float *tl_l = reinterpret_cast<float *>(sm + S::TLS), *tl_m = tl_l + NW * GQ;
   // ---- chunk selection of (b, h): the top k_eff chunks by (score desc, index
   // asc), in ascending index order.  With the scores at hand every workgroup
   // selects them itself: wave 0 holds the order keys of all chunks (chunk
@@ -423,12 +438,12 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   // there (a uniform branch, rare outside crafted ties).  Every count is a
   // 64-lane compare mask and a popcount.  Chunks whose whole key equals the
   // threshold (equal doubles) are taken lowest index first.  Split 0 also
-  // writes the whole selection to sel_out.
-  if (a.score_part) {
-    double *scL = reinterpret_cast<double *>(sm + S::PS);
-    if (tid < n_c) scL[tid] = scv;
-    __syncthreads();
-    if (w == 0) {
+  // writes the whole selection to sel_out.  The other waves attend the tail meanwhile.
+  double *scL = reinterpret_cast<double *>(sm + S::PS);
+  if (a.score_part && tid < n_c) scL[tid] = scv;
+  __syncthreads();
+  if (w == 0) {
+    if (a.score_part) {
       constexpr int NSL = CHAIN_SELECT_MAX_NC / WAVE;  // key slots per lane
       uint32_t khi[NSL], klo[NSL];
       uint64_t valid[NSL];
@@ -523,9 +538,93 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
         }
         base += __popcll(sel[i]);
       }
+    } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
+      selL[tid] = selv;
     }
-  } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
-    selL[tid] = selv;
+    if (lane < GQ) {  // wave 0 attends no tail tokens
+      tl_l[lane] = 0.f;
+      tl_m[lane] = -INFINITY;
+    }
+  } else {
+    // W1 -> fp16, head dims permuted (two 4-dim runs per piece)
+#pragma unroll
+    for (int k = 0; k < W1P; ++k) {
+      const int p = tw + W1T * k, f = p / (DH / 8), d0 = 8 * (p % (DH / 8));
+      if (p >= W1N) break;
+      const u32x4 v = w1r[k];
+      auto sc = [](uint32_t u) { return bf16_bits_to_f32(u) * NEG_LOG2E; };
+      const uint2 lo = make_uint2(pack2(sc(v.x & 0xFFFFu), sc(v.x >> 16)), pack2(sc(v.y & 0xFFFFu), sc(v.y >> 16)));
+      const uint2 hi = make_uint2(pack2(sc(v.z & 0xFFFFu), sc(v.z >> 16)), pack2(sc(v.w & 0xFFFFu), sc(v.w >> 16)));
+      *reinterpret_cast<uint2 *>(W1s + f * WLD + dpos(d0)) = lo;
+      *reinterpret_cast<uint2 *>(W1s + f * WLD + dpos(d0 + 4)) = hi;
+    }
+    // ---- the split's share of the uncompressed tail, attended while wave 0
+    // selects: wave w takes tokens tb + w - 1, tb + w - 1 + (NW - 1), ..., two
+    // at a time, logits and p . v on the vector ALUs (lane: head dims 2 lane,
+    // 2 lane + 1).  The eight partial logits of a pair (token u, head gi) are
+    // summed over the wave by a transposing butterfly.  Nothing has been added
+    // to the hidden sums yet, so the tiles' rescaling covers everything.
+    constexpr int NTW = NW - 1;  // tail waves
+    float l_t = 0.f;             // partials over the lane groups kg, like l_run
+    float qd[GQ][2];  // q of the kv head's query heads at the lane's dims (fp16 values)
+#pragma unroll
+    for (int gi = 0; gi < GQ; ++gi) {
+      const uint32_t qq = *reinterpret_cast<const uint32_t *>(Qs + gi * WLD + dpos(2 * lane));
+      qd[gi][0] = f16_bits_to_f32(qq & 0xFFFFu);
+      qd[gi][1] = f16_bits_to_f32(qq >> 16);
+    }
+    auto row = [&](const uint16_t *lds, const uint16_t *glb, int t, float &x0, float &x1) {
+      const int tl = t - tb;
+      const uint32_t v2 = tl < TP ? *reinterpret_cast<const uint32_t *>(lds + tl * DH + 2 * lane)
+                                  : *reinterpret_cast<const uint32_t *>(glb + (long)t * DH + 2 * lane);
+      x0 = bf16_bits_to_f32(v2 & 0xFFFFu);
+      x1 = bf16_bits_to_f32(v2 >> 16);
+    };
+    for (int t0 = tb + w - 1; t0 < te; t0 += 2 * NTW) {
+      const bool two = t0 + NTW < te;
+      float k0[2][2], v0[2][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = u == 0 || two ? t0 + NTW * u : t0;
+        row(Tk, kt, t, k0[u][0], k0[u][1]);
+        row(Tv, vt, t, v0[u][0], v0[u][1]);
+      }
+      float pl[2 * GQ];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int gi = 0; gi < GQ; ++gi) pl[GQ * u + gi] = fmaf(qd[gi][0], k0[u][0], qd[gi][1] * k0[u][1]);
+      // lane l ends with the logit of pair (l >> 3): token (l >> 5), head (l >> 3) & 3
+      const float lsum = xpose_sum_f<2 * GQ, 32>(pl, lane);
+      const int hq = l16 & (GQ - 1);  // this lane's head (lanes past g are padding)
+      float lt2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) lt2[u] = __shfl(lsum, 32 * u + 8 * hq, 64) * a.scale_log2;
+      if (!two) lt2[1] = -INFINITY;
+      const float m_new = fmaxf(m_run, fmaxf(lt2[0], lt2[1]));
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      float p2[2], ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        p2[u] = lt2[u] == -INFINITY ? 0.f : (float)(_Float16)__builtin_amdgcn_exp2f(lt2[u] - m_new);
+        ps += p2[u];
+      }
+      l_t = l_t * alpha + (kg == 0 ? ps : 0.f);
+      m_run = m_new;
+#pragma unroll
+      for (int gi = 0; gi < GQ; ++gi) {
+        const float av = __shfl(alpha, gi, 64);
+        const float pa = __shfl(p2[0], gi, 64), pb = __shfl(p2[1], gi, 64);
+        accV[gi][0] = fmaf(pb, v0[1][0], fmaf(pa, v0[0][0], accV[gi][0] * av));
+        accV[gi][1] = fmaf(pb, v0[1][1], fmaf(pa, v0[0][1], accV[gi][1] * av));
+      }
+    }
+    l_t += __shfl_xor(l_t, 16, 64);
+    l_t += __shfl_xor(l_t, 32, 64);
+    if (lane < GQ) {
+      tl_l[w * GQ + lane] = l_t;
+      tl_m[w * GQ + lane] = m_run;
+    }
   }
   __syncthreads();
   if (tau0 < t_end) row0 = tile_row(tau0);
@@ -535,40 +634,11 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) cr[q][tt] = CT::ld(Cr, c_voff, c_soff(tt, q));
 
-  // W1 -> fp16, head dims permuted (two 4-dim runs per piece)
-#pragma unroll
-  for (int k = 0; k < W1P; ++k) {
-    const int p = tid + NTH * k, f = p / (DH / 8), d0 = 8 * (p % (DH / 8));
-    const u32x4 v = w1r[k];
-    auto sc = [](uint32_t u) { return bf16_bits_to_f32(u) * NEG_LOG2E; };
-    const uint2 lo = make_uint2(pack2(sc(v.x & 0xFFFFu), sc(v.x >> 16)), pack2(sc(v.y & 0xFFFFu), sc(v.y >> 16)));
-    const uint2 hi = make_uint2(pack2(sc(v.z & 0xFFFFu), sc(v.z >> 16)), pack2(sc(v.w & 0xFFFFu), sc(v.w >> 16)));
-    *reinterpret_cast<uint2 *>(W1s + f * WLD + dpos(d0)) = lo;
-    *reinterpret_cast<uint2 *>(W1s + f * WLD + dpos(d0 + 4)) = hi;
-  }
-  // q rows of this kv head as fp16 with permuted dims; rows g..15 are zero
-  for (int i = tid; i < (16 - g) * (DH / 2); i += NTH)
-    reinterpret_cast<uint32_t *>(Qs)[(g + i / (DH / 2)) * (WLD / 2) + i % (DH / 2)] = 0u;
-  if (tid < g * (DH / 8)) {
-    const int gi = tid / (DH / 8), d0 = 8 * (tid % (DH / 8));
-    const uint2 lo = make_uint2(pack2(bf16_bits_to_f32(qraw.x & 0xFFFFu), bf16_bits_to_f32(qraw.x >> 16)),
-                                pack2(bf16_bits_to_f32(qraw.y & 0xFFFFu), bf16_bits_to_f32(qraw.y >> 16)));
-    const uint2 hi = make_uint2(pack2(bf16_bits_to_f32(qraw.z & 0xFFFFu), bf16_bits_to_f32(qraw.z >> 16)),
-                                pack2(bf16_bits_to_f32(qraw.w & 0xFFFFu), bf16_bits_to_f32(qraw.w >> 16)));
-    *reinterpret_cast<uint2 *>(Qs + gi * WLD + dpos(d0)) = lo;
-    *reinterpret_cast<uint2 *>(Qs + gi * WLD + dpos(d0 + 4)) = hi;
-  }
   if (tid < F / 8) {
     float *bo = B1s + 8 * tid;
     auto sc = [](uint32_t u) { return bf16_bits_to_f32(u) * NEG_LOG2E; };
     *reinterpret_cast<f32x4 *>(bo) = f32x4{sc(braw.x & 0xFFFFu), sc(braw.x >> 16), sc(braw.y & 0xFFFFu), sc(braw.y >> 16)};
     *reinterpret_cast<f32x4 *>(bo + 4) = f32x4{sc(braw.z & 0xFFFFu), sc(braw.z >> 16), sc(braw.w & 0xFFFFu), sc(braw.w >> 16)};
-  }
-#pragma unroll
-  for (int i = 0; i < TPP; ++i) {
-    const int p = tid + NTH * i, row = p >> 4, c8 = (p & 15) * 8;
-    lst16(Tk + row * DH + c8, tkr[i]);
-    lst16(Tv + row * DH + c8, tvr[i]);
   }
   // the wave's running accH starts at zero (a wave without a tile leaves it so)
 #pragma unroll
@@ -577,11 +647,6 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   ST::st(Us, ur[0], us_[0]);   // slab 0 -> buffer 0
   __syncthreads();
 
-  // per-wave softmax state: lane holds query head l16 (rows >= g are padding)
-  float m_run = -INFINITY, l_run = 0.f;
-  float accV[GQ][2];
-#pragma unroll
-  for (int i = 0; i < GQ; ++i) accV[i][0] = accV[i][1] = 0.f;
   float rs0 = 1.f, rs1 = 1.f;  // int8 residual scales of the lane's two dims
   if (sizeof(TC) == 1 && a.res_scale) {
     const uint16_t *rsc = a.res_scale + bh * DH;
@@ -657,20 +722,12 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       // than the coefficients then due
       if constexpr (ks + LU < NR)
         ST::ld(Ur, csc, u_voff, r, (ks + LU) * KS, ur[(ks + LU) % NU], us_[(ks + LU) % NU]);
-      // coefficients DC - 1 steps ahead, then the L2 prefetch PD steps ahead.
+      // coefficients DC - 1 steps ahead.
       // Every load here is unconditional (a wave without a tile reads out of
       // range), so the wait counts stay exact across steps.
       if constexpr (ks + DC - 1 < NR) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) cr[(ks + DC - 1) % DC][tt] = CT::ld(Cr, c_voff, c_soff(tt, ks + DC - 1));
-      }
-      if constexpr (ks >= PD) {  // the prefetch of this k-step
-#pragma unroll
-        for (int i = 0; i < PFN; ++i) asm volatile("" ::"v"(pfr[ks % PD][i]));
-      }
-      if constexpr (ks + PD < NR) {
-#pragma unroll
-        for (int i = 0; i < PFN; ++i) pfr[ks % PD][i] = prefetch(ks + PD, i);
       }
       // residual entries of the chunk: their tokens two steps before the end,
       // the tile's rows in the last step (read after the softmax)
@@ -876,87 +933,21 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     restart(it + 1);
   }
 
-  // ---- the split's share of the uncompressed tail: every wave takes tokens
-  // tb + w, tb + w + NW, ..., two at a time, logits and p . v on the vector ALUs
-  // (lane: head dims 2 lane, 2 lane + 1).  The eight partial logits of a pair
-  // (token u, head gi) are summed over the wave by a transposing butterfly.
-  float l_t = 0.f;   // tail part of l
-  float hsc = 1.f;   // rescale still owed by the running accH (applied in the merge)
-  {
-    float qd[GQ][2];  // q of the kv head's query heads at the lane's dims (fp16 values)
-#pragma unroll
-    for (int gi = 0; gi < GQ; ++gi) {
-      const uint32_t qq = *reinterpret_cast<const uint32_t *>(Qs + gi * WLD + dpos(2 * lane));
-      qd[gi][0] = f16_bits_to_f32(qq & 0xFFFFu);
-      qd[gi][1] = f16_bits_to_f32(qq >> 16);
-    }
-    auto row = [&](const uint16_t *lds, const uint16_t *glb, int t, float &x0, float &x1) {
-      const int tl = t - tb;
-      const uint32_t v2 = tl < TP ? *reinterpret_cast<const uint32_t *>(lds + tl * DH + 2 * lane)
-                                  : *reinterpret_cast<const uint32_t *>(glb + (long)t * DH + 2 * lane);
-      x0 = bf16_bits_to_f32(v2 & 0xFFFFu);
-      x1 = bf16_bits_to_f32(v2 >> 16);
-    };
-    for (int t0 = tb + w; t0 < te; t0 += 2 * NW) {
-      const bool two = t0 + NW < te;
-      float k0[2][2], v0[2][2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = u == 0 || two ? t0 + NW * u : t0;
-        row(Tk, kt, t, k0[u][0], k0[u][1]);
-        row(Tv, vt, t, v0[u][0], v0[u][1]);
-      }
-      float pl[2 * GQ];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int gi = 0; gi < GQ; ++gi) pl[GQ * u + gi] = fmaf(qd[gi][0], k0[u][0], qd[gi][1] * k0[u][1]);
-      // lane l ends with the logit of pair (l >> 3): token (l >> 5), head (l >> 3) & 3
-      const float lsum = xpose_sum_f<2 * GQ, 32>(pl, lane);
-      const int hq = l16 & (GQ - 1);  // this lane's head (lanes past g are padding)
-      float lt2[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) lt2[u] = __shfl(lsum, 32 * u + 8 * hq, 64) * a.scale_log2;
-      if (!two) lt2[1] = -INFINITY;
-      const float m_new = fmaxf(m_run, fmaxf(lt2[0], lt2[1]));
-      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      float p2[2], ps = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        p2[u] = lt2[u] == -INFINITY ? 0.f : (float)(_Float16)__builtin_amdgcn_exp2f(lt2[u] - m_new);
-        ps += p2[u];
-      }
-      l_run *= alpha;
-      l_t = l_t * alpha + (kg == 0 ? ps : 0.f);  // l is kept as partials over the lane groups kg
-      hsc *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int gi = 0; gi < GQ; ++gi) {
-        const float av = __shfl(alpha, gi, 64);
-        const float pa = __shfl(p2[0], gi, 64), pb = __shfl(p2[1], gi, 64);
-        accV[gi][0] = fmaf(pb, v0[1][0], fmaf(pa, v0[0][0], accV[gi][0] * av));
-        accV[gi][1] = fmaf(pb, v0[1][1], fmaf(pa, v0[0][1], accV[gi][1] * av));
-      }
-    }
-  }
-
   // ---- merge the waves into one partial --------------------------------------------
   __syncthreads();  // W1 and the basis slabs are free from here
   float *mm = reinterpret_cast<float *>(sm + S::MM), *mlc = reinterpret_cast<float *>(sm + S::MLC);
-  float *mlt = reinterpret_cast<float *>(sm + S::MLT), *mhs = reinterpret_cast<float *>(sm + S::MHS);
+  float *mlt = reinterpret_cast<float *>(sm + S::MLT);
   float *mv = reinterpret_cast<float *>(sm + S::MV);
   const float *AH = reinterpret_cast<const float *>(sm + S::AH);
   {
-    float lc = l_run, lt = l_t;
+    float lc = l_run;
     lc += __shfl_xor(lc, 16, 64);
     lc += __shfl_xor(lc, 32, 64);
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
     if (lane < GQ) {
+      const float lt = tl_l[w * GQ + lane];  // the tail's l, brought to this wave's final maximum
       mm[w * GQ + lane] = m_run;
       mlc[w * GQ + lane] = lc;
-      mlt[w * GQ + lane] = lt;
-      mhs[w * GQ + lane] = hsc * NEG_LN2;  // hidden sums were accumulated in -log2(e) units
+      mlt[w * GQ + lane] = lt == 0.f ? 0.f : lt * __builtin_amdgcn_exp2f(tl_m[w * GQ + lane] - m_run);
     }
     float *aw = mv + w * GQ * DH;
 #pragma unroll
@@ -976,7 +967,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     const float mk = mm[k * GQ + gi];
     const float wt = (gi >= g || mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
     mwt[k * GQ + gi] = wt;
-    mwh[k * GQ + gi] = wt * mhs[k * GQ + gi];
+    mwh[k * GQ + gi] = wt * NEG_LN2;  // hidden sums were accumulated in -log2(e) units
     if (k == 0 && gi < g) part[(long)gi * a.PW + 0] = M;
   }
   __syncthreads();
