@@ -170,7 +170,8 @@ def main():
     # per (query set, layer) pre-marshalled calls
     kk = P.k_eff(d)
     ws = P.workspace(d, P._lib.OP_DECODE)
-    out = torch.empty((s.B, s.Hq, s.dh), dtype=torch.bfloat16, device="cuda")
+    from decode_attention_compressed_amd.api import TORCH_DT
+    out = torch.empty((s.B, s.Hq, s.dh), dtype=TORCH_DT[d.act], device="cuda")
     sels = [[torch.empty((s.B, s.Hkv, kk), dtype=torch.int32, device="cuda") for _ in range(s.G)] for _ in range(n_q)]
     calls = [[P.DecodeCall(d, l, model, cache, dev["q"][i, l], dev["k_tail"], dev["v_tail"], out, ws, sels[i][l])
               for l in range(s.G)] for i in range(n_q)]
@@ -302,7 +303,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": {"f32": "f32", "bf16": "bf16"}[s.act],
         "data": "synthetic (seeded spectrum-decayed keys, MLP+Student-t values, N(0,1) queries)",
         "config": {"workload": s.name, "B": s.B, "G": s.G, "Hq": s.Hq, "Hkv": s.Hkv, "dh": s.dh,
                    "r": s.r, "F": s.F, "N": s.N_after, "C": s.C, "top_k": s.k, "T": s.T,

@@ -270,8 +270,8 @@ __global__ __launch_bounds__(TK_NT) void k_topk_small(const double *__restrict__
 // D4-D6 on the vector ALUs.  grid (n_split + 1, Hkv, B), 256 threads; the last
 // split of each (b, h) is the tail.  TT tokens per tile.
 // ---------------------------------------------------------------------------
-template <typename TA, typename TC, typename TR>
-__global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT) {
+template <typename TA, typename TC, typename TR, bool STAGE>
+__global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT) {  // STAGE: U and W1 in LDS
   extern __shared__ __align__(16) float fsm[];
   const int h = blockIdx.y, b = blockIdx.z, split = blockIdx.x, tid = threadIdx.x;
   const int g = a.g, dh = a.dh, r = a.r, F = a.F, C = a.C;
@@ -309,6 +309,15 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
   const TR *rval = reinterpret_cast<const TR *>(a.res_val) + bh * a.n_res * dh;
   const uint16_t *rsc = a.res_scale ? a.res_scale + bh * dh : nullptr;
   const int32_t *selp = a.sel + ((long)b * a.Hkv + h) * a.k_eff;
+  // with STAGE the basis slice [dh][r] and W1 [F][dh] are read once into LDS
+  // (as fp32, after the tile region) instead of element by element per token.
+  // Rows are padded by one word: neighbouring threads read neighbouring rows.
+  float *Ul = hb + TT * F, *W1l = Ul + dh * (r + 1);
+  if (STAGE) {
+    for (int i = tid; i < dh * r; i += 256) Ul[(i / r) * (r + 1) + i % r] = ldf(U, i);
+    for (int i = tid; i < F * dh; i += 256) W1l[(i / dh) * (dh + 1) + i % dh] = ldf(W1, i);
+    __syncthreads();
+  }
 
   const int s_end = min(a.k_eff, (split + 1) * a.cps);
   for (int slot = split * a.cps; slot < s_end; ++slot) {
@@ -325,8 +334,9 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
       for (int idx = tid; idx < nt * dh; idx += 256) {
         const int t = idx / dh, d = idx % dh;
         const TA *ur = U + (long)d * r;
+        const float *ul = Ul + d * (r + 1);
         float s = 0.f;
-        for (int i = 0; i < r; ++i) s = fmaf(ldf(ur, i), cb[t * r + i], s);
+        for (int i = 0; i < r; ++i) s = fmaf(STAGE ? ul[i] : ldf(ur, i), cb[t * r + i], s);
         kh[idx] = s;
       }
       __syncthreads();
@@ -339,8 +349,9 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
       for (int idx = tid; idx < nt * F; idx += 256) {
         const int t = idx / F, f = idx % F;
         const TA *wr = W1 + (long)f * dh;
+        const float *wl = W1l + f * (dh + 1);
         float s = ldf(B1, f);
-        for (int d = 0; d < dh; ++d) s = fmaf(ldf(wr, d), kh[t * dh + d], s);
+        for (int d = 0; d < dh; ++d) s = fmaf(STAGE ? wl[d] : ldf(wr, d), kh[t * dh + d], s);
         hb[idx] = silu_f(s);
       }
       __syncthreads();
@@ -718,21 +729,28 @@ int valu_tile(int g, int dh, int r, int F) {
   return TT;
 }
 
+template <typename TA, typename TC, typename TR>
+static void go_valu(const AttendArgs &a, int TT, size_t smem, bool stage, hipStream_t st) {
+  dim3 grid(a.n_split + 1, a.Hkv, a.B);
+  if (stage) {
+    allow_dynamic_lds(k_attend_valu<TA, TC, TR, true>, smem);
+    hipLaunchKernelGGL((k_attend_valu<TA, TC, TR, true>), grid, dim3(256), smem, st, a, TT);
+  } else {
+    hipLaunchKernelGGL((k_attend_valu<TA, TC, TR, false>), grid, dim3(256), smem, st, a, TT);
+  }
+}
+
 hipError_t launch_attend_valu(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st) {
   const int TT = valu_tile(a.g, a.dh, a.r, a.F);
-  const size_t smem = valu_smem_bytes(a.g, a.dh, a.r, a.F, TT);
-  dim3 grid(a.n_split + 1, a.Hkv, a.B);
-  if (act == LOWRAM_F32) {
-    hipLaunchKernelGGL((k_attend_valu<float, float, float>), grid, dim3(256), smem, st, a, TT);
-  } else if (coeff == LOWRAM_BF16 && resid == LOWRAM_BF16) {
-    hipLaunchKernelGGL((k_attend_valu<bf16, bf16, bf16>), grid, dim3(256), smem, st, a, TT);
-  } else if (coeff == LOWRAM_I8 && resid == LOWRAM_I8) {
-    hipLaunchKernelGGL((k_attend_valu<bf16, int8_t, int8_t>), grid, dim3(256), smem, st, a, TT);
-  } else if (coeff == LOWRAM_I8) {
-    hipLaunchKernelGGL((k_attend_valu<bf16, int8_t, bf16>), grid, dim3(256), smem, st, a, TT);
-  } else {
-    hipLaunchKernelGGL((k_attend_valu<bf16, bf16, int8_t>), grid, dim3(256), smem, st, a, TT);
-  }
+  size_t smem = valu_smem_bytes(a.g, a.dh, a.r, a.F, TT);
+  const size_t staged = smem + sizeof(float) * ((size_t)a.dh * (a.r + 1) + (size_t)a.F * (a.dh + 1));
+  const bool stage = staged <= 160 * 1024;
+  if (stage) smem = staged;
+  if (act == LOWRAM_F32) go_valu<float, float, float>(a, TT, smem, stage, st);
+  else if (coeff == LOWRAM_BF16 && resid == LOWRAM_BF16) go_valu<bf16, bf16, bf16>(a, TT, smem, stage, st);
+  else if (coeff == LOWRAM_I8 && resid == LOWRAM_I8) go_valu<bf16, int8_t, int8_t>(a, TT, smem, stage, st);
+  else if (coeff == LOWRAM_I8) go_valu<bf16, int8_t, bf16>(a, TT, smem, stage, st);
+  else go_valu<bf16, bf16, int8_t>(a, TT, smem, stage, st);
   return hipGetLastError();
 }
 
