@@ -122,7 +122,14 @@ def cpu_baseline(s, host, inp, budget_s):
         if time.perf_counter() - t0 >= budget_s or steps >= 8:
             break
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": s.B * steps / dt, "unit": "seq-steps/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"{steps} full decode step(s) ({s.G} layers x B={s.B}) of the {s.name} workload, "
                       f"float64 numpy oracle, {dt:.1f} s"}
 
@@ -211,6 +218,27 @@ def main():
     ms_step = ms_total / args.steps
     log(f"{args.steps} steps in {ms_total:.3f} ms -> {ms_step * 1e3:.1f} us/step (graph={graph is not None})")
 
+    # ---- per-step distribution: a one-step graph replayed with events around each replay
+    step_dist = None
+    if graph is not None:
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1):
+            step(0)
+        g1.replay()
+        torch.cuda.synchronize()
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a_, b_ in pev:
+            a_.record()
+            g1.replay()
+            b_.record()
+        torch.cuda.synchronize()
+        per = np.array([a_.elapsed_time(b_) for a_, b_ in pev]) * 1e3
+        step_dist = {"us_p50": round(float(np.median(per)), 1), "us_p90": round(float(np.percentile(per, 90)), 1),
+                     "us_min": round(float(per.min()), 1), "n": int(per.size),
+                     "how": "one-step graph replayed with HIP events around each replay (adds the replay launch)"}
+        log(f"per-step: p50 {step_dist['us_p50']} us, p90 {step_dist['us_p90']} us")
+        del g1
+
     # ---- attend-kernel timing with events on its stream ------------------------
     stream = torch.cuda.current_stream()
     n_time = min(args.steps, n_q)
@@ -244,7 +272,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
     roof["traffic"] = traffic_for_current_kernel()
-    roof.update({"kernel": "k_attend_chain (top-k + rebuild-and-attend)", "avg_launch_us": round(t_attend * 1e6, 2),
+    kname = {"chain": "k_attend_chain (top-k + rebuild-and-attend)", "mfma": "k_attend_mfma (rebuild-and-attend)",
+             "valu": "k_attend_valu (rebuild-and-attend)", "none": "tail only"}[P.decode_kernel(d)]
+    roof.update({"kernel": kname, "avg_launch_us": round(t_attend * 1e6, 2),
                  "algorithmic_bytes_per_launch": int(a_bytes), "algorithmic_flops_per_launch": int(a_flops),
                  "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                  "hbm_gbps": round(gbps, 1), "roof_time_us": round(max(t_hbm, t_mfma) * 1e6, 2),
@@ -317,6 +347,7 @@ def main():
         "compression_ratio": round(dense_bytes / comp_bytes, 3),
         "selected_chunk_union_per_seq": round(float(union), 1),
         "compress_ms": round(compress_ms, 2),
+        "step_time_distribution": step_dist,
         "graph": graph is not None,
         "device": dev_name,
     }

@@ -47,6 +47,7 @@ vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_in
 SIGNATURES = {
     "lowram_workspace_bytes": [P(Dims), i32, P(sz)],
     "lowram_cache_bytes": [P(Dims), P(ctypes.c_uint64), P(ctypes.c_uint64)],
+    "lowram_decode_kernel": [P(Dims), P(i32)],
     "lowram_compress": [P(Dims), P(Model), vp, vp, P(Cache), vp, sz, vp],
     "lowram_decode_attn": [P(Dims), i32, P(Model), P(Cache), vp, vp, vp, vp, vp, vp, sz, vp],
     "lowram_decode_select": [P(Dims), i32, P(Model), P(Cache), vp, vp, vp, sz, vp],

@@ -75,6 +75,17 @@ def workspace(d: L.Dims, op: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(1, workspace_bytes(d, op)), dtype=torch.uint8, device=device)
 
 
+DECODE_KERNELS = {0: "none", 1: "chain", 2: "mfma", 3: "valu"}
+
+
+def decode_kernel(d: L.Dims) -> str:
+    """Which rebuild-and-attend kernel decode calls with dims d run:
+    "chain", "mfma", "valu" or "none" (no chunk selected)."""
+    p = ctypes.c_int32(-1)
+    L.check(L.lib().lowram_decode_kernel(ctypes.byref(d), ctypes.byref(p)))
+    return DECODE_KERNELS[p.value]
+
+
 def cache_bytes(d: L.Dims):
     c, dn = ctypes.c_uint64(0), ctypes.c_uint64(0)
     L.check(L.lib().lowram_cache_bytes(ctypes.byref(d), ctypes.byref(c), ctypes.byref(dn)))

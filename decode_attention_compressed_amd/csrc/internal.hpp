@@ -49,6 +49,8 @@ hipError_t launch_select(int act, const void *q, long q_bstride, const void *bas
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
                          double *part, double *scores, hipStream_t st);
 hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st);
+// True when the per-chunk MFMA kernel covers these shapes (else the VALU kernel)
+bool mfma_supported(const AttendArgs &a, int act, int coeff, int resid);
 // Register-chained rebuild-and-attend: the shapes it covers, its split plan
 // (splits per (b, h), 64-token tiles per split, tail tokens per split) and the
 // launcher.  Its partials fold the tail in: n_split of them per (b, h).

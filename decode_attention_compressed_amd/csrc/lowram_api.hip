@@ -262,6 +262,20 @@ lowram_status lowram_workspace_bytes(const lowram_dims *d, int32_t op, size_t *b
   return fail(LOWRAM_E_INVALID, "unknown op %d", op);
 }
 
+lowram_status lowram_decode_kernel(const lowram_dims *d, int32_t *path) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  if (!path) return fail(LOWRAM_E_INVALID, "path is NULL");
+  const DecodePlan p = decode_plan(d);
+  if (p.k_eff == 0) *path = LOWRAM_PATH_NONE;
+  else if (p.tps > 0) *path = LOWRAM_PATH_CHAIN;
+  else {
+    const AttendArgs a = make_attend(d, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p, nullptr);
+    *path = mfma_supported(a, d->act, d->coeff, d->resid) ? LOWRAM_PATH_MFMA : LOWRAM_PATH_VALU;
+  }
+  return LOWRAM_OK;
+}
+
 lowram_status lowram_cache_bytes(const lowram_dims *d, uint64_t *compressed, uint64_t *dense) {
   lowram_status st = check_dims(d);
   if (st != LOWRAM_OK) return st;

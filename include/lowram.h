@@ -109,6 +109,20 @@ typedef struct {
 /* Workspace bytes `op` needs for these dims (host only, enqueues nothing). */
 lowram_status lowram_workspace_bytes(const lowram_dims *dims, int32_t op, size_t *bytes);
 
+/* Which rebuild-and-attend kernel decode calls with these dims run (host only,
+ * enqueues nothing).  *path is one of:
+ *   LOWRAM_PATH_CHAIN  register-chained kernel (d_h = 128, C = 128, g <= 4,
+ *                      compiled (r, F, dtype) shapes); with n_c <= 512 it also
+ *                      ranks the chunk scores in its prologue;
+ *   LOWRAM_PATH_MFMA   one workgroup per selected chunk on the matrix cores
+ *                      (bf16 shapes compiled for it);
+ *   LOWRAM_PATH_VALU   vector-ALU kernel (float32 and every other shape);
+ *   LOWRAM_PATH_NONE   no chunk is selected (top_k = 0): only the tail.
+ * The choice depends on the dims alone; results agree with the oracle on
+ * every path. */
+enum { LOWRAM_PATH_NONE = 0, LOWRAM_PATH_CHAIN = 1, LOWRAM_PATH_MFMA = 2, LOWRAM_PATH_VALU = 3 };
+lowram_status lowram_decode_kernel(const lowram_dims *dims, int32_t *path);
+
 /* Storage accounting (host only).  *dense = M_KV = 2 L H_kv d_h N s for the
  * group with s = 2 (bf16) or 4 (f32 act) -- the M_KV formula of the zicq.com
  * English summary, "Core Mechanism" -- and *compressed = coefficients + basis

@@ -166,3 +166,18 @@ def test_product_path_does_not_import_the_oracle():
                 assert not re.search(r"^\s*(from|import)\s+(oracle|synth)\b", text, re.M), f
     ora = open(os.path.join(ROOT, "oracle", "lowram_oracle.py")).read()
     assert not re.search(r"^\s*(from|import)\s+(decode_attention_compressed_amd|synth|torch)\b", ora, re.M)
+
+
+@pytest.mark.parametrize("name,path", [("tiny-fp32", "valu"), ("llama8b-32k", "chain"), ("mistral7b-16k", "chain"),
+                                       ("qwen4b-64k", "mfma"), ("composed-int8-evict-128k", "chain")])
+def test_decode_kernel_per_workload(name, path):
+    from synth.configs import BY_NAME
+    s = BY_NAME[name]
+    # decode runs on the cache after eviction
+    assert P.decode_kernel(dims_of(s, n_ctx=s.N_after)) == path
+
+
+def test_decode_kernel_tail_only_and_errors():
+    d = dims_of(TINY)
+    assert P.decode_kernel(P.with_(d, top_k=0)) == "none"
+    assert L.lib().lowram_decode_kernel(ctypes.byref(d), None) == L.E_INVALID
