@@ -24,7 +24,9 @@ Where the pages leave a step open, the reading taken here is stated in the
 docstring of the function that takes it (scorer = group-summed query against
 the chunk's mean coefficient; predictor input = reconstructed key; squared L2
 error per (layer, head); lowest index wins ties; symmetric per-channel int8
-with fp16 scales; eviction by the group-summed score of observation queries).
+with fp16 scales; eviction by the group-summed score of observation queries;
+tail growth by re-packing the oldest C tail tokens as a new chunk against the
+existing basis, predictor and int8 scales).
 
 Stored tensors are passed as numpy arrays in their storage dtype: float64,
 float32, float16, int8, or uint16 holding bfloat16 bit patterns.
@@ -451,6 +453,100 @@ def evict(cache: dict, inp: dict, s, obs_q: np.ndarray, keep: int) -> dict:
                         n += 1
                 ptr[b, l, h, keep] = n
     new["res_ptr"], new["res_idx"], new["res_val"] = ptr, idx, val
+    return new
+
+
+# ============================================================================
+# tail growth: re-pack the oldest tail chunk into the compressed cache
+# ============================================================================
+def quantise_with(x: np.ndarray, scale: np.ndarray, axis: int) -> np.ndarray:
+    """int8 with given per-channel fp16 scales: q = clamp(rne(x / s), -127, 127),
+    zero where s = 0 (the rule of `quantise`, scales kept)."""
+    x = np.asarray(x, dtype=np.float64)
+    s = np.expand_dims(np.asarray(scale).astype(np.float64), axis)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint(x / np.where(s > 0, s, 1.0)), 0.0)
+    return np.clip(q, -127, 127).astype(np.int8)
+
+
+def repack(cache: dict, model: dict, k_new: np.ndarray, v_new: np.ndarray, s, m: int,
+           stored_coeff: np.ndarray | None = None) -> dict:
+    """Append C post-prefill tokens to the compressed cache as one new chunk.
+
+    The rit.work page (section on generation) keeps tokens generated after the
+    prefill uncompressed; the pages do not say what happens as that tail grows.
+    Reading taken here: once C tail tokens have accumulated they are compressed
+    the way the prefill was, against the existing basis and predictor, and
+    appended as chunk n_c:
+      1. c_t = U^T k_t^cat for the C tokens; stored rounded to the coefficient
+         dtype, or for int8 with the cache's existing per-channel scales
+         (clamped; the scales, and so every stored value, stay unchanged);
+      2. landmark_{n_c} = mean of the stored (dequantised) c_t, fp32;
+      3. per (l, h): e_t = ||v_t - f(U_{l,h} deq(c~_t))||^2 over the C tokens and
+         the m tokens with the largest e (lowest index first on ties) keep
+         delta = v - v_hat, stored rounded (int8: existing per-dim scales);
+         residual sets of earlier chunks are unchanged;
+      4. the residual CSR gains one chunk: the new entries follow the live ones
+         (res_ptr[n_c] of the old cache), token indices N + t ascending.
+    k_new, v_new: [B][G][Hkv][C][dh] stored act dtype.  `stored_coeff` (optional,
+    [B][C][r] stored) replaces step 1's rounding so that steps 2-4 can be
+    checked on another implementation's stored bits.  Returns the new cache
+    (residual capacity old capacity + m).
+    """
+    B, G, Hkv, dh, C, r = s.B, s.G, s.Hkv, s.dh, s.C, s.r
+    act, cdt, rdt = s.act, s.coeff, s.resid
+    N = cache["coeff"].shape[1]
+    n_c = N // C
+    cap = cache["res_idx"].shape[-1]
+    U_all = decode(model["basis"], act)
+    coeff_new, lm_new = [], []
+    ptr = np.zeros((B, G, Hkv, n_c + 2), dtype=np.int32)
+    idx = np.zeros((B, G, Hkv, cap + m), dtype=np.int32)
+    val = np.zeros((B, G, Hkv, cap + m, dh), dtype=cache["res_val"].dtype)
+    errors = np.zeros((B, G, Hkv, C))
+    for b in range(B):
+        U = U_all[b]
+        k = decode(k_new[b], act)
+        v = decode(v_new[b], act)
+        k_cat = k.transpose(2, 0, 1, 3).reshape(C, -1)
+        c = project(k_cat, U)
+        if stored_coeff is not None:
+            cst = np.asarray(stored_coeff[b])
+        elif cdt == I8:
+            cst = quantise_with(c, cache["coeff_scale"][b], axis=0)
+        else:
+            cst = round_to(c, cdt)
+        cdeq = dequantise(cst, cache["coeff_scale"][b], axis=0) if cdt == I8 else decode(cst, cdt)
+        coeff_new.append(cst)
+        lm_new.append(landmarks(cdeq, C))
+        for l in range(G):
+            for h in range(Hkv):
+                Ulh = basis_slice(U, l, h, Hkv, dh)
+                khat = cdeq @ Ulh.T
+                w1, b1 = decode(model["w1"][b, l, h], act), decode(model["b1"][b, l, h], act)
+                w2, b2 = decode(model["w2"][b, l, h], act), decode(model["b2"][b, l, h], act)
+                vhat = predict(khat, w1, b1, w2, b2)
+                e = l2_errors(v[l, h], vhat)
+                errors[b, l, h] = e
+                R = topk_indices(e, m)
+                delta = v[l, h][R] - vhat[R]
+                if rdt == I8:
+                    dst = quantise_with(delta, cache["res_scale"][b, l, h], axis=0)
+                else:
+                    dst = round_to(delta, rdt)
+                op = cache["res_ptr"][b, l, h]
+                live = int(op[n_c])
+                ptr[b, l, h, :n_c + 1] = op
+                ptr[b, l, h, n_c + 1] = live + m
+                idx[b, l, h, :live] = cache["res_idx"][b, l, h, :live]
+                idx[b, l, h, live:live + m] = N + R
+                val[b, l, h, :live] = cache["res_val"][b, l, h, :live]
+                val[b, l, h, live:live + m] = dst
+    new = dict(cache)
+    new["coeff"] = np.concatenate([cache["coeff"], np.stack(coeff_new)], axis=1)
+    new["landmark"] = np.concatenate([cache["landmark"], np.stack(lm_new)], axis=1)
+    new["res_ptr"], new["res_idx"], new["res_val"] = ptr, idx, val
+    new["repack_errors"] = errors
     return new
 
 

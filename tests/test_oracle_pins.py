@@ -447,3 +447,162 @@ def test_eviction_keep_all_is_identity():
     new = O.evict(cache, inp, s, inp["obs_q"], s.n_c)
     for name in ("coeff", "landmark", "res_ptr", "res_idx", "res_val"):
         assert np.array_equal(new[name], cache[name]), name
+
+
+# ---------------------------------------------------------------------------
+# tail growth: re-pack of the oldest C tail tokens as a new chunk
+# ---------------------------------------------------------------------------
+def _tail_chunk(inp, lo, C):
+    return inp["k_tail"][:, :, :, lo:lo + C], inp["v_tail"][:, :, :, lo:lo + C]
+
+
+def _grown(inp, C):
+    """The same sequences with the first C tail tokens moved into the prefill."""
+    g = dict(inp)
+    for a in ("k", "v"):
+        g[a] = np.concatenate([inp[a], inp[a + "_tail"][:, :, :, :C]], axis=3)
+        g[a + "_tail"] = inp[a + "_tail"][:, :, :, C:]
+    return g
+
+
+@pytest.mark.parametrize("dt", [F64, BF16])
+def test_repack_without_residuals_equals_compress_of_longer_prefill(dt):
+    s = tiny64(T=12, B=2, act=dt, coeff=dt, resid=dt)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    new = O.repack(cache, inp, *_tail_chunk(inp, 0, s.C), s, m=0)
+    ref = O.compress(_grown(inp, s.C), tiny64(T=4, N=72, B=2, act=dt, coeff=dt, resid=dt))
+    assert np.array_equal(new["coeff"], ref["coeff"])
+    assert np.array_equal(new["landmark"], ref["landmark"])
+    assert np.allclose(new["repack_errors"], ref["errors"][..., s.N:], rtol=1e-12, atol=0)
+    # no new residuals: the old CSR with its last pointer repeated
+    assert np.array_equal(new["res_ptr"][..., :-1], cache["res_ptr"])
+    assert np.array_equal(new["res_ptr"][..., -1], cache["res_ptr"][..., -1])
+    assert np.array_equal(new["res_idx"], cache["res_idx"])
+    assert np.array_equal(new["res_val"], cache["res_val"])
+
+
+def test_repack_residuals_are_brute_force_topk_of_the_new_chunk():
+    s = tiny64(T=12, B=2, act=BF16, coeff=BF16, resid=BF16)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    m, C, N, n_c = 3, s.C, s.N, s.n_c
+    kt, vt = _tail_chunk(inp, 0, C)
+    new = O.repack(cache, inp, kt, vt, s, m)
+    assert new["res_idx"].shape[-1] == s.n_res + m
+    for b in range(s.B):
+        U = O.decode(inp["basis"][b], s.act)
+        kcat = O.decode(kt[b], s.act).transpose(2, 0, 1, 3).reshape(C, -1)
+        c = np.einsum("dr,td->tr", U, kcat)
+        cst = O.decode(new["coeff"][b, N:], s.coeff)
+        assert np.all(np.abs(cst - c) <= np.abs(c) * 2.0 ** -8)
+        assert np.allclose(new["landmark"][b, n_c], cst.mean(axis=0), rtol=1e-6, atol=1e-7)
+        for l in range(s.G):
+            for h in range(s.Hkv):
+                r0 = (l * s.Hkv + h) * s.dh
+                kh = np.einsum("tr,dr->td", cst, U[r0:r0 + s.dh])
+                w = [O.decode(inp[n][b, l, h], s.act) for n in ("w1", "b1", "w2", "b2")]
+                v = O.decode(vt[b, l, h], s.act)
+                d = v - mlp_explicit(kh, *w)
+                e = new["repack_errors"][b, l, h]
+                assert np.allclose(e, np.sum(d * d, axis=1), rtol=1e-12)
+                want = sorted(sorted(range(C), key=lambda t: (-e[t], t))[:m])
+                op, ptr = cache["res_ptr"][b, l, h], new["res_ptr"][b, l, h]
+                live = int(op[n_c])
+                assert np.array_equal(ptr[:n_c + 1], op) and ptr[n_c + 1] == live + m
+                assert list(new["res_idx"][b, l, h, live:live + m]) == [N + t for t in want]
+                assert np.array_equal(new["res_idx"][b, l, h, :live], cache["res_idx"][b, l, h, :live])
+                assert np.array_equal(new["res_val"][b, l, h, :live], cache["res_val"][b, l, h, :live])
+                got = O.decode(new["res_val"][b, l, h, live:live + m], s.resid)
+                assert np.all(np.abs(got - d[want]) <= np.abs(d[want]) * 2.0 ** -8)
+
+
+def test_repacked_exact_cache_equals_dense_attention():
+    s = tiny64(r=32, rho=1.0, B=2, T=12)  # r = D, every token keeps its residual
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    new = O.repack(cache, inp, *_tail_chunk(inp, 0, s.C), s, m=s.C)
+    s2 = tiny64(r=32, rho=1.0, B=2, T=4, N=72)
+    g = _grown(inp, s.C)
+    for l in range(s.G):
+        q = inp["q"][1, l]
+        out, sel = O.decode_layer(new, g, s2, l, q, s2.n_c)
+        assert np.array_equal(sel[0, 0], np.arange(s2.n_c))
+        for b in range(s.B):
+            for gq in range(s.Hq):
+                h = gq * s.Hkv // s.Hq
+                K = np.concatenate([inp["k"][b, l, h], inp["k_tail"][b, l, h]])
+                V = np.concatenate([inp["v"][b, l, h], inp["v_tail"][b, l, h]])
+                assert np.allclose(out[b, gq], sdpa64(q[b, gq], K, V), rtol=1e-10, atol=1e-11)
+
+
+def test_repack_twice_matches_exact_attention_after_eviction():
+    # eviction leaves spare residual capacity; two re-packs append after the live entries
+    s = tiny64(r=32, rho=1.0, B=2, T=20, N=64, n_obs=2)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    keep = 5
+    ev = O.evict(cache, inp, s, inp["obs_q"], keep)
+    kt, vt = _tail_chunk(inp, 0, s.C)
+    s1 = tiny64(r=32, rho=1.0, B=2, T=12, N=keep * s.C)
+    one = O.repack(ev, inp, kt, vt, s1, m=s.C)
+    kt2, vt2 = _tail_chunk(inp, s.C, s.C)
+    s2 = tiny64(r=32, rho=1.0, B=2, T=4, N=(keep + 1) * s.C)
+    two = O.repack(one, inp, kt2, vt2, s2, m=s.C)
+    assert two["res_idx"].shape[-1] == s.N + 2 * s.C
+    g = dict(inp)
+    g["k_tail"], g["v_tail"] = inp["k_tail"][:, :, :, 2 * s.C:], inp["v_tail"][:, :, :, 2 * s.C:]
+    s3 = tiny64(r=32, rho=1.0, B=2, T=4, N=(keep + 2) * s.C)
+    for l in range(s.G):
+        q = inp["q"][0, l]
+        out, _ = O.decode_layer(two, g, s3, l, q, keep + 2)
+        for b in range(s.B):
+            toks = np.concatenate([np.arange(j * s.C, (j + 1) * s.C) for j in ev["keep"][b]])
+            for gq in range(s.Hq):
+                h = gq * s.Hkv // s.Hq
+                K = np.concatenate([inp["k"][b, l, h][toks], inp["k_tail"][b, l, h]])
+                V = np.concatenate([inp["v"][b, l, h][toks], inp["v_tail"][b, l, h]])
+                assert np.allclose(out[b, gq], sdpa64(q[b, gq], K, V), rtol=1e-10, atol=1e-11)
+
+
+def test_repack_int8_keeps_scales_and_reproduces_prefill_codes():
+    s = tiny64(T=12, B=2, act=BF16, coeff=I8, resid=I8)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    C, N, n_c = s.C, s.N, s.n_c
+    # the prefill's own first chunk, re-packed, gives back its stored codes and landmark
+    again = O.repack(cache, inp, inp["k"][:, :, :, :C], inp["v"][:, :, :, :C], s, m=2)
+    assert np.array_equal(again["coeff"][:, N:], cache["coeff"][:, :C])
+    assert np.array_equal(again["landmark"][:, n_c], cache["landmark"][:, 0])
+    assert np.array_equal(again["coeff_scale"], cache["coeff_scale"])
+    assert np.array_equal(again["res_scale"], cache["res_scale"])
+    # new tokens: round-to-nearest codes on the old scales, clamped to +-127
+    kt, vt = _tail_chunk(inp, 0, C)
+    new = O.repack(cache, inp, kt, vt, s, m=3)
+    n_in = n_out = 0
+    for b in range(s.B):
+        U = O.decode(inp["basis"][b], s.act)
+        kcat = O.decode(kt[b], s.act).transpose(2, 0, 1, 3).reshape(C, -1)
+        c = np.einsum("dr,td->tr", U, kcat)
+        sc = cache["coeff_scale"][b].astype(np.float64)[None, :]
+        q = new["coeff"][b, N:].astype(np.float64)
+        inside = np.abs(c) <= 127 * sc
+        assert np.all(np.abs(q) <= 127)
+        assert np.all(np.abs(q * sc - c)[inside] <= (sc / 2 * (1 + 1e-12) + 0 * c)[inside])
+        assert np.all((q == 127 * np.sign(c))[~inside])
+        for l in range(s.G):
+            for h in range(s.Hkv):
+                live = int(cache["res_ptr"][b, l, h, n_c])
+                rs = cache["res_scale"][b, l, h].astype(np.float64)[None, :]
+                dq = new["res_val"][b, l, h, live:live + 3].astype(np.float64)
+                R = new["res_idx"][b, l, h, live:live + 3] - N
+                r0 = (l * s.Hkv + h) * s.dh
+                kh = np.einsum("tr,dr->td", q * sc, U[r0:r0 + s.dh])
+                w = [O.decode(inp[n][b, l, h], s.act) for n in ("w1", "b1", "w2", "b2")]
+                d = (O.decode(vt[b, l, h], s.act) - mlp_explicit(kh, *w))[R]
+                ok = np.abs(d) <= 127 * rs
+                assert np.all(np.abs(dq) <= 127)
+                assert np.all(np.abs(dq * rs - d)[ok] <= (rs / 2 * (1 + 1e-9) + 0 * d)[ok])
+                assert np.all((dq == 127 * np.sign(d))[~ok])
+                n_in += int(ok.sum()); n_out += int((~ok).sum())
+    assert n_in > 0 and n_out > 0  # both the rounding and the clamp are exercised
