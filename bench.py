@@ -16,6 +16,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -106,6 +107,49 @@ def traffic_for_current_kernel():
     return t.get("bytes_per_launch")
 
 
+def repack_bytes(s, d, live_rows, m):
+    """Algorithmic HBM bytes of one re-pack call: the existing cache read once and
+    written once into the grown cache, plus the new chunk (C tail tokens of K and
+    V, the basis, the predictor, and the rows it writes)."""
+    cb = 1 if s.coeff == "i8" else (4 if s.act == "f32" else 2)
+    rb = s.dh * (1 if s.resid == "i8" else (4 if s.act == "f32" else 2))
+    ab = 4 if s.act == "f32" else 2
+    N, C, n_c, lh = d.n_ctx, s.C, d.n_ctx // s.C, s.G * s.Hkv
+    old = N * s.r * cb + n_c * s.r * 4 + live_rows * (rb + 4) + lh * (n_c + 1) * 4
+    new = (2 * lh * C * s.dh * ab + s.D * s.r * ab + lh * (2 * s.F * s.dh + s.F + s.dh) * ab
+           + C * s.r * cb + s.r * 4 + lh * m * (rb + 4) + lh * 4)
+    return s.B * (2 * old + new)
+
+
+def time_repack(P, s, d, model, cache, dev, ev, reps=5):
+    """Time lowram_repack (oldest C tail tokens -> one new chunk) on this cache."""
+    import torch
+    if d.n_tail < s.C:
+        return None
+    m = min(s.C, int(math.ceil(s.rho * s.C - 1e-9)))
+    d2 = P.with_(d, n_ctx=d.n_ctx + s.C, n_res=d.n_res + m, n_tail=d.n_tail - s.C)
+    dst = P.alloc_cache(d2)
+    for name in ("coeff_scale", "res_scale"):
+        if name in cache:
+            dst[name] = cache[name]
+    ws = P.workspace(d, P._lib.OP_REPACK)
+    P.repack(d, model, cache, dev["k_tail"], dev["v_tail"], m, dst=dst, ws=ws)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        P.repack(d, model, cache, dev["k_tail"], dev["v_tail"], m, dst=dst, ws=ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+    live = int(cache["res_ptr"][..., -1].sum().item()) // s.B
+    nbytes = repack_bytes(s, d, live, m)
+    del dst, ws
+    log(f"repack {us:.1f} us/call ({us / s.C:.2f} us per decode step amortised over C = {s.C})")
+    return {"us_per_call": round(us, 1), "amortised_us_per_step": round(us / s.C, 3), "new_res_rows": m,
+            "algorithmic_bytes": int(nbytes), "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "how": f"{reps} eager calls between HIP events; once per C decode steps"}
+
+
 def cpu_baseline(s, host, inp, budget_s):
     from oracle import lowram_oracle as O
     try:
@@ -173,6 +217,7 @@ def main():
         cache, d, _ = P.evict(d, model, cache, to_dev(inp["obs_q"]), s.keep_chunks)
         torch.cuda.synchronize()
     comp_bytes, dense_bytes = P.cache_bytes(dims_of(s))
+    repack = time_repack(P, s, d, model, cache, dev, ev)
 
     # per (query set, layer) pre-marshalled calls
     kk = P.k_eff(d)
@@ -347,6 +392,7 @@ def main():
         "compression_ratio": round(dense_bytes / comp_bytes, 3),
         "selected_chunk_union_per_seq": round(float(union), 1),
         "compress_ms": round(compress_ms, 2),
+        "repack": repack,
         "step_time_distribution": step_dist,
         "graph": graph is not None,
         "device": dev_name,

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(HERE, "liblowram.so")
 
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
 F32, BF16, F16, I8 = range(4)
-OP_COMPRESS, OP_DECODE, OP_EVICT, OP_DENSE = range(4)
+OP_COMPRESS, OP_DECODE, OP_EVICT, OP_DENSE, OP_REPACK = range(5)
 
 DIM_FIELDS = ("batch", "layers", "heads_q", "heads_kv", "head_dim", "rank", "hidden", "n_ctx",
               "chunk", "top_k", "n_tail", "n_res", "act", "coeff", "resid")
@@ -54,6 +54,7 @@ SIGNATURES = {
     "lowram_decode_attend": [P(Dims), i32, P(Model), P(Cache), vp, vp, vp, vp, sz, vp],
     "lowram_decode_combine": [P(Dims), i32, P(Model), vp, vp, sz, vp],
     "lowram_evict": [P(Dims), P(Model), P(Cache), vp, i32, i32, P(Cache), vp, vp, sz, vp],
+    "lowram_repack": [P(Dims), P(Model), P(Cache), vp, vp, i32, P(Cache), vp, sz, vp],
     "lowram_dense_decode_attn": [P(Dims), vp, vp, vp, i32, i64, vp, vp, sz, vp],
     "lowram_status_string": [i32],
     "lowram_last_error": [],

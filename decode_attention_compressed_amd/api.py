@@ -229,6 +229,30 @@ def evict(d: L.Dims, model: dict, src: dict, obs_q, keep: int, dst=None, keep_ou
     return dst, d2, keep_out
 
 
+def repack(d: L.Dims, model: dict, src: dict, k_tail, v_tail, n_new_res: int, dst=None, ws=None,
+           stream=None):
+    """Move the oldest d.chunk tail tokens into the cache as one new chunk.
+    Returns (dst cache, its dims: n_ctx + chunk, n_res + n_new_res, n_tail - chunk)."""
+    dt = TORCH_DT[d.act]
+    d2 = with_(d, n_ctx=d.n_ctx + d.chunk, n_res=d.n_res + n_new_res, n_tail=d.n_tail - d.chunk)
+    dev = k_tail.device
+    if dst is None:
+        dst = alloc_cache(d2, dev)
+        if d.coeff == L.I8:
+            dst["coeff_scale"] = src["coeff_scale"]
+        if d.resid == L.I8:
+            dst["res_scale"] = src["res_scale"]
+    ws = workspace(d, L.OP_REPACK, dev) if ws is None else ws
+    tail_shape = (d.batch, d.layers, d.heads_kv, d.n_tail, d.head_dim)
+    L.check(L.lib().lowram_repack(ctypes.byref(d), ctypes.byref(model_struct(d, model)),
+                                  ctypes.byref(cache_struct(d, src)),
+                                  _ptr(k_tail, dt, tail_shape, "k_tail"),
+                                  _ptr(v_tail, dt, tail_shape, "v_tail"), n_new_res,
+                                  ctypes.byref(cache_struct(d2, dst)), _ptr(ws, torch.uint8),
+                                  ws.numel(), _stream(stream)))
+    return dst, d2
+
+
 def dense_workspace(d: L.Dims, n_tokens: int, device="cuda") -> torch.Tensor:
     return workspace(with_(d, n_ctx=n_tokens), L.OP_DENSE, device)
 

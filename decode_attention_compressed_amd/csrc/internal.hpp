@@ -96,6 +96,32 @@ struct EvictArgs {
 };
 hipError_t run_evict(const EvictArgs &a, hipStream_t st);
 
+struct RepackArgs {
+  const void *basis, *w1, *b1, *w2, *b2;
+  const void *k_tail, *v_tail;  // [B][G][Hkv][T][dh] act; tokens [0, C) are packed
+  const void *coeff; const uint16_t *coeff_scale; const float *landmark;
+  const int32_t *res_ptr, *res_idx; const void *res_val; const uint16_t *res_scale;
+  void *d_coeff; uint16_t *d_coeff_scale; float *d_landmark;
+  int32_t *d_res_ptr, *d_res_idx; void *d_res_val; uint16_t *d_res_scale;
+  double *err;                  // workspace [B][G][Hkv][C]
+  double *c64;                  // workspace [B][C][r] (int8 coefficients only)
+  double *part;                 // workspace [S][B][C][r], S = project_splits(B, C, D, r) > 1
+  int32_t *t_idx;               // workspace [B][G][Hkv][C]
+  int32_t *t_ptr;               // workspace [B][G][Hkv][2]
+  double *dall;                 // workspace [B][G][Hkv][C][dh]: float64 delta of every new token
+  int B, G, Hq, Hkv, dh, r, F, N, C, T, n_res, m, act, coeff_dt, resid_dt;
+};
+hipError_t run_repack(const RepackArgs &a, hipStream_t st);
+
+// Slices of the D-long reduction of a projection of N tokens: doubled while the
+// launch stays within about 512 workgroups and each slice keeps >= 256 of D.
+inline int project_splits(int B, int N, int D, int r) {
+  const long tiles = (long)((r + 63) / 64) * ((N + 63) / 64) * B;
+  int S = 1;
+  while (tiles * S * 2 <= 512 && D / (S * 2) >= 256) S *= 2;
+  return S;
+}
+
 // Kernels with more than 64 KiB of dynamic LDS declare it once per instantiation.
 template <typename K>
 inline void allow_dynamic_lds(K kernel, size_t bytes) {

@@ -32,30 +32,39 @@ __device__ __forceinline__ void st_round(bf16 *p, double x) { p->u = f64_to_bf16
 __device__ __forceinline__ void st_round(double *p, double x) { *p = x; }
 
 // ---------------------------------------------------------------------------
-// C1: out[b][t][i] = sum_kk K(b, t, kk) U[b][kk][i], float64 accumulate.
-// K(b, t, kk) = k[b][l][h][t][d] with kk = (l*Hkv + h)*dh + d.
-// grid (ceil(r/64), ceil(N/64), B), 256 threads, 4x4 outputs per thread.
+// C1: out[b][o0 + t][i] = sum_kk K(b, t, kk) U[b][kk][i] for t < N, float64
+// accumulate.  K(b, t, kk) = k[b][l][h][t][d] with kk = (l*Hkv + h)*dh + d and
+// Nk tokens per (l, h) block of k; out holds No rows per sequence.
+// With S > 1 the reduction over kk is split in S slices of Dsl (a multiple of
+// 16): slice s writes its float64 partial sums to out + s * s_stride (TO =
+// double) and k_project_sum adds the slices in order.
+// grid (ceil(r/64), ceil(N/64), B * S), 256 threads, 4x4 outputs per thread.
 // ---------------------------------------------------------------------------
 template <typename TA, typename TO>
 __global__ __launch_bounds__(256) void k_project(const TA *__restrict__ k, const TA *__restrict__ U,
-                                                 TO *__restrict__ out, int N, int D, int dh, int r) {
+                                                 TO *__restrict__ out, int N, int D, int dh, int r,
+                                                 int Nk, int No, int o0, int S, int Dsl,
+                                                 long s_stride) {
   __shared__ double As[16][64 + 1];
   __shared__ double Bs[16][64];
-  const int b = blockIdx.z, t0 = blockIdx.y * 64, i0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int b = blockIdx.z / S, sl = blockIdx.z % S;
+  const int t0 = blockIdx.y * 64, i0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int kbeg = sl * Dsl, kend = min(D, kbeg + Dsl);
+  out += sl * s_stride;
   const int tx = tid % 16, ty = tid / 16;
-  const TA *kb = k + (long)b * D * N;  // [G*Hkv][N][dh] blocks
+  const TA *kb = k + (long)b * D * Nk;  // [G*Hkv][Nk][dh] blocks
   const TA *Ub = U + (long)b * D * r;
   double acc[4][4] = {};
-  for (int k0 = 0; k0 < D; k0 += 16) {
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
     for (int idx = tid; idx < 16 * 64; idx += 256) {
       const int kk = idx % 16, t = idx / 16;  // consecutive threads walk d (contiguous)
       const int gk = k0 + kk, tt = t0 + t;
-      As[kk][t] = (tt < N && gk < D) ? ldd(kb, (long)(gk / dh) * N * dh + (long)tt * dh + gk % dh) : 0.0;
+      As[kk][t] = (tt < N && gk < kend) ? ldd(kb, (long)(gk / dh) * Nk * dh + (long)tt * dh + gk % dh) : 0.0;
     }
     for (int idx = tid; idx < 16 * 64; idx += 256) {
       const int kk = idx / 64, i = idx % 64;
       const int gk = k0 + kk, ii = i0 + i;
-      Bs[kk][i] = (gk < D && ii < r) ? ldd(Ub, (long)gk * r + ii) : 0.0;
+      Bs[kk][i] = (gk < kend && ii < r) ? ldd(Ub, (long)gk * r + ii) : 0.0;
     }
     __syncthreads();
 #pragma unroll
@@ -78,9 +87,23 @@ __global__ __launch_bounds__(256) void k_project(const TA *__restrict__ k, const
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int ii = i0 + tx + 16 * c;
-      if (tt < N && ii < r) st_round(out + ((long)b * N + tt) * r + ii, acc[a][c]);
+      if (tt < N && ii < r) st_round(out + ((long)b * No + o0 + tt) * r + ii, acc[a][c]);
     }
   }
+}
+
+// out[b][o0 + t][i] = round(sum over s = 0..S-1 of part[s][b][t][i]), slices
+// added in order.  part: [S][B][N][r] float64.  grid (ceil(B*N*r / 256)).
+template <typename TO>
+__global__ __launch_bounds__(256) void k_project_sum(const double *__restrict__ part,
+                                                     TO *__restrict__ out, int B, int N, int r,
+                                                     int S, int No, int o0) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x, per = (long)B * N * r;
+  if (i >= per) return;
+  double s = 0.0;
+  for (int j = 0; j < S; ++j) s += part[j * per + i];
+  const long b = i / ((long)N * r), rem = i - b * N * r;
+  st_round(out + ((long)b * No + o0) * r + rem, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -104,33 +127,44 @@ __global__ __launch_bounds__(256) void k_colmax(const double *__restrict__ x, ui
 }
 
 // q = clamp(rne(x / s), -127, 127); zero where the scale is zero.
+// x: [batch][rows][cols] float64, s: [batch][cols]; row t of batch bt is
+// written to row o0 + t of a [batch][out_rows][cols] int8 array.
 __global__ __launch_bounds__(256) void k_quant(const double *__restrict__ x,
                                                const uint16_t *__restrict__ s,
                                                int8_t *__restrict__ q, long rows, int cols,
-                                               long total) {
+                                               long total, long out_rows, long o0) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
   const long bt = i / (rows * cols);
+  const long rc = i - bt * rows * cols;
   const int c = (int)(i % cols);
   const double sc = (double)f16_bits_to_f32(s[bt * cols + c]);
   double v = 0.0;
   if (sc > 0.0) v = fmin(127.0, fmax(-127.0, rint(x[i] / sc)));
-  q[i] = (int8_t)v;
+  q[(bt * out_rows + o0) * cols + rc] = (int8_t)v;
 }
 
-// C2: landmark[b][j][i] = float32(mean_t deq(coeff[b][jC + t][i])).  grid (n_c, B).
+// C2: landmark[b][j][i] = float32(mean_t deq(coeff[b][jC + t][i])) for chunks
+// j = j0 + blockIdx.y of an N-token cache, 64 channels i per workgroup: four
+// row groups sum rows t = g, g+4, ... in float64 and are added in a fixed
+// order.  grid (ceil(r/64), chunks, B), 256 threads.
 template <typename TC>
 __global__ __launch_bounds__(256) void k_landmark(const TC *__restrict__ coeff,
                                                   const uint16_t *__restrict__ cscale,
-                                                  float *__restrict__ lm, int N, int C, int r) {
-  const int j = blockIdx.x, b = blockIdx.y;
+                                                  float *__restrict__ lm, int N, int C, int r, int j0) {
+  __shared__ double red[4][64];
+  const int j = j0 + blockIdx.y, b = blockIdx.z;
+  const int c = threadIdx.x % 64, g = threadIdx.x / 64, i = blockIdx.x * 64 + c;
   const TC *cb = coeff + ((long)b * N + (long)j * C) * r;
   const uint16_t *sc = cscale ? cscale + (long)b * r : nullptr;
-  for (int i = threadIdx.x; i < r; i += 256) {
-    double s = 0.0;
-    for (int t = 0; t < C; ++t) s += ld_cdeq(cb, (long)t * r + i, sc, i);
-    lm[((long)b * (N / C) + j) * r + i] = (float)(s / (double)C);
-  }
+  double s = 0.0;
+  if (i < r)
+    for (int t = g; t < C; t += 4) s += ld_cdeq(cb, (long)t * r + i, sc, i);
+  red[g][c] = s;
+  __syncthreads();
+  if (g == 0 && i < r)
+    lm[((long)b * (N / C) + j) * r + i] =
+        (float)(((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) / (double)C);
 }
 
 // ---------------------------------------------------------------------------
@@ -138,6 +172,11 @@ __global__ __launch_bounds__(256) void k_landmark(const TC *__restrict__ coeff,
 // MODE 0: rows are tokens t, writes err[b][l][h][t] = ||v_t - v_hat_t||^2.
 // MODE 1: rows are residual entries e, token res_idx[e]; writes delta rows
 //         (rounded to TD) to dout[b][l][h][e][:].
+// MODE 2: as MODE 0, and also writes every token's float64 delta row to
+//         dout[b][l][h][t][:].
+// Token t reads coefficient row c0 + t of a cache with Nc rows per sequence and
+// value row t of v[b][l][h] (Nv rows per (b, l, h)); err has N entries per
+// (b, l, h).
 // grid (ceil(rows/TM), G*Hkv, B), 256 threads (16 x 16).
 // ---------------------------------------------------------------------------
 template <int DH, int TM, int MODE, typename TA, typename TC, typename TD>
@@ -148,7 +187,8 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
                                               const TA *__restrict__ b2, const TA *__restrict__ v,
                                               const int32_t *__restrict__ res_idx,
                                               double *__restrict__ err, TD *__restrict__ dout,
-                                              int Hkv, int N, int r, int F, int n_rows, int n_res) {
+                                              int Hkv, int N, int r, int F, int n_rows, int n_res,
+                                              int Nc, int c0, int Nv) {
   constexpr int NA = TM / 16, NC = DH / 16;
   constexpr int KS = DH + 1, HS = 64 + 1;
   extern __shared__ __align__(16) double psm[];
@@ -169,13 +209,13 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
   const TA *B1 = b1 + bh * F;
   const TA *W2 = w2 + bh * DH * F;
   const TA *B2 = b2 + bh * DH;
-  const TA *V = v + bh * N * DH;
-  const TC *cb = coeff + (long)b * N * r;
+  const TA *V = v + bh * Nv * DH;
+  const TC *cb = coeff + ((long)b * Nc + c0) * r;
   const uint16_t *sc = cscale ? cscale + (long)b * r : nullptr;
   for (int i = tid; i < TM; i += 256) {
     const int rr = row0 + i;
     int t = -1;
-    if (rr < n_rows) t = MODE == 0 ? rr : res_idx[bh * n_res + rr];
+    if (rr < n_rows) t = MODE == 1 ? res_idx[bh * n_res + rr] : rr;
     tok[i] = t;
   }
   __syncthreads();
@@ -272,7 +312,7 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
   for (int a = 0; a < NA; ++a) {
     const int m = ty + 16 * a;
     const int t = tok[m];
-    if (MODE == 0) {
+    if (MODE != 1) {
       double e = 0.0;
       if (t >= 0) {
 #pragma unroll
@@ -280,6 +320,7 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
           const int d = tx + 16 * c;
           const double dv = ldd(V, (long)t * DH + d) - (vacc[a][c] + ldd(B2, d));
           e = fma(dv, dv, e);
+          if (MODE == 2) st_round(dout + (bh * N + t) * DH + d, dv);
         }
       }
       // sum over the 16 threads of this row (lanes tx = 0..15 of one wave quarter)
@@ -393,76 +434,226 @@ __global__ __launch_bounds__(256) void k_evict_resid(const int32_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
+// tail re-pack
+// ---------------------------------------------------------------------------
+// dst[b][0..words) = src[b][0..words) for b = blockIdx.y, in 8-byte words, with
+// per-sequence strides src_stride / dst_stride (words).  grid (ceil(words/256), B).
+__global__ __launch_bounds__(256) void k_copy_rows(const uint2 *__restrict__ src, long src_stride,
+                                                   uint2 *__restrict__ dst, long dst_stride,
+                                                   long words) {
+  const long w = (long)blockIdx.x * 256 + threadIdx.x;
+  if (w >= words) return;
+  dst[(long)blockIdx.y * dst_stride + w] = src[(long)blockIdx.y * src_stride + w];
+}
+
+// Residual CSR of one (b, l, h) after appending a chunk: the source's n_c + 1
+// pointers and its live rows (ptr[n_c] of them, read on the device and clamped
+// to the capacity n_res), then the indices N + t_idx[e] of the m new rows
+// (whose values k_repack_rows writes), then zeros up to the new capacity
+// n_res + m.  Each workgroup moves RB rows in 8-byte words; the first also
+// writes the pointers.
+// grid (ceil((n_res + m) / RB), G*Hkv, B), 256 threads.
+constexpr int REPACK_RB = 64;
+__global__ __launch_bounds__(256) void k_repack_resid(
+    const int32_t *__restrict__ ptr, const int32_t *__restrict__ idx,
+    const unsigned char *__restrict__ val, const int32_t *__restrict__ t_idx,
+    int32_t *__restrict__ d_ptr,
+    int32_t *__restrict__ d_idx, unsigned char *__restrict__ d_val, int n_c, int N, int n_res,
+    int m, int row_bytes) {
+  const long bh = (long)blockIdx.z * gridDim.y + blockIdx.y;
+  const int tid = threadIdx.x, cap = n_res + m, words = row_bytes / 8;
+  const int e0 = blockIdx.x * REPACK_RB, e1 = min(cap, e0 + REPACK_RB);
+  const int32_t *op = ptr + bh * (n_c + 1);
+  const int live = min(max(op[n_c], 0), n_res);
+  if (blockIdx.x == 0)
+    for (int j = tid; j <= n_c + 1; j += 256) d_ptr[bh * (n_c + 2) + j] = j <= n_c ? op[j] : live + m;
+  for (int e = e0 + tid; e < e1; e += 256) {
+    int32_t x = 0;
+    if (e < live) x = idx[bh * n_res + e];
+    else if (e < live + m) x = N + t_idx[bh * m + (e - live)];
+    d_idx[bh * cap + e] = x;
+  }
+  const uint2 *sv = reinterpret_cast<const uint2 *>(val + bh * n_res * row_bytes);
+  uint2 *dv = reinterpret_cast<uint2 *>(d_val + bh * cap * row_bytes);
+  for (long w = (long)e0 * words + tid; w < (long)e1 * words; w += 256) {
+    const int e = (int)(w / words), o = (int)(w % words);
+    if (e >= live && e < live + m) continue;
+    dv[w] = e < live ? sv[(long)e * words + o] : make_uint2(0u, 0u);
+  }
+}
+
+__device__ __forceinline__ void st_resid(float *p, double x, const uint16_t *) { *p = (float)x; }
+__device__ __forceinline__ void st_resid(bf16 *p, double x, const uint16_t *) { p->u = f64_to_bf16_bits(x); }
+__device__ __forceinline__ void st_resid(int8_t *p, double x, const uint16_t *sc) {
+  const double s = (double)f16_bits_to_f32(*sc);
+  *p = (int8_t)(s > 0.0 ? fmin(127.0, fmax(-127.0, rint(x / s))) : 0.0);
+}
+
+// The m new residual rows of one (b, l, h): row e is token t_idx[e]'s float64
+// delta (dall, [B][G][Hkv][C][dh]) stored at row live + e of the grown cache,
+// rounded to TR (int8: the existing per-dim scales rscale[b][l][h][:]).
+// grid (G*Hkv, B), 256 threads.
+template <typename TR>
+__global__ __launch_bounds__(256) void k_repack_rows(const int32_t *__restrict__ ptr,
+                                                     const int32_t *__restrict__ t_idx,
+                                                     const double *__restrict__ dall,
+                                                     const uint16_t *__restrict__ rscale,
+                                                     TR *__restrict__ d_val, int n_c, int n_res,
+                                                     int m, int C, int dh) {
+  const long bh = (long)blockIdx.y * gridDim.x + blockIdx.x;
+  const int live = min(max(ptr[bh * (n_c + 1) + n_c], 0), n_res);
+  const long cap = n_res + m;
+  for (int i = threadIdx.x; i < m * dh; i += 256) {
+    const int e = i / dh, d = i % dh;
+    const int t = t_idx[bh * m + e];
+    st_resid(d_val + (bh * cap + live + e) * dh + d, dall[(bh * C + t) * dh + d],
+             rscale ? rscale + bh * dh + d : nullptr);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host sequencing
 // ---------------------------------------------------------------------------
+// One predictor pass over the tokens of every (b, l, h): errors over n_tok
+// tokens (coefficient rows c0.. of a cache with Nc rows per sequence, value
+// rows of v with Nv rows per (b, l, h)), the residual set (top n_sel, with
+// chunk CSR pointers), and the delta rows of that set -- float64 into d64 for
+// int8 residuals (quantised afterwards), else rounded into val.  With
+// delta_all the error pass also leaves every token's float64 delta row in d64
+// ([B][G][Hkv][n_tok][dh]) and no second pass runs: the caller gathers the
+// selected rows.
+struct PredPass {
+  const void *coeff; const uint16_t *cscale;
+  const void *basis, *w1, *b1, *w2, *b2, *v;
+  double *err; int32_t *idx, *ptr; void *val; double *d64;
+  int B, G, Hkv, r, F, n_tok, C, n_sel, Nc, c0, Nv, resid_i8, delta_all;
+};
+
 template <int DH, int TM, int MODE, typename TA, typename TC, typename TD>
-static void launch_pred(const CompressArgs &a, int n_rows, TD *dout, hipStream_t st) {
+static void launch_pred(const PredPass &p, int n_rows, TD *dout, hipStream_t st) {
   const size_t smem = sizeof(double) * ((size_t)TM * (DH + 1) + (size_t)TM * 65 + 16 * TM + 16 * DH);
-  dim3 grid((n_rows + TM - 1) / TM, a.G * a.Hkv, a.B);
+  dim3 grid((n_rows + TM - 1) / TM, p.G * p.Hkv, p.B);
   static const bool lds_ok = (allow_dynamic_lds(k_pred<DH, TM, MODE, TA, TC, TD>, smem), true);
   (void)lds_ok;
   hipLaunchKernelGGL((k_pred<DH, TM, MODE, TA, TC, TD>), grid, dim3(256), smem, st,
-                     (const TC *)a.coeff, a.coeff_scale, (const TA *)a.basis, (const TA *)a.w1,
-                     (const TA *)a.b1, (const TA *)a.w2, (const TA *)a.b2, (const TA *)a.v,
-                     a.res_idx, a.err, dout, a.Hkv, a.N, a.r, a.F, n_rows, a.n_res);
+                     (const TC *)p.coeff, p.cscale, (const TA *)p.basis, (const TA *)p.w1,
+                     (const TA *)p.b1, (const TA *)p.w2, (const TA *)p.b2, (const TA *)p.v,
+                     p.idx, p.err, dout, p.Hkv, p.n_tok, p.r, p.F, n_rows, p.n_sel, p.Nc, p.c0,
+                     p.Nv);
 }
 
 template <int DH, int TM, typename TA, typename TC, typename TR>
-static void pred_both(const CompressArgs &a, hipStream_t st) {
-  launch_pred<DH, TM, 0, TA, TC, double>(a, a.N, nullptr, st);
-  hipLaunchKernelGGL(k_err_topk, dim3(a.G * a.Hkv, a.B), dim3(1024), 0, st, a.err, a.N, a.C,
-                     a.n_res, a.res_idx, a.res_ptr);
-  if (a.n_res > 0) {
-    if (a.resid_dt == LOWRAM_I8)
-      launch_pred<DH, TM, 1, TA, TC, double>(a, a.n_res, a.d64, st);
+static void pred_both(const PredPass &p, hipStream_t st) {
+  if (p.delta_all)
+    launch_pred<DH, TM, 2, TA, TC, double>(p, p.n_tok, p.d64, st);
+  else
+    launch_pred<DH, TM, 0, TA, TC, double>(p, p.n_tok, nullptr, st);
+  hipLaunchKernelGGL(k_err_topk, dim3(p.G * p.Hkv, p.B), dim3(1024), 0, st, p.err, p.n_tok, p.C,
+                     p.n_sel, p.idx, p.ptr);
+  if (p.n_sel > 0 && !p.delta_all) {
+    if (p.resid_i8)
+      launch_pred<DH, TM, 1, TA, TC, double>(p, p.n_sel, p.d64, st);
     else
-      launch_pred<DH, TM, 1, TA, TC, TR>(a, a.n_res, (TR *)a.res_val, st);
+      launch_pred<DH, TM, 1, TA, TC, TR>(p, p.n_sel, (TR *)p.val, st);
   }
 }
 
 template <typename TA, typename TC, typename TR>
-static void pred_dispatch(const CompressArgs &a, hipStream_t st) {
-  if (a.dh == 64) pred_both<64, 128, TA, TC, TR>(a, st);
-  else if (a.dh == 128) pred_both<128, 64, TA, TC, TR>(a, st);
-  else pred_both<256, 32, TA, TC, TR>(a, st);
+static void pred_by_dh(int dh, const PredPass &p, hipStream_t st) {
+  if (dh == 64) pred_both<64, 128, TA, TC, TR>(p, st);
+  else if (dh == 128) pred_both<128, 64, TA, TC, TR>(p, st);
+  else pred_both<256, 32, TA, TC, TR>(p, st);
+}
+
+// Residual rows are either float32 (act F32), bf16, or int8 whose float64
+// deltas pred_both leaves in d64; the template argument only names the type
+// non-int8 rows are rounded to.
+static void pred_dispatch(int act, int coeff_dt, int dh, const PredPass &p, hipStream_t st) {
+  if (act == LOWRAM_F32) pred_by_dh<float, float, float>(dh, p, st);
+  else if (coeff_dt == LOWRAM_BF16) pred_by_dh<bf16, bf16, bf16>(dh, p, st);
+  else pred_by_dh<bf16, int8_t, bf16>(dh, p, st);
+}
+
+static void launch_landmark(int act, int coeff_dt, const void *coeff, const uint16_t *cscale,
+                            float *lm, int B, int N, int C, int r, int j0, int chunks,
+                            hipStream_t st) {
+  const dim3 grid((r + 63) / 64, chunks, B);
+  if (act == LOWRAM_F32)
+    hipLaunchKernelGGL(k_landmark<float>, grid, dim3(256), 0, st, (const float *)coeff, nullptr,
+                       lm, N, C, r, j0);
+  else if (coeff_dt == LOWRAM_BF16)
+    hipLaunchKernelGGL(k_landmark<bf16>, grid, dim3(256), 0, st, (const bf16 *)coeff, nullptr,
+                       lm, N, C, r, j0);
+  else
+    hipLaunchKernelGGL(k_landmark<int8_t>, grid, dim3(256), 0, st, (const int8_t *)coeff, cscale,
+                       lm, N, C, r, j0);
+}
+
+// Projection of N tokens (Nk per (l, h) block of k) into rows o0.. of a cache
+// with No rows per sequence, the reduction over D split in S slices
+// (project_splits; partial sums in part, [S][B][N][r] float64, when S > 1).
+// int8 coefficients go through c64 ([B][N][r]) and are quantised with the
+// scales in cscale.
+template <typename TA, typename TO>
+static void project_typed(const void *k, const void *basis, TO *out, double *part, int B, int N,
+                          int D, int dh, int r, int Nk, int No, int o0, int S, hipStream_t st) {
+  const int Dsl = ((D + S - 1) / S + 15) / 16 * 16;
+  const dim3 grid((r + 63) / 64, (N + 63) / 64, B * S);
+  if (S == 1) {
+    hipLaunchKernelGGL((k_project<TA, TO>), grid, dim3(256), 0, st, (const TA *)k,
+                       (const TA *)basis, out, N, D, dh, r, Nk, No, o0, 1, Dsl, 0L);
+    return;
+  }
+  const long per = (long)B * N * r;
+  hipLaunchKernelGGL((k_project<TA, double>), grid, dim3(256), 0, st, (const TA *)k,
+                     (const TA *)basis, part, N, D, dh, r, Nk, N, 0, S, Dsl, per);
+  hipLaunchKernelGGL(k_project_sum<TO>, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, st,
+                     (const double *)part, out, B, N, r, S, No, o0);
+}
+
+static void launch_project(int act, int coeff_dt, const void *k, const void *basis, void *coeff,
+                           double *c64, double *part, const uint16_t *cscale, int B, int N, int D,
+                           int dh, int r, int Nk, int No, int o0, int S, hipStream_t st) {
+  if (act == LOWRAM_F32) {
+    project_typed<float, float>(k, basis, (float *)coeff, part, B, N, D, dh, r, Nk, No, o0, S, st);
+  } else if (coeff_dt == LOWRAM_BF16) {
+    project_typed<bf16, bf16>(k, basis, (bf16 *)coeff, part, B, N, D, dh, r, Nk, No, o0, S, st);
+  } else {
+    project_typed<bf16, double>(k, basis, c64, part, B, N, D, dh, r, Nk, N, 0, S, st);
+    const long total = (long)B * N * r;
+    hipLaunchKernelGGL(k_quant, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, c64,
+                       cscale, (int8_t *)coeff, (long)N, r, total, (long)No, (long)o0);
+  }
 }
 
 hipError_t run_compress(const CompressArgs &a, hipStream_t st) {
   const int D = a.G * a.Hkv * a.dh, n_c = a.N / a.C;
-  dim3 pgrid((a.r + 63) / 64, (a.N + 63) / 64, a.B);
-  // C1 (+ Q1 for int8 coefficients)
-  if (a.act == LOWRAM_F32) {
-    hipLaunchKernelGGL((k_project<float, float>), pgrid, dim3(256), 0, st, (const float *)a.k,
-                       (const float *)a.basis, (float *)a.coeff, a.N, D, a.dh, a.r);
-  } else if (a.coeff_dt == LOWRAM_BF16) {
-    hipLaunchKernelGGL((k_project<bf16, bf16>), pgrid, dim3(256), 0, st, (const bf16 *)a.k,
-                       (const bf16 *)a.basis, (bf16 *)a.coeff, a.N, D, a.dh, a.r);
-  } else {
-    double *c64 = a.c64;
-    hipLaunchKernelGGL((k_project<bf16, double>), pgrid, dim3(256), 0, st, (const bf16 *)a.k,
-                       (const bf16 *)a.basis, c64, a.N, D, a.dh, a.r);
-    hipLaunchKernelGGL(k_colmax, dim3((a.r + 63) / 64, a.B), dim3(256), 0, st, c64,
+  // C1 (+ Q1 for int8 coefficients: scales over the N tokens first)
+  if (a.act != LOWRAM_F32 && a.coeff_dt == LOWRAM_I8) {
+    project_typed<bf16, double>(a.k, a.basis, a.c64, nullptr, a.B, a.N, D, a.dh, a.r, a.N, a.N, 0,
+                                1, st);
+    hipLaunchKernelGGL(k_colmax, dim3((a.r + 63) / 64, a.B), dim3(256), 0, st, a.c64,
                        a.coeff_scale, a.N, a.r);
     const long total = (long)a.B * a.N * a.r;
-    hipLaunchKernelGGL(k_quant, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, c64,
-                       a.coeff_scale, (int8_t *)a.coeff, (long)a.N, a.r, total);
+    hipLaunchKernelGGL(k_quant, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a.c64,
+                       a.coeff_scale, (int8_t *)a.coeff, (long)a.N, a.r, total, (long)a.N, 0L);
+  } else {
+    launch_project(a.act, a.coeff_dt, a.k, a.basis, a.coeff, nullptr, nullptr, nullptr, a.B, a.N, D,
+                   a.dh, a.r, a.N, a.N, 0, 1, st);
   }
   // C2
-  if (a.act == LOWRAM_F32)
-    hipLaunchKernelGGL(k_landmark<float>, dim3(n_c, a.B), dim3(256), 0, st, (const float *)a.coeff,
-                       nullptr, a.landmark, a.N, a.C, a.r);
-  else if (a.coeff_dt == LOWRAM_BF16)
-    hipLaunchKernelGGL(k_landmark<bf16>, dim3(n_c, a.B), dim3(256), 0, st, (const bf16 *)a.coeff,
-                       nullptr, a.landmark, a.N, a.C, a.r);
-  else
-    hipLaunchKernelGGL(k_landmark<int8_t>, dim3(n_c, a.B), dim3(256), 0, st,
-                       (const int8_t *)a.coeff, a.coeff_scale, a.landmark, a.N, a.C, a.r);
+  launch_landmark(a.act, a.coeff_dt, a.coeff, a.coeff_scale, a.landmark, a.B, a.N, a.C, a.r, 0,
+                  n_c, st);
   // C3, C4, C5
-  if (a.act == LOWRAM_F32) pred_dispatch<float, float, float>(a, st);
-  else if (a.coeff_dt == LOWRAM_BF16 && a.resid_dt == LOWRAM_BF16) pred_dispatch<bf16, bf16, bf16>(a, st);
-  else if (a.coeff_dt == LOWRAM_I8 && a.resid_dt == LOWRAM_BF16) pred_dispatch<bf16, int8_t, bf16>(a, st);
-  else if (a.coeff_dt == LOWRAM_BF16) pred_dispatch<bf16, bf16, bf16>(a, st);
-  else pred_dispatch<bf16, int8_t, bf16>(a, st);
+  PredPass p;
+  p.coeff = a.coeff; p.cscale = a.coeff_scale;
+  p.basis = a.basis; p.w1 = a.w1; p.b1 = a.b1; p.w2 = a.w2; p.b2 = a.b2; p.v = a.v;
+  p.err = a.err; p.idx = a.res_idx; p.ptr = a.res_ptr; p.val = a.res_val; p.d64 = a.d64;
+  p.B = a.B; p.G = a.G; p.Hkv = a.Hkv; p.r = a.r; p.F = a.F;
+  p.n_tok = a.N; p.C = a.C; p.n_sel = a.n_res; p.Nc = a.N; p.c0 = 0; p.Nv = a.N;
+  p.resid_i8 = a.resid_dt == LOWRAM_I8;
+  p.delta_all = 0;
+  pred_dispatch(a.act, a.coeff_dt, a.dh, p, st);
   // Q1 on residual rows
   if (a.resid_dt == LOWRAM_I8 && a.n_res > 0) {
     const int bl = a.B * a.G * a.Hkv;
@@ -470,7 +661,8 @@ hipError_t run_compress(const CompressArgs &a, hipStream_t st) {
                        a.n_res, a.dh);
     const long total = (long)bl * a.n_res * a.dh;
     hipLaunchKernelGGL(k_quant, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a.d64,
-                       a.res_scale, (int8_t *)a.res_val, (long)a.n_res, a.dh, total);
+                       a.res_scale, (int8_t *)a.res_val, (long)a.n_res, a.dh, total,
+                       (long)a.n_res, 0L);
   } else if (a.resid_dt == LOWRAM_I8) {
     const int bl = a.B * a.G * a.Hkv;
     hipLaunchKernelGGL(k_colmax, dim3((a.dh + 63) / 64, bl), dim3(256), 0, st, a.d64, a.res_scale,
@@ -505,6 +697,68 @@ hipError_t run_evict(const EvictArgs &a, hipStream_t st) {
                      (const unsigned char *)a.res_val, a.keep_out, a.d_res_ptr, a.d_res_idx,
                      (unsigned char *)a.d_res_val, n_c, a.keep, a.C, a.n_res,
                      a.dh * dtype_bytes(a.resid_dt));
+  return hipGetLastError();
+}
+
+// Batched copy of `bytes` per sequence (a multiple of 8) between arrays with
+// per-sequence strides in bytes (multiples of 8); nothing when bytes is 0.
+static void copy_rows(const void *src, long src_stride, void *dst, long dst_stride, long bytes,
+                      int B, hipStream_t st) {
+  const long words = bytes / 8;
+  if (words <= 0 || B <= 0) return;
+  hipLaunchKernelGGL(k_copy_rows, dim3((unsigned)((words + 255) / 256), B), dim3(256), 0, st,
+                     (const uint2 *)src, src_stride / 8, (uint2 *)dst, dst_stride / 8, words);
+}
+
+hipError_t run_repack(const RepackArgs &a, hipStream_t st) {
+  const int D = a.G * a.Hkv * a.dh, n_c = a.N / a.C, Nd = a.N + a.C;
+  const int bl = a.B * a.G * a.Hkv;
+  const long cb = dtype_bytes(a.coeff_dt), rb = (long)a.dh * dtype_bytes(a.resid_dt);
+  // the existing chunks: coefficient rows, landmarks, scales
+  copy_rows(a.coeff, (long)a.N * a.r * cb, a.d_coeff, (long)Nd * a.r * cb, (long)a.N * a.r * cb,
+            a.B, st);
+  copy_rows(a.landmark, (long)n_c * a.r * 4, a.d_landmark, (long)(n_c + 1) * a.r * 4,
+            (long)n_c * a.r * 4, a.B, st);
+  if (a.coeff_dt == LOWRAM_I8 && a.d_coeff_scale != a.coeff_scale)
+    copy_rows(a.coeff_scale, 0, a.d_coeff_scale, 0, (long)a.B * a.r * 2, 1, st);
+  if (a.resid_dt == LOWRAM_I8 && a.d_res_scale != a.res_scale)
+    copy_rows(a.res_scale, 0, a.d_res_scale, 0, (long)bl * a.dh * 2, 1, st);
+  // C1 on the oldest C tail tokens into rows N.. (int8: the existing scales)
+  launch_project(a.act, a.coeff_dt, a.k_tail, a.basis, a.d_coeff, a.c64, a.part, a.coeff_scale,
+                 a.B, a.C, D, a.dh, a.r, a.T, Nd, a.N, project_splits(a.B, a.C, D, a.r), st);
+  // C2 for the new chunk
+  launch_landmark(a.act, a.coeff_dt, a.d_coeff, a.coeff_scale, a.d_landmark, a.B, Nd, a.C, a.r,
+                  n_c, 1, st);
+  // C3-C5 over the new chunk: errors and delta rows of its C tokens, its top m
+  if (a.m > 0) {
+    PredPass p;
+    p.coeff = a.d_coeff; p.cscale = a.coeff_scale;
+    p.basis = a.basis; p.w1 = a.w1; p.b1 = a.b1; p.w2 = a.w2; p.b2 = a.b2; p.v = a.v_tail;
+    p.err = a.err; p.idx = a.t_idx; p.ptr = a.t_ptr; p.val = nullptr; p.d64 = a.dall;
+    p.B = a.B; p.G = a.G; p.Hkv = a.Hkv; p.r = a.r; p.F = a.F;
+    p.n_tok = a.C; p.C = a.C; p.n_sel = a.m; p.Nc = Nd; p.c0 = a.N; p.Nv = a.T;
+    p.resid_i8 = a.resid_dt == LOWRAM_I8;
+    p.delta_all = 1;
+    pred_dispatch(a.act, a.coeff_dt, a.dh, p, st);
+  }
+  // the residual CSR with one more chunk, then the new rows (Q1 on the existing scales)
+  const int n_blk = (a.n_res + a.m + REPACK_RB - 1) / REPACK_RB;
+  hipLaunchKernelGGL(k_repack_resid, dim3(n_blk > 0 ? n_blk : 1, a.G * a.Hkv, a.B), dim3(256), 0,
+                     st, a.res_ptr, a.res_idx, (const unsigned char *)a.res_val, a.t_idx,
+                     a.d_res_ptr, a.d_res_idx, (unsigned char *)a.d_res_val, n_c, a.N, a.n_res,
+                     a.m, (int)rb);
+  if (a.m > 0) {
+    const dim3 grid(a.G * a.Hkv, a.B);
+    if (a.resid_dt == LOWRAM_I8)
+      hipLaunchKernelGGL(k_repack_rows<int8_t>, grid, dim3(256), 0, st, a.res_ptr, a.t_idx, a.dall,
+                         a.res_scale, (int8_t *)a.d_res_val, n_c, a.n_res, a.m, a.C, a.dh);
+    else if (a.act == LOWRAM_F32)
+      hipLaunchKernelGGL(k_repack_rows<float>, grid, dim3(256), 0, st, a.res_ptr, a.t_idx, a.dall,
+                         nullptr, (float *)a.d_res_val, n_c, a.n_res, a.m, a.C, a.dh);
+    else
+      hipLaunchKernelGGL(k_repack_rows<bf16>, grid, dim3(256), 0, st, a.res_ptr, a.t_idx, a.dall,
+                         nullptr, (bf16 *)a.d_res_val, n_c, a.n_res, a.m, a.C, a.dh);
+  }
   return hipGetLastError();
 }
 

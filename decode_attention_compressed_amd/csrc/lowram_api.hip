@@ -135,6 +135,26 @@ EvictPlan evict_plan(const lowram_dims *d) {
   return p;
 }
 
+// Re-pack workspace: sized for m = C (the most a C-token chunk can keep).
+struct RepackPlan {
+  size_t err_off, c64_off, part_off, idx_off, ptr_off, dall_off, bytes;
+};
+
+RepackPlan repack_plan(const lowram_dims *d) {
+  RepackPlan p;
+  const size_t bl = (size_t)d->batch * d->layers * d->heads_kv, C = (size_t)d->chunk;
+  const int D = d->layers * d->heads_kv * d->head_dim;
+  const int S = project_splits(d->batch, d->chunk, D, d->rank);
+  p.err_off = 0;
+  p.c64_off = align_up(sizeof(double) * bl * C);
+  p.part_off = p.c64_off + (d->coeff == LOWRAM_I8 ? align_up(sizeof(double) * (size_t)d->batch * C * d->rank) : 0);
+  p.idx_off = p.part_off + (S > 1 ? align_up(sizeof(double) * (size_t)S * d->batch * C * d->rank) : 0);
+  p.ptr_off = p.idx_off + align_up(sizeof(int32_t) * bl * C);
+  p.dall_off = p.ptr_off + align_up(sizeof(int32_t) * bl * 2);
+  p.bytes = p.dall_off + align_up(sizeof(double) * bl * C * d->head_dim);
+  return p;
+}
+
 struct DensePlan {
   int tps, n_split, PW;
   size_t bytes;
@@ -258,6 +278,7 @@ lowram_status lowram_workspace_bytes(const lowram_dims *d, int32_t op, size_t *b
     case LOWRAM_OP_DECODE: *bytes = decode_plan(d).bytes; return LOWRAM_OK;
     case LOWRAM_OP_EVICT: *bytes = evict_plan(d).bytes; return LOWRAM_OK;
     case LOWRAM_OP_DENSE: *bytes = dense_plan(d, d->n_ctx).bytes; return LOWRAM_OK;
+    case LOWRAM_OP_REPACK: *bytes = repack_plan(d).bytes; return LOWRAM_OK;
   }
   return fail(LOWRAM_E_INVALID, "unknown op %d", op);
 }
@@ -465,6 +486,60 @@ lowram_status lowram_evict(const lowram_dims *d, const lowram_model *m, const lo
   a.r = d->rank; a.N = d->n_ctx; a.C = d->chunk; a.n_res = d->n_res;
   a.act = d->act; a.coeff_dt = d->coeff; a.resid_dt = d->resid;
   return hip_status(run_evict(a, (hipStream_t)stream), "lowram_evict");
+}
+
+lowram_status lowram_repack(const lowram_dims *d, const lowram_model *m, const lowram_cache *src,
+                            const void *k_tail, const void *v_tail, int32_t n_new_res,
+                            const lowram_cache *dst, void *ws, size_t ws_bytes, void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  if (d->n_tail < d->chunk)
+    return fail(LOWRAM_E_INVALID, "re-pack needs a full chunk in the tail (n_tail %d < chunk %d)",
+                d->n_tail, d->chunk);
+  if (n_new_res < 0 || n_new_res > d->chunk)
+    return fail(LOWRAM_E_INVALID, "n_new_res %d outside [0, chunk %d]", n_new_res, d->chunk);
+  if ((d->coeff == LOWRAM_I8 || d->resid == LOWRAM_I8) && d->n_ctx < d->chunk)
+    return fail(LOWRAM_E_INVALID, "int8 re-pack needs the scales of a compressed prefill (n_ctx >= chunk)");
+  lowram_dims d2 = *d;
+  d2.n_ctx = d->n_ctx + d->chunk;
+  d2.n_res = d->n_res + n_new_res;
+  if ((st = check_dims(&d2)) != LOWRAM_OK) return st;
+  if (!m || !src || !dst) return fail(LOWRAM_E_INVALID, "model, src and dst must not be NULL");
+  REQUIRE_PTR(k_tail); REQUIRE_PTR(v_tail);
+  REQUIRE_PTR(m->basis); REQUIRE_PTR(m->w1); REQUIRE_PTR(m->b1); REQUIRE_PTR(m->w2); REQUIRE_PTR(m->b2);
+  REQUIRE_PTR(src->res_ptr);
+  if (d->n_ctx > 0) { REQUIRE_PTR(src->coeff); REQUIRE_PTR(src->landmark); }
+  if (d->n_res > 0) { REQUIRE_PTR(src->res_idx); REQUIRE_PTR(src->res_val); }
+  REQUIRE_PTR(dst->coeff); REQUIRE_PTR(dst->landmark); REQUIRE_PTR(dst->res_ptr);
+  if (d2.n_res > 0) { REQUIRE_PTR(dst->res_idx); REQUIRE_PTR(dst->res_val); }
+  if (d->coeff == LOWRAM_I8) { REQUIRE_PTR(src->coeff_scale); REQUIRE_PTR(dst->coeff_scale); }
+  if (d->resid == LOWRAM_I8) { REQUIRE_PTR(src->res_scale); REQUIRE_PTR(dst->res_scale); }
+  if (src->coeff == dst->coeff || src->landmark == dst->landmark || src->res_ptr == dst->res_ptr ||
+      (d->n_res > 0 && (src->res_idx == dst->res_idx || src->res_val == dst->res_val)))
+    return fail(LOWRAM_E_INVALID, "src and dst must not share coefficient, landmark or residual storage");
+  const RepackPlan p = repack_plan(d);
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  RepackArgs a;
+  memset(&a, 0, sizeof a);
+  a.basis = m->basis; a.w1 = m->w1; a.b1 = m->b1; a.w2 = m->w2; a.b2 = m->b2;
+  a.k_tail = k_tail; a.v_tail = v_tail;
+  a.coeff = src->coeff; a.coeff_scale = (const uint16_t *)src->coeff_scale; a.landmark = src->landmark;
+  a.res_ptr = src->res_ptr; a.res_idx = src->res_idx; a.res_val = src->res_val;
+  a.res_scale = (const uint16_t *)src->res_scale;
+  a.d_coeff = dst->coeff; a.d_coeff_scale = (uint16_t *)dst->coeff_scale; a.d_landmark = dst->landmark;
+  a.d_res_ptr = dst->res_ptr; a.d_res_idx = dst->res_idx; a.d_res_val = dst->res_val;
+  a.d_res_scale = (uint16_t *)dst->res_scale;
+  a.err = reinterpret_cast<double *>((char *)ws + p.err_off);
+  a.c64 = reinterpret_cast<double *>((char *)ws + p.c64_off);
+  a.part = reinterpret_cast<double *>((char *)ws + p.part_off);
+  a.t_idx = reinterpret_cast<int32_t *>((char *)ws + p.idx_off);
+  a.t_ptr = reinterpret_cast<int32_t *>((char *)ws + p.ptr_off);
+  a.dall = reinterpret_cast<double *>((char *)ws + p.dall_off);
+  a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
+  a.r = d->rank; a.F = d->hidden; a.N = d->n_ctx; a.C = d->chunk; a.T = d->n_tail;
+  a.n_res = d->n_res; a.m = n_new_res;
+  a.act = d->act; a.coeff_dt = d->coeff; a.resid_dt = d->resid;
+  return hip_status(run_repack(a, (hipStream_t)stream), "lowram_repack");
 }
 
 lowram_status lowram_dense_decode_attn(const lowram_dims *d, const void *q, const void *k,

@@ -63,7 +63,8 @@ typedef enum {
   LOWRAM_OP_COMPRESS = 0,
   LOWRAM_OP_DECODE = 1,
   LOWRAM_OP_EVICT = 2,
-  LOWRAM_OP_DENSE = 3
+  LOWRAM_OP_DENSE = 3,
+  LOWRAM_OP_REPACK = 4
 } lowram_op;
 
 /* Sizes of one xKV group over a batch.  All counts are per sequence. */
@@ -197,6 +198,36 @@ lowram_status lowram_evict(const lowram_dims *dims, const lowram_model *model,
                            const lowram_cache *src, const void *obs_q, int32_t n_obs,
                            int32_t keep_chunks, const lowram_cache *dst, int32_t *keep_out,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Tail growth: move the oldest `chunk` tokens of the uncompressed tail into
+ * the compressed cache as one new chunk.  The rit.work page (generation
+ * section) keeps post-prefill tokens uncompressed and leaves open what happens
+ * as that tail grows; the reading implemented here compresses each full chunk
+ * of it the way the prefill was compressed (zicq.com "Core Mechanism" and
+ * "Cross-Layer Low-Rank Key Compression"), against the existing basis,
+ * predictor and int8 scales:
+ *   c_t = U^T k_t^cat for tail tokens t = 0..C-1, stored rounded to coeff
+ *   dtype (I8: q = clamp(rne(c/s), +-127) with src's coeff_scale, unchanged);
+ *   landmark_{n_c} = mean of deq(c_t), float64 rounded to float32;
+ *   per (layer, head): e_t = ||v_t - f(U_{l,h} deq(c_t))||^2 in float64 and
+ *   the n_new_res tokens with the largest e (lowest index wins ties) keep
+ *   delta = v - v_hat rounded to resid dtype (I8: src's res_scale, unchanged);
+ *   the residual sets of the existing chunks are kept as they are.
+ * dims describe src: n_ctx = N (may be 0 for float caches; >= chunk for
+ * int8), n_res = src's residual capacity, n_tail = T >= chunk.  k_tail,
+ * v_tail: [B][G][Hkv][T][dh] act dtype, tokens [0, chunk) are packed (the
+ * caller then drops them from its tail).  dst: a cache for n_ctx' = N + chunk
+ * and capacity n_res' = n_res + n_new_res, 0 <= n_new_res <= chunk: coeff
+ * rows 0..N-1 and landmarks 0..n_c-1 are copied from src; dst res_ptr has
+ * n_c + 2 entries, equal to src's for j <= n_c, and the new rows (tokens
+ * N + t, ascending) follow src's res_ptr[n_c] live rows; the rest of the
+ * capacity is zeroed.  Scales: dst coeff_scale / res_scale receive src's (they
+ * may alias src's).  src and dst must not share any other storage.
+ * Workspace: LOWRAM_OP_REPACK. */
+lowram_status lowram_repack(const lowram_dims *dims, const lowram_model *model,
+                            const lowram_cache *src, const void *k_tail, const void *v_tail,
+                            int32_t n_new_res, const lowram_cache *dst, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /* Uncompressed decode attention, the comparator for the compressed path:
  * out[b][g] = softmax(k_b,h q_g / sqrt(d_h)) v_b,h over n_tokens tokens

@@ -53,7 +53,7 @@ def test_llama_ratio_and_composed_ratio():
 @pytest.mark.parametrize("s", ALL, ids=lambda s: s.name)
 def test_workspace_sizes_are_positive_and_aligned(s):
     d = dims_of(s)
-    for op in (L.OP_COMPRESS, L.OP_DECODE, L.OP_EVICT, L.OP_DENSE):
+    for op in (L.OP_COMPRESS, L.OP_DECODE, L.OP_EVICT, L.OP_DENSE, L.OP_REPACK):
         n = P.workspace_bytes(d, op)
         assert n > 0 and n % 256 == 0
 
@@ -139,6 +139,36 @@ def test_compress_and_evict_argument_errors():
     assert ev(n_c + 1) == L.E_INVALID
     assert ev(2, n_obs=-1) == L.E_INVALID
     assert ev(2, dst_=c) == L.E_INVALID        # in-place eviction is refused
+
+
+def test_repack_argument_errors():
+    lib = L.lib()
+    d = P.with_(base_dims(), n_tail=base_dims().chunk + 3)
+    m = L.Model(FAKE, FAKE, FAKE, FAKE, FAKE)
+    src = L.Cache(FAKE, None, FAKE, FAKE, FAKE, FAKE, None)
+    dst = L.Cache(FAKE * 2, None, FAKE * 2, FAKE * 2, FAKE * 2, FAKE * 2, None)
+    need = P.workspace_bytes(d, L.OP_REPACK)
+
+    def rp(d_=d, n_new=2, dst_=dst, k=FAKE, ws=FAKE, have=need, src_=src):
+        return lib.lowram_repack(ctypes.byref(d_), ctypes.byref(m), ctypes.byref(src_), k, FAKE, n_new,
+                                 ctypes.byref(dst_), ws, have, None)
+
+    assert rp(n_new=-1) == L.E_INVALID
+    assert rp(n_new=d.chunk + 1) == L.E_INVALID             # more rows than the chunk has
+    assert rp(d_=P.with_(d, n_tail=d.chunk - 1)) == L.E_INVALID  # no full chunk in the tail
+    assert rp(k=None) == L.E_INVALID
+    assert rp(k=FAKE + 8) == L.E_INVALID                     # k_tail not 16-byte aligned
+    assert rp(have=need - 1) == L.E_WORKSPACE
+    assert rp(ws=FAKE + 64) == L.E_INVALID
+    for shared in range(4):                                  # dst sharing src storage
+        fields = [FAKE * 2, None, FAKE * 2, FAKE * 2, FAKE * 2, FAKE * 2, None]
+        fields[(0, 2, 3, 5)[shared]] = FAKE
+        assert rp(dst_=L.Cache(*fields)) == L.E_INVALID
+    i8 = P.with_(d, coeff=L.I8)
+    assert rp(d_=i8) == L.E_INVALID                          # int8 without coefficient scales
+    assert rp(d_=P.with_(i8, n_ctx=0, n_res=0)) == L.E_INVALID  # int8 needs a prefill's scales
+    full = P.with_(d, n_ctx=(1 << 22), n_res=0)               # the grown cache would exceed n_ctx limits
+    assert rp(d_=full) != L.OK
 
 
 def test_dense_argument_errors():
