@@ -26,7 +26,8 @@ the chunk's mean coefficient; predictor input = reconstructed key; squared L2
 error per (layer, head); lowest index wins ties; symmetric per-channel int8
 with fp16 scales; eviction by the group-summed score of observation queries;
 tail growth by re-packing the oldest C tail tokens as a new chunk against the
-existing basis, predictor and int8 scales).
+existing basis, predictor and int8 scales; test-time fitting of the predictor
+as full-batch gradient descent on the mean squared value error).
 
 Stored tensors are passed as numpy arrays in their storage dtype: float64,
 float32, float16, int8, or uint16 holding bfloat16 bit patterns.
@@ -548,6 +549,79 @@ def repack(cache: dict, model: dict, k_new: np.ndarray, v_new: np.ndarray, s, m:
     new["res_ptr"], new["res_idx"], new["res_val"] = ptr, idx, val
     new["repack_errors"] = errors
     return new
+
+
+# ============================================================================
+# test-time fitting of the value predictor
+# ============================================================================
+def predictor_loss_grad(khat: np.ndarray, v: np.ndarray, w1, b1, w2, b2):
+    """L = (1/N) sum_t ||v_t - f(k_hat_t)||^2 over the N tokens of one head and
+    its gradient with respect to (W1, b1, W2, b2), by the chain rule (fp64).
+
+    With a = W1 k + b1, SiLU(a) = a s(a), s the logistic function, the
+    derivative is SiLU'(a) = s(a) (1 + a (1 - s(a))).
+    """
+    N = khat.shape[0]
+    a = khat @ w1.T + b1
+    sg = 1.0 / (1.0 + np.exp(-a))
+    hid = a * sg
+    r = hid @ w2.T + b2 - v
+    loss = float(np.sum(r * r)) / N
+    gv = (2.0 / N) * r                       # dL / d v_hat
+    gw2 = gv.T @ hid
+    gb2 = gv.sum(axis=0)
+    ga = (gv @ w2) * (sg * (1.0 + a * (1.0 - sg)))
+    gw1 = ga.T @ khat
+    gb1 = ga.sum(axis=0)
+    return loss, (gw1, gb1, gw2, gb2)
+
+
+def fit_predictor(inp: dict, s, steps: int, lr: float, init: dict | None = None) -> dict:
+    """Fit each head's value predictor to its context at test time.
+
+    The abstract fits a lightweight per-head predictor at test time, either
+    from scratch or from a meta-learned initialisation that needs fewer
+    steps; the rit.work page (values section) trains it during prefill on the
+    context's keys to reproduce their values.  Reading taken here: `steps`
+    steps of full-batch gradient descent with step size `lr` on the mean
+    squared value error L above, per (b, l, h), starting from `init`'s
+    weights (default: the ones in inp), with the reconstructed keys
+    k_hat = U_{l,h} deq(c~) as inputs -- the keys the predictor sees at decode
+    -- where c~ are the coefficients compress stores (same rounding; int8
+    scales over the N tokens).  The weights are kept in float64 across the
+    steps and rounded to the act dtype once at the end.
+    Returns {"w1", "b1", "w2", "b2"} (stored act dtype) and "loss"
+    [B][G][Hkv][steps + 1]: L before each step and after the last one.
+    """
+    B, G, Hkv, dh, N = s.B, s.G, s.Hkv, s.dh, s.N
+    act, cdt = s.act, s.coeff
+    init = inp if init is None else init
+    U_all = decode(inp["basis"], act)
+    out = {n: np.empty_like(np.asarray(init[n])) for n in ("w1", "b1", "w2", "b2")}
+    loss = np.zeros((B, G, Hkv, steps + 1))
+    for b in range(B):
+        U = U_all[b]
+        k = decode(inp["k"][b], act)
+        v = decode(inp["v"][b], act)
+        c = project(k.transpose(2, 0, 1, 3).reshape(N, -1), U)
+        if cdt == I8:
+            cq, cs = quantise(c, axis=0)
+            cdeq = dequantise(cq, cs, axis=0)
+        else:
+            cdeq = decode(round_to(c, cdt), cdt)
+        for l in range(G):
+            for h in range(Hkv):
+                khat = cdeq @ basis_slice(U, l, h, Hkv, dh).T
+                w = [decode(init[n][b, l, h], act) for n in ("w1", "b1", "w2", "b2")]
+                for st in range(steps + 1):
+                    L, grads = predictor_loss_grad(khat, v[l, h], *w)
+                    loss[b, l, h, st] = L
+                    if st < steps:
+                        w = [wi - lr * gi for wi, gi in zip(w, grads)]
+                for n, wi in zip(("w1", "b1", "w2", "b2"), w):
+                    out[n][b, l, h] = round_to(wi, act)
+    out["loss"] = loss
+    return out
 
 
 # ============================================================================

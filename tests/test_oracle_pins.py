@@ -606,3 +606,87 @@ def test_repack_int8_keeps_scales_and_reproduces_prefill_codes():
                 assert np.all((dq == 127 * np.sign(d))[~ok])
                 n_in += int(ok.sum()); n_out += int((~ok).sum())
     assert n_in > 0 and n_out > 0  # both the rounding and the clamp are exercised
+
+
+# ---------------------------------------------------------------------------
+# test-time fitting of the value predictor
+# ---------------------------------------------------------------------------
+def _mlp_case(seed=11, N=40, dh=8, F=16):
+    rng = np.random.default_rng(seed)
+    khat = rng.standard_normal((N, dh))
+    v = rng.standard_normal((N, dh))
+    w = [rng.standard_normal((F, dh)) / np.sqrt(dh), 0.1 * rng.standard_normal(F),
+         rng.standard_normal((dh, F)) / np.sqrt(F), 0.1 * rng.standard_normal(dh)]
+    return khat, v, w
+
+
+def test_predictor_gradient_matches_torch_autograd():
+    khat, v, w = _mlp_case()
+    loss, grads = O.predictor_loss_grad(khat, v, *w)
+    wt = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in w]
+    kt, vt = torch.from_numpy(khat), torch.from_numpy(v)
+    pred = torch.nn.functional.silu(kt @ wt[0].T + wt[1]) @ wt[2].T + wt[3]
+    lt = ((pred - vt) ** 2).sum(dim=1).mean()
+    lt.backward()
+    assert loss == pytest.approx(lt.item(), rel=1e-13)
+    for g, x in zip(grads, wt):
+        assert np.allclose(g, x.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+def test_predictor_gradient_matches_finite_differences():
+    khat, v, w = _mlp_case(seed=12)
+    _, grads = O.predictor_loss_grad(khat, v, *w)
+    rng = np.random.default_rng(3)
+    eps = 1e-6
+    for i in range(4):
+        d = rng.standard_normal(w[i].shape)
+        wp = [x.copy() for x in w]
+        wm = [x.copy() for x in w]
+        wp[i] = wp[i] + eps * d
+        wm[i] = wm[i] - eps * d
+        fd = (O.predictor_loss_grad(khat, v, *wp)[0] - O.predictor_loss_grad(khat, v, *wm)[0]) / (2 * eps)
+        assert fd == pytest.approx(float(np.sum(grads[i] * d)), rel=1e-7, abs=1e-10)
+
+
+def test_fit_zero_steps_keeps_weights_and_reports_the_error():
+    s = tiny64(B=2)
+    inp = gen.make(s)
+    fit = O.fit_predictor(inp, s, steps=0, lr=0.1)
+    cache = O.compress(inp, s)
+    for n in ("w1", "b1", "w2", "b2"):
+        assert np.array_equal(fit[n], inp[n])
+    # loss = mean over tokens of the compress-side squared errors
+    assert np.allclose(fit["loss"][..., 0], cache["errors"].mean(axis=-1), rtol=1e-12)
+
+
+def test_fit_stationary_at_an_exact_predictor():
+    s = tiny64(r=32)  # r = D: k_hat = k
+    inp = gen.make(s, noise_scale=0.0)
+    fit = O.fit_predictor(inp, s, steps=3, lr=0.5)
+    assert np.max(fit["loss"]) < 1e-24
+    for n in ("w1", "b1", "w2", "b2"):
+        assert np.max(np.abs(fit[n] - inp[n])) < 1e-12
+
+
+def test_fit_descends_and_equals_explicit_gradient_steps():
+    s = tiny64(B=1, G=1, Hkv=1, Hq=2)
+    inp = gen.make(s)
+    lr, steps = 0.05, 6
+    fit = O.fit_predictor(inp, s, steps=steps, lr=lr)
+    L = fit["loss"][0, 0, 0]
+    assert np.all(np.diff(L) < 0), L
+    # the same steps written out with torch autograd from the oracle's k_hat
+    U = O.decode(inp["basis"][0], s.act)
+    kcat = kcat_of(inp, s, 0)
+    khat = torch.from_numpy(np.einsum("tr,dr->td", np.einsum("td,dr->tr", kcat, U), U[:s.dh]))
+    v = torch.from_numpy(O.decode(inp["v"][0, 0, 0], s.act))
+    wt = [torch.from_numpy(O.decode(inp[n][0, 0, 0], s.act)).clone() for n in ("w1", "b1", "w2", "b2")]
+    for st in range(steps):
+        for x in wt:
+            x.requires_grad_(True)
+        lt = ((torch.nn.functional.silu(khat @ wt[0].T + wt[1]) @ wt[2].T + wt[3] - v) ** 2).sum(1).mean()
+        assert lt.item() == pytest.approx(L[st], rel=1e-11)
+        gs = torch.autograd.grad(lt, wt)
+        wt = [(x - lr * g).detach() for x, g in zip(wt, gs)]
+    for n, x in zip(("w1", "b1", "w2", "b2"), wt):
+        assert np.allclose(fit[n][0, 0, 0], x.numpy(), rtol=1e-10, atol=1e-13)
