@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic_llama8b_32k.json")
 ATTEND_SRC = os.path.join(ROOT, "decode_attention_compressed_amd", "csrc", "k_attend_chain.hip")
 
@@ -47,6 +48,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches (for counter runs)")
+    ap.add_argument("--no-fit", action="store_true", help="skip timing the predictor fit")
+    ap.add_argument("--fit-steps", type=int, default=4)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times: a kernel of known "
                          "traffic that scales hardware byte counters")
@@ -150,6 +153,33 @@ def time_repack(P, s, d, model, cache, dev, ev, reps=5):
             "how": f"{reps} eager calls between HIP events; once per C decode steps"}
 
 
+def time_fit(P, s, d, model, dev, ev, steps=4, lr=0.01):
+    """Time lowram_fit_predictor (gradient descent on the prefill, once per
+    context) into side buffers; the benchmarked predictor is left as it is."""
+    import torch
+    Z = s.B * s.G * s.Hkv
+    flops = Z * (steps * 10 * s.N * s.F * s.dh + 4 * s.N * s.F * s.dh + 2 * s.N * s.r * s.dh)
+    ws = P.workspace(d, P._lib.OP_FIT)
+    out, loss = P.fit_predictor(d, model, dev["k"], dev["v"], 0, lr, ws=ws)  # warm-up
+    torch.cuda.synchronize()
+    ev[0].record()
+    out, loss = P.fit_predictor(d, model, dev["k"], dev["v"], steps, lr, out=out, ws=ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    L = loss.cpu().numpy()
+    tf = flops / (ms * 1e-3) / 1e12
+    ws_gb = ws.numel() / 1e9
+    del ws, out
+    torch.cuda.empty_cache()
+    log(f"fit {steps} steps in {ms:.1f} ms ({tf:.1f} TFLOP/s fp32), loss {L[..., 0].mean():.4f} -> {L[..., -1].mean():.4f}")
+    return {"steps": steps, "lr": lr, "ms": round(ms, 2), "algorithmic_flops": int(flops),
+            "tflops": round(tf, 2), "bound": "alu", "peak_tflops": FP32_PEAK_TFLOPS,
+            "frac": round(tf / FP32_PEAK_TFLOPS, 4), "workspace_gb": round(ws_gb, 2),
+            "loss_first_mean": round(float(L[..., 0].mean()), 5), "loss_last_mean": round(float(L[..., -1].mean()), 5),
+            "how": "one call between HIP events after a zero-step warm-up; float32 products on the vector ALUs"}
+
+
 def cpu_baseline(s, host, inp, budget_s):
     from oracle import lowram_oracle as O
     try:
@@ -218,6 +248,7 @@ def main():
         torch.cuda.synchronize()
     comp_bytes, dense_bytes = P.cache_bytes(dims_of(s))
     repack = time_repack(P, s, d, model, cache, dev, ev)
+    fit = None if args.no_fit else time_fit(P, s, dims_of(s), model, dev, ev, steps=args.fit_steps)
 
     # per (query set, layer) pre-marshalled calls
     kk = P.k_eff(d)
@@ -393,6 +424,7 @@ def main():
         "selected_chunk_union_per_seq": round(float(union), 1),
         "compress_ms": round(compress_ms, 2),
         "repack": repack,
+        "fit": fit,
         "step_time_distribution": step_dist,
         "graph": graph is not None,
         "device": dev_name,

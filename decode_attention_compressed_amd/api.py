@@ -253,6 +253,31 @@ def repack(d: L.Dims, model: dict, src: dict, k_tail, v_tail, n_new_res: int, ds
     return dst, d2
 
 
+def fit_predictor(d: L.Dims, model: dict, k, v, steps: int, lr: float, out=None, with_loss=True,
+                  ws=None, stream=None):
+    """Fit the value predictor by gradient descent on the context (k, v).
+    Returns (weights dict with w1, b1, w2, b2 in act dtype, loss [B][G][Hkv][steps+1]
+    float64 or None).  out may be the model dict itself (in-place update)."""
+    dt = TORCH_DT[d.act]
+    dev = k.device
+    shapes = model_shapes(d)
+    if out is None:
+        out = {n: torch.empty(shapes[n], dtype=dt, device=dev) for n in ("w1", "b1", "w2", "b2")}
+    loss = (torch.empty((d.batch, d.layers, d.heads_kv, steps + 1), dtype=torch.float64, device=dev)
+            if with_loss else None)
+    pr = L.Predictor()
+    for n in ("w1", "b1", "w2", "b2"):
+        setattr(pr, n, _ptr(out[n], dt, shapes[n], n).value)
+    ws = workspace(d, L.OP_FIT, dev) if ws is None else ws
+    kv_shape = (d.batch, d.layers, d.heads_kv, d.n_ctx, d.head_dim)
+    L.check(L.lib().lowram_fit_predictor(ctypes.byref(d), ctypes.byref(model_struct(d, model)),
+                                         _ptr(k, dt, kv_shape, "k"), _ptr(v, dt, kv_shape, "v"),
+                                         int(steps), float(lr), ctypes.byref(pr),
+                                         _ptr(loss, torch.float64, None, "loss"), _ptr(ws, torch.uint8),
+                                         ws.numel(), _stream(stream)))
+    return out, loss
+
+
 def dense_workspace(d: L.Dims, n_tokens: int, device="cuda") -> torch.Tensor:
     return workspace(with_(d, n_ctx=n_tokens), L.OP_DENSE, device)
 

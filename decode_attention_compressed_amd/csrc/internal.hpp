@@ -80,6 +80,21 @@ struct CompressArgs {
   int B, G, Hq, Hkv, dh, r, F, N, C, n_res, act, coeff_dt, resid_dt;
 };
 hipError_t run_compress(const CompressArgs &a, hipStream_t st);
+void compress_coefficients(const CompressArgs &a, hipStream_t st);  // C1 (+ Q1) only
+
+struct FitArgs {
+  const void *basis, *w1, *b1, *w2, *b2;  // initial weights (act)
+  const void *k, *v;                       // [B][G][Hkv][N][dh] act
+  void *o_w1, *o_b1, *o_w2, *o_b2;         // fitted weights (act); may alias the initial ones
+  double *loss;                            // [B][G][Hkv][steps + 1] or null
+  void *coeff; uint16_t *coeff_scale; double *c64;  // workspace: stored coefficients
+  float *khat, *apre, *hid, *res;          // workspace: [z][N][dh], [z][N][F], [z][N][F], [z][N][dh]
+  float *m_w1, *m_b1, *m_w2, *m_b2;        // workspace: float32 master weights
+  double *part;                            // workspace: [z][64][max(F, dh)] partial sums
+  int B, G, Hkv, dh, r, F, N, steps, act, coeff_dt;
+  float lr;
+};
+hipError_t run_fit(const FitArgs &a, hipStream_t st);
 
 struct EvictArgs {
   const void *basis;

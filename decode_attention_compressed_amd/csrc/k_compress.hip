@@ -626,9 +626,10 @@ static void launch_project(int act, int coeff_dt, const void *k, const void *bas
   }
 }
 
-hipError_t run_compress(const CompressArgs &a, hipStream_t st) {
-  const int D = a.G * a.Hkv * a.dh, n_c = a.N / a.C;
-  // C1 (+ Q1 for int8 coefficients: scales over the N tokens first)
+// C1 (+ Q1 for int8 coefficients: scales over the N tokens first) into
+// a.coeff / a.coeff_scale; a.c64 is the int8 staging buffer.
+void compress_coefficients(const CompressArgs &a, hipStream_t st) {
+  const int D = a.G * a.Hkv * a.dh;
   if (a.act != LOWRAM_F32 && a.coeff_dt == LOWRAM_I8) {
     project_typed<bf16, double>(a.k, a.basis, a.c64, nullptr, a.B, a.N, D, a.dh, a.r, a.N, a.N, 0,
                                 1, st);
@@ -641,6 +642,11 @@ hipError_t run_compress(const CompressArgs &a, hipStream_t st) {
     launch_project(a.act, a.coeff_dt, a.k, a.basis, a.coeff, nullptr, nullptr, nullptr, a.B, a.N, D,
                    a.dh, a.r, a.N, a.N, 0, 1, st);
   }
+}
+
+hipError_t run_compress(const CompressArgs &a, hipStream_t st) {
+  const int n_c = a.N / a.C;
+  compress_coefficients(a, st);
   // C2
   launch_landmark(a.act, a.coeff_dt, a.coeff, a.coeff_scale, a.landmark, a.B, a.N, a.C, a.r, 0,
                   n_c, st);

@@ -155,6 +155,31 @@ RepackPlan repack_plan(const lowram_dims *d) {
   return p;
 }
 
+// Predictor-fit workspace: the stored coefficients (+ int8 staging), float32
+// k_hat, pre-activations (later their gradient), hidden activations,
+// residuals, and the float32 master weights.
+struct FitPlan {
+  size_t coeff_off, cscale_off, c64_off, khat_off, apre_off, hid_off, res_off, master_off, part_off, bytes;
+};
+
+FitPlan fit_plan(const lowram_dims *d) {
+  FitPlan p;
+  const size_t B = d->batch, N = d->n_ctx, r = d->rank, F = d->hidden, dh = d->head_dim;
+  const size_t Z = B * d->layers * d->heads_kv;
+  const size_t cb = d->coeff == LOWRAM_I8 ? 1 : (d->coeff == LOWRAM_F32 ? 4 : 2);
+  p.coeff_off = 0;
+  p.cscale_off = align_up(B * N * r * cb);
+  p.c64_off = p.cscale_off + align_up(B * r * 2);
+  p.khat_off = p.c64_off + (d->coeff == LOWRAM_I8 ? align_up(sizeof(double) * B * N * r) : 0);
+  p.apre_off = p.khat_off + align_up(4 * Z * N * dh);
+  p.hid_off = p.apre_off + align_up(4 * Z * N * F);
+  p.res_off = p.hid_off + align_up(4 * Z * N * F);
+  p.master_off = p.res_off + align_up(4 * Z * N * dh);
+  p.part_off = p.master_off + align_up(4 * Z * (2 * F * dh + F + dh));
+  p.bytes = p.part_off + align_up(sizeof(double) * Z * 64 * (F > dh ? F : dh));
+  return p;
+}
+
 struct DensePlan {
   int tps, n_split, PW;
   size_t bytes;
@@ -279,6 +304,7 @@ lowram_status lowram_workspace_bytes(const lowram_dims *d, int32_t op, size_t *b
     case LOWRAM_OP_EVICT: *bytes = evict_plan(d).bytes; return LOWRAM_OK;
     case LOWRAM_OP_DENSE: *bytes = dense_plan(d, d->n_ctx).bytes; return LOWRAM_OK;
     case LOWRAM_OP_REPACK: *bytes = repack_plan(d).bytes; return LOWRAM_OK;
+    case LOWRAM_OP_FIT: *bytes = fit_plan(d).bytes; return LOWRAM_OK;
   }
   return fail(LOWRAM_E_INVALID, "unknown op %d", op);
 }
@@ -540,6 +566,48 @@ lowram_status lowram_repack(const lowram_dims *d, const lowram_model *m, const l
   a.n_res = d->n_res; a.m = n_new_res;
   a.act = d->act; a.coeff_dt = d->coeff; a.resid_dt = d->resid;
   return hip_status(run_repack(a, (hipStream_t)stream), "lowram_repack");
+}
+
+lowram_status lowram_fit_predictor(const lowram_dims *d, const lowram_model *m, const void *k,
+                                   const void *v, int32_t steps, float lr,
+                                   const lowram_predictor *out, double *loss, void *ws,
+                                   size_t ws_bytes, void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  if (d->n_ctx < d->chunk) return fail(LOWRAM_E_INVALID, "fitting needs at least one chunk of tokens");
+  if (steps < 0 || steps > 100000) return fail(LOWRAM_E_INVALID, "steps %d outside [0, 100000]", steps);
+  if (!(lr >= 0.f) || lr > 1e6f) return fail(LOWRAM_E_INVALID, "lr must be a finite value >= 0");
+  if (!m || !out) return fail(LOWRAM_E_INVALID, "model and out must not be NULL");
+  REQUIRE_PTR(k); REQUIRE_PTR(v);
+  REQUIRE_PTR(m->basis); REQUIRE_PTR(m->w1); REQUIRE_PTR(m->b1); REQUIRE_PTR(m->w2); REQUIRE_PTR(m->b2);
+  REQUIRE_PTR(out->w1); REQUIRE_PTR(out->b1); REQUIRE_PTR(out->w2); REQUIRE_PTR(out->b2);
+  OPTIONAL_PTR(loss);
+  const FitPlan p = fit_plan(d);
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  const size_t Z = (size_t)d->batch * d->layers * d->heads_kv, F = d->hidden, dh = d->head_dim;
+  char *w = (char *)ws;
+  FitArgs a;
+  memset(&a, 0, sizeof a);
+  a.basis = m->basis; a.w1 = m->w1; a.b1 = m->b1; a.w2 = m->w2; a.b2 = m->b2;
+  a.k = k; a.v = v;
+  a.o_w1 = out->w1; a.o_b1 = out->b1; a.o_w2 = out->w2; a.o_b2 = out->b2;
+  a.loss = loss;
+  a.coeff = w + p.coeff_off;
+  a.coeff_scale = reinterpret_cast<uint16_t *>(w + p.cscale_off);
+  a.c64 = reinterpret_cast<double *>(w + p.c64_off);
+  a.khat = reinterpret_cast<float *>(w + p.khat_off);
+  a.apre = reinterpret_cast<float *>(w + p.apre_off);
+  a.hid = reinterpret_cast<float *>(w + p.hid_off);
+  a.res = reinterpret_cast<float *>(w + p.res_off);
+  a.m_w1 = reinterpret_cast<float *>(w + p.master_off);
+  a.m_b1 = a.m_w1 + Z * F * dh;
+  a.m_w2 = a.m_b1 + Z * F;
+  a.m_b2 = a.m_w2 + Z * dh * F;
+  a.part = reinterpret_cast<double *>(w + p.part_off);
+  a.B = d->batch; a.G = d->layers; a.Hkv = d->heads_kv; a.dh = d->head_dim; a.r = d->rank;
+  a.F = d->hidden; a.N = d->n_ctx; a.steps = steps; a.act = d->act; a.coeff_dt = d->coeff;
+  a.lr = lr;
+  return hip_status(run_fit(a, (hipStream_t)stream), "lowram_fit_predictor");
 }
 
 lowram_status lowram_dense_decode_attn(const lowram_dims *d, const void *q, const void *k,

@@ -64,7 +64,8 @@ typedef enum {
   LOWRAM_OP_DECODE = 1,
   LOWRAM_OP_EVICT = 2,
   LOWRAM_OP_DENSE = 3,
-  LOWRAM_OP_REPACK = 4
+  LOWRAM_OP_REPACK = 4,
+  LOWRAM_OP_FIT = 5
 } lowram_op;
 
 /* Sizes of one xKV group over a batch.  All counts are per sequence. */
@@ -106,6 +107,15 @@ typedef struct {
   void *res_val;      /* [B][G][Hkv][n_res][dh] resid dtype: delta = v - v_hat              */
   void *res_scale;    /* [B][G][Hkv][dh] float16 when resid is I8, else NULL                */
 } lowram_cache;
+
+/* Predictor weights written by lowram_fit_predictor (act dtype, shapes as in
+ * lowram_model). */
+typedef struct {
+  void *w1;           /* [B][G][Hkv][F][dh] */
+  void *b1;           /* [B][G][Hkv][F]     */
+  void *w2;           /* [B][G][Hkv][dh][F] */
+  void *b2;           /* [B][G][Hkv][dh]    */
+} lowram_predictor;
 
 /* Workspace bytes `op` needs for these dims (host only, enqueues nothing). */
 lowram_status lowram_workspace_bytes(const lowram_dims *dims, int32_t op, size_t *bytes);
@@ -228,6 +238,27 @@ lowram_status lowram_repack(const lowram_dims *dims, const lowram_model *model,
                             const lowram_cache *src, const void *k_tail, const void *v_tail,
                             int32_t n_new_res, const lowram_cache *dst, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/* Test-time fitting of the value predictor (abstract: a lightweight per-head
+ * predictor fitted at test time, from scratch or from a meta-learned start
+ * that needs fewer steps; rit.work values section: trained during prefill on
+ * the context's keys).  Reading implemented: `steps` steps of full-batch
+ * gradient descent with step size lr on
+ *   L = (1/N) sum_t ||v_t - f(k_hat_t)||^2,  f(k) = W2 SiLU(W1 k + b1) + b2,
+ * per (sequence, layer, kv head), starting from model's weights, with
+ * k_hat = U_{l,h} deq(c~) from the coefficients lowram_compress would store
+ * for these keys (same rounding; int8 scales over the N tokens).  Gradients
+ * and master weights are float32 (sums over tokens in a fixed order); the
+ * weights are rounded to act dtype once, into out (which may alias model's
+ * weight arrays).  k, v: [B][G][Hkv][N][dh] act dtype.  loss: optional
+ * [B][G][Hkv][steps + 1] float64, L before each step and after the last.
+ * Call it before lowram_compress, which then uses the fitted weights.
+ * Workspace: LOWRAM_OP_FIT (float32 activations of all N tokens:
+ * about 4 B (G Hkv N (2 F + 2 dh)) bytes). */
+lowram_status lowram_fit_predictor(const lowram_dims *dims, const lowram_model *model,
+                                   const void *k, const void *v, int32_t steps, float lr,
+                                   const lowram_predictor *out, double *loss, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /* Uncompressed decode attention, the comparator for the compressed path:
  * out[b][g] = softmax(k_b,h q_g / sqrt(d_h)) v_b,h over n_tokens tokens

@@ -53,7 +53,7 @@ def test_llama_ratio_and_composed_ratio():
 @pytest.mark.parametrize("s", ALL, ids=lambda s: s.name)
 def test_workspace_sizes_are_positive_and_aligned(s):
     d = dims_of(s)
-    for op in (L.OP_COMPRESS, L.OP_DECODE, L.OP_EVICT, L.OP_DENSE, L.OP_REPACK):
+    for op in (L.OP_COMPRESS, L.OP_DECODE, L.OP_EVICT, L.OP_DENSE, L.OP_REPACK, L.OP_FIT):
         n = P.workspace_bytes(d, op)
         assert n > 0 and n % 256 == 0
 
@@ -169,6 +169,32 @@ def test_repack_argument_errors():
     assert rp(d_=P.with_(i8, n_ctx=0, n_res=0)) == L.E_INVALID  # int8 needs a prefill's scales
     full = P.with_(d, n_ctx=(1 << 22), n_res=0)               # the grown cache would exceed n_ctx limits
     assert rp(d_=full) != L.OK
+
+
+def test_fit_argument_errors():
+    lib = L.lib()
+    d = base_dims()
+    m = L.Model(FAKE, FAKE, FAKE, FAKE, FAKE)
+    out = L.Predictor(FAKE, FAKE, FAKE, FAKE)
+    need = P.workspace_bytes(d, L.OP_FIT)
+
+    def fit(d_=d, steps=2, lr=0.1, out_=out, k=FAKE, have=need, loss=None):
+        return lib.lowram_fit_predictor(ctypes.byref(d_), ctypes.byref(m), k, FAKE, steps, lr,
+                                        ctypes.byref(out_) if out_ is not None else None, loss, FAKE,
+                                        have, None)
+
+    assert fit(steps=-1) == L.E_INVALID
+    assert fit(lr=-0.5) == L.E_INVALID
+    assert fit(lr=float("nan")) == L.E_INVALID
+    assert fit(out_=None) == L.E_INVALID
+    assert fit(out_=L.Predictor(FAKE, None, FAKE, FAKE)) == L.E_INVALID
+    assert fit(k=None) == L.E_INVALID
+    assert fit(loss=FAKE + 4) == L.E_INVALID                  # loss not 16-byte aligned
+    assert fit(have=need - 1) == L.E_WORKSPACE
+    assert fit(d_=P.with_(d, n_ctx=0, n_res=0)) == L.E_INVALID  # no tokens to fit on
+    # the workspace holds float32 activations of every token
+    Z = d.batch * d.layers * d.heads_kv
+    assert need >= 4 * Z * d.n_ctx * (2 * d.hidden + 2 * d.head_dim)
 
 
 def test_dense_argument_errors():
