@@ -27,7 +27,8 @@ error per (layer, head); lowest index wins ties; symmetric per-channel int8
 with fp16 scales; eviction by the group-summed score of observation queries;
 tail growth by re-packing the oldest C tail tokens as a new chunk against the
 existing basis, predictor and int8 scales; test-time fitting of the predictor
-as full-batch gradient descent on the mean squared value error).
+as full-batch gradient descent on the mean squared value error; the key basis
+as the leading eigenvectors of the group's key Gram matrix).
 
 Stored tensors are passed as numpy arrays in their storage dtype: float64,
 float32, float16, int8, or uint16 holding bfloat16 bit patterns.
@@ -549,6 +550,50 @@ def repack(cache: dict, model: dict, k_new: np.ndarray, v_new: np.ndarray, s, m:
     new["res_ptr"], new["res_idx"], new["res_val"] = ptr, idx, val
     new["repack_errors"] = errors
     return new
+
+
+# ============================================================================
+# the group key basis at prefill
+# ============================================================================
+def key_basis(inp: dict, s, N: int | None = None):
+    """Principal directions of a group's keys (float64).
+
+    xKV finds a few principal directions of the keys and shares the basis
+    across adjacent layers (rit.work page, keys section; zicq.com English
+    summary, "Cross-Layer Low-Rank Key Compression").  Reading: for each
+    sequence, U = the eigenvectors of K_cat^T K_cat for its r largest
+    eigenvalues, K_cat the N x D stored keys of tokens [0, N) concatenated
+    over (layer, kv head, dim); descending order, each vector's entry of
+    largest magnitude made positive.
+    Returns (U [B][D][r] float64, eigenvalues [B][r] descending).
+    """
+    B, r = s.B, s.r
+    N = s.N if N is None else N
+    Us, lams = [], []
+    for b in range(B):
+        k = decode(inp["k"][b][:, :, :N], s.act)
+        kcat = k.transpose(2, 0, 1, 3).reshape(N, -1)
+        lam, vec = np.linalg.eigh(kcat.T @ kcat)
+        order = np.argsort(-lam, kind="stable")[:r]
+        U = vec[:, order]
+        piv = np.argmax(np.abs(U), axis=0)
+        U = U * np.sign(U[piv, np.arange(r)])[None, :]
+        Us.append(U)
+        lams.append(lam[order])
+    return np.stack(Us), np.stack(lams)
+
+
+def residual_energy(inp: dict, s, U: np.ndarray, N: int | None = None) -> np.ndarray:
+    """||K_cat - K_cat U U^T||_F^2 / ||K_cat||_F^2 per sequence (float64), for a
+    basis U [B][D][r] given in float64."""
+    N = s.N if N is None else N
+    out = np.zeros(s.B)
+    for b in range(s.B):
+        k = decode(inp["k"][b][:, :, :N], s.act)
+        kcat = k.transpose(2, 0, 1, 3).reshape(N, -1)
+        rec = (kcat @ U[b]) @ U[b].T
+        out[b] = np.sum((kcat - rec) ** 2) / np.sum(kcat ** 2)
+    return out
 
 
 # ============================================================================

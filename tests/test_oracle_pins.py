@@ -690,3 +690,47 @@ def test_fit_descends_and_equals_explicit_gradient_steps():
         wt = [(x - lr * g).detach() for x, g in zip(wt, gs)]
     for n, x in zip(("w1", "b1", "w2", "b2"), wt):
         assert np.allclose(fit[n][0, 0, 0], x.numpy(), rtol=1e-10, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# the group key basis at prefill
+# ---------------------------------------------------------------------------
+def test_key_basis_is_eckart_young_optimal():
+    s = tiny64(B=2, r=8, N=64)
+    inp = gen.make(s)
+    U, lam = O.key_basis(inp, s)
+    for b in range(s.B):
+        kcat = kcat_of(inp, s, b)
+        sv = np.linalg.svd(kcat, compute_uv=False)          # library SVD, not the Gram
+        tail = np.sum(sv[s.r:] ** 2)
+        res = np.sum((kcat - kcat @ U[b] @ U[b].T) ** 2)
+        assert res == pytest.approx(tail, rel=1e-9)
+        assert np.allclose(lam[b], sv[:s.r] ** 2, rtol=1e-10)
+        assert np.allclose(U[b].T @ U[b], np.eye(s.r), atol=1e-12)
+        assert np.all(np.diff(lam[b]) <= 0)
+        # columns are eigenvectors of the Gram matrix, largest entry positive
+        G = kcat.T @ kcat
+        assert np.allclose(G @ U[b], U[b] * lam[b][None, :], atol=1e-9 * lam[b][0])
+        assert np.all(U[b][np.argmax(np.abs(U[b]), axis=0), np.arange(s.r)] > 0)
+    assert np.allclose(O.residual_energy(inp, s, U),
+                       [np.sum(np.linalg.svd(kcat_of(inp, s, b), compute_uv=False)[s.r:] ** 2) /
+                        np.sum(kcat_of(inp, s, b) ** 2) for b in range(s.B)], rtol=1e-9)
+
+
+def test_key_basis_spans_exactly_low_rank_keys():
+    s = tiny64(r=8, key_cols=6)          # keys drawn in a 6-dim subspace of D = 32
+    inp = gen.make(s)
+    U, lam = O.key_basis(inp, s)
+    assert np.max(O.residual_energy(inp, s, U)) < 1e-24
+    assert lam[0, 6] < 1e-12 * lam[0, 0]  # eigh resolves zero to about eps * ||G||
+    # the generator's frame lies in the span of the leading 6 directions
+    F = O.decode(inp["basis"][0], s.act)[:, :6]
+    assert np.allclose(U[0][:, :6] @ (U[0][:, :6].T @ F), F, atol=1e-10)
+
+
+def test_key_basis_full_rank_is_complete():
+    s = tiny64(r=32)
+    inp = gen.make(s)
+    U, _ = O.key_basis(inp, s)
+    assert np.allclose(U[0] @ U[0].T, np.eye(32), atol=1e-12)
+    assert np.max(O.residual_energy(inp, s, U)) < 1e-25
