@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches (for counter runs)")
     ap.add_argument("--no-fit", action="store_true", help="skip timing the predictor fit")
     ap.add_argument("--fit-steps", type=int, default=4)
+    ap.add_argument("--no-basis", action="store_true", help="skip timing the key basis")
+    ap.add_argument("--basis-iterations", type=int, default=8)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times: a kernel of known "
                          "traffic that scales hardware byte counters")
@@ -180,6 +182,38 @@ def time_fit(P, s, d, model, dev, ev, steps=4, lr=0.01):
             "how": "one call between HIP events after a zero-step warm-up; float32 products on the vector ALUs"}
 
 
+def time_basis(P, s, d, dev, ev, iterations=8):
+    """Time lowram_key_basis on the prefill keys (once per context) and report
+    how much key energy its basis leaves out next to the basis the inputs carry."""
+    import torch
+    D = s.G * s.Hkv * s.dh
+    flops = s.B * (s.N * D * D + iterations * 2 * s.r * D * D)   # upper-triangle Gram + G Q products
+    ws = P.workspace(d, P._lib.OP_BASIS)
+    out = P.key_basis(d, dev["k"], 0, ws=ws)  # warm-up
+    torch.cuda.synchronize()
+    ev[0].record()
+    out = P.key_basis(d, dev["k"], iterations, out=out, ws=ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    tf = flops / (ms * 1e-3) / 1e12
+    # energy outside span(U) on a sample of tokens, for the GPU basis and the given one
+    n = min(s.N, 4096)
+    kc = dev["k"][:, :, :, :n].float().permute(0, 3, 1, 2, 4).reshape(s.B, n, D)
+    def resid(U):
+        U = U.float()
+        rec = (kc @ U) @ U.transpose(1, 2)
+        return float(((kc - rec) ** 2).sum() / (kc ** 2).sum())
+    r_gpu, r_given = resid(out), resid(dev["basis"])
+    del ws, out, kc
+    torch.cuda.empty_cache()
+    log(f"basis {iterations} iterations in {ms:.1f} ms ({tf:.1f} TFLOP/s fp32), residual energy {r_gpu:.2e} (given basis {r_given:.2e})")
+    return {"iterations": iterations, "ms": round(ms, 2), "algorithmic_flops": int(flops), "tflops": round(tf, 2),
+            "bound": "alu", "peak_tflops": FP32_PEAK_TFLOPS, "frac": round(tf / FP32_PEAK_TFLOPS, 4),
+            "residual_energy": r_gpu, "residual_energy_given_basis": r_given, "sample_tokens": n,
+            "how": "one call between HIP events after a zero-iteration warm-up; float32 on the vector ALUs"}
+
+
 def cpu_baseline(s, host, inp, budget_s):
     from oracle import lowram_oracle as O
     try:
@@ -249,6 +283,7 @@ def main():
     comp_bytes, dense_bytes = P.cache_bytes(dims_of(s))
     repack = time_repack(P, s, d, model, cache, dev, ev)
     fit = None if args.no_fit else time_fit(P, s, dims_of(s), model, dev, ev, steps=args.fit_steps)
+    basis = None if args.no_basis else time_basis(P, s, dims_of(s), dev, ev, iterations=args.basis_iterations)
 
     # per (query set, layer) pre-marshalled calls
     kk = P.k_eff(d)
@@ -425,6 +460,7 @@ def main():
         "compress_ms": round(compress_ms, 2),
         "repack": repack,
         "fit": fit,
+        "basis": basis,
         "step_time_distribution": step_dist,
         "graph": graph is not None,
         "device": dev_name,

@@ -6,9 +6,9 @@ this package marshals torch tensors into it.
 from . import _lib
 from ._lib import LowramError
 from .api import (DecodeCall, alloc_cache, cache_bytes, compress, decode_attn, decode_kernel,
-                  dense_decode_attn, dense_workspace, evict, fit_predictor, k_eff, make_dims, repack, with_, workspace,
+                  dense_decode_attn, dense_workspace, evict, fit_predictor, k_eff, key_basis, make_dims, repack, with_, workspace,
                   workspace_bytes)
 
 __all__ = ["DecodeCall", "LowramError", "alloc_cache", "cache_bytes", "compress", "decode_attn",
-           "decode_kernel", "dense_decode_attn", "dense_workspace", "evict", "fit_predictor", "k_eff", "make_dims", "repack", "with_",
+           "decode_kernel", "dense_decode_attn", "dense_workspace", "evict", "fit_predictor", "k_eff", "key_basis", "make_dims", "repack", "with_",
            "workspace", "workspace_bytes", "_lib"]

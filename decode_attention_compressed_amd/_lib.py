@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(HERE, "liblowram.so")
 
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
 F32, BF16, F16, I8 = range(4)
-OP_COMPRESS, OP_DECODE, OP_EVICT, OP_DENSE, OP_REPACK, OP_FIT = range(6)
+OP_COMPRESS, OP_DECODE, OP_EVICT, OP_DENSE, OP_REPACK, OP_FIT, OP_BASIS = range(7)
 
 DIM_FIELDS = ("batch", "layers", "heads_q", "heads_kv", "head_dim", "rank", "hidden", "n_ctx",
               "chunk", "top_k", "n_tail", "n_res", "act", "coeff", "resid")
@@ -60,6 +60,7 @@ SIGNATURES = {
     "lowram_evict": [P(Dims), P(Model), P(Cache), vp, i32, i32, P(Cache), vp, vp, sz, vp],
     "lowram_repack": [P(Dims), P(Model), P(Cache), vp, vp, i32, P(Cache), vp, sz, vp],
     "lowram_fit_predictor": [P(Dims), P(Model), vp, vp, i32, ctypes.c_float, P(Predictor), vp, vp, sz, vp],
+    "lowram_key_basis": [P(Dims), vp, i32, vp, vp, sz, vp],
     "lowram_dense_decode_attn": [P(Dims), vp, vp, vp, i32, i64, vp, vp, sz, vp],
     "lowram_status_string": [i32],
     "lowram_last_error": [],

@@ -278,6 +278,19 @@ def fit_predictor(d: L.Dims, model: dict, k, v, steps: int, lr: float, out=None,
     return out, loss
 
 
+def key_basis(d: L.Dims, k, iterations: int = 8, out=None, ws=None, stream=None):
+    """The group key basis [B][D][r] (act dtype) from the prefill keys k."""
+    dt = TORCH_DT[d.act]
+    D = d.layers * d.heads_kv * d.head_dim
+    out = torch.empty((d.batch, D, d.rank), dtype=dt, device=k.device) if out is None else out
+    ws = workspace(d, L.OP_BASIS, k.device) if ws is None else ws
+    kv_shape = (d.batch, d.layers, d.heads_kv, d.n_ctx, d.head_dim)
+    L.check(L.lib().lowram_key_basis(ctypes.byref(d), _ptr(k, dt, kv_shape, "k"), int(iterations),
+                                     _ptr(out, dt, (d.batch, D, d.rank), "basis"), _ptr(ws, torch.uint8),
+                                     ws.numel(), _stream(stream)))
+    return out
+
+
 def dense_workspace(d: L.Dims, n_tokens: int, device="cuda") -> torch.Tensor:
     return workspace(with_(d, n_ctx=n_tokens), L.OP_DENSE, device)
 

@@ -96,6 +96,18 @@ struct FitArgs {
 };
 hipError_t run_fit(const FitArgs &a, hipStream_t st);
 
+struct BasisArgs {
+  const void *k;                 // [B][G][Hkv][N][dh] act
+  void *basis;                   // [B][D][r] act (output)
+  float *gram;                   // workspace [B][D][D]
+  float *yt, *qt;                // workspace [B][r][D] each
+  float *cbuf;                   // workspace [B][32][r]
+  double *nrm;                   // workspace [B][32]
+  int B, G, Hkv, dh, r, N, iterations, act;
+};
+hipError_t run_basis(const BasisArgs &a, hipStream_t st);
+int basis_max_dim();             // largest D the basis kernels take
+
 struct EvictArgs {
   const void *basis;
   const void *obs_q;            // [n_obs][B][G][Hq][dh]

@@ -21,39 +21,14 @@
 #include <cstring>
 
 #include "common.hpp"
+#include "gemm_f32.hpp"
 #include "internal.hpp"
 
 namespace lowram {
 namespace fit {
 
-// Offset of head z's block in an array: (z / div) * hi + (z % div) * lo.
-struct ZOff {
-  int div;
-  long hi, lo;
-  __device__ long operator()(int z) const { return (long)(z / div) * hi + (long)(z % div) * lo; }
-};
+using namespace f32gemm;
 
-__device__ __forceinline__ float ldf(const float *p, long i) { return p[i]; }
-__device__ __forceinline__ float ldf(const bf16 *p, long i) { return bf16_bits_to_f32(p[i].u); }
-
-// A(z, i, k) operands.  KC: k is the contiguous index.
-template <typename T, bool KC_>
-struct AOp {
-  static constexpr bool KC = KC_;
-  const T *p; ZOff zo; int ld;
-  __device__ float operator()(int z, int i, int k) const {
-    return ldf(p, zo(z) + (KC ? (long)i * ld + k : (long)k * ld + i));
-  }
-};
-// B(z, k, j) operands.  KC: k is the contiguous index.
-template <typename T, bool KC_>
-struct BOp {
-  static constexpr bool KC = KC_;
-  const T *p; ZOff zo; int ld;
-  __device__ float operator()(int z, int k, int j) const {
-    return ldf(p, zo(z) + (KC ? (long)j * ld + k : (long)k * ld + j));
-  }
-};
 // Stored coefficients of head z's sequence, dequantised: A(z, t, i) = deq(c~[b][t][i]).
 template <typename TC>
 struct CoefOp {
@@ -66,50 +41,6 @@ struct CoefOp {
     else return ldf(p, o);
   }
 };
-
-// C(z)[i][j] = sum_k A(z, i, k) B(z, k, j) handed to ep(z, i, j, c).
-// grid (ceil(N/64), ceil(M/64), Z), 256 threads.
-template <class LA, class LB, class EP>
-__global__ __launch_bounds__(256) void k_gemm(LA A, LB Bm, EP ep, int M, int N, int K) {
-  __shared__ float As[16][64 + 1];
-  __shared__ float Bs[16][64 + 1];
-  const int z = blockIdx.z, i0 = blockIdx.y * 64, j0 = blockIdx.x * 64, tid = threadIdx.x;
-  const int tx = tid % 16, ty = tid / 16;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int idx = tid; idx < 16 * 64; idx += 256) {
-      const int kk = LA::KC ? idx % 16 : idx / 64, m = LA::KC ? idx / 16 : idx % 64;
-      const int gi = i0 + m, gk = k0 + kk;
-      As[kk][m] = (gi < M && gk < K) ? A(z, gi, gk) : 0.f;
-    }
-    for (int idx = tid; idx < 16 * 64; idx += 256) {
-      const int kk = LB::KC ? idx % 16 : idx / 64, n = LB::KC ? idx / 16 : idx % 64;
-      const int gj = j0 + n, gk = k0 + kk;
-      Bs[kk][n] = (gj < N && gk < K) ? Bm(z, gk, gj) : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = As[kk][ty + 16 * a];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = Bs[kk][tx + 16 * c];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(av[a], bv[c], acc[a][c]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int i = i0 + ty + 16 * a, j = j0 + tx + 16 * c;
-      if (i < M && j < N) ep(z, i, j, acc[a][c]);
-    }
-}
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
 
@@ -223,12 +154,6 @@ template <typename TA>
 __global__ __launch_bounds__(256) void k_from_master(const float *__restrict__ m, TA *__restrict__ w, long n) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i < n) store_f32(w + i, m[i]);
-}
-
-template <class LA, class LB, class EP>
-static void gemm(LA A, LB Bm, EP ep, int M, int N, int K, int Z, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm<LA, LB, EP>), dim3((N + 63) / 64, (M + 63) / 64, Z), dim3(256), 0, st,
-                     A, Bm, ep, M, N, K);
 }
 
 static inline unsigned blocks(long n) { return (unsigned)((n + 255) / 256); }

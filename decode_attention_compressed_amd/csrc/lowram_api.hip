@@ -180,6 +180,24 @@ FitPlan fit_plan(const lowram_dims *d) {
   return p;
 }
 
+// Key-basis workspace: the D x D Gram matrix, two r x D row sets, the block
+// products and row norms (float32 / float64).
+struct BasisPlan {
+  size_t gram_off, yt_off, qt_off, c_off, nrm_off, bytes;
+};
+
+BasisPlan basis_plan(const lowram_dims *d) {
+  BasisPlan p;
+  const size_t B = d->batch, r = d->rank, D = (size_t)d->layers * d->heads_kv * d->head_dim;
+  p.gram_off = 0;
+  p.yt_off = align_up(4 * B * D * D);
+  p.qt_off = p.yt_off + align_up(4 * B * r * D);
+  p.c_off = p.qt_off + align_up(4 * B * r * D);
+  p.nrm_off = p.c_off + align_up(4 * B * 32 * r);
+  p.bytes = p.nrm_off + align_up(8 * B * 32);
+  return p;
+}
+
 struct DensePlan {
   int tps, n_split, PW;
   size_t bytes;
@@ -305,6 +323,7 @@ lowram_status lowram_workspace_bytes(const lowram_dims *d, int32_t op, size_t *b
     case LOWRAM_OP_DENSE: *bytes = dense_plan(d, d->n_ctx).bytes; return LOWRAM_OK;
     case LOWRAM_OP_REPACK: *bytes = repack_plan(d).bytes; return LOWRAM_OK;
     case LOWRAM_OP_FIT: *bytes = fit_plan(d).bytes; return LOWRAM_OK;
+    case LOWRAM_OP_BASIS: *bytes = basis_plan(d).bytes; return LOWRAM_OK;
   }
   return fail(LOWRAM_E_INVALID, "unknown op %d", op);
 }
@@ -608,6 +627,32 @@ lowram_status lowram_fit_predictor(const lowram_dims *d, const lowram_model *m, 
   a.F = d->hidden; a.N = d->n_ctx; a.steps = steps; a.act = d->act; a.coeff_dt = d->coeff;
   a.lr = lr;
   return hip_status(run_fit(a, (hipStream_t)stream), "lowram_fit_predictor");
+}
+
+lowram_status lowram_key_basis(const lowram_dims *d, const void *k, int32_t iterations, void *basis,
+                               void *ws, size_t ws_bytes, void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  const int D = d->layers * d->heads_kv * d->head_dim;
+  if (d->n_ctx < 1) return fail(LOWRAM_E_INVALID, "the basis needs at least one token (n_ctx >= 1)");
+  if (D > basis_max_dim())
+    return fail(LOWRAM_E_UNSUPPORTED, "group key dim %d above %d for the basis kernels", D, basis_max_dim());
+  if (iterations < 0 || iterations > 1000) return fail(LOWRAM_E_INVALID, "iterations %d outside [0, 1000]", iterations);
+  REQUIRE_PTR(k); REQUIRE_PTR(basis);
+  const BasisPlan p = basis_plan(d);
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  char *w = (char *)ws;
+  BasisArgs a;
+  memset(&a, 0, sizeof a);
+  a.k = k; a.basis = basis;
+  a.gram = reinterpret_cast<float *>(w + p.gram_off);
+  a.yt = reinterpret_cast<float *>(w + p.yt_off);
+  a.qt = reinterpret_cast<float *>(w + p.qt_off);
+  a.cbuf = reinterpret_cast<float *>(w + p.c_off);
+  a.nrm = reinterpret_cast<double *>(w + p.nrm_off);
+  a.B = d->batch; a.G = d->layers; a.Hkv = d->heads_kv; a.dh = d->head_dim; a.r = d->rank;
+  a.N = d->n_ctx; a.iterations = iterations; a.act = d->act;
+  return hip_status(run_basis(a, (hipStream_t)stream), "lowram_key_basis");
 }
 
 lowram_status lowram_dense_decode_attn(const lowram_dims *d, const void *q, const void *k,

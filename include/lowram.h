@@ -65,7 +65,8 @@ typedef enum {
   LOWRAM_OP_EVICT = 2,
   LOWRAM_OP_DENSE = 3,
   LOWRAM_OP_REPACK = 4,
-  LOWRAM_OP_FIT = 5
+  LOWRAM_OP_FIT = 5,
+  LOWRAM_OP_BASIS = 6
 } lowram_op;
 
 /* Sizes of one xKV group over a batch.  All counts are per sequence. */
@@ -259,6 +260,21 @@ lowram_status lowram_fit_predictor(const lowram_dims *dims, const lowram_model *
                                    const void *k, const void *v, int32_t steps, float lr,
                                    const lowram_predictor *out, double *loss, void *workspace,
                                    size_t workspace_bytes, void *stream);
+
+/* The group key basis at prefill (rit.work keys section: xKV finds a few
+ * principal directions of the keys; zicq.com "Cross-Layer Low-Rank Key
+ * Compression": one basis shared by adjacent layers).  Per sequence: the
+ * float32 Gram matrix G = K_cat^T K_cat of the N prefill keys (K_cat: N x D,
+ * dims ordered (layer, kv head, dim)), then `iterations` steps of subspace
+ * iteration Q <- orth(G Q) from a fixed counter-hash start, orth = block
+ * Gram-Schmidt run twice.  basis (out): [B][D][r] act dtype, orthonormal
+ * columns spanning the dominant r-dimensional subspace of G; unlike an
+ * eigensolver's output they are not rotated to individual eigenvectors, which
+ * changes no reconstruction U U^T k.  Deterministic.  k: [B][G][Hkv][N][dh]
+ * act dtype (N = n_ctx >= 1).  D <= 8192.  Workspace: LOWRAM_OP_BASIS
+ * (4 B (D^2 + 2 r D) bytes and a little more). */
+lowram_status lowram_key_basis(const lowram_dims *dims, const void *k, int32_t iterations, void *basis,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Uncompressed decode attention, the comparator for the compressed path:
  * out[b][g] = softmax(k_b,h q_g / sqrt(d_h)) v_b,h over n_tokens tokens

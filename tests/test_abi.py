@@ -53,7 +53,7 @@ def test_llama_ratio_and_composed_ratio():
 @pytest.mark.parametrize("s", ALL, ids=lambda s: s.name)
 def test_workspace_sizes_are_positive_and_aligned(s):
     d = dims_of(s)
-    for op in (L.OP_COMPRESS, L.OP_DECODE, L.OP_EVICT, L.OP_DENSE, L.OP_REPACK, L.OP_FIT):
+    for op in (L.OP_COMPRESS, L.OP_DECODE, L.OP_EVICT, L.OP_DENSE, L.OP_REPACK, L.OP_FIT, L.OP_BASIS):
         n = P.workspace_bytes(d, op)
         assert n > 0 and n % 256 == 0
 
@@ -195,6 +195,25 @@ def test_fit_argument_errors():
     # the workspace holds float32 activations of every token
     Z = d.batch * d.layers * d.heads_kv
     assert need >= 4 * Z * d.n_ctx * (2 * d.hidden + 2 * d.head_dim)
+
+
+def test_key_basis_argument_errors():
+    lib = L.lib()
+    d = base_dims()
+    need = P.workspace_bytes(d, L.OP_BASIS)
+
+    def kb(d_=d, it=4, k=FAKE, out=FAKE, have=need):
+        return lib.lowram_key_basis(ctypes.byref(d_), k, it, out, FAKE, have, None)
+
+    assert kb(it=-1) == L.E_INVALID
+    assert kb(k=None) == L.E_INVALID
+    assert kb(out=FAKE + 2) == L.E_INVALID
+    assert kb(have=need - 1) == L.E_WORKSPACE
+    assert kb(d_=P.with_(d, n_ctx=0, n_res=0)) == L.E_INVALID
+    wide = P.with_(d, layers=8, heads_kv=8, heads_q=8, head_dim=256)   # D = 16384
+    assert kb(d_=wide) == L.E_UNSUPPORTED
+    D = d.layers * d.heads_kv * d.head_dim
+    assert need >= 4 * d.batch * (D * D + 2 * d.rank * D)
 
 
 def test_dense_argument_errors():
