@@ -102,6 +102,7 @@ struct BasisArgs {
   float *gram;                   // workspace [B][D][D]
   float *yt, *qt;                // workspace [B][r][D] each
   float *cbuf;                   // workspace [B][32][r]
+  float *cpart;                  // workspace [B][16][32][r]: sliced block dots
   double *nrm;                   // workspace [B][32]
   int B, G, Hkv, dh, r, N, iterations, act;
 };

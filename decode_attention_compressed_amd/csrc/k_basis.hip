@@ -13,8 +13,8 @@
 // orthonormalised one by one inside one workgroup (each thread owns a fixed
 // set of columns, so it only ever reads back what it wrote).  In the first
 // pass a row whose remainder falls below TAU of its norm (numerically in the
-// span of the rows before it) is replaced by a pseudo-random row orthogonalised
-// against every row before it.  The result spans the dominant r-dimensional
+// span of the rows before it) is replaced by a pseudo-random row, which the
+// second pass orthogonalises like any other.  The result spans the dominant r-dimensional
 // subspace; no rotation within it is made (reconstructions U U^T k do not
 // depend on one).
 #include <cstring>
@@ -32,6 +32,7 @@ constexpr int NB = 32;          // rows per Gram-Schmidt block
 constexpr int ONT = 1024;       // threads of the in-block kernel
 constexpr int MAXE = 8;         // columns per thread (D <= ONT * MAXE)
 constexpr int PBATCH = 16;      // rows whose dots are reduced together
+constexpr int KSPLIT = 16;      // most column slices of the block dots
 constexpr float TAU = 1e-4f;    // remainder / norm below which a row counts as dependent
 
 // K_cat(b, t, i) = k[b][i / dh][t][i % dh], read as A(b, i, t) = K_cat(b, t, i)
@@ -137,7 +138,7 @@ __device__ __forceinline__ void project_rows(float (&v)[MAXE], const float *q, l
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int c0 = first; c0 < first + count; c0 += PB) {
     const int nc = min(PB, first + count - c0);
-#pragma unroll 1
+#pragma unroll 4
     for (int c = 0; c < nc; ++c) {
       const float *row = q + base + (long)(c0 + c) * D;
       float s = 0.f;
@@ -151,7 +152,7 @@ __device__ __forceinline__ void project_rows(float (&v)[MAXE], const float *q, l
       if (lane == 0) red[c * NWV + w] = s;
     }
     __syncthreads();
-#pragma unroll 1
+#pragma unroll 4
     for (int c = 0; c < nc; ++c) {
       float d = 0.f;
 #pragma unroll
@@ -178,9 +179,11 @@ __device__ __forceinline__ float row_norm(const float (&v)[MAXE], float *red) {
 // Rows row0 .. row0 + nb - 1 of src orthonormalised one by one against the
 // rows before them inside the block (two passes each) and written to rows
 // row0.. of q (src may be q).  DETECT: a row whose remainder is <= TAU *
-// nrm0[a] is replaced by a pseudo-random row orthogonalised (twice) against
-// every row of q before it.  Thread t owns columns t + ONT e and only reads
-// back columns it wrote itself.  grid (B), ONT threads.
+// nrm0[a] is replaced by a pseudo-random row, orthogonalised here against the
+// block's earlier rows; the second block pass projects it off the earlier
+// blocks (a random row is far from their span, so one projection suffices).
+// Thread t owns columns t + ONT e and only reads back columns it wrote itself.
+// grid (B), ONT threads.
 template <bool DETECT>
 __global__ __launch_bounds__(ONT) void k_intra(const float *src, float *q, int r, int D, int row0, int nb,
                                                const double *__restrict__ nrm0, uint32_t salt) {
@@ -203,8 +206,8 @@ __global__ __launch_bounds__(ONT) void k_intra(const float *src, float *q, int r
         const int i = tid + ONT * e;
         v[e] = i < D ? hash_uniform(b, row0 + a, i, salt) : 0.f;
       }
-      project_rows<PBATCH>(v, q, base, D, 0, row0 + a, red);
-      project_rows<PBATCH>(v, q, base, D, 0, row0 + a, red);
+      project_rows<PBATCH>(v, q, base, D, row0, a, red);
+      project_rows<PBATCH>(v, q, base, D, row0, a, red);
       nrm = row_norm(v, red);
     }
     const float inv = nrm > 0.f ? 1.0f / nrm : 0.f;
@@ -216,6 +219,18 @@ __global__ __launch_bounds__(ONT) void k_intra(const float *src, float *q, int r
   }
 }
 
+// C[b][a][c] = sum over slices s of part[b * S + s][a][c], in order.
+// grid (ceil(nb * j0 / 256), B), 256 threads.
+__global__ __launch_bounds__(256) void k_sum_slices(const float *__restrict__ part, float *__restrict__ c, int S,
+                                                    int nb, int j0, int r) {
+  const int idx = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
+  if (idx >= nb * j0) return;
+  const int a = idx / j0, cc = idx % j0;
+  float s = 0.f;
+  for (int k = 0; k < S; ++k) s += part[(((long)b * S + k) * NB + a) * r + cc];
+  c[((long)b * NB + a) * r + cc] = s;
+}
+
 // U[b][i][j] = round(Qt[b][j][i]).  grid (ceil(r/64), ceil(D/4), B), 256 threads.
 template <typename TA>
 __global__ __launch_bounds__(256) void k_store_basis(const float *__restrict__ qt, TA *__restrict__ u, int r,
@@ -225,19 +240,30 @@ __global__ __launch_bounds__(256) void k_store_basis(const float *__restrict__ q
 }
 
 // rows of src -> orthonormal rows of q (block Gram-Schmidt, twice).
-static void orth(float *src, float *q, float *cbuf, double *nrm, int B, int r, int D, uint32_t salt,
-                 hipStream_t st) {
+// Slices of D for the block dots: about 256 columns each, at most KSPLIT.
+static int dot_slices(int D) {
+  int S = 1;
+  while (S < KSPLIT && D / (2 * S) >= 256 && D % (2 * S * 16) == 0) S *= 2;
+  return S;
+}
+
+static void orth(float *src, float *q, float *cbuf, float *cpart, double *nrm, int B, int r, int D,
+                 uint32_t salt, hipStream_t st) {
   const long zs = (long)r * D;
+  const int S = dot_slices(D), Dsl = D / S;
   for (int j0 = 0; j0 < r; j0 += NB) {
     const int nb = min(NB, r - j0);
     hipLaunchKernelGGL(k_rownorm, dim3(nb, B), dim3(256), 0, st, (const float *)src, r, D, j0, nrm);
     for (int pass = 0; pass < 2; ++pass) {
       float *blk = pass == 0 ? src : q;  // pass 0 reads the block from src, pass 1 from q
       if (j0 > 0) {
-        // C[b][a][c] = <blk row j0 + a, q row c>, then blk rows -= C q[:j0]
-        AOp<float, true> Ab{blk + (long)j0 * D, ZOff{1, zs, 0}, D};
-        BOp<float, true> Qk{q, ZOff{1, zs, 0}, D};
-        gemm(Ab, Qk, EpPut{cbuf, (long)NB * r, r}, nb, j0, D, B, st);
+        // C[b][a][c] = <blk row j0 + a, q row c> (S slices of the columns, added
+        // in order), then blk rows -= C q[:j0]
+        AOp<float, true> Ab{blk + (long)j0 * D, ZOff{S, zs, Dsl}, D};
+        BOp<float, true> Qk{q, ZOff{S, zs, Dsl}, D};
+        gemm(Ab, Qk, EpPut{cpart, (long)NB * r, r}, nb, j0, Dsl, B * S, st);
+        hipLaunchKernelGGL(k_sum_slices, dim3((nb * j0 + 255) / 256, B), dim3(256), 0, st,
+                           (const float *)cpart, cbuf, S, nb, j0, r);
         AOp<float, true> Ac{cbuf, ZOff{1, (long)NB * r, 0}, r};
         BOp<float, false> Qn{q, ZOff{1, zs, 0}, D};
         gemm(Ac, Qn, EpSub{blk, zs, D, j0}, nb, D, j0, B, st);
@@ -262,12 +288,12 @@ static void basis_typed(const BasisArgs &a, hipStream_t st) {
   gemm<true>(Ka, Kb, EpSym{a.gram, D}, D, D, N, B, st);
   // start
   hipLaunchKernelGGL(k_start, dim3((D + 255) / 256, r, B), dim3(256), 0, st, a.yt, r, D);
-  orth(a.yt, a.qt, a.cbuf, a.nrm, B, r, D, 1u, st);
+  orth(a.yt, a.qt, a.cbuf, a.cpart, a.nrm, B, r, D, 1u, st);
   AOp<float, true> Qa{a.qt, ZOff{1, zs, 0}, D};
   BOp<float, false> Gb{a.gram, ZOff{1, (long)D * D, 0}, D};
   for (int it = 0; it < a.iterations; ++it) {
     gemm(Qa, Gb, EpPut{a.yt, zs, D}, r, D, D, B, st);   // Yt = Qt G
-    orth(a.yt, a.qt, a.cbuf, a.nrm, B, r, D, 2u + it, st);
+    orth(a.yt, a.qt, a.cbuf, a.cpart, a.nrm, B, r, D, 2u + it, st);
   }
   hipLaunchKernelGGL(k_store_basis<TA>, dim3((r + 63) / 64, (D + 3) / 4, B), dim3(256), 0, st,
                      (const float *)a.qt, (TA *)a.basis, r, D);

@@ -183,7 +183,7 @@ FitPlan fit_plan(const lowram_dims *d) {
 // Key-basis workspace: the D x D Gram matrix, two r x D row sets, the block
 // products and row norms (float32 / float64).
 struct BasisPlan {
-  size_t gram_off, yt_off, qt_off, c_off, nrm_off, bytes;
+  size_t gram_off, yt_off, qt_off, c_off, cpart_off, nrm_off, bytes;
 };
 
 BasisPlan basis_plan(const lowram_dims *d) {
@@ -193,7 +193,8 @@ BasisPlan basis_plan(const lowram_dims *d) {
   p.yt_off = align_up(4 * B * D * D);
   p.qt_off = p.yt_off + align_up(4 * B * r * D);
   p.c_off = p.qt_off + align_up(4 * B * r * D);
-  p.nrm_off = p.c_off + align_up(4 * B * 32 * r);
+  p.cpart_off = p.c_off + align_up(4 * B * 32 * r);
+  p.nrm_off = p.cpart_off + align_up(4 * B * 16 * 32 * r);
   p.bytes = p.nrm_off + align_up(8 * B * 32);
   return p;
 }
@@ -649,6 +650,7 @@ lowram_status lowram_key_basis(const lowram_dims *d, const void *k, int32_t iter
   a.yt = reinterpret_cast<float *>(w + p.yt_off);
   a.qt = reinterpret_cast<float *>(w + p.qt_off);
   a.cbuf = reinterpret_cast<float *>(w + p.c_off);
+  a.cpart = reinterpret_cast<float *>(w + p.cpart_off);
   a.nrm = reinterpret_cast<double *>(w + p.nrm_off);
   a.B = d->batch; a.G = d->layers; a.Hkv = d->heads_kv; a.dh = d->head_dim; a.r = d->rank;
   a.N = d->n_ctx; a.iterations = iterations; a.act = d->act;
