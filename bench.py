@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--fit-steps", type=int, default=4)
     ap.add_argument("--no-basis", action="store_true", help="skip timing the key basis")
     ap.add_argument("--basis-iterations", type=int, default=8)
+    ap.add_argument("--no-reuse", action="store_true", help="skip timing reuse of rebuilt chunks")
+    ap.add_argument("--reuse-rho", type=float, default=0.95, help="step-to-step query correlation for the reuse timing")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times: a kernel of known "
                          "traffic that scales hardware byte counters")
@@ -214,6 +216,59 @@ def time_basis(P, s, d, dev, ev, iterations=8):
             "how": "one call between HIP events after a zero-iteration warm-up; float32 on the vector ALUs"}
 
 
+def time_reuse(P, s, d, model, cache, dev, rho=0.95, steps=32, slots_per_k=2):
+    """Decode steps on a stream of correlated queries, plain and with reuse of
+    rebuilt chunks (slot table of slots_per_k * k chunks per head), each
+    captured in one HIP graph and replayed after a warm-up replay."""
+    import torch
+    from synth import gen
+    from tests.harness import to_dev
+    if P.decode_kernel(d) != "chain":
+        return None
+    k = P.k_eff(d)
+    qs = to_dev(gen.make_correlated_queries(s, steps, rho), s.act)
+    table = P.alloc_reuse(d, slots_per_k * k)
+    ws = P.workspace(d, P._lib.OP_DECODE)
+    out = torch.empty((s.B, s.Hq, s.dh), dtype=qs.dtype, device="cuda")
+    hits = torch.zeros((steps, s.G, s.B, s.Hkv), dtype=torch.int32, device="cuda")
+
+    def run(use_reuse):
+        for st in range(steps):
+            for l in range(s.G):
+                q = qs[st, l]
+                if use_reuse:
+                    P.decode_attn_reuse(d, l, model, cache, q, dev["k_tail"], dev["v_tail"], table, out=out,
+                                        hits_out=hits[st, l], ws=ws)
+                else:
+                    P.decode_attn(d, l, model, cache, q, dev["k_tail"], dev["v_tail"], out=out, ws=ws)
+
+    res = {}
+    for name, flag in (("plain", False), ("reuse", True)):
+        run(flag)  # eager warm-up (fills the table)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(flag)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / steps
+        del g
+    hit_rate = float(hits.sum().item()) / (steps * s.G * s.B * s.Hkv * k)
+    del table, ws
+    torch.cuda.empty_cache()
+    log(f"reuse rho {rho}: plain {res['plain']:.1f} us/step, reuse {res['reuse']:.1f} us/step, hit rate {hit_rate:.3f}")
+    return {"rho": rho, "slots": slots_per_k * k, "steps": steps, "hit_rate": round(hit_rate, 4),
+            "us_per_step_plain": round(res["plain"], 1), "us_per_step_reuse": round(res["reuse"], 1),
+            "speedup": round(res["plain"] / res["reuse"], 3),
+            "how": "correlated queries q_s = rho q_(s-1) + sqrt(1 - rho^2) xi; both paths captured in one HIP graph "
+                   "each; the step time includes the reuse path's separate selection and slot kernels"}
+
+
 def cpu_baseline(s, host, inp, budget_s):
     from oracle import lowram_oracle as O
     try:
@@ -284,6 +339,7 @@ def main():
     repack = time_repack(P, s, d, model, cache, dev, ev)
     fit = None if args.no_fit else time_fit(P, s, dims_of(s), model, dev, ev, steps=args.fit_steps)
     basis = None if args.no_basis else time_basis(P, s, dims_of(s), dev, ev, iterations=args.basis_iterations)
+    reuse = None if args.no_reuse else time_reuse(P, s, d, model, cache, dev, rho=args.reuse_rho)
 
     # per (query set, layer) pre-marshalled calls
     kk = P.k_eff(d)
@@ -461,6 +517,7 @@ def main():
         "repack": repack,
         "fit": fit,
         "basis": basis,
+        "reuse": reuse,
         "step_time_distribution": step_dist,
         "graph": graph is not None,
         "device": dev_name,

@@ -36,6 +36,11 @@ class Predictor(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "b1", "w2", "b2")]
 
 
+class Reuse(ctypes.Structure):
+    _fields_ = [("tiles", ctypes.c_void_p), ("slot_chunk", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
+                ("clock", ctypes.c_void_p), ("slots", ctypes.c_int32)]
+
+
 class LowramError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"lowram status {status}: {msg}")
@@ -61,6 +66,8 @@ SIGNATURES = {
     "lowram_repack": [P(Dims), P(Model), P(Cache), vp, vp, i32, P(Cache), vp, sz, vp],
     "lowram_fit_predictor": [P(Dims), P(Model), vp, vp, i32, ctypes.c_float, P(Predictor), vp, vp, sz, vp],
     "lowram_key_basis": [P(Dims), vp, i32, vp, vp, sz, vp],
+    "lowram_reuse_tile_bytes": [P(Dims), P(sz)],
+    "lowram_decode_attn_reuse": [P(Dims), i32, P(Model), P(Cache), vp, vp, vp, vp, vp, P(Reuse), vp, vp, sz, vp],
     "lowram_dense_decode_attn": [P(Dims), vp, vp, vp, i32, i64, vp, vp, sz, vp],
     "lowram_status_string": [i32],
     "lowram_last_error": [],

@@ -169,6 +169,47 @@ def decode_attn(d: L.Dims, layer: int, model: dict, cache: dict, q, k_tail, v_ta
     return out
 
 
+def reuse_tile_bytes(d: L.Dims) -> int:
+    n = ctypes.c_size_t(0)
+    L.check(L.lib().lowram_reuse_tile_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_reuse(d: L.Dims, slots: int, device="cuda") -> dict:
+    """A fresh reuse table: slot_chunk -1, stamps and clocks 0."""
+    B, G, H = d.batch, d.layers, d.heads_kv
+    return {"tiles": torch.empty((B, G, H, slots, reuse_tile_bytes(d)), dtype=torch.uint8, device=device),
+            "slot_chunk": torch.full((B, G, H, slots), -1, dtype=torch.int32, device=device),
+            "slot_stamp": torch.zeros((B, G, H, slots), dtype=torch.int32, device=device),
+            "clock": torch.zeros((B, G, H), dtype=torch.int32, device=device), "slots": slots}
+
+
+def reuse_struct(d: L.Dims, r: dict) -> L.Reuse:
+    B, G, H, S = d.batch, d.layers, d.heads_kv, r["slots"]
+    s = L.Reuse()
+    s.tiles = _ptr(r["tiles"], torch.uint8, (B, G, H, S, reuse_tile_bytes(d)), "tiles").value
+    s.slot_chunk = _ptr(r["slot_chunk"], torch.int32, (B, G, H, S), "slot_chunk").value
+    s.slot_stamp = _ptr(r["slot_stamp"], torch.int32, (B, G, H, S), "slot_stamp").value
+    s.clock = _ptr(r["clock"], torch.int32, (B, G, H), "clock").value
+    s.slots = S
+    return s
+
+
+def decode_attn_reuse(d: L.Dims, layer: int, model: dict, cache: dict, q, k_tail, v_tail, reuse: dict,
+                      out=None, sel_out=None, hits_out=None, ws=None, stream=None):
+    qp, kt, vt = _decode_common(d, q, k_tail, v_tail)
+    out = torch.empty_like(q) if out is None else out
+    ws = workspace(d, L.OP_DECODE, q.device) if ws is None else ws
+    sp = _ptr(sel_out, torch.int32, (d.batch, d.heads_kv, k_eff(d)), "sel_out")
+    hp = _ptr(hits_out, torch.int32, (d.batch, d.heads_kv), "hits_out")
+    L.check(L.lib().lowram_decode_attn_reuse(ctypes.byref(d), layer, ctypes.byref(model_struct(d, model)),
+                                             ctypes.byref(cache_struct(d, cache)), qp, kt, vt,
+                                             _ptr(out, TORCH_DT[d.act], tuple(q.shape), "out"), sp,
+                                             ctypes.byref(reuse_struct(d, reuse)), hp, _ptr(ws, torch.uint8),
+                                             ws.numel(), _stream(stream)))
+    return out
+
+
 class DecodeCall:
     """Pre-marshalled arguments of one decode call, for tight loops and timing:
     the three stages can be issued separately on the current stream."""

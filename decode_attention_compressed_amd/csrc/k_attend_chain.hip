@@ -66,6 +66,9 @@ constexpr int TP = 32;            // tail tokens staged in LDS per split
 constexpr int CPT = 2;            // tiles per chunk: 128-token chunks
 constexpr int MAXIT = 8;          // tiles per wave and split (at most)
 constexpr int MAXSLOT = MAXIT * NW / CPT;  // selected chunks per split (at most)
+// A cached tile: the rebuilt keys KA[NJ][NTT] in 16-byte words, laid out as
+// the registers hold them (lane fastest).
+constexpr int KA_W = NJ * NTT * WAVE;
 
 template <int I, int N, typename Fn>
 __device__ __forceinline__ void sfor_impl(Fn &f) {
@@ -281,11 +284,12 @@ template <> struct Res<int8_t> {
   }
 };
 
-template <typename TC, int NR, int NF>
+template <typename TC, int NR, int NF, bool REUSE>
 __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   static_assert(NR % NU == 0, "the basis register ring must divide the k-step count");
   static_assert(NR >= 4, "step 1 needs at least four k-steps");
   constexpr int F = NF * 16;
+  constexpr int TILE_W = KA_W;
   using S = Smem<F>;
   using CT = Coef<TC>;
   using ST = Slab<TC>;
@@ -706,6 +710,47 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     int r_lo = 0, r_n = 0;                     // first row and count of this tile's rows
     typename Res<TC>::raw dr[RP];
 
+    // residual entries of the chunk: their tokens (issued two k-steps before the
+    // end of step 1), then the tile's rows (issued in its last k-step, read after
+    // the softmax)
+    auto res_tokens = [&]() {
+      e0 = has ? e0r : 0;
+      e1 = has ? e1r : 0;
+      const int cnt = e1 - e0;
+#pragma unroll
+      for (int m = 0; m < RM; ++m) {
+        const int i = lane + 64 * m;
+        rtok[m] = (int)__builtin_amdgcn_raw_buffer_load_b32(Ir, 4u * (uint32_t)(i < cnt ? e0 + i : a.n_res), 0u, 0);
+      }
+    };
+    auto res_rows = [&]() {  // this tile's rows: a contiguous run of the chunk's
+      const int cnt = e1 - e0;
+      int below = 0, inside = 0;
+#pragma unroll
+      for (int m = 0; m < RM; ++m) {
+        const bool valid = lane + 64 * m < cnt;
+        rtok[m] -= (int)row0;  // token within the tile
+        below += __popcll(__ballot(valid && rtok[m] < 0));
+        inside += __popcll(__ballot(valid && rtok[m] >= 0 && rtok[m] < TT));
+      }
+      r_lo = e0 + below;
+      r_n = inside;
+#pragma unroll
+      for (int k = 0; k < RP; ++k) dr[k] = Res<TC>::ld(Rr, k < r_n ? r_lo + k : a.n_res, lane);
+    };
+
+    // reuse: the slot code of this tile's chunk (wave-uniform; read again after
+    // step 1 so that nothing of it stays live there); a workgroup whose tiles
+    // all hit skips step 1 and reads its rebuilt keys back
+    auto slot_code = [&]() -> int {
+      return has ? a.rslot[((long)b * a.Hkv + h) * a.k_eff + tau / cpt] : -1;
+    };
+    bool skip1 = false;
+    if constexpr (REUSE) {
+      const int code = slot_code();
+      skip1 = __syncthreads_and(!has || (code >= 0 && (code & REUSE_HIT) != 0));
+    }
+
     // ---- step 1: K_hat^T = U . C^T over NR k-steps ------------------------
     const uint16_t *u_rd = Us + l16 * ULD + 8 * kg;  // lane's basis fragment, head-dim tile 0
     f32x4 acc[NDT][NTT];
@@ -721,45 +766,24 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       // loads so that waiting for it LU - 1 steps later waits for nothing newer
       // than the coefficients then due
       if constexpr (ks + LU < NR)
-        ST::ld(Ur, csc, u_voff, r, (ks + LU) * KS, ur[(ks + LU) % NU], us_[(ks + LU) % NU]);
+        if (!skip1) ST::ld(Ur, csc, u_voff, r, (ks + LU) * KS, ur[(ks + LU) % NU], us_[(ks + LU) % NU]);
       // coefficients DC - 1 steps ahead.
       // Every load here is unconditional (a wave without a tile reads out of
-      // range), so the wait counts stay exact across steps.
+      // range), so the wait counts stay exact across steps; only a workgroup
+      // whose tiles are all read back (reuse) skips them, uniformly.
       if constexpr (ks + DC - 1 < NR) {
+        if (!skip1) {
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) cr[(ks + DC - 1) % DC][tt] = CT::ld(Cr, c_voff, c_soff(tt, ks + DC - 1));
-      }
-      // residual entries of the chunk: their tokens two steps before the end,
-      // the tile's rows in the last step (read after the softmax)
-      if constexpr (ks == NR - 3) {
-        e0 = has ? e0r : 0;
-        e1 = has ? e1r : 0;
-        const int cnt = e1 - e0;
-#pragma unroll
-        for (int m = 0; m < RM; ++m) {
-          const int i = lane + 64 * m;
-          rtok[m] = (int)__builtin_amdgcn_raw_buffer_load_b32(Ir, 4u * (uint32_t)(i < cnt ? e0 + i : a.n_res), 0u, 0);
+          for (int tt = 0; tt < NTT; ++tt) cr[(ks + DC - 1) % DC][tt] = CT::ld(Cr, c_voff, c_soff(tt, ks + DC - 1));
         }
       }
-      if constexpr (ks == NR - 1) {  // this tile's rows: a contiguous run of the chunk's
-        const int cnt = e1 - e0;
-        int below = 0, inside = 0;
-#pragma unroll
-        for (int m = 0; m < RM; ++m) {
-          const bool valid = lane + 64 * m < cnt;
-          rtok[m] -= (int)row0;  // token within the tile
-          below += __popcll(__ballot(valid && rtok[m] < 0));
-          inside += __popcll(__ballot(valid && rtok[m] >= 0 && rtok[m] < TT));
-        }
-        r_lo = e0 + below;
-        r_n = inside;
-#pragma unroll
-        for (int k = 0; k < RP; ++k) dr[k] = Res<TC>::ld(Rr, k < r_n ? r_lo + k : a.n_res, lane);
-      }
+      if constexpr (ks == NR - 3) res_tokens();
+      if constexpr (ks == NR - 1) res_rows();
       __builtin_amdgcn_sched_barrier(0);  // this step's loads go out before its MFMAs
       // basis slab ks + 1 -> LDS (its load was issued LU - 1 steps ago)
-      if constexpr (ks + 1 < NR) ST::st(Us + ((ks + 1) & 1) * DH * ULD, ur[(ks + 1) % NU], us_[(ks + 1) % NU]);
-      {  // basis fragments one head-dim tile ahead of the MFMAs that use them
+      if constexpr (ks + 1 < NR)
+        if (!skip1) ST::st(Us + ((ks + 1) & 1) * DH * ULD, ur[(ks + 1) % NU], us_[(ks + 1) % NU]);
+      if (!skip1) {  // basis fragments one head-dim tile ahead of the MFMAs that use them
         const uint16_t *ub = u_rd + (ks & 1) * DH * ULD;
         typename CT::op bc[NTT];
 #pragma unroll
@@ -782,16 +806,43 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     }
 
     // ---- rebuilt keys as fp16 A operands --------------------------------------
+    int rslot = -1;
+    bool rhit = false;
+    const u32x4 *rtile = nullptr;
+    if constexpr (REUSE) {
+      const int code = slot_code();
+      rhit = code >= 0 && (code & REUSE_HIT) != 0;
+      rslot = code < 0 ? -1 : (code & ~REUSE_HIT);
+      if (rslot >= 0)
+        rtile = reinterpret_cast<const u32x4 *>(a.rtiles) +
+                ((((long)b * a.G + a.layer) * a.Hkv + h) * a.rslots + rslot) * (long)(CPT * TILE_W) +
+                (long)(tau % cpt) * TILE_W;
+    }
     f16x8 KA[NJ][NTT];
+    if (skip1) {  // every tile of the workgroup is cached: the operands as stored
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
+      for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
+        for (int tt = 0; tt < NTT; ++tt)
+          KA[jj][tt] = __builtin_bit_cast(f16x8, rtile[(jj * NTT + tt) * WAVE + lane]);
+    } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          KA[jj][tt][v] = (_Float16)acc[2 * jj][tt][v];
-          KA[jj][tt][4 + v] = (_Float16)acc[2 * jj + 1][tt][v];
-        }
+      for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            KA[jj][tt][v] = (_Float16)acc[2 * jj][tt][v];
+            KA[jj][tt][4 + v] = (_Float16)acc[2 * jj + 1][tt][v];
+          }
+      if (REUSE && rslot >= 0 && !rhit) {
+        u32x4 *wt = const_cast<u32x4 *>(rtile);
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) wt[(jj * NTT + tt) * WAVE + lane] = __builtin_bit_cast(u32x4, KA[jj][tt]);
+      }
+    }
 
     // ---- step 2: logits and online softmax ------------------------------------
     const uint16_t *q_rd = Qs + l16 * WLD + 8 * kg;
@@ -1011,12 +1062,12 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   }
 }
 
-template <typename TC, int NR, int NF>
+template <typename TC, int NR, int NF, bool REUSE>
 static hipError_t go(const AttendArgs &a, hipStream_t st) {
   const size_t smem = Smem<NF * 16>::BYTES;
-  static const bool lds_ok = (allow_dynamic_lds(k_attend_chain<TC, NR, NF>, smem), true);
+  static const bool lds_ok = (allow_dynamic_lds(k_attend_chain<TC, NR, NF, REUSE>, smem), true);
   (void)lds_ok;
-  hipLaunchKernelGGL((k_attend_chain<TC, NR, NF>), dim3(a.B * a.Hkv * a.n_split), dim3(NTH), smem, st, a);
+  hipLaunchKernelGGL((k_attend_chain<TC, NR, NF, REUSE>), dim3(a.B * a.Hkv * a.n_split), dim3(NTH), smem, st, a);
   return hipGetLastError();
 }
 
@@ -1062,11 +1113,15 @@ void chain_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps,
 
 hipError_t launch_attend_chain(int coeff, const AttendArgs &a, hipStream_t st) {
   const bool i8 = coeff == LOWRAM_I8;
-#define X(r_, f_, t_) \
-  if (a.r == r_ && a.F == f_ && i8 == (sizeof(t_) == 1)) return chain::go<t_, r_ / chain::KS, f_ / 16>(a, st);
+#define X(r_, f_, t_)                                                              \
+  if (a.r == r_ && a.F == f_ && i8 == (sizeof(t_) == 1))                           \
+    return a.rtiles ? chain::go<t_, r_ / chain::KS, f_ / 16, true>(a, st)           \
+                    : chain::go<t_, r_ / chain::KS, f_ / 16, false>(a, st);
   LOWRAM_CHAIN_SHAPES(X)
 #undef X
   return hipErrorInvalidValue;
 }
+
+size_t chain_tile_bytes(int) { return (size_t)chain::CPT * 16 * chain::KA_W; }
 
 }  // namespace lowram

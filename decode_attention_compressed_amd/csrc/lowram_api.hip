@@ -78,7 +78,7 @@ lowram_status check_dims(const lowram_dims *d) {
 // partial per selected chunk plus one for the tail.
 struct DecodePlan {
   int k_eff, cps, n_split, n_part, PW, tps, tail_per_split;
-  size_t sel_off, sp_off, sc_off, part_off, bytes;
+  size_t sel_off, sp_off, sc_off, part_off, rslot_off, bytes;
 };
 
 DecodePlan decode_plan(const lowram_dims *d) {
@@ -102,7 +102,8 @@ DecodePlan decode_plan(const lowram_dims *d) {
   p.sc_off = p.sp_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * select_rank_blocks(d->rank) *
                                  (n_c > 0 ? n_c : 1));
   p.part_off = p.sc_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * (n_c > 0 ? n_c : 1));
-  p.bytes = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * p.n_part * g * p.PW);
+  p.rslot_off = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * p.n_part * g * p.PW);
+  p.bytes = p.rslot_off + align_up(sizeof(int32_t) * (size_t)d->batch * d->heads_kv * (p.k_eff > 0 ? p.k_eff : 1));
   return p;
 }
 
@@ -488,6 +489,57 @@ lowram_status lowram_decode_attn(const lowram_dims *d, int32_t layer, const lowr
     return st;
   const AttendArgs a = make_attend(d, layer, m, c, q, k_tail, v_tail, ws, p, sel_out);
   if ((st = hip_status(launch_attend(d->act, d->coeff, d->resid, a, (hipStream_t)stream), "lowram_decode_attend")) != LOWRAM_OK)
+    return st;
+  return lowram_decode_combine(d, layer, m, out, ws, ws_bytes, stream);
+}
+
+lowram_status lowram_reuse_tile_bytes(const lowram_dims *d, size_t *bytes) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  if (!bytes) return fail(LOWRAM_E_INVALID, "bytes is NULL");
+  const DecodePlan p = decode_plan(d);
+  if (p.tps == 0)
+    return fail(LOWRAM_E_UNSUPPORTED, "reuse needs the register-chained attend kernel (see lowram_decode_kernel)");
+  *bytes = chain_tile_bytes(d->hidden);
+  return LOWRAM_OK;
+}
+
+lowram_status lowram_decode_attn_reuse(const lowram_dims *d, int32_t layer, const lowram_model *m,
+                                       const lowram_cache *c, const void *q, const void *k_tail,
+                                       const void *v_tail, void *out, int32_t *sel_out,
+                                       const lowram_reuse *reuse, int32_t *hits_out, void *ws,
+                                       size_t ws_bytes, void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  const DecodePlan p = decode_plan(d);
+  if ((st = check_decode_inputs(d, layer, m, c, p)) != LOWRAM_OK) return st;
+  if (p.tps == 0 || p.k_eff == 0)
+    return fail(LOWRAM_E_UNSUPPORTED, "reuse needs the register-chained attend kernel and a selected chunk");
+  REQUIRE_PTR(q); REQUIRE_PTR(out); OPTIONAL_PTR(sel_out); OPTIONAL_PTR(hits_out);
+  if (d->n_tail > 0) { REQUIRE_PTR(k_tail); REQUIRE_PTR(v_tail); }
+  REQUIRE_PTR(m->w2); REQUIRE_PTR(m->b2);
+  if (!reuse) return fail(LOWRAM_E_INVALID, "reuse is NULL");
+  if (reuse->slots < 1 || reuse->slots > REUSE_MAX_SLOTS)
+    return fail(LOWRAM_E_INVALID, "reuse slots %d outside [1, %d]", reuse->slots, REUSE_MAX_SLOTS);
+  REQUIRE_PTR(reuse->tiles); REQUIRE_PTR(reuse->slot_chunk); REQUIRE_PTR(reuse->slot_stamp);
+  REQUIRE_PTR(reuse->clock);
+  if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
+  // selection into the workspace (the attend kernel does not select here), slots, attend, combine
+  if ((st = run_select(d, layer, m, c, q, sel_out, ws, p, true, stream)) != LOWRAM_OK) return st;
+  int32_t *rslot = reinterpret_cast<int32_t *>((char *)ws + p.rslot_off);
+  const int32_t *sel = reinterpret_cast<const int32_t *>((char *)ws + p.sel_off);
+  if ((st = hip_status(launch_reuse_assign(sel, p.k_eff, reuse->slot_chunk, reuse->slot_stamp, reuse->clock,
+                                           reuse->slots, d->batch, d->layers, d->heads_kv, layer, rslot,
+                                           hits_out, (hipStream_t)stream),
+                       "lowram_decode_attn_reuse")) != LOWRAM_OK)
+    return st;
+  AttendArgs a = make_attend(d, layer, m, c, q, k_tail, v_tail, ws, p, nullptr);
+  a.score_part = nullptr;
+  a.sel_out = nullptr;
+  a.rtiles = reuse->tiles;
+  a.rslot = rslot;
+  a.rslots = reuse->slots;
+  if ((st = hip_status(launch_attend(d->act, d->coeff, d->resid, a, (hipStream_t)stream), "lowram_decode_attn_reuse")) != LOWRAM_OK)
     return st;
   return lowram_decode_combine(d, layer, m, out, ws, ws_bytes, stream);
 }

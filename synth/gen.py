@@ -32,7 +32,7 @@ import numpy as np
 from .configs import BF16, F16, F32, F64, Shape
 
 SEED_ROOT = 20261106
-STREAM_K, STREAM_FRAME, STREAM_MLP, STREAM_NOISE, STREAM_OUTLIER, STREAM_Q, STREAM_OBS = range(7)
+STREAM_K, STREAM_FRAME, STREAM_MLP, STREAM_NOISE, STREAM_OUTLIER, STREAM_Q, STREAM_OBS, STREAM_QCORR = range(8)
 
 
 def _rng(cfg_id: int, b: int, stream: int) -> np.random.Generator:
@@ -175,6 +175,24 @@ def make_queries(s: Shape, steps: int, seed_offset: int = 0) -> np.ndarray:
     for b in range(s.B):
         draws = _rng(cid, b, STREAM_Q).standard_normal((steps, s.G, s.Hq, s.dh))
         q[:, :, b] = store(draws, s.act)
+    return q
+
+
+def make_correlated_queries(s: Shape, steps: int, rho: float, seed_offset: int = 0) -> np.ndarray:
+    """Queries of consecutive decode steps that drift slowly, [steps][G][B][Hq][dh]
+    stored: q_0 ~ N(0, 1) and q_s = rho q_{s-1} + sqrt(1 - rho^2) xi_s per (b, l),
+    so each step keeps unit variance and successive steps tend to pick the same
+    chunks.  (Consecutive tokens' queries are related; i.i.d. queries are the
+    other extreme.)"""
+    cid = s.cfg_id * 1000 + seed_offset
+    q = np.empty((steps, s.G, s.B, s.Hq, s.dh), dtype=_np_dtype(s.act))
+    for b in range(s.B):
+        xi = _rng(cid, b, STREAM_QCORR).standard_normal((steps, s.G, s.Hq, s.dh))
+        cur = xi[0]
+        q[0, :, b] = store(cur, s.act)
+        for st in range(1, steps):
+            cur = rho * cur + np.sqrt(1.0 - rho * rho) * xi[st]
+            q[st, :, b] = store(cur, s.act)
     return q
 
 

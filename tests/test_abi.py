@@ -216,6 +216,31 @@ def test_key_basis_argument_errors():
     assert need >= 4 * d.batch * (D * D + 2 * d.rank * D)
 
 
+def test_reuse_argument_errors():
+    lib = L.lib()
+    d = base_dims()
+    m = L.Model(FAKE, FAKE, FAKE, FAKE, FAKE)
+    c = L.Cache(FAKE, None, FAKE, FAKE, FAKE, FAKE, None)
+    need = P.workspace_bytes(d, L.OP_DECODE)
+    tile = P.reuse_tile_bytes(d)
+    assert tile == 128 * d.head_dim * 2                                  # 128 rebuilt keys, fp16
+
+    def call(reuse, d_=d):
+        return lib.lowram_decode_attn_reuse(ctypes.byref(d_), 0, ctypes.byref(m), ctypes.byref(c), FAKE, FAKE, FAKE,
+                                            FAKE, None, ctypes.byref(reuse) if reuse is not None else None,
+                                            None, FAKE, need, None)
+
+    assert call(None) == L.E_INVALID
+    assert call(L.Reuse(FAKE, FAKE, FAKE, FAKE, 0)) == L.E_INVALID         # no slots
+    assert call(L.Reuse(FAKE, FAKE, FAKE, FAKE, 4096)) == L.E_INVALID      # above the slot limit
+    assert call(L.Reuse(None, FAKE, FAKE, FAKE, 8)) == L.E_INVALID
+    assert call(L.Reuse(FAKE, FAKE, FAKE + 4, FAKE, 8)) == L.E_INVALID     # misaligned stamps
+    other = P.with_(d, head_dim=64)                                          # not a chain shape
+    assert call(L.Reuse(FAKE, FAKE, FAKE, FAKE, 8), d_=other) == L.E_UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert lib.lowram_reuse_tile_bytes(ctypes.byref(other), ctypes.byref(n)) == L.E_UNSUPPORTED
+
+
 def test_dense_argument_errors():
     lib = L.lib()
     d = P.with_(base_dims(), n_ctx=1000, chunk=7)   # the comparator ignores chunking
