@@ -6,11 +6,11 @@ this package marshals torch tensors into it.
 from . import _lib
 from ._lib import LowramError
 from .api import (DecodeCall, alloc_cache, alloc_reuse, cache_bytes, compress, decode_attn, decode_attn_reuse,
-                  decode_kernel, reuse_tile_bytes,
+                  decode_kernel, reuse_current, reuse_tile_bytes,
                   dense_decode_attn, dense_workspace, evict, fit_predictor, k_eff, key_basis, make_dims, repack, with_, workspace,
                   workspace_bytes)
 
 __all__ = ["DecodeCall", "LowramError", "alloc_cache", "alloc_reuse", "cache_bytes", "compress", "decode_attn",
-           "decode_attn_reuse", "reuse_tile_bytes",
+           "decode_attn_reuse", "reuse_current", "reuse_tile_bytes",
            "decode_kernel", "dense_decode_attn", "dense_workspace", "evict", "fit_predictor", "k_eff", "key_basis", "make_dims", "repack", "with_",
            "workspace", "workspace_bytes", "_lib"]

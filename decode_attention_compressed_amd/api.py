@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import ctypes
 
+import numpy as np
 import torch
 
 from . import _lib as L
@@ -176,20 +177,29 @@ def reuse_tile_bytes(d: L.Dims) -> int:
 
 
 def alloc_reuse(d: L.Dims, slots: int, device="cuda") -> dict:
-    """A fresh reuse table: slot_chunk -1, stamps and clocks 0."""
+    """A fresh reuse table: slot_chunk -1 (both halves), stamps and clocks 0."""
     B, G, H = d.batch, d.layers, d.heads_kv
     return {"tiles": torch.empty((B, G, H, slots, reuse_tile_bytes(d)), dtype=torch.uint8, device=device),
-            "slot_chunk": torch.full((B, G, H, slots), -1, dtype=torch.int32, device=device),
-            "slot_stamp": torch.zeros((B, G, H, slots), dtype=torch.int32, device=device),
+            "slot_chunk": torch.full((B, G, H, 2, slots), -1, dtype=torch.int32, device=device),
+            "slot_stamp": torch.zeros((B, G, H, 2, slots), dtype=torch.int32, device=device),
             "clock": torch.zeros((B, G, H), dtype=torch.int32, device=device), "slots": slots}
+
+
+def reuse_current(r: dict):
+    """(slot_chunk, slot_stamp) of each head's current half, [B][G][Hkv][slots], on the host."""
+    clock = r["clock"].cpu().numpy()
+    half = (clock & 1)[..., None, None]
+    ch = np.take_along_axis(r["slot_chunk"].cpu().numpy(), half, axis=3)[:, :, :, 0]
+    st = np.take_along_axis(r["slot_stamp"].cpu().numpy(), half, axis=3)[:, :, :, 0]
+    return ch, st
 
 
 def reuse_struct(d: L.Dims, r: dict) -> L.Reuse:
     B, G, H, S = d.batch, d.layers, d.heads_kv, r["slots"]
     s = L.Reuse()
     s.tiles = _ptr(r["tiles"], torch.uint8, (B, G, H, S, reuse_tile_bytes(d)), "tiles").value
-    s.slot_chunk = _ptr(r["slot_chunk"], torch.int32, (B, G, H, S), "slot_chunk").value
-    s.slot_stamp = _ptr(r["slot_stamp"], torch.int32, (B, G, H, S), "slot_stamp").value
+    s.slot_chunk = _ptr(r["slot_chunk"], torch.int32, (B, G, H, 2, S), "slot_chunk").value
+    s.slot_stamp = _ptr(r["slot_stamp"], torch.int32, (B, G, H, 2, S), "slot_stamp").value
     s.clock = _ptr(r["clock"], torch.int32, (B, G, H), "clock").value
     s.slots = S
     return s

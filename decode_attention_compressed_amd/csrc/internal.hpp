@@ -23,11 +23,14 @@ struct AttendArgs {
   const double *score_part;     // [B][Hkv][select_rank_blocks(r)][n_c] fp64 partial chunk scores
                                 // when the attend kernel selects itself, else null
   int32_t *sel_out;             // [B][Hkv][k_eff] copy of the selection (in-kernel selection only) or null
-  // reuse of rebuilt tiles across steps (register-chained kernel only): per
-  // selected chunk of (b, h) its slot code (REUSE_HIT set when the slot already
-  // holds the chunk, -1 for no slot); rtiles null when reuse is off
+  // reuse of rebuilt tiles across steps (register-chained kernel only); rtiles
+  // null when reuse is off.  The slot table has two halves; the clock's parity
+  // names the current one, the combine advances the clock.
   void *rtiles;                 // [B][G][Hkv][rslots][chain_tile_bytes(F)]: rebuilt keys
-  const int32_t *rslot;         // [B][Hkv][k_eff]
+  int32_t *rt_chunk;            // [B][G][Hkv][2][rslots] chunk held by each slot, -1 if none
+  int32_t *rt_stamp;            // [B][G][Hkv][2][rslots] use count of each slot's last use
+  const int32_t *rclock;        // [B][G][Hkv] calls made on each head's table
+  int32_t *rhits;               // [B][Hkv] chunks read back this step, or null
   int rslots;
   float *part;                  // [B][Hkv][n_split+1][g][PW]
   int B, G, Hq, Hkv, dh, r, F, N, C, T, k_eff, n_res, layer;
@@ -38,6 +41,7 @@ struct AttendArgs {
 
 struct CombineArgs {
   const float *part;    // [B][Hkv][n_total][g][PW]
+  int32_t *rclock;      // [B][G][Hkv] reuse clocks advanced once per (b, h), or null
   const void *w2, *b2;  // [B][G][Hkv][dh][F], [B][G][Hkv][dh] act (null when F == 0)
   void *out;            // [B][Hq][dh] act
   int B, G, Hq, Hkv, dh, F, layer, g, n_comp, n_total, PW;
@@ -68,10 +72,7 @@ void chain_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps,
 hipError_t launch_attend_chain(int coeff, const AttendArgs &a, hipStream_t st);
 constexpr int REUSE_HIT = 1 << 30;
 size_t chain_tile_bytes(int F);  // bytes of one cached 128-token chunk (its rebuilt keys)
-constexpr int REUSE_MAX_SLOTS = 2048;
-hipError_t launch_reuse_assign(const int32_t *sel, int k, int32_t *slot_chunk, int32_t *slot_stamp,
-                               int32_t *clock, int S, int B, int G, int Hkv, int layer, int32_t *rslot,
-                               int32_t *hits_out, hipStream_t st);
+constexpr int REUSE_MAX_SLOTS = 256;
 hipError_t launch_combine(int act, const CombineArgs &a, hipStream_t st);
 hipError_t launch_dense(int act, const void *q, const void *k, const void *v, long batch_stride,
                         int B, int Hq, int Hkv, int dh, int n, int tps, int n_split, float *part,

@@ -152,7 +152,14 @@ struct Smem {
   static constexpr int AH = TV + TP * DH * 2;            // [NW][F][GQ] fp32 running accH per wave
   static constexpr int SEL = AH + NW * GQ * F * 4;       // [MAXSLOT] chunks of this split, [NW] counts
   static constexpr int TLS = SEL + (MAXSLOT + NW) * 4;   // [2][NW][GQ] tail l and the m it is taken at
-  static constexpr int BYTES = TLS + 2 * NW * GQ * 4;
+  static constexpr int RCODE = TLS + 2 * NW * GQ * 4;    // [MAXSLOT] reuse slot codes of this split's chunks
+  static constexpr int BYTES = RCODE + MAXSLOT * 4;
+  // reuse, prologue only: the whole selection after the chunk scores in the p
+  // area, the slot table of (b, l, h) in the accH area
+  static constexpr int SELALL = PS + CHAIN_SELECT_MAX_NC * 8;
+  static_assert(CHAIN_SELECT_MAX_NC * 12 <= NW * GQ * TT * 4, "selection staging does not fit");
+  static_assert((3 * REUSE_MAX_SLOTS + CHAIN_SELECT_MAX_NC) * 4 <= NW * GQ * F * 4,
+                "slot table staging does not fit");
   // the chunk scores of the in-kernel selection use the p area (free until the first softmax)
   static_assert(CHAIN_SELECT_MAX_NC * 8 <= NW * GQ * TT * 4, "score staging does not fit");
   // merge area (after the last tile): per wave and query head m, l of rebuilt
@@ -224,9 +231,10 @@ template <> struct Coef<int8_t> {
 template <typename TC> struct Slab;
 template <> struct Slab<bf16> {
   typedef bf16x8 op;
-  __device__ static void ld(rsrc_t U, const uint16_t *, uint32_t voff, int r, int k0, u32x4 *u, u32x4 &) {
+  __device__ static void ld(rsrc_t U, const uint16_t *, uint32_t voff, int r, int k0, u32x4 *u, u32x4 &,
+                            uint32_t skip = 0u) {
 #pragma unroll
-    for (int i = 0; i < SP; ++i) u[i] = bld16(U, voff, 2u * (k0 + i * (NTH / 4) * r));
+    for (int i = 0; i < SP; ++i) u[i] = bld16(U, voff, 2u * (k0 + i * (NTH / 4) * r) + skip);
   }
   __device__ static void st(uint16_t *Ub, const u32x4 *u, const u32x4 &) {
     const int tid = threadIdx.x;
@@ -237,9 +245,10 @@ template <> struct Slab<bf16> {
 };
 template <> struct Slab<int8_t> {  // fp16 slab with the coefficient scale folded in
   typedef f16x8 op;
-  __device__ static void ld(rsrc_t U, const uint16_t *csc, uint32_t voff, int r, int k0, u32x4 *u, u32x4 &sc) {
+  __device__ static void ld(rsrc_t U, const uint16_t *csc, uint32_t voff, int r, int k0, u32x4 *u, u32x4 &sc,
+                            uint32_t skip = 0u) {
 #pragma unroll
-    for (int i = 0; i < SP; ++i) u[i] = bld16(U, voff, 2u * (k0 + i * (NTH / 4) * r));
+    for (int i = 0; i < SP; ++i) u[i] = bld16(U, voff, 2u * (k0 + i * (NTH / 4) * r) + skip);
     sc = gld16(csc + k0 + 8 * (threadIdx.x & 3));
   }
   __device__ static void st(uint16_t *Ub, const u32x4 *u, const u32x4 &sc) {
@@ -283,6 +292,112 @@ template <> struct Res<int8_t> {
     d1 = (float)(int8_t)((v >> 8) & 0xFFu) * s1;
   }
 };
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Reuse slots for the k selected chunks of one (b, l, h), by one wave (lane
+// order fixes every decision): a chunk held by a slot of the table's current
+// half is a hit (code slot | REUSE_HIT); the others, in ascending chunk order,
+// take the free slots (not hit this step) by (stamp, slot index) and are
+// stored there (code slot), or get no slot (code -1) when none is left.
+// Codes of selection positions [q0, q0 + MAXSLOT) go to codeL; with `write`
+// the updated table goes to the other half and the hit count to hits_out.
+// Slot j lives in lane j % 64, register j / 64; selected chunk i is read from
+// LDS as a broadcast.  Scratch: 3 S + k int32 of LDS.
+__device__ void reuse_assign_wave(const int32_t *selAll, int k, const int32_t *chunk_in,
+                                  const int32_t *stamp_in, int32_t *chunk_out, int32_t *stamp_out, int S,
+                                  int t, int32_t *scr, int32_t *codeL, int q0, bool write,
+                                  int32_t *hits_out) {
+  constexpr int SPL = REUSE_MAX_SLOTS / WAVE;  // slots per lane
+  const int lane = threadIdx.x & (WAVE - 1);
+  int32_t *ch = scr, *stp = scr + S, *by_rank = scr + 2 * S, *held = scr + 3 * S;
+  int myc[SPL], mys[SPL];
+  bool myhit[SPL];
+#pragma unroll
+  for (int u = 0; u < SPL; ++u) {
+    const int j = u * WAVE + lane;
+    myc[u] = j < S ? chunk_in[j] : -1;
+    mys[u] = j < S ? stamp_in[j] : 0;
+    myhit[u] = false;
+  }
+  // hits: one ballot per selected chunk and slot register
+  int hits = 0;
+  for (int i = 0; i < k; ++i) {
+    const int c = selAll[i];
+    int found = -1;
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      if (u * WAVE >= S) break;
+      const uint64_t m = __ballot(myc[u] == c && u * WAVE + lane < S);
+      if (found < 0 && m) {
+        const int l = __ffsll((unsigned long long)m) - 1;
+        found = u * WAVE + l;
+        if (lane == l) myhit[u] = true;
+      }
+    }
+    hits += found >= 0;
+    if (lane == 0) {
+      held[i] = found >= 0;
+      if (i >= q0 && i < q0 + MAXSLOT) codeL[i - q0] = found >= 0 ? (found | REUSE_HIT) : -1;
+    }
+  }
+  // free slots ranked by (stamp, index): each lane ranks its own slots
+  int n_free = 0;
+#pragma unroll
+  for (int u = 0; u < SPL; ++u)
+    if (u * WAVE < S) n_free += __popcll(__ballot(!myhit[u] && u * WAVE + lane < S));
+#pragma unroll
+  for (int u = 0; u < SPL; ++u) {
+    if (u * WAVE >= S) break;
+    const int j = u * WAVE + lane;
+    int rank = 0;
+#pragma unroll
+    for (int u2 = 0; u2 < SPL; ++u2) {
+      if (u2 * WAVE >= S) break;
+      for (int l2 = 0; l2 < WAVE; ++l2) {
+        const int s2 = __shfl(mys[u2], l2, WAVE);
+        const bool f2 = __shfl((int)!myhit[u2], l2, WAVE) != 0;
+        const int j2 = u2 * WAVE + l2;
+        rank += (j2 < S && f2 && (s2 < mys[u] || (s2 == mys[u] && j2 < j))) ? 1 : 0;
+      }
+    }
+    if (j < S && !myhit[u]) by_rank[rank] = j;
+    if (j < S) {
+      ch[j] = myc[u];
+      stp[j] = myhit[u] ? t : mys[u];
+    }
+  }
+  wave_lds_fence();
+  // misses, in ascending chunk order, take the free slots in rank order
+  int before = 0;
+  for (int i0 = 0; i0 < k; i0 += WAVE) {
+    const int i = i0 + lane;
+    const bool miss = i < k && !held[i];
+    const uint64_t mm = __ballot(miss);
+    const int m = before + __popcll(mm & lanemask_lt());
+    if (miss) {
+      const int v = m < n_free ? by_rank[m] : -1;
+      if (i >= q0 && i < q0 + MAXSLOT) codeL[i - q0] = v;
+      if (v >= 0) {
+        ch[v] = selAll[i];
+        stp[v] = t;
+      }
+    }
+    before += __popcll(mm);
+  }
+  wave_lds_fence();
+  if (write) {
+    for (int j = lane; j < S; j += WAVE) {
+      chunk_out[j] = ch[j];
+      stamp_out[j] = stp[j];
+    }
+    if (lane == 0 && hits_out) *hits_out = hits;
+  }
+}
 
 template <typename TC, int NR, int NF, bool REUSE>
 __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
@@ -538,12 +653,26 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
         if ((sel[i] >> lane) & 1ull) {
           const int pos = base + __popcll(sel[i] & lanemask_lt()), c = WAVE * i + lane;
           if (pos >= q0 && pos < q0 + MAXSLOT) selL[pos - q0] = c;
+          if constexpr (REUSE) reinterpret_cast<int32_t *>(sm + S::SELALL)[pos] = c;
           if (s == 0 && a.sel_out) a.sel_out[((long)b * a.Hkv + h) * a.k_eff + pos] = c;
         }
         base += __popcll(sel[i]);
       }
     } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
       selL[tid] = selv;
+    }
+    if constexpr (REUSE) {  // slots of this step's chunks (every split decides the same)
+      int32_t *selAll = reinterpret_cast<int32_t *>(sm + S::SELALL);
+      if (!a.score_part)
+        for (int i = lane; i < a.k_eff; i += WAVE) selAll[i] = selp[i];
+      wave_lds_fence();
+      const long trow = ((long)b * a.G + a.layer) * a.Hkv + h;
+      const int clk = a.rclock[trow], half = clk & 1;
+      const long tin = (trow * 2 + half) * a.rslots, tout = (trow * 2 + (half ^ 1)) * a.rslots;
+      reuse_assign_wave(selAll, a.k_eff, a.rt_chunk + tin, a.rt_stamp + tin, a.rt_chunk + tout,
+                        a.rt_stamp + tout, a.rslots, clk + 1, reinterpret_cast<int32_t *>(sm + S::AH),
+                        reinterpret_cast<int32_t *>(sm + S::RCODE), q0, s == 0,
+                        a.rhits ? a.rhits + (long)b * a.Hkv + h : nullptr);
     }
     if (lane < GQ) {  // wave 0 attends no tail tokens
       tl_l[lane] = 0.f;
@@ -743,13 +872,14 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     // step 1 so that nothing of it stays live there); a workgroup whose tiles
     // all hit skips step 1 and reads its rebuilt keys back
     auto slot_code = [&]() -> int {
-      return has ? a.rslot[((long)b * a.Hkv + h) * a.k_eff + tau / cpt] : -1;
+      return has ? reinterpret_cast<const int32_t *>(sm + S::RCODE)[tau / cpt - q0] : -1;
     };
     bool skip1 = false;
     if constexpr (REUSE) {
       const int code = slot_code();
       skip1 = __syncthreads_and(!has || (code >= 0 && (code & REUSE_HIT) != 0));
     }
+    const uint32_t lskip = skip1 ? 0x80000000u : 0u;  // past every buffer's end
 
     // ---- step 1: K_hat^T = U . C^T over NR k-steps ------------------------
     const uint16_t *u_rd = Us + l16 * ULD + 8 * kg;  // lane's basis fragment, head-dim tile 0
@@ -766,23 +896,21 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       // loads so that waiting for it LU - 1 steps later waits for nothing newer
       // than the coefficients then due
       if constexpr (ks + LU < NR)
-        if (!skip1) ST::ld(Ur, csc, u_voff, r, (ks + LU) * KS, ur[(ks + LU) % NU], us_[(ks + LU) % NU]);
+        ST::ld(Ur, csc, u_voff, r, (ks + LU) * KS, ur[(ks + LU) % NU], us_[(ks + LU) % NU], lskip);
       // coefficients DC - 1 steps ahead.
       // Every load here is unconditional (a wave without a tile reads out of
-      // range), so the wait counts stay exact across steps; only a workgroup
-      // whose tiles are all read back (reuse) skips them, uniformly.
+      // range), so the wait counts stay exact across steps; a workgroup whose
+      // tiles are all read back (reuse) points them past the end (zeros, no
+      // memory traffic) and skips the products.
       if constexpr (ks + DC - 1 < NR) {
-        if (!skip1) {
 #pragma unroll
-          for (int tt = 0; tt < NTT; ++tt) cr[(ks + DC - 1) % DC][tt] = CT::ld(Cr, c_voff, c_soff(tt, ks + DC - 1));
-        }
+        for (int tt = 0; tt < NTT; ++tt) cr[(ks + DC - 1) % DC][tt] = CT::ld(Cr, c_voff, c_soff(tt, ks + DC - 1) + lskip);
       }
       if constexpr (ks == NR - 3) res_tokens();
       if constexpr (ks == NR - 1) res_rows();
       __builtin_amdgcn_sched_barrier(0);  // this step's loads go out before its MFMAs
       // basis slab ks + 1 -> LDS (its load was issued LU - 1 steps ago)
-      if constexpr (ks + 1 < NR)
-        if (!skip1) ST::st(Us + ((ks + 1) & 1) * DH * ULD, ur[(ks + 1) % NU], us_[(ks + 1) % NU]);
+      if constexpr (ks + 1 < NR) ST::st(Us + ((ks + 1) & 1) * DH * ULD, ur[(ks + 1) % NU], us_[(ks + 1) % NU]);
       if (!skip1) {  // basis fragments one head-dim tile ahead of the MFMAs that use them
         const uint16_t *ub = u_rd + (ks & 1) * DH * ULD;
         typename CT::op bc[NTT];

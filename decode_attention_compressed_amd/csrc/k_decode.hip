@@ -401,6 +401,7 @@ __global__ __launch_bounds__(256) void k_combine(const CombineArgs a) {
   float *red = acc + n_out;              // [8]
   float *stage = red + 8;                // [CB][n_out]
   const float *p = a.part + ((long)b * a.Hkv + h) * a.n_total * a.g * a.PW + (long)gi * a.PW;
+  if (a.rclock && gi == 0 && tid == 0) a.rclock[((long)b * a.G + a.layer) * a.Hkv + h] += 1;
   const long sstride = (long)a.g * a.PW;
   float mx = -INFINITY;
   for (int s = tid; s < a.n_total; s += 256) {
@@ -781,6 +782,7 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
   const long sstride = (long)g * a.PW;
   const float *p0 = a.part + ((long)b * a.Hkv + h) * S * sstride;
   const long bh = ((long)b * a.G + a.layer) * a.Hkv + h;
+  if (a.rclock && dq == 0 && tid == 0) a.rclock[bh] += 1;  // the attend kernel has read it
   const uint16_t *W2 = reinterpret_cast<const uint16_t *>(a.w2) + (bh * DH + (long)dq * KV_DQ) * F;
   const uint16_t *B2 = reinterpret_cast<const uint16_t *>(a.b2) + bh * DH + dq * KV_DQ;
 

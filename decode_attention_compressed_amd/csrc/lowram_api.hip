@@ -78,7 +78,7 @@ lowram_status check_dims(const lowram_dims *d) {
 // partial per selected chunk plus one for the tail.
 struct DecodePlan {
   int k_eff, cps, n_split, n_part, PW, tps, tail_per_split;
-  size_t sel_off, sp_off, sc_off, part_off, rslot_off, bytes;
+  size_t sel_off, sp_off, sc_off, part_off, bytes;
 };
 
 DecodePlan decode_plan(const lowram_dims *d) {
@@ -102,8 +102,7 @@ DecodePlan decode_plan(const lowram_dims *d) {
   p.sc_off = p.sp_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * select_rank_blocks(d->rank) *
                                  (n_c > 0 ? n_c : 1));
   p.part_off = p.sc_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * (n_c > 0 ? n_c : 1));
-  p.rslot_off = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * p.n_part * g * p.PW);
-  p.bytes = p.rslot_off + align_up(sizeof(int32_t) * (size_t)d->batch * d->heads_kv * (p.k_eff > 0 ? p.k_eff : 1));
+  p.bytes = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * p.n_part * g * p.PW);
   return p;
 }
 
@@ -398,6 +397,21 @@ namespace {
 // Partial chunk scores, and the summed scores and the selection itself unless
 // the attend kernel will rank the scores (with_topk false); arguments already
 // validated.
+// The combine stage; with rclock it also advances the reuse clock of every
+// (b, layer, h) once, after the attend kernel has read it.
+lowram_status run_combine(const lowram_dims *d, int32_t layer, const lowram_model *m, void *out, void *ws,
+                          const DecodePlan &p, int32_t *rclock, void *stream) {
+  CombineArgs a;
+  memset(&a, 0, sizeof a);
+  a.part = reinterpret_cast<const float *>((char *)ws + p.part_off);
+  a.rclock = rclock;
+  a.w2 = m ? m->w2 : nullptr; a.b2 = m ? m->b2 : nullptr; a.out = out;
+  a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
+  a.F = d->hidden; a.layer = layer; a.g = d->heads_q / d->heads_kv;
+  a.n_comp = p.k_eff > 0 ? p.n_split : 0; a.n_total = p.n_part; a.PW = p.PW;
+  return hip_status(launch_combine(d->act, a, (hipStream_t)stream), "lowram_decode_combine");
+}
+
 lowram_status run_select(const lowram_dims *d, int32_t layer, const lowram_model *m,
                          const lowram_cache *c, const void *q, int32_t *sel_out, void *ws,
                          const DecodePlan &p, bool with_topk, void *stream) {
@@ -460,14 +474,7 @@ lowram_status lowram_decode_combine(const lowram_dims *d, int32_t layer, const l
     REQUIRE_PTR(m->w2); REQUIRE_PTR(m->b2);
   }
   if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
-  CombineArgs a;
-  memset(&a, 0, sizeof a);
-  a.part = reinterpret_cast<const float *>((char *)ws + p.part_off);
-  a.w2 = m ? m->w2 : nullptr; a.b2 = m ? m->b2 : nullptr; a.out = out;
-  a.B = d->batch; a.G = d->layers; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
-  a.F = d->hidden; a.layer = layer; a.g = d->heads_q / d->heads_kv;
-  a.n_comp = p.k_eff > 0 ? p.n_split : 0; a.n_total = p.n_part; a.PW = p.PW;
-  return hip_status(launch_combine(d->act, a, (hipStream_t)stream), "lowram_decode_combine");
+  return run_combine(d, layer, m, out, ws, p, nullptr, stream);
 }
 
 lowram_status lowram_decode_attn(const lowram_dims *d, int32_t layer, const lowram_model *m,
@@ -524,24 +531,19 @@ lowram_status lowram_decode_attn_reuse(const lowram_dims *d, int32_t layer, cons
   REQUIRE_PTR(reuse->tiles); REQUIRE_PTR(reuse->slot_chunk); REQUIRE_PTR(reuse->slot_stamp);
   REQUIRE_PTR(reuse->clock);
   if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
-  // selection into the workspace (the attend kernel does not select here), slots, attend, combine
-  if ((st = run_select(d, layer, m, c, q, sel_out, ws, p, true, stream)) != LOWRAM_OK) return st;
-  int32_t *rslot = reinterpret_cast<int32_t *>((char *)ws + p.rslot_off);
-  const int32_t *sel = reinterpret_cast<const int32_t *>((char *)ws + p.sel_off);
-  if ((st = hip_status(launch_reuse_assign(sel, p.k_eff, reuse->slot_chunk, reuse->slot_stamp, reuse->clock,
-                                           reuse->slots, d->batch, d->layers, d->heads_kv, layer, rslot,
-                                           hits_out, (hipStream_t)stream),
-                       "lowram_decode_attn_reuse")) != LOWRAM_OK)
+  const bool in_attend = attend_selects(d, p);
+  if ((st = run_select(d, layer, m, c, q, in_attend ? nullptr : sel_out, ws, p, !in_attend, stream)) != LOWRAM_OK)
     return st;
-  AttendArgs a = make_attend(d, layer, m, c, q, k_tail, v_tail, ws, p, nullptr);
-  a.score_part = nullptr;
-  a.sel_out = nullptr;
+  AttendArgs a = make_attend(d, layer, m, c, q, k_tail, v_tail, ws, p, sel_out);
   a.rtiles = reuse->tiles;
-  a.rslot = rslot;
+  a.rt_chunk = reuse->slot_chunk;
+  a.rt_stamp = reuse->slot_stamp;
+  a.rclock = reuse->clock;
+  a.rhits = hits_out;
   a.rslots = reuse->slots;
   if ((st = hip_status(launch_attend(d->act, d->coeff, d->resid, a, (hipStream_t)stream), "lowram_decode_attn_reuse")) != LOWRAM_OK)
     return st;
-  return lowram_decode_combine(d, layer, m, out, ws, ws_bytes, stream);
+  return run_combine(d, layer, m, out, ws, p, reuse->clock, stream);
 }
 
 lowram_status lowram_evict(const lowram_dims *d, const lowram_model *m, const lowram_cache *src,

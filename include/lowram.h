@@ -199,26 +199,27 @@ lowram_status lowram_decode_combine(const lowram_dims *dims, int32_t layer, cons
  * and data already rebuilt is reused).  A table of `slots` slots per (sequence,
  * layer, kv head) keeps the rebuilt keys U_{l,h} deq(c~) of recently selected
  * chunks, as fp16, in a layout private to the library
- * (lowram_reuse_tile_bytes per slot).  Each call maps the selected
- * chunks to slots before attending: a chunk already held is read back instead of
- * rebuilt (a hit); the others, in ascending chunk order, take the least
- * recently used slots that no hit of this step holds (older use first, then
- * lower slot) and are stored there once rebuilt; when slots run out a chunk is
- * rebuilt and not stored.  A workgroup whose chunks all hit reads their keys
- * back instead of streaming and multiplying their coefficients; the keys read
- * back are the bits the kernel would compute, so the output equals
- * lowram_decode_attn's bit for bit.
+ * (lowram_reuse_tile_bytes per slot).  Each call maps the selected chunks to
+ * slots inside the attend kernel: a chunk already held is a hit; the others,
+ * in ascending chunk order, take the least recently used slots that no hit of
+ * this step holds (older use first, then lower slot) and are stored there once
+ * rebuilt; when slots run out a chunk is rebuilt and not stored.  A workgroup
+ * whose chunks all hit reads their keys back instead of streaming and
+ * multiplying their coefficients; the keys read back are the bits the kernel
+ * would compute, so the output equals lowram_decode_attn's bit for bit.
+ * The slot bookkeeping has two halves: clock's parity names the current one,
+ * each call writes the updated table into the other half and advances clock.
  * The caller allocates the table and, before its first use, fills slot_chunk
- * with -1 and slot_stamp and clock with 0.  It must reset the table when
- * the cache's chunks change meaning (eviction renumbers them) or the
- * model's basis, W1 or b1 change; a re-pack only appends chunks and keeps it
+ * (both halves) with -1 and slot_stamp and clock with 0.  It must reset the
+ * table when the cache's chunks change meaning (eviction renumbers them) or
+ * the model's basis changes; a re-pack only appends chunks and keeps it
  * valid.  Calls that share a table must not overlap. */
 typedef struct {
-  void *tiles;          /* [B][G][Hkv][slots][tile bytes]                          */
-  int32_t *slot_chunk;  /* [B][G][Hkv][slots] chunk held by each slot, -1 if none  */
-  int32_t *slot_stamp;  /* [B][G][Hkv][slots] use count of each slot's last use    */
-  int32_t *clock;       /* [B][G][Hkv] calls made on each head                     */
-  int32_t slots;        /* slots per (b, layer, kv head), 1 .. 2048                */
+  void *tiles;          /* [B][G][Hkv][slots][tile bytes]                            */
+  int32_t *slot_chunk;  /* [B][G][Hkv][2][slots] chunk held by each slot, -1 if none */
+  int32_t *slot_stamp;  /* [B][G][Hkv][2][slots] use count of each slot's last use   */
+  int32_t *clock;       /* [B][G][Hkv] calls made on each head's table               */
+  int32_t slots;        /* slots per (b, layer, kv head), 1 .. 256                   */
 } lowram_reuse;
 
 /* Bytes of one slot for these dims (host only).  LOWRAM_E_UNSUPPORTED unless
@@ -226,9 +227,9 @@ typedef struct {
 lowram_status lowram_reuse_tile_bytes(const lowram_dims *dims, size_t *bytes);
 
 /* lowram_decode_attn with the reuse table above (same arguments, plus reuse and
- * hits_out: optional [B][Hkv] int32, the number of selected chunks that were
- * read back).  Needs the register-chained kernel; LOWRAM_E_UNSUPPORTED
- * otherwise.  Workspace: LOWRAM_OP_DECODE. */
+ * hits_out: optional [B][Hkv] int32, the number of selected chunks found in the
+ * table).  Same kernels as lowram_decode_attn.  Needs the register-chained
+ * kernel; LOWRAM_E_UNSUPPORTED otherwise.  Workspace: LOWRAM_OP_DECODE. */
 lowram_status lowram_decode_attn_reuse(const lowram_dims *dims, int32_t layer, const lowram_model *model,
                                        const lowram_cache *cache, const void *q, const void *k_tail,
                                        const void *v_tail, void *out, int32_t *sel_out,

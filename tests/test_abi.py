@@ -232,7 +232,7 @@ def test_reuse_argument_errors():
 
     assert call(None) == L.E_INVALID
     assert call(L.Reuse(FAKE, FAKE, FAKE, FAKE, 0)) == L.E_INVALID         # no slots
-    assert call(L.Reuse(FAKE, FAKE, FAKE, FAKE, 4096)) == L.E_INVALID      # above the slot limit
+    assert call(L.Reuse(FAKE, FAKE, FAKE, FAKE, 257)) == L.E_INVALID       # above the slot limit
     assert call(L.Reuse(None, FAKE, FAKE, FAKE, 8)) == L.E_INVALID
     assert call(L.Reuse(FAKE, FAKE, FAKE + 4, FAKE, 8)) == L.E_INVALID     # misaligned stamps
     other = P.with_(d, head_dim=64)                                          # not a chain shape

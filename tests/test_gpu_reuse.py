@@ -115,9 +115,10 @@ def test_reuse_equals_plain_decode_and_the_slot_policy(stream, slots_per_k):
                     want = models[(b, l, h)].step([int(c) for c in sel[b, h]])
                     assert hh[b, h] == want, (st, l, b, h, hh[b, h], want)
                     total_hits += want
-        chunk = to_host(table["slot_chunk"])
+        chunk, _ = P().reuse_current(table)
         for (b, l, h), m in models.items():
             assert list(chunk[b, l, h]) == m.chunk, (st, b, l, h)
+        assert np.all(to_host(table["clock"]) == st + 1)
     assert total_hits > 0  # correlated queries do revisit chunks
 
 
