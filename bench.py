@@ -9,7 +9,10 @@ seeded synthetic data resident in HBM before the timed region.
 
 Prints one JSON line: seq-steps/s, the roofline of the rebuild-and-attend
 kernel (HIP events on its stream), the dense bf16 comparator on the same
-queries (x vs dense), and the CPU oracle on a bounded sample.
+queries (x vs dense), and the CPU oracle on a bounded sample.  After the
+decode step it also times, outside the headline: the tail re-pack, the
+predictor fit, the key basis, and reuse of rebuilt chunks on correlated
+queries (--no-fit / --no-basis / --no-reuse skip the last three).
 """
 from __future__ import annotations
 
@@ -336,10 +339,6 @@ def main():
         cache, d, _ = P.evict(d, model, cache, to_dev(inp["obs_q"]), s.keep_chunks)
         torch.cuda.synchronize()
     comp_bytes, dense_bytes = P.cache_bytes(dims_of(s))
-    repack = time_repack(P, s, d, model, cache, dev, ev)
-    fit = None if args.no_fit else time_fit(P, s, dims_of(s), model, dev, ev, steps=args.fit_steps)
-    basis = None if args.no_basis else time_basis(P, s, dims_of(s), dev, ev, iterations=args.basis_iterations)
-    reuse = None if args.no_reuse else time_reuse(P, s, d, model, cache, dev, rho=args.reuse_rho)
 
     # per (query set, layer) pre-marshalled calls
     kk = P.k_eff(d)
@@ -471,6 +470,12 @@ def main():
                  "kernel": "k_dense (bf16 split-K, eager launches)"}
         log(f"dense {dense_ms * 1e3:.1f} us/step, {dense['hbm_gbps']} GB/s")
         del kd, vd
+
+    # ---- once-per-context and optional paths, timed after the decode step ------
+    repack = time_repack(P, s, d, model, cache, dev, ev)
+    fit = None if args.no_fit else time_fit(P, s, dims_of(s), model, dev, ev, steps=args.fit_steps)
+    basis = None if args.no_basis else time_basis(P, s, dims_of(s), dev, ev, iterations=args.basis_iterations)
+    reuse = None if args.no_reuse else time_reuse(P, s, d, model, cache, dev, rho=args.reuse_rho)
 
     # ---- CPU oracle on a bounded sample ---------------------------------------
     cpu = None
