@@ -30,6 +30,12 @@
 // The second predictor layer is linear and is applied once per query head in
 // the combine: sum_t p_t v_t = W2 accH + b2 mass + accV.
 //
+// The REUSE variant also keeps rebuilt keys across decode steps: wave 0 maps
+// the selected chunks to slots of a per-head table right after selecting them
+// (reuse_assign_wave); a workgroup whose tiles all hit reads its keys back and
+// skips the step-1 products (its coefficient loads point past the buffer end),
+// and tiles given a slot on a miss store their keys after step 1.
+//
 // Method: keys rebuilt from per-token coefficients on a group basis (zicq.com
 // English summary, "Cross-Layer Low-Rank Key Compression"); values from the
 // per-head predictor plus residuals of the worst tokens ("Core Mechanism");
