@@ -569,101 +569,110 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   __syncthreads();
   if (w == 0) {
     if (a.score_part) {
-      constexpr int NSL = CHAIN_SELECT_MAX_NC / WAVE;  // key slots per lane
-      uint32_t khi[NSL], klo[NSL];
-      uint64_t valid[NSL];
-      double sv[NSL];  // the staging area holds CHAIN_SELECT_MAX_NC scores: read all, mask later
+      // NSL key slots per lane: four while n_c <= 256, so that no count spends
+      // compares and popcounts on empty slots
+      auto select_wave = [&](auto nsl) {
+        constexpr int NSL = decltype(nsl)::value;
+        uint32_t khi[NSL], klo[NSL];
+        uint64_t valid[NSL];
+        double sv[NSL];  // the staging area holds CHAIN_SELECT_MAX_NC scores: read all, mask later
 #pragma unroll
-      for (int i = 0; i < NSL; ++i) sv[i] = scL[WAVE * i + lane];
-#pragma unroll
-      for (int i = 0; i < NSL; ++i) {
-        const int c = WAVE * i + lane;
-        const uint64_t key = c < n_c ? f64_order_key(sv[i]) : 0ull;
-        khi[i] = (uint32_t)(key >> 32);
-        klo[i] = (uint32_t)key;
-        valid[i] = __ballot(c < n_c);
-      }
-      const int k = a.k_eff;
-      // count of chunks with top half >= x (slots past n_c have no valid lanes),
-      // summed as a tree
-      auto count_hi = [&](uint32_t x) {
-        int c8[NSL];
-#pragma unroll
-        for (int i = 0; i < NSL; ++i) c8[i] = __popcll(__ballot(khi[i] >= x) & valid[i]);
-#pragma unroll
-        for (int n = NSL / 2; n > 0; n /= 2)
-#pragma unroll
-          for (int i = 0; i < n; ++i) c8[i] += c8[i + n];
-        return c8[0];
-      };
-      // the k-th largest top half, highest bit first; stops as soon as exactly
-      // k chunks lie at or above the bits fixed so far (further low bits could
-      // only drop chunks below k)
-      uint32_t th = 0u;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = th | (1u << bit);
-        const int cnt = count_hi(cand);
-        if (cnt >= k) th = cand;
-        if (cnt == k) break;
-      }
-      uint64_t eq_hi[NSL], sel[NSL];
-      int n_gt = 0, n_eq = 0;
-#pragma unroll
-      for (int i = 0; i < NSL; ++i) {
-        sel[i] = __ballot(khi[i] > th) & valid[i];
-        eq_hi[i] = __ballot(khi[i] == th) & valid[i];
-        n_gt += __popcll(sel[i]);
-        n_eq += __popcll(eq_hi[i]);
-      }
-      if (n_gt + n_eq == k) {  // the threshold's top half is shared by exactly the missing chunks
-#pragma unroll
-        for (int i = 0; i < NSL; ++i) sel[i] |= eq_hi[i];
-      } else {  // more chunks share that top half than are missing: decide on the low halves
-        const int need = k - n_gt;
-        auto count_lo = [&](uint32_t x) {
-          int cnt = 0;
-#pragma unroll
-          for (int i = 0; i < NSL; ++i) cnt += __popcll(__ballot(klo[i] >= x) & eq_hi[i]);
-          return cnt;
-        };
-        uint32_t tl = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-          const uint32_t cand = tl | (1u << bit);
-          const int cnt = count_lo(cand);
-          if (cnt >= need) tl = cand;
-          if (cnt == need) break;
-        }
-        int rem = need;
-        uint64_t eq[NSL];
+        for (int i = 0; i < NSL; ++i) sv[i] = scL[WAVE * i + lane];
 #pragma unroll
         for (int i = 0; i < NSL; ++i) {
-          const uint64_t gt = __ballot(klo[i] > tl) & eq_hi[i];
-          sel[i] |= gt;
-          rem -= __popcll(gt);
-          eq[i] = __ballot(klo[i] == tl) & eq_hi[i];
+          const int c = WAVE * i + lane;
+          const uint64_t key = c < n_c ? f64_order_key(sv[i]) : 0ull;
+          khi[i] = (uint32_t)(key >> 32);
+          klo[i] = (uint32_t)key;
+          valid[i] = __ballot(c < n_c);
         }
+        const int k = a.k_eff;
+        // count of chunks with top half >= x (slots past n_c have no valid lanes),
+        // summed as a tree
+        auto count_hi = [&](uint32_t x) {
+          int c8[NSL];
 #pragma unroll
-        for (int i = 0; i < NSL; ++i) {  // equal keys: lowest chunk index first
-          uint64_t e = eq[i];
-          while (rem > 0 && e) {
-            const uint64_t low = e & (~e + 1ull);
-            sel[i] |= low;
-            e ^= low;
-            --rem;
+          for (int i = 0; i < NSL; ++i) c8[i] = __popcll(__ballot(khi[i] >= x) & valid[i]);
+#pragma unroll
+          for (int n = NSL / 2; n > 0; n /= 2)
+#pragma unroll
+            for (int i = 0; i < n; ++i) c8[i] += c8[i + n];
+          return c8[0];
+        };
+        // the k-th largest top half, highest bit first; stops as soon as exactly
+        // k chunks lie at or above the bits fixed so far (further low bits could
+        // only drop chunks below k).  The threshold is kept wave-uniform.
+        uint32_t th = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = __builtin_amdgcn_readfirstlane(th | (1u << bit));
+          const int cnt = count_hi(cand);
+          if (cnt >= k) th = cand;
+          if (cnt == k) break;
+        }
+        uint64_t eq_hi[NSL], sel[NSL];
+        int n_gt = 0, n_eq = 0;
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) {
+          sel[i] = __ballot(khi[i] > th) & valid[i];
+          eq_hi[i] = __ballot(khi[i] == th) & valid[i];
+          n_gt += __popcll(sel[i]);
+          n_eq += __popcll(eq_hi[i]);
+        }
+        if (n_gt + n_eq == k) {  // the threshold's top half is shared by exactly the missing chunks
+#pragma unroll
+          for (int i = 0; i < NSL; ++i) sel[i] |= eq_hi[i];
+        } else {  // more chunks share that top half than are missing: decide on the low halves
+          const int need = k - n_gt;
+          auto count_lo = [&](uint32_t x) {
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < NSL; ++i) cnt += __popcll(__ballot(klo[i] >= x) & eq_hi[i]);
+            return cnt;
+          };
+          uint32_t tl = 0u;
+          for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = __builtin_amdgcn_readfirstlane(tl | (1u << bit));
+            const int cnt = count_lo(cand);
+            if (cnt >= need) tl = cand;
+            if (cnt == need) break;
+          }
+          int rem = need;
+          uint64_t eq[NSL];
+#pragma unroll
+          for (int i = 0; i < NSL; ++i) {
+            const uint64_t gt = __ballot(klo[i] > tl) & eq_hi[i];
+            sel[i] |= gt;
+            rem -= __popcll(gt);
+            eq[i] = __ballot(klo[i] == tl) & eq_hi[i];
+          }
+#pragma unroll
+          for (int i = 0; i < NSL; ++i) {  // equal keys: lowest chunk index first
+            uint64_t e = eq[i];
+            while (rem > 0 && e) {
+              const uint64_t low = e & (~e + 1ull);
+              sel[i] |= low;
+              e ^= low;
+              --rem;
+            }
           }
         }
-      }
-      int base = 0;
+        int base = 0;
 #pragma unroll
-      for (int i = 0; i < NSL; ++i) {
-        if ((sel[i] >> lane) & 1ull) {
-          const int pos = base + __popcll(sel[i] & lanemask_lt()), c = WAVE * i + lane;
-          if (pos >= q0 && pos < q0 + MAXSLOT) selL[pos - q0] = c;
-          if constexpr (REUSE) reinterpret_cast<int32_t *>(sm + S::SELALL)[pos] = c;
-          if (s == 0 && a.sel_out) a.sel_out[((long)b * a.Hkv + h) * a.k_eff + pos] = c;
+        for (int i = 0; i < NSL; ++i) {
+          if ((sel[i] >> lane) & 1ull) {
+            const int pos = base + __popcll(sel[i] & lanemask_lt()), c = WAVE * i + lane;
+            if (pos >= q0 && pos < q0 + MAXSLOT) selL[pos - q0] = c;
+            if constexpr (REUSE) reinterpret_cast<int32_t *>(sm + S::SELALL)[pos] = c;
+            if (s == 0 && a.sel_out) a.sel_out[((long)b * a.Hkv + h) * a.k_eff + pos] = c;
+          }
+          base += __popcll(sel[i]);
         }
-        base += __popcll(sel[i]);
-      }
+      };
+      static_assert(CHAIN_SELECT_MAX_NC % (4 * WAVE) == 0, "slot counts");
+      if (n_c <= 4 * WAVE)
+        select_wave(std::integral_constant<int, 4>{});
+      else
+        select_wave(std::integral_constant<int, CHAIN_SELECT_MAX_NC / WAVE>{});
     } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
       selL[tid] = selv;
     }

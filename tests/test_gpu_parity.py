@@ -218,8 +218,10 @@ def test_dense_comparator_matches_oracle(run):
 # ---------------------------------------------------------------------------
 # special shapes
 # ---------------------------------------------------------------------------
-def _roundtrip(s, top_k):
+def _roundtrip(s, top_k, edit=None):
     inp = gen.make(s)
+    if edit is not None:
+        edit(inp, s)
     dev = upload(inp)
     d = dims_of(s, top_k=top_k)
     cache = P().alloc_cache(d)
@@ -245,6 +247,10 @@ def _roundtrip(s, top_k):
     ("nc-2048-unfused", TINY.replace(N=131072, T=8), 11),
     ("rank-1024", small(LLAMA8B_32K, B=1, N=1024, r=1024, T=16), 3),
     ("rank-2048", small(LLAMA8B_32K, B=1, N=1024, r=2048, T=16), 3),
+    # the chained kernel's own top-k with eight key slots per lane (256 < n_c <= 512),
+    # a ragged last slot and a full one
+    ("chain-nc-320", small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=40960, T=16), 9),
+    ("chain-nc-512", small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=65536, T=16), 9),
 ])
 def test_special_shapes(name, shape, top_k):
     if not torch.cuda.is_available():
@@ -256,3 +262,41 @@ def test_special_shapes(name, shape, top_k):
     assert ok, worst
     if shape.rho == 1.0:
         assert np.array_equal(host["res_idx"][0, 0, 0], np.arange(shape.N))
+
+
+# ---------------------------------------------------------------------------
+# equal chunk scores: the selection takes the lower chunk index first
+# ---------------------------------------------------------------------------
+def _copy_chunks(src_of):
+    """An input edit that makes chunk j's keys and values those of chunk
+    src_of(j), so their coefficients, landmarks and scores are equal."""
+    def edit(inp, s):
+        for name in ("k", "v"):
+            x = inp[name]
+            for j in range(s.N // s.C):
+                i = src_of(j)
+                if i != j:
+                    x[:, :, :, j * s.C:(j + 1) * s.C] = x[:, :, :, i * s.C:(i + 1) * s.C]
+    return edit
+
+
+@pytest.mark.parametrize("name,shape,top_k,src_of", [
+    # pairs of equal chunks, an odd k splits the pair at the threshold
+    ("pairs", small(LLAMA8B_32K, B=1, N=2048, T=16), 5, lambda j: j - j % 2),
+    # every chunk equal: the first k chunks
+    ("all-equal", small(LLAMA8B_32K, B=1, N=2048, T=16), 6, lambda j: 0),
+    # runs of three equal chunks over 320 chunks (eight key slots per lane)
+    ("triples-nc-320", small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=40960, T=16), 10, lambda j: j - j % 3),
+])
+def test_selection_ties(name, shape, top_k, src_of):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"\n[case] ties {name}: {shape}", flush=True)
+    out, sel, ref, rsel, host, inp = _roundtrip(shape, top_k, edit=_copy_chunks(src_of))
+    lm = host["landmark"][0]
+    assert any(np.array_equal(lm[j], lm[src_of(j)]) for j in range(1, lm.shape[0]) if src_of(j) != j)
+    assert np.array_equal(sel, rsel)
+    if name == "all-equal":
+        assert np.array_equal(sel[0, 0], np.arange(top_k))
+    ok, worst = within_tol(out, ref)
+    assert ok, worst
