@@ -587,12 +587,12 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
           valid[i] = __ballot(c < n_c);
         }
         const int k = a.k_eff;
-        // count of chunks with top half >= x (slots past n_c have no valid lanes),
-        // summed as a tree
+        // count of chunks with top half >= x, summed as a tree.  Lanes past n_c
+        // hold key 0 and every x searched below is at least 1, so they never count.
         auto count_hi = [&](uint32_t x) {
           int c8[NSL];
 #pragma unroll
-          for (int i = 0; i < NSL; ++i) c8[i] = __popcll(__ballot(khi[i] >= x) & valid[i]);
+          for (int i = 0; i < NSL; ++i) c8[i] = __popcll(__ballot(khi[i] >= x));
 #pragma unroll
           for (int n = NSL / 2; n > 0; n /= 2)
 #pragma unroll
@@ -601,10 +601,10 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
         };
         // the k-th largest top half, highest bit first; stops as soon as exactly
         // k chunks lie at or above the bits fixed so far (further low bits could
-        // only drop chunks below k).  The threshold is kept wave-uniform.
+        // only drop chunks below k)
         uint32_t th = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-          const uint32_t cand = __builtin_amdgcn_readfirstlane(th | (1u << bit));
+        for (uint32_t m = 0x80000000u; m != 0u; m >>= 1) {
+          const uint32_t cand = th | m;
           const int cnt = count_hi(cand);
           if (cnt >= k) th = cand;
           if (cnt == k) break;
@@ -630,8 +630,8 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
             return cnt;
           };
           uint32_t tl = 0u;
-          for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = __builtin_amdgcn_readfirstlane(tl | (1u << bit));
+          for (uint32_t m = 0x80000000u; m != 0u; m >>= 1) {
+            const uint32_t cand = tl | m;
             const int cnt = count_lo(cand);
             if (cnt >= need) tl = cand;
             if (cnt == need) break;
