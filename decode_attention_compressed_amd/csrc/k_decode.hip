@@ -227,12 +227,14 @@ __global__ __launch_bounds__(TK_NT) void k_topk(const double *__restrict__ score
   }
 }
 
-// grid (Hkv, B), 1024 threads, n_c <= 256: four threads per chunk j each
+// grid (Hkv, B), 1024 threads, n_c <= 256.  A chunk's score is the sum of its
+// NRB rank-block partials in block order (the sum k_select_sum forms), taken
+// here so that no separate launch is needed.  Four threads per chunk j each
 // count, over a quarter of the chunks, those ranked above j (higher score, or
 // equal score and lower index); j is kept iff fewer than k are in total.
 // Positions in the output follow chunk order.
 constexpr int TK_SMALL = 256;
-__global__ __launch_bounds__(TK_NT) void k_topk_small(const double *__restrict__ scores, int Hkv,
+__global__ __launch_bounds__(TK_NT) void k_topk_small(const double *__restrict__ part, int NRB, int Hkv,
                                                       int n_c, int k_eff, int32_t *__restrict__ sel,
                                                       int32_t *__restrict__ sel_out) {
   __shared__ __align__(16) double s[TK_SMALL];
@@ -240,7 +242,15 @@ __global__ __launch_bounds__(TK_NT) void k_topk_small(const double *__restrict__
   __shared__ TopkSmem tk;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int j = tid % TK_SMALL, qp = tid / TK_SMALL;
-  if (tid < TK_SMALL) s[tid] = tid < n_c ? scores[((long)b * Hkv + h) * n_c + tid] : -INFINITY;
+  if (tid < TK_SMALL) {
+    double v = -INFINITY;
+    if (tid < n_c) {
+      const double *pp = part + ((long)b * Hkv + h) * NRB * n_c + tid;
+      v = pp[0];
+      for (int rb = 1; rb < NRB; ++rb) v += pp[(long)rb * n_c];
+    }
+    s[tid] = v;
+  }
   __syncthreads();
   const double mine = s[j];
   int above = 0;
@@ -701,18 +711,18 @@ hipError_t launch_select(int act, const void *q, long q_bstride, const void *bas
   else
     launch_partial<bf16>((const bf16 *)q, q_bstride, (const bf16 *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, st);
   if (!scores) return k_eff > 0 ? hipErrorInvalidValue : hipGetLastError();
+  if (k_eff > 0 && n_c <= TK_SMALL) {  // sums the partials itself
+    hipLaunchKernelGGL(k_topk_small, dim3(Hkv, B), dim3(TK_NT), 0, st, part, select_rank_blocks(r), Hkv,
+                       n_c, k_eff, sel, sel_out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_select_sum, dim3((n_c + 255) / 256, Hkv, B), dim3(256), 0, st, part, Hkv, n_c,
                      select_rank_blocks(r), scores);
   if (k_eff > 0) {
-    if (n_c <= TK_SMALL) {
-      hipLaunchKernelGGL(k_topk_small, dim3(Hkv, B), dim3(TK_NT), 0, st, scores, Hkv, n_c, k_eff,
-                         sel, sel_out);
-    } else {
-      const size_t sm3 = (size_t)n_c * 8 + sizeof(int32_t) * (size_t)k_eff;
-      allow_dynamic_lds(k_topk, sm3);
-      hipLaunchKernelGGL(k_topk, dim3(Hkv, B), dim3(TK_NT), sm3, st, scores, Hkv, n_c, k_eff, sel,
-                         sel_out);
-    }
+    const size_t sm3 = (size_t)n_c * 8 + sizeof(int32_t) * (size_t)k_eff;
+    allow_dynamic_lds(k_topk, sm3);
+    hipLaunchKernelGGL(k_topk, dim3(Hkv, B), dim3(TK_NT), sm3, st, scores, Hkv, n_c, k_eff, sel,
+                       sel_out);
   }
   return hipGetLastError();
 }
@@ -756,20 +766,20 @@ hipError_t launch_attend_valu(int act, int coeff, int resid, const AttendArgs &a
 }
 
 // ---------------------------------------------------------------------------
-// D7 for d_h = 128, bf16, at most 4 query heads per kv head and F a multiple
-// of 128: one workgroup per (sequence, kv head, quarter of the head dims)
-// merges the splits of all query heads of the kv head and applies the rows of
-// W2 it owns.  Every global read is issued before the first is used (split
+// D7 for d_h = 128 or 256, bf16, at most 4 query heads per kv head and F a
+// multiple of 128: one workgroup per (sequence, kv head, 32 head dims) merges
+// the splits of all query heads of the kv head and applies the rows of W2 it
+// owns.  Every global read is issued before the first is used (split
 // heads, hidden sums, value sums, W2 rows and b2): one memory round trip.
 // Sums run in split order, so the result is deterministic.
-// grid (4, Hkv, B), 256 threads.
+// grid (d_h / 32, Hkv, B), 256 threads.
 // ---------------------------------------------------------------------------
 constexpr int KV_DQ = 32;    // head dims per workgroup
 constexpr int KV_SB = 16;    // splits whose loads are in flight together
 
-template <int F>
+template <int F, int DH>
 __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
-  constexpr int DH = 128, GM = 4, FP = F / 4;       // float4 pieces of a hidden row
+  constexpr int GM = 4, FP = F / 4;                   // float4 pieces of a hidden row
   constexpr int PPT = (GM * FP + 255) / 256;          // (g, piece) pairs per thread
   constexpr int WPT = F / 8 / 8;                      // 16-byte W2 pieces per thread (8 threads per row)
   __shared__ float hd[64][GM][3];                     // split heads m, l, mass
@@ -902,11 +912,17 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
 }
 
 hipError_t launch_combine(int act, const CombineArgs &a, hipStream_t st) {
-  if (act == LOWRAM_BF16 && a.F > 0 && a.n_comp > 0 && a.dh == 128 && a.g <= 4 && a.n_total <= 64) {
-    const dim3 grid(128 / KV_DQ, a.Hkv, a.B);
-    if (a.F == 128) { hipLaunchKernelGGL(k_combine_kv<128>, grid, dim3(256), 0, st, a); return hipGetLastError(); }
-    if (a.F == 256) { hipLaunchKernelGGL(k_combine_kv<256>, grid, dim3(256), 0, st, a); return hipGetLastError(); }
-    if (a.F == 512) { hipLaunchKernelGGL(k_combine_kv<512>, grid, dim3(256), 0, st, a); return hipGetLastError(); }
+  if (act == LOWRAM_BF16 && a.F > 0 && a.n_comp > 0 && (a.dh == 128 || a.dh == 256) && a.g <= 4 &&
+      a.n_total <= 64) {
+    const dim3 grid(a.dh / KV_DQ, a.Hkv, a.B);
+#define LOWRAM_COMBINE_KV(FF, DD)                                                   \
+    if (a.F == FF && a.dh == DD) {                                                  \
+      hipLaunchKernelGGL((k_combine_kv<FF, DD>), grid, dim3(256), 0, st, a);        \
+      return hipGetLastError();                                                     \
+    }
+    LOWRAM_COMBINE_KV(128, 128) LOWRAM_COMBINE_KV(256, 128) LOWRAM_COMBINE_KV(512, 128)
+    LOWRAM_COMBINE_KV(128, 256) LOWRAM_COMBINE_KV(256, 256) LOWRAM_COMBINE_KV(512, 256)
+#undef LOWRAM_COMBINE_KV
   }
   // stage: CB * sub splits of (F + dh) floats, sub = 256 / (piece stride) <= 1024 / (F + dh)
   const int n_out = a.F + a.dh, per = n_out / 4;
