@@ -49,14 +49,16 @@ __device__ inline void softmax_tile(float *lg, int ld, int nt, int g, float *ms,
 }
 
 // ---------------------------------------------------------------------------
-// Uncompressed tail of one (b, h): dense softmax over T tokens (shared by the
-// VALU and MFMA kernels).  qs[g][dh] floats already loaded; lg scratch
-// [g][TT]; accV [g][dh]; ms/ls/al [g]; kv scratch of 2*TT*(dh+1) floats where
-// each tile's keys and values are staged with 16-byte loads.
+// Uncompressed tail of one (b, h): dense softmax over tail tokens [t_begin,
+// t_end) (shared by the VALU and MFMA kernels).  qs[g][dh] floats already
+// loaded; lg scratch [g][TT]; accV [g][dh]; ms/ls/al [g]; kv scratch of
+// 2*TT*(dh+1) floats where each tile's keys and values are staged with 16-byte
+// loads.
 // ---------------------------------------------------------------------------
 template <typename TA>
 __device__ void tail_split(const AttendArgs &a, int h, int b, const float *qs, float *lg, int TT,
-                           float *accV, float *ms, float *ls, float *al, float *kv) {
+                           float *accV, float *ms, float *ls, float *al, float *kv, int t_begin,
+                           int t_end) {
   const int tid = threadIdx.x;
   const int g = a.g, dh = a.dh, ld = dh + 1;
   const long base = ((((long)b * a.G + a.layer) * a.Hkv + h) * a.T) * dh;
@@ -64,8 +66,8 @@ __device__ void tail_split(const AttendArgs &a, int h, int b, const float *qs, f
   const TA *vt = reinterpret_cast<const TA *>(a.v_tail) + base;
   float *ks = kv, *vs = kv + TT * ld;
   constexpr int PER = 16 / sizeof(TA);  // elements per 16-byte piece
-  for (int t0 = 0; t0 < a.T; t0 += TT) {
-    const int nt = min(TT, a.T - t0);
+  for (int t0 = t_begin; t0 < t_end; t0 += TT) {
+    const int nt = min(TT, t_end - t0);
     for (int pc = tid; pc < nt * dh / PER; pc += 256) {
       const int t = pc / (dh / PER), d0 = (pc % (dh / PER)) * PER;
       const u32x4 kr = gld16(kt + (long)(t0 + t) * dh + d0);

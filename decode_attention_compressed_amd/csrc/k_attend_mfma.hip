@@ -1,7 +1,9 @@
 // Fused rebuild-and-attend on gfx950 matrix cores (bf16/fp16 MFMA, fp32 accumulate).
 //
-// One workgroup (4 waves) owns one (sequence b, kv head h) and a run of the
-// chunks selected for it.  For each 128-token tile of a selected chunk:
+// One workgroup (4 waves) owns one (sequence b, kv head h), a run of the
+// chunks selected for it and an equal share of the uncompressed tail (on the
+// vector ALUs after the chunks, merged into the same partial).  For each
+// 128-token tile of a selected chunk:
 //   1. K_hat^T[dh][128] = U_{l,h}[dh][r] . deq(coeff tile)^T  (32x32x16 MFMA).
 //      Rank slabs of 64 are staged through LDS while the next slab is already
 //      in flight in registers.  bf16 coefficients and basis enter as stored;
@@ -221,16 +223,18 @@ template <> struct ResRow<int8_t> {
 // remapped so that every split of one (sequence, kv head) lands on the same
 // XCD, next to the other heads of that sequence: the head's basis slice and
 // first predictor layer then stay L2-resident, and chunks picked by several
-// heads of a sequence are fetched once per XCD.  Tail splits are dispatched
-// first so that they overlap the rebuild work instead of trailing it.
+// heads of a sequence are fetched once per XCD.  Every split also attends its
+// share of the tail, so the grid holds no tail-only workgroups (which would
+// exceed one workgroup per CU at B Hkv n_split = 256); with no chunk selected
+// there is one tail workgroup per (sequence, kv head), split 0 = n_split.
 __device__ __forceinline__ void block_coords(const AttendArgs &a, int &h, int &b, int &split) {
   const int S = a.n_split, BH = a.B * a.Hkv;
-  if ((int)blockIdx.x < BH) {  // tail splits
+  if (S == 0) {
     const int bh = blockIdx.x;
-    b = bh / a.Hkv; h = bh % a.Hkv; split = S;
+    b = bh / a.Hkv; h = bh % a.Hkv; split = 0;
     return;
   }
-  const int lin = blockIdx.x - BH;
+  const int lin = blockIdx.x;
   int bh;
   if (BH % 8 == 0) {
     const int xcd = lin % 8, i = lin / 8;
@@ -267,17 +271,18 @@ __global__ __launch_bounds__(256, (dual_occupancy<DH, NF64>() ? 2 : 1)) void k_a
   const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int g = a.g, r = a.r, C = a.C;
   constexpr int TAIL_TT = tail_tile<DH>();
-  static_assert((2 * 16 * DH + 16 * TAIL_TT + 48 + 2 * TAIL_TT * (DH + 1)) * 4 <= S::BYTES,
+  // the tail scratch ends below the float area (m, l, alpha of the rebuilt tokens)
+  static_assert((2 * 16 * DH + 16 * TAIL_TT + 48 + 2 * TAIL_TT * (DH + 1)) * 4 <= S::END16 * 2,
                 "tail split does not fit the LDS of the rebuild kernel");
 
-  if (split == a.n_split) {  // uncompressed tail on the vector ALUs
+  if (split == a.n_split) {  // no chunk selected: the whole tail on the vector ALUs
     float *qs = reinterpret_cast<float *>(msm), *accV = qs + g * DH, *lgs = accV + g * DH;
     float *tms = lgs + g * TAIL_TT, *tls = tms + 16, *tal = tls + 16, *kv = tal + 16;
     const bf16 *qb = reinterpret_cast<const bf16 *>(a.q) + ((long)b * a.Hq + (long)h * g) * DH;
     for (int i = tid; i < g * DH; i += 256) { qs[i] = to_f32(qb[i]); accV[i] = 0.f; }
     if (tid < 16) { tms[tid] = -INFINITY; tls[tid] = 0.f; tal[tid] = 0.f; }
     __syncthreads();
-    tail_split<bf16>(a, h, b, qs, lgs, TAIL_TT, accV, tms, tls, tal, kv);
+    tail_split<bf16>(a, h, b, qs, lgs, TAIL_TT, accV, tms, tls, tal, kv, 0, a.T);
     write_partial(a, h, b, split, tms, tls, nullptr, accV);
     return;
   }
@@ -579,17 +584,51 @@ __global__ __launch_bounds__(256, (dual_occupancy<DH, NF64>() ? 2 : 1)) void k_a
     }
   }
 
+  // ---- this split's share of the tail, on the vector ALUs ----------------------
+  // Tokens [tb, te) of the T tail tokens; the LDS below the float area is free
+  // once the last tile is done.  Its own softmax state (m, l, accV over the
+  // tail tokens) is merged with the rebuilt tokens' below.
+  const int tshare = (a.T + a.n_split - 1) / a.n_split;
+  const int tb = min(a.T, split * tshare), te = min(a.T, tb + tshare);
+  float *qt = reinterpret_cast<float *>(msm), *accVt = qt + g * DH, *lgt = accVt + g * DH;
+  float *tms = lgt + g * TAIL_TT, *tls = tms + 16, *tal = tls + 16, *kvt = tal + 16;
+  {
+    const bf16 *qb = reinterpret_cast<const bf16 *>(a.q) + ((long)b * a.Hq + (long)h * g) * DH;
+    for (int i = tid; i < g * DH; i += 256) { qt[i] = to_f32(qb[i]); accVt[i] = 0.f; }
+    if (tid < 16) { tms[tid] = -INFINITY; tls[tid] = 0.f; tal[tid] = 0.f; }
+    __syncthreads();
+    tail_split<bf16>(a, h, b, qt, lgt, TAIL_TT, accVt, tms, tls, tal, kvt, tb, te);
+  }
+  // merge weights: rebuilt tokens 2^(m_c - M), tail tokens 2^(m_t - M)
+  float *wc = red, *wt = red + 16;
+  if (tid < g) {
+    const float mc = ms[tid], mt = tms[tid], M = fmaxf(mc, mt);
+    wc[tid] = mc == -INFINITY ? 0.f : exp2f(mc - M);
+    wt[tid] = mt == -INFINITY ? 0.f : exp2f(mt - M);
+  }
+  __syncthreads();
+
   // ---- partials ---------------------------------------------------------------
-  float *p = a.part + (((long)b * a.Hkv + h) * (a.n_split + 1) + split) * g * a.PW;
-  if (tid < g) { p[tid * a.PW] = ms[tid]; p[tid * a.PW + 1] = ls[tid]; p[tid * a.PW + 2] = ls[tid]; p[tid * a.PW + 3] = 0.f; }
+  float *p = a.part + (((long)b * a.Hkv + h) * a.n_split + split) * g * a.PW;
+  if (tid < g) {
+    const float lc = wc[tid] * ls[tid];
+    p[tid * a.PW] = fmaxf(ms[tid], tms[tid]);
+    p[tid * a.PW + 1] = fmaf(wt[tid], tls[tid], lc);
+    p[tid * a.PW + 2] = lc;
+    p[tid * a.PW + 3] = 0.f;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int gq = 4 * (lane >> 4) + i;
     if (gq < g) {
+      const float c = wc[gq], u = wt[gq];
 #pragma unroll
-      for (int fb = 0; fb < NF64; ++fb) p[gq * a.PW + 4 + fb * 64 + 16 * w + (lane & 15)] = accH[fb][i];
+      for (int fb = 0; fb < NF64; ++fb) p[gq * a.PW + 4 + fb * 64 + 16 * w + (lane & 15)] = c * accH[fb][i];
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) p[gq * a.PW + 4 + a.F + 16 * (w * NVT + vt) + (lane & 15)] = accV[vt][i];
+      for (int vt = 0; vt < NVT; ++vt) {
+        const int d = 16 * (w * NVT + vt) + (lane & 15);
+        p[gq * a.PW + 4 + a.F + d] = fmaf(u, accVt[gq * DH + d], c * accV[vt][i]);
+      }
     }
   }
 }
@@ -601,7 +640,7 @@ static hipError_t go(const AttendArgs &a, hipStream_t st) {
   const size_t smem = MfmaSmem<DH>::BYTES;
   static const bool lds_ok = (allow_dynamic_lds(k_attend_mfma<DH, NF64, NSLAB, TC, TR>, smem), true);
   (void)lds_ok;
-  hipLaunchKernelGGL((k_attend_mfma<DH, NF64, NSLAB, TC, TR>), dim3((a.n_split + 1) * a.Hkv * a.B),
+  hipLaunchKernelGGL((k_attend_mfma<DH, NF64, NSLAB, TC, TR>), dim3((a.n_split > 0 ? a.n_split : 1) * a.Hkv * a.B),
                      dim3(256), smem, st, a);
   return hipGetLastError();
 }

@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
   __syncthreads();
 
   if (split == a.n_split) {
-    tail_split<TA>(a, h, b, qs, lg, TT, accV, ms, ls, al, cb);
+    tail_split<TA>(a, h, b, qs, lg, TT, accV, ms, ls, al, cb, 0, a.T);
     write_partial(a, h, b, split, ms, ls, nullptr, accV);
     return;
   }

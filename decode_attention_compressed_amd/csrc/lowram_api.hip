@@ -73,9 +73,9 @@ lowram_status check_dims(const lowram_dims *d) {
   return LOWRAM_OK;
 }
 
-// Decode workspace plan.  The register-chained attend kernel folds the tail
-// into its n_split partials per (b, h); the other attend kernels write one
-// partial per selected chunk plus one for the tail.
+// Decode workspace plan.  The register-chained and matrix-core attend kernels
+// fold the tail into their n_split partials per (b, h); the vector kernel
+// writes one partial per selected chunk plus one for the tail.
 struct DecodePlan {
   int k_eff, cps, n_split, n_part, PW, tps, tail_per_split;
   size_t sel_off, sp_off, sc_off, part_off, bytes;
@@ -94,7 +94,15 @@ DecodePlan decode_plan(const lowram_dims *d) {
     p.n_part = p.n_split;
   } else {
     p.n_split = p.k_eff > 0 ? (p.k_eff + p.cps - 1) / p.cps : 0;
-    p.n_part = p.n_split + 1;
+    // the matrix-core kernel folds the tail into its splits (one tail partial
+    // when nothing is selected); the vector kernel writes it separately
+    AttendArgs t;
+    memset(&t, 0, sizeof t);
+    t.C = d->chunk; t.g = g; t.dh = d->head_dim; t.F = d->hidden; t.r = d->rank;
+    if (mfma_supported(t, d->act, d->coeff, d->resid))
+      p.n_part = p.n_split > 0 ? p.n_split : 1;
+    else
+      p.n_part = p.n_split + 1;
   }
   p.PW = 4 + d->hidden + d->head_dim;
   p.sel_off = 0;
