@@ -331,7 +331,10 @@ def main():
     log(f"workload {s.name}: {s}")
     t0 = time.perf_counter()
     n_q = min(64, max(args.steps, 1))
-    inp = gen.make(s, steps=n_q)
+    def gen_progress(done, total):  # large batches take minutes to draw on the host
+        if total >= 16 and (done % 8 == 0 or done == total):
+            log(f"generated {done}/{total} sequences")
+    inp = gen.make(s, steps=n_q, progress=gen_progress)
     log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
     dev = upload(inp)
     d = dims_of(s)

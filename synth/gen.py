@@ -93,8 +93,9 @@ def _mlp_true(x, w1, b1, w2, b2):
 
 
 def make(s: Shape, seed_offset: int = 0, steps: int | None = None, noise_scale: float = 0.1,
-         with_dense: bool = False) -> dict:
-    """Draw one workload.  Returns stored arrays keyed by name.
+         with_dense: bool = False, progress=None) -> dict:
+    """Draw one workload.  Returns stored arrays keyed by name.  `progress`,
+    if given, is called as progress(done, B) after each sequence.
 
     Layouts (row-major):
       k, v            [B][G][Hkv][N][dh]
@@ -159,6 +160,8 @@ def make(s: Shape, seed_offset: int = 0, steps: int | None = None, noise_scale: 
                 out["v"][b, l, h] = store(vals[:N], act)
                 out["v_tail"][b, l, h] = store(vals[N:], act)
         del kcat, kfull
+        if progress is not None:
+            progress(b + 1, B)
 
     out["q"] = make_queries(s, steps, seed_offset)
     if s.n_obs:
