@@ -884,17 +884,22 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     };
 
     // reuse: the slot code of this tile's chunk (wave-uniform; read again after
-    // step 1 so that nothing of it stays live there); a workgroup whose tiles
-    // all hit skips step 1 and reads its rebuilt keys back
+    // step 1 so that nothing of it stays live there).  A wave whose tile hits
+    // skips its step-1 products and coefficient loads and reads its rebuilt keys
+    // back; the basis slabs are shared, so only a workgroup whose tiles all hit
+    // skips their loads too.
     auto slot_code = [&]() -> int {
       return has ? reinterpret_cast<const int32_t *>(sm + S::RCODE)[tau / cpt - q0] : -1;
     };
-    bool skip1 = false;
+    bool skip1 = false, skip_all = false;
     if constexpr (REUSE) {
       const int code = slot_code();
-      skip1 = __syncthreads_and(!has || (code >= 0 && (code & REUSE_HIT) != 0));
+      const bool hit = !has || (code >= 0 && (code & REUSE_HIT) != 0);
+      skip1 = __builtin_amdgcn_readfirstlane((int)hit) != 0;
+      skip_all = __syncthreads_and(hit);
     }
-    const uint32_t lskip = skip1 ? 0x80000000u : 0u;  // past every buffer's end
+    const uint32_t lskip = skip1 ? 0x80000000u : 0u;       // past every buffer's end
+    const uint32_t uskip = skip_all ? 0x80000000u : 0u;
 
     // ---- step 1: K_hat^T = U . C^T over NR k-steps ------------------------
     const uint16_t *u_rd = Us + l16 * ULD + 8 * kg;  // lane's basis fragment, head-dim tile 0
@@ -911,12 +916,12 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       // loads so that waiting for it LU - 1 steps later waits for nothing newer
       // than the coefficients then due
       if constexpr (ks + LU < NR)
-        ST::ld(Ur, csc, u_voff, r, (ks + LU) * KS, ur[(ks + LU) % NU], us_[(ks + LU) % NU], lskip);
+        ST::ld(Ur, csc, u_voff, r, (ks + LU) * KS, ur[(ks + LU) % NU], us_[(ks + LU) % NU], uskip);
       // coefficients DC - 1 steps ahead.
       // Every load here is unconditional (a wave without a tile reads out of
-      // range), so the wait counts stay exact across steps; a workgroup whose
-      // tiles are all read back (reuse) points them past the end (zeros, no
-      // memory traffic) and skips the products.
+      // range), so the wait counts stay exact across steps; a wave whose tile
+      // is read back (reuse) points them past the end (zeros, no memory
+      // traffic) and skips the products.
       if constexpr (ks + DC - 1 < NR) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) cr[(ks + DC - 1) % DC][tt] = CT::ld(Cr, c_voff, c_soff(tt, ks + DC - 1) + lskip);
@@ -962,7 +967,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
                 (long)(tau % cpt) * TILE_W;
     }
     f16x8 KA[NJ][NTT];
-    if (skip1) {  // every tile of the workgroup is cached: the operands as stored
+    if (skip1) {  // this wave's tile is cached: the operands as stored
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll

@@ -249,6 +249,10 @@ def _roundtrip(s, top_k, edit=None):
     ("rank-2048", small(LLAMA8B_32K, B=1, N=1024, r=2048, T=16), 3),
     # the chained kernel's own top-k with eight key slots per lane (256 < n_c <= 512),
     # a ragged last slot and a full one
+    # the per-chunk kernel's share of the tail: fewer tail tokens than splits (two
+    # splits get one token, three get none), and one split with a ragged 70-token tail
+    ("mfma-tail-2-of-5", small(QWEN4B_64K, B=1, N=2048, T=2), 5),
+    ("mfma-tail-70-k1", small(QWEN4B_64K, B=1, N=1024, T=70), 1),
     ("chain-nc-320", small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=40960, T=16), 9),
     ("chain-nc-512", small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=65536, T=16), 9),
 ])
