@@ -27,8 +27,10 @@ namespace lowram {
 // reads in flight together):
 //   k_select_partial q~_{b,h} = U_{l,h}^T sum_{g in group(h)} q_g, and the
 //                    partial scores q~ . landmark_{b,j} of one rank block  (float64)
-//   k_select_sum     s_{b,h,j}: the blocks' partials summed in block order
-//   k_topk           top min(k, n_c) chunks per (b, h) by (s desc, j asc), ascending
+//   k_topk_small     n_c <= 256: s_{b,h,j}, the blocks' partials summed in block
+//                    order, and the top min(k, n_c) chunks per (b, h) by
+//                    (s desc, j asc), ascending
+//   k_select_sum     n_c > 256: s_{b,h,j} as above, then k_topk selects
 // Every score is reduced in the same fixed order (lane partials, then a
 // butterfly), so equal landmark rows give equal scores.
 // ---------------------------------------------------------------------------
