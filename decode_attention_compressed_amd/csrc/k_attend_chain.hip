@@ -467,45 +467,25 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   auto c_soff = [&](int tt, int q) -> uint32_t {  // scalar offset of k-step q of token tile tt
     return (uint32_t)(((row0 + 16 * tt) * r + q * KS) * CT::ES);
   };
-  // the selection inputs are read first: everything below waits on them
+  // the selection inputs are read first.  A chunk's score is its rank blocks'
+  // partials summed in block order; the sum is taken only after every other
+  // prologue load is issued, so that their round trips overlap.
   static_assert(CHAIN_SELECT_MAX_NC <= NTH, "one chunk score per thread");
   const int n_c = a.N / C;
-  double scv = 0.0;
+  constexpr int NRB = NR * KS / 64;
+  static_assert(NR * KS % 64 == 0, "whole rank blocks");
+  double spv[NRB];
+#pragma unroll
+  for (int k = 0; k < NRB; ++k) spv[k] = 0.0;
   int selv = 0;
-  if (a.score_part) {  // a chunk's score: its rank blocks' partials summed in block order
-    constexpr int NRB = NR * KS / 64;
-    static_assert(NR * KS % 64 == 0, "whole rank blocks");
+  if (a.score_part) {
     if (tid < n_c) {
       const double *sp = a.score_part + ((long)b * a.Hkv + h) * NRB * n_c + tid;
-      double pv[NRB];
 #pragma unroll
-      for (int k = 0; k < NRB; ++k) pv[k] = sp[(long)k * n_c];
-      scv = pv[0];
-#pragma unroll
-      for (int k = 1; k < NRB; ++k) scv += pv[k];
+      for (int k = 0; k < NRB; ++k) spv[k] = sp[(long)k * n_c];
     }
   } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
     selv = selp[q0 + tid];
-  }
-  u32x4 ur[NU][SP], us_[NU];
-#pragma unroll
-  for (int k = 0; k < NU; ++k) {
-#pragma unroll
-    for (int i = 0; i < SP; ++i) ur[k][i] = v4(0, 0, 0, 0);
-    us_[k] = v4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int q = 0; q < LU; ++q) ST::ld(Ur, csc, u_voff, r, q * KS, ur[q % NU], us_[q % NU]);
-  // W1 is read and converted by waves 1..NW-1 while wave 0 selects
-  constexpr int W1N = F * DH / 8;                             // 16-byte W1 pieces
-  constexpr int W1T = NTH - WAVE;                             // threads of waves 1..NW-1
-  constexpr int W1P = (W1N + W1T - 1) / W1T;                  // pieces per such thread
-  const int tw = tid - WAVE;
-  u32x4 w1r[W1P];
-#pragma unroll
-  for (int k = 0; k < W1P; ++k) {
-    const int p = tw + W1T * k;
-    w1r[k] = (w != 0 && p < W1N) ? gld16(W1 + (long)(p / (DH / 8)) * DH + 8 * (p % (DH / 8))) : v4(0, 0, 0, 0);
   }
   const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + ((long)b * a.Hq + (long)h * g) * DH;
   const u32x4 qraw = tid < g * (DH / 8) ? gld16(qb + 8 * tid) : v4(0, 0, 0, 0);
@@ -528,6 +508,32 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     }
   }
 
+  u32x4 ur[NU][SP], us_[NU];
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+#pragma unroll
+    for (int i = 0; i < SP; ++i) ur[k][i] = v4(0, 0, 0, 0);
+    us_[k] = v4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < LU; ++q) ST::ld(Ur, csc, u_voff, r, q * KS, ur[q % NU], us_[q % NU]);
+  // W1 is read and converted by waves 1..NW-1 while wave 0 selects.  These
+  // loads and the basis slabs' are issued after the scores, q and the tail
+  // rows, which the first barrier waits for: loads complete in issue order, and
+  // the W1 loads are unconditional (wave 0 and spare pieces read past the end:
+  // zeros, no memory traffic) so that the waits before the barrier need not
+  // cover them.
+  constexpr int W1N = F * DH / 8;                             // 16-byte W1 pieces
+  constexpr int W1T = NTH - WAVE;                             // threads of waves 1..NW-1
+  constexpr int W1P = (W1N + W1T - 1) / W1T;                  // pieces per such thread
+  const int tw = tid - WAVE;
+  const rsrc_t W1r = make_rsrc(W1, (uint32_t)(F * DH * 2));
+  u32x4 w1r[W1P];
+#pragma unroll
+  for (int k = 0; k < W1P; ++k) {
+    const int p = tw + W1T * k;  // W1 rows are contiguous: piece p starts at byte 16 p
+    w1r[k] = bld16(W1r, (w != 0 && p < W1N) ? 16u * (uint32_t)p : 0x80000000u, 0u);
+  }
   // q rows of this kv head as fp16 with permuted dims (rows g..15 zero), and the
   // tail rows: both are read while wave 0 selects
   for (int i = tid; i < (16 - g) * (DH / 2); i += NTH)
@@ -565,7 +571,12 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   // threshold (equal doubles) are taken lowest index first.  Split 0 also
   // writes the whole selection to sel_out.  The other waves attend the tail meanwhile.
   double *scL = reinterpret_cast<double *>(sm + S::PS);
-  if (a.score_part && tid < n_c) scL[tid] = scv;
+  if (a.score_part && tid < n_c) {
+    double scv = spv[0];
+#pragma unroll
+    for (int k = 1; k < NRB; ++k) scv += spv[k];
+    scL[tid] = scv;
+  }
   __syncthreads();
   if (w == 0) {
     if (a.score_part) {
