@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from oracle import lowram_oracle as O
-from synth.configs import ALL, COMPOSED_128K, LLAMA8B_32K, TINY
+from synth.configs import ALL, COMPOSED_128K, LLAMA8B_32K, QWEN4B_64K, TINY
 from tests.harness import dims_of
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -281,3 +281,26 @@ def test_decode_kernel_tail_only_and_errors():
     d = dims_of(TINY)
     assert P.decode_kernel(P.with_(d, top_k=0)) == "none"
     assert L.lib().lowram_decode_kernel(ctypes.byref(d), None) == L.E_INVALID
+
+
+def _decode_ws_expected(s, n_part):
+    """Decode workspace of the plan: selection, rank-block partial scores,
+    summed scores, then n_part split partials per (b, h) of g (4 + F + dh) floats."""
+    up = lambda x: (x + 255) // 256 * 256
+    n_c, g, k = s.N // s.C, s.Hq // s.Hkv, min(s.k, s.N // s.C)
+    nrb = (s.r + 63) // 64
+    return (up(4 * s.B * s.Hkv * max(k, 1)) + up(8 * s.B * s.Hkv * nrb * n_c) + up(8 * s.B * s.Hkv * n_c)
+            + up(4 * s.B * s.Hkv * n_part * g * (4 + s.F + s.dh)))
+
+
+def test_decode_workspace_counts_the_partials_of_each_attend_kernel():
+    # qwen4b-64k runs the per-chunk matrix-core kernel: one partial per selected
+    # chunk, each carrying a share of the tail (no separate tail partial)
+    s = QWEN4B_64K
+    assert P.workspace_bytes(dims_of(s), L.OP_DECODE) == _decode_ws_expected(s, s.k)
+    # nothing selected: one tail partial per (b, h)
+    d0 = P.with_(dims_of(s), top_k=0)
+    assert P.workspace_bytes(d0, L.OP_DECODE) == _decode_ws_expected(s.replace(k=0), 1)
+    # tiny-fp32 runs the vector kernel: one partial per chunk plus the tail's
+    s = TINY
+    assert P.workspace_bytes(dims_of(s), L.OP_DECODE) == _decode_ws_expected(s, s.k + 1)
