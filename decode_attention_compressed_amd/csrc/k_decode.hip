@@ -787,7 +787,10 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
   __shared__ float hd[64][GM][3];                     // split heads m, l, mass
   __shared__ float wt[64][GM];                        // split weights
   __shared__ float fin[GM][3];                        // M, 1/L, mass
-  __shared__ __align__(16) float accHm[GM][F];
+  // merged hidden sums; the eighth of a row that one W2 thread reads is padded
+  // by 4 floats, so that the eight eighths fall in different LDS banks
+  constexpr int SEG = F / 8, SPAD = 4;
+  __shared__ __align__(16) float accHm[GM][F + 8 * SPAD];
   __shared__ float accVm[GM][KV_DQ];
   const int dq = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int g = a.g, S = a.n_total;
@@ -879,7 +882,7 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
 #pragma unroll
   for (int k = 0; k < PPT; ++k) {
     const int pr = tid + 256 * k, gi = pr / FP, pc = pr % FP;
-    if (gi < GM) *reinterpret_cast<f32v4 *>(&accHm[gi][4 * pc]) = hacc[k];
+    if (gi < GM) *reinterpret_cast<f32v4 *>(&accHm[gi][4 * pc + (4 * pc / SEG) * SPAD]) = hacc[k];
   }
   __syncthreads();
   // out[gi][d] = (W2[d] . accH[gi] + b2[d] mass[gi] + accV[gi][d]) / L[gi]
@@ -890,8 +893,8 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
     const uint32_t wv[4] = {w2r[i].x, w2r[i].y, w2r[i].z, w2r[i].w};
 #pragma unroll
     for (int gi = 0; gi < GM; ++gi) {
-      const f32v4 h0 = *reinterpret_cast<const f32v4 *>(&accHm[gi][f0]);
-      const f32v4 h1 = *reinterpret_cast<const f32v4 *>(&accHm[gi][f0 + 4]);
+      const f32v4 h0 = *reinterpret_cast<const f32v4 *>(&accHm[gi][f0 + ws * SPAD]);
+      const f32v4 h1 = *reinterpret_cast<const f32v4 *>(&accHm[gi][f0 + ws * SPAD + 4]);
       const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
