@@ -304,10 +304,21 @@ def cpu_baseline(s, host, inp, budget_s):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": s.B * steps / dt, "unit": "seq-steps/s", "cores": int(threads), "kind": "oracle",
-            "cpu_model": model,
-            "sample": f"{steps} full decode step(s) ({s.G} layers x B={s.B}) of the {s.name} workload, "
-                      f"float64 numpy oracle, {dt:.1f} s"}
+    out = {"value": s.B * steps / dt, "unit": "seq-steps/s", "cores": int(threads), "kind": "oracle",
+           "cpu_model": model,
+           "sample": f"{steps} full decode step(s) ({s.G} layers x B={s.B}) of the {s.name} workload, "
+                     f"float64 numpy oracle, {dt:.1f} s"}
+    try:  # the same oracle on one thread: one layer call of the same workload
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            O.decode_layer(host, inp, s, 0, inp["q"][0, 0], s.k, N=s.N_after)
+            d1 = time.perf_counter() - t1
+        out["single_thread"] = {"value": s.B / (s.G * d1), "unit": "seq-steps/s", "cores": 1,
+                                "sample": f"one layer call (B={s.B}), {d1:.2f} s, scaled to a {s.G}-layer step"}
+    except Exception as e:  # pragma: no cover
+        out["single_thread"] = {"value": None, "error": str(e)}
+    return out
 
 
 def main():
@@ -495,7 +506,8 @@ def main():
     if not args.no_cpu:
         host = cache_to_host(cache)
         cpu = cpu_baseline(s, host, inp, args.cpu_seconds)
-        log(f"cpu oracle {cpu['value']:.3f} seq-steps/s on {cpu['cores']} threads")
+        log(f"cpu oracle {cpu['value']:.3f} seq-steps/s on {cpu['cores']} threads, "
+            f"{cpu['single_thread'].get('value') or 0:.3f} on one")
 
     if args.copy_ref_mib:
         src = torch.ones((args.copy_ref_mib << 20) // 4, dtype=torch.float32, device="cuda")
