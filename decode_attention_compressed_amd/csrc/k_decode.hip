@@ -197,14 +197,27 @@ __global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q
 
 // scores[b][h][j] = sum over rank blocks rb (in order) of part[b][h][rb][j].
 // grid (ceil(n_c / 256), Hkv, B), 256 threads.
+// p[0] + p[n] + p[2 n] + ... over NRB rank blocks, added in block order.  The
+// loads go out eight at a time (NRB is a runtime count), so that the sum
+// waits for one round trip per eight blocks rather than one per block.
+__device__ __forceinline__ double sum_rank_blocks(const double *__restrict__ p, int NRB, int n) {
+  double s = 0.0;
+  for (int rb0 = 0; rb0 < NRB; rb0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = rb0 + u < NRB ? p[(long)(rb0 + u) * n] : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (rb0 + u < NRB) s = rb0 + u == 0 ? v[u] : s + v[u];
+  }
+  return s;
+}
+
 __global__ __launch_bounds__(256) void k_select_sum(const double *__restrict__ part, int Hkv, int n_c,
                                                     int NRB, double *__restrict__ scores) {
   const int j = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y, b = blockIdx.z;
   if (j >= n_c) return;
-  const double *p = part + ((long)b * Hkv + h) * NRB * n_c + j;
-  double s = p[0];
-  for (int rb = 1; rb < NRB; ++rb) s += p[(long)rb * n_c];
-  scores[((long)b * Hkv + h) * n_c + j] = s;
+  scores[((long)b * Hkv + h) * n_c + j] = sum_rank_blocks(part + ((long)b * Hkv + h) * NRB * n_c + j, NRB, n_c);
 }
 
 constexpr int TK_NT = 1024;
@@ -244,15 +257,8 @@ __global__ __launch_bounds__(TK_NT) void k_topk_small(const double *__restrict__
   __shared__ TopkSmem tk;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int j = tid % TK_SMALL, qp = tid / TK_SMALL;
-  if (tid < TK_SMALL) {
-    double v = -INFINITY;
-    if (tid < n_c) {
-      const double *pp = part + ((long)b * Hkv + h) * NRB * n_c + tid;
-      v = pp[0];
-      for (int rb = 1; rb < NRB; ++rb) v += pp[(long)rb * n_c];
-    }
-    s[tid] = v;
-  }
+  if (tid < TK_SMALL) s[tid] = tid < n_c ? sum_rank_blocks(part + ((long)b * Hkv + h) * NRB * n_c + tid, NRB, n_c)
+                                         : -INFINITY;
   __syncthreads();
   const double mine = s[j];
   int above = 0;
