@@ -62,7 +62,7 @@ SIGNATURES = {
     "lowram_decode_select": [P(Dims), i32, P(Model), P(Cache), vp, vp, vp, sz, vp],
     "lowram_decode_attend": [P(Dims), i32, P(Model), P(Cache), vp, vp, vp, vp, sz, vp],
     "lowram_decode_combine": [P(Dims), i32, P(Model), vp, vp, sz, vp],
-    "lowram_evict": [P(Dims), P(Model), P(Cache), vp, i32, i32, P(Cache), vp, vp, sz, vp],
+    "lowram_evict": [P(Dims), P(Model), P(Cache), vp, i32, i32, i32, P(Cache), vp, vp, vp, sz, vp],
     "lowram_repack": [P(Dims), P(Model), P(Cache), vp, vp, i32, P(Cache), vp, sz, vp],
     "lowram_fit_predictor": [P(Dims), P(Model), vp, vp, i32, ctypes.c_float, P(Predictor), vp, vp, sz, vp],
     "lowram_key_basis": [P(Dims), vp, i32, vp, vp, sz, vp],

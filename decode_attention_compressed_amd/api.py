@@ -257,25 +257,38 @@ class DecodeCall:
 
 
 def evict(d: L.Dims, model: dict, src: dict, obs_q, keep: int, dst=None, keep_out=None, ws=None,
-          stream=None):
-    """Returns (dst cache, dims of the evicted cache, keep indices)."""
+          stream=None, n_res=None):
+    """Returns (dst cache, dims of the evicted cache, keep indices).
+
+    The evicted cache holds n_res residual rows per (b, layer, kv head).  By
+    default that is the largest number the kept chunks of any head carry: a
+    first library call reports the rows per head (dst NULL), the host reads
+    them (one stream synchronisation, once per context) and the second call
+    fills a cache of that size.  Pass n_res to skip the first call."""
     dt = TORCH_DT[d.act]
     n_obs = 0 if obs_q is None else obs_q.shape[0]
-    d2 = with_(d, n_ctx=keep * d.chunk)
     dev = src["coeff"].device
+    ws = workspace(d, L.OP_EVICT, dev) if ws is None else ws
+    qp = _ptr(obs_q, dt, (n_obs, d.batch, d.layers, d.heads_q, d.head_dim), "obs_q") if n_obs else None
+    keep_out = torch.empty((d.batch, keep), dtype=torch.int32, device=dev) if keep_out is None else keep_out
+    kp = _ptr(keep_out, torch.int32, (d.batch, keep), "keep_out")
+    if n_res is None:
+        live = torch.empty((d.batch, d.layers, d.heads_kv), dtype=torch.int32, device=dev)
+        L.check(L.lib().lowram_evict(ctypes.byref(d), ctypes.byref(model_struct(d, model)),
+                                     ctypes.byref(cache_struct(d, src)), qp, n_obs, keep, 0, None, kp,
+                                     _ptr(live, torch.int32, None, "live"), _ptr(ws, torch.uint8),
+                                     ws.numel(), _stream(stream)))
+        n_res = int(live.max().item())
+    d2 = with_(d, n_ctx=keep * d.chunk, n_res=n_res)
     if dst is None:
         dst = alloc_cache(d2, dev)
         if d.coeff == L.I8:
             dst["coeff_scale"] = src["coeff_scale"]
         if d.resid == L.I8:
             dst["res_scale"] = src["res_scale"]
-    keep_out = torch.empty((d.batch, keep), dtype=torch.int32, device=dev) if keep_out is None else keep_out
-    ws = workspace(d, L.OP_EVICT, dev) if ws is None else ws
-    qp = _ptr(obs_q, dt, (n_obs, d.batch, d.layers, d.heads_q, d.head_dim), "obs_q") if n_obs else None
     L.check(L.lib().lowram_evict(ctypes.byref(d), ctypes.byref(model_struct(d, model)),
-                                 ctypes.byref(cache_struct(d, src)), qp, n_obs, keep,
-                                 ctypes.byref(cache_struct(d2, dst)),
-                                 _ptr(keep_out, torch.int32, (d.batch, keep), "keep_out"),
+                                 ctypes.byref(cache_struct(d, src)), qp, n_obs, keep, n_res,
+                                 ctypes.byref(cache_struct(d2, dst)), kp, None,
                                  _ptr(ws, torch.uint8), ws.numel(), _stream(stream)))
     return dst, d2, keep_out
 

@@ -128,8 +128,10 @@ struct EvictArgs {
   int n_obs, keep;
   const void *coeff; const float *landmark;
   const int32_t *res_ptr, *res_idx; const void *res_val;
-  void *d_coeff; float *d_landmark; int32_t *d_res_ptr, *d_res_idx; void *d_res_val;
+  void *d_coeff; float *d_landmark; int32_t *d_res_ptr, *d_res_idx; void *d_res_val;  // d_coeff null: count only
+  int d_n_res;                  // residual rows per (b, l, h) that dst holds
   int32_t *keep_out;            // [B][keep]
+  int32_t *live_out;            // [B][G][Hkv] residual rows of the kept chunks, or null
   double *spart;                // workspace [B][Hkv][select_rank_blocks(r)][n_c]
   double *scores;               // workspace [B][Hkv][n_c]
   double *acc;                  // workspace [B][n_c]

@@ -391,20 +391,24 @@ __global__ __launch_bounds__(256) void k_evict_copy(const unsigned char *__restr
 }
 
 // rebuild the residual CSR of the kept chunks.  grid (G*Hkv, B), 256 threads.
+// dst holds d_cap rows per (b, l, h): rows past it are not copied and the
+// pointers are clamped to it, so the new CSR never names a row it lacks.
+// live (optional) receives each head's row count before clamping.  With
+// d_ptr null only live is written.
 __global__ __launch_bounds__(256) void k_evict_resid(const int32_t *__restrict__ ptr,
                                                      const int32_t *__restrict__ idx,
                                                      const unsigned char *__restrict__ val,
                                                      const int32_t *__restrict__ keep_idx,
                                                      int32_t *__restrict__ d_ptr,
                                                      int32_t *__restrict__ d_idx,
-                                                     unsigned char *__restrict__ d_val, int n_c,
-                                                     int keep, int C, int n_res, int row_bytes) {
+                                                     unsigned char *__restrict__ d_val,
+                                                     int32_t *__restrict__ live, int n_c, int keep,
+                                                     int C, int n_res, int d_cap, int row_bytes) {
   __shared__ int32_t part[257];
   const long bh = (long)blockIdx.y * gridDim.x + blockIdx.x;
   const int b = blockIdx.y, tid = threadIdx.x;
   const int32_t *p = ptr + bh * (n_c + 1);
   const int32_t *kp = keep_idx + (long)b * keep;
-  int32_t *dp = d_ptr + bh * (keep + 1);
   // each thread sums a contiguous run of kept chunks, then a serial scan of the runs
   const int per = (keep + 255) / 256;
   const int j0 = min(keep, tid * per), j1 = min(keep, j0 + per);
@@ -416,21 +420,24 @@ __global__ __launch_bounds__(256) void k_evict_resid(const int32_t *__restrict__
     int32_t run = 0;
     for (int i = 0; i < 256; ++i) { const int32_t c = part[i]; part[i] = run; run += c; }
     part[256] = run;
+    if (live) live[bh] = run;
   }
   __syncthreads();
+  if (!d_ptr) return;
+  int32_t *dp = d_ptr + bh * (keep + 1);
   int32_t run = part[tid];
   for (int jn = j0; jn < j1; ++jn) {
-    dp[jn] = run;
+    dp[jn] = min(run, d_cap);
     const int jo = kp[jn];
-    for (int e = p[jo]; e < p[jo + 1]; ++e, ++run) {
-      d_idx[bh * n_res + run] = idx[bh * n_res + e] - jo * C + jn * C;
+    for (int e = p[jo]; e < p[jo + 1] && run < d_cap; ++e, ++run) {
+      d_idx[bh * d_cap + run] = idx[bh * n_res + e] - jo * C + jn * C;
       const unsigned char *sr = val + (bh * n_res + e) * (long)row_bytes;
-      unsigned char *dr = d_val + (bh * n_res + run) * (long)row_bytes;
+      unsigned char *dr = d_val + (bh * d_cap + run) * (long)row_bytes;
       for (int i = 0; i < row_bytes; i += 16)
         lst16(dr + i, gld16(sr + i));
     }
   }
-  if (tid == 0) dp[keep] = part[256];
+  if (tid == 0) dp[keep] = min(part[256], d_cap);
 }
 
 // ---------------------------------------------------------------------------
@@ -695,14 +702,17 @@ hipError_t run_evict(const EvictArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(k_evict_accum, dim3((n_c + 255) / 256, a.B), dim3(256), 0, st, a.scores,
                        a.acc, 0, n_c, 1);
   hipLaunchKernelGGL(k_evict_select, dim3(a.B), dim3(1024), 0, st, a.acc, n_c, a.keep, a.keep_out);
-  const long chunk_bytes = (long)a.C * a.r * dtype_bytes(a.coeff_dt);
-  hipLaunchKernelGGL(k_evict_copy, dim3(a.keep, a.B), dim3(256), 0, st,
-                     (const unsigned char *)a.coeff, a.landmark, a.keep_out,
-                     (unsigned char *)a.d_coeff, a.d_landmark, a.keep, n_c, chunk_bytes, a.r);
-  hipLaunchKernelGGL(k_evict_resid, dim3(a.G * a.Hkv, a.B), dim3(256), 0, st, a.res_ptr, a.res_idx,
-                     (const unsigned char *)a.res_val, a.keep_out, a.d_res_ptr, a.d_res_idx,
-                     (unsigned char *)a.d_res_val, n_c, a.keep, a.C, a.n_res,
-                     a.dh * dtype_bytes(a.resid_dt));
+  if (a.d_coeff) {
+    const long chunk_bytes = (long)a.C * a.r * dtype_bytes(a.coeff_dt);
+    hipLaunchKernelGGL(k_evict_copy, dim3(a.keep, a.B), dim3(256), 0, st,
+                       (const unsigned char *)a.coeff, a.landmark, a.keep_out,
+                       (unsigned char *)a.d_coeff, a.d_landmark, a.keep, n_c, chunk_bytes, a.r);
+  }
+  if (a.d_coeff || a.live_out)
+    hipLaunchKernelGGL(k_evict_resid, dim3(a.G * a.Hkv, a.B), dim3(256), 0, st, a.res_ptr, a.res_idx,
+                       (const unsigned char *)a.res_val, a.keep_out, a.d_coeff ? a.d_res_ptr : nullptr,
+                       a.d_res_idx, (unsigned char *)a.d_res_val, a.live_out, n_c, a.keep, a.C, a.n_res,
+                       a.d_n_res, a.dh * dtype_bytes(a.resid_dt));
   return hipGetLastError();
 }
 

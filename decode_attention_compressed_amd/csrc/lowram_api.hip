@@ -530,6 +530,9 @@ lowram_status lowram_decode_attn_reuse(const lowram_dims *d, int32_t layer, cons
   if ((st = check_decode_inputs(d, layer, m, c, p)) != LOWRAM_OK) return st;
   if (p.tps == 0 || p.k_eff == 0)
     return fail(LOWRAM_E_UNSUPPORTED, "reuse needs the register-chained attend kernel and a selected chunk");
+  if (p.k_eff > CHAIN_SELECT_MAX_NC)
+    return fail(LOWRAM_E_UNSUPPORTED, "reuse assigns slots to at most %d selected chunks (top_k %d)",
+                CHAIN_SELECT_MAX_NC, p.k_eff);
   REQUIRE_PTR(q); REQUIRE_PTR(out); OPTIONAL_PTR(sel_out); OPTIONAL_PTR(hits_out);
   if (d->n_tail > 0) { REQUIRE_PTR(k_tail); REQUIRE_PTR(v_tail); }
   REQUIRE_PTR(m->w2); REQUIRE_PTR(m->b2);
@@ -555,9 +558,9 @@ lowram_status lowram_decode_attn_reuse(const lowram_dims *d, int32_t layer, cons
 }
 
 lowram_status lowram_evict(const lowram_dims *d, const lowram_model *m, const lowram_cache *src,
-                           const void *obs_q, int32_t n_obs, int32_t keep_chunks,
-                           const lowram_cache *dst, int32_t *keep_out, void *ws, size_t ws_bytes,
-                           void *stream) {
+                           const void *obs_q, int32_t n_obs, int32_t keep_chunks, int32_t dst_n_res,
+                           const lowram_cache *dst, int32_t *keep_out, int32_t *live_out, void *ws,
+                           size_t ws_bytes, void *stream) {
   lowram_status st = check_dims(d);
   if (st != LOWRAM_OK) return st;
   const int n_c = n_chunks(d);
@@ -565,18 +568,23 @@ lowram_status lowram_evict(const lowram_dims *d, const lowram_model *m, const lo
   if (keep_chunks < 1 || keep_chunks > n_c)
     return fail(LOWRAM_E_INVALID, "keep_chunks %d outside [1, %d]", keep_chunks, n_c);
   if (n_obs < 0) return fail(LOWRAM_E_INVALID, "n_obs must be >= 0");
-  if (!m || !src || !dst) return fail(LOWRAM_E_INVALID, "model, src and dst must not be NULL");
+  if (!m || !src) return fail(LOWRAM_E_INVALID, "model and src must not be NULL");
+  if (!dst && !keep_out && !live_out)
+    return fail(LOWRAM_E_INVALID, "nothing to write: dst, keep_out and live_out are all NULL");
   if (n_obs > 0) REQUIRE_PTR(obs_q);
   REQUIRE_PTR(m->basis);
   REQUIRE_PTR(src->coeff); REQUIRE_PTR(src->landmark); REQUIRE_PTR(src->res_ptr);
-  REQUIRE_PTR(dst->coeff); REQUIRE_PTR(dst->landmark); REQUIRE_PTR(dst->res_ptr);
-  if (d->n_res > 0) {
-    REQUIRE_PTR(src->res_idx); REQUIRE_PTR(src->res_val);
-    REQUIRE_PTR(dst->res_idx); REQUIRE_PTR(dst->res_val);
+  if (d->n_res > 0) { REQUIRE_PTR(src->res_idx); REQUIRE_PTR(src->res_val); }
+  OPTIONAL_PTR(keep_out); OPTIONAL_PTR(live_out);
+  if (dst) {
+    if (dst_n_res < 0 || dst_n_res > d->n_res)
+      return fail(LOWRAM_E_INVALID, "dst_n_res %d outside [0, n_res %d]", dst_n_res, d->n_res);
+    REQUIRE_PTR(dst->coeff); REQUIRE_PTR(dst->landmark); REQUIRE_PTR(dst->res_ptr);
+    if (dst_n_res > 0) { REQUIRE_PTR(dst->res_idx); REQUIRE_PTR(dst->res_val); }
+    if (src->coeff == dst->coeff || src->res_ptr == dst->res_ptr ||
+        (dst_n_res > 0 && src->res_val == dst->res_val))
+      return fail(LOWRAM_E_INVALID, "src and dst must not share coefficient or residual storage");
   }
-  OPTIONAL_PTR(keep_out);
-  if (src->coeff == dst->coeff || src->res_val == dst->res_val || src->res_ptr == dst->res_ptr)
-    return fail(LOWRAM_E_INVALID, "src and dst must not share coefficient or residual storage");
   const EvictPlan p = evict_plan(d);
   if ((st = check_ws(ws, ws_bytes, p.bytes)) != LOWRAM_OK) return st;
   EvictArgs a;
@@ -584,9 +592,12 @@ lowram_status lowram_evict(const lowram_dims *d, const lowram_model *m, const lo
   a.basis = m->basis; a.obs_q = obs_q; a.n_obs = n_obs; a.keep = keep_chunks;
   a.coeff = src->coeff; a.landmark = src->landmark; a.res_ptr = src->res_ptr;
   a.res_idx = src->res_idx; a.res_val = src->res_val;
-  a.d_coeff = dst->coeff; a.d_landmark = dst->landmark; a.d_res_ptr = dst->res_ptr;
-  a.d_res_idx = dst->res_idx; a.d_res_val = dst->res_val;
+  if (dst) {
+    a.d_coeff = dst->coeff; a.d_landmark = dst->landmark; a.d_res_ptr = dst->res_ptr;
+    a.d_res_idx = dst->res_idx; a.d_res_val = dst->res_val; a.d_n_res = dst_n_res;
+  }
   a.keep_out = keep_out ? keep_out : reinterpret_cast<int32_t *>((char *)ws + p.keep_off);
+  a.live_out = live_out;
   a.scores = reinterpret_cast<double *>((char *)ws + p.scores_off);
   a.spart = reinterpret_cast<double *>((char *)ws + p.spart_off);
   a.acc = reinterpret_cast<double *>((char *)ws + p.acc_off);

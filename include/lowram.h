@@ -243,14 +243,24 @@ lowram_status lowram_decode_attn_reuse(const lowram_dims *dims, int32_t layer, c
  * (lowest index wins ties) are copied to dst in ascending chunk order:
  * coefficients, landmarks and residual rows, with residual token indices
  * renumbered to the new positions.  dst has n_ctx' = keep_chunks * chunk and
- * the same residual capacity n_res (dst res_ptr[n_c'] rows are live); scales
- * are unchanged (dst coeff_scale / res_scale may alias src's).
+ * dst_n_res residual rows per (b, layer, kv head), 0 <= dst_n_res <= n_res;
+ * dst res_ptr[n_c'] rows are live.  Scales are unchanged (dst coeff_scale /
+ * res_scale may alias src's).
+ * Sizing: the kept chunks of a head hold some number of residual rows, known
+ * only once the chunks are chosen.  With dst = NULL nothing is copied and only
+ * keep_out and live_out are written; a caller that wants a cache sized to its
+ * rows runs that first and then calls again with dst_n_res = max(live_out).
+ * A head whose kept rows exceed dst_n_res keeps its first dst_n_res rows (its
+ * pointers are clamped, so decode never reads a row dst lacks); live_out shows
+ * the count before that clamp.
  * obs_q: [n_obs][B][G][Hq][dh] act dtype.  keep_out: optional [B][keep_chunks]
- * int32 kept source chunk indices.  Workspace: LOWRAM_OP_EVICT. */
+ * int32 kept source chunk indices.  live_out: optional [B][G][Hkv] int32.
+ * Workspace: LOWRAM_OP_EVICT. */
 lowram_status lowram_evict(const lowram_dims *dims, const lowram_model *model,
                            const lowram_cache *src, const void *obs_q, int32_t n_obs,
-                           int32_t keep_chunks, const lowram_cache *dst, int32_t *keep_out,
-                           void *workspace, size_t workspace_bytes, void *stream);
+                           int32_t keep_chunks, int32_t dst_n_res, const lowram_cache *dst,
+                           int32_t *keep_out, int32_t *live_out, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* Tail growth: move the oldest `chunk` tokens of the uncompressed tail into
  * the compressed cache as one new chunk.  The rit.work page (generation

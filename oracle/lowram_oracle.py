@@ -680,16 +680,19 @@ def m_kv(L: int, Hkv: int, dh: int, N: int, s_bytes: int) -> int:
     return 2 * L * Hkv * dh * N * s_bytes
 
 
-def compressed_bytes(G, Hkv, dh, N, C, r, F, n_res, act, coeff, resid) -> int:
+def compressed_bytes(G, Hkv, dh, N, C, r, F, n_res, act, coeff, resid, rows=None) -> int:
     """Bytes of one sequence's compressed group: coefficients, basis, predictor,
     residual rows with their int32 token index, CSR pointers, fp32 landmarks
     and fp16 scales.  The uncompressed tail is identical on both sides and is
-    not counted."""
+    not counted.  Residual storage is n_res rows for each of the G * Hkv heads,
+    or, if `rows` is given, `rows` rows in all (the live rows of a cache whose
+    heads hold different counts, e.g. after eviction)."""
     D = G * Hkv * dh
     n_c = N // C
     s, sc, sr = DTYPE_BYTES[act], DTYPE_BYTES[coeff], DTYPE_BYTES[resid]
+    n_rows = G * Hkv * n_res if rows is None else rows
     total = N * r * sc + D * r * s + G * Hkv * (2 * F * dh + F + dh) * s
-    total += G * Hkv * n_res * (dh * sr + 4) + G * Hkv * (n_c + 1) * 4 + n_c * r * 4
+    total += n_rows * (dh * sr + 4) + G * Hkv * (n_c + 1) * 4 + n_c * r * 4
     if coeff == I8:
         total += r * 2
     if resid == I8:

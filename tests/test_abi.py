@@ -48,6 +48,13 @@ def test_llama_ratio_and_composed_ratio():
     assert dn / c == pytest.approx(7.008, abs=1e-3)
     c, dn = P.cache_bytes(dims_of(TINY))
     assert dn / c == pytest.approx(3.006, abs=1e-3)
+    # the composed int8 workload before eviction, its scales counted
+    c, dn = P.cache_bytes(dims_of(COMPOSED_128K))
+    assert dn / c == pytest.approx(28.4, abs=0.05)
+    s = COMPOSED_128K
+    assert c == O.compressed_bytes(s.G, s.Hkv, s.dh, s.N, s.C, s.r, s.F, s.n_res, s.act, s.coeff, s.resid)
+    assert c - P.cache_bytes(dims_of(s.replace(coeff="bf16", resid="bf16")))[0] == \
+        (s.r * 2 + s.G * s.Hkv * s.dh * 2) - s.N * s.r - s.G * s.Hkv * s.n_res * s.dh
 
 
 @pytest.mark.parametrize("s", ALL, ids=lambda s: s.name)
@@ -134,11 +141,18 @@ def test_compress_and_evict_argument_errors():
     dst = L.Cache(FAKE * 2, None, FAKE * 2, FAKE * 2, FAKE * 2, FAKE * 2, None)
     ne = P.workspace_bytes(d, L.OP_EVICT)
     n_c = d.n_ctx // d.chunk
-    ev = lambda keep, dst_=dst, n_obs=1: lib.lowram_evict(ctypes.byref(d), ctypes.byref(m), ctypes.byref(c), FAKE, n_obs, keep, ctypes.byref(dst_), None, FAKE, ne, None)
+    def ev(keep, dst_=dst, n_obs=1, cap=d.n_res, keep_out=None, live=None):
+        dp = ctypes.byref(dst_) if dst_ is not None else None
+        return lib.lowram_evict(ctypes.byref(d), ctypes.byref(m), ctypes.byref(c), FAKE, n_obs, keep, cap,
+                                dp, keep_out, live, FAKE, ne, None)
     assert ev(0) == L.E_INVALID
     assert ev(n_c + 1) == L.E_INVALID
     assert ev(2, n_obs=-1) == L.E_INVALID
     assert ev(2, dst_=c) == L.E_INVALID        # in-place eviction is refused
+    assert ev(2, cap=-1) == L.E_INVALID        # dst capacity outside [0, n_res]
+    assert ev(2, cap=d.n_res + 1) == L.E_INVALID
+    assert ev(2, dst_=None) == L.E_INVALID     # nothing to write
+    assert ev(2, dst_=None, live=FAKE + 4) == L.E_INVALID  # unaligned live_out
 
 
 def test_repack_argument_errors():
@@ -239,6 +253,16 @@ def test_reuse_argument_errors():
     assert call(L.Reuse(FAKE, FAKE, FAKE, FAKE, 8), d_=other) == L.E_UNSUPPORTED
     n = ctypes.c_size_t(0)
     assert lib.lowram_reuse_tile_bytes(ctypes.byref(other), ctypes.byref(n)) == L.E_UNSUPPORTED
+    # the slot assignment stages at most 512 selected chunks in LDS: a larger
+    # top-k on a chained shape is refused before anything is enqueued
+    big = P.with_(d, n_ctx=1024 * d.chunk, top_k=513, n_res=0)
+    assert P.decode_kernel(big) == "chain"
+    need_big = P.workspace_bytes(big, L.OP_DECODE)
+    st = lib.lowram_decode_attn_reuse(ctypes.byref(big), 0, ctypes.byref(m), ctypes.byref(c), FAKE, FAKE, FAKE,
+                                      FAKE, None, ctypes.byref(L.Reuse(FAKE, FAKE, FAKE, FAKE, 8)), None, FAKE,
+                                      need_big, None)
+    assert st == L.E_UNSUPPORTED
+    assert "512" in L.lib().lowram_last_error().decode()
 
 
 def test_dense_argument_errors():

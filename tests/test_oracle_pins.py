@@ -331,6 +331,28 @@ def test_mha_reduces_to_per_head_attention():
         assert np.allclose(out[0, g], sdpa64(q[0, g], K, V), rtol=1e-10, atol=1e-11)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(16, 4), (8, 2), (6, 3), (4, 4)])
+def test_dense_decode_layer_matches_torch_gqa_attention(Hq, Hkv):
+    """The uncompressed comparator's attention equals torch's scaled dot-product
+    attention (float64, CPU), whose enable_gqa mode maps query head g to kv head
+    g // (Hq / Hkv) by itself: a head-mapping or scale slip fails here."""
+    rng = np.random.default_rng(Hq * 10 + Hkv)
+    B, n, dh = 2, 37, 16
+    q = rng.standard_normal((B, Hq, dh)) * 2.0
+    k = rng.standard_normal((B, Hkv, n, dh))
+    v = rng.standard_normal((B, Hkv, n, dh))
+    out = O.dense_decode_layer(q, k, v, Hq, Hkv)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None, :], torch.from_numpy(k), torch.from_numpy(v),
+        enable_gqa=True)[:, :, 0, :].numpy()
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-13)
+    if Hq != Hkv:  # a wrong grouping (interleaved heads) would differ
+        perm = np.array([g % Hkv for g in range(Hq)])
+        wrong = np.stack([[O.softmax_attend(q[b, g], k[b, perm[g]], v[b, perm[g]]) for g in range(Hq)]
+                          for b in range(B)])
+        assert not np.allclose(wrong, want)
+
+
 def test_tail_only_and_no_tail():
     s = tiny64(B=1)
     inp = gen.make(s)
@@ -380,6 +402,72 @@ def test_compressed_bytes_counts_each_stored_tensor():
               + cache["res_val"][0].nbytes + cache["res_idx"][0].nbytes
               + cache["res_ptr"][0].nbytes + cache["landmark"][0].nbytes)
     assert O.compressed_bytes(s.G, s.Hkv, s.dh, s.N, s.C, s.r, s.F, s.n_res, s.act, s.coeff, s.resid) == stored
+
+
+def _stored_nbytes(cache, inp, b, n_rows=None):
+    """Bytes of every array one sequence's compressed group stores, read off
+    the arrays themselves (residual arrays cut to n_rows rows per head)."""
+    sl = (lambda a: a) if n_rows is None else (lambda a: a[..., :n_rows] if a.ndim == 3 else a[:, :, :n_rows])
+    total = cache["coeff"][b].nbytes + inp["basis"][b].nbytes + cache["landmark"][b].nbytes
+    total += sum(inp[n][b].nbytes for n in ("w1", "b1", "w2", "b2"))
+    total += sl(cache["res_idx"][b]).nbytes + sl(cache["res_val"][b]).nbytes + cache["res_ptr"][b].nbytes
+    for name in ("coeff_scale", "res_scale"):
+        if cache.get(name) is not None:
+            total += cache[name][b].nbytes
+    return total
+
+
+@pytest.mark.parametrize("coeff,resid", [(I8, I8), (BF16, I8), (I8, BF16), (BF16, BF16)])
+def test_compressed_bytes_counts_scales_of_int8_caches(coeff, resid):
+    """Int8 and mixed caches: the formula equals the summed nbytes of every
+    stored array, the fp16 coefficient and residual scales included."""
+    s = tiny64(act=BF16, coeff=coeff, resid=resid, dh=16, r=16, N=128, C=16, B=2)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    assert (cache.get("coeff_scale") is not None) == (coeff == I8)
+    assert (cache.get("res_scale") is not None) == (resid == I8)
+    for b in range(s.B):
+        assert O.compressed_bytes(s.G, s.Hkv, s.dh, s.N, s.C, s.r, s.F, s.n_res, s.act, s.coeff,
+                                  s.resid) == _stored_nbytes(cache, inp, b)
+
+
+def test_evicted_cache_bytes_capacity_and_live_rows():
+    """After eviction each head keeps the rows of its kept chunks.  Sized to
+    the largest head's rows, the cache's arrays hold exactly the formula's
+    bytes at that capacity; counting live rows only gives the formula with
+    rows = their sum.  The live count is at most the capacity."""
+    s = tiny64(act=BF16, coeff=I8, resid=I8, dh=16, r=16, N=256, C=16, B=2, n_obs=3, rho=0.25)
+    inp = gen.make(s)
+    cache = O.compress(inp, s)
+    keep = 5
+    ev = O.evict(cache, inp, s, inp["obs_q"], keep)
+    N2 = keep * s.C
+    for b in range(s.B):
+        live = ev["res_ptr"][b, :, :, keep]
+        cap = int(live.max())
+        assert O.compressed_bytes(s.G, s.Hkv, s.dh, N2, s.C, s.r, s.F, cap, s.act, s.coeff,
+                                  s.resid) == _stored_nbytes(ev, inp, b, n_rows=cap)
+        by_rows = O.compressed_bytes(s.G, s.Hkv, s.dh, N2, s.C, s.r, s.F, cap, s.act, s.coeff, s.resid,
+                                     rows=int(live.sum()))
+        spare = (s.G * s.Hkv * cap - int(live.sum())) * (s.dh * 1 + 4)
+        assert by_rows == _stored_nbytes(ev, inp, b, n_rows=cap) - spare
+
+
+def test_composed_workload_ratios():
+    """The composed int8 workload against a dense bf16 cache of its 131072
+    tokens: 28.4x before eviction; after keeping a quarter of the chunks, the
+    formula gives 90.8x when the kept chunks carry a quarter of each head's
+    residual rows (the expected share for rows spread evenly over chunks).
+    Both figures are derived independently from the workload sizes."""
+    from synth.configs import COMPOSED_128K as s
+    dense = O.m_kv(s.G, s.Hkv, s.dh, s.N, 2)
+    assert dense == 2 * 2 ** 30
+    before = O.compressed_bytes(s.G, s.Hkv, s.dh, s.N, s.C, s.r, s.F, s.n_res, s.act, s.coeff, s.resid)
+    assert dense / before == pytest.approx(28.4, abs=0.05)
+    N2 = s.keep_chunks * s.C
+    after = O.compressed_bytes(s.G, s.Hkv, s.dh, N2, s.C, s.r, s.F, s.n_res, s.act, s.coeff, s.resid,
+                               rows=s.G * s.Hkv * s.n_res // 4)
+    assert dense / after == pytest.approx(90.8, abs=0.1)
 
 
 # ---------------------------------------------------------------------------
