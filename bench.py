@@ -63,24 +63,32 @@ def parse():
     return ap.parse_args()
 
 
-def attend_accounting(s, sel, res_ptr, layer):
+def attend_accounting(s, sel, res_ptr, layer, kernel="chain"):
     """Algorithmic HBM bytes and FLOPs of one rebuild-and-attend launch.
 
     bytes: the union over kv heads of the selected coefficient tiles (each
     read once per sequence), the layer's basis slice and first predictor
     layer, residual rows (+int32 index) and CSR pointers of the selected
     chunks, the layer's tail K/V, the queries and the chunk scores the kernel
-    ranks for its own top-k.
-    flops: per selected token-head 2(d_h r + F d_h + g d_h + g F) (rebuilt key,
-    hidden layer, logits, p-weighted hidden sum), plus the tail's 4 T d_h per
-    query head."""
+    ranks for its own top-k.  The absorbed kernel (head dim 256) reads the
+    first layer in its absorbed form A = W1 U_{l,h} (F r values) and q~ (g r)
+    in place of the basis slice and W1, and its selection comes from the
+    separate top-k (no scores read).
+    flops: per selected token-head the cheaper exact form of the product
+    chain: 2(d_h r + F d_h + g d_h + g F) (rebuilt key, hidden layer, logits,
+    p-weighted hidden sum) or, absorbed, 2(F r + g r + g F); plus the tail's
+    4 T d_h per query head."""
     B, Hkv, C, r, dh, F, T = s.B, s.Hkv, s.C, s.r, s.dh, s.F, s.T
     sa, sc, sr = 2, (1 if s.coeff == "i8" else 2), (1 if s.resid == "i8" else 2)
+    g = s.Hq // Hkv
     union = sum(len(np.unique(sel[b])) for b in range(B))
     nbytes = union * C * r * sc
     if s.coeff == "i8":
         nbytes += B * r * 2
-    nbytes += B * Hkv * dh * r * sa + B * Hkv * (F * dh + F) * sa
+    if kernel == "absorb":
+        nbytes += B * Hkv * (F * r + 2 * 4 * r) * sa + B * Hkv * F * sa
+    else:
+        nbytes += B * Hkv * dh * r * sa + B * Hkv * (F * dh + F) * sa
     rows = 0
     for b in range(B):
         for h in range(Hkv):
@@ -90,9 +98,10 @@ def attend_accounting(s, sel, res_ptr, layer):
     if s.resid == "i8":
         nbytes += B * Hkv * dh * 2
     nbytes += 2 * B * Hkv * T * dh * sa + B * s.Hq * dh * sa
-    nbytes += B * Hkv * (s.N_after // C) * 8
-    g = s.Hq // Hkv
-    flops = B * Hkv * sel.shape[-1] * C * 2 * (dh * r + F * dh + g * dh + g * F) + B * s.Hq * T * dh * 4
+    if kernel == "chain":
+        nbytes += B * Hkv * (s.N_after // C) * 8
+    per_tok = min(dh * r + F * dh + g * dh + g * F, F * r + g * r + g * F)
+    flops = B * Hkv * sel.shape[-1] * C * 2 * per_tok + B * s.Hq * T * dh * 4
     return nbytes, flops, union
 
 
@@ -359,10 +368,26 @@ def main():
     torch.cuda.synchronize()
     compress_ms = ev[0].elapsed_time(ev[1])
     log(f"compress {compress_ms:.1f} ms")
+    comp_bytes, dense_bytes = P.cache_bytes(dims_of(s))   # as compressed, before any eviction
+    evicted = None
     if s.evict_keep < 1.0:
         cache, d, _ = P.evict(d, model, cache, to_dev(inp["obs_q"]), s.keep_chunks)
         torch.cuda.synchronize()
-    comp_bytes, dense_bytes = P.cache_bytes(dims_of(s))
+        # against the dense bf16 cache of all s.N tokens: the evicted cache as
+        # allocated (every head sized to the largest head's kept rows), and by
+        # the rows the kept chunks actually hold
+        comp_ev, _ = P.cache_bytes(d)
+        live = float(cache["res_ptr"][..., -1].sum().item()) / s.B
+        row_b = s.dh * (1 if s.resid == "i8" else 2) + 4
+        comp_live = comp_ev - (s.G * s.Hkv * d.n_res - live) * row_b
+        evicted = {"n_ctx": d.n_ctx, "res_rows_capacity": d.n_res, "res_rows_live_per_seq": live,
+                   "compressed_bytes_per_seq": comp_ev, "ratio_vs_dense_bf16": round(dense_bytes / comp_ev, 2),
+                   "ratio_vs_dense_bf16_live_rows": round(dense_bytes / comp_live, 2),
+                   "dense_bytes_per_seq": dense_bytes,
+                   "how": f"dense = M_KV of the {s.N}-token context in bf16; compressed = the evicted cache "
+                          f"({d.n_ctx} tokens) with its residual arrays as allocated, or counting live rows only"}
+        log(f"evicted cache: {evicted['ratio_vs_dense_bf16']}x as allocated, "
+            f"{evicted['ratio_vs_dense_bf16_live_rows']}x by live rows")
 
     # per (query set, layer) pre-marshalled calls
     kk = P.k_eff(d)
@@ -446,7 +471,8 @@ def main():
     torch.cuda.synchronize()
     attend_ms = np.array([a.elapsed_time(b) for a, b in evs])
     host_ptr = to_host(cache["res_ptr"])
-    acc = [attend_accounting(s, to_host(sels[i][l]), host_ptr, l) for i in range(n_time) for l in range(s.G)]
+    kern = P.decode_kernel(d)
+    acc = [attend_accounting(s, to_host(sels[i][l]), host_ptr, l, kern) for i in range(n_time) for l in range(s.G)]
     a_bytes = np.mean([a[0] for a in acc])
     a_flops = np.mean([a[1] for a in acc])
     union = np.mean([a[2] for a in acc]) / s.B
@@ -463,7 +489,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
     roof["traffic"] = traffic_for_current_kernel()
     kname = {"chain": "k_attend_chain (top-k + rebuild-and-attend)", "mfma": "k_attend_mfma (rebuild-and-attend)",
-             "valu": "k_attend_valu (rebuild-and-attend)", "none": "tail only"}[P.decode_kernel(d)]
+             "absorb": "k_attend_absorb (absorbed first layer; A = W1 U formed with the selection)",
+             "valu": "k_attend_valu (rebuild-and-attend)", "none": "tail only"}[kern]
     roof.update({"kernel": kname, "avg_launch_us": round(t_attend * 1e6, 2),
                  "algorithmic_bytes_per_launch": int(a_bytes), "algorithmic_flops_per_launch": int(a_flops),
                  "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -471,29 +498,49 @@ def main():
                  "frac_of_binding_roof": round(max(t_hbm, t_mfma) / t_attend, 4)})
     log(f"attend {t_attend * 1e6:.1f} us/launch, {gbps:.0f} GB/s, {tflops:.1f} TF/s, union {union:.1f} chunks/seq")
 
-    # ---- dense comparator on the same queries ---------------------------------
+    # ---- dense comparator on the same queries, timed like the compressed step:
+    # K steps of G layer calls captured in one HIP graph ----------------------
     dense = None
     if not args.no_dense:
         kd = torch.cat([dev["k"], dev["k_tail"]], dim=3).contiguous()
         vd = torch.cat([dev["v"], dev["v_tail"]], dim=3).contiguous()
         dws = P.dense_workspace(d, kd.shape[3])
         dout = torch.empty_like(out)
-        for i in range(2):
-            for l in range(s.G):
-                P.dense_decode_attn(d, dev["q"][i, l], kd, vd, l, out=dout, ws=dws)
-        torch.cuda.synchronize()
-        ev[0].record()
-        for i in range(args.steps):
+
+        def dense_step(i):
             for l in range(s.G):
                 P.dense_decode_attn(d, dev["q"][i % n_q, l], kd, vd, l, out=dout, ws=dws)
+
+        for i in range(2):
+            dense_step(i)
+        torch.cuda.synchronize()
+        dgraph = None
+        if graph is not None:
+            dgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(dgraph):
+                for i in range(args.steps):
+                    dense_step(i)
+            dgraph.replay()
+            torch.cuda.synchronize()
+        ev[0].record()
+        if dgraph is not None:
+            dgraph.replay()
+        else:
+            for i in range(args.steps):
+                dense_step(i)
         ev[1].record()
         torch.cuda.synchronize()
         dense_ms = ev[0].elapsed_time(ev[1]) / args.steps
-        dense_bytes_step = 2 * s.B * s.G * s.Hkv * kd.shape[3] * s.dh * 2
-        dense = {"ms_per_step": round(dense_ms, 4), "hbm_gbps": round(dense_bytes_step / (dense_ms * 1e-3) / 1e9, 1),
-                 "kernel": "k_dense (bf16 split-K, eager launches)"}
-        log(f"dense {dense_ms * 1e3:.1f} us/step, {dense['hbm_gbps']} GB/s")
-        del kd, vd
+        dense_bytes_step = 2 * s.B * s.G * s.Hkv * kd.shape[3] * s.dh * 2 + 2 * s.B * s.G * s.Hq * s.dh * 2
+        ideal_ms = dense_bytes_step / (HBM_PEAK_GBPS * 1e9) * 1e3
+        gb = dense_bytes_step / (dense_ms * 1e-3) / 1e9
+        dense = {"ms_per_step": round(dense_ms, 4), "hbm_gbps": round(gb, 1),
+                 "hbm_frac": round(gb / HBM_PEAK_GBPS, 4), "ideal_ms_per_step": round(ideal_ms, 4),
+                 "kernel": "k_dense_mfma (bf16 split-K) + combine, "
+                           + ("captured in one HIP graph like the compressed step" if dgraph is not None
+                              else "eager launches")}
+        log(f"dense {dense_ms * 1e3:.1f} us/step, {gb:.0f} GB/s ({gb / HBM_PEAK_GBPS:.1%} of HBM peak)")
+        del kd, vd, dgraph
 
     # ---- once-per-context and optional paths, timed after the decode step ------
     repack = time_repack(P, s, d, model, cache, dev, ev)
@@ -540,8 +587,10 @@ def main():
         "step_hbm_gbps": round(step_b / (ms_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_b / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "x_vs_dense": round(dense["ms_per_step"] / ms_step, 3) if dense else None,
+        "x_vs_dense_at_hbm_peak": round(dense["ideal_ms_per_step"] / ms_step, 3) if dense else None,
         "dense": dense,
         "compression_ratio": round(dense_bytes / comp_bytes, 3),
+        "evicted": evicted,
         "selected_chunk_union_per_seq": round(float(union), 1),
         "compress_ms": round(compress_ms, 2),
         "repack": repack,

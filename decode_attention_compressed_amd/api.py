@@ -76,12 +76,12 @@ def workspace(d: L.Dims, op: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(1, workspace_bytes(d, op)), dtype=torch.uint8, device=device)
 
 
-DECODE_KERNELS = {0: "none", 1: "chain", 2: "mfma", 3: "valu"}
+DECODE_KERNELS = {0: "none", 1: "chain", 2: "mfma", 3: "valu", 4: "absorb"}
 
 
 def decode_kernel(d: L.Dims) -> str:
     """Which rebuild-and-attend kernel decode calls with dims d run:
-    "chain", "mfma", "valu" or "none" (no chunk selected)."""
+    "chain", "absorb", "mfma", "valu" or "none" (no chunk selected)."""
     p = ctypes.c_int32(-1)
     L.check(L.lib().lowram_decode_kernel(ctypes.byref(d), ctypes.byref(p)))
     return DECODE_KERNELS[p.value]

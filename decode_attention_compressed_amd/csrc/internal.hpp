@@ -35,8 +35,13 @@ struct AttendArgs {
   float *part;                  // [B][Hkv][n_split+1][g][PW]
   int B, G, Hq, Hkv, dh, r, F, N, C, T, k_eff, n_res, layer;
   int g, cps, n_split, PW;
-  int tps, tail_per_split;      // register-chained kernel: tiles and tail tokens per split
+  int path;                     // LOWRAM_PATH_* of these dims
+  int tps, tail_per_split;      // chained / absorbed kernels: tiles (slices) and tail tokens per split
   float scale_log2;             // log2(e) / sqrt(dh)
+  const float *qtg;             // chained kernel: [B][Hkv][QTG_G][r] float32 U_{l,h}^T q_g (select stage)
+  // absorbed kernel (head dim 256): workspace of the absorbed first layer
+  uint16_t *absA;               // [B][Hkv][F][r] fp16: -log2(e) W1 U_{l,h} (int8: times the rank scales)
+  uint16_t *absQ;               // [B][Hkv][2][4][r] fp16: U_{l,h}^T q_g, hi then lo parts
 };
 
 struct CombineArgs {
@@ -54,10 +59,14 @@ struct CombineArgs {
 // written to scores [B][Hkv][n_c], and if k_eff > 0 (scores required) the
 // selection into sel and, optionally, a copy into sel_out.
 inline int select_rank_blocks(int r) { return (r + 63) / 64; }
+// With qtg the partial-score kernel also writes U_{l,h}^T q_g of each of the
+// first QTG_G query heads of every kv head in float32, qtg [B][Hkv][QTG_G][r]
+// (rows past the group are zero); heads per kv head must then be <= QTG_G.
+constexpr int QTG_G = 4;
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
-                         double *part, double *scores, hipStream_t st);
+                         double *part, double *scores, hipStream_t st, float *qtg = nullptr);
 hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st);
 // True when the per-chunk MFMA kernel covers these shapes (else the VALU kernel)
 bool mfma_supported(const AttendArgs &a, int act, int coeff, int resid);
@@ -70,6 +79,15 @@ bool chain_supported(int act, int coeff, int resid, int dh, int F, int r, int C,
 constexpr int CHAIN_SELECT_MAX_NC = 512;
 void chain_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps, int &tail_per_split);
 hipError_t launch_attend_chain(int coeff, const AttendArgs &a, hipStream_t st);
+// Absorbed-first-layer rebuild-and-attend (head dim 256): shapes, split plan
+// (splits per (b, h), 64-token slices per split, tail tokens per split), the
+// per-call formation of A = W1 U_{l,h} and q~ (with the selection) and the
+// attend launcher.  Two partial rows per split:
+// the split's chunks, then its share of the tail.
+bool absorb_supported(int act, int coeff, int resid, int dh, int F, int r, int C, int g, int k_eff);
+void absorb_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps, int &tail_per_split);
+hipError_t launch_attend_absorb(int coeff, const AttendArgs &a, hipStream_t st);
+hipError_t launch_absorb(const AttendArgs &a, hipStream_t st);  // A and q~ into the workspace
 constexpr int REUSE_HIT = 1 << 30;
 size_t chain_tile_bytes(int F);  // bytes of one cached 128-token chunk (its rebuilt keys)
 constexpr int REUSE_MAX_SLOTS = 256;

@@ -72,9 +72,10 @@ constexpr int TP = 32;            // tail tokens staged in LDS per split
 constexpr int CPT = 2;            // tiles per chunk: 128-token chunks
 constexpr int MAXIT = 8;          // tiles per wave and split (at most)
 constexpr int MAXSLOT = MAXIT * NW / CPT;  // selected chunks per split (at most)
-// A cached tile: the rebuilt keys KA[NJ][NTT] in 16-byte words, laid out as
-// the registers hold them (lane fastest).
+// A cached tile: the rebuilt keys KA[NJ][NTT] (fp16) in 16-byte words, laid
+// out as the registers hold them (lane fastest).
 constexpr int KA_W = NJ * NTT * WAVE;
+
 
 template <int I, int N, typename Fn>
 __device__ __forceinline__ void sfor_impl(Fn &f) {
@@ -97,6 +98,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)h16(lo) | ((uint32_t)h16(hi) << 16);
 }
 __device__ __forceinline__ f16x8 ldh8(const uint16_t *p) { return *reinterpret_cast<const f16x8 *>(p); }
+__device__ __forceinline__ u32x4 lds16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ bf16x8 ldb8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
 // The hidden pre-activation is kept in units of -log2(e): W1 and b1 are scaled
@@ -146,7 +148,7 @@ __device__ __forceinline__ float xpose_sum_f(float (&v)[R], int lane) {
 
 // LDS layout (bytes).  The merge area at the end reuses W1 and the basis slabs;
 // each wave's running accH stays in LDS across its tiles.
-template <int F>
+template <int F, int R>
 struct Smem {
   static constexpr int W1S = 0;                          // [F][WLD] fp16, dims permuted
   static constexpr int US = W1S + F * WLD * 2;           // 2 x [DH][ULD] basis slabs
@@ -159,7 +161,9 @@ struct Smem {
   static constexpr int SEL = AH + NW * GQ * F * 4;       // [MAXSLOT] chunks of this split, [NW] counts
   static constexpr int TLS = SEL + (MAXSLOT + NW) * 4;   // [2][NW][GQ] tail l and the m it is taken at
   static constexpr int RCODE = TLS + 2 * NW * GQ * 4;    // [MAXSLOT] reuse slot codes of this split's chunks
-  static constexpr int BYTES = RCODE + MAXSLOT * 4;
+  // logits in coefficient space: q~_g (int8: times the rank scales), hi then lo parts [2][GQ][R]
+  static constexpr int QSC = (RCODE + MAXSLOT * 4 + 15) / 16 * 16;
+  static constexpr int BYTES = QSC + 2 * GQ * R * 2;
   // reuse, prologue only: the whole selection after the chunk scores in the p
   // area, the slot table of (b, l, h) in the accH area
   static constexpr int SELALL = PS + CHAIN_SELECT_MAX_NC * 8;
@@ -411,7 +415,8 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   static_assert(NR >= 4, "step 1 needs at least four k-steps");
   constexpr int F = NF * 16;
   constexpr int TILE_W = KA_W;
-  using S = Smem<F>;
+  constexpr bool I8 = sizeof(TC) == 1;
+  using S = Smem<F, NR * KS>;
   using CT = Coef<TC>;
   using ST = Slab<TC>;
   extern __shared__ __align__(16) unsigned char sm[];
@@ -717,6 +722,34 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       *reinterpret_cast<uint2 *>(W1s + f * WLD + dpos(d0)) = lo;
       *reinterpret_cast<uint2 *>(W1s + f * WLD + dpos(d0 + 4)) = hi;
     }
+    {
+      // Logits are taken in coefficient space: q_g . k_hat_t = sum_r
+      // (U^T q_g)_r s_r c_t,r with the stored coefficients c (bf16 as stored;
+      // int8 codes, exact in fp16, with their rank scales s; s = 1 for bf16).
+      // x = (U^T q_g)_r s_r (U^T q_g in float32 from the select stage) is split
+      // into a hi part in the codes' MFMA type and the rounding of the
+      // remainder, so a logit carries the fp32 product to about 2^-16 (bf16) or
+      // 2^-22 (fp16) relative: a key rebuilt and rounded to fp16 would move
+      // logits in the hundreds by ~0.1.
+      uint16_t *qsh = reinterpret_cast<uint16_t *>(sm + S::QSC), *qsl = qsh + GQ * r;
+      const float *qtb = a.qtg + ((long)b * a.Hkv + h) * QTG_G * r;
+      static_assert(QTG_G == GQ, "q~ rows per kv head");
+      for (int i = tw; i < GQ * r; i += W1T) {
+        const int gi = i / r, rr = i - gi * r;
+        const float v = gi < g ? qtb[i] * (I8 ? f16_bits_to_f32(csc[rr]) : 1.f) : 0.f;
+        uint16_t hi, lo;
+        if constexpr (I8) {
+          const _Float16 hv = (_Float16)v;
+          hi = __builtin_bit_cast(uint16_t, hv);
+          lo = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)hv));
+        } else {
+          hi = f32_to_bf16_bits(v);
+          lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+        }
+        qsh[i] = hi;
+        qsl[i] = lo;
+      }
+    }
     // ---- the split's share of the uncompressed tail, attended while wave 0
     // selects: wave w takes tokens tb + w - 1, tb + w - 1 + (NW - 1), ..., two
     // at a time, logits and p . v on the vector ALUs (lane: head dims 2 lane,
@@ -866,8 +899,8 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     typename Res<TC>::raw dr[RP];
 
     // residual entries of the chunk: their tokens (issued two k-steps before the
-    // end of step 1), then the tile's rows (issued in its last k-step, read after
-    // the softmax)
+    // end of step 1), then the tile's rows (issued after step 1, read after the
+    // softmax)
     auto res_tokens = [&]() {
       e0 = has ? e0r : 0;
       e1 = has ? e1r : 0;
@@ -908,10 +941,22 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       const bool hit = !has || (code >= 0 && (code & REUSE_HIT) != 0);
       skip1 = __builtin_amdgcn_readfirstlane((int)hit) != 0;
       skip_all = __syncthreads_and(hit);
+    } else {
+      // always false, but opaque: each k-step's products then sit behind a
+      // branch, which keeps the scheduler from stretching register lifetimes
+      // across k-steps (the unbranched form spills)
+      int sk = 0;
+      asm volatile("" : "+s"(sk));
+      skip1 = sk != 0;
     }
-    const uint32_t lskip = skip1 ? 0x80000000u : 0u;       // past every buffer's end
+    // coefficient loads are never skipped: the logits come from them
+    (void)skip1;
     const uint32_t uskip = skip_all ? 0x80000000u : 0u;
 
+    // logits[t][g] of the tile (int8: accumulated during step 1)
+    f32x4 lg[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) lg[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     // ---- step 1: K_hat^T = U . C^T over NR k-steps ------------------------
     const uint16_t *u_rd = Us + l16 * ULD + 8 * kg;  // lane's basis fragment, head-dim tile 0
     f32x4 acc[NDT][NTT];
@@ -935,13 +980,20 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       // traffic) and skips the products.
       if constexpr (ks + DC - 1 < NR) {
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) cr[(ks + DC - 1) % DC][tt] = CT::ld(Cr, c_voff, c_soff(tt, ks + DC - 1) + lskip);
+        for (int tt = 0; tt < NTT; ++tt) cr[(ks + DC - 1) % DC][tt] = CT::ld(Cr, c_voff, c_soff(tt, ks + DC - 1));
       }
       if constexpr (ks == NR - 3) res_tokens();
-      if constexpr (ks == NR - 1) res_rows();
       __builtin_amdgcn_sched_barrier(0);  // this step's loads go out before its MFMAs
       // basis slab ks + 1 -> LDS (its load was issued LU - 1 steps ago)
       if constexpr (ks + 1 < NR) ST::st(Us + ((ks + 1) & 1) * DH * ULD, ur[(ks + 1) % NU], us_[(ks + 1) % NU]);
+      {  // logits from the coefficients: B operand column l16 < GQ is q~ hi of
+         // head l16, column GQ + g' its lo part; the two are added after step 1
+        const uint16_t *qsb = reinterpret_cast<const uint16_t *>(sm + S::QSC) + l16 * r + ks * KS + 8 * kg;
+        typedef typename CT::op OP;
+        const OP qhl = l16 < 2 * GQ ? __builtin_bit_cast(OP, lds16(qsb)) : __builtin_bit_cast(OP, v4(0, 0, 0, 0));
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) lg[tt] = mfma(CT::get(cr[ks % DC][tt]), qhl, lg[tt]);
+      }
       if (!skip1) {  // basis fragments one head-dim tile ahead of the MFMAs that use them
         const uint16_t *ub = u_rd + (ks & 1) * DH * ULD;
         typename CT::op bc[NTT];
@@ -959,6 +1011,9 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     });
+    // this tile's residual rows: issued now, read after the softmax (their
+    // registers are not held through step 1)
+    res_rows();
     if (!has) {
       restart(it + 1);
       continue;
@@ -977,6 +1032,8 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
                 ((((long)b * a.G + a.layer) * a.Hkv + h) * a.rslots + rslot) * (long)(CPT * TILE_W) +
                 (long)(tau % cpt) * TILE_W;
     }
+    // ---- rebuilt keys as fp16 A operands of the hidden layer (the logits were
+    // taken during step 1)
     f16x8 KA[NJ][NTT];
     if (skip1) {  // this wave's tile is cached: the operands as stored
 #pragma unroll
@@ -1002,18 +1059,11 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
           for (int tt = 0; tt < NTT; ++tt) wt[(jj * NTT + tt) * WAVE + lane] = __builtin_bit_cast(u32x4, KA[jj][tt]);
       }
     }
-
-    // ---- step 2: logits and online softmax ------------------------------------
-    const uint16_t *q_rd = Qs + l16 * WLD + 8 * kg;
-    f32x4 lg[NTT];
+    // logit of head g (lane l16 = g < GQ): hi column plus the lo column GQ + g
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) lg[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const f16x8 qf = ldh8(q_rd + 32 * jj);
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) lg[tt] = mfma(KA[jj][tt], qf, lg[tt]);
-    }
+      for (int v = 0; v < 4; ++v) lg[tt][v] += __shfl_down(lg[tt][v], GQ, 16);
     float mt = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
@@ -1092,9 +1142,15 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     // is zero, so the fold needs no first-tile case.  Software-pipelined: the
     // W1 products of tile fi + 1 are issued before the SiLU of tile fi, so the
     // matrix cores work while the vector ALUs evaluate SiLU.
-    const uint16_t *w1_rd = W1s + l16 * WLD + 8 * kg;   // + 16 fi WLD + 32 jj
-    const float *b1_rd = B1s + l16;
-    f32x4 *ah_rw = reinterpret_cast<f32x4 *>(AHw) + l16;  // + 16 fi
+    // Lane offsets of the hidden phase are formed here, in every tile, from an
+    // offset the compiler cannot see through: hoisted out of the tile loop
+    // they would be held through step 1, where no register is left for them.
+    int hl = lane;
+    asm volatile("" : "+v"(hl));
+    const int hl16 = hl & 15, hkg = hl >> 4;
+    const uint16_t *w1_rd = W1s + hl16 * WLD + 8 * hkg;   // + 16 fi WLD + 32 jj
+    const float *b1_rd = B1s + hl16;
+    f32x4 *ah_rw = reinterpret_cast<f32x4 *>(AHw) + hl16;  // + 16 fi
     const f32x4 ahv = f32x4{ah[0], ah[1], ah[2], ah[3]};
     // W1 fragments and b1 of a hidden tile are read from LDS one tile before
     // the products that use them; both buffers are indexed by the tile's
@@ -1223,7 +1279,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
 
 template <typename TC, int NR, int NF, bool REUSE>
 static hipError_t go(const AttendArgs &a, hipStream_t st) {
-  const size_t smem = Smem<NF * 16>::BYTES;
+  const size_t smem = Smem<NF * 16, NR * KS>::BYTES;
   static const bool lds_ok = (allow_dynamic_lds(k_attend_chain<TC, NR, NF, REUSE>, smem), true);
   (void)lds_ok;
   hipLaunchKernelGGL((k_attend_chain<TC, NR, NF, REUSE>), dim3(a.B * a.Hkv * a.n_split), dim3(NTH), smem, st, a);

@@ -669,7 +669,8 @@ bool mfma_supported(const AttendArgs &a, int act, int coeff, int resid) {
 }
 
 hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st) {
-  if (a.tps > 0) return launch_attend_chain(coeff, a, st);  // planned for the chained kernel
+  if (a.path == LOWRAM_PATH_CHAIN) return launch_attend_chain(coeff, a, st);
+  if (a.path == LOWRAM_PATH_ABSORB) return launch_attend_absorb(coeff, a, st);
   if (!mfma_supported(a, act, coeff, resid)) return launch_attend_valu(act, coeff, resid, a, st);
   const bool i8 = coeff == LOWRAM_I8;
 #define X(dh_, f_, r_, t_) \

@@ -87,6 +87,24 @@ __device__ __forceinline__ double xpose_sum(double (&v)[R], int lane) {
   xpose_step<R, OFF0>(v, lane);
   return v[0];
 }
+template <int N, int OFF>
+__device__ __forceinline__ void xpose_step_f32(float *v, int lane) {
+  if constexpr (N > 1) {
+    const bool hi = (lane & OFF) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float keep = hi ? v[N / 2 + i] : v[i];
+      const float send = hi ? v[i] : v[N / 2 + i];
+      v[i] = keep + __shfl_xor(send, OFF, WAVE);
+    }
+    xpose_step_f32<N / 2, OFF / 2>(v, lane);
+  }
+}
+template <int R, int OFF0>
+__device__ __forceinline__ float xpose_sum_f32(float (&v)[R], int lane) {
+  xpose_step_f32<R, OFF0>(v, lane);
+  return v[0];
+}
 
 // D1 and D2 per block of 64 ranks.  grid (ceil(r / 64), Hkv, B), 256 threads;
 // block rb of (b, h) writes part[b][h][rb][j] = sum over its ranks i of
@@ -110,11 +128,13 @@ __global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q
                                                         const TA *__restrict__ basis,
                                                         const float *__restrict__ landmark, int Hq,
                                                         int Hkv, int r, int n_c, int D, int layer,
-                                                        double *__restrict__ part) {
+                                                        double *__restrict__ part, float *__restrict__ qtg) {
   constexpr int RPS = DH / 32;  // basis rows per slice
   __shared__ double qsum[DH];
   __shared__ double qtp[4][SEL_RB];
   __shared__ double qt[SEL_RB];
+  __shared__ float qg[QTG_G][DH];             // q of each query head (qtg only)
+  __shared__ float qtpg[4][QTG_G][SEL_RB];    // per-wave parts of q~_g (qtg only)
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int NRB = gridDim.x;
   int rb, h, b;
@@ -148,14 +168,43 @@ __global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q
     for (int m = 0; m < MB; ++m) lv[m] = gld16(L + (long)min(j_base + 16 * m + 4 * w + gq, n_c - 1) * r);
   };
   load_rows(0);
+  const int grp = Hq / Hkv;
   if (tid < DH) {
-    const int grp = Hq / Hkv;
     const TA *qb = q + (long)b * q_bstride + (long)h * grp * DH;
     double sq = 0.0;
     for (int gi = 0; gi < grp; ++gi) sq += to_f64(qb[gi * DH + tid]);
     qsum[tid] = sq;
+    if (qtg)
+      for (int gi = 0; gi < QTG_G; ++gi) qg[gi][tid] = gi < grp ? to_f32(qb[gi * DH + tid]) : 0.f;
   }
   __syncthreads();
+  if (qtg) {  // q~_g of each query head over the block's ranks, in float32
+    float acc[QTG_G][8];
+#pragma unroll
+    for (int gi = 0; gi < QTG_G; ++gi)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < RPS; ++k) {
+      double u[8];
+      Load8<TA>::f64(raw[k], u);
+#pragma unroll
+      for (int gi = 0; gi < QTG_G; ++gi) {
+        const float wq = qg[gi][sl + 32 * k];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[gi][e] = fmaf((float)u[e], wq, acc[gi][e]);
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < QTG_G; ++gi) {
+      float v = acc[gi][0];
+      float t[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = acc[gi][e];
+      v = xpose_sum_f32<8, 32>(t, lane);   // rank 8 rg + (lane >> 3), this wave's slices
+      qtpg[w][gi][8 * rg + (lane >> 3)] = v;
+    }
+  }
   {
     double acc[8];
 #pragma unroll
@@ -173,6 +222,12 @@ __global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q
   }
   __syncthreads();
   if (tid < SEL_RB) qt[tid] = ((qtp[0][tid] + qtp[1][tid]) + qtp[2][tid]) + qtp[3][tid];
+  if (qtg) {  // [b][h][g][r] for the query heads of h (zero rows past the group)
+    const int gi = tid / SEL_RB, ri = tid % SEL_RB;
+    if (ri < nr)
+      qtg[(((long)b * Hkv + h) * QTG_G + gi) * r + i0 + ri] =
+          ((qtpg[0][gi][ri] + qtpg[1][gi][ri]) + qtpg[2][gi][ri]) + qtpg[3][gi][ri];
+  }
   __syncthreads();
 
   double qv[4];
@@ -700,24 +755,24 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 template <typename TA>
 static void launch_partial(const TA *q, long q_bstride, const TA *basis, const float *landmark, int B,
                            int Hq, int Hkv, int dh, int r, int n_c, int D, int layer, double *part,
-                           hipStream_t st) {
+                           float *qtg, hipStream_t st) {
   const dim3 g(select_rank_blocks(r), Hkv, B);
   if (dh == 64)
-    hipLaunchKernelGGL((k_select_partial<TA, 64>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part);
+    hipLaunchKernelGGL((k_select_partial<TA, 64>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qtg);
   else if (dh == 128)
-    hipLaunchKernelGGL((k_select_partial<TA, 128>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part);
+    hipLaunchKernelGGL((k_select_partial<TA, 128>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qtg);
   else
-    hipLaunchKernelGGL((k_select_partial<TA, 256>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part);
+    hipLaunchKernelGGL((k_select_partial<TA, 256>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qtg);
 }
 
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
-                         double *part, double *scores, hipStream_t st) {
+                         double *part, double *scores, hipStream_t st, float *qtg) {
   if (act == LOWRAM_F32)
-    launch_partial<float>((const float *)q, q_bstride, (const float *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, st);
+    launch_partial<float>((const float *)q, q_bstride, (const float *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qtg, st);
   else
-    launch_partial<bf16>((const bf16 *)q, q_bstride, (const bf16 *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, st);
+    launch_partial<bf16>((const bf16 *)q, q_bstride, (const bf16 *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qtg, st);
   if (!scores) return k_eff > 0 ? hipErrorInvalidValue : hipGetLastError();
   if (k_eff > 0 && n_c <= TK_SMALL) {  // sums the partials itself
     hipLaunchKernelGGL(k_topk_small, dim3(Hkv, B), dim3(TK_NT), 0, st, part, select_rank_blocks(r), Hkv,

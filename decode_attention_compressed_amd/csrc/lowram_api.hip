@@ -77,8 +77,9 @@ lowram_status check_dims(const lowram_dims *d) {
 // fold the tail into their n_split partials per (b, h); the vector kernel
 // writes one partial per selected chunk plus one for the tail.
 struct DecodePlan {
+  int path;  // LOWRAM_PATH_*
   int k_eff, cps, n_split, n_part, PW, tps, tail_per_split;
-  size_t sel_off, sp_off, sc_off, part_off, bytes;
+  size_t sel_off, sp_off, sc_off, part_off, absA_off, absQ_off, qtg_off, bytes;
 };
 
 DecodePlan decode_plan(const lowram_dims *d) {
@@ -89,9 +90,16 @@ DecodePlan decode_plan(const lowram_dims *d) {
   p.cps = 1;
   p.tps = 0;
   p.tail_per_split = 0;
+  p.path = LOWRAM_PATH_NONE;
   if (chain_supported(d->act, d->coeff, d->resid, d->head_dim, d->hidden, d->rank, d->chunk, g, p.k_eff)) {
     chain_plan(d->batch, d->heads_kv, p.k_eff, d->chunk, d->n_tail, p.n_split, p.tps, p.tail_per_split);
     p.n_part = p.n_split;
+    p.path = LOWRAM_PATH_CHAIN;
+  } else if (absorb_supported(d->act, d->coeff, d->resid, d->head_dim, d->hidden, d->rank, d->chunk, g, p.k_eff) &&
+             (long)d->n_ctx * d->rank * 2 < (1L << 31)) {
+    absorb_plan(d->batch, d->heads_kv, p.k_eff, d->chunk, d->n_tail, p.n_split, p.tps, p.tail_per_split);
+    p.n_part = 2 * p.n_split;
+    p.path = LOWRAM_PATH_ABSORB;
   } else {
     p.n_split = p.k_eff > 0 ? (p.k_eff + p.cps - 1) / p.cps : 0;
     // the matrix-core kernel folds the tail into its splits (one tail partial
@@ -99,18 +107,27 @@ DecodePlan decode_plan(const lowram_dims *d) {
     AttendArgs t;
     memset(&t, 0, sizeof t);
     t.C = d->chunk; t.g = g; t.dh = d->head_dim; t.F = d->hidden; t.r = d->rank;
-    if (mfma_supported(t, d->act, d->coeff, d->resid))
+    if (mfma_supported(t, d->act, d->coeff, d->resid)) {
       p.n_part = p.n_split > 0 ? p.n_split : 1;
-    else
+      p.path = LOWRAM_PATH_MFMA;
+    } else {
       p.n_part = p.n_split + 1;
+      p.path = LOWRAM_PATH_VALU;
+    }
   }
+  if (p.k_eff == 0) p.path = LOWRAM_PATH_NONE;
   p.PW = 4 + d->hidden + d->head_dim;
   p.sel_off = 0;
   p.sp_off = align_up(sizeof(int32_t) * (size_t)d->batch * d->heads_kv * (p.k_eff > 0 ? p.k_eff : 1));
   p.sc_off = p.sp_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * select_rank_blocks(d->rank) *
                                  (n_c > 0 ? n_c : 1));
   p.part_off = p.sc_off + align_up(sizeof(double) * (size_t)d->batch * d->heads_kv * (n_c > 0 ? n_c : 1));
-  p.bytes = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * p.n_part * g * p.PW);
+  p.absA_off = p.part_off + align_up(sizeof(float) * (size_t)d->batch * d->heads_kv * p.n_part * g * p.PW);
+  const bool absorbed = p.path == LOWRAM_PATH_ABSORB;
+  p.absQ_off = p.absA_off + (absorbed ? align_up(2 * (size_t)d->batch * d->heads_kv * d->hidden * d->rank) : 0);
+  p.qtg_off = p.absQ_off + (absorbed ? align_up(2 * (size_t)d->batch * d->heads_kv * 2 * 4 * d->rank) : 0);
+  const bool chained = p.path == LOWRAM_PATH_CHAIN;
+  p.bytes = p.qtg_off + (chained ? align_up(4 * (size_t)d->batch * d->heads_kv * QTG_G * d->rank) : 0);
   return p;
 }
 
@@ -276,7 +293,7 @@ lowram_status check_decode_inputs(const lowram_dims *d, int32_t layer, const low
 
 // True when the chained attend kernel ranks the chunk scores itself.
 bool attend_selects(const lowram_dims *d, const DecodePlan &p) {
-  return p.tps > 0 && n_chunks(d) <= CHAIN_SELECT_MAX_NC;
+  return p.path == LOWRAM_PATH_CHAIN && n_chunks(d) <= CHAIN_SELECT_MAX_NC;
 }
 
 AttendArgs make_attend(const lowram_dims *d, int32_t layer, const lowram_model *m,
@@ -299,8 +316,13 @@ AttendArgs make_attend(const lowram_dims *d, int32_t layer, const lowram_model *
   a.r = d->rank; a.F = d->hidden; a.N = d->n_ctx; a.C = d->chunk; a.T = d->n_tail;
   a.k_eff = p.k_eff; a.n_res = d->n_res; a.layer = layer;
   a.g = d->heads_q / d->heads_kv; a.cps = p.cps; a.n_split = p.n_split; a.PW = p.PW;
-  a.tps = p.tps; a.tail_per_split = p.tail_per_split;
+  a.path = p.path; a.tps = p.tps; a.tail_per_split = p.tail_per_split;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)d->head_dim);
+  if (p.path == LOWRAM_PATH_CHAIN && ws) a.qtg = reinterpret_cast<const float *>((char *)ws + p.qtg_off);
+  if (p.path == LOWRAM_PATH_ABSORB && ws) {
+    a.absA = reinterpret_cast<uint16_t *>((char *)ws + p.absA_off);
+    a.absQ = reinterpret_cast<uint16_t *>((char *)ws + p.absQ_off);
+  }
   return a;
 }
 
@@ -341,13 +363,7 @@ lowram_status lowram_decode_kernel(const lowram_dims *d, int32_t *path) {
   lowram_status st = check_dims(d);
   if (st != LOWRAM_OK) return st;
   if (!path) return fail(LOWRAM_E_INVALID, "path is NULL");
-  const DecodePlan p = decode_plan(d);
-  if (p.k_eff == 0) *path = LOWRAM_PATH_NONE;
-  else if (p.tps > 0) *path = LOWRAM_PATH_CHAIN;
-  else {
-    const AttendArgs a = make_attend(d, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p, nullptr);
-    *path = mfma_supported(a, d->act, d->coeff, d->resid) ? LOWRAM_PATH_MFMA : LOWRAM_PATH_VALU;
-  }
+  *path = decode_plan(d).path;
   return LOWRAM_OK;
 }
 
@@ -428,11 +444,18 @@ lowram_status run_select(const lowram_dims *d, int32_t layer, const lowram_model
   int32_t *sel = reinterpret_cast<int32_t *>((char *)ws + p.sel_off);
   double *sp = reinterpret_cast<double *>((char *)ws + p.sp_off);
   double *sc = reinterpret_cast<double *>((char *)ws + p.sc_off);
-  return hip_status(launch_select(d->act, q, (long)d->heads_q * d->head_dim, m->basis, c->landmark,
-                                  d->batch, d->heads_q, d->heads_kv, d->head_dim, d->rank,
-                                  n_chunks(d), (int)D, layer, with_topk ? p.k_eff : 0, sel, sel_out,
-                                  sp, with_topk ? sc : nullptr, (hipStream_t)stream),
-                    "lowram_decode_select");
+  lowram_status st = hip_status(launch_select(d->act, q, (long)d->heads_q * d->head_dim, m->basis, c->landmark,
+                                              d->batch, d->heads_q, d->heads_kv, d->head_dim, d->rank,
+                                              n_chunks(d), (int)D, layer, with_topk ? p.k_eff : 0, sel, sel_out,
+                                              sp, with_topk ? sc : nullptr, (hipStream_t)stream,
+                                              p.path == LOWRAM_PATH_CHAIN
+                                                  ? reinterpret_cast<float *>((char *)ws + p.qtg_off)
+                                                  : nullptr),
+                                "lowram_decode_select");
+  if (st != LOWRAM_OK || p.path != LOWRAM_PATH_ABSORB) return st;
+  // absorbed path: A = W1 U_{l,h} and q~ for this call, next to the selection
+  const AttendArgs a = make_attend(d, layer, m, c, q, nullptr, nullptr, ws, p, nullptr);
+  return hip_status(launch_absorb(a, (hipStream_t)stream), "lowram_decode_select");
 }
 
 }  // namespace
@@ -513,7 +536,7 @@ lowram_status lowram_reuse_tile_bytes(const lowram_dims *d, size_t *bytes) {
   if (st != LOWRAM_OK) return st;
   if (!bytes) return fail(LOWRAM_E_INVALID, "bytes is NULL");
   const DecodePlan p = decode_plan(d);
-  if (p.tps == 0)
+  if (p.path != LOWRAM_PATH_CHAIN)
     return fail(LOWRAM_E_UNSUPPORTED, "reuse needs the register-chained attend kernel (see lowram_decode_kernel)");
   *bytes = chain_tile_bytes(d->hidden);
   return LOWRAM_OK;
@@ -528,7 +551,7 @@ lowram_status lowram_decode_attn_reuse(const lowram_dims *d, int32_t layer, cons
   if (st != LOWRAM_OK) return st;
   const DecodePlan p = decode_plan(d);
   if ((st = check_decode_inputs(d, layer, m, c, p)) != LOWRAM_OK) return st;
-  if (p.tps == 0 || p.k_eff == 0)
+  if (p.path != LOWRAM_PATH_CHAIN)
     return fail(LOWRAM_E_UNSUPPORTED, "reuse needs the register-chained attend kernel and a selected chunk");
   if (p.k_eff > CHAIN_SELECT_MAX_NC)
     return fail(LOWRAM_E_UNSUPPORTED, "reuse assigns slots to at most %d selected chunks (top_k %d)",

@@ -126,13 +126,18 @@ lowram_status lowram_workspace_bytes(const lowram_dims *dims, int32_t op, size_t
  *   LOWRAM_PATH_CHAIN  register-chained kernel (d_h = 128, C = 128, g <= 4,
  *                      compiled (r, F, dtype) shapes); with n_c <= 512 it also
  *                      ranks the chunk scores in its prologue;
+ *   LOWRAM_PATH_ABSORB head dim 256 (F = 512, r = 384 or 512, g <= 4): the
+ *                      first predictor layer absorbed into the basis
+ *                      (A = W1 U_{l,h}, formed per call in the workspace) and
+ *                      logits taken in coefficient space, on the matrix cores;
  *   LOWRAM_PATH_MFMA   one workgroup per selected chunk on the matrix cores
- *                      (bf16 shapes compiled for it);
+ *                      (other bf16 shapes compiled for it);
  *   LOWRAM_PATH_VALU   vector-ALU kernel (float32 and every other shape);
  *   LOWRAM_PATH_NONE   no chunk is selected (top_k = 0): only the tail.
  * The choice depends on the dims alone; results agree with the oracle on
  * every path. */
-enum { LOWRAM_PATH_NONE = 0, LOWRAM_PATH_CHAIN = 1, LOWRAM_PATH_MFMA = 2, LOWRAM_PATH_VALU = 3 };
+enum { LOWRAM_PATH_NONE = 0, LOWRAM_PATH_CHAIN = 1, LOWRAM_PATH_MFMA = 2, LOWRAM_PATH_VALU = 3,
+       LOWRAM_PATH_ABSORB = 4 };
 lowram_status lowram_decode_kernel(const lowram_dims *dims, int32_t *path);
 
 /* Storage accounting (host only).  *dense = M_KV = 2 L H_kv d_h N s for the
@@ -179,7 +184,8 @@ lowram_status lowram_decode_attn(const lowram_dims *dims, int32_t layer, const l
  * them separately.  They communicate through the workspace, which must be the
  * same buffer with the same dims and layer for all three.
  *   select:  chunk scores and top-k (writes the selection into the workspace
- *            and, if sel_out != NULL, into sel_out);
+ *            and, if sel_out != NULL, into sel_out); on LOWRAM_PATH_ABSORB
+ *            also W1 U_{l,h} and U_{l,h}^T q_g of this call into the workspace;
  *   attend:  rebuild-and-attend over the selected chunks and the tail, writing
  *            per-split softmax partials into the workspace;
  *   combine: merges the partials and applies the hoisted second predictor
@@ -203,10 +209,11 @@ lowram_status lowram_decode_combine(const lowram_dims *dims, int32_t layer, cons
  * slots inside the attend kernel: a chunk already held is a hit; the others,
  * in ascending chunk order, take the least recently used slots that no hit of
  * this step holds (older use first, then lower slot) and are stored there once
- * rebuilt; when slots run out a chunk is rebuilt and not stored.  A workgroup
- * whose chunks all hit reads their keys back instead of streaming and
- * multiplying their coefficients; the keys read back are the bits the kernel
- * would compute, so the output equals lowram_decode_attn's bit for bit.
+ * rebuilt; when slots run out a chunk is rebuilt and not stored.  A wave
+ * whose tile hits reads its keys back instead of multiplying the coefficients
+ * by the basis (the coefficients are still read: the logits are taken from
+ * them); the keys read back are the bits the kernel would compute, so the
+ * output equals lowram_decode_attn's bit for bit.
  * The slot bookkeeping has two halves: clock's parity names the current one,
  * each call writes the updated table into the other half and advances clock.
  * The caller allocates the table and, before its first use, fills slot_chunk

@@ -41,6 +41,9 @@ class Shape:
     evict_keep: float = 1.0     # fraction of chunks kept by eviction
     n_obs: int = 0              # observation queries per (b, layer) for eviction
     key_cols: int = 0           # 0: all D spectrum columns drawn
+    key_scale: float = 1.0      # keys drawn with this standard deviation per element
+    q_scale: float = 1.0        # queries drawn with this standard deviation per element
+    w1_scale: float = 1.0       # factor on the value model's first layer (and so on the predictor's)
 
     # ----- derived sizes -------------------------------------------------
     @property

@@ -16,6 +16,11 @@ relies on:
   x20 outlier tokens;
 * queries are i.i.d. N(0, 1).
 
+Shape.key_scale and Shape.q_scale widen the key and query distributions (keys
+of norm ~100, queries x16) to drive the softmax into its peaked regime;
+Shape.w1_scale scales the value model's first layer (1 / key_scale keeps the
+hidden activations and values at their usual scale).
+
 The basis handed to the method is the population principal frame Q[:, :r]
 (the leading principal directions of the generated keys), and the predictor
 handed to the method is MLP_true itself.
@@ -112,7 +117,7 @@ def make(s: Shape, seed_offset: int = 0, steps: int | None = None, noise_scale: 
     act = s.act
     work = np.float64 if act in (F64, F32) else np.float32
     m = s.m_cols
-    sig = spectrum(D)[:m]
+    sig = s.key_scale * spectrum(D)[:m]
     n_out = int(round(s.outlier_frac * N))
 
     out = {
@@ -138,7 +143,7 @@ def make(s: Shape, seed_offset: int = 0, steps: int | None = None, noise_scale: 
         out["k_tail"][b] = store(kfull[:, :, N:], act)
 
         mrng = _rng(cid, b, STREAM_MLP)
-        w1 = store(mrng.standard_normal((G, Hkv, F, dh)) / np.sqrt(dh), act)
+        w1 = store(s.w1_scale * mrng.standard_normal((G, Hkv, F, dh)) / np.sqrt(dh), act)
         b1 = store(0.1 * mrng.standard_normal((G, Hkv, F)), act)
         w2 = store(mrng.standard_normal((G, Hkv, dh, F)) / np.sqrt(F), act)
         b2 = store(0.1 * mrng.standard_normal((G, Hkv, dh)), act)
@@ -177,7 +182,7 @@ def make_queries(s: Shape, steps: int, seed_offset: int = 0) -> np.ndarray:
     q = np.empty((steps, s.G, s.B, s.Hq, s.dh), dtype=_np_dtype(s.act))
     for b in range(s.B):
         draws = _rng(cid, b, STREAM_Q).standard_normal((steps, s.G, s.Hq, s.dh))
-        q[:, :, b] = store(draws, s.act)
+        q[:, :, b] = store(s.q_scale * draws, s.act)
     return q
 
 

@@ -41,11 +41,13 @@ def full(request):
     P().compress(d, model_of(dev), dev["k"], dev["v"], cache)
     torch.cuda.synchronize()
     pre = cache_to_host(cache)
+    keep = None
     if s.evict_keep < 1.0:
-        cache, d, _ = P().evict(d, model_of(dev), cache, to_dev(inp["obs_q"]), s.keep_chunks)
+        cache, d, keep = P().evict(d, model_of(dev), cache, to_dev(inp["obs_q"]), s.keep_chunks)
         torch.cuda.synchronize()
+        keep = to_host(keep)
     print(f"[full] {request.param}: compressed", flush=True)
-    yield dict(s=s, inp=inp, dev=dev, d=d, cache=cache, pre=pre, host=cache_to_host(cache))
+    yield dict(s=s, inp=inp, dev=dev, d=d, cache=cache, pre=pre, host=cache_to_host(cache), keep=keep)
     del dev, cache
     torch.cuda.empty_cache()
 
@@ -68,7 +70,27 @@ def test_full_selection_and_outputs(full):
             ref, rsel = O.decode_layer(host, inp, s, layer, inp["q"][0, layer], s.k, N=d.n_ctx)
             assert np.array_equal(rsel, sel_h)
             ok, worst = within_tol(f32_of(out), ref)
-            assert ok, f"layer {layer}: worst excess {worst}"
+            assert ok, f"layer {layer}: worst |err|/tol {worst:.3f}"
+
+
+def test_full_eviction_matches_oracle(full):
+    """The composed workload's eviction at full size (1024 -> 256 chunks per
+    sequence): kept chunks, coefficients, landmarks, CSR pointers and every
+    live residual row against the oracle's eviction of the same stored cache."""
+    s, inp, pre, host, d = (full[k] for k in ("s", "inp", "pre", "host", "d"))
+    if s.evict_keep >= 1.0:
+        pytest.skip("no eviction in this workload")
+    ref = O.evict(pre, inp, s, inp["obs_q"], s.keep_chunks)
+    assert np.array_equal(full["keep"], ref["keep"])
+    assert np.array_equal(host["coeff"], ref["coeff"])
+    assert np.array_equal(host["landmark"], ref["landmark"])
+    assert np.array_equal(host["res_ptr"], ref["res_ptr"])
+    live = ref["res_ptr"][..., -1]
+    assert d.n_res == live.max()  # the evicted cache is sized to the largest head's rows
+    for i in np.ndindex(live.shape):
+        n = live[i]
+        assert np.array_equal(host["res_idx"][i][:n], ref["res_idx"][i][:n]), i
+        assert np.array_equal(host["res_val"][i][:n], ref["res_val"][i][:n]), i
 
 
 def test_full_residual_sets_sampled(full):

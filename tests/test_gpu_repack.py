@@ -146,7 +146,7 @@ def test_decode_after_repack_matches_oracle(grown):
                                        N=d2.n_ctx)
             assert np.array_equal(to_host(sel), rsel), (layer, top_k)
             ok, worst = within_tol(f32_of(out), ref)
-            assert ok, f"layer {layer} top_k {top_k}: worst excess {worst}"
+            assert ok, f"layer {layer} top_k {top_k}: worst |err|/tol {worst:.3f}"
 
 
 def test_repack_twice_and_from_empty():

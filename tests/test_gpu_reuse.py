@@ -27,6 +27,9 @@ STEPS = 6
 CASES = {
     "llama8b-small": small(LLAMA8B_32K, k=6, T=100),
     "composed-small": small(COMPOSED_128K, k=3, T=72),
+    # 1024 chunks: the kernel reads the separate top-k's selection and stages
+    # all of it for the slot assignment
+    "chain-nc-1024": small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=131072, T=16, k=9),
 }
 
 
@@ -132,4 +135,4 @@ def test_reuse_step_matches_oracle(stream):
         torch.cuda.synchronize()
         want, _ = O.decode_layer(host, inp, s, 0, stream["qs"][st, 0], d.top_k, N=d.n_ctx)
         ok, worst = within_tol(out.float().cpu().numpy().astype(np.float64), want)
-        assert ok, (st, worst)
+        assert ok, f"step {st}: worst |err|/tol {worst:.3f}"

@@ -52,3 +52,17 @@ def test_chain_kernel_has_no_scratch():
     for name, v in reuse.items():
         assert v.get("ScratchSize", 999) <= 16, (name, v)
         assert v.get("VGPRs", 999) <= 256, (name, v)
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
+def test_absorbed_kernel_has_no_scratch():
+    """The head-dim-256 attend kernel (absorbed first layer) and its A = W1 U
+    kernel: every instantiation within 256 VGPRs and without scratch, so that
+    a two-wave-per-SIMD launch holds (and no spill traffic reaches HBM)."""
+    use = resource_usage("k_attend_absorb.hip")
+    kernels = {k: v for k, v in use.items() if "k_attend_absorb" in k or "k_absorb" in k}
+    assert len([k for k in kernels if "k_attend_absorb" in k]) == 4, sorted(kernels)
+    for name, v in kernels.items():
+        assert v.get("ScratchSize") == 0, (name, v)
+        assert v.get("VGPRs Spill") == 0, (name, v)
+        assert v.get("VGPRs", 999) <= 256, (name, v)
