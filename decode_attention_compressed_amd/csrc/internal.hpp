@@ -39,6 +39,7 @@ struct AttendArgs {
   int tps, tail_per_split;      // chained / absorbed kernels: tiles (slices) and tail tokens per split
   float scale_log2;             // log2(e) / sqrt(dh)
   const float *qtg;             // chained kernel: [B][Hkv][QTG_G][r] float32 U_{l,h}^T q_g (select stage)
+  const uint16_t *qfrag;        // per-chunk kernel: [B][Hkv][2][16][r] hi/lo operand columns (select stage)
   // absorbed kernel (head dim 256): workspace of the absorbed first layer
   uint16_t *absA;               // [B][Hkv][F][r] fp16: -log2(e) W1 U_{l,h} (int8: times the rank scales)
   uint16_t *absQ;               // [B][Hkv][2][4][r] fp16: U_{l,h}^T q_g, hi then lo parts
@@ -59,14 +60,26 @@ struct CombineArgs {
 // written to scores [B][Hkv][n_c], and if k_eff > 0 (scores required) the
 // selection into sel and, optionally, a copy into sel_out.
 inline int select_rank_blocks(int r) { return (r + 63) / 64; }
-// With qtg the partial-score kernel also writes U_{l,h}^T q_g of each of the
-// first QTG_G query heads of every kv head in float32, qtg [B][Hkv][QTG_G][r]
-// (rows past the group are zero); heads per kv head must then be <= QTG_G.
+// Besides the scores, the partial-score kernel can write q~_g = U_{l,h}^T q_g
+// of the query heads of every kv head, for the kernels that take logits in
+// coefficient space:
+//  qtg:   float32 [B][Hkv][QTG_G][r] (g <= QTG_G; rows past the group zero),
+//         the chained kernel's form;
+//  qfrag: 16-bit [B][Hkv][2][16][r] MFMA operand columns of hi/lo halves
+//         (mode 1: bf16; mode 2: fp16 of q~ times the int8 rank scales
+//         `scale` [B][r]), the per-chunk kernel's form (g <= 16).
 constexpr int QTG_G = 4;
+constexpr int QTG_MAX = 16;
+struct QOut {
+  float *qtg = nullptr;
+  uint16_t *qfrag = nullptr;
+  const uint16_t *scale = nullptr;
+  int mode = 0;
+};
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
-                         double *part, double *scores, hipStream_t st, float *qtg = nullptr);
+                         double *part, double *scores, hipStream_t st, const QOut &qo = QOut());
 hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st);
 // True when the per-chunk MFMA kernel covers these shapes (else the VALU kernel)
 bool mfma_supported(const AttendArgs &a, int act, int coeff, int resid);

@@ -9,8 +9,10 @@
 //      in flight in registers.  bf16 coefficients and basis enter as stored;
 //      int8 coefficients are exact in fp16 and their per-channel scale is
 //      folded into an fp16 basis slab.
-//   2. logits = K_hat . q^T for the g query heads of h (16x16x32 MFMA, g padded
-//      to 16); online softmax in log2 units; p rounded to fp16 in LDS.
+//   2. logits in coefficient space, q_g . k_hat_t = (U^T q_g) . c_t, on the
+//      coefficient slabs staged for step 1 (16x16x32 MFMA, heads padded to 16)
+//      with U^T q_g from the select stage split into hi/lo halves; online
+//      softmax in log2 units; p rounded to fp16 in LDS.
 //   5. residual rows of the tile scattered into a dense, transposed delta
 //      tile; accV += p . delta (16x16x32 MFMA).
 //   3. H = SiLU(K_hat . W1^T + b1) per 64-wide hidden block (32x32x16 MFMA),
@@ -72,6 +74,9 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ uint16_t h16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 __device__ __forceinline__ float f16f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
@@ -97,8 +102,7 @@ struct MfmaSmem {
   static constexpr int M13 = A1 > A3 ? A1 : A3;
   static constexpr int REGION_A = M13 > A5 ? M13 : A5;          // 16-bit elements
   static constexpr int KS_OFF = REGION_A;
-  static constexpr int QS_OFF = KS_OFF + TM * KS_LD;
-  static constexpr int PS_OFF = QS_OFF + 16 * KS_LD;
+  static constexpr int PS_OFF = KS_OFF + TM * KS_LD;
   static constexpr int END16 = PS_OFF + 16 * PS_LD;
   static constexpr int FLOATS = 4 * 16 * 2 + 16 * 3;            // red, red2, ms, ls, al
   static constexpr size_t BYTES = (size_t)END16 * 2 + FLOATS * 4;
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(256, (dual_occupancy<DH, NF64>() ? 2 : 1)) void k_a
   uint16_t *Cs = sm16, *Us = sm16 + TM * CS_LD;               // step 1
   uint16_t *W1s = sm16, *Hs = sm16 + 64 * KS_LD;              // steps 3/4
   uint16_t *Dt = sm16;                                         // step 5: delta^T [DH][TM+8]
-  uint16_t *Ks = sm16 + S::KS_OFF, *Qs = sm16 + S::QS_OFF, *Ps = sm16 + S::PS_OFF;
+  uint16_t *Ks = sm16 + S::KS_OFF, *Ps = sm16 + S::PS_OFF;
   float *fl = reinterpret_cast<float *>(sm16 + S::END16);
   float *red = fl, *red2 = fl + 64, *ms = fl + 128, *ls = ms + 16, *al = ls + 16;
 
@@ -300,13 +304,18 @@ __global__ __launch_bounds__(256, (dual_occupancy<DH, NF64>() ? 2 : 1)) void k_a
   const uint16_t *rsc = a.res_scale ? a.res_scale + bh * DH : nullptr;
   const int32_t *selp = a.sel + ((long)b * a.Hkv + h) * a.k_eff;
 
-  {  // query rows of this kv head as fp16, zero-padded to 16
-    const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + ((long)b * a.Hq + (long)h * g) * DH;
-    for (int i = tid; i < 16 * DH; i += 256) {
-      const int gi = i / DH, d = i % DH;
-      Qs[gi * KS_LD + d] = gi < g ? h16(bf16_bits_to_f32(qb[gi * DH + d])) : (uint16_t)0;
-    }
-  }
+  // Logit operand (16x16x32 B operand: column lane & 15, ranks 8 (lane >> 4)
+  // .. + 8 of each k-step), written by the select stage: x = U^T q_g (times
+  // the int8 rank scales) as hi = x rounded to the codes' MFMA type and lo =
+  // (x - hi) rounded, so hi + lo carries x to about 2^-16 (bf16) or 2^-22
+  // (fp16) relative where a key rebuilt and rounded to fp16 would move logits
+  // in the hundreds by ~0.1.  With 2g <= 16 column c of tile 0 holds hi of
+  // head c or lo of head c - g, added after the MFMAs; with g > 8 tile 1 holds
+  // the lo halves and accumulates into the same logits.
+  const bool q_two = g > 8;
+  // (wave-uniform base, 32-bit lane offset: one VGPR for the address)
+  const uint16_t *qfb = a.qfrag + ((long)b * a.Hkv + h) * 2 * 16 * r;
+  uint32_t qfo = (uint32_t)((lane & 15) * r + 8 * (lane >> 4));
   if (tid < 16) { ms[tid] = -INFINITY; ls[tid] = 0.f; al[tid] = 0.f; }
 
   f32x4 accH[NF64], accV[NVT];
@@ -321,6 +330,9 @@ __global__ __launch_bounds__(256, (dual_occupancy<DH, NF64>() ? 2 : 1)) void k_a
     const int j = selp[slot];
     for (int t0 = 0; t0 < C; t0 += TM) {
       const long row0 = (long)j * C + t0;
+      // the operand loads are the same for every tile: an opaque offset keeps
+      // them in the tile loop rather than hoisted into 8 NSLAB live registers
+      asm volatile("" : "+v"(qfo));
       // ---- step 1: K_hat^T = U . C^T --------------------------------------
       f32x16 acc1[NT1][2];
 #pragma unroll
@@ -329,6 +341,8 @@ __global__ __launch_bounds__(256, (dual_occupancy<DH, NF64>() ? 2 : 1)) void k_a
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc1[mi][ni][i] = 0.f;
+      // logits of the wave's 32 tokens (rows 32 w + 16 mi ..)
+      f32x4 acc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       // ring of PFD slabs in flight, PFD-1 ahead of the one being multiplied
       int e0, e1, rt = -1;
       u32x4 rv = v4(0, 0, 0, 0);
@@ -394,6 +408,26 @@ __global__ __launch_bounds__(256, (dual_occupancy<DH, NF64>() ? 2 : 1)) void k_a
                 for (int ni = 0; ni < 2; ++ni) acc1[mi][ni] = mfma32(au[cur][mi], bc[cur][ni], acc1[mi][ni]);
             }
           }
+          // step 2's logits over this slab's ranks: coefficient rows of the wave's tokens
+#pragma unroll
+          for (int ks = 0; ks < RS / 32; ++ks) {
+            const int kof = 32 * ks + 8 * (lane >> 4);
+            const typename ST::frag qb = __builtin_bit_cast(typename ST::frag, gld16(qfb + (qfo + (uint32_t)(s * RS + 32 * ks))));
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+              acc2[mi] = mfma16(ST::ld(Cs + (32 * w + 16 * mi + (lane & 15)) * CS_LD + kof), qb, acc2[mi]);
+          }
+          if (q_two) {  // lo halves of g > 8 heads (second operand tile)
+#pragma unroll
+            for (int ks = 0; ks < RS / 32; ++ks) {
+              const int kof = 32 * ks + 8 * (lane >> 4);
+              const typename ST::frag ql =
+                  __builtin_bit_cast(typename ST::frag, gld16(qfb + (qfo + (uint32_t)(16 * r + s * RS + 32 * ks))));
+#pragma unroll
+              for (int mi = 0; mi < 2; ++mi)
+                acc2[mi] = mfma16(ST::ld(Cs + (32 * w + 16 * mi + (lane & 15)) * CS_LD + kof), ql, acc2[mi]);
+            }
+          }
           __syncthreads();
         });
       }
@@ -424,16 +458,13 @@ __global__ __launch_bounds__(256, (dual_occupancy<DH, NF64>() ? 2 : 1)) void k_a
           }
       __syncthreads();
 
-      // ---- step 2: logits and online softmax ----------------------------
-      f32x4 acc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int ks = 0; ks < DH / 32; ++ks) {
-        const int kof = 32 * ks + 8 * (lane >> 4);
-        const f16x8 bq = ldh8(Qs + (lane & 15) * KS_LD + kof);
+      // ---- step 2: online softmax ----------------------------------------
+      // with 2g <= 16: hi (column gi) + lo (column g + gi) of each head's logit
+      if (!q_two)
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
-          acc2[mi] = mfma16(ldh8(Ks + (32 * w + 16 * mi + (lane & 15)) * KS_LD + kof), bq, acc2[mi]);
-      }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc2[mi][i] += __shfl_down(acc2[mi][i], g, 16);
       const int gi = lane & 15;
       float mx = -INFINITY;
 #pragma unroll
@@ -637,6 +668,7 @@ hipError_t launch_attend_valu(int act, int coeff, int resid, const AttendArgs &a
 
 template <int DH, int NF64, int NSLAB, typename TC, typename TR>
 static hipError_t go(const AttendArgs &a, hipStream_t st) {
+  if (a.n_split > 0 && !a.qfrag) return hipErrorInvalidValue;  // logits need the select stage's U^T q
   const size_t smem = MfmaSmem<DH>::BYTES;
   static const bool lds_ok = (allow_dynamic_lds(k_attend_mfma<DH, NF64, NSLAB, TC, TR>, smem), true);
   (void)lds_ok;

@@ -123,18 +123,20 @@ __device__ __forceinline__ float xpose_sum_f32(float (&v)[R], int lane) {
 // rank block) share an XCD and its L2 copy of those landmark columns.
 constexpr int SEL_RB = 64;
 
-template <typename TA, int DH>
+template <typename TA, int DH, int QG>
 __global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q, long q_bstride,
                                                         const TA *__restrict__ basis,
                                                         const float *__restrict__ landmark, int Hq,
                                                         int Hkv, int r, int n_c, int D, int layer,
-                                                        double *__restrict__ part, float *__restrict__ qtg) {
+                                                        double *__restrict__ part, float *__restrict__ qtg,
+                                                        uint16_t *__restrict__ qfrag,
+                                                        const uint16_t *__restrict__ qf_scale, int qf_mode) {
   constexpr int RPS = DH / 32;  // basis rows per slice
   __shared__ double qsum[DH];
   __shared__ double qtp[4][SEL_RB];
   __shared__ double qt[SEL_RB];
-  __shared__ float qg[QTG_G][DH];             // q of each query head (qtg only)
-  __shared__ float qtpg[4][QTG_G][SEL_RB];    // per-wave parts of q~_g (qtg only)
+  __shared__ float qg[QG][DH];             // q of each query head (qtg only)
+  __shared__ float qtpg[4][QG][SEL_RB];    // per-wave parts of q~_g (qtg only)
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int NRB = gridDim.x;
   int rb, h, b;
@@ -174,37 +176,35 @@ __global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q
     double sq = 0.0;
     for (int gi = 0; gi < grp; ++gi) sq += to_f64(qb[gi * DH + tid]);
     qsum[tid] = sq;
-    if (qtg)
-      for (int gi = 0; gi < QTG_G; ++gi) qg[gi][tid] = gi < grp ? to_f32(qb[gi * DH + tid]) : 0.f;
+    if (qtg || qfrag)
+      for (int gi = 0; gi < QG; ++gi) qg[gi][tid] = gi < grp ? to_f32(qb[gi * DH + tid]) : 0.f;
   }
   __syncthreads();
-  if (qtg) {  // q~_g of each query head over the block's ranks, in float32
-    float acc[QTG_G][8];
+  // q~_g of each query head over the block's ranks, in float32, four heads at
+  // a time (groups past the kv head's query heads are skipped: zero rows)
+  const int ng4 = (min(grp, QG) + 3) / 4;
+  if (qtg || qfrag)
+    for (int g4 = 0; g4 < ng4; ++g4) {
+      float acc[4][8];
 #pragma unroll
-    for (int gi = 0; gi < QTG_G; ++gi)
+      for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
+        for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
 #pragma unroll
-    for (int k = 0; k < RPS; ++k) {
-      double u[8];
-      Load8<TA>::f64(raw[k], u);
+      for (int k = 0; k < RPS; ++k) {
+        double u[8];
+        Load8<TA>::f64(raw[k], u);
 #pragma unroll
-      for (int gi = 0; gi < QTG_G; ++gi) {
-        const float wq = qg[gi][sl + 32 * k];
+        for (int gi = 0; gi < 4; ++gi) {
+          const float wq = qg[4 * g4 + gi][sl + 32 * k];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[gi][e] = fmaf((float)u[e], wq, acc[gi][e]);
+          for (int e = 0; e < 8; ++e) acc[gi][e] = fmaf((float)u[e], wq, acc[gi][e]);
+        }
       }
-    }
 #pragma unroll
-    for (int gi = 0; gi < QTG_G; ++gi) {
-      float v = acc[gi][0];
-      float t[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = acc[gi][e];
-      v = xpose_sum_f32<8, 32>(t, lane);   // rank 8 rg + (lane >> 3), this wave's slices
-      qtpg[w][gi][8 * rg + (lane >> 3)] = v;
+      for (int gi = 0; gi < 4; ++gi)
+        qtpg[w][4 * g4 + gi][8 * rg + (lane >> 3)] = xpose_sum_f32<8, 32>(acc[gi], lane);  // rank 8 rg + (lane >> 3)
     }
-  }
   {
     double acc[8];
 #pragma unroll
@@ -222,11 +222,40 @@ __global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q
   }
   __syncthreads();
   if (tid < SEL_RB) qt[tid] = ((qtp[0][tid] + qtp[1][tid]) + qtp[2][tid]) + qtp[3][tid];
-  if (qtg) {  // [b][h][g][r] for the query heads of h (zero rows past the group)
-    const int gi = tid / SEL_RB, ri = tid % SEL_RB;
-    if (ri < nr)
-      qtg[(((long)b * Hkv + h) * QTG_G + gi) * r + i0 + ri] =
-          ((qtpg[0][gi][ri] + qtpg[1][gi][ri]) + qtpg[2][gi][ri]) + qtpg[3][gi][ri];
+  if (qtg)  // [b][h][QG][r]; rows past the group are zero
+    for (int it = tid; it < QG * SEL_RB; it += 256) {
+      const int gi = it / SEL_RB, ri = it % SEL_RB;
+      if (ri < nr)
+        qtg[(((long)b * Hkv + h) * QG + gi) * r + i0 + ri] =
+            gi < 4 * ng4 ? ((qtpg[0][gi][ri] + qtpg[1][gi][ri]) + qtpg[2][gi][ri]) + qtpg[3][gi][ri] : 0.f;
+    }
+  if (qfrag) {
+    // MFMA operand columns for the per-chunk kernel's coefficient-space logits,
+    // [b][h][2][16][r] 16-bit.  x = q~_g (times the rank scale for int8 codes)
+    // is split into hi = x rounded to the codes' MFMA type (bf16 for bf16
+    // codes, fp16 for int8) and lo = (x - hi) rounded.  With 2g <= 16, tile 0
+    // column c holds hi of head c (c < g) or lo of head c - g (c < 2g); with
+    // g > 8, tile 0 holds the hi halves and tile 1 the lo halves.  Other
+    // columns are zero.
+    const bool two = grp > 8;
+    for (int it = tid; it < 2 * 16 * SEL_RB; it += 256) {
+      const int tile = it / (16 * SEL_RB), c = (it / SEL_RB) % 16, ri = it % SEL_RB;
+      if (ri >= nr || (tile == 1 && !two)) continue;
+      const bool ok = two ? c < grp : c < 2 * grp;
+      const bool lo = two ? tile == 1 : c >= grp;
+      const int gi = ok ? (two ? c : (lo ? c - grp : c)) : 0;
+      float x = ok ? ((qtpg[0][gi][ri] + qtpg[1][gi][ri]) + qtpg[2][gi][ri]) + qtpg[3][gi][ri] : 0.f;
+      uint16_t v;
+      if (qf_mode == 2) {
+        x *= f16_bits_to_f32(qf_scale[(long)b * r + i0 + ri]);
+        const _Float16 xh = (_Float16)x;
+        v = __builtin_bit_cast(uint16_t, lo ? (_Float16)(x - (float)xh) : xh);
+      } else {
+        const uint16_t xh = f32_to_bf16_bits(x);
+        v = lo ? f32_to_bf16_bits(x - bf16_bits_to_f32(xh)) : xh;
+      }
+      qfrag[((((long)b * Hkv + h) * 2 + tile) * 16 + c) * r + i0 + ri] = v;
+    }
   }
   __syncthreads();
 
@@ -752,27 +781,36 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+template <typename TA, int QG>
+static void launch_partial_g(const TA *q, long q_bstride, const TA *basis, const float *landmark, int B,
+                             int Hq, int Hkv, int dh, int r, int n_c, int D, int layer, double *part,
+                             const QOut &qo, hipStream_t st) {
+  const dim3 g(select_rank_blocks(r), Hkv, B);
+  if (dh == 64)
+    hipLaunchKernelGGL((k_select_partial<TA, 64, QG>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qo.qtg, qo.qfrag, qo.scale, qo.mode);
+  else if (dh == 128)
+    hipLaunchKernelGGL((k_select_partial<TA, 128, QG>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qo.qtg, qo.qfrag, qo.scale, qo.mode);
+  else
+    hipLaunchKernelGGL((k_select_partial<TA, 256, QG>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qo.qtg, qo.qfrag, qo.scale, qo.mode);
+}
 template <typename TA>
 static void launch_partial(const TA *q, long q_bstride, const TA *basis, const float *landmark, int B,
                            int Hq, int Hkv, int dh, int r, int n_c, int D, int layer, double *part,
-                           float *qtg, hipStream_t st) {
-  const dim3 g(select_rank_blocks(r), Hkv, B);
-  if (dh == 64)
-    hipLaunchKernelGGL((k_select_partial<TA, 64>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qtg);
-  else if (dh == 128)
-    hipLaunchKernelGGL((k_select_partial<TA, 128>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qtg);
+                           const QOut &qo, hipStream_t st) {
+  if (qo.qfrag && Hq / Hkv > QTG_G)
+    launch_partial_g<TA, QTG_MAX>(q, q_bstride, basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qo, st);
   else
-    hipLaunchKernelGGL((k_select_partial<TA, 256>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qtg);
+    launch_partial_g<TA, QTG_G>(q, q_bstride, basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qo, st);
 }
 
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
-                         double *part, double *scores, hipStream_t st, float *qtg) {
+                         double *part, double *scores, hipStream_t st, const QOut &qo) {
   if (act == LOWRAM_F32)
-    launch_partial<float>((const float *)q, q_bstride, (const float *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qtg, st);
+    launch_partial<float>((const float *)q, q_bstride, (const float *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qo, st);
   else
-    launch_partial<bf16>((const bf16 *)q, q_bstride, (const bf16 *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qtg, st);
+    launch_partial<bf16>((const bf16 *)q, q_bstride, (const bf16 *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qo, st);
   if (!scores) return k_eff > 0 ? hipErrorInvalidValue : hipGetLastError();
   if (k_eff > 0 && n_c <= TK_SMALL) {  // sums the partials itself
     hipLaunchKernelGGL(k_topk_small, dim3(Hkv, B), dim3(TK_NT), 0, st, part, select_rank_blocks(r), Hkv,

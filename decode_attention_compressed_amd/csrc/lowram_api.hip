@@ -82,6 +82,16 @@ struct DecodePlan {
   size_t sel_off, sp_off, sc_off, part_off, absA_off, absQ_off, qtg_off, bytes;
 };
 
+// bytes of the select stage's U^T q_g for the kernels that take logits in
+// coefficient space: float32 rows (chained kernel) or hi/lo operand columns
+// (per-chunk matrix-core kernel)
+size_t qtilde_bytes(const lowram_dims *d, int path) {
+  const size_t bh = (size_t)d->batch * d->heads_kv;
+  if (path == LOWRAM_PATH_CHAIN) return 4 * bh * QTG_G * d->rank;
+  if (path == LOWRAM_PATH_MFMA) return 2 * bh * 2 * 16 * d->rank;
+  return 0;
+}
+
 DecodePlan decode_plan(const lowram_dims *d) {
   DecodePlan p;
   const int n_c = n_chunks(d);
@@ -126,8 +136,7 @@ DecodePlan decode_plan(const lowram_dims *d) {
   const bool absorbed = p.path == LOWRAM_PATH_ABSORB;
   p.absQ_off = p.absA_off + (absorbed ? align_up(2 * (size_t)d->batch * d->heads_kv * d->hidden * d->rank) : 0);
   p.qtg_off = p.absQ_off + (absorbed ? align_up(2 * (size_t)d->batch * d->heads_kv * 2 * 4 * d->rank) : 0);
-  const bool chained = p.path == LOWRAM_PATH_CHAIN;
-  p.bytes = p.qtg_off + (chained ? align_up(4 * (size_t)d->batch * d->heads_kv * QTG_G * d->rank) : 0);
+  p.bytes = p.qtg_off + align_up(qtilde_bytes(d, p.path));
   return p;
 }
 
@@ -319,6 +328,7 @@ AttendArgs make_attend(const lowram_dims *d, int32_t layer, const lowram_model *
   a.path = p.path; a.tps = p.tps; a.tail_per_split = p.tail_per_split;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)d->head_dim);
   if (p.path == LOWRAM_PATH_CHAIN && ws) a.qtg = reinterpret_cast<const float *>((char *)ws + p.qtg_off);
+  if (p.path == LOWRAM_PATH_MFMA && ws) a.qfrag = reinterpret_cast<const uint16_t *>((char *)ws + p.qtg_off);
   if (p.path == LOWRAM_PATH_ABSORB && ws) {
     a.absA = reinterpret_cast<uint16_t *>((char *)ws + p.absA_off);
     a.absQ = reinterpret_cast<uint16_t *>((char *)ws + p.absQ_off);
@@ -444,13 +454,17 @@ lowram_status run_select(const lowram_dims *d, int32_t layer, const lowram_model
   int32_t *sel = reinterpret_cast<int32_t *>((char *)ws + p.sel_off);
   double *sp = reinterpret_cast<double *>((char *)ws + p.sp_off);
   double *sc = reinterpret_cast<double *>((char *)ws + p.sc_off);
+  QOut qo;
+  if (p.path == LOWRAM_PATH_CHAIN) qo.qtg = reinterpret_cast<float *>((char *)ws + p.qtg_off);
+  if (p.path == LOWRAM_PATH_MFMA) {
+    qo.qfrag = reinterpret_cast<uint16_t *>((char *)ws + p.qtg_off);
+    qo.mode = d->coeff == LOWRAM_I8 ? 2 : 1;
+    qo.scale = reinterpret_cast<const uint16_t *>(c->coeff_scale);
+  }
   lowram_status st = hip_status(launch_select(d->act, q, (long)d->heads_q * d->head_dim, m->basis, c->landmark,
                                               d->batch, d->heads_q, d->heads_kv, d->head_dim, d->rank,
                                               n_chunks(d), (int)D, layer, with_topk ? p.k_eff : 0, sel, sel_out,
-                                              sp, with_topk ? sc : nullptr, (hipStream_t)stream,
-                                              p.path == LOWRAM_PATH_CHAIN
-                                                  ? reinterpret_cast<float *>((char *)ws + p.qtg_off)
-                                                  : nullptr),
+                                              sp, with_topk ? sc : nullptr, (hipStream_t)stream, qo),
                                 "lowram_decode_select");
   if (st != LOWRAM_OK || p.path != LOWRAM_PATH_ABSORB) return st;
   // absorbed path: A = W1 U_{l,h} and q~ for this call, next to the selection

@@ -131,7 +131,8 @@ lowram_status lowram_workspace_bytes(const lowram_dims *dims, int32_t op, size_t
  *                      (A = W1 U_{l,h}, formed per call in the workspace) and
  *                      logits taken in coefficient space, on the matrix cores;
  *   LOWRAM_PATH_MFMA   one workgroup per selected chunk on the matrix cores
- *                      (other bf16 shapes compiled for it);
+ *                      (other bf16 shapes compiled for it, g <= 16), logits in
+ *                      coefficient space;
  *   LOWRAM_PATH_VALU   vector-ALU kernel (float32 and every other shape);
  *   LOWRAM_PATH_NONE   no chunk is selected (top_k = 0): only the tail.
  * The choice depends on the dims alone; results agree with the oracle on
@@ -184,8 +185,9 @@ lowram_status lowram_decode_attn(const lowram_dims *dims, int32_t layer, const l
  * them separately.  They communicate through the workspace, which must be the
  * same buffer with the same dims and layer for all three.
  *   select:  chunk scores and top-k (writes the selection into the workspace
- *            and, if sel_out != NULL, into sel_out); on LOWRAM_PATH_ABSORB
- *            also W1 U_{l,h} and U_{l,h}^T q_g of this call into the workspace;
+ *            and, if sel_out != NULL, into sel_out); also U_{l,h}^T q_g of
+ *            every query head of this call into the workspace on the CHAIN,
+ *            MFMA and ABSORB paths, and W1 U_{l,h} on LOWRAM_PATH_ABSORB;
  *   attend:  rebuild-and-attend over the selected chunks and the tail, writing
  *            per-split softmax partials into the workspace;
  *   combine: merges the partials and applies the hoisted second predictor

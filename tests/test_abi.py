@@ -321,16 +321,19 @@ def test_decode_workspace_counts_the_partials_of_each_attend_kernel():
     up = lambda x: (x + 255) // 256 * 256
     # qwen4b-64k runs the absorbed kernel: 8 splits of 8 slices per (b, h) for
     # 256 workgroups over the two halves of F, a chunk row and a tail row per
-    # split, then A = W1 U (bf16 [B][Hkv][F][r]) and q~ (bf16 hi/lo [B][Hkv][2][4][r])
+    # split, then A = W1 U (fp16 [B][Hkv][F][r]) and q~ (fp16 hi/lo [B][Hkv][2][4][r])
     s = QWEN4B_64K
     assert P.decode_kernel(dims_of(s)) == "absorb"
     absorbed = up(2 * s.B * s.Hkv * s.F * s.r) + up(2 * s.B * s.Hkv * 2 * 4 * s.r)
     assert P.workspace_bytes(dims_of(s), L.OP_DECODE) == _decode_ws_expected(s, 2 * 8) + absorbed
     # eight query heads per kv head: the per-chunk matrix-core kernel, one partial
-    # per selected chunk, each carrying a share of the tail (no separate tail partial)
+    # per selected chunk, each carrying a share of the tail (no separate tail
+    # partial), then the select stage's logit operand: 16-bit hi/lo columns of
+    # U^T q_g, [B][Hkv][2][16][r]
     s8 = QWEN4B_64K.replace(Hq=32)
     assert P.decode_kernel(dims_of(s8)) == "mfma"
-    assert P.workspace_bytes(dims_of(s8), L.OP_DECODE) == _decode_ws_expected(s8, s8.k)
+    assert P.workspace_bytes(dims_of(s8), L.OP_DECODE) == (_decode_ws_expected(s8, s8.k)
+                                                           + up(2 * s8.B * s8.Hkv * 2 * 16 * s8.r))
     # nothing selected: one tail partial per (b, h)
     d0 = P.with_(dims_of(s), top_k=0)
     assert P.workspace_bytes(d0, L.OP_DECODE) == _decode_ws_expected(s.replace(k=0), 1)
