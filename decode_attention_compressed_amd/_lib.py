@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(HERE, "liblowram.so")
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = range(5)
 F32, BF16, F16, I8 = range(4)
 OP_COMPRESS, OP_DECODE, OP_EVICT, OP_DENSE, OP_REPACK, OP_FIT, OP_BASIS = range(7)
+NOALLOC_SCRATCH_BYTES = 32 << 20   # LOWRAM_NOALLOC_SCRATCH_BYTES
 
 DIM_FIELDS = ("batch", "layers", "heads_q", "heads_kv", "head_dim", "rank", "hidden", "n_ctx",
               "chunk", "top_k", "n_tail", "n_res", "act", "coeff", "resid")
@@ -67,6 +68,7 @@ SIGNATURES = {
     "lowram_fit_predictor": [P(Dims), P(Model), vp, vp, i32, ctypes.c_float, P(Predictor), vp, vp, sz, vp],
     "lowram_key_basis": [P(Dims), vp, i32, vp, vp, sz, vp],
     "lowram_reuse_tile_bytes": [P(Dims), P(sz)],
+    "lowram_decode_attn_noalloc": [P(Dims), i32, P(Model), P(Cache), vp, vp, vp, vp, vp, vp],
     "lowram_decode_attn_reuse": [P(Dims), i32, P(Model), P(Cache), vp, vp, vp, vp, vp, P(Reuse), vp, vp, sz, vp],
     "lowram_dense_decode_attn": [P(Dims), vp, vp, vp, i32, i64, vp, vp, sz, vp],
     "lowram_status_string": [i32],

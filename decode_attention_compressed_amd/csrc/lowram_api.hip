@@ -5,11 +5,19 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "internal.hpp"
 
 using namespace lowram;
+
+// Device memory of lowram_decode_attn_noalloc: its decode workspace (chunk
+// selection, partial scores, split partials).  Every GPU the library runs on
+// holds one copy, at an address of its own, until the process ends.  Host code
+// never passes this name to a kernel or a copy: it takes the device address
+// from hipGetSymbolAddress once per device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[LOWRAM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -789,6 +797,59 @@ lowram_status lowram_dense_decode_attn(const lowram_dims *d, const void *q, cons
   a.B = d->batch; a.G = 1; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.dh = d->head_dim;
   a.F = 0; a.layer = 0; a.g = d->heads_q / d->heads_kv; a.n_comp = 0; a.n_total = p.n_split; a.PW = p.PW;
   return hip_status(launch_combine(d->act, a, (hipStream_t)stream), "lowram_dense_decode_attn");
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_noalloc_mu;
+void *g_noalloc_ptr[NOALLOC_MAX_DEVICES];  // device address of `scratch`, per device
+
+// The current device's copy of the scratch array: looked up once per device,
+// with that device current, and kept.
+lowram_status noalloc_scratch(void *stream, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+    return fail(LOWRAM_E_UNSUPPORTED, "device %d: at most %d devices", dev, NOALLOC_MAX_DEVICES);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if ((e = hipStreamGetDevice((hipStream_t)stream, &sdev)) != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(LOWRAM_E_INVALID, "stream belongs to device %d, the current device is %d", (int)sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(LOWRAM_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return LOWRAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lowram_status lowram_decode_attn_noalloc(const lowram_dims *d, int32_t layer, const lowram_model *m,
+                                         const lowram_cache *c, const void *q, const void *k_tail,
+                                         const void *v_tail, void *out, int32_t *sel_out, void *stream) {
+  lowram_status st = check_dims(d);
+  if (st != LOWRAM_OK) return st;
+  const size_t need = decode_plan(d).bytes;
+  if (need > (size_t)LOWRAM_NOALLOC_SCRATCH_BYTES)
+    return fail(LOWRAM_E_WORKSPACE, "decode needs %zu bytes of workspace, the static scratch holds %zu",
+                need, (size_t)LOWRAM_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if ((st = noalloc_scratch(stream, &ws)) != LOWRAM_OK) return st;
+  return lowram_decode_attn(d, layer, m, c, q, k_tail, v_tail, out, sel_out, ws,
+                            (size_t)LOWRAM_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

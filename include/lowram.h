@@ -202,6 +202,23 @@ lowram_status lowram_decode_attend(const lowram_dims *dims, int32_t layer, const
 lowram_status lowram_decode_combine(const lowram_dims *dims, int32_t layer, const lowram_model *model,
                                     void *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* lowram_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array of
+ * LOWRAM_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
+ * runs on until the process ends; this call allocates nothing.  Same
+ * arguments, kernels and results as lowram_decode_attn (same bits).
+ * Errors: LOWRAM_E_WORKSPACE when lowram_workspace_bytes(LOWRAM_OP_DECODE)
+ * exceeds the array; LOWRAM_E_INVALID when `stream` belongs to another device
+ * than the current one.  Every call on one GPU uses that GPU's array: calls that
+ * may overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  The kernels write every workspace byte they read,
+ * so the array's contents from an earlier call do not matter. */
+#define LOWRAM_NOALLOC_SCRATCH_BYTES (32u << 20)
+lowram_status lowram_decode_attn_noalloc(const lowram_dims *dims, int32_t layer, const lowram_model *model,
+                                         const lowram_cache *cache, const void *q, const void *k_tail,
+                                         const void *v_tail, void *out, int32_t *sel_out, void *stream);
+
 /* Reuse of rebuilt chunks across decode steps (rit.work generation section: the
  * context is split into chunks, those suited to the current query are picked,
  * and data already rebuilt is reused).  A table of `slots` slots per (sequence,
