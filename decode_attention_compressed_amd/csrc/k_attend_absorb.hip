@@ -174,14 +174,20 @@ template <> struct ResRow<int8_t> {
 };
 
 // ---------------------------------------------------------------------------
-// A = -log2(e) W1 U_{l,h} (bf16) and q~_g = U_{l,h}^T q_g (bf16 hi, lo) for
+// A = -log2(e) W1 U_{l,h} (fp16) and q~_g = U_{l,h}^T q_g (fp16 hi, lo) for
 // one 64 x 64 tile of (hidden unit, rank); grid (F / 64, r / 64, B Hkv), 256
 // threads.  int8 caches: both carry the per-rank scale of the codes.
+// All of a wave's W1 fragments are loaded first, under the staging of the
+// U^T tile (dword LDS writes of two head dims, consecutive over the lanes);
+// the q~ products are bf16 x bf16 (exact) accumulated in fp32 on the matrix
+// cores, like A's; the A tile leaves through LDS in 16-byte rows.
 // ---------------------------------------------------------------------------
 constexpr int AK = 64;
+constexpr int UT_LD = DH + 8;     // U^T tile row (rank) stride, 16-bit elements
+constexpr int OT_LD = AK + 8;     // output tile row (hidden unit) stride
 struct AbsorbSmem {
-  uint16_t ut[AK][DH + 8];   // U^T tile, bf16 (rank rows, head dims contiguous)
-  float qs[GQ][DH];          // q_g, fp32
+  uint16_t ut[AK][UT_LD];         // U^T tile, bf16 (rank rows, head dims contiguous)
+  uint16_t ot[AK][OT_LD];         // A tile, fp16 (hidden-unit rows, ranks contiguous)
 };
 
 __global__ __launch_bounds__(256) void k_absorb(const AttendArgs a) {
@@ -191,76 +197,95 @@ __global__ __launch_bounds__(256) void k_absorb(const AttendArgs a) {
   const int r = a.r, D = a.G * a.Hkv * DH, g = a.g;
   const uint16_t *U = reinterpret_cast<const uint16_t *>(a.basis) + ((long)b * D + (long)(a.layer * a.Hkv + h) * DH) * r;
   const uint16_t *W1 = reinterpret_cast<const uint16_t *>(a.w1) + (((long)b * a.G + a.layer) * a.Hkv + h) * (long)FF * DH;
-  // U^T tile: thread loads 8 consecutive ranks of one head-dim row and scatters them
-  for (int p = tid; p < DH * AK / 8; p += 256) {
-    const int d = p / (AK / 8), r8 = (p % (AK / 8)) * 8;
-    const u32x4 v = gld16(U + (long)d * r + rt * AK + r8);
-    const uint16_t *e = reinterpret_cast<const uint16_t *>(&v);
+  const int wf = w >> 1, wr = w & 1, l16 = lane & 15, kg = lane >> 4;
+  // W1 fragments of the wave: rows ft 64 + 32 wf + 16 mi + l16, head dims 32 ks + 8 kg
+  constexpr int NKS = DH / 32;
+  u32x4 w1f[NKS][2];
+  const uint16_t *w1r = W1 + (long)(ft * AK + 32 * wf + l16) * DH + 8 * kg;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sm.ut[r8 + i][d] = e[i];
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) w1f[ks][mi] = gld16(w1r + (long)16 * mi * DH + 32 * ks);
+  // q of the group as bf16 A fragments (rows = query heads l16 < g), q~ tiles only
+  const bool do_q = ft == 0;
+  u32x4 qf[NKS];
+  if (do_q) {
+    const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + ((long)b * a.Hq + (long)h * g + (l16 < g ? l16 : 0)) * DH + 8 * kg;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = l16 < g ? gld16(qb + 32 * ks) : v4(0, 0, 0, 0);
   }
-  if (ft == 0) {
-    const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + ((long)b * a.Hq + (long)h * g) * DH;
-    for (int i = tid; i < GQ * DH; i += 256) {
-      const int gi = i / DH;
-      sm.qs[gi][i % DH] = gi < g ? bf16_bits_to_f32(qb[i]) : 0.f;
+  // U^T tile: item (head-dim pair dp, rank octet oc) loads U[2 dp][8 oc ..] and
+  // U[2 dp + 1][8 oc ..] and writes eight dwords ut[8 oc + i][2 dp .. 2 dp + 1]
+  constexpr int NIT = (DH / 2) * (AK / 8) / 256;   // items per thread (4)
+  u32x4 ua[NIT], ub[NIT];
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int it = tid + 256 * k, dp = it % (DH / 2), oc = it / (DH / 2);
+    const uint16_t *up = U + (long)(2 * dp) * r + rt * AK + 8 * oc;
+    ua[k] = gld16(up);
+    ub[k] = gld16(up + r);
+  }
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int it = tid + 256 * k, dp = it % (DH / 2), oc = it / (DH / 2);
+    const uint32_t x[4] = {ua[k].x, ua[k].y, ua[k].z, ua[k].w}, y[4] = {ub[k].x, ub[k].y, ub[k].z, ub[k].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint32_t *>(&sm.ut[8 * oc + 2 * i][2 * dp]) = (x[i] & 0xFFFFu) | (y[i] << 16);
+      *reinterpret_cast<uint32_t *>(&sm.ut[8 * oc + 2 * i + 1][2 * dp]) = (x[i] >> 16) | (y[i] & 0xFFFF0000u);
     }
   }
   __syncthreads();
   // A tile: wave (wf, wr) computes 32 x 32 outputs as 2 x 2 blocks
-  const int wf = w >> 1, wr = w & 1, l16 = lane & 15, kg = lane >> 4;
   f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t *w1r = W1 + (long)(ft * AK + 32 * wf + l16) * DH + 8 * kg;
-#pragma unroll 2
-  for (int ks = 0; ks < DH / 32; ++ks) {
-    bf16x8 af[2], bfr[2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) af[mi] = __builtin_bit_cast(bf16x8, gld16(w1r + (long)16 * mi * DH + 32 * ks));
+  for (int ks = 0; ks < NKS; ++ks) {
+    bf16x8 bfr[2];
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) bfr[ni] = ldb8(&sm.ut[32 * wr + 16 * ni + l16][32 * ks + 8 * kg]);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma(af[mi], bfr[ni], acc[mi][ni]);
+      for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma(__builtin_bit_cast(bf16x8, w1f[ks][mi]), bfr[ni], acc[mi][ni]);
   }
-  uint16_t *A = a.absA + (long)bh * FF * r;
   const uint16_t *csc = a.coeff_scale ? a.coeff_scale + (long)b * r : nullptr;
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) {
-    const int col = rt * AK + 32 * wr + 16 * ni + l16;
-    const float sc = NEG_LOG2E * (csc ? f16_bits_to_f32(csc[col]) : 1.f);
+    const int cl = 32 * wr + 16 * ni + l16;   // rank within the tile
+    const float sc = NEG_LOG2E * (csc ? f16_bits_to_f32(csc[rt * AK + cl]) : 1.f);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = ft * AK + 32 * wf + 16 * mi + 4 * kg + v;
-        A[(long)row * r + col] = h16(acc[mi][ni][v] * sc);
-      }
+      for (int v = 0; v < 4; ++v) sm.ot[32 * wf + 16 * mi + 4 * kg + v][cl] = h16(acc[mi][ni][v] * sc);
   }
-  if (ft == 0) {  // q~ of this rank tile: thread (rank, head)
-    const int rl = tid & 63, gi = tid >> 6;
-    float x = 0.f;
-    for (int d = 0; d < DH; d += 8) {
-      const u32x4 u = *reinterpret_cast<const u32x4 *>(&sm.ut[rl][d]);
-      const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+  if (do_q) {  // q~ of the tile's ranks 16 w .. 16 w + 15: rows = heads, columns = ranks
+    f32x4 qa = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x = fmaf(bf16_bits_to_f32(uu[i] & 0xFFFFu), sm.qs[gi][d + 2 * i], x);
-        x = fmaf(bf16_bits_to_f32(uu[i] >> 16), sm.qs[gi][d + 2 * i + 1], x);
+    for (int ks = 0; ks < NKS; ++ks)
+      qa = mfma(__builtin_bit_cast(bf16x8, qf[ks]), ldb8(&sm.ut[16 * w + l16][32 * ks + 8 * kg]), qa);
+    if (kg == 0) {   // lane holds heads v = 0..3 of rank 16 w + l16
+      const int col = rt * AK + 16 * w + l16;
+      const float s = csc ? f16_bits_to_f32(csc[col]) : 1.f;
+      uint16_t *Q = a.absQ + (long)bh * 2 * GQ * r;
+#pragma unroll
+      for (int v = 0; v < GQ; ++v) {
+        const float x = v < g ? qa[v] * s : 0.f;
+        const _Float16 hv = (_Float16)x;
+        Q[(long)v * r + col] = __builtin_bit_cast(uint16_t, hv);
+        Q[(long)(GQ + v) * r + col] = h16(x - (float)hv);
       }
     }
-    const int col = rt * AK + rl;
-    if (csc) x *= f16_bits_to_f32(csc[col]);
-    const _Float16 hv = (_Float16)x;
-    const uint16_t hi = __builtin_bit_cast(uint16_t, hv);
-    const uint16_t lo = h16(x - (float)hv);
-    uint16_t *Q = a.absQ + (long)bh * 2 * GQ * r;
-    Q[(long)gi * r + col] = hi;
-    Q[(long)(GQ + gi) * r + col] = lo;
+  }
+  __syncthreads();
+  uint16_t *A = a.absA + (long)bh * FF * r + (long)(ft * AK) * r + rt * AK;
+#pragma unroll
+  for (int k = 0; k < AK * AK / 8 / 256; ++k) {
+    const int pc = tid + 256 * k, row = pc / (AK / 8), part = pc % (AK / 8);
+    *reinterpret_cast<u32x4 *>(A + (long)row * r + 8 * part) = *reinterpret_cast<const u32x4 *>(&sm.ot[row][8 * part]);
   }
 }
 
