@@ -98,7 +98,8 @@ hipError_t launch_attend_chain(int coeff, const AttendArgs &a, hipStream_t st);
 // attend launcher.  Two partial rows per split:
 // the split's chunks, then its share of the tail.
 bool absorb_supported(int act, int coeff, int resid, int dh, int F, int r, int C, int g, int k_eff);
-void absorb_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps, int &tail_per_split);
+void absorb_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps, int &tail_per_split,
+                 int &n_part);
 hipError_t launch_attend_absorb(int coeff, const AttendArgs &a, hipStream_t st);
 hipError_t launch_absorb(const AttendArgs &a, hipStream_t st);  // A and q~ into the workspace
 constexpr int REUSE_HIT = 1 << 30;

@@ -17,32 +17,33 @@
 // the g query heads (fp32, split into an fp16 part and the fp16 rounding of
 // the remainder).
 //
-// k_attend_absorb: one workgroup of 8 waves per (sequence b, kv head h, split
-// s, half of F).  A split is a run of 64-token slices of the chunks selected
-// for h; a round takes two of them (128 tokens).  Wave (tw, fw) owns slice tw
-// of the round and hidden units [64 fw, 64 fw + 64) of the half.  Per round,
-// over the rank in 32-wide k-steps:
-//   H^T[t][f] += C[t][r] A^T[r][f] on fp16 MFMAs: coefficient fragments go
-//     straight from global memory into registers and are converted to fp16
-//     (bf16 coefficients are exact in fp16's range, int8 codes always); the A
-//     slab of a k-step is shared by the 8 waves through LDS (double-buffered,
-//     loaded two k-steps ahead, one barrier per k-step); fp16 A (11
-//     significant bits) rather than bf16 keeps the hidden pre-activations at
-//     the accuracy of an fp16 rebuilt key;
-//   logits[t][g] += C[t][r] q~^T[r][g] with q~ as fp16 hi and lo parts, taken
-//     in turn by the four waves of a slice (wave fw on k-steps ks = fw mod 4),
-//     so each logit carries the fp32 q~ to about 2^-22 relative against exact
-//     coefficients.
-// Then, per round: the logits are summed over the four waves (fixed order),
-// a workgroup-wide online softmax per query head (p in fp16), SiLU of the
-// hidden pre-activations (held in -log2(e) units: one exp2, one reciprocal),
-// accH^T[g][f] += p^T H^T on the matrix cores, and, in the first half, the
-// residual rows of the round's tokens on the vector ALUs.
-// Both halves compute the same logits bit for bit, so their softmax states
-// agree; each writes its half of the hidden sums into the split's partial row
-// and the first half writes (m, l, mass, accV).  The second half also attends
-// its share of the uncompressed tail into a separate partial row (hidden sums
-// zero), so the combine merges 2 n_split rows per (b, h).
+// k_attend_absorb: one workgroup of 4 waves (one per SIMD) per (sequence b,
+// kv head h, split s, quarter q of F).  Its quarter of A (128 hidden units x r,
+// 96 KB at r = 384) is copied into LDS once and stays there; a split is a run
+// of 64-token slices of the chunks selected for h and a round gives one slice
+// to each wave (256 tokens).  Per round, over the rank in 32-wide k-steps and
+// without a barrier:
+//   H^T[t][f] += C[t][r] A^T[r][f] on fp16 MFMAs: the wave's coefficient
+//     fragments go straight from global memory into a register ring several
+//     k-steps deep (bf16 coefficients are exact in fp16's range, int8 codes
+//     always) and A's fragments are read from LDS (16-byte granules XOR-
+//     swizzled by row, so the 16 rows of a fragment fall in distinct banks);
+//     fp16 A (11 significant bits) keeps the hidden pre-activations at the
+//     accuracy of an fp16 rebuilt key;
+//   logits[t][g] += C[t][r] q~^T[r][g] with q~ as fp16 hi and lo parts in one
+//     operand (columns 0..3 hi, 4..7 lo), so each logit carries the fp32 q~ to
+//     about 2^-22 relative against exact coefficients.
+// Then: a workgroup-wide online softmax per query head (p in fp16), SiLU of
+// the hidden pre-activations (held in -log2(e) units: one exp2, one
+// reciprocal), accH^T[g][f] += p^T H^T on the matrix cores, and the residual
+// rows of the round's tokens on the vector ALUs (each quarter a quarter of the
+// head dims, the rows' loads in flight under the p . H products).
+// The four quarters compute the same logits bit for bit, so their softmax
+// states agree; each writes its quarter of the hidden sums and of the value
+// sums into the split's partial row and quarter 0 writes (m, l, mass).
+// Quarters 1..3 then attend a third each of the split's share of the
+// uncompressed tail into partial rows of their own (hidden sums zero), so the
+// combine merges 4 n_split rows per (b, h).
 //
 // Method: keys as per-token coefficients on a group basis (zicq.com English
 // summary, "Cross-Layer Low-Rank Key Compression"); values from the per-head
@@ -62,26 +63,27 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
 constexpr int DH = 256;          // head dim handled here
 constexpr int FF = 512;          // predictor hidden width handled here
-constexpr int FH = FF / 2;       // hidden units per workgroup (one half)
-constexpr int NW = 8;            // waves per workgroup
+constexpr int NQ = 4;            // quarters of F (one workgroup each)
+constexpr int FQ = FF / NQ;      // hidden units per workgroup (128)
+constexpr int NW = 4;            // waves per workgroup
 constexpr int NTH = NW * WAVE;
 constexpr int TT = 64;           // tokens per wave slice
-constexpr int RT = 2 * TT;       // tokens per round
+constexpr int RT = NW * TT;      // tokens per round
 constexpr int NTT = TT / 16;     // 16-token blocks of a slice
-constexpr int FWV = FH / 4;      // hidden units per wave (64)
-constexpr int NFB = FWV / 16;    // 16-wide hidden blocks per wave
+constexpr int NFB = FQ / 16;     // 16-wide hidden blocks of a quarter
 constexpr int KS = 32;           // ranks per k-step
-constexpr int ALD = KS + 8;      // A slab row stride, 16-bit elements (80 bytes)
 constexpr int GQ = 4;            // query heads per kv head (at most)
-// coefficient k-steps in registers (DC - 1 ahead; DC divides the k-step count):
-// 3 at r = 384 (12 k-steps), 2 at r = 512, where four would not fit the
-// register file
-template <int NK> constexpr int dc_of() { return NK % 3 == 0 ? 3 : 2; }
-constexpr int SLAB_P = FH * KS / 8 / NTH;   // 16-byte A slab pieces per thread and k-step (2)
+// coefficient k-steps in the register ring (DC - 1 ahead; DC divides the
+// k-step count, so the ring runs on across rounds); four fit the register
+// file next to the accumulators without scratch (six measured slower)
+template <int NK> constexpr int dc_of() { return 4; }
 constexpr int MAXSEL = 512;      // selected chunks staged per (b, h)
-constexpr int MAXRES = TT;       // residual rows listed per slice and round
-constexpr int RSTAGE = 32;       // residual rows of a round staged in LDS (more: read from global)
-constexpr int TCH = 32;          // tail tokens per staged chunk
+constexpr int TCH = 64;          // tail tokens per staged chunk (one 16-token tile per wave)
+constexpr int NTQ = NQ - 1;      // quarters that attend the tail (1 .. 3), one partial row each
+constexpr int DQ = DH / NQ;      // head dims of the residual pass per quarter (64)
+constexpr int RB = 8;            // residual rows per thread whose loads are in flight together
+// A granule (8 ranks, 16 bytes) k8 of hidden unit f sits at granule k8 ^ (f & 15)
+__host__ __device__ constexpr int swz(int f, int k8) { return k8 ^ (f & 15); }
 constexpr float NEG_LOG2E = -1.4426950408889634f;
 constexpr float NEG_LN2 = -0.6931471805599453f;
 
@@ -155,28 +157,24 @@ template <> struct Coef<int8_t> {
     return o;
   }
 };
+// head dim d of residual row e as stored (int8 codes: before their scale)
 template <typename TR> struct ResRow;
 template <> struct ResRow<bf16> {
-  static constexpr int ES = 2;
-  __device__ static void get(const void *rv, long e, int d, float s0, float s1, float &x0, float &x1) {
-    const uint32_t v = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(rv) + e * DH + d);
-    x0 = bf16_bits_to_f32(v & 0xFFFFu);
-    x1 = bf16_bits_to_f32(v >> 16);
+  __device__ static float get1(const void *rv, long e, int d) {
+    return bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(rv)[e * DH + d]);
   }
 };
 template <> struct ResRow<int8_t> {
-  static constexpr int ES = 1;
-  __device__ static void get(const void *rv, long e, int d, float s0, float s1, float &x0, float &x1) {
-    const uint16_t v = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const int8_t *>(rv) + e * DH + d);
-    x0 = (float)(int8_t)(v & 0xFFu) * s0;
-    x1 = (float)(int8_t)(v >> 8) * s1;
+  __device__ static float get1(const void *rv, long e, int d) {
+    return (float)reinterpret_cast<const int8_t *>(rv)[e * DH + d];
   }
 };
 
 // ---------------------------------------------------------------------------
-// A = -log2(e) W1 U_{l,h} (fp16) and q~_g = U_{l,h}^T q_g (fp16 hi, lo) for
-// one 64 x 64 tile of (hidden unit, rank); grid (F / 64, r / 64, B Hkv), 256
-// threads.  int8 caches: both carry the per-rank scale of the codes.
+// A = -log2(e) W1 U_{l,h} (fp16, rows swizzled as the attend kernel's LDS
+// copy) and q~_g = U_{l,h}^T q_g (fp16 hi, lo) for one 64 x 64 tile of
+// (hidden unit, rank); grid (F / 64, r / 64, B Hkv), 256 threads.  int8
+// caches: both carry the per-rank scale of the codes.
 // All of a wave's W1 fragments are loaded first, under the staging of the
 // U^T tile (dword LDS writes of two head dims, consecutive over the lanes);
 // the q~ products are bf16 x bf16 (exact) accumulated in fp32 on the matrix
@@ -281,11 +279,14 @@ __global__ __launch_bounds__(256) void k_absorb(const AttendArgs a) {
     }
   }
   __syncthreads();
-  uint16_t *A = a.absA + (long)bh * FF * r + (long)(ft * AK) * r + rt * AK;
+  // rows of A as the attend kernel keeps them in LDS: granule k8 of unit f at swz(f, k8)
+  uint16_t *A = a.absA + (long)bh * FF * r;
 #pragma unroll
   for (int k = 0; k < AK * AK / 8 / 256; ++k) {
     const int pc = tid + 256 * k, row = pc / (AK / 8), part = pc % (AK / 8);
-    *reinterpret_cast<u32x4 *>(A + (long)row * r + 8 * part) = *reinterpret_cast<const u32x4 *>(&sm.ot[row][8 * part]);
+    const int f = ft * AK + row;
+    *reinterpret_cast<u32x4 *>(A + (long)f * r + 8 * swz(f, rt * (AK / 8) + part)) =
+        *reinterpret_cast<const u32x4 *>(&sm.ot[row][8 * part]);
   }
 }
 
@@ -294,39 +295,39 @@ __global__ __launch_bounds__(256) void k_absorb(const AttendArgs a) {
 // ---------------------------------------------------------------------------
 template <int R>
 struct Smem {
-  static constexpr int AS = 0;                            // 2 x [FH][ALD] bf16 A slabs
-  static constexpr int QT = AS + 2 * FH * ALD * 2;        // [2][GQ][R] bf16 q~ hi, lo
-  static constexpr int B1S = QT + 2 * GQ * R * 2;         // [FH] fp32 -log2(e) b1 of this half
-  static constexpr int LGP = B1S + FH * 4;                // [4 fw][RT][GQ] fp32 logit parts
-  static constexpr int PS = LGP + 4 * RT * GQ * 4;        // [RT][GQ] fp32 p of the round
+  static constexpr int QLD = R + 16;                      // q~ row stride (16-bit): rows in distinct banks
+  static constexpr int AQ = 0;                            // [FQ][R] fp16 A quarter (swizzled granules)
+  static constexpr int QT = AQ + FQ * R * 2;              // [8][QLD] fp16 q~ hi rows 0..3, lo rows 4..7
+  static constexpr int B1S = QT + 8 * QLD * 2;            // [FQ] fp32 -log2(e) b1 of this quarter
+  static constexpr int LG = B1S + FQ * 4;                 // [RT][GQ] fp32 logits of the round
+  static constexpr int PS = LG + RT * GQ * 4;             // [RT][GQ] fp32 p of the round
   static constexpr int P16 = PS + RT * GQ * 4;            // [GQ][RT] fp16 p (MFMA operand)
   static constexpr int ST = P16 + GQ * RT * 2;            // [3][GQ] m, l, alpha
-  static constexpr int RC = ST + 3 * GQ * 4;              // [2] residual row counts of the round's slices
-  static constexpr int RL = RC + 4 * 4;                   // [2][MAXRES] residual rows (entry, token in round)
-  static constexpr int SEL = RL + 2 * MAXRES * 4;         // [MAXSEL] selected chunks of (b, h)
-  static constexpr int QF = SEL + MAXSEL * 4;             // [GQ][DH] fp32 q (tail)
-  static constexpr int RS = QF + GQ * DH * 4;             // [RSTAGE][DH * ES] residual rows of the round
-  static constexpr int BYTES = RS + RSTAGE * DH * 2;
-  // the tail (second half, after the rounds) stages TCH tokens of K and V in the slab area
-  static constexpr int TKS = 0, TVS = TKS + TCH * DH * 2;
+  static constexpr int RC = ST + 3 * GQ * 4;              // [2][NW] residual rows of the wave slices
+  static constexpr int RL = RC + 2 * NW * 4;              // [2][NW][TT] residual rows (entry << 8 | token in round)
+  static constexpr int SEL = RL + 2 * NW * TT * 4;        // [MAXSEL] selected chunks of (b, h)
+  static constexpr int BYTES = SEL + MAXSEL * 4;
+  // after the rounds the A area holds the per-wave hidden sums [NW][FQ][GQ]
+  // of the merge, then the tail's staged V rows
+  static constexpr int TVS = 0;
   static_assert(TVS + TCH * DH * 2 <= QT, "tail staging does not fit");
-  // end of the kernel: per-wave hidden sums [NW][FWV][GQ] over the A slabs
   static constexpr int AHM = 0;
-  static_assert(AHM + NW * FWV * GQ * 4 <= QT, "merge area does not fit");
+  static constexpr int RVR = AHM + NW * FQ * GQ * 4;     // [NW row groups][GQ][DQ] value sums
+  static_assert(RVR + NW * GQ * DQ * 4 <= QT, "merge area does not fit");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-// Block -> (b, h, split, half).  Workgroups are dispatched round-robin over
+// Block -> (b, h, split, quarter).  Workgroups are dispatched round-robin over
 // the 8 XCDs; the linear id is remapped so that each XCD receives a contiguous
-// run of (b, h, split, half): the two halves of a split share the coefficient
-// tiles and the splits of a (b, h) share A in one L2.
-__device__ __forceinline__ void coords(const AttendArgs &a, int &b, int &h, int &s, int &fh) {
+// run of (b, h, split, quarter): the quarters of a split share the
+// coefficient tiles and the splits of a (b, h) share A in one L2.
+__device__ __forceinline__ void coords(const AttendArgs &a, int &b, int &h, int &s, int &fq) {
   const int n = gridDim.x;
   int u = blockIdx.x;
   if (n % 8 == 0) u = (blockIdx.x % 8) * (n / 8) + blockIdx.x / 8;
-  fh = u & 1;
-  s = (u >> 1) % a.n_split;
-  const int bh = (u >> 1) / a.n_split;
+  fq = u % NQ;
+  s = (u / NQ) % a.n_split;
+  const int bh = (u / NQ) / a.n_split;
   h = bh % a.Hkv;
   b = bh / a.Hkv;
 }
@@ -337,133 +338,167 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
   constexpr int DC = dc_of<NK>();
   using S = Smem<R>;
   using CT = Coef<TC>;
+  static_assert(NK % DC == 0, "the coefficient ring must divide the k-step count");
   extern __shared__ __align__(16) unsigned char sm[];
-  uint16_t *As = reinterpret_cast<uint16_t *>(sm + S::AS);
+  const uint16_t *Aq = reinterpret_cast<const uint16_t *>(sm + S::AQ);
   const uint16_t *Qt = reinterpret_cast<const uint16_t *>(sm + S::QT);
   float *B1s = reinterpret_cast<float *>(sm + S::B1S);
-  float *Lgp = reinterpret_cast<float *>(sm + S::LGP);
+  float *Lg = reinterpret_cast<float *>(sm + S::LG);
   float *Ps = reinterpret_cast<float *>(sm + S::PS);
   uint16_t *P16 = reinterpret_cast<uint16_t *>(sm + S::P16);
   float *st = reinterpret_cast<float *>(sm + S::ST);   // m [GQ], l [GQ], alpha [GQ]
   int32_t *rc = reinterpret_cast<int32_t *>(sm + S::RC);
   int32_t *rl = reinterpret_cast<int32_t *>(sm + S::RL);
   int32_t *selS = reinterpret_cast<int32_t *>(sm + S::SEL);
-  float *qf = reinterpret_cast<float *>(sm + S::QF);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tw = w & 1, fw = w >> 1;
   const int l16 = lane & 15, kg = lane >> 4;
-  int b, h, s, fh;
-  coords(a, b, h, s, fh);
+  int b, h, s, fq;
+  coords(a, b, h, s, fq);
   const int g = a.g, C = a.C;
   const long bh = ((long)b * a.G + a.layer) * a.Hkv + h;   // (b, layer, h)
   const long bhs = (long)b * a.Hkv + h;                      // (b, h)
 
-  // ---- prologue ---------------------------------------------------------------
-  const uint16_t *Aw = a.absA + bhs * (long)FF * R + (long)fh * FH * R;   // this half's rows of A
-  const rsrc_t Ar = make_rsrc(Aw, (uint32_t)(FH * R * 2));
-  // A slab pieces: thread loads 16 bytes of rows tid / 4 + 128 i, ranks 8 (tid % 4) + 32 ks
-  const uint32_t a_voff = (uint32_t)(((tid >> 2) * R + 8 * (tid & 3)) * 2);
-  auto slab_ld = [&](int ks, u32x4 *u) {
+  // ---- prologue: A quarter, q~, b1, selection, tail q ------------------------
+  // A quarter: every piece in flight at once (nothing else holds registers yet)
+  constexpr int NP = FQ * R * 2 / 16 / NTH;   // 16-byte pieces per thread
+  u32x4 apc[NP];
+  {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.absA + bhs * (long)FF * R + (long)fq * FQ * R);
 #pragma unroll
-    for (int i = 0; i < SLAB_P; ++i)
-      u[i] = __builtin_amdgcn_raw_buffer_load_b128(Ar, a_voff, (uint32_t)((ks * KS + i * (NTH / 4) * R) * 2), 0);
-  };
-  auto slab_st = [&](int buf, const u32x4 *u) {
-#pragma unroll
-    for (int i = 0; i < SLAB_P; ++i)
-      lst16(As + buf * FH * ALD + ((tid >> 2) + i * (NTH / 4)) * ALD + 8 * (tid & 3), u[i]);
-  };
-  u32x4 ur[2][SLAB_P];
-  slab_ld(0, ur[0]);
-  slab_ld(1, ur[1]);
-
+    for (int i = 0; i < NP; ++i) apc[i] = src[i * NTH + tid];
+  }
+  {  // q~ hi and lo rows of this (b, h): absQ [2][GQ][R] -> rows 0..7 of QT
+    const uint16_t *Qg = a.absQ + bhs * 2 * GQ * R;
+    uint16_t *qd = reinterpret_cast<uint16_t *>(sm + S::QT);
+    for (int i = tid; i < 2 * GQ * R / 8; i += NTH) {
+      const int row = (8 * i) / R, col = (8 * i) % R;
+      lst16(qd + row * S::QLD + col, gld16(Qg + 8 * i));
+    }
+  }
   const int k_eff = a.k_eff;
   const int32_t *selp = a.sel + bhs * k_eff;
   for (int i = tid; i < k_eff; i += NTH) selS[i] = selp[i];
-  {  // q~ hi and lo rows of this (b, h)
-    const uint16_t *Qg = a.absQ + bhs * 2 * GQ * R;
-    for (int i = tid; i < 2 * GQ * R / 8; i += NTH)
-      lst16(reinterpret_cast<uint16_t *>(sm + S::QT) + 8 * i, gld16(Qg + 8 * i));
-  }
-  const uint16_t *B1 = reinterpret_cast<const uint16_t *>(a.b1) + bh * FF + fh * FH;
-  for (int i = tid; i < FH; i += NTH) B1s[i] = bf16_bits_to_f32(B1[i]) * NEG_LOG2E;
+  const uint16_t *B1 = reinterpret_cast<const uint16_t *>(a.b1) + bh * FF + fq * FQ;
+  for (int i = tid; i < FQ; i += NTH) B1s[i] = bf16_bits_to_f32(B1[i]) * NEG_LOG2E;
   if (tid < GQ) {
     st[tid] = -INFINITY;
     st[GQ + tid] = 0.f;
     st[2 * GQ + tid] = 0.f;
   }
-  if (fh == 1) {  // the tail share needs q itself
-    const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + ((long)b * a.Hq + (long)h * g) * DH;
-    for (int i = tid; i < GQ * DH; i += NTH) qf[i] = (i / DH) < g ? bf16_bits_to_f32(qb[i]) : 0.f;
+  {
+    u32x4 *dst = reinterpret_cast<u32x4 *>(sm + S::AQ);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) dst[i * NTH + tid] = apc[i];
   }
 
   const int n_slices = k_eff * (C / TT);
   const int sl0 = s * a.tps, sl1 = min(n_slices, sl0 + a.tps);
-  const int rounds = (a.tps + 1) / 2;
+  const int rounds = a.tps / NW;
   const int r = R;
   const TC *cf = reinterpret_cast<const TC *>(a.coeff) + (long)b * a.N * r;
   const rsrc_t Cr = make_rsrc(cf, (uint32_t)((long)a.N * r * CT::ES));
   const uint32_t c_voff = (uint32_t)((l16 * r + 8 * kg) * CT::ES);   // + (row + 16 tt) r + 32 ks
   const int32_t *rptr = a.res_ptr + bh * (a.N / C + 1);
   const int32_t *ridx = a.res_idx + bh * a.n_res;
-  // residual scales of this thread's two head dims (int8), residual-pass mapping:
-  // thread (query head vg, dims 2 vd, 2 vd + 1)
-  const int vg = tid >> 7, vd = 2 * (tid & 127);
-  float rs0 = 1.f, rs1 = 1.f;
-  if (sizeof(TC) == 1 && a.res_scale) {
-    rs0 = f16_bits_to_f32(a.res_scale[bh * DH + vd]);
-    rs1 = f16_bits_to_f32(a.res_scale[bh * DH + vd + 1]);
-  }
-  float accV0 = 0.f, accV1 = 0.f;   // first half: residual sums of (vg, vd), (vg, vd + 1)
-  f32x4 accH[NFB];                  // hidden sums [16 g][16 f] per block (rows g < GQ live)
+  const TC *rval = reinterpret_cast<const TC *>(a.res_val) + bh * (long)a.n_res * DH;
+  // residual pass: thread (row group rg: rows rg, rg + NW, ... of the round;
+  // head dim vd of this quarter's DQ), all query heads
+  const int rg = w, vd = fq * DQ + lane, vg = tid >> 6;
+  const float rsv = (sizeof(TC) == 1 && a.res_scale) ? f16_bits_to_f32(a.res_scale[bh * DH + vd]) : 1.f;
+  float accV[GQ] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 accH[NFB];   // hidden sums [16 g][16 f] per block (rows g < GQ live)
 #pragma unroll
   for (int fb = 0; fb < NFB; ++fb) accH[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // token row of slice sig for this wave (a slice past the split reads zeros)
+  // token row of slice sig (a slice past the split reads zeros)
   auto slice_row = [&](int sig) -> long {
     return sig < sl1 ? (long)selS[(sig * TT) / C] * C + (sig * TT) % C : (long)a.N;
   };
   auto c_soff = [&](long row, int tt, int ks) -> uint32_t {
     return (uint32_t)(((row + 16 * tt) * r + ks * KS) * CT::ES);
   };
+  // residual rows of the wave's slice at token row `row` (past the split: none)
+  // into list buffer buf, as (entry << 8 | token in round); x0 = the index
+  // entry e0 + lane, already loaded
+  auto list_res = [&](long row, int x0, int e0, int e1, int buf) {
+    int cnt = 0;
+    if (row < a.N) {
+      const int jc = (int)(row / C), t0 = (int)(row % C);
+      for (int base = e0; base < e1; base += WAVE) {
+        const int e = base + lane;
+        const int x = base == e0 ? x0 : (e < e1 ? ridx[e] : -1);
+        const int t = e < e1 ? x - jc * C - t0 : -1;
+        const bool in = e < e1 && t >= 0 && t < TT;
+        const uint64_t m = __ballot(in);
+        const int pos = cnt + __popcll(m & lanemask_lt());
+        if (in && pos < TT) rl[(buf * NW + w) * TT + pos] = (e << 8) | (TT * w + t);
+        cnt += __popcll(m);
+      }
+    }
+    if (lane == 0) rc[buf * NW + w] = min(cnt, TT);
+  };
   __syncthreads();
-  slab_st(0, ur[0]);
-  slab_ld(2, ur[0]);
-  long row0 = slice_row(sl0 + tw);
+  long row0 = slice_row(sl0 + w);
   typename CT::raw cr[DC][NTT];   // coefficient ring: k-step ks in cr[ks % DC]
 #pragma unroll
   for (int q = 0; q < DC - 1; ++q)
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) cr[q][tt] = CT::ld(Cr, c_voff, c_soff(row0, tt, q));
-  __syncthreads();
+  {  // round 0's list
+    int e0 = 0, e1 = 0, x0 = -1;
+    if (row0 < a.N) {
+      const int jc = (int)(row0 / C);
+      e0 = rptr[jc];
+      e1 = rptr[jc + 1];
+      x0 = e0 + lane < e1 ? ridx[e0 + lane] : -1;
+    }
+    list_res(row0, x0, e0, e1, 0);
+  }
+  __syncthreads();   // every wave's round-0 list before any wave reads them
 
-  static_assert(NK % DC == 0 && NK % 2 == 0 && NK >= 4, "ring sizes must divide the k-step count");
+  // A fragment of k-step ks, block fb: unit 16 fb + l16, ranks 32 ks + 8 kg .. + 8;
+  // q~ fragment: row l16 (< 8) of the q~ table.  The offsets are made opaque
+  // once per round: the fragments are the same in every round, and hoisted out
+  // of the round loop they would hold 12 k-steps of registers.
+  uint32_t a_off = (uint32_t)(l16 * R), q_off = (uint32_t)((l16 & 7) * S::QLD + 8 * kg);
+  const f16x8 z8 = __builtin_bit_cast(f16x8, v4(0, 0, 0, 0));
+
   for (int rd = 0; rd < rounds; ++rd) {
-    const int sig = sl0 + 2 * rd + tw;
+    const int sig = sl0 + NW * rd + w;
     const bool has = sig < sl1;
     const bool more = rd + 1 < rounds;
-    const long row0n = more ? slice_row(sig + 2) : (long)a.N;
-    // residual rows of this wave's slice (first half; waves fw == 0 list them)
-    if (fh == 0 && fw == 0) {
-      int cnt = 0;
-      if (has) {
-        const int jc = (int)(row0 / C), t0 = (int)(row0 % C);
-        const int e0 = rptr[jc], e1 = rptr[jc + 1];
-        for (int base = e0; base < e1; base += WAVE) {
-          const int e = base + lane;
-          const int t = e < e1 ? ridx[e] - jc * C - t0 : -1;
-          const bool in = e < e1 && t >= 0 && t < TT;
-          const uint64_t m = __ballot(in);
-          const int pos = cnt + __popcll(m & lanemask_lt());
-          if (in && pos < MAXRES) rl[tw * MAXRES + pos] = (e << 8) | (TT * tw + t);
-          cnt += __popcll(m);
-        }
-      }
-      if (lane == 0) rc[tw] = cnt;
+    const long row0n = more ? slice_row(sig + NW) : (long)a.N;
+    // the next round's slice: its chunk's residual range now, its first 64
+    // index entries under this round's k-loop (listed after the round)
+    int e0n = 0, e1n = 0, xn = -1;
+    if (row0n < a.N) {
+      const int jcn = (int)(row0n / C);
+      e0n = rptr[jcn];
+      e1n = rptr[jcn + 1];
     }
-    // ---- k-loop: hidden pre-activations and logit parts ----------------------
+    // residual rows of the round (listed at the end of the previous round): the
+    // first RB rows' values of this thread's head dim, in flight under the
+    // k-loop (row k of the round: list wl, entry k - rows of the lists before wl)
+    const int *rcb = rc + (rd & 1) * NW, *rlb = rl + (rd & 1) * NW * TT;
+    const int rn0 = rcb[0], rn1 = rcb[1], rn2 = rcb[2], rn3 = rcb[3];
+    const int n_rows = rn0 + rn1 + rn2 + rn3;
+    auto res_code = [&](int k) -> int {
+      const int k1 = k - rn0, k2 = k1 - rn1, k3 = k2 - rn2;
+      return rlb[k < rn0 ? k : k1 < rn1 ? TT + k1 : k2 < rn2 ? 2 * TT + k2 : 3 * TT + k3];
+    };
+    // this thread's rows: k0 + rg + NW u, u < RB
+    float rx[RB];
+    int rcode[RB];
+    auto res_load = [&](int k0) {
+#pragma unroll
+      for (int u = 0; u < RB; ++u) rcode[u] = res_code(min(k0 + rg + NW * u, n_rows - 1));
+#pragma unroll
+      for (int u = 0; u < RB; ++u) rx[u] = ResRow<TC>::get1(rval, (long)(rcode[u] >> 8), vd);
+    };
+    if (n_rows > 0) res_load(0);
+    // ---- k-loop: hidden pre-activations and logits ----------------------------
     f32x4 acc[NTT][NFB];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
@@ -472,10 +507,22 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
     f32x4 lg[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) lg[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t *a_rd = As + (FWV * fw + l16) * ALD + 8 * kg;   // + buf FH ALD + 16 fb ALD
+    // lane values of the swizzle, opaque per round for the same reason (the
+    // twelve per-k-step granule offsets would otherwise be hoisted and spilled)
+    uint32_t sw_l = (uint32_t)l16, sw_k = (uint32_t)kg;
+    asm volatile("" : "+v"(a_off), "+v"(q_off), "+v"(sw_l), "+v"(sw_k));
+    const uint16_t *a_rd = Aq + a_off;
+    const uint16_t *q_rd = Qt + q_off;
+    // A and q~ fragments double-buffered: k-step ks + 1's read under k-step ks's products
+    f16x8 af[2][NFB + 1];   // [NFB] is the q~ operand
+    auto load_af = [&](int ks, f16x8 *dst) {
+#pragma unroll
+      for (int fb = 0; fb < NFB; ++fb) dst[fb] = ldh8(a_rd + 16 * fb * R + 8 * (((uint32_t)(4 * ks) + sw_k) ^ sw_l));
+      dst[NFB] = l16 < 8 ? ldh8(q_rd + ks * KS) : z8;
+    };
+    load_af(0, af[0]);
     sfor<NK>([&](auto ksc) {
       constexpr int ks = decltype(ksc)::value;
-      constexpr int buf = ks & 1;
       __builtin_amdgcn_sched_barrier(0);
       // coefficients DC - 1 k-steps ahead; past the round's end, the next
       // round's first k-steps (k-step kl of this round and kl - NK of the next
@@ -490,106 +537,44 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
           for (int tt = 0; tt < NTT; ++tt) cr[kl % DC][tt] = CT::ld(Cr, c_voff, c_soff(row0n, tt, kl - NK));
         }
       }
-      // slab ks + 1 (of this round, or slab 0 of the next) -> the other buffer,
-      // slab ks + 3 into the register ring; both buffers were last read before
-      // the previous barrier
-      if (ks + 1 < NK || more) {
-        slab_st(buf ^ 1, ur[(ks + 1) & 1]);
-        if (ks + 3 < NK || more) slab_ld((ks + 3) % NK, ur[(ks + 1) & 1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ks + 1 < NK) load_af(ks + 1, af[(ks + 1) & 1]);
+      if constexpr (ks == 1) xn = e0n + lane < e1n ? ridx[e0n + lane] : -1;
       f16x8 c8[NTT];
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) c8[tt] = CT::get(cr[ks % DC][tt]);
 #pragma unroll
-      for (int fb = 0; fb < NFB; ++fb) {
-        const f16x8 af = ldh8(a_rd + buf * FH * ALD + 16 * fb * ALD);
+      for (int tt = 0; tt < NTT; ++tt) {
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) acc[tt][fb] = mfma(c8[tt], af, acc[tt][fb]);
+        for (int fb = 0; fb < NFB; ++fb) acc[tt][fb] = mfma(c8[tt], af[ks & 1][fb], acc[tt][fb]);
+        lg[tt] = mfma(c8[tt], af[ks & 1][NFB], lg[tt]);
       }
-      if ((ks & 3) == fw) {  // this wave's turn at the logits: q~ hi, lo as B operands (head l16)
-        const f16x8 z8 = __builtin_bit_cast(f16x8, v4(0, 0, 0, 0));
-        const uint16_t *qr = Qt + l16 * r + ks * KS + 8 * kg;
-        const f16x8 qh = l16 < GQ ? ldh8(qr) : z8, ql = l16 < GQ ? ldh8(qr + GQ * r) : z8;
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          lg[tt] = mfma(c8[tt], qh, lg[tt]);
-          lg[tt] = mfma(c8[tt], ql, lg[tt]);
-        }
-      }
-      __syncthreads();
     });
+    __builtin_amdgcn_sched_barrier(0);
     row0 = row0n;
-    // residual rows of the round (first half): rows k < RSTAGE of the two
-    // slices' lists, 16-byte pieces issued now and stored to LDS after SiLU
-    constexpr int RPC = DH * (int)sizeof(TC) / 16;   // 16-byte pieces per row
-    constexpr int RSP = RSTAGE * RPC / NTH;          // pieces per thread
-    static_assert(RSTAGE * RPC % NTH == 0, "residual staging pieces");
-    const TC *rval = reinterpret_cast<const TC *>(a.res_val) + bh * (long)a.n_res * DH;
-    int n_r0 = 0, n_rows = 0;
-    u32x4 rsv[RSP];
-    if (fh == 0) {
-      n_r0 = min(rc[0], MAXRES);
-      n_rows = n_r0 + min(rc[1], MAXRES);
+    // ---- logits of the round: hi (column gi) + lo (column 4 + gi) -------------
 #pragma unroll
-      for (int i = 0; i < RSP; ++i) {
-        const int pc = tid + NTH * i, k = pc / RPC, part = pc % RPC;
-        rsv[i] = v4(0, 0, 0, 0);
-        if (k < n_rows) {
-          const int code = k < n_r0 ? rl[k] : rl[MAXRES + k - n_r0];
-          rsv[i] = gld16(reinterpret_cast<const unsigned char *>(rval) + ((long)(code >> 8) * DH * sizeof(TC)) + 16 * part);
-        }
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float x = lg[tt][v] + __shfl_down(lg[tt][v], GQ, 16);
+        if (l16 < GQ) Lg[(TT * w + 16 * tt + 4 * kg + v) * GQ + l16] = x;
       }
-    }
-    // ---- logits of the round: parts of the four waves of each slice ---------
-    // lg[tt] lane (l16 = head, kg): tokens 16 tt + 4 kg + v of the slice
-    if (l16 < GQ) {
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Lgp[(fw * RT + TT * tw + 16 * tt + 4 * kg + v) * GQ + l16] = lg[tt][v];
-    }
-    // SiLU of the pre-activations (independent of the softmax): hidden block fb,
-    // token pair i of blocks (2 i, 2 i + 1) as the fp16 B operand of the p . H product
-    f16x8 hb[NTT / 2][NFB];
-#pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) {
-      const float bias = B1s[FWV * fw + 16 * fb + l16];
-#pragma unroll
-      for (int i = 0; i < NTT / 2; ++i)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          hb[i][fb][v] = (_Float16)silu_scaled(acc[2 * i][fb][v] + bias);
-          hb[i][fb][4 + v] = (_Float16)silu_scaled(acc[2 * i + 1][fb][v] + bias);
-        }
-    }
-    if (fh == 0) {
-      unsigned char *rs = sm + S::RS;
-#pragma unroll
-      for (int i = 0; i < RSP; ++i) {
-        const int pc = tid + NTH * i;
-        if (pc / RPC < n_rows) lst16(rs + 16 * pc, rsv[i]);
-      }
-    }
     __syncthreads();
-    // ---- softmax of the round, workgroup-wide: waves 0..3 take head w --------
-    if (w < GQ) {
+    // ---- softmax of the round, workgroup-wide: wave w takes query head w -----
+    if (w < g) {
       const int gi = w;
-      float x[2];
+      float x[4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = lane + WAVE * u;           // token of the round
-        const int sl = sl0 + 2 * rd + u;         // its slice
-        float v = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v += Lgp[(k * RT + t) * GQ + gi];
-        x[u] = (sl < sl1 && gi < g) ? v * a.scale_log2 : -INFINITY;
+      for (int u = 0; u < 4; ++u) {
+        const int t = lane + WAVE * u;            // token of the round (slice u)
+        const int sl = sl0 + NW * rd + u;
+        x[u] = sl < sl1 ? Lg[t * GQ + gi] * a.scale_log2 : -INFINITY;
       }
-      const float mx = wave_max(fmaxf(x[0], x[1]));
+      const float mx = wave_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
       const float m_old = st[gi], m_new = fmaxf(m_old, mx);
       float ps = 0.f;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 4; ++u) {
         const int t = lane + WAVE * u;
         const float p = x[u] == -INFINITY ? 0.f : (float)(_Float16)__builtin_amdgcn_exp2f(x[u] - m_new);
         Ps[t * GQ + gi] = p;
@@ -604,6 +589,14 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
         st[GQ + gi] = st[GQ + gi] * alpha + ps;
         st[gi] = m_new;
       }
+    } else if (lane < RT / NW) {   // heads past the group: p = 0
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = (lane + (RT / NW) * u);
+        Ps[t * GQ + w] = 0.f;
+        P16[w * RT + t] = 0;
+      }
+      if (lane == 0) st[2 * GQ + w] = 1.f;
     }
     __syncthreads();
     // ---- accH^T[g][f] += p^T H^T: rescale, then two 32-token k-steps ----------
@@ -617,135 +610,145 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
         for (int v = 0; v < 4; ++v) accH[fb][v] *= al[v];
       // p^T A operand: lane (head l16, kg) holds p at the tokens of the H
       // operand's k positions: 16 (2 i) + 4 kg + v, then 16 (2 i + 1) + 4 kg + v
-      const f16x8 z8 = __builtin_bit_cast(f16x8, v4(0, 0, 0, 0));
 #pragma unroll
       for (int i = 0; i < NTT / 2; ++i) {
         f16x8 pa = z8;
         if (l16 < GQ) {
-          const uint16_t *pr = P16 + l16 * RT + TT * tw + 32 * i + 4 * kg;
+          const uint16_t *pr = P16 + l16 * RT + TT * w + 32 * i + 4 * kg;
           const uint2 lo = *reinterpret_cast<const uint2 *>(pr);
           const uint2 hi = *reinterpret_cast<const uint2 *>(pr + 16);
           pa = __builtin_bit_cast(f16x8, v4(lo.x, lo.y, hi.x, hi.y));
         }
+        // SiLU of the pre-activations of token blocks (2 i, 2 i + 1), hidden
+        // block fb, as the fp16 B operand
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) accH[fb] = mfma(pa, hb[i][fb], accH[fb]);
+        for (int fb = 0; fb < NFB; ++fb) {
+          const float bias = B1s[16 * fb + l16];
+          f16x8 hb;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            hb[v] = (_Float16)silu_scaled(acc[2 * i][fb][v] + bias);
+            hb[4 + v] = (_Float16)silu_scaled(acc[2 * i + 1][fb][v] + bias);
+          }
+          accH[fb] = mfma(pa, hb, accH[fb]);
+        }
       }
     }
-    // ---- residual rows of the round (first half, vector ALUs): thread
-    // (head vg, dims vd, vd + 1); staged rows from LDS, any past RSTAGE from
-    // global memory eight at a time ----------------------------------------------
-    if (fh == 0) {
-      const float alpha = st[2 * GQ + vg];
-      accV0 *= alpha;
-      accV1 *= alpha;
-      if (vg < g) {
-        const unsigned char *rs = sm + S::RS;
-        const int ns = min(n_rows, RSTAGE);
-        for (int k = 0; k < ns; ++k) {
-          const int code = k < n_r0 ? rl[k] : rl[MAXRES + k - n_r0];
-          const float p = Ps[(code & 0xFF) * GQ + vg];
-          float x0, x1;
-          ResRow<TC>::get(rs + (long)k * DH * sizeof(TC), 0, vd, rs0, rs1, x0, x1);
-          accV0 = fmaf(p, x0, accV0);
-          accV1 = fmaf(p, x1, accV1);
-        }
-        for (int k0 = RSTAGE; k0 < n_rows; k0 += 8) {
-          float x0v[8], x1v[8], pv[8];
+    // ---- residual rows of the round (vector ALUs): accV[g][vd] += p delta ----
+    {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int k = min(k0 + u, n_rows - 1);
-            const int code = k < n_r0 ? rl[k] : rl[MAXRES + k - n_r0];
-            pv[u] = k0 + u < n_rows ? Ps[(code & 0xFF) * GQ + vg] : 0.f;
-            ResRow<TC>::get(rval, (long)(code >> 8), vd, rs0, rs1, x0v[u], x1v[u]);
-          }
+      for (int gi = 0; gi < GQ; ++gi) accV[gi] *= st[2 * GQ + gi];
+      for (int k0 = 0; k0 < n_rows; k0 += NW * RB) {
+        if (k0 > 0) res_load(k0);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            accV0 = fmaf(pv[u], x0v[u], accV0);
-            accV1 = fmaf(pv[u], x1v[u], accV1);
+        for (int u = 0; u < RB; ++u) {
+          if (k0 + rg + NW * u < n_rows) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4 *>(Ps + (rcode[u] & 0xFF) * GQ);
+            const float x = rx[u] * rsv;
+#pragma unroll
+            for (int gi = 0; gi < GQ; ++gi) accV[gi] = fmaf(p4[gi], x, accV[gi]);
           }
         }
       }
     }
-    __syncthreads();   // round's LDS (logit parts, p, residual lists) free again
+    // the next round's residual list (its first 64 index entries prefetched)
+    list_res(row0, xn, e0n, e1n, (rd + 1) & 1);
+    __syncthreads();   // round's LDS (logits, p, residual lists) free again
   }
 
   // ---- partial rows -------------------------------------------------------------
-  const int n_prow = 2 * a.n_split;   // partial rows per (b, h): chunk rows, then tail rows
+  const int n_prow = (1 + NTQ) * a.n_split;   // per (b, h): chunk rows, then NTQ tail rows per split
   float *part = a.part + (bhs * n_prow + s) * g * a.PW;
-  // hidden sums of the two slices' waves of each block of 64 units
+  // hidden sums of the four waves (their slices) of every unit of the quarter
   float *ahm = reinterpret_cast<float *>(sm + S::AHM);
   if (kg == 0) {
 #pragma unroll
     for (int fb = 0; fb < NFB; ++fb)
-      *reinterpret_cast<f32x4 *>(ahm + ((w * FWV) + 16 * fb + l16) * GQ) = accH[fb];
+      *reinterpret_cast<f32x4 *>(ahm + ((w * FQ) + 16 * fb + l16) * GQ) = accH[fb];
   }
   __syncthreads();
-  for (int i = tid; i < FH * GQ; i += NTH) {   // (unit of the half, head)
-    const int f = i / GQ, gi = i % GQ, fwi = f / FWV, fl = f % FWV;
-    const float x = ahm[((2 * fwi) * FWV + fl) * GQ + gi] + ahm[((2 * fwi + 1) * FWV + fl) * GQ + gi];
-    if (gi < g) part[(long)gi * a.PW + 4 + fh * FH + f] = x * NEG_LN2;
+  for (int i = tid; i < FQ * GQ; i += NTH) {   // (unit of the quarter, head)
+    const int f = i / GQ, gi = i % GQ;
+    const float x = (ahm[(0 * FQ + f) * GQ + gi] + ahm[(1 * FQ + f) * GQ + gi]) +
+                    (ahm[(2 * FQ + f) * GQ + gi] + ahm[(3 * FQ + f) * GQ + gi]);
+    if (gi < g) part[(long)gi * a.PW + 4 + fq * FQ + f] = x * NEG_LN2;
   }
-  if (fh == 0) {
+  {  // value sums of this quarter's head dims: the four row groups in order
+    float *rvr = reinterpret_cast<float *>(sm + S::RVR);
+#pragma unroll
+    for (int gi = 0; gi < GQ; ++gi) rvr[(rg * GQ + gi) * DQ + lane] = accV[gi];
+    __syncthreads();
+    if (vg < g) {
+      const float x = (rvr[(0 * GQ + vg) * DQ + lane] + rvr[(1 * GQ + vg) * DQ + lane]) +
+                      (rvr[(2 * GQ + vg) * DQ + lane] + rvr[(3 * GQ + vg) * DQ + lane]);
+      part[(long)vg * a.PW + 4 + FF + fq * DQ + lane] = x;
+    }
+  }
+  if (fq == 0) {
     if (tid < g) {
       part[(long)tid * a.PW + 0] = st[tid];
       part[(long)tid * a.PW + 1] = st[GQ + tid];
       part[(long)tid * a.PW + 2] = st[GQ + tid];
       part[(long)tid * a.PW + 3] = 0.f;
     }
-    if (vg < g) {
-      part[(long)vg * a.PW + 4 + FF + vd] = accV0;
-      part[(long)vg * a.PW + 4 + FF + vd + 1] = accV1;
-    }
     return;
   }
 
-  // ---- second half: this split's share of the tail, its own partial row -----------
-  // Chunks of TCH tokens: K and V rows staged in the (now free) slab area with
-  // all loads in flight at once, logits per wave and token (lane: 4 head dims),
-  // then an online softmax per query head over the chunks.
-  const int tb = min(a.T, s * a.tail_per_split), te = min(a.T, tb + a.tail_per_split);
+  // ---- quarters 1..3: a third each of this split's share of the tail -----------
+  // Chunks of up to TCH tokens: V rows staged in the (now free) A area; the
+  // logits of 16-token tile w on the matrix cores (K rows as the A operand
+  // straight from memory, bf16 q as the B operand, fp32 sums); an online
+  // softmax per query head over the chunks; p . V on the vector ALUs.
+  const int t0s = min(a.T, s * a.tail_per_split), t1s = min(a.T, t0s + a.tail_per_split);
+  const int tq = (t1s - t0s + NTQ - 1) / NTQ;
+  const int tb = min(t1s, t0s + (fq - 1) * tq), te = min(t1s, tb + tq);
   const long tail_base = (bh * a.T) * DH;
   const uint16_t *kt = reinterpret_cast<const uint16_t *>(a.k_tail) + tail_base;
   const uint16_t *vt = reinterpret_cast<const uint16_t *>(a.v_tail) + tail_base;
-  uint16_t *tks = reinterpret_cast<uint16_t *>(sm + S::TKS), *tvs = reinterpret_cast<uint16_t *>(sm + S::TVS);
+  uint16_t *tvs = reinterpret_cast<uint16_t *>(sm + S::TVS);
   float *tp = Ps;   // [TCH][GQ] logits, then p, of the chunk
+  __syncthreads();   // the merge area is read
   if (tid < GQ) {
     st[tid] = -INFINITY;
     st[GQ + tid] = 0.f;
   }
-  float tv0 = 0.f, tv1 = 0.f;   // (vg, vd), (vg, vd + 1)
-  constexpr int TPC = TCH * DH / 8 / NTH;   // 16-byte pieces per thread of K (and of V)
+  // q of head l16 (< g) as bf16 B operands, dims 32 ks + 8 kg .. + 8
+  constexpr int NKD = DH / 32;
+  u32x4 qfr[NKD];
+  {
+    const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + ((long)b * a.Hq + (long)h * g + (l16 < g ? l16 : 0)) * DH + 8 * kg;
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) qfr[ks] = l16 < g ? gld16(qb + 32 * ks) : v4(0, 0, 0, 0);
+  }
+  float tv[4] = {0.f, 0.f, 0.f, 0.f};   // (vg, dims 4 lane .. 4 lane + 3)
+  constexpr int TPC = TCH * DH / 8 / NTH;   // 16-byte pieces per thread of V
   for (int c0 = tb; c0 < te; c0 += TCH) {
     const int nt = min(TCH, te - c0);
-    u32x4 kp[TPC], vp[TPC];
+    u32x4 vp[TPC], kf[NKD];
 #pragma unroll
     for (int i = 0; i < TPC; ++i) {
-      const int pc = tid + NTH * i, t = pc / (DH / 8), part = pc % (DH / 8);
-      const long off = (long)(c0 + min(t, nt - 1)) * DH + 8 * part;
-      kp[i] = gld16(kt + off);
-      vp[i] = gld16(vt + off);
+      const int pc = tid + NTH * i, t = pc / (DH / 8), part8 = pc % (DH / 8);
+      vp[i] = gld16(vt + (long)(c0 + min(t, nt - 1)) * DH + 8 * part8);
+    }
+    {
+      const uint16_t *kr = kt + (long)(c0 + min(16 * w + l16, nt - 1)) * DH + 8 * kg;
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) kf[ks] = gld16(kr + 32 * ks);
     }
 #pragma unroll
-    for (int i = 0; i < TPC; ++i) {
-      const int pc = tid + NTH * i;
-      lst16(tks + 8 * pc, kp[i]);
-      lst16(tvs + 8 * pc, vp[i]);
-    }
-    __syncthreads();
-    for (int t = w; t < nt; t += NW) {
-      const uint2 kr = *reinterpret_cast<const uint2 *>(tks + t * DH + 4 * lane);
-      const float k4[4] = {bf16_bits_to_f32(kr.x & 0xFFFFu), bf16_bits_to_f32(kr.x >> 16),
-                           bf16_bits_to_f32(kr.y & 0xFFFFu), bf16_bits_to_f32(kr.y >> 16)};
-      float x[GQ];
+    for (int i = 0; i < TPC; ++i) lst16(tvs + 8 * (tid + NTH * i), vp[i]);
+    {  // logits of tokens 16 w .. 16 w + 15 (lane: head l16, tokens 4 kg + v)
+      f32x4 la = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int gi = 0; gi < GQ; ++gi) {
-        const f32x4 qv = *reinterpret_cast<const f32x4 *>(qf + gi * DH + 4 * lane);
-        x[gi] = fmaf(qv[0], k4[0], fmaf(qv[1], k4[1], fmaf(qv[2], k4[2], qv[3] * k4[3])));
-      }
+      for (int ks = 0; ks < NKD; ++ks)
+        la = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ks]),
+                                                     __builtin_bit_cast(bf16x8, qfr[ks]), la, 0, 0, 0);
+      if (l16 < GQ)
 #pragma unroll
-      for (int gi = 0; gi < GQ; ++gi) x[gi] = wave_sum(x[gi]);
-      const float xl = lane == 0 ? x[0] : lane == 1 ? x[1] : lane == 2 ? x[2] : x[3];
-      if (lane < GQ) tp[t * GQ + lane] = lane < g ? xl * a.scale_log2 : -INFINITY;
+        for (int v = 0; v < 4; ++v) {
+          const int t = 16 * w + 4 * kg + v;
+          tp[t * GQ + l16] = (t < nt && l16 < g) ? la[v] * a.scale_log2 : -INFINITY;
+        }
     }
     __syncthreads();
     if (w < GQ) {   // online softmax of head w over the chunk's nt <= TCH tokens
@@ -763,20 +766,22 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
       }
     }
     __syncthreads();
-    if (vg < g) {
+    if (vg < g) {   // p . V: thread (vg, dims 4 lane .. 4 lane + 3)
       const float alpha = st[2 * GQ + vg];
-      tv0 *= alpha;
-      tv1 *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tv[i] *= alpha;
       for (int t = 0; t < nt; ++t) {
         const float p = tp[t * GQ + vg];
-        const uint32_t v2 = *reinterpret_cast<const uint32_t *>(tvs + t * DH + vd);
-        tv0 = fmaf(p, bf16_bits_to_f32(v2 & 0xFFFFu), tv0);
-        tv1 = fmaf(p, bf16_bits_to_f32(v2 >> 16), tv1);
+        const uint2 v2 = *reinterpret_cast<const uint2 *>(tvs + t * DH + 4 * lane);
+        tv[0] = fmaf(p, bf16_bits_to_f32(v2.x & 0xFFFFu), tv[0]);
+        tv[1] = fmaf(p, bf16_bits_to_f32(v2.x >> 16), tv[1]);
+        tv[2] = fmaf(p, bf16_bits_to_f32(v2.y & 0xFFFFu), tv[2]);
+        tv[3] = fmaf(p, bf16_bits_to_f32(v2.y >> 16), tv[3]);
       }
     }
     __syncthreads();   // the chunk's staging and p are free again
   }
-  float *tpart = a.part + (bhs * n_prow + a.n_split + s) * g * a.PW;
+  float *tpart = a.part + (bhs * n_prow + a.n_split + s * NTQ + (fq - 1)) * g * a.PW;
   if (tid < g) {
     tpart[(long)tid * a.PW + 0] = st[tid];
     tpart[(long)tid * a.PW + 1] = st[GQ + tid];
@@ -784,10 +789,9 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
     tpart[(long)tid * a.PW + 3] = 0.f;
   }
   for (int i = tid; i < g * FF; i += NTH) tpart[(long)(i / FF) * a.PW + 4 + i % FF] = 0.f;
-  if (vg < g) {
-    tpart[(long)vg * a.PW + 4 + FF + vd] = tv0;
-    tpart[(long)vg * a.PW + 4 + FF + vd + 1] = tv1;
-  }
+  if (vg < g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tpart[(long)vg * a.PW + 4 + FF + 4 * lane + i] = tv[i];
 }
 
 template <typename TC, int NK>
@@ -795,7 +799,8 @@ static hipError_t go(const AttendArgs &a, hipStream_t st) {
   const size_t smem = Smem<NK * KS>::BYTES;
   static const bool lds_ok = (allow_dynamic_lds(k_attend_absorb<TC, NK>, smem), true);
   (void)lds_ok;
-  hipLaunchKernelGGL((k_attend_absorb<TC, NK>), dim3(a.B * a.Hkv * a.n_split * 2), dim3(NTH), smem, st, a);
+  if (a.tps % NW != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_attend_absorb<TC, NK>), dim3(a.B * a.Hkv * a.n_split * NQ), dim3(NTH), smem, st, a);
   return hipGetLastError();
 }
 
@@ -807,26 +812,23 @@ bool absorb_supported(int act, int coeff, int resid, int dh, int F, int r, int C
          g <= absorb::GQ && k_eff >= 1 && k_eff <= absorb::MAXSEL;
 }
 
-// Splits per (b, h): about one workgroup per CU over the two halves, at least
-// one round (two slices) per split, at most 32 splits (64 partial rows with the
-// tail's); tps = 64-token slices per split (even); tail tokens per split.
-void absorb_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps, int &tail_per_split) {
+// Splits per (b, h): about one workgroup per CU over the four quarters, at
+// least one round (four slices) per split, at most 16 splits (64 partial rows
+// with the tail's three per split); tps = 64-token slices per split (a
+// multiple of four); tail tokens per split; partial rows per (b, h).
+void absorb_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps, int &tail_per_split,
+                 int &n_part) {
   const int n_slices = k_eff * (C / absorb::TT);
-  int want = (256 + 2 * B * Hkv - 1) / (2 * B * Hkv);
-  const int max_split = (n_slices + 1) / 2;
+  int want = (256 + absorb::NQ * B * Hkv - 1) / (absorb::NQ * B * Hkv);
+  const int max_split = (n_slices + absorb::NW - 1) / absorb::NW;
   if (want > max_split) want = max_split;
-  if (want > 32) want = 32;
+  if (want > 16) want = 16;
   if (want < 1) want = 1;
   tps = (n_slices + want - 1) / want;
-  tps += tps & 1;
+  tps = (tps + absorb::NW - 1) / absorb::NW * absorb::NW;
   n_split = (n_slices + tps - 1) / tps;
   tail_per_split = (T + n_split - 1) / n_split;
-  if (tail_per_split > absorb::RT) {  // the tail share must fit one round's p area
-    n_split = (T + absorb::RT - 1) / absorb::RT;
-    tps = (n_slices + n_split - 1) / n_split;
-    tps += tps & 1;
-    tail_per_split = (T + n_split - 1) / n_split;
-  }
+  n_part = (1 + absorb::NTQ) * n_split;
 }
 
 hipError_t launch_absorb(const AttendArgs &a, hipStream_t st) {

@@ -115,8 +115,7 @@ DecodePlan decode_plan(const lowram_dims *d) {
     p.path = LOWRAM_PATH_CHAIN;
   } else if (absorb_supported(d->act, d->coeff, d->resid, d->head_dim, d->hidden, d->rank, d->chunk, g, p.k_eff) &&
              (long)d->n_ctx * d->rank * 2 < (1L << 31)) {
-    absorb_plan(d->batch, d->heads_kv, p.k_eff, d->chunk, d->n_tail, p.n_split, p.tps, p.tail_per_split);
-    p.n_part = 2 * p.n_split;
+    absorb_plan(d->batch, d->heads_kv, p.k_eff, d->chunk, d->n_tail, p.n_split, p.tps, p.tail_per_split, p.n_part);
     p.path = LOWRAM_PATH_ABSORB;
   } else {
     p.n_split = p.k_eff > 0 ? (p.k_eff + p.cps - 1) / p.cps : 0;

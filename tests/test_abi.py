@@ -319,13 +319,13 @@ def _decode_ws_expected(s, n_part):
 
 def test_decode_workspace_counts_the_partials_of_each_attend_kernel():
     up = lambda x: (x + 255) // 256 * 256
-    # qwen4b-64k runs the absorbed kernel: 8 splits of 8 slices per (b, h) for
-    # 256 workgroups over the two halves of F, a chunk row and a tail row per
-    # split, then A = W1 U (fp16 [B][Hkv][F][r]) and q~ (fp16 hi/lo [B][Hkv][2][4][r])
+    # qwen4b-64k runs the absorbed kernel: 4 splits of 16 slices per (b, h) for
+    # 256 workgroups over the four quarters of F, a chunk row and three tail rows
+    # per split, then A = W1 U (fp16 [B][Hkv][F][r]) and q~ (fp16 hi/lo [B][Hkv][2][4][r])
     s = QWEN4B_64K
     assert P.decode_kernel(dims_of(s)) == "absorb"
     absorbed = up(2 * s.B * s.Hkv * s.F * s.r) + up(2 * s.B * s.Hkv * 2 * 4 * s.r)
-    assert P.workspace_bytes(dims_of(s), L.OP_DECODE) == _decode_ws_expected(s, 2 * 8) + absorbed
+    assert P.workspace_bytes(dims_of(s), L.OP_DECODE) == _decode_ws_expected(s, 4 * 4) + absorbed
     # eight query heads per kv head: the per-chunk matrix-core kernel, one partial
     # per selected chunk, each carrying a share of the tail (no separate tail
     # partial), then the select stage's logit operand: 16-bit hi/lo columns of
