@@ -32,8 +32,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic_llama8b_32k.json")
-ATTEND_SRC = os.path.join(ROOT, "decode_attention_compressed_amd", "csrc", "k_attend_chain.hip")
+CSRC = os.path.join(ROOT, "decode_attention_compressed_amd", "csrc")
+# the source file of each attend kernel (its code hash keys the stored counters)
+ATTEND_SRC = {"chain": "k_attend_chain.hip", "absorb": "k_attend_absorb.hip", "mfma": "k_attend_mfma.hip",
+              "valu": "k_decode.hip"}
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", "attend_traffic_" + workload.replace("-", "_") + ".json")
 
 
 def log(msg):
@@ -124,14 +130,15 @@ def kernel_code_hash(path):
     return hashlib.sha256("\n".join(keep).encode()).hexdigest()
 
 
-def traffic_for_current_kernel():
-    """HBM bytes per attend launch measured by rocprofv3 counters, if they were
-    taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_for_current_kernel(workload, kern):
+    """HBM bytes per attend launch measured by rocprofv3 counters for this
+    workload, if they were taken on the current source of its attend kernel."""
+    path = traffic_file(workload)
+    if kern not in ATTEND_SRC or not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha256") != kernel_code_hash(ATTEND_SRC):
+    if t.get("workload") != workload or t.get("kernel_sha256") != kernel_code_hash(os.path.join(CSRC, ATTEND_SRC[kern])):
         return None
     return t.get("bytes_per_launch")
 
@@ -487,7 +494,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = traffic_for_current_kernel()
+    roof["traffic"] = traffic_for_current_kernel(s.name, kern)
     kname = {"chain": "k_attend_chain (top-k + rebuild-and-attend)", "mfma": "k_attend_mfma (rebuild-and-attend)",
              "absorb": "k_attend_absorb (absorbed first layer; A = W1 U formed with the selection)",
              "valu": "k_attend_valu (rebuild-and-attend)", "none": "tail only"}[kern]

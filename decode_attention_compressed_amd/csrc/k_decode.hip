@@ -652,13 +652,22 @@ __global__ __launch_bounds__(256) void k_dense(const TA *__restrict__ q, const T
 // Dense split-K decode attention for bf16 caches on the matrix cores.
 // grid (n_split, Hkv, B), 256 threads; 64-token tiles.  Logits: each wave
 // feeds its 16 tokens' key rows straight from global memory as the A operand
-// of a 16x16x32 bf16 MFMA against the zero-padded queries; values are staged
-// in LDS and reduced on the vector ALUs.  The next tile's keys and values are
+// of a 16x16x32 bf16 MFMA against the zero-padded queries.  Values: each
+// thread loads the rows of a token pair for 8 head dims and stores them
+// transposed into LDS (fp16, one dword per head dim and token pair, so a
+// wave's stores fall in distinct banks); p . V is then a 16x16x32 fp16 MFMA
+// per 16 head dims and 32 tokens, with p rounded to fp16 (the softmax
+// denominator sums the same rounded p).  The next tile's keys and values are
 // in flight in registers while the current tile is reduced.
 // ---------------------------------------------------------------------------
 typedef __bf16 dbf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 df16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef float df32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef u32x4 dvec4;
+
+__device__ __forceinline__ uint32_t dense_h2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
 
 template <int DH>
 __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__ q,
@@ -666,12 +675,16 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
                                                     const uint16_t *__restrict__ v, long bstride,
                                                     int Hq, int Hkv, int n, int tps, int n_split,
                                                     float *__restrict__ part, int PW, float scale_log2) {
-  constexpr int TT = 64, VS_LD = DH + 8, NK = DH / 32, NV = TT * DH / 8 / 256;
-  __shared__ __align__(16) uint16_t Vs[TT * VS_LD];
-  __shared__ __align__(16) float Ps[16][TT + 4];
+  constexpr int TT = 64, NK = DH / 32;
+  constexpr int VT_LD = TT + 8;                        // transposed V row (one head dim), fp16
+  constexpr int NPP = DH / 8;                          // 8-dim parts of a row
+  constexpr int NVI = (TT / 2) * NPP / 256;            // (token pair, part) items per thread
+  constexpr int NDT = DH / 64;                         // 16-dim output tiles per wave
+  __shared__ __align__(16) uint16_t Vt[DH * VT_LD];
+  __shared__ __align__(16) uint16_t Pt[16 * VT_LD];    // p [head][token] fp16 (rows past the group zero)
   __shared__ float red[64], red2[64], ms[16], ls[16], al[16];
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, gi = lane & 15;
+  const int lane = tid & 63, w = tid >> 6, gi = lane & 15, l16 = lane & 15, kg = lane >> 4;
   const int g = Hq / Hkv;
   const uint16_t *kb = k + (long)b * bstride + (long)h * n * DH;
   const uint16_t *vb = v + (long)b * bstride + (long)h * n * DH;
@@ -681,29 +694,29 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       u32x4 u = v4(0, 0, 0, 0);
-      if (gi < g) u = gld16(qr + 32 * ks + 8 * (lane >> 4));
+      if (gi < g) u = gld16(qr + 32 * ks + 8 * kg);
       qf[ks] = __builtin_bit_cast(dbf16x8, u);
     }
   }
   if (tid < 16) { ms[tid] = -INFINITY; ls[tid] = 0.f; al[tid] = 0.f; }
-  // (query head, dim pair) items of the value reduction
-  constexpr int ITEMS = 16 * DH / 2 / 256;
-  float acc0[ITEMS], acc1[ITEMS];
+  df32x4 oacc[NDT];   // out^T[d][head]: lane (head l16, dims 4 kg + v of tile dt)
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it) { acc0[it] = 0.f; acc1[it] = 0.f; }
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = df32x4{0.f, 0.f, 0.f, 0.f};
   const int t_beg = split * tps, t_end = min(n, t_beg + tps);
-  dvec4 kr[NK], vr[NV];
+  dvec4 kr[NK], vr[NVI][2];
   auto fetch = [&](int t0) {
     // rows past the split's end are clamped to its last row: the loads stay
     // unconditional, and those rows get p = 0
-    const int t = min(t0 + 16 * w + (lane & 15), t_end - 1);
+    const int t = min(t0 + 16 * w + l16, t_end - 1);
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks)
-      kr[ks] = *reinterpret_cast<const dvec4 *>(kb + (long)t * DH + 32 * ks + 8 * (lane >> 4));
+      kr[ks] = *reinterpret_cast<const dvec4 *>(kb + (long)t * DH + 32 * ks + 8 * kg);
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int pc = tid + 256 * u, row = pc / (DH / 8), part = pc % (DH / 8);
-      vr[u] = *reinterpret_cast<const dvec4 *>(vb + (long)min(t0 + row, t_end - 1) * DH + part * 8);
+    for (int u = 0; u < NVI; ++u) {
+      const int it = tid + 256 * u, j = it % (TT / 2), pt = it / (TT / 2);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        vr[u][e] = *reinterpret_cast<const dvec4 *>(vb + (long)min(t0 + 2 * j + e, t_end - 1) * DH + 8 * pt);
     }
   };
   if (t_beg < t_end) fetch(t_beg);
@@ -713,17 +726,23 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8, kr[ks]), qf[ks], acc, 0, 0, 0);
+    // values transposed into LDS: dword (d, token pair j) = (v[2j][d], v[2j + 1][d]) in fp16
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int pc = tid + 256 * u, row = pc / (DH / 8), part = pc % (DH / 8);
-      *reinterpret_cast<dvec4 *>(Vs + row * VS_LD + part * 8) = vr[u];
+    for (int u = 0; u < NVI; ++u) {
+      const int it = tid + 256 * u, j = it % (TT / 2), pt = it / (TT / 2);
+      const uint16_t *a0 = reinterpret_cast<const uint16_t *>(&vr[u][0]);
+      const uint16_t *a1 = reinterpret_cast<const uint16_t *>(&vr[u][1]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint32_t *>(Vt + (8 * pt + i) * VT_LD + 2 * j) =
+            dense_h2(bf16_bits_to_f32(a0[i]), bf16_bits_to_f32(a1[i]));
     }
     if (t0 + TT < t_end) fetch(t0 + TT);
     float mx = -INFINITY;
     float lg[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * w + 4 * (lane >> 4) + i;
+      const int t = t0 + 16 * w + 4 * kg + i;
       lg[i] = t < t_end ? acc[i] * scale_log2 : -INFINITY;
       mx = fmaxf(mx, lg[i]);
     }
@@ -734,11 +753,16 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
     const float m_old = ms[gi];
     const float m_new = fmaxf(m_old, fmaxf(fmaxf(red[gi], red[16 + gi]), fmaxf(red[32 + gi], red[48 + gi])));
     float psum = 0.f;
+    {
+      float pv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = (gi < g && lg[i] != -INFINITY) ? exp2f(lg[i] - m_new) : 0.f;
-      Ps[gi][16 * w + 4 * (lane >> 4) + i] = p;
-      psum += p;
+      for (int i = 0; i < 4; ++i) {
+        const float p = (gi < g && lg[i] != -INFINITY) ? exp2f(lg[i] - m_new) : 0.f;
+        pv[i] = (float)(_Float16)p;
+        psum += pv[i];
+      }
+      *reinterpret_cast<uint2 *>(Pt + gi * VT_LD + 16 * w + 4 * kg) =
+          make_uint2(dense_h2(pv[0], pv[1]), dense_h2(pv[2], pv[3]));
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
@@ -751,31 +775,29 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
       ms[tid] = m_new;
     }
     __syncthreads();
+    {  // out^T[d][head] = alpha out^T + V^T p^T over the tile's 64 tokens
+      const float a_h = al[l16];
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int item = tid + 256 * it, gq = item / (DH / 2), d2 = item % (DH / 2);
-      if (gq < g) {
-        float s0 = acc0[it] * al[gq], s1 = acc1[it] * al[gq];
-#pragma unroll 8
-        for (int t = 0; t < TT; ++t) {
-          const uint32_t vv = *reinterpret_cast<const uint32_t *>(Vs + t * VS_LD + 2 * d2);
-          const float p = Ps[gq][t];
-          s0 = fmaf(p, bf16_bits_to_f32(vv & 0xFFFFu), s0);
-          s1 = fmaf(p, bf16_bits_to_f32(vv >> 16), s1);
-        }
-        acc0[it] = s0;
-        acc1[it] = s1;
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[dt][i] *= a_h;
+        const int d = (w * NDT + dt) * 16 + l16;
+#pragma unroll
+        for (int ks = 0; ks < TT / 32; ++ks)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              *reinterpret_cast<const df16x8 *>(Vt + d * VT_LD + 32 * ks + 8 * kg),
+              *reinterpret_cast<const df16x8 *>(Pt + l16 * VT_LD + 32 * ks + 8 * kg), oacc[dt], 0, 0, 0);
       }
     }
     __syncthreads();
   }
   float *pp = part + (((long)b * Hkv + h) * n_split + split) * g * PW;
   if (tid < g) { pp[tid * PW] = ms[tid]; pp[tid * PW + 1] = ls[tid]; pp[tid * PW + 2] = 0.f; pp[tid * PW + 3] = 0.f; }
+  if (l16 < g)
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it) {
-    const int item = tid + 256 * it, gq = item / (DH / 2), d2 = item % (DH / 2);
-    if (gq < g) { pp[gq * PW + 4 + 2 * d2] = acc0[it]; pp[gq * PW + 4 + 2 * d2 + 1] = acc1[it]; }
-  }
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pp[l16 * PW + 4 + (w * NDT + dt) * 16 + 4 * kg + i] = oacc[dt][i];
 }
 
 // ---------------------------------------------------------------------------
