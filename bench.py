@@ -66,7 +66,34 @@ def parse():
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times: a kernel of known "
                          "traffic that scales hardware byte counters")
+    ap.add_argument("--bw-probe", action="store_true",
+                    help="only report the HBM bandwidth torch's own reduction and copy kernels reach "
+                         "on 2 GiB (what a plain streaming kernel attains on this GPU), then exit")
     return ap.parse_args()
+
+
+def bw_probe():
+    """Read (sum) and read+write (copy) bandwidth of torch's own kernels over a
+    2 GiB bf16 buffer, eager, 10 launches each after 3 untimed ones."""
+    import torch
+    x = torch.ones((2 << 30) // 2, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        x.sum()
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn, nbytes in (("sum_read", lambda: x.sum(), x.numel() * 2),
+                             ("copy_read_write", lambda: y.copy_(x), 2 * x.numel() * 2)):
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 10 * 1e-3
+        res[name + "_gbps"] = round(nbytes / t / 1e9, 1)
+    print(json.dumps({"bw_probe": res, "hbm_peak_gbps": HBM_PEAK_GBPS}))
 
 
 def attend_accounting(s, sel, res_ptr, layer, kernel="chain"):
@@ -343,6 +370,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards over "
               "sequences with no exchange, so N GPUs run N independent copies).", file=sys.stderr)
         sys.exit(2)
+    if args.bw_probe:
+        bw_probe()
+        return
     import torch
 
     import decode_attention_compressed_amd as P
