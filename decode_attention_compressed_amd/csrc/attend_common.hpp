@@ -96,6 +96,110 @@ __device__ void tail_split(const AttendArgs &a, int h, int b, const float *qs, f
   }
 }
 
+// ---------------------------------------------------------------------------
+// Top-k chunk selection by one wave: the k chunks of [0, n_c) with the largest
+// fp64 score in scL (LDS, NSL * 64 entries readable; those past n_c are
+// ignored), the lowest index first among equal scores.  Lane l holds the
+// order keys of chunks 64 i + l in slot i; the k-th largest key is found by a
+// bitwise search on the top 32 bits, then on the low 32 bits among the chunks
+// that tie there (a uniform branch, rare outside crafted ties).  Every count
+// is a 64-lane compare mask and a popcount.  emit(pos, c) is called once per
+// selected chunk c, pos its rank in ascending chunk order.  1 <= k <= n_c <=
+// 64 NSL; lanes of the wave call it together.
+// ---------------------------------------------------------------------------
+template <int NSL, typename Emit>
+__device__ __forceinline__ void wave_topk(const double *scL, int n_c, int k, Emit emit) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  uint32_t khi[NSL], klo[NSL];
+  uint64_t valid[NSL];
+  double sv[NSL];  // the caller's score area holds NSL * 64 entries: read all, mask later
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) sv[i] = scL[WAVE * i + lane];
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) {
+    const int c = WAVE * i + lane;
+    const uint64_t key = c < n_c ? f64_order_key(sv[i]) : 0ull;
+    khi[i] = (uint32_t)(key >> 32);
+    klo[i] = (uint32_t)key;
+    valid[i] = __ballot(c < n_c);
+  }
+  // count of chunks with top half >= x, summed as a tree.  Lanes past n_c
+  // hold key 0 and every x searched below is at least 1, so they never count.
+  auto count_hi = [&](uint32_t x) {
+    int c8[NSL];
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) c8[i] = __popcll(__ballot(khi[i] >= x));
+#pragma unroll
+    for (int n = NSL / 2; n > 0; n /= 2)
+#pragma unroll
+      for (int i = 0; i < n; ++i) c8[i] += c8[i + n];
+    return c8[0];
+  };
+  // the k-th largest top half, highest bit first; stops as soon as exactly
+  // k chunks lie at or above the bits fixed so far (further low bits could
+  // only drop chunks below k)
+  uint32_t th = 0u;
+  for (uint32_t m = 0x80000000u; m != 0u; m >>= 1) {
+    const uint32_t cand = th | m;
+    const int cnt = count_hi(cand);
+    if (cnt >= k) th = cand;
+    if (cnt == k) break;
+  }
+  uint64_t eq_hi[NSL], sel[NSL];
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) {
+    sel[i] = __ballot(khi[i] > th) & valid[i];
+    eq_hi[i] = __ballot(khi[i] == th) & valid[i];
+    n_gt += __popcll(sel[i]);
+    n_eq += __popcll(eq_hi[i]);
+  }
+  if (n_gt + n_eq == k) {  // the threshold's top half is shared by exactly the missing chunks
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) sel[i] |= eq_hi[i];
+  } else {  // more chunks share that top half than are missing: decide on the low halves
+    const int need = k - n_gt;
+    auto count_lo = [&](uint32_t x) {
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < NSL; ++i) cnt += __popcll(__ballot(klo[i] >= x) & eq_hi[i]);
+      return cnt;
+    };
+    uint32_t tl = 0u;
+    for (uint32_t m = 0x80000000u; m != 0u; m >>= 1) {
+      const uint32_t cand = tl | m;
+      const int cnt = count_lo(cand);
+      if (cnt >= need) tl = cand;
+      if (cnt == need) break;
+    }
+    int rem = need;
+    uint64_t eq[NSL];
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) {
+      const uint64_t gt = __ballot(klo[i] > tl) & eq_hi[i];
+      sel[i] |= gt;
+      rem -= __popcll(gt);
+      eq[i] = __ballot(klo[i] == tl) & eq_hi[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) {  // equal keys: lowest chunk index first
+      uint64_t e = eq[i];
+      while (rem > 0 && e) {
+        const uint64_t low = e & (~e + 1ull);
+        sel[i] |= low;
+        e ^= low;
+        --rem;
+      }
+    }
+  }
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) {
+    if ((sel[i] >> lane) & 1ull) emit(base + __popcll(sel[i] & lanemask_lt()), WAVE * i + lane);
+    base += __popcll(sel[i]);
+  }
+}
+
 // Partial of one split for each query head: m, l, the part of l from rebuilt
 // tokens (all of it for a rebuilt split, none for the tail), 0, then accH[F]
 // (zero for the tail) and accV[dh].

@@ -50,6 +50,8 @@ struct CombineArgs {
   int32_t *rclock;      // [B][G][Hkv] reuse clocks advanced once per (b, h), or null
   const void *w2, *b2;  // [B][G][Hkv][dh][F], [B][G][Hkv][dh] act (null when F == 0)
   void *out;            // [B][Hq][dh] act
+  // rows [0, n_comp) of the n_total per (b, h) carry rebuilt chunks; the rows
+  // after them hold tail tokens only, and their hidden sums (zero) are not read
   int B, G, Hq, Hkv, dh, F, layer, g, n_comp, n_total, PW;
 };
 
@@ -79,7 +81,8 @@ struct QOut {
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
-                         double *part, double *scores, hipStream_t st, const QOut &qo = QOut());
+                         double *part, double *scores, hipStream_t st, const QOut &qo = QOut(),
+                         const AttendArgs *absorb = nullptr);
 hipError_t launch_attend(int act, int coeff, int resid, const AttendArgs &a, hipStream_t st);
 // True when the per-chunk MFMA kernel covers these shapes (else the VALU kernel)
 bool mfma_supported(const AttendArgs &a, int act, int coeff, int resid);
@@ -92,16 +95,22 @@ bool chain_supported(int act, int coeff, int resid, int dh, int F, int r, int C,
 constexpr int CHAIN_SELECT_MAX_NC = 512;
 void chain_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps, int &tail_per_split);
 hipError_t launch_attend_chain(int coeff, const AttendArgs &a, hipStream_t st);
+// Largest chunk count for which the absorbed kernel ranks the chunk scores
+// itself (one chunk per thread of its prologue).
+constexpr int ABSORB_SELECT_MAX_NC = 256;
 // Absorbed-first-layer rebuild-and-attend (head dim 256): shapes, split plan
 // (splits per (b, h), 64-token slices per split, tail tokens per split), the
-// per-call formation of A = W1 U_{l,h} and q~ (with the selection) and the
-// attend launcher.  Two partial rows per split:
-// the split's chunks, then its share of the tail.
+// per-call formation of A = W1 U_{l,h} and q~ (in the launch of the partial
+// chunk scores) and the attend launcher.  1 + 3 partial rows per split: the
+// split's chunks, then three shares of its part of the tail.
 bool absorb_supported(int act, int coeff, int resid, int dh, int F, int r, int C, int g, int k_eff);
 void absorb_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps, int &tail_per_split,
                  int &n_part);
 hipError_t launch_attend_absorb(int coeff, const AttendArgs &a, hipStream_t st);
-hipError_t launch_absorb(const AttendArgs &a, hipStream_t st);  // A and q~ into the workspace
+// The partial chunk scores (bf16, d_h = 256) and A, q~ into the workspace,
+// in one launch.
+hipError_t launch_select_absorb(const AttendArgs &a, const float *landmark, double *part, long q_bstride,
+                                hipStream_t st);
 constexpr int REUSE_HIT = 1 << 30;
 size_t chain_tile_bytes(int F);  // bytes of one cached 128-token chunk (its rebuilt keys)
 constexpr int REUSE_MAX_SLOTS = 256;

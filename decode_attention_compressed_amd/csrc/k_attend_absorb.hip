@@ -53,6 +53,7 @@
 #include <type_traits>
 
 #include "attend_common.hpp"
+#include "select_partial.hpp"
 
 namespace lowram {
 namespace absorb {
@@ -173,10 +174,11 @@ template <> struct ResRow<int8_t> {
 // ---------------------------------------------------------------------------
 // A = -log2(e) W1 U_{l,h} (fp16, rows swizzled as the attend kernel's LDS
 // copy) and q~_g = U_{l,h}^T q_g (fp16 hi, lo) for one 64 x 64 tile of
-// (hidden unit, rank); grid (F / 64, r / 64, B Hkv), 256 threads.  int8
+// (hidden unit, rank); (F / 64) (r / 64) B Hkv workgroups, 256 threads.  int8
 // caches: both carry the per-rank scale of the codes.
 // All of a wave's W1 fragments are loaded first, under the staging of the
-// U^T tile (dword LDS writes of two head dims, consecutive over the lanes);
+// U^T tile (whole 128-byte row segments loaded, dword LDS writes of two head
+// dims);
 // the q~ products are bf16 x bf16 (exact) accumulated in fp32 on the matrix
 // cores, like A's; the A tile leaves through LDS in 16-byte rows.
 // ---------------------------------------------------------------------------
@@ -188,9 +190,18 @@ struct AbsorbSmem {
   uint16_t ot[AK][OT_LD];         // A tile, fp16 (hidden-unit rows, ranks contiguous)
 };
 
-__global__ __launch_bounds__(256) void k_absorb(const AttendArgs a) {
-  __shared__ __align__(16) AbsorbSmem sm;
-  const int ft = blockIdx.x, rt = blockIdx.y, bh = blockIdx.z;
+// Tile `lin` of the n = (F / 64) (r / 64) B Hkv tiles, lin counted from a
+// workgroup id that is a multiple of 8.
+__device__ __forceinline__ void absorb_tile(const AttendArgs &a, int lin, int n, AbsorbSmem &sm) {
+  // Workgroups are dispatched round-robin over the 8 XCDs (linear id mod 8),
+  // each with its own L2.  The id is remapped so that an XCD receives a
+  // contiguous run of (hidden tile, rank tile, (b, h)): all tiles of one or
+  // two (b, h), whose W1 and basis slice it then reads from HBM once.
+  constexpr int NFT = FF / AK;
+  const int nrt = a.r / AK;
+  int u = lin;
+  if (n % 8 == 0) u = (lin % 8) * (n / 8) + lin / 8;
+  const int ft = u % NFT, rt = (u / NFT) % nrt, bh = u / (NFT * nrt);
   const int b = bh / a.Hkv, h = bh % a.Hkv, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = a.r, D = a.G * a.Hkv * DH, g = a.g;
   const uint16_t *U = reinterpret_cast<const uint16_t *>(a.basis) + ((long)b * D + (long)(a.layer * a.Hkv + h) * DH) * r;
@@ -213,19 +224,21 @@ __global__ __launch_bounds__(256) void k_absorb(const AttendArgs a) {
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = l16 < g ? gld16(qb + 32 * ks) : v4(0, 0, 0, 0);
   }
   // U^T tile: item (head-dim pair dp, rank octet oc) loads U[2 dp][8 oc ..] and
-  // U[2 dp + 1][8 oc ..] and writes eight dwords ut[8 oc + i][2 dp .. 2 dp + 1]
+  // U[2 dp + 1][8 oc ..] and writes eight dwords ut[8 oc + i][2 dp .. 2 dp + 1].
+  // The octets of a row are consecutive items, so a wave's load covers eight
+  // whole 128-byte row segments.
   constexpr int NIT = (DH / 2) * (AK / 8) / 256;   // items per thread (4)
   u32x4 ua[NIT], ub[NIT];
 #pragma unroll
   for (int k = 0; k < NIT; ++k) {
-    const int it = tid + 256 * k, dp = it % (DH / 2), oc = it / (DH / 2);
+    const int it = tid + 256 * k, oc = it % (AK / 8), dp = it / (AK / 8);
     const uint16_t *up = U + (long)(2 * dp) * r + rt * AK + 8 * oc;
     ua[k] = gld16(up);
     ub[k] = gld16(up + r);
   }
 #pragma unroll
   for (int k = 0; k < NIT; ++k) {
-    const int it = tid + 256 * k, dp = it % (DH / 2), oc = it / (DH / 2);
+    const int it = tid + 256 * k, oc = it % (AK / 8), dp = it / (AK / 8);
     const uint32_t x[4] = {ua[k].x, ua[k].y, ua[k].z, ua[k].w}, y[4] = {ub[k].x, ub[k].y, ub[k].z, ub[k].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -288,6 +301,40 @@ __global__ __launch_bounds__(256) void k_absorb(const AttendArgs a) {
     *reinterpret_cast<u32x4 *>(A + (long)f * r + 8 * swz(f, rt * (AK / 8) + part)) =
         *reinterpret_cast<const u32x4 *>(&sm.ot[row][8 * part]);
   }
+}
+
+// The selection stage of the absorbed path in one launch: workgroups
+// [0, n_sel) compute the partial chunk scores (select_partial_block, bf16,
+// d_h = 256; no q~ output: the tiles below form it), up to the next multiple
+// of 8 idle, the rest form A and q~ (absorb_tile).  The two roles share
+// nothing but the launch.
+struct SelectAbsorbArgs {
+  const float *landmark;  // [B][n_c][r]
+  double *part;           // [B][Hkv][r / 64][n_c] partial chunk scores
+  long q_bstride;         // elements between the query rows of consecutive sequences
+  int n_sel;              // r / 64 * Hkv * B
+};
+
+__global__ __launch_bounds__(256) void k_select_absorb(const AttendArgs a, const SelectAbsorbArgs x) {
+  __shared__ __align__(16) union {
+    SelectSmem<DH, QTG_G> s;
+    AbsorbSmem t;
+  } sm;
+  const int n_pad = (x.n_sel + 7) & ~7;
+  const int id = blockIdx.x;
+  if (id < n_pad) {
+    if (id < x.n_sel) {
+      const int NRB = a.r / SEL_RB;
+      int rb, h, b;
+      select_coords(id, NRB, a.Hkv, a.B, rb, h, b);
+      select_partial_block<bf16, DH, QTG_G>(sm.s, rb, h, b, NRB, reinterpret_cast<const bf16 *>(a.q), x.q_bstride,
+                                            reinterpret_cast<const bf16 *>(a.basis), x.landmark, a.Hq, a.Hkv, a.r,
+                                            a.N / a.C, a.G * a.Hkv * DH, a.layer, x.part, nullptr, nullptr,
+                                            nullptr, 0);
+    }
+    return;
+  }
+  absorb_tile(a, id - n_pad, gridDim.x - n_pad, sm.t);
 }
 
 // ---------------------------------------------------------------------------
@@ -360,14 +407,51 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
   const long bh = ((long)b * a.G + a.layer) * a.Hkv + h;   // (b, layer, h)
   const long bhs = (long)b * a.Hkv + h;                      // (b, h)
 
-  // ---- prologue: A quarter, q~, b1, selection, tail q ------------------------
-  // A quarter: every piece in flight at once (nothing else holds registers yet)
+  // ---- prologue: selection, A quarter, q~, b1 ---------------------------------
+  // With the partial chunk scores at hand (n_c <= NTH), each workgroup ranks
+  // them itself: their loads go first, so that the sum waits for nothing else.
+  // A chunk's score is its rank blocks' partials summed in block order.
+  const int k_eff = a.k_eff, n_c = a.N / C;
+  constexpr int NRB = R / 64;
+  double spv[NRB];
+  if (a.score_part && tid < n_c) {
+    const double *sp = a.score_part + bhs * NRB * n_c + tid;
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) spv[k] = sp[(long)k * n_c];
+  }
+  // A quarter: every piece in flight at once
   constexpr int NP = FQ * R * 2 / 16 / NTH;   // 16-byte pieces per thread
   u32x4 apc[NP];
   {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(a.absA + bhs * (long)FF * R + (long)fq * FQ * R);
 #pragma unroll
     for (int i = 0; i < NP; ++i) apc[i] = src[i * NTH + tid];
+  }
+  if (a.score_part) {
+    // the top k_eff chunks by (score desc, index asc) in ascending index
+    // order, ranked by wave 0 (wave_topk) while the others stage q~, b1 and
+    // their part of A; the (split 0, quarter 0) workgroup writes sel_out.
+    // The scores sit in the round buffers, unused until the first round.
+    static_assert(ABSORB_SELECT_MAX_NC <= NTH && ABSORB_SELECT_MAX_NC == 4 * WAVE, "one chunk per thread");
+    static_assert(S::PS - S::LG >= ABSORB_SELECT_MAX_NC * 8, "score staging");
+    double *scL = reinterpret_cast<double *>(sm + S::LG);
+    if (tid < n_c) {
+      double v = spv[0];
+#pragma unroll
+      for (int k = 1; k < NRB; ++k) v += spv[k];
+      scL[tid] = v;
+    }
+    __syncthreads();
+    if (w == 0) {
+      int32_t *so = (s == 0 && fq == 0 && a.sel_out) ? a.sel_out + bhs * k_eff : nullptr;
+      wave_topk<4>(scL, n_c, k_eff, [&](int pos, int c) {
+        selS[pos] = c;
+        if (so) so[pos] = c;
+      });
+    }
+  } else {
+    const int32_t *selp = a.sel + bhs * k_eff;
+    for (int i = tid; i < k_eff; i += NTH) selS[i] = selp[i];
   }
   {  // q~ hi and lo rows of this (b, h): absQ [2][GQ][R] -> rows 0..7 of QT
     const uint16_t *Qg = a.absQ + bhs * 2 * GQ * R;
@@ -377,9 +461,6 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
       lst16(qd + row * S::QLD + col, gld16(Qg + 8 * i));
     }
   }
-  const int k_eff = a.k_eff;
-  const int32_t *selp = a.sel + bhs * k_eff;
-  for (int i = tid; i < k_eff; i += NTH) selS[i] = selp[i];
   const uint16_t *B1 = reinterpret_cast<const uint16_t *>(a.b1) + bh * FF + fq * FQ;
   for (int i = tid; i < FQ; i += NTH) B1s[i] = bf16_bits_to_f32(B1[i]) * NEG_LOG2E;
   if (tid < GQ) {
@@ -788,7 +869,6 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
     tpart[(long)tid * a.PW + 2] = 0.f;
     tpart[(long)tid * a.PW + 3] = 0.f;
   }
-  for (int i = tid; i < g * FF; i += NTH) tpart[(long)(i / FF) * a.PW + 4 + i % FF] = 0.f;
   if (vg < g)
 #pragma unroll
     for (int i = 0; i < 4; ++i) tpart[(long)vg * a.PW + 4 + FF + 4 * lane + i] = tv[i];
@@ -831,9 +911,15 @@ void absorb_plan(int B, int Hkv, int k_eff, int C, int T, int &n_split, int &tps
   n_part = (1 + absorb::NTQ) * n_split;
 }
 
-hipError_t launch_absorb(const AttendArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(absorb::k_absorb, dim3(absorb::FF / absorb::AK, a.r / absorb::AK, a.B * a.Hkv), dim3(256), 0,
-                     st, a);
+hipError_t launch_select_absorb(const AttendArgs &a, const float *landmark, double *part, long q_bstride,
+                                hipStream_t st) {
+  absorb::SelectAbsorbArgs x;
+  x.landmark = landmark;
+  x.part = part;
+  x.q_bstride = q_bstride;
+  x.n_sel = select_rank_blocks(a.r) * a.Hkv * a.B;
+  const int n_tiles = (absorb::FF / absorb::AK) * (a.r / absorb::AK) * a.B * a.Hkv;
+  hipLaunchKernelGGL(absorb::k_select_absorb, dim3(((x.n_sel + 7) & ~7) + n_tiles), dim3(256), 0, st, a, x);
   return hipGetLastError();
 }
 

@@ -568,13 +568,8 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   float *tl_l = reinterpret_cast<float *>(sm + S::TLS), *tl_m = tl_l + NW * GQ;
   // ---- chunk selection of (b, h): the top k_eff chunks by (score desc, index
   // asc), in ascending index order.  With the scores at hand every workgroup
-  // selects them itself: wave 0 holds the order keys of all chunks (chunk
-  // 64 i + lane in slot i) and finds the k-th largest key by a bitwise search
-  // on its top 32 bits, then on the low 32 bits among the chunks that tie
-  // there (a uniform branch, rare outside crafted ties).  Every count is a
-  // 64-lane compare mask and a popcount.  Chunks whose whole key equals the
-  // threshold (equal doubles) are taken lowest index first.  Split 0 also
-  // writes the whole selection to sel_out.  The other waves attend the tail meanwhile.
+  // selects them itself, on wave 0 (wave_topk); split 0 also writes the whole
+  // selection to sel_out.  The other waves attend the tail meanwhile.
   double *scL = reinterpret_cast<double *>(sm + S::PS);
   if (a.score_part && tid < n_c) {
     double scv = spv[0];
@@ -587,108 +582,16 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     if (a.score_part) {
       // NSL key slots per lane: four while n_c <= 256, so that no count spends
       // compares and popcounts on empty slots
-      auto select_wave = [&](auto nsl) {
-        constexpr int NSL = decltype(nsl)::value;
-        uint32_t khi[NSL], klo[NSL];
-        uint64_t valid[NSL];
-        double sv[NSL];  // the staging area holds CHAIN_SELECT_MAX_NC scores: read all, mask later
-#pragma unroll
-        for (int i = 0; i < NSL; ++i) sv[i] = scL[WAVE * i + lane];
-#pragma unroll
-        for (int i = 0; i < NSL; ++i) {
-          const int c = WAVE * i + lane;
-          const uint64_t key = c < n_c ? f64_order_key(sv[i]) : 0ull;
-          khi[i] = (uint32_t)(key >> 32);
-          klo[i] = (uint32_t)key;
-          valid[i] = __ballot(c < n_c);
-        }
-        const int k = a.k_eff;
-        // count of chunks with top half >= x, summed as a tree.  Lanes past n_c
-        // hold key 0 and every x searched below is at least 1, so they never count.
-        auto count_hi = [&](uint32_t x) {
-          int c8[NSL];
-#pragma unroll
-          for (int i = 0; i < NSL; ++i) c8[i] = __popcll(__ballot(khi[i] >= x));
-#pragma unroll
-          for (int n = NSL / 2; n > 0; n /= 2)
-#pragma unroll
-            for (int i = 0; i < n; ++i) c8[i] += c8[i + n];
-          return c8[0];
-        };
-        // the k-th largest top half, highest bit first; stops as soon as exactly
-        // k chunks lie at or above the bits fixed so far (further low bits could
-        // only drop chunks below k)
-        uint32_t th = 0u;
-        for (uint32_t m = 0x80000000u; m != 0u; m >>= 1) {
-          const uint32_t cand = th | m;
-          const int cnt = count_hi(cand);
-          if (cnt >= k) th = cand;
-          if (cnt == k) break;
-        }
-        uint64_t eq_hi[NSL], sel[NSL];
-        int n_gt = 0, n_eq = 0;
-#pragma unroll
-        for (int i = 0; i < NSL; ++i) {
-          sel[i] = __ballot(khi[i] > th) & valid[i];
-          eq_hi[i] = __ballot(khi[i] == th) & valid[i];
-          n_gt += __popcll(sel[i]);
-          n_eq += __popcll(eq_hi[i]);
-        }
-        if (n_gt + n_eq == k) {  // the threshold's top half is shared by exactly the missing chunks
-#pragma unroll
-          for (int i = 0; i < NSL; ++i) sel[i] |= eq_hi[i];
-        } else {  // more chunks share that top half than are missing: decide on the low halves
-          const int need = k - n_gt;
-          auto count_lo = [&](uint32_t x) {
-            int cnt = 0;
-#pragma unroll
-            for (int i = 0; i < NSL; ++i) cnt += __popcll(__ballot(klo[i] >= x) & eq_hi[i]);
-            return cnt;
-          };
-          uint32_t tl = 0u;
-          for (uint32_t m = 0x80000000u; m != 0u; m >>= 1) {
-            const uint32_t cand = tl | m;
-            const int cnt = count_lo(cand);
-            if (cnt >= need) tl = cand;
-            if (cnt == need) break;
-          }
-          int rem = need;
-          uint64_t eq[NSL];
-#pragma unroll
-          for (int i = 0; i < NSL; ++i) {
-            const uint64_t gt = __ballot(klo[i] > tl) & eq_hi[i];
-            sel[i] |= gt;
-            rem -= __popcll(gt);
-            eq[i] = __ballot(klo[i] == tl) & eq_hi[i];
-          }
-#pragma unroll
-          for (int i = 0; i < NSL; ++i) {  // equal keys: lowest chunk index first
-            uint64_t e = eq[i];
-            while (rem > 0 && e) {
-              const uint64_t low = e & (~e + 1ull);
-              sel[i] |= low;
-              e ^= low;
-              --rem;
-            }
-          }
-        }
-        int base = 0;
-#pragma unroll
-        for (int i = 0; i < NSL; ++i) {
-          if ((sel[i] >> lane) & 1ull) {
-            const int pos = base + __popcll(sel[i] & lanemask_lt()), c = WAVE * i + lane;
-            if (pos >= q0 && pos < q0 + MAXSLOT) selL[pos - q0] = c;
-            if constexpr (REUSE) reinterpret_cast<int32_t *>(sm + S::SELALL)[pos] = c;
-            if (s == 0 && a.sel_out) a.sel_out[((long)b * a.Hkv + h) * a.k_eff + pos] = c;
-          }
-          base += __popcll(sel[i]);
-        }
+      auto emit = [&](int pos, int c) {
+        if (pos >= q0 && pos < q0 + MAXSLOT) selL[pos - q0] = c;
+        if constexpr (REUSE) reinterpret_cast<int32_t *>(sm + S::SELALL)[pos] = c;
+        if (s == 0 && a.sel_out) a.sel_out[((long)b * a.Hkv + h) * a.k_eff + pos] = c;
       };
       static_assert(CHAIN_SELECT_MAX_NC % (4 * WAVE) == 0, "slot counts");
       if (n_c <= 4 * WAVE)
-        select_wave(std::integral_constant<int, 4>{});
+        wave_topk<4>(scL, n_c, a.k_eff, emit);
       else
-        select_wave(std::integral_constant<int, CHAIN_SELECT_MAX_NC / WAVE>{});
+        wave_topk<CHAIN_SELECT_MAX_NC / WAVE>(scL, n_c, a.k_eff, emit);
     } else if (tid < MAXSLOT && q0 + tid < a.k_eff) {
       selL[tid] = selv;
     }

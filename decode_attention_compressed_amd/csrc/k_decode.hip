@@ -18,6 +18,7 @@
 #include "common.hpp"
 #include "internal.hpp"
 #include "attend_common.hpp"
+#include "select_partial.hpp"
 
 namespace lowram {
 
@@ -34,251 +35,6 @@ namespace lowram {
 // Every score is reduced in the same fixed order (lane partials, then a
 // butterfly), so equal landmark rows give equal scores.
 // ---------------------------------------------------------------------------
-// 8 consecutive basis values of one row as float64
-template <typename TA> struct Load8;
-template <> struct Load8<bf16> {
-  typedef u32x4 raw;
-  static constexpr int N = 1;
-  __device__ static void ld(const bf16 *p, raw *v) { v[0] = gld16(p); }
-  __device__ static void f64(const raw *v, double *o) {
-    const uint32_t w[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[2 * i] = (double)bf16_bits_to_f32(w[i] & 0xFFFFu);
-      o[2 * i + 1] = (double)bf16_bits_to_f32(w[i] >> 16);
-    }
-  }
-};
-template <> struct Load8<float> {
-  typedef u32x4 raw;
-  static constexpr int N = 2;
-  __device__ static void ld(const float *p, raw *v) { v[0] = gld16(p); v[1] = gld16(p + 4); }
-  __device__ static void f64(const raw *v, double *o) {
-    const uint32_t w[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (double)__uint_as_float(w[i]);
-  }
-};
-
-// Sums R rows of per-lane partials over the lanes that differ in the log2 R
-// lane bits OFF0, OFF0 / 2, ... (R a power of two).  Each step also
-// transposes: over lane bit k a lane keeps the half of its rows that its bit
-// selects and adds the partner's partials of those rows, so one value per
-// lane remains.  Every row is summed by the same pairwise tree whatever its
-// position, so equal inputs give equal sums.  On return a lane holds the row
-// whose index has the lane's bits OFF0, OFF0 / 2, ... as its binary digits,
-// most significant first.
-template <int N, int OFF>
-__device__ __forceinline__ void xpose_step(double *v, int lane) {
-  if constexpr (N > 1) {
-    const bool hi = (lane & OFF) != 0;
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-      const double keep = hi ? v[N / 2 + i] : v[i];
-      const double send = hi ? v[i] : v[N / 2 + i];
-      v[i] = keep + __shfl_xor(send, OFF, WAVE);
-    }
-    xpose_step<N / 2, OFF / 2>(v, lane);
-  }
-}
-template <int R, int OFF0>
-__device__ __forceinline__ double xpose_sum(double (&v)[R], int lane) {
-  static_assert((R & (R - 1)) == 0 && R <= 2 * OFF0, "R a power of two within the lane bits");
-  xpose_step<R, OFF0>(v, lane);
-  return v[0];
-}
-template <int N, int OFF>
-__device__ __forceinline__ void xpose_step_f32(float *v, int lane) {
-  if constexpr (N > 1) {
-    const bool hi = (lane & OFF) != 0;
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-      const float keep = hi ? v[N / 2 + i] : v[i];
-      const float send = hi ? v[i] : v[N / 2 + i];
-      v[i] = keep + __shfl_xor(send, OFF, WAVE);
-    }
-    xpose_step_f32<N / 2, OFF / 2>(v, lane);
-  }
-}
-template <int R, int OFF0>
-__device__ __forceinline__ float xpose_sum_f32(float (&v)[R], int lane) {
-  xpose_step_f32<R, OFF0>(v, lane);
-  return v[0];
-}
-
-// D1 and D2 per block of 64 ranks.  grid (ceil(r / 64), Hkv, B), 256 threads;
-// block rb of (b, h) writes part[b][h][rb][j] = sum over its ranks i of
-// q~_i landmark_{b,j,i}, with q~ = U_{l,h}^T sum_g q_g restricted to the block.
-// The chunk score is the sum of the blocks' partials in block order (summed by
-// the consumer).  Splitting the rank dimension reads every basis row once and
-// each landmark row once per kv head; a split over chunks would make every
-// workgroup rebuild the whole q~.
-//
-// q~ of the block: lane (rank group lane & 7, slice 8 w + (lane >> 3)) sums
-// eight ranks over head dims slice + 32 k in ascending k; the wave's eight
-// slices are added by a transposing butterfly and the four waves in order.
-// Partials: 16 lanes per chunk, four ranks (one 16-byte landmark piece) each,
-// sixteen chunk rows in flight per lane, then a transposing butterfly over
-// the 16 lanes.  Blocks are regrouped so that the heads of one (sequence,
-// rank block) share an XCD and its L2 copy of those landmark columns.
-constexpr int SEL_RB = 64;
-
-template <typename TA, int DH, int QG>
-__global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q, long q_bstride,
-                                                        const TA *__restrict__ basis,
-                                                        const float *__restrict__ landmark, int Hq,
-                                                        int Hkv, int r, int n_c, int D, int layer,
-                                                        double *__restrict__ part, float *__restrict__ qtg,
-                                                        uint16_t *__restrict__ qfrag,
-                                                        const uint16_t *__restrict__ qf_scale, int qf_mode) {
-  constexpr int RPS = DH / 32;  // basis rows per slice
-  __shared__ double qsum[DH];
-  __shared__ double qtp[4][SEL_RB];
-  __shared__ double qt[SEL_RB];
-  __shared__ float qg[QG][DH];             // q of each query head (qtg only)
-  __shared__ float qtpg[4][QG][SEL_RB];    // per-wave parts of q~_g (qtg only)
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const int NRB = gridDim.x;
-  int rb, h, b;
-  {
-    const int P = NRB * gridDim.z;  // (sequence, rank block) pairs
-    const int lin = blockIdx.x + NRB * (blockIdx.y + Hkv * blockIdx.z);
-    if (P % 8 == 0) {
-      const int xcd = lin % 8, i = lin / 8, pr = xcd * (P / 8) + i / Hkv;
-      h = i % Hkv; b = pr / NRB; rb = pr % NRB;
-    } else {
-      rb = blockIdx.x; h = blockIdx.y; b = blockIdx.z;
-    }
-  }
-  const int i0 = rb * SEL_RB, nr = min(SEL_RB, r - i0);  // ranks of this block (a multiple of 16)
-
-  // basis rows of this thread: rank group rg, head dims sl + 32 k
-  const int rg = lane & 7, sl = 8 * w + (lane >> 3);
-  const bool rg_ok = 8 * rg < nr;
-  const TA *U = basis + ((long)b * D + (long)(layer * Hkv + h) * DH) * r + i0 + 8 * (rg_ok ? rg : 0);
-  typename Load8<TA>::raw raw[RPS][Load8<TA>::N];
-#pragma unroll
-  for (int k = 0; k < RPS; ++k) Load8<TA>::ld(U + (long)(sl + 32 * k) * r, raw[k]);
-  // landmark pieces of the first 16 chunk rows (independent of q~)
-  const int gq = lane >> 4, li = lane & 15;
-  const bool li_ok = 4 * li < nr;
-  const float *L = landmark + (long)b * n_c * r + i0 + 4 * (li_ok ? li : 0);
-  constexpr int MB = 16;  // chunk rows per lane in flight
-  u32x4 lv[MB];
-  auto load_rows = [&](int j_base) {
-#pragma unroll
-    for (int m = 0; m < MB; ++m) lv[m] = gld16(L + (long)min(j_base + 16 * m + 4 * w + gq, n_c - 1) * r);
-  };
-  load_rows(0);
-  const int grp = Hq / Hkv;
-  if (tid < DH) {
-    const TA *qb = q + (long)b * q_bstride + (long)h * grp * DH;
-    double sq = 0.0;
-    for (int gi = 0; gi < grp; ++gi) sq += to_f64(qb[gi * DH + tid]);
-    qsum[tid] = sq;
-    if (qtg || qfrag)
-      for (int gi = 0; gi < QG; ++gi) qg[gi][tid] = gi < grp ? to_f32(qb[gi * DH + tid]) : 0.f;
-  }
-  __syncthreads();
-  // q~_g of each query head over the block's ranks, in float32, four heads at
-  // a time (groups past the kv head's query heads are skipped: zero rows)
-  const int ng4 = (min(grp, QG) + 3) / 4;
-  if (qtg || qfrag)
-    for (int g4 = 0; g4 < ng4; ++g4) {
-      float acc[4][8];
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[gi][e] = 0.f;
-#pragma unroll
-      for (int k = 0; k < RPS; ++k) {
-        double u[8];
-        Load8<TA>::f64(raw[k], u);
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const float wq = qg[4 * g4 + gi][sl + 32 * k];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[gi][e] = fmaf((float)u[e], wq, acc[gi][e]);
-        }
-      }
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
-        qtpg[w][4 * g4 + gi][8 * rg + (lane >> 3)] = xpose_sum_f32<8, 32>(acc[gi], lane);  // rank 8 rg + (lane >> 3)
-    }
-  {
-    double acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-#pragma unroll
-    for (int k = 0; k < RPS; ++k) {
-      double u[8];
-      Load8<TA>::f64(raw[k], u);
-      const double wq = qsum[sl + 32 * k];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fma(u[e], wq, acc[e]);
-    }
-    const double v = xpose_sum<8, 32>(acc, lane);  // rank 8 rg + (lane >> 3), this wave's slices
-    qtp[w][8 * rg + (lane >> 3)] = v;
-  }
-  __syncthreads();
-  if (tid < SEL_RB) qt[tid] = ((qtp[0][tid] + qtp[1][tid]) + qtp[2][tid]) + qtp[3][tid];
-  if (qtg)  // [b][h][QG][r]; rows past the group are zero
-    for (int it = tid; it < QG * SEL_RB; it += 256) {
-      const int gi = it / SEL_RB, ri = it % SEL_RB;
-      if (ri < nr)
-        qtg[(((long)b * Hkv + h) * QG + gi) * r + i0 + ri] =
-            gi < 4 * ng4 ? ((qtpg[0][gi][ri] + qtpg[1][gi][ri]) + qtpg[2][gi][ri]) + qtpg[3][gi][ri] : 0.f;
-    }
-  if (qfrag) {
-    // MFMA operand columns for the per-chunk kernel's coefficient-space logits,
-    // [b][h][2][16][r] 16-bit.  x = q~_g (times the rank scale for int8 codes)
-    // is split into hi = x rounded to the codes' MFMA type (bf16 for bf16
-    // codes, fp16 for int8) and lo = (x - hi) rounded.  With 2g <= 16, tile 0
-    // column c holds hi of head c (c < g) or lo of head c - g (c < 2g); with
-    // g > 8, tile 0 holds the hi halves and tile 1 the lo halves.  Other
-    // columns are zero.
-    const bool two = grp > 8;
-    for (int it = tid; it < 2 * 16 * SEL_RB; it += 256) {
-      const int tile = it / (16 * SEL_RB), c = (it / SEL_RB) % 16, ri = it % SEL_RB;
-      if (ri >= nr || (tile == 1 && !two)) continue;
-      const bool ok = two ? c < grp : c < 2 * grp;
-      const bool lo = two ? tile == 1 : c >= grp;
-      const int gi = ok ? (two ? c : (lo ? c - grp : c)) : 0;
-      float x = ok ? ((qtpg[0][gi][ri] + qtpg[1][gi][ri]) + qtpg[2][gi][ri]) + qtpg[3][gi][ri] : 0.f;
-      uint16_t v;
-      if (qf_mode == 2) {
-        x *= f16_bits_to_f32(qf_scale[(long)b * r + i0 + ri]);
-        const _Float16 xh = (_Float16)x;
-        v = __builtin_bit_cast(uint16_t, lo ? (_Float16)(x - (float)xh) : xh);
-      } else {
-        const uint16_t xh = f32_to_bf16_bits(x);
-        v = lo ? f32_to_bf16_bits(x - bf16_bits_to_f32(xh)) : xh;
-      }
-      qfrag[((((long)b * Hkv + h) * 2 + tile) * 16 + c) * r + i0 + ri] = v;
-    }
-  }
-  __syncthreads();
-
-  double qv[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) qv[e] = li_ok ? qt[4 * li + e] : 0.0;
-  double *pb = part + (((long)b * Hkv + h) * NRB + rb) * n_c;
-  for (int j_base = 0; j_base < n_c; j_base += 16 * MB) {
-    if (j_base > 0) load_rows(j_base);
-    double sacc[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      const uint32_t w4[4] = {lv[m].x, lv[m].y, lv[m].z, lv[m].w};
-      sacc[m] = 0.0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sacc[m] = fma((double)__uint_as_float(w4[e]), qv[e], sacc[m]);
-    }
-    const double tot = xpose_sum<MB, 8>(sacc, lane);  // chunk row li of lane group gq
-    const int j = j_base + 16 * li + 4 * w + gq;
-    if (j < n_c) pb[j] = tot;
-  }
-}
-
 // scores[b][h][j] = sum over rank blocks rb (in order) of part[b][h][rb][j].
 // grid (ceil(n_c / 256), Hkv, B), 256 threads.
 // p[0] + p[n] + p[2 n] + ... over NRB rank blocks, added in block order.  The
@@ -539,8 +295,11 @@ __global__ __launch_bounds__(256) void k_combine(const CombineArgs a) {
       if (so + u * sub < nb && pc < per_split) lst16(stage + (so + u * sub) * n_out + 4 * pc, v[u]);
     __syncthreads();
     for (int o = tid; o < n_out; o += 256) {
-      float vv = acc[o];  // (a tail split's accH is zero)
-      for (int u = 0; u < nb; ++u) vv = fmaf(wts[s0 + u], stage[u * n_out + o], vv);
+      // hidden sums only from the rows that rebuilt chunks (a tail-only row's
+      // hidden sums are zero and its kernel need not write them)
+      const int nu = o < a.F ? min(nb, max(a.n_comp - s0, 0)) : nb;
+      float vv = acc[o];
+      for (int u = 0; u < nu; ++u) vv = fmaf(wts[s0 + u], stage[u * n_out + o], vv);
       acc[o] = vv;
     }
   }
@@ -828,8 +587,12 @@ static void launch_partial(const TA *q, long q_bstride, const TA *basis, const f
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
                          const float *landmark, int B, int Hq, int Hkv, int dh, int r, int n_c,
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
-                         double *part, double *scores, hipStream_t st, const QOut &qo) {
-  if (act == LOWRAM_F32)
+                         double *part, double *scores, hipStream_t st, const QOut &qo,
+                         const AttendArgs *absorb) {
+  if (absorb) {
+    const hipError_t e = launch_select_absorb(*absorb, landmark, part, q_bstride, st);
+    if (e != hipSuccess) return e;
+  } else if (act == LOWRAM_F32)
     launch_partial<float>((const float *)q, q_bstride, (const float *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qo, st);
   else
     launch_partial<bf16>((const bf16 *)q, q_bstride, (const bf16 *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qo, st);
@@ -914,7 +677,9 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
   __shared__ __align__(16) float accHm[GM][F + 8 * SPAD];
   __shared__ float accVm[GM][KV_DQ];
   const int dq = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int g = a.g, S = a.n_total;
+  // rows past the first n_comp hold tail tokens only: their hidden sums are
+  // zero by definition and are neither written nor read
+  const int g = a.g, S = a.n_total, nc = a.n_comp;
   const long sstride = (long)g * a.PW;
   const float *p0 = a.part + ((long)b * a.Hkv + h) * S * sstride;
   const long bh = ((long)b * a.G + a.layer) * a.Hkv + h;
@@ -939,7 +704,7 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
       const int pr = tid + 256 * k, gi = pr / FP, pc = pr % FP;
 #pragma unroll
       for (int u = 0; u < KV_SB; ++u)
-        if (u < nb && gi < g)
+        if (u < nb && gi < g && s0 + u < nc)
           hp[k][u] = *reinterpret_cast<const f32v4 *>(p0 + (long)(s0 + u) * sstride + (long)gi * a.PW + 4 + 4 * pc);
     }
 #pragma unroll
@@ -984,7 +749,7 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
       if (gi < g) {
 #pragma unroll
         for (int u = 0; u < KV_SB; ++u)
-          if (u < nb) {
+          if (u < nb && s0 + u < nc) {
             const float w = wt[s0 + u][gi];
             hacc[k].x = fmaf(w, hp[k][u].x, hacc[k].x);
             hacc[k].y = fmaf(w, hp[k][u].y, hacc[k].y);

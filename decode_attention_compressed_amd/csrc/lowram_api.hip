@@ -307,9 +307,10 @@ lowram_status check_decode_inputs(const lowram_dims *d, int32_t layer, const low
   return LOWRAM_OK;
 }
 
-// True when the chained attend kernel ranks the chunk scores itself.
+// True when the attend kernel ranks the chunk scores itself.
 bool attend_selects(const lowram_dims *d, const DecodePlan &p) {
-  return p.path == LOWRAM_PATH_CHAIN && n_chunks(d) <= CHAIN_SELECT_MAX_NC;
+  return (p.path == LOWRAM_PATH_CHAIN && n_chunks(d) <= CHAIN_SELECT_MAX_NC) ||
+         (p.path == LOWRAM_PATH_ABSORB && n_chunks(d) <= ABSORB_SELECT_MAX_NC);
 }
 
 AttendArgs make_attend(const lowram_dims *d, int32_t layer, const lowram_model *m,
@@ -468,15 +469,16 @@ lowram_status run_select(const lowram_dims *d, int32_t layer, const lowram_model
     qo.mode = d->coeff == LOWRAM_I8 ? 2 : 1;
     qo.scale = reinterpret_cast<const uint16_t *>(c->coeff_scale);
   }
-  lowram_status st = hip_status(launch_select(d->act, q, (long)d->heads_q * d->head_dim, m->basis, c->landmark,
-                                              d->batch, d->heads_q, d->heads_kv, d->head_dim, d->rank,
-                                              n_chunks(d), (int)D, layer, with_topk ? p.k_eff : 0, sel, sel_out,
-                                              sp, with_topk ? sc : nullptr, (hipStream_t)stream, qo),
-                                "lowram_decode_select");
-  if (st != LOWRAM_OK || p.path != LOWRAM_PATH_ABSORB) return st;
-  // absorbed path: A = W1 U_{l,h} and q~ for this call, next to the selection
-  const AttendArgs a = make_attend(d, layer, m, c, q, nullptr, nullptr, ws, p, nullptr);
-  return hip_status(launch_absorb(a, (hipStream_t)stream), "lowram_decode_select");
+  // absorbed path: A = W1 U_{l,h} and q~ for this call, in the launch of the
+  // partial scores
+  AttendArgs ab;
+  if (p.path == LOWRAM_PATH_ABSORB) ab = make_attend(d, layer, m, c, q, nullptr, nullptr, ws, p, nullptr);
+  return hip_status(launch_select(d->act, q, (long)d->heads_q * d->head_dim, m->basis, c->landmark,
+                                  d->batch, d->heads_q, d->heads_kv, d->head_dim, d->rank,
+                                  n_chunks(d), (int)D, layer, with_topk ? p.k_eff : 0, sel, sel_out,
+                                  sp, with_topk ? sc : nullptr, (hipStream_t)stream, qo,
+                                  p.path == LOWRAM_PATH_ABSORB ? &ab : nullptr),
+                    "lowram_decode_select");
 }
 
 }  // namespace

@@ -130,6 +130,8 @@ lowram_status lowram_workspace_bytes(const lowram_dims *dims, int32_t op, size_t
  *                      first predictor layer absorbed into the basis
  *                      (A = W1 U_{l,h}, formed per call in the workspace) and
  *                      logits taken in coefficient space, on the matrix cores;
+ *                      with n_c <= 256 it also ranks the chunk scores in its
+ *                      prologue;
  *   LOWRAM_PATH_MFMA   one workgroup per selected chunk on the matrix cores
  *                      (other bf16 shapes compiled for it, g <= 16), logits in
  *                      coefficient space;
@@ -189,7 +191,8 @@ lowram_status lowram_decode_attn(const lowram_dims *dims, int32_t layer, const l
  *            every query head of this call into the workspace on the CHAIN,
  *            MFMA and ABSORB paths, and W1 U_{l,h} on LOWRAM_PATH_ABSORB;
  *   attend:  rebuild-and-attend over the selected chunks and the tail, writing
- *            per-split softmax partials into the workspace;
+ *            per-split softmax partials into the workspace (a kernel that
+ *            ranks the chunk scores itself takes the same selection again);
  *   combine: merges the partials and applies the hoisted second predictor
  *            layer, writing out. */
 lowram_status lowram_decode_select(const lowram_dims *dims, int32_t layer, const lowram_model *model,

@@ -310,16 +310,20 @@ def _copy_chunks(src_of):
     ("all-equal", small(LLAMA8B_32K, B=1, N=2048, T=16), 6, lambda j: 0),
     # runs of three equal chunks over 320 chunks (eight key slots per lane)
     ("triples-nc-320", small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=40960, T=16), 10, lambda j: j - j % 3),
+    # the absorbed kernel (head dim 256) ranks the scores in its own prologue
+    ("absorb-pairs", small(QWEN4B_64K, B=1, N=4096, T=16), 5, lambda j: j - j % 2),
+    ("absorb-all-equal", small(QWEN4B_64K, B=1, N=4096, T=16), 6, lambda j: 0),
 ])
 def test_selection_ties(name, shape, top_k, src_of):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     print(f"\n[case] ties {name}: {shape}", flush=True)
+    assert P().decode_kernel(dims_of(shape, top_k=top_k)) == ("absorb" if name.startswith("absorb") else "chain")
     out, sel, ref, rsel, host, inp = _roundtrip(shape, top_k, edit=_copy_chunks(src_of))
     lm = host["landmark"][0]
     assert any(np.array_equal(lm[j], lm[src_of(j)]) for j in range(1, lm.shape[0]) if src_of(j) != j)
     assert np.array_equal(sel, rsel)
-    if name == "all-equal":
+    if name.endswith("all-equal"):
         assert np.array_equal(sel[0, 0], np.arange(top_k))
     ok, worst = within_tol(out, ref)
     assert ok, worst
