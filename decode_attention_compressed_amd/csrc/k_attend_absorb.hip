@@ -454,11 +454,20 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_absorb(const AttendArgs a) {
     for (int i = tid; i < k_eff; i += NTH) selS[i] = selp[i];
   }
   {  // q~ hi and lo rows of this (b, h): absQ [2][GQ][R] -> rows 0..7 of QT
+    // (a thread's pieces loaded together)
+    constexpr int NQP = 2 * GQ * R / 8, QPT = (NQP + NTH - 1) / NTH;
     const uint16_t *Qg = a.absQ + bhs * 2 * GQ * R;
     uint16_t *qd = reinterpret_cast<uint16_t *>(sm + S::QT);
-    for (int i = tid; i < 2 * GQ * R / 8; i += NTH) {
-      const int row = (8 * i) / R, col = (8 * i) % R;
-      lst16(qd + row * S::QLD + col, gld16(Qg + 8 * i));
+    u32x4 qp[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int i = tid + NTH * k;
+      if (i < NQP) qp[k] = gld16(Qg + 8 * i);
+    }
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int i = tid + NTH * k;
+      if (i < NQP) lst16(qd + ((8 * i) / R) * S::QLD + (8 * i) % R, qp[k]);
     }
   }
   const uint16_t *B1 = reinterpret_cast<const uint16_t *>(a.b1) + bh * FF + fq * FQ;

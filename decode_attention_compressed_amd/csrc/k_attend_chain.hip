@@ -513,6 +513,34 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
     }
   }
 
+  // U^T q_g of the kv head's query heads (fp32, from the select stage), split
+  // by waves 1..NW-1 into MFMA halves below: all of a thread's values are
+  // loaded here at once (wave 0 and spare items read past the end: zeros)
+  constexpr int W1T = NTH - WAVE;                             // threads of waves 1..NW-1
+  constexpr int QTP = (GQ * NR * KS + W1T - 1) / W1T;         // q~ values per such thread
+  static_assert(QTG_G == GQ, "q~ rows per kv head");
+  const int tw = tid - WAVE;
+  float qtv[QTP];
+  uint16_t qts[QTP];  // int8 codes: the rank scale of each value
+  {
+    const rsrc_t Qr = make_rsrc(a.qtg + ((long)b * a.Hkv + h) * QTG_G * r, (uint32_t)(GQ * r * 4));
+#pragma unroll
+    for (int k = 0; k < QTP; ++k) {
+      const int i = tw + W1T * k;
+      const bool ok = w != 0 && i < GQ * r;
+      qtv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(Qr, ok ? 4u * (uint32_t)i : 0x80000000u, 0u, 0));
+    }
+    if constexpr (I8) {
+      const rsrc_t Sr = make_rsrc(csc, (uint32_t)(r * 2));
+#pragma unroll
+      for (int k = 0; k < QTP; ++k) {
+        const int i = tw + W1T * k;
+        const bool ok = w != 0 && i < GQ * r;
+        qts[k] = __builtin_amdgcn_raw_buffer_load_b16(Sr, ok ? 2u * (uint32_t)(i % r) : 0x80000000u, 0u, 0);
+      }
+    }
+  }
+
   u32x4 ur[NU][SP], us_[NU];
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
@@ -529,9 +557,7 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
   // zeros, no memory traffic) so that the waits before the barrier need not
   // cover them.
   constexpr int W1N = F * DH / 8;                             // 16-byte W1 pieces
-  constexpr int W1T = NTH - WAVE;                             // threads of waves 1..NW-1
   constexpr int W1P = (W1N + W1T - 1) / W1T;                  // pieces per such thread
-  const int tw = tid - WAVE;
   const rsrc_t W1r = make_rsrc(W1, (uint32_t)(F * DH * 2));
   u32x4 w1r[W1P];
 #pragma unroll
@@ -635,11 +661,12 @@ __global__ __launch_bounds__(NTH, 1) void k_attend_chain(const AttendArgs a) {
       // 2^-22 (fp16) relative: a key rebuilt and rounded to fp16 would move
       // logits in the hundreds by ~0.1.
       uint16_t *qsh = reinterpret_cast<uint16_t *>(sm + S::QSC), *qsl = qsh + GQ * r;
-      const float *qtb = a.qtg + ((long)b * a.Hkv + h) * QTG_G * r;
-      static_assert(QTG_G == GQ, "q~ rows per kv head");
-      for (int i = tw; i < GQ * r; i += W1T) {
-        const int gi = i / r, rr = i - gi * r;
-        const float v = gi < g ? qtb[i] * (I8 ? f16_bits_to_f32(csc[rr]) : 1.f) : 0.f;
+#pragma unroll
+      for (int k = 0; k < QTP; ++k) {
+        const int i = tw + W1T * k;
+        if (i >= GQ * r) break;
+        const int gi = i / r;
+        const float v = gi < g ? qtv[k] * (I8 ? f16_bits_to_f32(qts[k]) : 1.f) : 0.f;
         uint16_t hi, lo;
         if constexpr (I8) {
           const _Float16 hv = (_Float16)v;
