@@ -656,7 +656,8 @@ hipError_t launch_attend_valu(int act, int coeff, int resid, const AttendArgs &a
 // multiple of 128: one workgroup per (sequence, kv head, 32 head dims) merges
 // the splits of all query heads of the kv head and applies the rows of W2 it
 // owns.  Every global read is issued before the first is used (split
-// heads, hidden sums, value sums, W2 rows and b2): one memory round trip.
+// heads first, then W2 rows and b2, hidden sums, value sums): one memory
+// round trip, and the split weights are formed while the rest is in flight.
 // Sums run in split order, so the result is deterministic.
 // grid (d_h / 32, Hkv, B), 256 threads.
 // ---------------------------------------------------------------------------
@@ -668,13 +669,10 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
   constexpr int GM = 4, FP = F / 4;                   // float4 pieces of a hidden row
   constexpr int PPT = (GM * FP + 255) / 256;          // (g, piece) pairs per thread
   constexpr int WPT = F / 8 / 8;                      // 16-byte W2 pieces per thread (8 threads per row)
-  __shared__ float hd[64][GM][3];                     // split heads m, l, mass
   __shared__ float wt[64][GM];                        // split weights
   __shared__ float fin[GM][3];                        // M, 1/L, mass
-  // merged hidden sums; the eighth of a row that one W2 thread reads is padded
-  // by 4 floats, so that the eight eighths fall in different LDS banks
-  constexpr int SEG = F / 8, SPAD = 4;
-  __shared__ __align__(16) float accHm[GM][F + 8 * SPAD];
+  // merged hidden sums
+  __shared__ __align__(16) float accHm[GM][F];
   __shared__ float accVm[GM][KV_DQ];
   const int dq = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   // rows past the first n_comp hold tail tokens only: their hidden sums are
@@ -687,62 +685,84 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
   const uint16_t *W2 = reinterpret_cast<const uint16_t *>(a.w2) + (bh * DH + (long)dq * KV_DQ) * F;
   const uint16_t *B2 = reinterpret_cast<const uint16_t *>(a.b2) + bh * DH + dq * KV_DQ;
 
-  // W2 rows of this quarter and b2 (independent of the partials)
-  const int wr = tid >> 3, ws = tid & 7;             // row, eighth of the row
+  // split heads (m, l, mass) first, thread (split tid / GM, head tid % GM):
+  // the weights need only them.  Every load below is unconditional (indices
+  // clamped into the partials of this (b, h), values past the counts unused),
+  // so the wait for the heads covers nothing issued after them.
+  static_assert(64 * GM <= 256, "one split head per thread");
+  const int hs = tid / GM, hg = tid % GM;
+  const bool h_ok = hs < S && hg < g;
+  const u32x4 hv = gld16(p0 + (long)min(hs, S - 1) * sstride + (long)min(hg, g - 1) * a.PW);
+  // W2 rows of this workgroup and b2 (independent of the partials): thread
+  // (row wr, lane ws of 8) takes the 16-byte pieces ws, ws + 8, ... of its
+  // row, so the eight threads of a row read 128 contiguous bytes per load
+  const int wr = tid >> 3, ws = tid & 7;
   u32x4 w2r[WPT];
 #pragma unroll
-  for (int i = 0; i < WPT; ++i) w2r[i] = gld16(W2 + (long)wr * F + ws * (F / 8) + 8 * i);
+  for (int i = 0; i < WPT; ++i) w2r[i] = gld16(W2 + (long)wr * F + 8 * (8 * i + ws));
   const float b2v = bf16_bits_to_f32(B2[wr]);
   // hidden and value sums of the first KV_SB splits: thread pairs (gi, piece)
-  // and (gi, dd), loads in flight before the split heads are combined
+  // and (gi, dd), in flight while the split weights are formed
   const int vg = tid / KV_DQ, vd = tid % KV_DQ;
   f32v4 hp[PPT][KV_SB];
   float vv[KV_SB];
-  auto load_batch = [&](int s0, int nb) {
+  auto load_batch = [&](int s0) {
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
-      const int pr = tid + 256 * k, gi = pr / FP, pc = pr % FP;
+      const int pr = tid + 256 * k, gi = min(pr / FP, g - 1), pc = pr % FP;
 #pragma unroll
       for (int u = 0; u < KV_SB; ++u)
-        if (u < nb && gi < g && s0 + u < nc)
-          hp[k][u] = *reinterpret_cast<const f32v4 *>(p0 + (long)(s0 + u) * sstride + (long)gi * a.PW + 4 + 4 * pc);
+        hp[k][u] = *reinterpret_cast<const f32v4 *>(p0 + (long)min(s0 + u, nc - 1) * sstride + (long)gi * a.PW + 4 +
+                                                     4 * pc);
     }
 #pragma unroll
     for (int u = 0; u < KV_SB; ++u)
-      if (u < nb && vg < g) vv[u] = p0[(long)(s0 + u) * sstride + (long)vg * a.PW + 4 + F + dq * KV_DQ + vd];
+      vv[u] = p0[(long)min(s0 + u, S - 1) * sstride + (long)min(vg, g - 1) * a.PW + 4 + F + dq * KV_DQ + vd];
   };
-  load_batch(0, min(KV_SB, S));
-  // split heads
-  for (int i = tid; i < S * g; i += 256) {
-    const u32x4 v = gld16(p0 + (long)(i / g) * sstride + (long)(i % g) * a.PW);
-    hd[i / g][i % g][0] = __uint_as_float(v.x);
-    hd[i / g][i % g][1] = __uint_as_float(v.y);
-    hd[i / g][i % g][2] = __uint_as_float(v.z);
-  }
+  load_batch(0);
+  // all four words of hv live until here: no register of the heads' load is
+  // reused (which would wait for it) before the loads above are issued
+  asm volatile("" ::"v"(hv.x), "v"(hv.y), "v"(hv.z), "v"(hv.w));
+  __builtin_amdgcn_sched_barrier(0);   // and no use of hv is moved above them
   f32v4 hacc[PPT];
 #pragma unroll
   for (int k = 0; k < PPT; ++k) hacc[k] = f32v4{0.f, 0.f, 0.f, 0.f};
+  // common maximum per head: over the lanes of a wave with the same head
+  // (lane bits 2..5), then over the waves
+  __shared__ float red[3][4][GM];   // per wave: max, then partial L and mass
+  const int lane = tid & 63, wv = tid >> 6;
+  const float m_s = h_ok ? __uint_as_float(hv.x) : -INFINITY;
+  float mx = m_s;
+#pragma unroll
+  for (int o = GM; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if (lane < GM) red[0][wv][lane] = mx;
   __syncthreads();
-  if (tid < g) {  // common maximum, weights, 1/L and the rebuilt-token mass
-    float M = -INFINITY;
-    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, hd[sp][tid][0]);
-    float L = 0.f, mass = 0.f;
-    for (int sp = 0; sp < S; ++sp) {
-      const float m = hd[sp][tid][0];
-      const float w = m == -INFINITY ? 0.f : exp2f(m - M);
-      wt[sp][tid] = w;
-      L = fmaf(w, hd[sp][tid][1], L);
-      mass = fmaf(w, hd[sp][tid][2], mass);
-    }
+  const float M = fmaxf(fmaxf(red[0][0][hg], red[0][1][hg]), fmaxf(red[0][2][hg], red[0][3][hg]));
+  const float w_s = m_s == -INFINITY ? 0.f : exp2f(m_s - M);
+  if (hs < 64) wt[hs][hg] = w_s;
+  // L and the rebuilt-token mass: the same lane tree, then the waves in order
+  float lsum = w_s * __uint_as_float(hv.y), msum = w_s * __uint_as_float(hv.z);
+  if (!h_ok) lsum = msum = 0.f;
+#pragma unroll
+  for (int o = GM; o < 64; o <<= 1) {
+    lsum += __shfl_xor(lsum, o, 64);
+    msum += __shfl_xor(msum, o, 64);
+  }
+  if (lane < GM) {
+    red[1][wv][lane] = lsum;
+    red[2][wv][lane] = msum;
+  }
+  __syncthreads();
+  if (tid < g) {
     fin[tid][0] = M;
-    fin[tid][1] = 1.0f / L;
-    fin[tid][2] = mass;
+    fin[tid][1] = 1.0f / (((red[1][0][tid] + red[1][1][tid]) + red[1][2][tid]) + red[1][3][tid]);
+    fin[tid][2] = ((red[2][0][tid] + red[2][1][tid]) + red[2][2][tid]) + red[2][3][tid];
   }
   __syncthreads();
   float vsum = 0.f;
   for (int s0 = 0; s0 < S; s0 += KV_SB) {
     const int nb = min(KV_SB, S - s0);
-    if (s0 > 0) load_batch(s0, nb);
+    if (s0 > 0) load_batch(s0);
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
       const int pr = tid + 256 * k, gi = pr / FP;
@@ -768,19 +788,19 @@ __global__ __launch_bounds__(256) void k_combine_kv(const CombineArgs a) {
 #pragma unroll
   for (int k = 0; k < PPT; ++k) {
     const int pr = tid + 256 * k, gi = pr / FP, pc = pr % FP;
-    if (gi < GM) *reinterpret_cast<f32v4 *>(&accHm[gi][4 * pc + (4 * pc / SEG) * SPAD]) = hacc[k];
+    if (gi < GM) *reinterpret_cast<f32v4 *>(&accHm[gi][4 * pc]) = hacc[k];
   }
   __syncthreads();
   // out[gi][d] = (W2[d] . accH[gi] + b2[d] mass[gi] + accV[gi][d]) / L[gi]
   float dot[GM] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
-    const int f0 = ws * (F / 8) + 8 * i;
+    const int f0 = 8 * (8 * i + ws);
     const uint32_t wv[4] = {w2r[i].x, w2r[i].y, w2r[i].z, w2r[i].w};
 #pragma unroll
     for (int gi = 0; gi < GM; ++gi) {
-      const f32v4 h0 = *reinterpret_cast<const f32v4 *>(&accHm[gi][f0 + ws * SPAD]);
-      const f32v4 h1 = *reinterpret_cast<const f32v4 *>(&accHm[gi][f0 + ws * SPAD + 4]);
+      const f32v4 h0 = *reinterpret_cast<const f32v4 *>(&accHm[gi][f0]);
+      const f32v4 h1 = *reinterpret_cast<const f32v4 *>(&accHm[gi][f0 + 4]);
       const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
