@@ -142,6 +142,14 @@ __device__ __forceinline__ void select_partial_block(SelectSmem<DH, QG> &sm, int
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int i0 = rb * SEL_RB, nr = min(SEL_RB, r - i0);  // ranks of this block (a multiple of 16)
 
+  // the group's q values at head dim tid, the first eight heads in one batch
+  // of unconditional loads (clamped indices, values past the group unused)
+  const int grp = Hq / Hkv;
+  const TA *qb = q + (long)b * q_bstride + (long)h * grp * DH;
+  constexpr int QB = 8;
+  float qg0[QB];
+#pragma unroll
+  for (int u = 0; u < QB; ++u) qg0[u] = to_f32(qb[min(u, grp - 1) * DH + min(tid, DH - 1)]);
   // basis rows of this thread: rank group rg, head dims sl + 32 k
   const int rg = lane & 7, sl = 8 * w + (lane >> 3);
   const bool rg_ok = 8 * rg < nr;
@@ -160,14 +168,27 @@ __device__ __forceinline__ void select_partial_block(SelectSmem<DH, QG> &sm, int
     for (int m = 0; m < MB; ++m) lv[m] = gld16(L + (long)min(j_base + 16 * m + 4 * w + gq, n_c - 1) * r);
   };
   load_rows(0);
-  const int grp = Hq / Hkv;
   if (tid < DH) {
-    const TA *qb = q + (long)b * q_bstride + (long)h * grp * DH;
+    // summed in head order in float64 (each value is exact in float32); heads
+    // past the first eight are loaded eight at a time
     double sq = 0.0;
-    for (int gi = 0; gi < grp; ++gi) sq += to_f64(qb[gi * DH + tid]);
+    auto add = [&](int g0, const float (&v)[QB]) {
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        if (g0 + u < grp) sq += (double)v[u];
+        if ((qtg || qfrag) && g0 + u < QG && g0 + u < grp) qg[g0 + u][tid] = v[u];
+      }
+    };
+    add(0, qg0);
+    for (int g0 = QB; g0 < grp; g0 += QB) {
+      float v[QB];
+#pragma unroll
+      for (int u = 0; u < QB; ++u) v[u] = to_f32(qb[min(g0 + u, grp - 1) * DH + tid]);
+      add(g0, v);
+    }
     qsum[tid] = sq;
     if (qtg || qfrag)
-      for (int gi = 0; gi < QG; ++gi) qg[gi][tid] = gi < grp ? to_f32(qb[gi * DH + tid]) : 0.f;
+      for (int gi = grp; gi < QG; ++gi) qg[gi][tid] = 0.f;
   }
   __syncthreads();
   // q~_g of each query head over the block's ranks, in float32, four heads at
