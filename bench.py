@@ -61,7 +61,9 @@ def parse():
     ap.add_argument("--fit-steps", type=int, default=4)
     ap.add_argument("--no-basis", action="store_true", help="skip timing the key basis")
     ap.add_argument("--basis-iterations", type=int, default=8)
-    ap.add_argument("--no-reuse", action="store_true", help="skip timing reuse of rebuilt chunks")
+    ap.add_argument("--reuse", action="store_true",
+                    help="also time reuse of rebuilt chunks (lowram_decode_attn_reuse, off the default decode path)")
+    ap.add_argument("--no-reuse", action="store_true", help="(the default) do not time reuse")
     ap.add_argument("--reuse-rho", type=float, default=0.95, help="step-to-step query correlation for the reuse timing")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times: a kernel of known "
@@ -583,7 +585,7 @@ def main():
     repack = time_repack(P, s, d, model, cache, dev, ev)
     fit = None if args.no_fit else time_fit(P, s, dims_of(s), model, dev, ev, steps=args.fit_steps)
     basis = None if args.no_basis else time_basis(P, s, dims_of(s), dev, ev, iterations=args.basis_iterations)
-    reuse = None if args.no_reuse else time_reuse(P, s, d, model, cache, dev, rho=args.reuse_rho)
+    reuse = time_reuse(P, s, d, model, cache, dev, rho=args.reuse_rho) if args.reuse and not args.no_reuse else None
 
     # ---- CPU oracle on a bounded sample ---------------------------------------
     cpu = None

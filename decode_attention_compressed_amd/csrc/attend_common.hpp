@@ -80,6 +80,7 @@ __device__ void tail_split(const AttendArgs &a, int h, int b, const float *qs, f
     for (int idx = tid; idx < g * nt; idx += 256) {
       const int gi = idx / nt, t = idx % nt;
       float s = 0.f;
+#pragma unroll 8
       for (int d = 0; d < dh; ++d) s = fmaf(qs[gi * dh + d], ks[t * ld + d], s);
       lg[gi * TT + t] = s * a.scale_log2;
     }
@@ -89,6 +90,7 @@ __device__ void tail_split(const AttendArgs &a, int h, int b, const float *qs, f
     for (int idx = tid; idx < g * dh; idx += 256) {
       const int gi = idx / dh, d = idx % dh;
       float acc = accV[idx] * al[gi];
+#pragma unroll 8
       for (int t = 0; t < nt; ++t) acc = fmaf(lg[gi * TT + t], vs[t * ld + d], acc);
       accV[idx] = acc;
     }

@@ -11,11 +11,14 @@
 // products.  (At d_h = 128 the plain form is cheaper, which is why the chained
 // kernel keeps it there.)
 //
-// k_absorb (run with the chunk selection, before the attend kernel) forms, per
-// (sequence, kv head) of the layer, A = -log2(e) W1 U_{l,h} (rounded to fp16
-// once; int8 caches fold the per-rank scale in) and q~_g = U_{l,h}^T q_g for
-// the g query heads (fp32, split into an fp16 part and the fp16 rounding of
-// the remainder).
+// k_select_absorb (the launch of the partial chunk scores, before the attend
+// kernel) also forms, per (sequence, kv head) of the layer,
+// A = -log2(e) W1 U_{l,h} (rounded to fp16 once; int8 caches fold the per-rank
+// scale in) and q~_g = U_{l,h}^T q_g for the g query heads (fp32, split into
+// an fp16 part and the fp16 rounding of the remainder).
+//
+// The attend kernel ranks the chunk scores itself in its prologue (wave 0,
+// while the other waves stage A).
 //
 // k_attend_absorb: one workgroup of 4 waves (one per SIMD) per (sequence b,
 // kv head h, split s, quarter q of F).  Its quarter of A (128 hidden units x r,

@@ -124,9 +124,27 @@ __global__ __launch_bounds__(TK_NT) void k_topk_small(const double *__restrict__
   }
 }
 
+// st(i, ld(i)) for i = threadIdx.x, + 256, ... < n, with eight of a thread's
+// loads in flight at a time (ld is called on indices clamped into [0, n)).
+template <typename Ld, typename St>
+__device__ __forceinline__ void batched_copy(int n, Ld ld, St st) {
+  constexpr int NB = 8;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 256 * NB) {
+    float v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) v[u] = ld(min(i0 + 256 * u, n - 1));
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (i0 + 256 * u < n) st(i0 + 256 * u, v[u]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // D4-D6 on the vector ALUs.  grid (n_split + 1, Hkv, B), 256 threads; the last
-// split of each (b, h) is the tail.  TT tokens per tile.
+// split of each (b, h) is the tail.  TT tokens per tile.  Global reads are
+// issued several at a time (staging, coefficient tiles, residual rows), and
+// the inner products are unrolled so that their LDS reads are in flight
+// together (each still sums in index order).
 // ---------------------------------------------------------------------------
 template <typename TA, typename TC, typename TR, bool STAGE>
 __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT) {  // STAGE: U and W1 in LDS
@@ -172,8 +190,10 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
   // Rows are padded by one word: neighbouring threads read neighbouring rows.
   float *Ul = hb + TT * F, *W1l = Ul + dh * (r + 1);
   if (STAGE) {
-    for (int i = tid; i < dh * r; i += 256) Ul[(i / r) * (r + 1) + i % r] = ldf(U, i);
-    for (int i = tid; i < F * dh; i += 256) W1l[(i / dh) * (dh + 1) + i % dh] = ldf(W1, i);
+    batched_copy(dh * r, [&](int i) { return ldf(U, i); },
+                 [&](int i, float v) { Ul[(i / r) * (r + 1) + i % r] = v; });
+    batched_copy(F * dh, [&](int i) { return ldf(W1, i); },
+                 [&](int i, float v) { W1l[(i / dh) * (dh + 1) + i % dh] = v; });
     __syncthreads();
   }
 
@@ -184,16 +204,15 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
     for (int t0 = 0; t0 < C; t0 += TT) {
       const int nt = min(TT, C - t0);
       const long row0 = (long)j * C + t0;
-      for (int idx = tid; idx < nt * r; idx += 256) {
-        const int t = idx / r, i = idx % r;
-        cb[idx] = ld_coeff(cf, (row0 + t) * r + i, csc, i);
-      }
+      batched_copy(nt * r, [&](int idx) { return ld_coeff(cf, row0 * r + idx, csc, idx % r); },
+                   [&](int idx, float v) { cb[idx] = v; });
       __syncthreads();
       for (int idx = tid; idx < nt * dh; idx += 256) {
         const int t = idx / dh, d = idx % dh;
         const TA *ur = U + (long)d * r;
         const float *ul = Ul + d * (r + 1);
         float s = 0.f;
+#pragma unroll 8
         for (int i = 0; i < r; ++i) s = fmaf(STAGE ? ul[i] : ldf(ur, i), cb[t * r + i], s);
         kh[idx] = s;
       }
@@ -201,6 +220,7 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
       for (int idx = tid; idx < g * nt; idx += 256) {
         const int gi = idx / nt, t = idx % nt;
         float s = 0.f;
+#pragma unroll 8
         for (int d = 0; d < dh; ++d) s = fmaf(qs[gi * dh + d], kh[t * dh + d], s);
         lg[gi * TT + t] = s * a.scale_log2;
       }
@@ -209,6 +229,7 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
         const TA *wr = W1 + (long)f * dh;
         const float *wl = W1l + f * (dh + 1);
         float s = ldf(B1, f);
+#pragma unroll 8
         for (int d = 0; d < dh; ++d) s = fmaf(STAGE ? wl[d] : ldf(wr, d), kh[t * dh + d], s);
         hb[idx] = silu_f(s);
       }
@@ -218,16 +239,25 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
       for (int idx = tid; idx < g * F; idx += 256) {
         const int gi = idx / F, f = idx % F;
         float acc = accH[idx] * al[gi];
+#pragma unroll 8
         for (int t = 0; t < nt; ++t) acc = fmaf(lg[gi * TT + t], hb[t * F + f], acc);
         accH[idx] = acc;
       }
       for (int idx = tid; idx < g * dh; idx += 256) {
         const int gi = idx / dh, d = idx % dh;
         float acc = accV[idx] * al[gi];
-        for (int e = e0; e < e1; ++e) {
-          const int t = ridx[e] - (int)row0;
-          if (t >= 0 && t < nt)
-            acc = fmaf(lg[gi * TT + t], ld_coeff(rval, (long)e * dh + d, rsc, d), acc);
+        for (int eb = e0; eb < e1; eb += 8) {  // eight rows' loads in flight, added in order
+          int tr[8];
+          float rv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int e = min(eb + u, e1 - 1);
+            tr[u] = ridx[e] - (int)row0;
+            rv[u] = ld_coeff(rval, (long)e * dh + d, rsc, d);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (eb + u < e1 && tr[u] >= 0 && tr[u] < nt) acc = fmaf(lg[gi * TT + tr[u]], rv[u], acc);
         }
         accV[idx] = acc;
       }
