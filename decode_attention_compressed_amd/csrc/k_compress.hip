@@ -31,6 +31,18 @@ __device__ __forceinline__ void st_round(float *p, double x) { *p = (float)x; }
 __device__ __forceinline__ void st_round(bf16 *p, double x) { p->u = f64_to_bf16_bits(x); }
 __device__ __forceinline__ void st_round(double *p, double x) { *p = x; }
 
+// st(i, ld(i)) for i = threadIdx.x + 256 u, u < NPT (n = 256 NPT items): all of
+// a thread's loads are issued before the first store, so a slab costs one
+// memory round trip.
+template <int NPT, typename Ld, typename St>
+__device__ __forceinline__ void stage_slab(Ld ld, St st) {
+  double v[NPT];
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) v[u] = ld((int)threadIdx.x + 256 * u);
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) st((int)threadIdx.x + 256 * u, v[u]);
+}
+
 // ---------------------------------------------------------------------------
 // C1: out[b][o0 + t][i] = sum_kk K(b, t, kk) U[b][kk][i] for t < N, float64
 // accumulate.  K(b, t, kk) = k[b][l][h][t][d] with kk = (l*Hkv + h)*dh + d and
@@ -56,15 +68,29 @@ __global__ __launch_bounds__(256) void k_project(const TA *__restrict__ k, const
   const TA *Ub = U + (long)b * D * r;
   double acc[4][4] = {};
   for (int k0 = kbeg; k0 < kend; k0 += 16) {
-    for (int idx = tid; idx < 16 * 64; idx += 256) {
-      const int kk = idx % 16, t = idx / 16;  // consecutive threads walk d (contiguous)
-      const int gk = k0 + kk, tt = t0 + t;
-      As[kk][t] = (tt < N && gk < kend) ? ldd(kb, (long)(gk / dh) * Nk * dh + (long)tt * dh + gk % dh) : 0.0;
+    // both slabs' loads in flight together: indices clamped into range, the
+    // values outside it zeroed when stored
+    double av0[4], bv0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + 256 * u, kk = idx % 16, t = idx / 16;  // consecutive threads walk d
+      const int gk = min(k0 + kk, kend - 1), tt = min(t0 + t, N - 1);
+      av0[u] = ldd(kb, (long)(gk / dh) * Nk * dh + (long)tt * dh + gk % dh);
     }
-    for (int idx = tid; idx < 16 * 64; idx += 256) {
-      const int kk = idx / 64, i = idx % 64;
-      const int gk = k0 + kk, ii = i0 + i;
-      Bs[kk][i] = (gk < kend && ii < r) ? ldd(Ub, (long)gk * r + ii) : 0.0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + 256 * u, kk = idx / 64, i = idx % 64;
+      bv0[u] = ldd(Ub, (long)min(k0 + kk, kend - 1) * r + min(i0 + i, r - 1));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + 256 * u, kk = idx % 16, t = idx / 16;
+      As[kk][t] = (t0 + t < N && k0 + kk < kend) ? av0[u] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + 256 * u, kk = idx / 64, i = idx % 64;
+      Bs[kk][i] = (k0 + kk < kend && i0 + i < r) ? bv0[u] : 0.0;
     }
     __syncthreads();
 #pragma unroll
@@ -222,15 +248,30 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
 
   // GEMM1: k_hat[TM][DH] = deq(c)[TM][r] . U_{l,h}^T
   double acc[NA][NC] = {};
+  static_assert(16 * TM % 256 == 0 && 16 * DH % 256 == 0, "whole slabs per thread");
   for (int k0 = 0; k0 < r; k0 += 16) {
-    for (int idx = tid; idx < 16 * TM; idx += 256) {
-      const int kk = idx % 16, m = idx / 16;
-      const int t = tok[m];
-      As[kk * TM + m] = t >= 0 ? ld_cdeq(cb, (long)t * r + k0 + kk, sc, k0 + kk) : 0.0;
+    // both slabs' loads in flight together (rows of absent tokens read token 0
+    // and are zeroed)
+    double av0[16 * TM / 256], bv0[16 * DH / 256];
+#pragma unroll
+    for (int u = 0; u < 16 * TM / 256; ++u) {
+      const int idx = tid + 256 * u, kk = idx % 16, t = tok[idx / 16];
+      av0[u] = ld_cdeq(cb, (long)max(t, 0) * r + k0 + kk, sc, k0 + kk);
     }
-    for (int idx = tid; idx < 16 * DH; idx += 256) {
-      const int kk = idx % 16, d = idx / 16;
-      Bs[kk * DH + d] = ldd(Ul, (long)d * r + k0 + kk);
+#pragma unroll
+    for (int u = 0; u < 16 * DH / 256; ++u) {
+      const int idx = tid + 256 * u, kk = idx % 16, d = idx / 16;
+      bv0[u] = ldd(Ul, (long)d * r + k0 + kk);
+    }
+#pragma unroll
+    for (int u = 0; u < 16 * TM / 256; ++u) {
+      const int idx = tid + 256 * u, kk = idx % 16, m = idx / 16;
+      As[kk * TM + m] = tok[m] >= 0 ? av0[u] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 16 * DH / 256; ++u) {
+      const int idx = tid + 256 * u;
+      Bs[(idx % 16) * DH + idx / 16] = bv0[u];
     }
     __syncthreads();
 #pragma unroll 4
@@ -258,10 +299,8 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
   for (int f0 = 0; f0 < F; f0 += 64) {
     double hacc[NA][4] = {};
     for (int k0 = 0; k0 < DH; k0 += 16) {
-      for (int idx = tid; idx < 16 * 64; idx += 256) {
-        const int kk = idx % 16, f = idx / 16;
-        Bs[kk * 64 + f] = ldd(W1, (long)(f0 + f) * DH + k0 + kk);
-      }
+      stage_slab<16 * 64 / 256>([&](int idx) { return ldd(W1, (long)(f0 + idx / 16) * DH + k0 + idx % 16); },
+                                [&](int idx, double x) { Bs[(idx % 16) * 64 + idx / 16] = x; });
       __syncthreads();
 #pragma unroll 4
       for (int kk = 0; kk < 16; ++kk) {
@@ -286,10 +325,8 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
       }
     __syncthreads();
     for (int k0 = 0; k0 < 64; k0 += 16) {
-      for (int idx = tid; idx < 16 * DH; idx += 256) {
-        const int kk = idx % 16, d = idx / 16;
-        Bs[kk * DH + d] = ldd(W2, (long)d * F + f0 + k0 + kk);
-      }
+      stage_slab<16 * DH / 256>([&](int idx) { return ldd(W2, (long)(idx / 16) * F + f0 + k0 + idx % 16); },
+                                [&](int idx, double x) { Bs[(idx % 16) * DH + idx / 16] = x; });
       __syncthreads();
 #pragma unroll 4
       for (int kk = 0; kk < 16; ++kk) {
