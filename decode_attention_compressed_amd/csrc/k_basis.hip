@@ -73,7 +73,13 @@ struct EpPut {  // X[b][i][j] = c
   __device__ void operator()(int b, int i, int j, float c) const { x[b * zs + (long)i * ld + j] = c; }
 };
 
-// Counter-hash uniform in [-1, 1) for (b, row, column, salt).
+// Counter-hash uniform in [-1, 1) for (b, row, column, salt).  The four
+// counters are combined with multiplicative-hashing constants (the 32-bit
+// golden-ratio constant 0x9E3779B1, the low word of the 64-bit golden gamma
+// 0x9E3779B97F4A7C15, and the 32-bit primes of the xxHash32 specification),
+// then mixed by the published "lowbias32" finaliser (Chris Wellons'
+// hash-prospector: xorshift 16, multiply, xorshift 15, multiply, xorshift 16).
+// The top 24 bits give the uniform value.
 __device__ __forceinline__ float hash_uniform(uint32_t b, uint32_t row, uint32_t col, uint32_t salt) {
   uint32_t x = b * 0x9E3779B1u ^ (row + 0x7F4A7C15u) * 0x85EBCA77u ^ (col + salt * 0x165667B1u) * 0xC2B2AE3Du;
   x ^= x >> 16; x *= 0x7FEB352Du;
