@@ -31,18 +31,6 @@ __device__ __forceinline__ void st_round(float *p, double x) { *p = (float)x; }
 __device__ __forceinline__ void st_round(bf16 *p, double x) { p->u = f64_to_bf16_bits(x); }
 __device__ __forceinline__ void st_round(double *p, double x) { *p = x; }
 
-// st(i, ld(i)) for i = threadIdx.x + 256 u, u < NPT (n = 256 NPT items): all of
-// a thread's loads are issued before the first store, so a slab costs one
-// memory round trip.
-template <int NPT, typename Ld, typename St>
-__device__ __forceinline__ void stage_slab(Ld ld, St st) {
-  double v[NPT];
-#pragma unroll
-  for (int u = 0; u < NPT; ++u) v[u] = ld((int)threadIdx.x + 256 * u);
-#pragma unroll
-  for (int u = 0; u < NPT; ++u) st((int)threadIdx.x + 256 * u, v[u]);
-}
-
 // ---------------------------------------------------------------------------
 // C1: out[b][o0 + t][i] = sum_kk K(b, t, kk) U[b][kk][i] for t < N, float64
 // accumulate.  K(b, t, kk) = k[b][l][h][t][d] with kk = (l*Hkv + h)*dh + d and
@@ -203,7 +191,10 @@ __global__ __launch_bounds__(256) void k_landmark(const TC *__restrict__ coeff,
 // Token t reads coefficient row c0 + t of a cache with Nc rows per sequence and
 // value row t of v[b][l][h] (Nv rows per (b, l, h)); err has N entries per
 // (b, l, h).
-// grid (ceil(rows/TM), G*Hkv, B), 256 threads (16 x 16).
+// grid (ceil(rows/TM), G*Hkv, B), 256 threads (16 x 16).  One workgroup fills a
+// CU's LDS, so no other workgroup hides its load latency: every 16-wide slab
+// of the three products is loaded into registers while the previous slab's
+// products run, and stored to LDS after them.
 // ---------------------------------------------------------------------------
 template <int DH, int TM, int MODE, typename TA, typename TC, typename TD>
 __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
@@ -249,10 +240,11 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
   // GEMM1: k_hat[TM][DH] = deq(c)[TM][r] . U_{l,h}^T
   double acc[NA][NC] = {};
   static_assert(16 * TM % 256 == 0 && 16 * DH % 256 == 0, "whole slabs per thread");
-  for (int k0 = 0; k0 < r; k0 += 16) {
-    // both slabs' loads in flight together (rows of absent tokens read token 0
-    // and are zeroed)
-    double av0[16 * TM / 256], bv0[16 * DH / 256];
+  // slab registers: both slabs' loads in flight together, the next slab's
+  // issued before the current one's products (rows of absent tokens read
+  // token 0 and are zeroed when stored)
+  double av0[16 * TM / 256], bv0[16 * DH / 256];
+  auto load_slab = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < 16 * TM / 256; ++u) {
       const int idx = tid + 256 * u, kk = idx % 16, t = tok[idx / 16];
@@ -263,6 +255,9 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
       const int idx = tid + 256 * u, kk = idx % 16, d = idx / 16;
       bv0[u] = ldd(Ul, (long)d * r + k0 + kk);
     }
+  };
+  load_slab(0);
+  for (int k0 = 0; k0 < r; k0 += 16) {
 #pragma unroll
     for (int u = 0; u < 16 * TM / 256; ++u) {
       const int idx = tid + 256 * u, kk = idx % 16, m = idx / 16;
@@ -274,6 +269,7 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
       Bs[(idx % 16) * DH + idx / 16] = bv0[u];
     }
     __syncthreads();
+    if (k0 + 16 < r) load_slab(k0 + 16);
 #pragma unroll 4
     for (int kk = 0; kk < 16; ++kk) {
       double av[NA], bv[NC];
@@ -298,10 +294,24 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
   double vacc[NA][NC] = {};
   for (int f0 = 0; f0 < F; f0 += 64) {
     double hacc[NA][4] = {};
+    // W1 slabs: the next one's loads in flight during the current products
+    double wv0[16 * 64 / 256];
+    auto load_w1 = [&](int k0) {
+#pragma unroll
+      for (int u = 0; u < 16 * 64 / 256; ++u) {
+        const int idx = tid + 256 * u;
+        wv0[u] = ldd(W1, (long)(f0 + idx / 16) * DH + k0 + idx % 16);
+      }
+    };
+    load_w1(0);
     for (int k0 = 0; k0 < DH; k0 += 16) {
-      stage_slab<16 * 64 / 256>([&](int idx) { return ldd(W1, (long)(f0 + idx / 16) * DH + k0 + idx % 16); },
-                                [&](int idx, double x) { Bs[(idx % 16) * 64 + idx / 16] = x; });
+#pragma unroll
+      for (int u = 0; u < 16 * 64 / 256; ++u) {
+        const int idx = tid + 256 * u;
+        Bs[(idx % 16) * 64 + idx / 16] = wv0[u];
+      }
       __syncthreads();
+      if (k0 + 16 < DH) load_w1(k0 + 16);
 #pragma unroll 4
       for (int kk = 0; kk < 16; ++kk) {
         double av[NA], bv[4];
@@ -324,10 +334,24 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
         Hs[(ty + 16 * a) * HS + tx + 16 * c] = x / (1.0 + exp(-x));
       }
     __syncthreads();
+    // W2 slabs of this hidden block, prefetched like W1's
+    double w2v0[16 * DH / 256];
+    auto load_w2 = [&](int k0) {
+#pragma unroll
+      for (int u = 0; u < 16 * DH / 256; ++u) {
+        const int idx = tid + 256 * u;
+        w2v0[u] = ldd(W2, (long)(idx / 16) * F + f0 + k0 + idx % 16);
+      }
+    };
+    load_w2(0);
     for (int k0 = 0; k0 < 64; k0 += 16) {
-      stage_slab<16 * DH / 256>([&](int idx) { return ldd(W2, (long)(idx / 16) * F + f0 + k0 + idx % 16); },
-                                [&](int idx, double x) { Bs[(idx % 16) * DH + idx / 16] = x; });
+#pragma unroll
+      for (int u = 0; u < 16 * DH / 256; ++u) {
+        const int idx = tid + 256 * u;
+        Bs[(idx % 16) * DH + idx / 16] = w2v0[u];
+      }
       __syncthreads();
+      if (k0 + 16 < 64) load_w2(k0 + 16);
 #pragma unroll 4
       for (int kk = 0; kk < 16; ++kk) {
         double av[NA], bv[NC];
