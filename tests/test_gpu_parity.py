@@ -257,6 +257,11 @@ def _roundtrip(s, top_k, edit=None):
     ("chain-nc-512", small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=65536, T=16), 9),
     # above 512 chunks the chained kernel reads the selection of the separate top-k
     ("chain-nc-1024", small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=131072, T=16), 9),
+    # the absorbed kernel (head dim 256): 6 score blocks in its shared launch
+    # (padded to 8 idle-ended workgroups before the A tiles), and above 256
+    # chunks, where it reads the selection of the separate top-k
+    ("absorb-sel-pad", small(QWEN4B_64K, B=1, Hq=4, Hkv=1, N=2048, T=16), 3),
+    ("absorb-nc-320", small(QWEN4B_64K, B=1, Hq=4, Hkv=1, N=81920, T=16), 5),
     # peaked softmax: keys of norm ~100 and queries x16 give logits in the
     # hundreds, on each attend kernel (chained bf16 and int8, absorbed at head
     # dim 256, per-chunk matrix-core at g = 8, vector).  The value model's first
@@ -274,6 +279,8 @@ def test_special_shapes(name, shape, top_k):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     print(f"\n[case] {name}: {shape}", flush=True)
+    if name.startswith("absorb"):
+        assert P().decode_kernel(dims_of(shape, top_k=top_k)) == "absorb"
     out, sel, ref, rsel, host, inp = _roundtrip(shape, top_k)
     assert np.array_equal(sel, rsel)
     ok, worst = within_tol(out, ref)
