@@ -262,6 +262,8 @@ def _roundtrip(s, top_k, edit=None):
     # chunks, where it reads the selection of the separate top-k
     ("absorb-sel-pad", small(QWEN4B_64K, B=1, Hq=4, Hkv=1, N=2048, T=16), 3),
     ("absorb-nc-320", small(QWEN4B_64K, B=1, Hq=4, Hkv=1, N=81920, T=16), 5),
+    # int8 codes on the absorbed path: the rank scales folded into A and q~
+    ("absorb-int8", small(QWEN4B_64K, B=1, N=2048, T=40, coeff=I8, resid=I8), 4),
     # peaked softmax: keys of norm ~100 and queries x16 give logits in the
     # hundreds, on each attend kernel (chained bf16 and int8, absorbed at head
     # dim 256, per-chunk matrix-core at g = 8, vector).  The value model's first
