@@ -264,6 +264,9 @@ def _roundtrip(s, top_k, edit=None):
     ("absorb-nc-320", small(QWEN4B_64K, B=1, Hq=4, Hkv=1, N=81920, T=16), 5),
     # int8 codes on the absorbed path: the rank scales folded into A and q~
     ("absorb-int8", small(QWEN4B_64K, B=1, N=2048, T=40, coeff=I8, resid=I8), 4),
+    # its other compiled rank (r = 512), and two query heads per kv head
+    ("absorb-r512", small(QWEN4B_64K, B=1, N=2048, T=24, r=512), 3),
+    ("absorb-g2", small(QWEN4B_64K, B=2, Hq=8, N=2048, T=24), 3),
     # peaked softmax: keys of norm ~100 and queries x16 give logits in the
     # hundreds, on each attend kernel (chained bf16 and int8, absorbed at head
     # dim 256, per-chunk matrix-core at g = 8, vector).  The value model's first
