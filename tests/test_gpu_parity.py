@@ -253,6 +253,10 @@ def _roundtrip(s, top_k, edit=None):
     # splits get one token, three get none), and one split with a ragged 70-token tail
     ("mfma-tail-2-of-5", small(QWEN4B_64K, B=1, N=2048, T=2), 5),
     ("mfma-tail-70-k1", small(QWEN4B_64K, B=1, N=1024, T=70), 1),
+    # the chained kernel's other compiled (rank, hidden width, codes)
+    ("chain-r256", small(LLAMA8B_32K, B=1, N=2048, r=256, T=16), 4),
+    ("chain-f128", small(LLAMA8B_32K, B=1, N=2048, F=128, T=16), 4),
+    ("chain-int8-r512", small(COMPOSED_128K, B=1, N=2048, evict_keep=1.0, n_obs=0, r=512, T=16), 4),
     ("chain-nc-320", small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=40960, T=16), 9),
     ("chain-nc-512", small(LLAMA8B_32K, B=1, Hq=8, Hkv=2, N=65536, T=16), 9),
     # above 512 chunks the chained kernel reads the selection of the separate top-k
@@ -284,8 +288,8 @@ def test_special_shapes(name, shape, top_k):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     print(f"\n[case] {name}: {shape}", flush=True)
-    if name.startswith("absorb"):
-        assert P().decode_kernel(dims_of(shape, top_k=top_k)) == "absorb"
+    if name.startswith("absorb") or name.startswith("chain"):
+        assert P().decode_kernel(dims_of(shape, top_k=top_k)) == name.split("-")[0]
     out, sel, ref, rsel, host, inp = _roundtrip(shape, top_k)
     assert np.array_equal(sel, rsel)
     ok, worst = within_tol(out, ref)
