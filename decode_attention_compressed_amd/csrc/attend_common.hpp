@@ -98,6 +98,31 @@ __device__ void tail_split(const AttendArgs &a, int h, int b, const float *qs, f
   }
 }
 
+// Eight int8 codes (two dwords, lowest byte first) as fp16, exactly.  Each
+// code x is biased to the byte u = x + 128 (a sign-bit flip) and placed as
+// the low mantissa byte of the fp16 word 0x64uu, which is the value 1024 + u
+// (fp16 has unit spacing in [1024, 2048)); subtracting 1152 leaves x.  One
+// byte permute and one packed fp16 subtraction per pair of codes.
+typedef _Float16 attend_h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 attend_f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+__device__ __forceinline__ attend_f16x8 i8x8_to_f16x8(uint32_t lo, uint32_t hi) {
+  const uint32_t w[2] = {lo ^ 0x80808080u, hi ^ 0x80808080u};
+  const attend_h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  attend_f16x8 o;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    // bytes (u_2i, 0x64, u_2i+1, 0x64): selector bytes 0-3 take the second
+    // operand's bytes, 4 the first operand's byte 0
+    const attend_h2 a = __builtin_bit_cast(attend_h2, __builtin_amdgcn_perm(0x64646464u, w[j], 0x04010400u)) - bias;
+    const attend_h2 b = __builtin_bit_cast(attend_h2, __builtin_amdgcn_perm(0x64646464u, w[j], 0x04030402u)) - bias;
+    o[4 * j] = a.x;
+    o[4 * j + 1] = a.y;
+    o[4 * j + 2] = b.x;
+    o[4 * j + 3] = b.y;
+  }
+  return o;
+}
+
 // ---------------------------------------------------------------------------
 // Top-k chunk selection by one wave: the k chunks of [0, n_c) with the largest
 // fp64 score in scL (LDS, NSL * 64 entries readable; those past n_c are

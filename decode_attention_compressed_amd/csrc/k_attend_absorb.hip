@@ -153,13 +153,7 @@ template <> struct Coef<int8_t> {
     const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
     return make_uint2(v.x, v.y);
   }
-  __device__ static f16x8 get(raw v) {  // |code| <= 127 is exact in fp16
-    const int8_t *b = reinterpret_cast<const int8_t *>(&v);
-    f16x8 o;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (_Float16)(float)b[i];
-    return o;
-  }
+  __device__ static f16x8 get(raw v) { return i8x8_to_f16x8(v.x, v.y); }  // |code| <= 127: exact
 };
 // head dim d of residual row e as stored (int8 codes: before their scale)
 template <typename TR> struct ResRow;
