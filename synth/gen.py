@@ -32,6 +32,10 @@ values, evaluated on the exact keys before storage.
 """
 from __future__ import annotations
 
+import concurrent.futures
+import contextlib
+import os
+
 import numpy as np
 
 from .configs import BF16, F16, F32, F64, Shape
@@ -40,17 +44,24 @@ SEED_ROOT = 20261106
 STREAM_K, STREAM_FRAME, STREAM_MLP, STREAM_NOISE, STREAM_OUTLIER, STREAM_Q, STREAM_OBS, STREAM_QCORR = range(8)
 
 
-def _rng(cfg_id: int, b: int, stream: int) -> np.random.Generator:
-    return np.random.default_rng(np.random.SeedSequence([SEED_ROOT, cfg_id, b, stream]))
+def _rng(cfg_id: int, b: int, stream: int, *sub: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([SEED_ROOT, cfg_id, b, stream, *sub]))
 
 
 # ----------------------------------------------------------------------------
 # storage casts (round to nearest even)
 # ----------------------------------------------------------------------------
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    """Round to nearest even.  For finite x the 32-bit sum cannot wrap
+    (|bits| <= 0x7F7FFFFF plus the sign bit, plus at most 0x8000); NaNs are
+    stored as the quiet NaN 0x7FC0."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(f)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
 
 
 def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
@@ -91,6 +102,21 @@ def spectrum(D: int) -> np.ndarray:
     return c * 0.9 ** np.arange(D)
 
 
+@contextlib.contextmanager
+def _one_blas_thread(on: bool):
+    """BLAS limited to one thread while several Python threads call it."""
+    if not on:
+        yield
+        return
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        yield
+        return
+    with threadpool_limits(limits=1, user_api="blas"):
+        yield
+
+
 def _mlp_true(x, w1, b1, w2, b2):
     pre = x @ w1.T + b1
     h = pre / (1.0 + np.exp(-pre))
@@ -98,9 +124,10 @@ def _mlp_true(x, w1, b1, w2, b2):
 
 
 def make(s: Shape, seed_offset: int = 0, steps: int | None = None, noise_scale: float = 0.1,
-         with_dense: bool = False, progress=None) -> dict:
+         with_dense: bool = False, progress=None, workers: int = 0) -> dict:
     """Draw one workload.  Returns stored arrays keyed by name.  `progress`,
-    if given, is called as progress(done, B) after each sequence.
+    if given, is called as progress(done, B) after each sequence.  `workers`
+    caps the threads that draw concurrently (0: one per CPU, at most 16).
 
     Layouts (row-major):
       k, v            [B][G][Hkv][N][dh]
@@ -132,7 +159,9 @@ def make(s: Shape, seed_offset: int = 0, steps: int | None = None, noise_scale: 
         "b2": np.empty((B, G, Hkv, dh), dtype=_np_dtype(act)),
         "outliers": np.zeros((B, n_out), dtype=np.int64),
     }
-    for b in range(B):
+    def keys_of(b: int):
+        """Keys, basis and predictor of sequence b; returns the exact keys
+        [G][Hkv][N + T][dh] and the stored predictor for the value draws."""
         frame = haar_frame(_rng(cid, b, STREAM_FRAME), D, max(m, r))
         z = _rng(cid, b, STREAM_K).standard_normal((N + T, m)).astype(work)
         kcat = (z * sig.astype(work)[None, :]) @ frame[:, :m].T.astype(work)
@@ -148,25 +177,44 @@ def make(s: Shape, seed_offset: int = 0, steps: int | None = None, noise_scale: 
         w2 = store(mrng.standard_normal((G, Hkv, dh, F)) / np.sqrt(F), act)
         b2 = store(0.1 * mrng.standard_normal((G, Hkv, dh)), act)
         out["w1"][b], out["b1"][b], out["w2"][b], out["b2"][b] = w1, b1, w2, b2
-
-        nrng = _rng(cid, b, STREAM_NOISE)
         if n_out:
-            outl = np.sort(_rng(cid, b, STREAM_OUTLIER).choice(N, size=n_out, replace=False))
-            out["outliers"][b] = outl
-        for l in range(G):
-            for h in range(Hkv):
-                W1, B1 = load(w1[l, h], act).astype(work), load(b1[l, h], act).astype(work)
-                W2, B2 = load(w2[l, h], act).astype(work), load(b2[l, h], act).astype(work)
-                vals = _mlp_true(kfull[l, h], W1, B1, W2, B2)
-                noise = noise_scale * nrng.standard_t(3, size=(N + T, dh))
-                if n_out:
-                    noise[outl] *= 20.0
-                vals = vals + noise.astype(work)
-                out["v"][b, l, h] = store(vals[:N], act)
-                out["v_tail"][b, l, h] = store(vals[N:], act)
-        del kcat, kfull
-        if progress is not None:
-            progress(b + 1, B)
+            out["outliers"][b] = np.sort(_rng(cid, b, STREAM_OUTLIER).choice(N, size=n_out, replace=False))
+        return kfull
+
+    def values_of(b: int, l: int, h: int, kfull) -> None:
+        """Values of (sequence b, layer l, kv head h): the value model on the
+        exact keys plus heavy-tailed noise from a generator of their own."""
+        W1, B1 = load(out["w1"][b, l, h], act).astype(work), load(out["b1"][b, l, h], act).astype(work)
+        W2, B2 = load(out["w2"][b, l, h], act).astype(work), load(out["b2"][b, l, h], act).astype(work)
+        vals = _mlp_true(kfull[l, h], W1, B1, W2, B2)
+        noise = noise_scale * _rng(cid, b, STREAM_NOISE, l, h).standard_t(3, size=(N + T, dh))
+        if n_out:
+            noise[out["outliers"][b]] *= 20.0
+        vals = vals + noise.astype(work)
+        out["v"][b, l, h] = store(vals[:N], act)
+        out["v_tail"][b, l, h] = store(vals[N:], act)
+
+    # Every array comes from generators seeded by (workload, sequence, stream)
+    # and, for the value noise, (layer, kv head), so the draws can run in any
+    # order or concurrently with the same result.  The keys of a group of
+    # sequences are drawn one sequence at a time (their products use every
+    # BLAS thread); the values of the group's (sequence, layer, head) items
+    # then run on threads with single-threaded BLAS (numpy releases the GIL in
+    # its generators, products and elementwise loops).  Grouping bounds the
+    # exact keys held in memory.
+    n_thr = max(1, min(workers if workers else (os.cpu_count() or 1), 16))
+    if B * N * G * Hkv * dh < (1 << 24):
+        n_thr = 1
+    with concurrent.futures.ThreadPoolExecutor(max_workers=n_thr) as ex:
+        for b0 in range(0, B, n_thr):
+            bs = list(range(b0, min(B, b0 + n_thr)))
+            keys = {b: keys_of(b) for b in bs}
+            items = [(b, l, h) for b in bs for l in range(G) for h in range(Hkv)]
+            with _one_blas_thread(n_thr > 1):
+                list(ex.map(lambda it: values_of(*it, keys[it[0]]), items))
+            del keys
+            if progress is not None:
+                progress(bs[-1] + 1, B)
 
     out["q"] = make_queries(s, steps, seed_offset)
     if s.n_obs:
