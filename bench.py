@@ -11,8 +11,12 @@ Prints one JSON line: seq-steps/s, the roofline of the rebuild-and-attend
 kernel (HIP events on its stream), the dense bf16 comparator on the same
 queries (x vs dense), and the CPU oracle on a bounded sample.  After the
 decode step it also times, outside the headline: the tail re-pack, the
-predictor fit, the key basis, and reuse of rebuilt chunks on correlated
-queries (--no-fit / --no-basis / --no-reuse skip the last three).
+predictor fit, the key basis, and (with --reuse) reuse of rebuilt chunks on
+correlated queries; then the other workloads of the method's configurations
+(tiny fp32, Mistral-7B-shaped at B = 16 and 64, Qwen-4B-shaped d_h = 256, and
+the composed int8 + eviction case), each with its step time, attend kernel,
+dense comparator and compression ratio under "other_workloads" (--configs
+none skips them).
 """
 from __future__ import annotations
 
@@ -36,6 +40,10 @@ CSRC = os.path.join(ROOT, "decode_attention_compressed_amd", "csrc")
 # the source file of each attend kernel (its code hash keys the stored counters)
 ATTEND_SRC = {"chain": "k_attend_chain.hip", "absorb": "k_attend_absorb.hip", "mfma": "k_attend_mfma.hip",
               "valu": "k_decode.hip"}
+
+
+# the other workloads of the method's configurations, timed after the headline
+DEFAULT_CONFIGS = "tiny-fp32,mistral7b-16k:16,mistral7b-16k:64,qwen4b-64k,composed-int8-evict-128k"
 
 
 def traffic_file(workload):
@@ -68,6 +76,10 @@ def parse():
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times: a kernel of known "
                          "traffic that scales hardware byte counters")
+    ap.add_argument("--configs", default=DEFAULT_CONFIGS,
+                    help="comma-separated workload[:batch] list timed after the headline ('none' skips): "
+                         "each gets its step time, attend kernel, dense comparator and compression ratio")
+    ap.add_argument("--config-steps", type=int, default=16, help="timed steps per other workload")
     ap.add_argument("--bw-probe", action="store_true",
                     help="only report the HBM bandwidth torch's own reduction and copy kernels reach "
                          "on 2 GiB (what a plain streaming kernel attains on this GPU), then exit")
@@ -366,141 +378,147 @@ def cpu_baseline(s, host, inp, budget_s):
     return out
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards over "
-              "sequences with no exchange, so N GPUs run N independent copies).", file=sys.stderr)
-        sys.exit(2)
-    if args.bw_probe:
-        bw_probe()
-        return
-    import torch
+class Workload:
+    """One workload on the GPU: inputs drawn and uploaded, the cache compressed
+    (and evicted where the workload evicts), and pre-marshalled decode calls for
+    n_q query sets."""
 
-    import decode_attention_compressed_amd as P
-    from synth import gen
-    from synth.configs import BY_NAME
-    from tests.harness import cache_to_host, dims_of, model_of, to_dev, to_host, upload
+    def __init__(self, P, s, n_q, quiet=False):
+        import torch
+        from synth import gen
+        from tests.harness import dims_of, model_of, to_dev, upload
+        from decode_attention_compressed_amd.api import TORCH_DT
 
-    s = BY_NAME[args.workload]
-    if args.batch:
-        s = s.replace(B=args.batch)
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev_name = torch.cuda.get_device_name(0)
-    log(f"workload {s.name}: {s}")
-    t0 = time.perf_counter()
-    n_q = min(64, max(args.steps, 1))
-    def gen_progress(done, total):  # large batches take minutes to draw on the host
-        if total >= 16 and (done % 8 == 0 or done == total):
-            log(f"generated {done}/{total} sequences")
-    inp = gen.make(s, steps=n_q, progress=gen_progress)
-    log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
-    dev = upload(inp)
-    d = dims_of(s)
-    model = model_of(dev)
-    cache = P.alloc_cache(d)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    ev[0].record()
-    P.compress(d, model, dev["k"], dev["v"], cache)
-    ev[1].record()
-    torch.cuda.synchronize()
-    compress_ms = ev[0].elapsed_time(ev[1])
-    log(f"compress {compress_ms:.1f} ms")
-    comp_bytes, dense_bytes = P.cache_bytes(dims_of(s))   # as compressed, before any eviction
-    evicted = None
-    if s.evict_keep < 1.0:
-        cache, d, _ = P.evict(d, model, cache, to_dev(inp["obs_q"]), s.keep_chunks)
+        self.s, self.n_q = s, n_q
+        t0 = time.perf_counter()
+
+        def gen_progress(done, total):  # large batches take a while to draw on the host
+            if not quiet and total >= 16 and (done % 8 == 0 or done == total):
+                log(f"generated {done}/{total} sequences")
+        self.inp = gen.make(s, steps=n_q, progress=gen_progress)
+        self.gen_s = time.perf_counter() - t0
+        log(f"{s.name} B={s.B}: generated inputs in {self.gen_s:.1f} s")
+        self.dev = dev = upload(self.inp)
+        self.d = d = dims_of(s)
+        self.model = model = model_of(dev)
+        self.cache = P.alloc_cache(d)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
-        # against the dense bf16 cache of all s.N tokens: the evicted cache as
-        # allocated (every head sized to the largest head's kept rows), and by
-        # the rows the kept chunks actually hold
-        comp_ev, _ = P.cache_bytes(d)
-        live = float(cache["res_ptr"][..., -1].sum().item()) / s.B
-        row_b = s.dh * (1 if s.resid == "i8" else 2) + 4
-        comp_live = comp_ev - (s.G * s.Hkv * d.n_res - live) * row_b
-        evicted = {"n_ctx": d.n_ctx, "res_rows_capacity": d.n_res, "res_rows_live_per_seq": live,
-                   "compressed_bytes_per_seq": comp_ev, "ratio_vs_dense_bf16": round(dense_bytes / comp_ev, 2),
-                   "ratio_vs_dense_bf16_live_rows": round(dense_bytes / comp_live, 2),
-                   "dense_bytes_per_seq": dense_bytes,
-                   "how": f"dense = M_KV of the {s.N}-token context in bf16; compressed = the evicted cache "
-                          f"({d.n_ctx} tokens) with its residual arrays as allocated, or counting live rows only"}
-        log(f"evicted cache: {evicted['ratio_vs_dense_bf16']}x as allocated, "
-            f"{evicted['ratio_vs_dense_bf16_live_rows']}x by live rows")
+        ev[0].record()
+        P.compress(d, model, dev["k"], dev["v"], self.cache)
+        ev[1].record()
+        torch.cuda.synchronize()
+        self.compress_ms = ev[0].elapsed_time(ev[1])
+        log(f"compress {self.compress_ms:.1f} ms")
+        self.comp_bytes, self.dense_bytes = P.cache_bytes(dims_of(s))   # as compressed, before any eviction
+        self.evicted = None
+        if s.evict_keep < 1.0:
+            self.cache, self.d, _ = P.evict(d, model, self.cache, to_dev(self.inp["obs_q"]), s.keep_chunks)
+            d = self.d
+            torch.cuda.synchronize()
+            # against the dense bf16 cache of all s.N tokens: the evicted cache as
+            # allocated (every head sized to the largest head's kept rows), and by
+            # the rows the kept chunks actually hold
+            comp_ev, _ = P.cache_bytes(d)
+            live = float(self.cache["res_ptr"][..., -1].sum().item()) / s.B
+            row_b = s.dh * (1 if s.resid == "i8" else 2) + 4
+            comp_live = comp_ev - (s.G * s.Hkv * d.n_res - live) * row_b
+            self.evicted = {
+                "n_ctx": d.n_ctx, "res_rows_capacity": d.n_res, "res_rows_live_per_seq": live,
+                "compressed_bytes_per_seq": comp_ev, "ratio_vs_dense_bf16": round(self.dense_bytes / comp_ev, 2),
+                "ratio_vs_dense_bf16_live_rows": round(self.dense_bytes / comp_live, 2),
+                "dense_bytes_per_seq": self.dense_bytes,
+                "how": f"dense = M_KV of the {s.N}-token context in bf16; compressed = the evicted cache "
+                       f"({d.n_ctx} tokens) with its residual arrays as allocated, or counting live rows only"}
+            log(f"evicted cache: {self.evicted['ratio_vs_dense_bf16']}x as allocated, "
+                f"{self.evicted['ratio_vs_dense_bf16_live_rows']}x by live rows")
+        kk = P.k_eff(d)
+        self.ws = P.workspace(d, P._lib.OP_DECODE)
+        self.out = torch.empty((s.B, s.Hq, s.dh), dtype=TORCH_DT[d.act], device="cuda")
+        self.sels = [[torch.empty((s.B, s.Hkv, kk), dtype=torch.int32, device="cuda") for _ in range(s.G)]
+                     for _ in range(n_q)]
+        self.calls = [[P.DecodeCall(d, l, model, self.cache, dev["q"][i, l], dev["k_tail"], dev["v_tail"],
+                                    self.out, self.ws, self.sels[i][l]) for l in range(s.G)] for i in range(n_q)]
 
-    # per (query set, layer) pre-marshalled calls
-    kk = P.k_eff(d)
-    ws = P.workspace(d, P._lib.OP_DECODE)
-    from decode_attention_compressed_amd.api import TORCH_DT
-    out = torch.empty((s.B, s.Hq, s.dh), dtype=TORCH_DT[d.act], device="cuda")
-    sels = [[torch.empty((s.B, s.Hkv, kk), dtype=torch.int32, device="cuda") for _ in range(s.G)] for _ in range(n_q)]
-    calls = [[P.DecodeCall(d, l, model, cache, dev["q"][i, l], dev["k_tail"], dev["v_tail"], out, ws, sels[i][l])
-              for l in range(s.G)] for i in range(n_q)]
-
-    def step(i):
-        for c in calls[i % n_q]:
+    def step(self, i):
+        for c in self.calls[i % self.n_q]:
             c()
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
 
-    # ---- timed region: K steps captured in one HIP graph -------------------
+def time_steps(W, steps, warmup, use_graph=True):
+    """Mean step time (ms) of `steps` decode steps: captured in one HIP graph
+    and replayed (eager launches if capture is off or fails).  Returns
+    (ms per step, the graph or None)."""
+    import torch
+    for i in range(warmup):
+        W.step(i)
+    torch.cuda.synchronize()
     graph = None
     try:
-        if args.no_graph:
+        if not use_graph:
             raise RuntimeError("disabled by --no-graph")
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                step(i)
+            for i in range(steps):
+                W.step(i)
         graph.replay()
         torch.cuda.synchronize()
     except Exception as e:  # capture unsupported: time eager launches instead
         log(f"graph capture failed ({e}); timing eager launches")
         graph = None
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     ev[0].record()
     if graph is not None:
         graph.replay()
     else:
-        for i in range(args.steps):
-            step(i)
+        for i in range(steps):
+            W.step(i)
     ev[1].record()
     torch.cuda.synchronize()
-    ms_total = ev[0].elapsed_time(ev[1])
-    ms_step = ms_total / args.steps
-    log(f"{args.steps} steps in {ms_total:.3f} ms -> {ms_step * 1e3:.1f} us/step (graph={graph is not None})")
+    ms_step = ev[0].elapsed_time(ev[1]) / steps
+    log(f"{W.s.name}: {steps} steps -> {ms_step * 1e3:.1f} us/step (graph={graph is not None})")
+    return ms_step, graph
 
-    # ---- per-step distribution: a one-step graph replayed with events around each replay
-    step_dist = None
-    if graph is not None:
-        g1 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g1):
-            step(0)
+
+def step_distribution(W, steps):
+    """p50/p90 of single steps: a one-step graph replayed with HIP events around
+    each replay (each figure includes one replay launch)."""
+    import torch
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        W.step(0)
+    g1.replay()
+    torch.cuda.synchronize()
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a_, b_ in pev:
+        a_.record()
         g1.replay()
-        torch.cuda.synchronize()
-        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        for a_, b_ in pev:
-            a_.record()
-            g1.replay()
-            b_.record()
-        torch.cuda.synchronize()
-        per = np.array([a_.elapsed_time(b_) for a_, b_ in pev]) * 1e3
-        step_dist = {"us_p50": round(float(np.median(per)), 1), "us_p90": round(float(np.percentile(per, 90)), 1),
-                     "us_min": round(float(per.min()), 1), "n": int(per.size),
-                     "how": "one-step graph replayed with HIP events around each replay (adds the replay launch)"}
-        log(f"per-step: p50 {step_dist['us_p50']} us, p90 {step_dist['us_p90']} us")
-        del g1
+        b_.record()
+    torch.cuda.synchronize()
+    per = np.array([a_.elapsed_time(b_) for a_, b_ in pev]) * 1e3
+    dist = {"us_p50": round(float(np.median(per)), 1), "us_p90": round(float(np.percentile(per, 90)), 1),
+            "us_min": round(float(per.min()), 1), "n": int(per.size),
+            "how": "one-step graph replayed with HIP events around each replay (adds the replay launch)"}
+    log(f"per-step: p50 {dist['us_p50']} us, p90 {dist['us_p90']} us")
+    del g1
+    return dist
 
-    # ---- attend-kernel timing with events on its stream ------------------------
+
+def time_attend(P, W, n_time):
+    """The rebuild-and-attend kernel alone: HIP events on its stream around each
+    attend launch of n_time steps (select and combine run outside the events),
+    against its algorithmic bytes and FLOPs.  Returns (roofline dict, bytes per
+    launch, union of selected chunks per sequence)."""
+    import torch
+    from tests.harness import to_host
+    s, d = W.s, W.d
     stream = torch.cuda.current_stream()
-    n_time = min(args.steps, n_q)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_time * s.G)]
     k = 0
     for i in range(n_time):
-        for c in calls[i]:
+        for c in W.calls[i]:
             c.select()
             evs[k][0].record(stream)
             c.attend()
@@ -509,9 +527,9 @@ def main():
             k += 1
     torch.cuda.synchronize()
     attend_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    host_ptr = to_host(cache["res_ptr"])
+    host_ptr = to_host(W.cache["res_ptr"])
     kern = P.decode_kernel(d)
-    acc = [attend_accounting(s, to_host(sels[i][l]), host_ptr, l, kern) for i in range(n_time) for l in range(s.G)]
+    acc = [attend_accounting(s, to_host(W.sels[i][l]), host_ptr, l, kern) for i in range(n_time) for l in range(s.G)]
     a_bytes = np.mean([a[0] for a in acc])
     a_flops = np.mean([a[1] for a in acc])
     union = np.mean([a[2] for a in acc]) / s.B
@@ -519,8 +537,7 @@ def main():
     gbps = a_bytes / t_attend / 1e9
     tflops = a_flops / t_attend / 1e12
     t_hbm, t_mfma = a_bytes / (HBM_PEAK_GBPS * 1e9), a_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-    bound = "hbm" if t_hbm >= t_mfma else "mfma"
-    if bound == "hbm":
+    if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     else:
@@ -536,50 +553,129 @@ def main():
                  "hbm_gbps": round(gbps, 1), "roof_time_us": round(max(t_hbm, t_mfma) * 1e6, 2),
                  "frac_of_binding_roof": round(max(t_hbm, t_mfma) / t_attend, 4)})
     log(f"attend {t_attend * 1e6:.1f} us/launch, {gbps:.0f} GB/s, {tflops:.1f} TF/s, union {union:.1f} chunks/seq")
+    return roof, a_bytes, union
 
-    # ---- dense comparator on the same queries, timed like the compressed step:
-    # K steps of G layer calls captured in one HIP graph ----------------------
-    dense = None
-    if not args.no_dense:
-        kd = torch.cat([dev["k"], dev["k_tail"]], dim=3).contiguous()
-        vd = torch.cat([dev["v"], dev["v_tail"]], dim=3).contiguous()
-        dws = P.dense_workspace(d, kd.shape[3])
-        dout = torch.empty_like(out)
 
-        def dense_step(i):
-            for l in range(s.G):
-                P.dense_decode_attn(d, dev["q"][i % n_q, l], kd, vd, l, out=dout, ws=dws)
+def time_dense(P, W, steps, use_graph):
+    """The dense bf16 comparator on the same queries, timed like the compressed
+    step: `steps` steps of G layer calls captured in one HIP graph."""
+    import torch
+    s, d, dev = W.s, W.d, W.dev
+    kd = torch.cat([dev["k"], dev["k_tail"]], dim=3).contiguous()
+    vd = torch.cat([dev["v"], dev["v_tail"]], dim=3).contiguous()
+    dws = P.dense_workspace(d, kd.shape[3])
+    dout = torch.empty_like(W.out)
 
-        for i in range(2):
-            dense_step(i)
-        torch.cuda.synchronize()
-        dgraph = None
-        if graph is not None:
-            dgraph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(dgraph):
-                for i in range(args.steps):
-                    dense_step(i)
-            dgraph.replay()
-            torch.cuda.synchronize()
-        ev[0].record()
-        if dgraph is not None:
-            dgraph.replay()
-        else:
-            for i in range(args.steps):
+    def dense_step(i):
+        for l in range(s.G):
+            P.dense_decode_attn(d, dev["q"][i % W.n_q, l], kd, vd, l, out=dout, ws=dws)
+
+    for i in range(2):
+        dense_step(i)
+    torch.cuda.synchronize()
+    dgraph = None
+    if use_graph:
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dgraph):
+            for i in range(steps):
                 dense_step(i)
-        ev[1].record()
+        dgraph.replay()
         torch.cuda.synchronize()
-        dense_ms = ev[0].elapsed_time(ev[1]) / args.steps
-        dense_bytes_step = 2 * s.B * s.G * s.Hkv * kd.shape[3] * s.dh * 2 + 2 * s.B * s.G * s.Hq * s.dh * 2
-        ideal_ms = dense_bytes_step / (HBM_PEAK_GBPS * 1e9) * 1e3
-        gb = dense_bytes_step / (dense_ms * 1e-3) / 1e9
-        dense = {"ms_per_step": round(dense_ms, 4), "hbm_gbps": round(gb, 1),
-                 "hbm_frac": round(gb / HBM_PEAK_GBPS, 4), "ideal_ms_per_step": round(ideal_ms, 4),
-                 "kernel": "k_dense_mfma (bf16 split-K) + combine, "
-                           + ("captured in one HIP graph like the compressed step" if dgraph is not None
-                              else "eager launches")}
-        log(f"dense {dense_ms * 1e3:.1f} us/step, {gb:.0f} GB/s ({gb / HBM_PEAK_GBPS:.1%} of HBM peak)")
-        del kd, vd, dgraph
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    if dgraph is not None:
+        dgraph.replay()
+    else:
+        for i in range(steps):
+            dense_step(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    dense_ms = ev[0].elapsed_time(ev[1]) / steps
+    dense_bytes_step = 2 * s.B * s.G * s.Hkv * kd.shape[3] * s.dh * 2 + 2 * s.B * s.G * s.Hq * s.dh * 2
+    ideal_ms = dense_bytes_step / (HBM_PEAK_GBPS * 1e9) * 1e3
+    gb = dense_bytes_step / (dense_ms * 1e-3) / 1e9
+    log(f"dense {dense_ms * 1e3:.1f} us/step, {gb:.0f} GB/s ({gb / HBM_PEAK_GBPS:.1%} of HBM peak)")
+    how = "captured in one HIP graph like the compressed step" if dgraph is not None else "eager launches"
+    del kd, vd, dgraph, dws, dout
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(dense_ms, 4), "hbm_gbps": round(gb, 1),
+            "hbm_frac": round(gb / HBM_PEAK_GBPS, 4), "ideal_ms_per_step": round(ideal_ms, 4),
+            "kernel": "k_dense_mfma (bf16 split-K) + combine, " + how}
+
+
+def other_workloads(P, spec, steps, warmup, use_graph):
+    """The other workloads of the method's configurations, each in the same
+    launch configuration as the headline (HIP-graph-timed steps, attend kernel
+    events, dense comparator): one compact record per (workload, batch)."""
+    import torch
+    from synth.configs import BY_NAME
+    rows = []
+    for item in spec:
+        name, _, batch = item.partition(":")
+        s = BY_NAME[name]
+        if batch:
+            s = s.replace(B=int(batch))
+        W = Workload(P, s, n_q=min(steps, 16), quiet=True)
+        ms_step, graph = time_steps(W, steps, warmup, use_graph)
+        roof, _, union = time_attend(P, W, min(steps, W.n_q))
+        del graph
+        dense = time_dense(P, W, steps, use_graph)
+        row = {"workload": s.name, "B": s.B, "us_per_step": round(ms_step * 1e3, 1),
+               "seq_steps_per_s": round(s.B / (ms_step * 1e-3), 1), "attend_kernel": P.decode_kernel(W.d),
+               "attend_us": roof["avg_launch_us"], "attend_bound": roof["bound"],
+               "attend_frac_of_binding_roof": roof["frac_of_binding_roof"],
+               "attend_hbm_frac": round(roof["hbm_gbps"] / HBM_PEAK_GBPS, 4), "attend_mfma_frac": roof["mfma_frac"],
+               "dense_us_per_step": round(dense["ms_per_step"] * 1e3, 1), "dense_hbm_frac": dense["hbm_frac"],
+               "x_vs_dense": round(dense["ms_per_step"] / ms_step, 3),
+               "compression_ratio": round(W.dense_bytes / W.comp_bytes, 3),
+               "selected_chunk_union_per_seq": round(float(union), 1), "gen_s": round(W.gen_s, 1)}
+        if W.evicted:
+            row["ratio_after_eviction"] = W.evicted["ratio_vs_dense_bf16"]
+            row["ratio_after_eviction_live_rows"] = W.evicted["ratio_vs_dense_bf16_live_rows"]
+        log(f"{s.name} B={s.B}: {row['us_per_step']} us/step, {row['x_vs_dense']}x vs dense")
+        rows.append(row)
+        del W
+        torch.cuda.empty_cache()
+    return rows
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards over "
+              "sequences with no exchange, so N GPUs run N independent copies).", file=sys.stderr)
+        sys.exit(2)
+    if args.bw_probe:
+        bw_probe()
+        return
+    import torch
+
+    import decode_attention_compressed_amd as P
+    from synth.configs import BY_NAME
+    from tests.harness import cache_to_host, dims_of
+
+    s = BY_NAME[args.workload]
+    if args.batch:
+        s = s.replace(B=args.batch)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev_name = torch.cuda.get_device_name(0)
+    log(f"workload {s.name}: {s}")
+    n_q = min(64, max(args.steps, 1))
+    W = Workload(P, s, n_q)
+    d, model, cache, dev, inp = W.d, W.model, W.cache, W.dev, W.inp
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    # ---- timed region: K steps captured in one HIP graph -------------------
+    ms_step, graph = time_steps(W, args.steps, args.warmup, use_graph=not args.no_graph)
+    graph_used = graph is not None
+    step_dist = step_distribution(W, args.steps) if graph_used else None
+    del graph
+
+    # ---- attend-kernel timing with events on its stream ------------------------
+    roof, a_bytes, union = time_attend(P, W, min(args.steps, n_q))
+
+    # ---- dense comparator on the same queries, timed like the compressed step
+    dense = None if args.no_dense else time_dense(P, W, args.steps, use_graph=graph_used)
 
     # ---- once-per-context and optional paths, timed after the decode step ------
     repack = time_repack(P, s, d, model, cache, dev, ev)
@@ -604,7 +700,14 @@ def main():
         log(f"copy reference: 3 x {args.copy_ref_mib} MiB")
         del src, dst
 
+    # ---- the other workloads, after the headline's own figures ------------------
     step_b = step_bytes(s, a_bytes) * s.G
+    comp_bytes, dense_bytes, evicted, compress_ms = W.comp_bytes, W.dense_bytes, W.evicted, W.compress_ms
+    del W, d, model, cache, dev, inp
+    torch.cuda.empty_cache()
+    spec = [] if args.configs in ("", "none") else args.configs.split(",")
+    others = other_workloads(P, spec, args.config_steps, 4, use_graph=not args.no_graph) if spec else None
+
     result = {
         "metric": "decode-attn seq-steps/s and HBM GB/s (% peak) at Llama-8B shape 32K; x vs dense",
         "value": round(s.B / (ms_step * 1e-3), 1),
@@ -637,7 +740,8 @@ def main():
         "basis": basis,
         "reuse": reuse,
         "step_time_distribution": step_dist,
-        "graph": graph is not None,
+        "graph": graph_used,
+        "other_workloads": others,
         "device": dev_name,
     }
     print(json.dumps(result), flush=True)
