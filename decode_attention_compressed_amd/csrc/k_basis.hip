@@ -31,7 +31,7 @@ using namespace f32gemm;
 constexpr int NB = 32;          // rows per Gram-Schmidt block
 constexpr int ONT = 1024;       // threads of the in-block kernel
 constexpr int MAXE = 8;         // columns per thread (D <= ONT * MAXE)
-constexpr int PBATCH = 16;      // rows whose dots are reduced together
+constexpr int PBATCH = 16;      // rows whose dots are reduced together (8 when D > 4 ONT)
 constexpr int KSPLIT = 16;      // most column slices of the block dots
 constexpr float TAU = 1e-4f;    // remainder / norm below which a row counts as dependent
 
@@ -134,50 +134,60 @@ __device__ void block_sums(float (&v)[NV], float *red /* [ONT / 64][NV] */) {
 }
 
 // v -= sum_c <v, q row c> q row c over rows first .. first + count - 1, in
-// batches of PB rows: each wave reduces its partial dot of a row with shuffles
-// and leaves it in LDS; after one barrier every thread adds the waves' parts in
-// order.  Thread t holds columns t + ONT e of v.  red: [PB][ONT / 64].
-template <int PB>
-__device__ __forceinline__ void project_rows(float (&v)[MAXE], const float *q, long base, int D, int first,
+// batches of PB rows: the batch's rows (the thread's ME columns of each) are
+// loaded into registers at once, so a batch costs one round trip to memory;
+// each wave reduces its partial dot of a row with shuffles and leaves it in
+// LDS; after one barrier every thread adds the waves' parts in order and
+// updates v from the rows it holds.  Thread t holds columns t + ONT e of v.
+// red: [PB][ONT / 64].
+template <int PB, int ME>
+__device__ __forceinline__ void project_rows(float (&v)[ME], const float *q, long base, int D, int first,
                                              int count, float *red) {
   constexpr int NWV = ONT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int c0 = first; c0 < first + count; c0 += PB) {
     const int nc = min(PB, first + count - c0);
-#pragma unroll 4
-    for (int c = 0; c < nc; ++c) {
-      const float *row = q + base + (long)(c0 + c) * D;
-      float s = 0.f;
+    float rw[PB][ME];
 #pragma unroll
-      for (int e = 0; e < MAXE; ++e) {
+    for (int c = 0; c < PB; ++c) {
+      const float *row = q + base + (long)min(c0 + c, first + count - 1) * D;
+#pragma unroll
+      for (int e = 0; e < ME; ++e) {
         const int i = tid + ONT * e;
-        if (i < D) s = fmaf(row[i], v[e], s);
+        rw[c][e] = i < D ? row[i] : 0.f;
       }
+    }
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-      if (lane == 0) red[c * NWV + w] = s;
+    for (int c = 0; c < PB; ++c) {
+      if (c < nc) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < ME; ++e) s = fmaf(rw[c][e], v[e], s);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (lane == 0) red[c * NWV + w] = s;
+      }
     }
     __syncthreads();
-#pragma unroll 4
-    for (int c = 0; c < nc; ++c) {
-      float d = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NWV; ++ww) d += red[c * NWV + ww];
-      const float *row = q + base + (long)(c0 + c) * D;
+    for (int c = 0; c < PB; ++c) {
+      if (c < nc) {
+        float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < MAXE; ++e) {
-        const int i = tid + ONT * e;
-        if (i < D) v[e] = fmaf(-d, row[i], v[e]);
+        for (int ww = 0; ww < NWV; ++ww) d += red[c * NWV + ww];
+#pragma unroll
+        for (int e = 0; e < ME; ++e) v[e] = fmaf(-d, rw[c][e], v[e]);
       }
     }
     __syncthreads();
   }
 }
 
-__device__ __forceinline__ float row_norm(const float (&v)[MAXE], float *red) {
+template <int ME>
+__device__ __forceinline__ float row_norm(const float (&v)[ME], float *red) {
   float n2[1] = {0.f};
 #pragma unroll
-  for (int e = 0; e < MAXE; ++e) n2[0] = fmaf(v[e], v[e], n2[0]);
+  for (int e = 0; e < ME; ++e) n2[0] = fmaf(v[e], v[e], n2[0]);
   block_sums<1>(n2, red);
   return sqrtf(n2[0]);
 }
@@ -188,41 +198,56 @@ __device__ __forceinline__ float row_norm(const float (&v)[MAXE], float *red) {
 // nrm0[a] is replaced by a pseudo-random row, orthogonalised here against the
 // block's earlier rows; the second block pass projects it off the earlier
 // blocks (a random row is far from their span, so one projection suffices).
-// Thread t owns columns t + ONT e and only reads back columns it wrote itself.
-// grid (B), ONT threads.
-template <bool DETECT>
+// Thread t owns columns t + ONT e (e < ME, ME = ceil(D / ONT)) and only reads
+// back columns it wrote itself.  grid (B), ONT threads.
+template <bool DETECT, int ME>
 __global__ __launch_bounds__(ONT) void k_intra(const float *src, float *q, int r, int D, int row0, int nb,
                                                const double *__restrict__ nrm0, uint32_t salt) {
-  __shared__ float red[PBATCH * (ONT / 64)];
+  constexpr int PB = ME <= 4 ? PBATCH : PBATCH / 2;  // the batch's columns stay within the registers
+  __shared__ float red[PB * (ONT / 64)];
   const int b = blockIdx.x, tid = threadIdx.x;
   const long base = (long)b * r * D;
   for (int a = 0; a < nb; ++a) {
-    float v[MAXE];
+    float v[ME];
 #pragma unroll
-    for (int e = 0; e < MAXE; ++e) {
+    for (int e = 0; e < ME; ++e) {
       const int i = tid + ONT * e;
       v[e] = i < D ? src[base + (long)(row0 + a) * D + i] : 0.f;
     }
-    project_rows<PBATCH>(v, q, base, D, row0, a, red);
-    project_rows<PBATCH>(v, q, base, D, row0, a, red);
+    project_rows<PB>(v, q, base, D, row0, a, red);
+    project_rows<PB>(v, q, base, D, row0, a, red);
     float nrm = row_norm(v, red);
     if (DETECT && (double)nrm <= (double)TAU * nrm0[(long)b * NB + a]) {
 #pragma unroll
-      for (int e = 0; e < MAXE; ++e) {
+      for (int e = 0; e < ME; ++e) {
         const int i = tid + ONT * e;
         v[e] = i < D ? hash_uniform(b, row0 + a, i, salt) : 0.f;
       }
-      project_rows<PBATCH>(v, q, base, D, row0, a, red);
-      project_rows<PBATCH>(v, q, base, D, row0, a, red);
+      project_rows<PB>(v, q, base, D, row0, a, red);
+      project_rows<PB>(v, q, base, D, row0, a, red);
       nrm = row_norm(v, red);
     }
     const float inv = nrm > 0.f ? 1.0f / nrm : 0.f;
 #pragma unroll
-    for (int e = 0; e < MAXE; ++e) {
+    for (int e = 0; e < ME; ++e) {
       const int i = tid + ONT * e;
       if (i < D) q[base + (long)(row0 + a) * D + i] = v[e] * inv;
     }
   }
+}
+
+template <bool DETECT>
+static void launch_intra(const float *src, float *q, int B, int r, int D, int row0, int nb, const double *nrm,
+                         uint32_t salt, hipStream_t st) {
+  const int me = (D + ONT - 1) / ONT;
+  if (me <= 1)
+    hipLaunchKernelGGL((k_intra<DETECT, 1>), dim3(B), dim3(ONT), 0, st, src, q, r, D, row0, nb, nrm, salt);
+  else if (me <= 2)
+    hipLaunchKernelGGL((k_intra<DETECT, 2>), dim3(B), dim3(ONT), 0, st, src, q, r, D, row0, nb, nrm, salt);
+  else if (me <= 4)
+    hipLaunchKernelGGL((k_intra<DETECT, 4>), dim3(B), dim3(ONT), 0, st, src, q, r, D, row0, nb, nrm, salt);
+  else
+    hipLaunchKernelGGL((k_intra<DETECT, MAXE>), dim3(B), dim3(ONT), 0, st, src, q, r, D, row0, nb, nrm, salt);
 }
 
 // C[b][a][c] = sum over slices s of part[b * S + s][a][c], in order.
@@ -275,11 +300,9 @@ static void orth(float *src, float *q, float *cbuf, float *cpart, double *nrm, i
         gemm(Ac, Qn, EpSub{blk, zs, D, j0}, nb, D, j0, B, st);
       }
       if (pass == 0)
-        hipLaunchKernelGGL(k_intra<true>, dim3(B), dim3(ONT), 0, st, (const float *)blk, q, r, D, j0, nb,
-                           (const double *)nrm, salt);
+        launch_intra<true>(blk, q, B, r, D, j0, nb, nrm, salt, st);
       else
-        hipLaunchKernelGGL(k_intra<false>, dim3(B), dim3(ONT), 0, st, (const float *)blk, q, r, D, j0, nb,
-                           (const double *)nrm, salt);
+        launch_intra<false>(blk, q, B, r, D, j0, nb, nrm, salt, st);
     }
   }
 }
