@@ -158,6 +158,9 @@ struct BasisArgs {
   float *cbuf;                   // workspace [B][32][r]
   float *cpart;                  // workspace [B][16][32][r]: sliced block dots
   double *nrm;                   // workspace [B][32]
+  double *mpart;                 // workspace [B][ceil(D / 256)][32][32]: in-block Gram slices
+  double *tri;                   // workspace [B][32][32]: inverse Cholesky factor of a block
+  int32_t *dep;                  // workspace [B][32]: rows of a block replaced as dependent
   int B, G, Hkv, dh, r, N, iterations, act;
 };
 hipError_t run_basis(const BasisArgs &a, hipStream_t st);

@@ -8,15 +8,17 @@
 //   Q = orth(Omega), Omega a counter-hash pseudo-random r x D start;
 //   `iterations` times: Q = orth(Q G)   (subspace iteration, rows of Q^T);
 //   U = Q^T rounded to the act dtype.
-// orth() is block Gram-Schmidt run twice (blocks of NB rows): each block is
-// projected off the finished rows with two products, then its rows are
-// orthonormalised one by one inside one workgroup (each thread owns a fixed
-// set of columns, so it only ever reads back what it wrote).  In the first
-// pass a row whose remainder falls below TAU of its norm (numerically in the
-// span of the rows before it) is replaced by a pseudo-random row, which the
-// second pass orthogonalises like any other.  The result spans the dominant r-dimensional
-// subspace; no rotation within it is made (reconstructions U U^T k do not
-// depend on one).
+// orth() orthonormalises blocks of NB rows in order, each twice: the block is
+// projected off the finished rows with two products, then orthonormalised in
+// itself by a Cholesky factorisation of its NB x NB Gram matrix M = V V^T
+// (float64, summed over column slices in a fixed order): with M = L L^T the
+// rows of L^{-1} V are orthonormal.  In the first pass a row whose pivot
+// (its remainder after the block's earlier rows, squared) falls below TAU^2
+// of its squared norm is numerically in the span before it: it is left out of
+// the factorisation and replaced by a pseudo-random row, which the second
+// pass orthogonalises like any other.  The result spans the dominant
+// r-dimensional subspace; no rotation within it is made (reconstructions
+// U U^T k do not depend on one).
 #include <cstring>
 
 #include "common.hpp"
@@ -28,12 +30,11 @@ namespace basis {
 
 using namespace f32gemm;
 
-constexpr int NB = 32;          // rows per Gram-Schmidt block
-constexpr int ONT = 1024;       // threads of the in-block kernel
-constexpr int MAXE = 8;         // columns per thread (D <= ONT * MAXE)
-constexpr int PBATCH = 16;      // rows whose dots are reduced together (8 when D > 4 ONT)
+constexpr int NB = 32;          // rows per orthonormalisation block
+constexpr int MAXD = 8192;      // largest group key dim D
+constexpr int GW = 256;         // columns per slice of the in-block Gram matrix
 constexpr int KSPLIT = 16;      // most column slices of the block dots
-constexpr float TAU = 1e-4f;    // remainder / norm below which a row counts as dependent
+constexpr double TAU = 1e-4;    // remainder / norm below which a row counts as dependent
 
 // K_cat(b, t, i) = k[b][i / dh][t][i % dh], read as A(b, i, t) = K_cat(b, t, i)
 // and B(b, t, j) = K_cat(b, t, j); consecutive dims of one (layer, head) block
@@ -111,143 +112,113 @@ __global__ __launch_bounds__(256) void k_rownorm(const float *__restrict__ x, in
   if (tid == 0) nrm[(long)b * NB + a] = sqrt(red[0]);
 }
 
-// Block sums of NV values per thread, in a fixed order; every thread gets the totals.
-template <int NV>
-__device__ void block_sums(float (&v)[NV], float *red /* [ONT / 64][NV] */) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int k = 0; k < NV; ++k)
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v[k] += __shfl_xor(v[k], o, 64);
-  if (lane == 0)
-#pragma unroll
-    for (int k = 0; k < NV; ++k) red[w * NV + k] = v[k];
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    float s = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < ONT / 64; ++ww) s += red[ww * NV + k];
-    v[k] = s;
+// In-block Gram matrix of rows row0 .. row0 + nb - 1 of x over the GW
+// columns of slice s: mpart[b][s][a][c] = sum_i x[a][i] x[c][i] in float64
+// (float32 products are exact in float64), columns in ascending order.  Both
+// triangles are written.  grid (ceil(D / GW), B), 256 threads.
+__global__ __launch_bounds__(256) void k_bgram(const float *__restrict__ x, int r, int D, int row0, int nb,
+                                               double *__restrict__ mpart) {
+  __shared__ float xs[NB][GW + 1];
+  const int s = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, S = gridDim.x;
+  const int c0 = s * GW;
+  for (int idx = tid; idx < NB * GW; idx += 256) {
+    const int a = idx / GW, i = idx % GW;
+    xs[a][i] = (a < nb && c0 + i < D) ? x[((long)b * r + row0 + a) * D + c0 + i] : 0.f;
   }
   __syncthreads();
-}
-
-// v -= sum_c <v, q row c> q row c over rows first .. first + count - 1, in
-// batches of PB rows: the batch's rows (the thread's ME columns of each) are
-// loaded into registers at once, so a batch costs one round trip to memory;
-// each wave reduces its partial dot of a row with shuffles and leaves it in
-// LDS; after one barrier every thread adds the waves' parts in order and
-// updates v from the rows it holds.  Thread t holds columns t + ONT e of v.
-// red: [PB][ONT / 64].
-template <int PB, int ME>
-__device__ __forceinline__ void project_rows(float (&v)[ME], const float *q, long base, int D, int first,
-                                             int count, float *red) {
-  constexpr int NWV = ONT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int c0 = first; c0 < first + count; c0 += PB) {
-    const int nc = min(PB, first + count - c0);
-    float rw[PB][ME];
-#pragma unroll
-    for (int c = 0; c < PB; ++c) {
-      const float *row = q + base + (long)min(c0 + c, first + count - 1) * D;
-#pragma unroll
-      for (int e = 0; e < ME; ++e) {
-        const int i = tid + ONT * e;
-        rw[c][e] = i < D ? row[i] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < PB; ++c) {
-      if (c < nc) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < ME; ++e) s = fmaf(rw[c][e], v[e], s);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-        if (lane == 0) red[c * NWV + w] = s;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < PB; ++c) {
-      if (c < nc) {
-        float d = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NWV; ++ww) d += red[c * NWV + ww];
-#pragma unroll
-        for (int e = 0; e < ME; ++e) v[e] = fmaf(-d, rw[c][e], v[e]);
-      }
-    }
-    __syncthreads();
+  double *mp = mpart + ((long)b * S + s) * NB * NB;
+  for (int p = tid; p < NB * NB; p += 256) {
+    const int a = p / NB, c = p % NB;
+    if (c > a) continue;
+    double acc = 0.0;
+    for (int i = 0; i < GW; ++i) acc = fma((double)xs[a][i], (double)xs[c][i], acc);
+    mp[a * NB + c] = acc;
+    mp[c * NB + a] = acc;
   }
 }
 
-template <int ME>
-__device__ __forceinline__ float row_norm(const float (&v)[ME], float *red) {
-  float n2[1] = {0.f};
-#pragma unroll
-  for (int e = 0; e < ME; ++e) n2[0] = fmaf(v[e], v[e], n2[0]);
-  block_sums<1>(n2, red);
-  return sqrtf(n2[0]);
-}
-
-// Rows row0 .. row0 + nb - 1 of src orthonormalised one by one against the
-// rows before them inside the block (two passes each) and written to rows
-// row0.. of q (src may be q).  DETECT: a row whose remainder is <= TAU *
-// nrm0[a] is replaced by a pseudo-random row, orthogonalised here against the
-// block's earlier rows; the second block pass projects it off the earlier
-// blocks (a random row is far from their span, so one projection suffices).
-// Thread t owns columns t + ONT e (e < ME, ME = ceil(D / ONT)) and only reads
-// back columns it wrote itself.  grid (B), ONT threads.
-template <bool DETECT, int ME>
-__global__ __launch_bounds__(ONT) void k_intra(const float *src, float *q, int r, int D, int row0, int nb,
-                                               const double *__restrict__ nrm0, uint32_t salt) {
-  constexpr int PB = ME <= 4 ? PBATCH : PBATCH / 2;  // the batch's columns stay within the registers
-  __shared__ float red[PB * (ONT / 64)];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const long base = (long)b * r * D;
-  for (int a = 0; a < nb; ++a) {
-    float v[ME];
-#pragma unroll
-    for (int e = 0; e < ME; ++e) {
-      const int i = tid + ONT * e;
-      v[e] = i < D ? src[base + (long)(row0 + a) * D + i] : 0.f;
-    }
-    project_rows<PB>(v, q, base, D, row0, a, red);
-    project_rows<PB>(v, q, base, D, row0, a, red);
-    float nrm = row_norm(v, red);
-    if (DETECT && (double)nrm <= (double)TAU * nrm0[(long)b * NB + a]) {
-#pragma unroll
-      for (int e = 0; e < ME; ++e) {
-        const int i = tid + ONT * e;
-        v[e] = i < D ? hash_uniform(b, row0 + a, i, salt) : 0.f;
-      }
-      project_rows<PB>(v, q, base, D, row0, a, red);
-      project_rows<PB>(v, q, base, D, row0, a, red);
-      nrm = row_norm(v, red);
-    }
-    const float inv = nrm > 0.f ? 1.0f / nrm : 0.f;
-#pragma unroll
-    for (int e = 0; e < ME; ++e) {
-      const int i = tid + ONT * e;
-      if (i < D) q[base + (long)(row0 + a) * D + i] = v[e] * inv;
-    }
-  }
-}
-
+// Per sequence: M = sum over the S slices (in order) of mpart; the Cholesky
+// factor M = L L^T column by column; tri = L^{-1} (lower, float64).  DETECT: a
+// row whose pivot is <= (TAU nrm0[a])^2 is left out (its row and column of L
+// are zero, so no later row is projected on it) and flagged in dep for
+// replacement; without DETECT only a pivot <= 0 is left out (its row stays
+// zero).  grid (B), NB * NB threads.
 template <bool DETECT>
-static void launch_intra(const float *src, float *q, int B, int r, int D, int row0, int nb, const double *nrm,
-                         uint32_t salt, hipStream_t st) {
-  const int me = (D + ONT - 1) / ONT;
-  if (me <= 1)
-    hipLaunchKernelGGL((k_intra<DETECT, 1>), dim3(B), dim3(ONT), 0, st, src, q, r, D, row0, nb, nrm, salt);
-  else if (me <= 2)
-    hipLaunchKernelGGL((k_intra<DETECT, 2>), dim3(B), dim3(ONT), 0, st, src, q, r, D, row0, nb, nrm, salt);
-  else if (me <= 4)
-    hipLaunchKernelGGL((k_intra<DETECT, 4>), dim3(B), dim3(ONT), 0, st, src, q, r, D, row0, nb, nrm, salt);
-  else
-    hipLaunchKernelGGL((k_intra<DETECT, MAXE>), dim3(B), dim3(ONT), 0, st, src, q, r, D, row0, nb, nrm, salt);
+__global__ __launch_bounds__(NB * NB) void k_chol(const double *__restrict__ mpart, int S, int nb,
+                                                  const double *__restrict__ nrm0, double *__restrict__ tri,
+                                                  int32_t *__restrict__ dep) {
+  __shared__ double M[NB][NB + 1], L[NB][NB + 1];
+  __shared__ int out_[NB];
+  const int b = blockIdx.x, tid = threadIdx.x, x = tid / NB, y = tid % NB;
+  {
+    const double *mp = mpart + (long)b * S * NB * NB + x * NB + y;
+    double acc = 0.0;
+    for (int s = 0; s < S; ++s) acc += mp[(long)s * NB * NB];
+    M[x][y] = acc;
+    L[x][y] = 0.0;
+  }
+  __syncthreads();
+  for (int a = 0; a < nb; ++a) {
+    // column a of L from the updated M; M[a][a] is the squared remainder of row a
+    const double d = M[a][a];
+    const bool drop = DETECT ? !(d > (TAU * nrm0[(long)b * NB + a]) * (TAU * nrm0[(long)b * NB + a])) : !(d > 0.0);
+    if (tid == 0) out_[a] = drop;
+    const double la = drop ? 0.0 : sqrt(d);
+    if (y == a && x >= a && x < nb) L[x][a] = drop ? 0.0 : (x == a ? la : M[x][a] / la);
+    __syncthreads();
+    // trailing update of the lower triangle: M[x][y] -= L[x][a] L[y][a]
+    if (y > a && x >= y && x < nb) M[x][y] = fma(-L[x][a], L[y][a], M[x][y]);
+    __syncthreads();
+  }
+  // tri = L^{-1} by forward substitution, one column c per thread of the first
+  // wave; left-out rows give zero rows (their L row is zero).  Only the first
+// pass flags rows for replacement.
+  if (tid < NB) {
+    const int c = tid;
+    double tcol[NB];
+#pragma unroll
+    for (int a = 0; a < NB; ++a) tcol[a] = 0.0;
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      if (a < c || a >= nb || out_[a]) continue;
+      double s = a == c ? 1.0 : 0.0;
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (k >= c && k < a) s = fma(-L[a][k], tcol[k], s);
+      tcol[a] = s / L[a][a];
+    }
+#pragma unroll
+    for (int a = 0; a < NB; ++a) tri[((long)b * NB + a) * NB + c] = tcol[a];
+    dep[(long)b * NB + c] = DETECT && c < nb ? out_[c] : 0;
+  }
+}
+
+// Rows row0 .. row0 + nb - 1 of q = tri (rows of src), column by column (src may
+// be q: a thread reads its column of every row before writing it).  Rows
+// flagged in dep get the pseudo-random values of (b, row, column, salt).
+// grid (ceil(D / 256), B), 256 threads.
+__global__ __launch_bounds__(256) void k_apply_tri(const float *src, float *q, int r, int D, int row0, int nb,
+                                                   const double *__restrict__ tri, const int32_t *__restrict__ dep,
+                                                   uint32_t salt) {
+  __shared__ double T[NB][NB];
+  __shared__ int dp[NB];
+  const int b = blockIdx.y, tid = threadIdx.x, i = blockIdx.x * 256 + tid;
+  for (int idx = tid; idx < NB * NB; idx += 256) T[idx / NB][idx % NB] = tri[(long)b * NB * NB + idx];
+  if (tid < NB) dp[tid] = dep[(long)b * NB + tid];
+  __syncthreads();
+  if (i >= D) return;
+  const long base = ((long)b * r + row0) * D + i;
+  double v[NB];
+#pragma unroll
+  for (int a = 0; a < NB; ++a) v[a] = a < nb ? (double)src[base + (long)a * D] : 0.0;
+#pragma unroll
+  for (int a = 0; a < NB; ++a) {
+    if (a >= nb) continue;
+    double s = 0.0;
+#pragma unroll
+    for (int c = 0; c <= a; ++c) s = fma(T[a][c], v[c], s);
+    q[base + (long)a * D] = dp[a] ? hash_uniform(b, row0 + a, i, salt) : (float)s;
+  }
 }
 
 // C[b][a][c] = sum over slices s of part[b * S + s][a][c], in order.
@@ -278,10 +249,11 @@ static int dot_slices(int D) {
   return S;
 }
 
-static void orth(float *src, float *q, float *cbuf, float *cpart, double *nrm, int B, int r, int D,
-                 uint32_t salt, hipStream_t st) {
+static void orth(float *src, float *q, float *cbuf, float *cpart, double *nrm, double *mpart, double *tri,
+                 int32_t *dep, int B, int r, int D, uint32_t salt, hipStream_t st) {
   const long zs = (long)r * D;
   const int S = dot_slices(D), Dsl = D / S;
+  const int SG = (D + GW - 1) / GW;
   for (int j0 = 0; j0 < r; j0 += NB) {
     const int nb = min(NB, r - j0);
     hipLaunchKernelGGL(k_rownorm, dim3(nb, B), dim3(256), 0, st, (const float *)src, r, D, j0, nrm);
@@ -299,10 +271,15 @@ static void orth(float *src, float *q, float *cbuf, float *cpart, double *nrm, i
         BOp<float, false> Qn{q, ZOff{1, zs, 0}, D};
         gemm(Ac, Qn, EpSub{blk, zs, D, j0}, nb, D, j0, B, st);
       }
+      hipLaunchKernelGGL(k_bgram, dim3(SG, B), dim3(256), 0, st, (const float *)blk, r, D, j0, nb, mpart);
       if (pass == 0)
-        launch_intra<true>(blk, q, B, r, D, j0, nb, nrm, salt, st);
+        hipLaunchKernelGGL(k_chol<true>, dim3(B), dim3(NB * NB), 0, st, (const double *)mpart, SG, nb,
+                           (const double *)nrm, tri, dep);
       else
-        launch_intra<false>(blk, q, B, r, D, j0, nb, nrm, salt, st);
+        hipLaunchKernelGGL(k_chol<false>, dim3(B), dim3(NB * NB), 0, st, (const double *)mpart, SG, nb,
+                           (const double *)nrm, tri, dep);
+      hipLaunchKernelGGL(k_apply_tri, dim3((D + 255) / 256, B), dim3(256), 0, st, (const float *)blk, q, r, D,
+                         j0, nb, (const double *)tri, (const int32_t *)dep, salt);
     }
   }
 }
@@ -317,12 +294,12 @@ static void basis_typed(const BasisArgs &a, hipStream_t st) {
   gemm<true>(Ka, Kb, EpSym{a.gram, D}, D, D, N, B, st);
   // start
   hipLaunchKernelGGL(k_start, dim3((D + 255) / 256, r, B), dim3(256), 0, st, a.yt, r, D);
-  orth(a.yt, a.qt, a.cbuf, a.cpart, a.nrm, B, r, D, 1u, st);
+  orth(a.yt, a.qt, a.cbuf, a.cpart, a.nrm, a.mpart, a.tri, a.dep, B, r, D, 1u, st);
   AOp<float, true> Qa{a.qt, ZOff{1, zs, 0}, D};
   BOp<float, false> Gb{a.gram, ZOff{1, (long)D * D, 0}, D};
   for (int it = 0; it < a.iterations; ++it) {
     gemm(Qa, Gb, EpPut{a.yt, zs, D}, r, D, D, B, st);   // Yt = Qt G
-    orth(a.yt, a.qt, a.cbuf, a.cpart, a.nrm, B, r, D, 2u + it, st);
+    orth(a.yt, a.qt, a.cbuf, a.cpart, a.nrm, a.mpart, a.tri, a.dep, B, r, D, 2u + it, st);
   }
   hipLaunchKernelGGL(k_store_basis<TA>, dim3((r + 63) / 64, (D + 3) / 4, B), dim3(256), 0, st,
                      (const float *)a.qt, (TA *)a.basis, r, D);
@@ -330,7 +307,7 @@ static void basis_typed(const BasisArgs &a, hipStream_t st) {
 
 }  // namespace basis
 
-int basis_max_dim() { return basis::ONT * basis::MAXE; }
+int basis_max_dim() { return basis::MAXD; }
 
 hipError_t run_basis(const BasisArgs &a, hipStream_t st) {
   if (a.act == LOWRAM_F32) basis::basis_typed<float>(a, st);

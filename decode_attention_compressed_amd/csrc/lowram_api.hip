@@ -224,7 +224,7 @@ FitPlan fit_plan(const lowram_dims *d) {
 // Key-basis workspace: the D x D Gram matrix, two r x D row sets, the block
 // products and row norms (float32 / float64).
 struct BasisPlan {
-  size_t gram_off, yt_off, qt_off, c_off, cpart_off, nrm_off, bytes;
+  size_t gram_off, yt_off, qt_off, c_off, cpart_off, nrm_off, mpart_off, tri_off, dep_off, bytes;
 };
 
 BasisPlan basis_plan(const lowram_dims *d) {
@@ -236,7 +236,10 @@ BasisPlan basis_plan(const lowram_dims *d) {
   p.c_off = p.qt_off + align_up(4 * B * r * D);
   p.cpart_off = p.c_off + align_up(4 * B * 32 * r);
   p.nrm_off = p.cpart_off + align_up(4 * B * 16 * 32 * r);
-  p.bytes = p.nrm_off + align_up(8 * B * 32);
+  p.mpart_off = p.nrm_off + align_up(8 * B * 32);
+  p.tri_off = p.mpart_off + align_up(8 * B * ((D + 255) / 256) * 32 * 32);
+  p.dep_off = p.tri_off + align_up(8 * B * 32 * 32);
+  p.bytes = p.dep_off + align_up(4 * B * 32);
   return p;
 }
 
@@ -771,6 +774,9 @@ lowram_status lowram_key_basis(const lowram_dims *d, const void *k, int32_t iter
   a.cbuf = reinterpret_cast<float *>(w + p.c_off);
   a.cpart = reinterpret_cast<float *>(w + p.cpart_off);
   a.nrm = reinterpret_cast<double *>(w + p.nrm_off);
+  a.mpart = reinterpret_cast<double *>(w + p.mpart_off);
+  a.tri = reinterpret_cast<double *>(w + p.tri_off);
+  a.dep = reinterpret_cast<int32_t *>(w + p.dep_off);
   a.B = d->batch; a.G = d->layers; a.Hkv = d->heads_kv; a.dh = d->head_dim; a.r = d->rank;
   a.N = d->n_ctx; a.iterations = iterations; a.act = d->act;
   return hip_status(run_basis(a, (hipStream_t)stream), "lowram_key_basis");

@@ -347,8 +347,11 @@ lowram_status lowram_fit_predictor(const lowram_dims *dims, const lowram_model *
  * Compression": one basis shared by adjacent layers).  Per sequence: the
  * float32 Gram matrix G = K_cat^T K_cat of the N prefill keys (K_cat: N x D,
  * dims ordered (layer, kv head, dim)), then `iterations` steps of subspace
- * iteration Q <- orth(G Q) from a fixed counter-hash start, orth = block
- * Gram-Schmidt run twice.  basis (out): [B][D][r] act dtype, orthonormal
+ * iteration Q <- orth(G Q) from a fixed counter-hash start, orth = blocks of
+ * 32 rows projected off the finished rows and orthonormalised by a float64
+ * Cholesky factorisation of their 32 x 32 Gram matrix, each block twice
+ * (numerically dependent rows replaced by pseudo-random ones in the first
+ * pass).  basis (out): [B][D][r] act dtype, orthonormal
  * columns spanning the dominant r-dimensional subspace of G; unlike an
  * eigensolver's output they are not rotated to individual eigenvectors, which
  * changes no reconstruction U U^T k.  Deterministic.  k: [B][G][Hkv][N][dh]
