@@ -3,8 +3,9 @@
 // xKV finds a few principal directions of the keys and shares the basis
 // across adjacent layers (rit.work page, keys section; zicq.com English
 // summary, "Cross-Layer Low-Rank Key Compression").  Here, per sequence:
-//   G = K_cat^T K_cat over the N prefill tokens (D x D, float32; only the
-//       upper tiles are computed, the epilogue writes both triangles);
+//   G = K_cat^T K_cat over the N prefill tokens (D x D, float32 sums; only
+//       the upper tiles are computed, the epilogue writes both triangles; on
+//       the matrix cores for bf16 keys);
 //   Q = orth(Omega), Omega a counter-hash pseudo-random r x D start;
 //   `iterations` times: Q = orth(Q G)   (subspace iteration, rows of Q^T);
 //   U = Q^T rounded to the act dtype.
@@ -20,6 +21,7 @@
 // r-dimensional subspace; no rotation within it is made (reconstructions
 // U U^T k do not depend on one).
 #include <cstring>
+#include <type_traits>
 
 #include "common.hpp"
 #include "gemm_f32.hpp"
@@ -110,6 +112,110 @@ __global__ __launch_bounds__(256) void k_rownorm(const float *__restrict__ x, in
     __syncthreads();
   }
   if (tid == 0) nrm[(long)b * NB + a] = sqrt(red[0]);
+}
+
+// G[b] = K_cat^T K_cat of bf16 keys on the matrix cores: bf16 x bf16
+// products are exact in float32 and the sums accumulate in float32, the
+// precision of the vector-ALU product it replaces.  One workgroup of 4 waves
+// per 128 x 128 tile of G with i0 <= j0 (the epilogue writes both triangles;
+// a diagonal tile writes only i <= j, so no element is stored twice); each
+// wave owns a 64 x 64 quarter, 16 blocks of v_mfma_f32_16x16x32_bf16.  Per
+// step of 32 tokens the tile's key columns (rows i and rows j of K_cat^T) are
+// staged through LDS token-contiguous per column, two tokens per dword, so a
+// lane reads its 8 consecutive tokens of a column as one MFMA operand; the
+// next step's keys are loaded into registers while the current step's
+// products run.  Tokens past N and columns past D are zero.
+// grid (ceil(D / 128), ceil(D / 128), B), 256 threads.
+namespace gram {
+constexpr int TI = 128, KS = 32, LD = KS + 8;  // tile, tokens per step, LDS row stride (elements)
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+}  // namespace gram
+
+__global__ __launch_bounds__(256) void k_gram_mfma(const uint16_t *__restrict__ k, float *__restrict__ g,
+                                                   int N, int dh, int D) {
+  using namespace gram;
+  __shared__ __align__(16) uint16_t As[2][TI * LD], Bs[2][TI * LD];
+  const int b = blockIdx.z, i0 = blockIdx.y * TI, j0 = blockIdx.x * TI;
+  if (i0 > j0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, kg = lane >> 4;
+  const uint16_t *kb = k + (long)b * D * N;
+  // staging: thread (token pair tp, column group cg) loads tokens 2 tp, 2 tp + 1
+  // of columns 8 cg .. 8 cg + 7 of the A (rows i) and B (rows j) tiles
+  const int tp = tid >> 4, cg = tid & 15;
+  auto col_ptr = [&](int c) -> const uint16_t * {  // K_cat(t = 0, column c)
+    return kb + (long)(c / dh) * N * dh + c % dh;
+  };
+  const int ca = i0 + 8 * cg, cb = j0 + 8 * cg;
+  const uint16_t *pa = col_ptr(ca < D ? ca : 0), *pb = col_ptr(cb < D ? cb : 0);
+  const bool oka = ca < D, okb = cb < D;
+  u32x4 ra[2], rb[2];
+  auto load = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = t0 + 2 * tp + u;
+      ra[u] = (oka && t < N) ? gld16(pa + (long)t * dh) : v4(0, 0, 0, 0);
+      rb[u] = (okb && t < N) ? gld16(pb + (long)t * dh) : v4(0, 0, 0, 0);
+    }
+  };
+  // column c = 8 cg + e of a tile gets the dword (token 2 tp, token 2 tp + 1)
+  auto stage = [&](uint16_t *dst, const u32x4 (&r)[2]) {
+    const uint32_t x0[4] = {r[0].x, r[0].y, r[0].z, r[0].w}, x1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t lo = (x0[m] & 0xFFFFu) | (x1[m] << 16);          // column 8 cg + 2 m
+      const uint32_t hi = (x0[m] >> 16) | (x1[m] & 0xFFFF0000u);      // column 8 cg + 2 m + 1
+      *reinterpret_cast<uint32_t *>(dst + (8 * cg + 2 * m) * LD + 2 * tp) = lo;
+      *reinterpret_cast<uint32_t *>(dst + (8 * cg + 2 * m + 1) * LD + 2 * tp) = hi;
+    }
+  };
+  const int wi = (w >> 1) * 64, wj = (w & 1) * 64;  // this wave's quarter of the tile
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int steps = (N + KS - 1) / KS;
+  load(0);
+  stage(As[0], ra);
+  stage(Bs[0], rb);
+  __syncthreads();
+  for (int st = 0; st < steps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < steps) load((st + 1) * KS);
+    bf16x8 af[4], bf[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      af[mi] = *reinterpret_cast<const bf16x8 *>(As[buf] + (wi + 16 * mi + l16) * LD + 8 * kg);
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj)
+      bf[nj] = *reinterpret_cast<const bf16x8 *>(Bs[buf] + (wj + 16 * nj + l16) * LD + 8 * kg);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < 4; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bf[nj], acc[mi][nj], 0, 0, 0);
+    if (st + 1 < steps) {
+      stage(As[buf ^ 1], ra);
+      stage(Bs[buf ^ 1], rb);
+    }
+    __syncthreads();
+  }
+  // lane holds G[i0 + wi + 16 mi + 4 kg + v][j0 + wj + 16 nj + l16]
+  float *gb = g + (long)b * D * D;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = i0 + wi + 16 * mi + 4 * kg + v, j = j0 + wj + 16 * nj + l16;
+        if (i < D && j < D && (i0 != j0 || i <= j)) {
+          gb[(long)i * D + j] = acc[mi][nj][v];
+          gb[(long)j * D + i] = acc[mi][nj][v];
+        }
+      }
 }
 
 // In-block Gram matrix of rows row0 .. row0 + nb - 1 of x over the GW
@@ -291,7 +397,12 @@ static void basis_typed(const BasisArgs &a, hipStream_t st) {
   // Gram matrix, upper tiles
   KcatA<TA> Ka{(const TA *)a.k, N, a.dh, D};
   KcatB<TA> Kb{(const TA *)a.k, N, a.dh, D};
-  gemm<true>(Ka, Kb, EpSym{a.gram, D}, D, D, N, B, st);
+  if (std::is_same<TA, bf16>::value && a.dh % 8 == 0) {
+    const int nt = (D + gram::TI - 1) / gram::TI;
+    hipLaunchKernelGGL(k_gram_mfma, dim3(nt, nt, B), dim3(256), 0, st, (const uint16_t *)a.k, a.gram, N, a.dh, D);
+  } else {
+    gemm<true>(Ka, Kb, EpSym{a.gram, D}, D, D, N, B, st);
+  }
   // start
   hipLaunchKernelGGL(k_start, dim3((D + 255) / 256, r, B), dim3(256), 0, st, a.yt, r, D);
   orth(a.yt, a.qt, a.cbuf, a.cpart, a.nrm, a.mpart, a.tri, a.dep, B, r, D, 1u, st);
