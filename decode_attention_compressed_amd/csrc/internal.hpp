@@ -37,6 +37,7 @@ struct AttendArgs {
   int g, cps, n_split, PW;
   int path;                     // LOWRAM_PATH_* of these dims
   int tps, tail_per_split;      // chained / absorbed kernels: tiles (slices) and tail tokens per split
+  int vsub;                     // vector kernel: token ranges per selected chunk (split = slot * vsub + range)
   float scale_log2;             // log2(e) / sqrt(dh)
   const float *qtg;             // chained kernel: [B][Hkv][QTG_G][r] float32 U_{l,h}^T q_g (select stage)
   const uint16_t *qfrag;        // per-chunk kernel: [B][Hkv][2][16][r] hi/lo operand columns (select stage)

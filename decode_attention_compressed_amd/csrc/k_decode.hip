@@ -140,7 +140,8 @@ __device__ __forceinline__ void batched_copy(int n, Ld ld, St st) {
 }
 
 // ---------------------------------------------------------------------------
-// D4-D6 on the vector ALUs.  grid (n_split + 1, Hkv, B), 256 threads; the last
+// D4-D6 on the vector ALUs.  grid (n_split + 1, Hkv, B), 256 threads; split
+// slot * vsub + range takes one token range of the slot's chunk, and the last
 // split of each (b, h) is the tail.  TT tokens per tile.  Global reads are
 // issued several at a time (staging, coefficient tiles, residual rows), and
 // the inner products are unrolled so that their LDS reads are in flight
@@ -197,12 +198,14 @@ __global__ __launch_bounds__(256) void k_attend_valu(const AttendArgs a, int TT)
     __syncthreads();
   }
 
-  const int s_end = min(a.k_eff, (split + 1) * a.cps);
-  for (int slot = split * a.cps; slot < s_end; ++slot) {
+  // split = slot * vsub + range: tokens [range * C / vsub, (range + 1) * C / vsub)
+  // of the slot's chunk
+  const int cr = C / a.vsub, slot0 = split / a.vsub, tr0 = (split % a.vsub) * cr;
+  for (int slot = slot0; slot < slot0 + 1 && slot < a.k_eff; ++slot) {
     const int j = selp[slot];
     const int e0 = rptr[j], e1 = rptr[j + 1];
-    for (int t0 = 0; t0 < C; t0 += TT) {
-      const int nt = min(TT, C - t0);
+    for (int t0 = tr0; t0 < tr0 + cr; t0 += TT) {
+      const int nt = min(TT, tr0 + cr - t0);
       const long row0 = (long)j * C + t0;
       batched_copy(nt * r, [&](int idx) { return ld_coeff(cf, row0 * r + idx, csc, idx % r); },
                    [&](int idx, float v) { cb[idx] = v; });

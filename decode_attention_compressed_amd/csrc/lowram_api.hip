@@ -87,6 +87,7 @@ lowram_status check_dims(const lowram_dims *d) {
 struct DecodePlan {
   int path;  // LOWRAM_PATH_*
   int k_eff, cps, n_split, n_part, PW, tps, tail_per_split;
+  int vsub;  // vector kernel: token ranges per selected chunk, one workgroup each
   size_t sel_off, sp_off, sc_off, part_off, absA_off, absQ_off, qtg_off, bytes;
 };
 
@@ -108,6 +109,7 @@ DecodePlan decode_plan(const lowram_dims *d) {
   p.cps = 1;
   p.tps = 0;
   p.tail_per_split = 0;
+  p.vsub = 1;
   p.path = LOWRAM_PATH_NONE;
   if (chain_supported(d->act, d->coeff, d->resid, d->head_dim, d->hidden, d->rank, d->chunk, g, p.k_eff)) {
     chain_plan(d->batch, d->heads_kv, p.k_eff, d->chunk, d->n_tail, p.n_split, p.tps, p.tail_per_split);
@@ -128,6 +130,12 @@ DecodePlan decode_plan(const lowram_dims *d) {
       p.n_part = p.n_split > 0 ? p.n_split : 1;
       p.path = LOWRAM_PATH_MFMA;
     } else {
+      // few (b, h, chunk) units: each chunk's tokens are split into up to 8
+      // ranges of at least 16 tokens, one workgroup each, toward 256 workgroups
+      const long units = (long)d->batch * d->heads_kv * p.k_eff;
+      while (p.vsub < 8 && units * p.vsub < 256 && d->chunk % (2 * p.vsub) == 0 && d->chunk / (2 * p.vsub) >= 16)
+        p.vsub *= 2;
+      p.n_split = p.k_eff * p.vsub;
       p.n_part = p.n_split + 1;
       p.path = LOWRAM_PATH_VALU;
     }
@@ -336,7 +344,7 @@ AttendArgs make_attend(const lowram_dims *d, int32_t layer, const lowram_model *
   a.r = d->rank; a.F = d->hidden; a.N = d->n_ctx; a.C = d->chunk; a.T = d->n_tail;
   a.k_eff = p.k_eff; a.n_res = d->n_res; a.layer = layer;
   a.g = d->heads_q / d->heads_kv; a.cps = p.cps; a.n_split = p.n_split; a.PW = p.PW;
-  a.path = p.path; a.tps = p.tps; a.tail_per_split = p.tail_per_split;
+  a.path = p.path; a.tps = p.tps; a.tail_per_split = p.tail_per_split; a.vsub = p.vsub;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)d->head_dim);
   if (p.path == LOWRAM_PATH_CHAIN && ws) a.qtg = reinterpret_cast<const float *>((char *)ws + p.qtg_off);
   if (p.path == LOWRAM_PATH_MFMA && ws) a.qfrag = reinterpret_cast<const uint16_t *>((char *)ws + p.qtg_off);

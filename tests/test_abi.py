@@ -337,6 +337,11 @@ def test_decode_workspace_counts_the_partials_of_each_attend_kernel():
     # nothing selected: one tail partial per (b, h)
     d0 = P.with_(dims_of(s), top_k=0)
     assert P.workspace_bytes(d0, L.OP_DECODE) == _decode_ws_expected(s.replace(k=0), 1)
-    # tiny-fp32 runs the vector kernel: one partial per chunk plus the tail's
+    # tiny-fp32 runs the vector kernel: one partial per token range of each
+    # selected chunk (4 ranges of 16 tokens: 8 (b, h, chunk) units are far
+    # below 256 workgroups) plus the tail's
     s = TINY
-    assert P.workspace_bytes(dims_of(s), L.OP_DECODE) == _decode_ws_expected(s, s.k + 1)
+    assert P.workspace_bytes(dims_of(s), L.OP_DECODE) == _decode_ws_expected(s, 4 * s.k + 1)
+    # with enough units (B = 64: 512) each chunk is one workgroup again
+    s64 = TINY.replace(B=64)
+    assert P.workspace_bytes(dims_of(s64), L.OP_DECODE) == _decode_ws_expected(s64, s64.k + 1)
