@@ -13,7 +13,7 @@
 // projected off the finished rows with two products, then orthonormalised in
 // itself by a Cholesky factorisation of its NB x NB Gram matrix M = V V^T
 // (float64, summed over column slices in a fixed order): with M = L L^T the
-// rows of L^{-1} V are orthonormal.  In the first pass a row whose pivot
+// rows of L^{-1} V (forward substitution) are orthonormal.  In the first pass a row whose pivot
 // (its remainder after the block's earlier rows, squared) falls below TAU^2
 // of its squared norm is numerically in the span before it: it is left out of
 // the factorisation and replaced by a pseudo-random row, which the second
@@ -227,9 +227,19 @@ __global__ __launch_bounds__(256) void k_bgram(const float *__restrict__ x, int 
   __shared__ float xs[NB][GW + 1];
   const int s = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, S = gridDim.x;
   const int c0 = s * GW;
-  for (int idx = tid; idx < NB * GW; idx += 256) {
-    const int a = idx / GW, i = idx % GW;
-    xs[a][i] = (a < nb && c0 + i < D) ? x[((long)b * r + row0 + a) * D + c0 + i] : 0.f;
+  {  // every load of the slice is issued before any is stored
+    constexpr int PER = NB * GW / 256;
+    float v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = tid + 256 * u, a = idx / GW, i = idx % GW;
+      v[u] = (a < nb && c0 + i < D) ? x[((long)b * r + row0 + a) * D + c0 + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = tid + 256 * u;
+      xs[idx / GW][idx % GW] = v[u];
+    }
   }
   __syncthreads();
   double *mp = mpart + ((long)b * S + s) * NB * NB;
@@ -243,73 +253,86 @@ __global__ __launch_bounds__(256) void k_bgram(const float *__restrict__ x, int 
   }
 }
 
-// Per sequence: M = sum over the S slices (in order) of mpart; the Cholesky
-// factor M = L L^T column by column; tri = L^{-1} (lower, float64).  DETECT: a
-// row whose pivot is <= (TAU nrm0[a])^2 is left out (its row and column of L
-// are zero, so no later row is projected on it) and flagged in dep for
-// replacement; without DETECT only a pivot <= 0 is left out (its row stays
-// zero).  grid (B), NB * NB threads.
+// Per sequence: M = sum over the S slices (in order) of mpart, then the
+// Cholesky factor M = L L^T column by column.  fac receives L below the
+// diagonal and 1 / L[a][a] on it.  DETECT: a row whose pivot is <=
+// (TAU nrm0[a])^2 is left out (its column of L and its reciprocal pivot are
+// zero, so no later row is projected on it and it solves to zero) and flagged
+// in dep for replacement; without DETECT only a pivot <= 0 is left out.  The
+// slice sums use every thread (eight slices' loads at a time); the
+// factorisation runs on the first wave, lane x holding row x of M in
+// registers, with the pivot and column values passed between lanes by
+// shuffles.  grid (B), NB * NB threads.
 template <bool DETECT>
 __global__ __launch_bounds__(NB * NB) void k_chol(const double *__restrict__ mpart, int S, int nb,
-                                                  const double *__restrict__ nrm0, double *__restrict__ tri,
+                                                  const double *__restrict__ nrm0, double *__restrict__ fac,
                                                   int32_t *__restrict__ dep) {
-  __shared__ double M[NB][NB + 1], L[NB][NB + 1];
-  __shared__ int out_[NB];
+  __shared__ double M[NB][NB + 1];
   const int b = blockIdx.x, tid = threadIdx.x, x = tid / NB, y = tid % NB;
   {
     const double *mp = mpart + (long)b * S * NB * NB + x * NB + y;
     double acc = 0.0;
-    for (int s = 0; s < S; ++s) acc += mp[(long)s * NB * NB];
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = s0 + u < S ? mp[(long)(s0 + u) * NB * NB] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < S) acc += v[u];
+    }
     M[x][y] = acc;
-    L[x][y] = 0.0;
   }
   __syncthreads();
-  for (int a = 0; a < nb; ++a) {
-    // column a of L from the updated M; M[a][a] is the squared remainder of row a
-    const double d = M[a][a];
-    const bool drop = DETECT ? !(d > (TAU * nrm0[(long)b * NB + a]) * (TAU * nrm0[(long)b * NB + a])) : !(d > 0.0);
-    if (tid == 0) out_[a] = drop;
+  if (tid >= WAVE) return;
+  const int lane = tid;
+  double mrow[NB];  // row `lane` of M (lanes past nb: zero), updated in place
+#pragma unroll
+  for (int c = 0; c < NB; ++c) mrow[c] = lane < nb ? M[lane][c] : 0.0;
+  // row `lane` of fac is written into M's row as each column is formed (the
+  // row's registers hold what is still needed)
+  uint32_t dropped = 0u;
+#pragma unroll
+  for (int a = 0; a < NB; ++a) {
+    if (a >= nb) continue;  // (uniform) keeps the loop fully unrolled, rows in registers
+    const double d = __shfl(mrow[a], a, WAVE);  // the updated pivot, held by lane a
+    const double t = DETECT ? TAU * nrm0[(long)b * NB + a] : 0.0;
+    const bool drop = !(d > t * t);
+    dropped |= drop ? 1u << a : 0u;
     const double la = drop ? 0.0 : sqrt(d);
-    if (y == a && x >= a && x < nb) L[x][a] = drop ? 0.0 : (x == a ? la : M[x][a] / la);
-    __syncthreads();
-    // trailing update of the lower triangle: M[x][y] -= L[x][a] L[y][a]
-    if (y > a && x >= y && x < nb) M[x][y] = fma(-L[x][a], L[y][a], M[x][y]);
-    __syncthreads();
-  }
-  // tri = L^{-1} by forward substitution, one column c per thread of the first
-  // wave; left-out rows give zero rows (their L row is zero).  Only the first
-// pass flags rows for replacement.
-  if (tid < NB) {
-    const int c = tid;
-    double tcol[NB];
+    const double ra = drop ? 0.0 : 1.0 / la;
+    // column a of L: L[lane][a] for lanes below the pivot
+    const double lx = lane > a && lane < nb ? mrow[a] * ra : 0.0;
+    if (lane < NB) M[lane][a] = lane == a ? ra : lx;
+    // trailing update of this lane's row: M[lane][c] -= L[lane][a] L[c][a]
 #pragma unroll
-    for (int a = 0; a < NB; ++a) tcol[a] = 0.0;
-#pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      if (a < c || a >= nb || out_[a]) continue;
-      double s = a == c ? 1.0 : 0.0;
-#pragma unroll
-      for (int k = 0; k < NB; ++k)
-        if (k >= c && k < a) s = fma(-L[a][k], tcol[k], s);
-      tcol[a] = s / L[a][a];
+    for (int c = a + 1; c < NB; ++c) {
+      const double lc = __shfl(lx, c, WAVE);
+      mrow[c] = fma(-lx, lc, mrow[c]);
     }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < NB) {
 #pragma unroll
-    for (int a = 0; a < NB; ++a) tri[((long)b * NB + a) * NB + c] = tcol[a];
-    dep[(long)b * NB + c] = DETECT && c < nb ? out_[c] : 0;
+    for (int c = 0; c < NB; ++c) fac[((long)b * NB + lane) * NB + c] = c <= lane && lane < nb ? M[lane][c] : 0.0;
+    dep[(long)b * NB + lane] = DETECT && lane < nb ? (int)((dropped >> lane) & 1u) : 0;
   }
 }
 
-// Rows row0 .. row0 + nb - 1 of q = tri (rows of src), column by column (src may
-// be q: a thread reads its column of every row before writing it).  Rows
-// flagged in dep get the pseudo-random values of (b, row, column, salt).
+// Rows row0 .. row0 + nb - 1 of q = L^{-1} (rows of src), column by column, by
+// forward substitution with the factor from k_chol (L below the diagonal, the
+// reciprocal pivots on it; left-out rows solve to zero).  src may be q: a
+// thread reads its column of every row before writing it.  Rows flagged in
+// dep get the pseudo-random values of (b, row, column, salt).
 // grid (ceil(D / 256), B), 256 threads.
 __global__ __launch_bounds__(256) void k_apply_tri(const float *src, float *q, int r, int D, int row0, int nb,
-                                                   const double *__restrict__ tri, const int32_t *__restrict__ dep,
+                                                   const double *__restrict__ fac, const int32_t *__restrict__ dep,
                                                    uint32_t salt) {
   __shared__ double T[NB][NB];
   __shared__ int dp[NB];
   const int b = blockIdx.y, tid = threadIdx.x, i = blockIdx.x * 256 + tid;
-  for (int idx = tid; idx < NB * NB; idx += 256) T[idx / NB][idx % NB] = tri[(long)b * NB * NB + idx];
+  for (int idx = tid; idx < NB * NB; idx += 256) T[idx / NB][idx % NB] = fac[(long)b * NB * NB + idx];
   if (tid < NB) dp[tid] = dep[(long)b * NB + tid];
   __syncthreads();
   if (i >= D) return;
@@ -320,10 +343,11 @@ __global__ __launch_bounds__(256) void k_apply_tri(const float *src, float *q, i
 #pragma unroll
   for (int a = 0; a < NB; ++a) {
     if (a >= nb) continue;
-    double s = 0.0;
+    double s = v[a];
 #pragma unroll
-    for (int c = 0; c <= a; ++c) s = fma(T[a][c], v[c], s);
-    q[base + (long)a * D] = dp[a] ? hash_uniform(b, row0 + a, i, salt) : (float)s;
+    for (int c = 0; c < a; ++c) s = fma(-T[a][c], v[c], s);
+    v[a] = s * T[a][a];  // the solved value replaces row a's input
+    q[base + (long)a * D] = dp[a] ? hash_uniform(b, row0 + a, i, salt) : (float)v[a];
   }
 }
 
