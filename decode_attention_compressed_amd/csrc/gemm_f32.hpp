@@ -1,7 +1,9 @@
-// Batched float32 products on the vector ALUs: 64 x 64 output tiles per
-// workgroup, 4 x 4 per thread, k-steps of 16 staged through LDS.  Operands are
-// read through loader functors, outputs handed to an epilogue functor, so one
-// kernel serves every product shape and fused elementwise step.
+// Batched float32 products on the matrix cores (v_mfma_f32_16x16x4_f32,
+// float32 operands and sums): 64 x 64 output tiles per workgroup, k-steps of 16
+// staged through LDS, each of the 4 waves a 32 x 32 quarter (2 x 2 blocks of
+// 16 x 16).  Operands are read through loader functors, outputs handed to an
+// epilogue functor, so one kernel serves every product shape and fused
+// elementwise step.
 #pragma once
 
 #include "common.hpp"
@@ -47,8 +49,14 @@ __global__ __launch_bounds__(256) void k_gemm(LA A, LB Bm, EP ep, int M, int N, 
   __shared__ float Bs[16][64 + 1];
   const int z = blockIdx.z, i0 = blockIdx.y * 64, j0 = blockIdx.x * 64, tid = threadIdx.x;
   if (UPPER && i0 > j0) return;
-  const int tx = tid % 16, ty = tid / 16;
-  float acc[4][4] = {};
+  const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, kg = lane >> 4;
+  const int wi = (w >> 1) * 32, wj = (w & 1) * 32;  // this wave's quarter of the tile
+  typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < 2; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < K; k0 += 16) {
     for (int idx = tid; idx < 16 * 64; idx += 256) {
       const int kk = LA::KC ? idx % 16 : idx / 64, m = LA::KC ? idx / 16 : idx % 64;
@@ -61,27 +69,32 @@ __global__ __launch_bounds__(256) void k_gemm(LA A, LB Bm, EP ep, int M, int N, 
       Bs[kk][n] = (gj < N && gk < K) ? Bm(z, gk, gj) : 0.f;
     }
     __syncthreads();
+    // four 4-wide k-steps: lane (l16, kg) holds A[row l16][k kg] and B[k kg][column l16]
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
+    for (int k4 = 0; k4 < 4; ++k4) {
+      float av[2], bv[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = As[kk][ty + 16 * a];
+      for (int mi = 0; mi < 2; ++mi) av[mi] = As[4 * k4 + kg][wi + 16 * mi + l16];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = Bs[kk][tx + 16 * c];
+      for (int nj = 0; nj < 2; ++nj) bv[nj] = Bs[4 * k4 + kg][wj + 16 * nj + l16];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(av[a], bv[c], acc[a][c]);
+        for (int nj = 0; nj < 2; ++nj)
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi], bv[nj], acc[mi][nj], 0, 0, 0);
     }
     __syncthreads();
   }
+  // lane holds C[wi + 16 mi + 4 kg + v][wj + 16 nj + l16]
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int i = i0 + ty + 16 * a, j = j0 + tx + 16 * c;
-      if (i < M && j < N) ep(z, i, j, acc[a][c]);
-    }
+    for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = i0 + wi + 16 * mi + 4 * kg + v, j = j0 + wj + 16 * nj + l16;
+        if (i < M && j < N) ep(z, i, j, acc[mi][nj][v]);
+      }
 }
 
 template <bool UPPER = false, class LA, class LB, class EP>
