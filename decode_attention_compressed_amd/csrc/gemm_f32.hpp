@@ -1,7 +1,8 @@
 // Batched float32 products on the matrix cores (v_mfma_f32_16x16x4_f32,
-// float32 operands and sums): 64 x 64 output tiles per workgroup, k-steps of 16
+// float32 operands and sums): 64 x 64 output tiles per workgroup, k-steps of 64
 // staged through LDS, each of the 4 waves a 32 x 32 quarter (2 x 2 blocks of
-// 16 x 16).  Operands are read through loader functors, outputs handed to an
+// 16 x 16); the next step's operands are read into registers while the
+// current step's products run.  Operands are read through loader functors, outputs handed to an
 // epilogue functor, so one kernel serves every product shape and fused
 // elementwise step.
 #pragma once
@@ -45,8 +46,10 @@ struct BOp {
 // writes both triangles).
 template <class LA, class LB, class EP, bool UPPER = false>
 __global__ __launch_bounds__(256) void k_gemm(LA A, LB Bm, EP ep, int M, int N, int K) {
-  __shared__ float As[16][64 + 1];
-  __shared__ float Bs[16][64 + 1];
+  constexpr int KT = 64;                 // k per staged step
+  constexpr int PER = KT * 64 / 256;     // operand values per thread and step
+  __shared__ float As[KT][64 + 1];
+  __shared__ float Bs[KT][64 + 1];
   const int z = blockIdx.z, i0 = blockIdx.y * 64, j0 = blockIdx.x * 64, tid = threadIdx.x;
   if (UPPER && i0 > j0) return;
   const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, kg = lane >> 4;
@@ -57,21 +60,48 @@ __global__ __launch_bounds__(256) void k_gemm(LA A, LB Bm, EP ep, int M, int N, 
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int nj = 0; nj < 2; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int idx = tid; idx < 16 * 64; idx += 256) {
-      const int kk = LA::KC ? idx % 16 : idx / 64, m = LA::KC ? idx / 16 : idx % 64;
-      const int gi = i0 + m, gk = k0 + kk;
-      As[kk][m] = (gi < M && gk < K) ? A(z, gi, gk) : 0.f;
-    }
-    for (int idx = tid; idx < 16 * 64; idx += 256) {
-      const int kk = LB::KC ? idx % 16 : idx / 64, n = LB::KC ? idx / 16 : idx % 64;
-      const int gj = j0 + n, gk = k0 + kk;
-      Bs[kk][n] = (gj < N && gk < K) ? Bm(z, gk, gj) : 0.f;
-    }
-    __syncthreads();
-    // four 4-wide k-steps: lane (l16, kg) holds A[row l16][k kg] and B[k kg][column l16]
+  // the next step's operands are read into registers while this step's
+  // products run
+  float ra[PER], rb[PER];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
+    for (int u = 0; u < PER; ++u) {
+      const int idx = tid + 256 * u;
+      const int kk = LA::KC ? idx % KT : idx / 64, m = LA::KC ? idx / KT : idx % 64;
+      const int gi = i0 + m, gk = k0 + kk;
+      ra[u] = (gi < M && gk < K) ? A(z, gi, gk) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = tid + 256 * u;
+      const int kk = LB::KC ? idx % KT : idx / 64, n = LB::KC ? idx / KT : idx % 64;
+      const int gj = j0 + n, gk = k0 + kk;
+      rb[u] = (gj < N && gk < K) ? Bm(z, gk, gj) : 0.f;
+    }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = tid + 256 * u;
+      const int kk = LA::KC ? idx % KT : idx / 64, m = LA::KC ? idx / KT : idx % 64;
+      As[kk][m] = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = tid + 256 * u;
+      const int kk = LB::KC ? idx % KT : idx / 64, n = LB::KC ? idx / KT : idx % 64;
+      Bs[kk][n] = rb[u];
+    }
+  };
+  fetch(0);
+  put();
+  __syncthreads();
+  for (int k0 = 0; k0 < K; k0 += KT) {
+    const bool more = k0 + KT < K;
+    if (more) fetch(k0 + KT);
+    // 4-wide k-steps: lane (l16, kg) holds A[row l16][k kg] and B[k kg][column l16]
+#pragma unroll
+    for (int k4 = 0; k4 < KT / 4; ++k4) {
       float av[2], bv[2];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) av[mi] = As[4 * k4 + kg][wi + 16 * mi + l16];
@@ -84,6 +114,10 @@ __global__ __launch_bounds__(256) void k_gemm(LA A, LB Bm, EP ep, int M, int N, 
           acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi], bv[nj], acc[mi][nj], 0, 0, 0);
     }
     __syncthreads();
+    if (more) {
+      put();
+      __syncthreads();
+    }
   }
   // lane holds C[wi + 16 mi + 4 kg + v][wj + 16 nj + l16]
 #pragma unroll
