@@ -1,6 +1,6 @@
 // Batched float32 products on the matrix cores (v_mfma_f32_16x16x4_f32,
-// float32 operands and sums): 64 x 64 output tiles per workgroup, k-steps of 64
-// staged through LDS, each of the 4 waves a 32 x 32 quarter (2 x 2 blocks of
+// float32 operands and sums): 64 x 64 output tiles per workgroup, k-steps of 16
+// or 64 staged through LDS, each of the 4 waves a 32 x 32 quarter (2 x 2 blocks of
 // 16 x 16); the next step's operands are read into registers while the
 // current step's products run.  Operands are read through loader functors, outputs handed to an
 // epilogue functor, so one kernel serves every product shape and fused
@@ -44,9 +44,9 @@ struct BOp {
 // grid (ceil(N/64), ceil(M/64), Z), 256 threads.
 // UPPER: only tiles with i0 <= j0 run (for symmetric products whose epilogue
 // writes both triangles).
-template <class LA, class LB, class EP, bool UPPER = false>
+template <class LA, class LB, class EP, bool UPPER, int KT>
 __global__ __launch_bounds__(256) void k_gemm(LA A, LB Bm, EP ep, int M, int N, int K) {
-  constexpr int KT = 64;                 // k per staged step
+  // KT: k per staged step
   constexpr int PER = KT * 64 / 256;     // operand values per thread and step
   __shared__ float As[KT][64 + 1];
   __shared__ float Bs[KT][64 + 1];
@@ -131,11 +131,17 @@ __global__ __launch_bounds__(256) void k_gemm(LA A, LB Bm, EP ep, int M, int N, 
       }
 }
 
+// Deep contractions (K >= 2048: the reductions over tokens) stage 64 k per
+// step, so fewer round trips; shorter ones 16, which keeps the registers low
+// and many workgroups per CU hiding each other's loads (their grids are large).
 template <bool UPPER = false, class LA, class LB, class EP>
 inline void gemm(LA A, LB Bm, EP ep, int M, int N, int K, int Z, hipStream_t st) {
   if (M <= 0 || N <= 0 || Z <= 0) return;
-  hipLaunchKernelGGL((k_gemm<LA, LB, EP, UPPER>), dim3((N + 63) / 64, (M + 63) / 64, Z), dim3(256), 0, st,
-                     A, Bm, ep, M, N, K);
+  const dim3 grid((N + 63) / 64, (M + 63) / 64, Z);
+  if (K >= 2048)
+    hipLaunchKernelGGL((k_gemm<LA, LB, EP, UPPER, 64>), grid, dim3(256), 0, st, A, Bm, ep, M, N, K);
+  else
+    hipLaunchKernelGGL((k_gemm<LA, LB, EP, UPPER, 16>), grid, dim3(256), 0, st, A, Bm, ep, M, N, K);
 }
 
 
