@@ -191,10 +191,10 @@ __global__ __launch_bounds__(256) void k_landmark(const TC *__restrict__ coeff,
 // Token t reads coefficient row c0 + t of a cache with Nc rows per sequence and
 // value row t of v[b][l][h] (Nv rows per (b, l, h)); err has N entries per
 // (b, l, h).
-// grid (ceil(rows/TM), G*Hkv, B), 256 threads (16 x 16).  One workgroup fills a
-// CU's LDS, so no other workgroup hides its load latency: every 16-wide slab
-// of the three products is loaded into registers while the previous slab's
-// products run, and stored to LDS after them.
+// grid (ceil(rows/TM), G*Hkv, B), 256 threads (4 waves).  The products run on
+// the float64 matrix cores.  Every 16-wide slab of the three products is
+// loaded into registers while the previous slab's products run, and stored to
+// LDS after them.
 // ---------------------------------------------------------------------------
 template <int DH, int TM, int MODE, typename TA, typename TC, typename TD>
 __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
@@ -206,7 +206,6 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
                                               double *__restrict__ err, TD *__restrict__ dout,
                                               int Hkv, int N, int r, int F, int n_rows, int n_res,
                                               int Nc, int c0, int Nv) {
-  constexpr int NA = TM / 16, NC = DH / 16;
   constexpr int KS = DH + 1, HS = 64 + 1;
   extern __shared__ __align__(16) double psm[];
   double *Ks = psm;              // [TM][DH+1]
@@ -237,8 +236,26 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
   }
   __syncthreads();
 
+  // The three products run on the float64 matrix cores
+  // (v_mfma_f64_16x16x4_f64: lane (l16, kg) holds A[row l16][k kg] and
+  // B[k kg][column l16], and the 16 x 16 result's rows kg + 4 v of column l16;
+  // the float32 and 16-bit variants hold rows 4 kg + v instead).
+  // Each wave owns a quarter of the head dims of k_hat and v_hat (NW4 blocks of
+  // 16 columns, all MB row blocks) and 16 columns of each 64-wide hidden block.
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
+  const int lane = tid & (WAVE - 1), w = tid / WAVE, l16 = lane & 15, kg = lane >> 4;
+  constexpr int MB = TM / 16, NW4 = DH / 64;
+  static_assert(DH % 64 == 0 && TM % 16 == 0, "whole blocks per wave");
+  const int wc0 = w * (DH / 4);   // this wave's first head-dim column
+  auto mma = [](double x, double y, f64x4 c) { return __builtin_amdgcn_mfma_f64_16x16x4f64(x, y, c, 0, 0, 0); };
+  const f64x4 z4 = {0.0, 0.0, 0.0, 0.0};
+
   // GEMM1: k_hat[TM][DH] = deq(c)[TM][r] . U_{l,h}^T
-  double acc[NA][NC] = {};
+  f64x4 acc[MB][NW4];
+#pragma unroll
+  for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < NW4; ++nj) acc[mi][nj] = z4;
   static_assert(16 * TM % 256 == 0 && 16 * DH % 256 == 0, "whole slabs per thread");
   // slab registers: both slabs' loads in flight together, the next slab's
   // issued before the current one's products (rows of absent tokens read
@@ -270,30 +287,38 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
     }
     __syncthreads();
     if (k0 + 16 < r) load_slab(k0 + 16);
-#pragma unroll 4
-    for (int kk = 0; kk < 16; ++kk) {
-      double av[NA], bv[NC];
 #pragma unroll
-      for (int a = 0; a < NA; ++a) av[a] = As[kk * TM + ty + 16 * a];
+    for (int k4 = 0; k4 < 4; ++k4) {
+      double xa[MB], xb[NW4];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) bv[c] = Bs[kk * DH + tx + 16 * c];
+      for (int mi = 0; mi < MB; ++mi) xa[mi] = As[(4 * k4 + kg) * TM + 16 * mi + l16];
 #pragma unroll
-      for (int a = 0; a < NA; ++a)
+      for (int nj = 0; nj < NW4; ++nj) xb[nj] = Bs[(4 * k4 + kg) * DH + wc0 + 16 * nj + l16];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
+      for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NW4; ++nj) acc[mi][nj] = mma(xa[mi], xb[nj], acc[mi][nj]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int a = 0; a < NA; ++a)
+  for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) Ks[(ty + 16 * a) * KS + tx + 16 * c] = acc[a][c];
+    for (int nj = 0; nj < NW4; ++nj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Ks[(16 * mi + kg + 4 * v) * KS + wc0 + 16 * nj + l16] = acc[mi][nj][v];
   __syncthreads();
 
   // GEMM2 + SiLU per 64-wide hidden block, GEMM3 accumulated: v_hat = H . W2^T
-  double vacc[NA][NC] = {};
+  f64x4 vacc[MB][NW4];
+#pragma unroll
+  for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < NW4; ++nj) vacc[mi][nj] = z4;
   for (int f0 = 0; f0 < F; f0 += 64) {
-    double hacc[NA][4] = {};
+    f64x4 hacc[MB];
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi) hacc[mi] = z4;
     // W1 slabs: the next one's loads in flight during the current products
     double wv0[16 * 64 / 256];
     auto load_w1 = [&](int k0) {
@@ -312,27 +337,25 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
       }
       __syncthreads();
       if (k0 + 16 < DH) load_w1(k0 + 16);
-#pragma unroll 4
-      for (int kk = 0; kk < 16; ++kk) {
-        double av[NA], bv[4];
 #pragma unroll
-        for (int a = 0; a < NA; ++a) av[a] = Ks[(ty + 16 * a) * KS + k0 + kk];
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const double xb = Bs[(4 * k4 + kg) * 64 + 16 * w + l16];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) bv[c] = Bs[kk * 64 + tx + 16 * c];
-#pragma unroll
-        for (int a = 0; a < NA; ++a)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) hacc[a][c] = fma(av[a], bv[c], hacc[a][c]);
+        for (int mi = 0; mi < MB; ++mi)
+          hacc[mi] = mma(Ks[(16 * mi + l16) * KS + k0 + 4 * k4 + kg], xb, hacc[mi]);
       }
       __syncthreads();
     }
+    {
+      const double bias = ldd(B1, f0 + 16 * w + l16);
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+      for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const double x = hacc[a][c] + ldd(B1, f0 + tx + 16 * c);
-        Hs[(ty + 16 * a) * HS + tx + 16 * c] = x / (1.0 + exp(-x));
-      }
+        for (int v = 0; v < 4; ++v) {
+          const double x = hacc[mi][v] + bias;
+          Hs[(16 * mi + kg + 4 * v) * HS + 16 * w + l16] = x / (1.0 + exp(-x));
+        }
+    }
     __syncthreads();
     // W2 slabs of this hidden block, prefetched like W1's
     double w2v0[16 * DH / 256];
@@ -352,51 +375,61 @@ __global__ __launch_bounds__(256) void k_pred(const TC *__restrict__ coeff,
       }
       __syncthreads();
       if (k0 + 16 < 64) load_w2(k0 + 16);
-#pragma unroll 4
-      for (int kk = 0; kk < 16; ++kk) {
-        double av[NA], bv[NC];
 #pragma unroll
-        for (int a = 0; a < NA; ++a) av[a] = Hs[(ty + 16 * a) * HS + k0 + kk];
+      for (int k4 = 0; k4 < 4; ++k4) {
+        double xa[MB], xb[NW4];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) bv[c] = Bs[kk * DH + tx + 16 * c];
+        for (int mi = 0; mi < MB; ++mi) xa[mi] = Hs[(16 * mi + l16) * HS + k0 + 4 * k4 + kg];
 #pragma unroll
-        for (int a = 0; a < NA; ++a)
+        for (int nj = 0; nj < NW4; ++nj) xb[nj] = Bs[(4 * k4 + kg) * DH + wc0 + 16 * nj + l16];
 #pragma unroll
-          for (int c = 0; c < NC; ++c) vacc[a][c] = fma(av[a], bv[c], vacc[a][c]);
+        for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+          for (int nj = 0; nj < NW4; ++nj) vacc[mi][nj] = mma(xa[mi], xb[nj], vacc[mi][nj]);
       }
       __syncthreads();
     }
   }
 
-  // epilogue
+  // epilogue: lane holds v_hat - b2 of rows m = 16 mi + kg + 4 v, head dims
+  // wc0 + 16 nj + l16.  The squared error of a row is summed over the lane's
+  // blocks, then over the 16 lanes of its row group, then over the 4 waves in
+  // order.
+  double *ered = As;  // [4][TM]: the first product's slab area, free since its last barrier
 #pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    const int m = ty + 16 * a;
-    const int t = tok[m];
-    if (MODE != 1) {
-      double e = 0.0;
-      if (t >= 0) {
+  for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int d = tx + 16 * c;
-          const double dv = ldd(V, (long)t * DH + d) - (vacc[a][c] + ldd(B2, d));
-          e = fma(dv, dv, e);
-          if (MODE == 2) st_round(dout + (bh * N + t) * DH + d, dv);
+    for (int v = 0; v < 4; ++v) {
+      const int m = 16 * mi + kg + 4 * v;
+      const int t = tok[m];
+      if (MODE != 1) {
+        double e = 0.0;
+        if (t >= 0) {
+#pragma unroll
+          for (int nj = 0; nj < NW4; ++nj) {
+            const int d = wc0 + 16 * nj + l16;
+            const double dv = ldd(V, (long)t * DH + d) - (vacc[mi][nj][v] + ldd(B2, d));
+            e = fma(dv, dv, e);
+            if (MODE == 2) st_round(dout + (bh * N + t) * DH + d, dv);
+          }
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) e += __shfl_xor(e, o, WAVE);
+        if (l16 == 0) ered[w * TM + m] = e;
+      } else if (t >= 0) {
+        const int rr = row0 + m;
+#pragma unroll
+        for (int nj = 0; nj < NW4; ++nj) {
+          const int d = wc0 + 16 * nj + l16;
+          const double dv = ldd(V, (long)t * DH + d) - (vacc[mi][nj][v] + ldd(B2, d));
+          st_round(dout + (bh * n_res + rr) * DH + d, dv);
         }
       }
-      // sum over the 16 threads of this row (lanes tx = 0..15 of one wave quarter)
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) e += __shfl_xor(e, o, WAVE);
-      if (tx == 0 && t >= 0) err[bh * N + t] = e;
-    } else if (t >= 0) {
-      const int rr = row0 + m;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int d = tx + 16 * c;
-        const double dv = ldd(V, (long)t * DH + d) - (vacc[a][c] + ldd(B2, d));
-        st_round(dout + (bh * n_res + rr) * DH + d, dv);
-      }
     }
+  if (MODE != 1) {
+    __syncthreads();
+    if (tid < TM && tok[tid] >= 0)
+      err[bh * N + tok[tid]] = ((ered[tid] + ered[TM + tid]) + ered[2 * TM + tid]) + ered[3 * TM + tid];
   }
 }
 
