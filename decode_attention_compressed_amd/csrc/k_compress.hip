@@ -1,9 +1,9 @@
 // Compress-side kernels for gfx950 (run once per context, before decoding):
-//   k_project     c_t = U^T k_t^cat in float64, rounded once to the storage type
+//   k_project     c_t = U^T k_t^cat in float64 (matrix cores), rounded once to the storage type
 //   k_colmax      per-channel max |x| -> fp16 scale = fp16(max / 127)
 //   k_quant       q = clamp(rne(x / s), -127, 127)
 //   k_landmark    mean dequantised coefficient of each chunk, float64 -> float32
-//   k_pred        float64 predictor: k_hat = U_{l,h} c~, v_hat = W2 SiLU(W1 k_hat + b1) + b2,
+//   k_pred        float64 predictor (matrix cores): k_hat = U_{l,h} c~, v_hat = W2 SiLU(W1 k_hat + b1) + b2,
 //                 emitting either e_t = ||v_t - v_hat_t||^2 or delta = v - v_hat
 //   k_err_topk    residual set: top n_res tokens by (e desc, t asc), ascending,
 //                 with chunk CSR pointers
@@ -33,32 +33,41 @@ __device__ __forceinline__ void st_round(double *p, double x) { *p = x; }
 
 // ---------------------------------------------------------------------------
 // C1: out[b][o0 + t][i] = sum_kk K(b, t, kk) U[b][kk][i] for t < N, float64
-// accumulate.  K(b, t, kk) = k[b][l][h][t][d] with kk = (l*Hkv + h)*dh + d and
-// Nk tokens per (l, h) block of k; out holds No rows per sequence.
+// products and sums on the float64 matrix cores (v_mfma_f64_16x16x4_f64).
+// K(b, t, kk) = k[b][l][h][t][d] with kk = (l*Hkv + h)*dh + d and Nk tokens per
+// (l, h) block of k; out holds No rows per sequence.
 // With S > 1 the reduction over kk is split in S slices of Dsl (a multiple of
 // 16): slice s writes its float64 partial sums to out + s * s_stride (TO =
 // double) and k_project_sum adds the slices in order.
-// grid (ceil(r/64), ceil(N/64), B * S), 256 threads, 4x4 outputs per thread.
+// grid (ceil(r/64), ceil(N/64), B * S), 256 threads; each wave a 32 x 32
+// quarter of the 64 x 64 tile, the next 16-wide slab's loads in flight during
+// the current slab's products.
 // ---------------------------------------------------------------------------
 template <typename TA, typename TO>
 __global__ __launch_bounds__(256) void k_project(const TA *__restrict__ k, const TA *__restrict__ U,
                                                  TO *__restrict__ out, int N, int D, int dh, int r,
                                                  int Nk, int No, int o0, int S, int Dsl,
                                                  long s_stride) {
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
   __shared__ double As[16][64 + 1];
   __shared__ double Bs[16][64];
   const int b = blockIdx.z / S, sl = blockIdx.z % S;
   const int t0 = blockIdx.y * 64, i0 = blockIdx.x * 64, tid = threadIdx.x;
   const int kbeg = sl * Dsl, kend = min(D, kbeg + Dsl);
   out += sl * s_stride;
-  const int tx = tid % 16, ty = tid / 16;
+  const int lane = tid & (WAVE - 1), w = tid / WAVE, l16 = lane & 15, kg = lane >> 4;
+  const int wr0 = (w >> 1) * 32, wc0 = (w & 1) * 32;  // this wave's quarter of the tile
   const TA *kb = k + (long)b * D * Nk;  // [G*Hkv][Nk][dh] blocks
   const TA *Ub = U + (long)b * D * r;
-  double acc[4][4] = {};
-  for (int k0 = kbeg; k0 < kend; k0 += 16) {
-    // both slabs' loads in flight together: indices clamped into range, the
-    // values outside it zeroed when stored
-    double av0[4], bv0[4];
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < 2; ++nj) acc[mi][nj] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // both slabs' loads in flight together: indices clamped into range, the
+  // values outside it zeroed when stored
+  double av0[4], bv0[4];
+  auto load = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = tid + 256 * u, kk = idx % 16, t = idx / 16;  // consecutive threads walk d
@@ -70,6 +79,9 @@ __global__ __launch_bounds__(256) void k_project(const TA *__restrict__ k, const
       const int idx = tid + 256 * u, kk = idx / 64, i = idx % 64;
       bv0[u] = ldd(Ub, (long)min(k0 + kk, kend - 1) * r + min(i0 + i, r - 1));
     }
+  };
+  load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = tid + 256 * u, kk = idx % 16, t = idx / 16;
@@ -81,29 +93,33 @@ __global__ __launch_bounds__(256) void k_project(const TA *__restrict__ k, const
       Bs[kk][i] = (k0 + kk < kend && i0 + i < r) ? bv0[u] : 0.0;
     }
     __syncthreads();
+    if (k0 + 16 < kend) load(k0 + 16);
+    // lane (l16, kg) holds A[row l16][k kg] and B[k kg][column l16]
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      double av[4], bv[4];
+    for (int k4 = 0; k4 < 4; ++k4) {
+      double xa[2], xb[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = As[kk][ty + 16 * a];
+      for (int mi = 0; mi < 2; ++mi) xa[mi] = As[4 * k4 + kg][wr0 + 16 * mi + l16];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = Bs[kk][tx + 16 * c];
+      for (int nj = 0; nj < 2; ++nj) xb[nj] = Bs[4 * k4 + kg][wc0 + 16 * nj + l16];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
+        for (int nj = 0; nj < 2; ++nj)
+          acc[mi][nj] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[mi], xb[nj], acc[mi][nj], 0, 0, 0);
     }
     __syncthreads();
   }
+  // item v of lane (l16, kg) is row kg + 4 v, column l16 of its 16 x 16 block
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int tt = t0 + ty + 16 * a;
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int ii = i0 + tx + 16 * c;
-      if (tt < N && ii < r) st_round(out + ((long)b * No + o0 + tt) * r + ii, acc[a][c]);
-    }
-  }
+    for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tt = t0 + wr0 + 16 * mi + kg + 4 * v, ii = i0 + wc0 + 16 * nj + l16;
+        if (tt < N && ii < r) st_round(out + ((long)b * No + o0 + tt) * r + ii, acc[mi][nj][v]);
+      }
 }
 
 // out[b][o0 + t][i] = round(sum over s = 0..S-1 of part[s][b][t][i]), slices
