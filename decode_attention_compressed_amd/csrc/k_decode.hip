@@ -598,23 +598,27 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 template <typename TA, int QG>
 static void launch_partial_g(const TA *q, long q_bstride, const TA *basis, const float *landmark, int B,
                              int Hq, int Hkv, int dh, int r, int n_c, int D, int layer, double *part,
-                             const QOut &qo, hipStream_t st) {
+                             const QOut &qo, hipStream_t st, int k_eff = 0, int32_t *sel = nullptr,
+                             int32_t *sel_out = nullptr) {
   const dim3 g(select_rank_blocks(r), Hkv, B);
   if (dh == 64)
-    hipLaunchKernelGGL((k_select_partial<TA, 64, QG>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qo.qtg, qo.qfrag, qo.scale, qo.mode);
+    hipLaunchKernelGGL((k_select_partial<TA, 64, QG>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qo.qtg, qo.qfrag, qo.scale, qo.mode, k_eff, sel, sel_out);
   else if (dh == 128)
-    hipLaunchKernelGGL((k_select_partial<TA, 128, QG>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qo.qtg, qo.qfrag, qo.scale, qo.mode);
+    hipLaunchKernelGGL((k_select_partial<TA, 128, QG>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qo.qtg, qo.qfrag, qo.scale, qo.mode, k_eff, sel, sel_out);
   else
-    hipLaunchKernelGGL((k_select_partial<TA, 256, QG>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qo.qtg, qo.qfrag, qo.scale, qo.mode);
+    hipLaunchKernelGGL((k_select_partial<TA, 256, QG>), g, dim3(256), 0, st, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D, layer, part, qo.qtg, qo.qfrag, qo.scale, qo.mode, k_eff, sel, sel_out);
 }
 template <typename TA>
 static void launch_partial(const TA *q, long q_bstride, const TA *basis, const float *landmark, int B,
                            int Hq, int Hkv, int dh, int r, int n_c, int D, int layer, double *part,
-                           const QOut &qo, hipStream_t st) {
+                           const QOut &qo, hipStream_t st, int k_eff = 0, int32_t *sel = nullptr,
+                           int32_t *sel_out = nullptr) {
   if (qo.qfrag && Hq / Hkv > QTG_G)
-    launch_partial_g<TA, QTG_MAX>(q, q_bstride, basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qo, st);
+    launch_partial_g<TA, QTG_MAX>(q, q_bstride, basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qo, st,
+                                  k_eff, sel, sel_out);
   else
-    launch_partial_g<TA, QTG_G>(q, q_bstride, basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qo, st);
+    launch_partial_g<TA, QTG_G>(q, q_bstride, basis, landmark, B, Hq, Hkv, dh, r, n_c, D, layer, part, qo, st,
+                                k_eff, sel, sel_out);
 }
 
 hipError_t launch_select(int act, const void *q, long q_bstride, const void *basis,
@@ -622,6 +626,17 @@ hipError_t launch_select(int act, const void *q, long q_bstride, const void *bas
                          int D, int layer, int k_eff, int32_t *sel, int32_t *sel_out,
                          double *part, double *scores, hipStream_t st, const QOut &qo,
                          const AttendArgs *absorb) {
+  // one rank block (r <= 64) and few chunks: the score kernel ranks its own
+  // scores, one launch instead of two
+  if (!absorb && scores && k_eff > 0 && n_c <= 4 * WAVE && select_rank_blocks(r) == 1) {
+    if (act == LOWRAM_F32)
+      launch_partial<float>((const float *)q, q_bstride, (const float *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D,
+                            layer, part, qo, st, k_eff, sel, sel_out);
+    else
+      launch_partial<bf16>((const bf16 *)q, q_bstride, (const bf16 *)basis, landmark, B, Hq, Hkv, dh, r, n_c, D,
+                           layer, part, qo, st, k_eff, sel, sel_out);
+    return hipGetLastError();
+  }
   if (absorb) {
     const hipError_t e = launch_select_absorb(*absorb, landmark, part, q_bstride, st);
     if (e != hipSuccess) return e;

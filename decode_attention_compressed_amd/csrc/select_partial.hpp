@@ -8,6 +8,7 @@
 #pragma once
 #include "common.hpp"
 #include "internal.hpp"
+#include "attend_common.hpp"
 
 namespace lowram {
 
@@ -133,7 +134,8 @@ __device__ __forceinline__ void select_partial_block(SelectSmem<DH, QG> &sm, int
                                                      int Hkv, int r, int n_c, int D, int layer,
                                                      double *__restrict__ part, float *__restrict__ qtg,
                                                      uint16_t *__restrict__ qfrag,
-                                                     const uint16_t *__restrict__ qf_scale, int qf_mode) {
+                                                     const uint16_t *__restrict__ qf_scale, int qf_mode,
+                                                     double *lds_scores = nullptr) {
   constexpr int RPS = DH / 32;  // basis rows per slice
   double *qsum = sm.qsum, *qt = sm.qt;
   auto &qtp = sm.qtp;
@@ -287,9 +289,14 @@ __device__ __forceinline__ void select_partial_block(SelectSmem<DH, QG> &sm, int
     const double tot = xpose_sum<MB, 8>(sacc, lane);  // chunk row li of lane group gq
     const int j = j_base + 16 * li + 4 * w + gq;
     if (j < n_c) pb[j] = tot;
+    if (lds_scores && j < n_c) lds_scores[j] = tot;
   }
 }
 
+// With sel set (one rank block, r <= 64, and n_c <= 256 only), the block's
+// partial scores are the chunk scores, and the workgroup ranks them itself:
+// wave 0 writes the top k_eff chunks of (b, h) by (score desc, index asc), in
+// ascending order, to sel (and sel_out), as the separate top-k launch would.
 template <typename TA, int DH, int QG>
 __global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q, long q_bstride,
                                                         const TA *__restrict__ basis,
@@ -297,12 +304,25 @@ __global__ __launch_bounds__(256) void k_select_partial(const TA *__restrict__ q
                                                         int Hkv, int r, int n_c, int D, int layer,
                                                         double *__restrict__ part, float *__restrict__ qtg,
                                                         uint16_t *__restrict__ qfrag,
-                                                        const uint16_t *__restrict__ qf_scale, int qf_mode) {
+                                                        const uint16_t *__restrict__ qf_scale, int qf_mode,
+                                                        int k_eff, int32_t *__restrict__ sel,
+                                                        int32_t *__restrict__ sel_out) {
   __shared__ SelectSmem<DH, QG> sm;
+  __shared__ double scs[4 * WAVE];
   int rb, h, b;
   select_coords(blockIdx.x + gridDim.x * (blockIdx.y + Hkv * blockIdx.z), gridDim.x, Hkv, gridDim.z, rb, h, b);
   select_partial_block<TA, DH, QG>(sm, rb, h, b, gridDim.x, q, q_bstride, basis, landmark, Hq, Hkv, r, n_c, D,
-                                   layer, part, qtg, qfrag, qf_scale, qf_mode);
+                                   layer, part, qtg, qfrag, qf_scale, qf_mode, sel ? scs : nullptr);
+  if (sel) {
+    __syncthreads();
+    if (threadIdx.x < WAVE) {
+      const long o = ((long)b * Hkv + h) * k_eff;
+      wave_topk<4>(scs, n_c, k_eff, [&](int pos, int c) {
+        sel[o + pos] = c;
+        if (sel_out) sel_out[o + pos] = c;
+      });
+    }
+  }
 }
 
 }  // namespace lowram
