@@ -243,6 +243,10 @@ def _roundtrip(s, top_k, edit=None):
     ("int8-ragged", small(COMPOSED_128K, B=1, N=2048, evict_keep=1.0, n_obs=0, T=5), 7),
     # selection paths: radix top-k inside the fused scorer (256 < n_c <= 1024),
     # the three-kernel scorer (n_c > 1024), two and four rank segments per lane
+    # one rank block (r <= 64) and n_c <= 256: the score kernel ranks its own
+    # scores, here at the most chunks it takes and at a ragged count
+    ("self-ranked-nc-256", TINY.replace(N=16384, T=8), 9),
+    ("self-ranked-nc-197", TINY.replace(N=197 * 64, T=8), 37),
     ("nc-512", TINY.replace(N=32768, T=8), 9),
     ("nc-2048-unfused", TINY.replace(N=131072, T=8), 11),
     ("rank-1024", small(LLAMA8B_32K, B=1, N=1024, r=1024, T=16), 3),
@@ -329,12 +333,16 @@ def _copy_chunks(src_of):
     # the absorbed kernel (head dim 256) ranks the scores in its own prologue
     ("absorb-pairs", small(QWEN4B_64K, B=1, N=4096, T=16), 5, lambda j: j - j % 2),
     ("absorb-all-equal", small(QWEN4B_64K, B=1, N=4096, T=16), 6, lambda j: 0),
+    # the score kernel ranking its own scores (r <= 64, n_c <= 256)
+    ("valu-pairs", TINY.replace(N=8192, T=16), 7, lambda j: j - j % 2),
+    ("valu-all-equal", TINY.replace(N=4096, T=16), 6, lambda j: 0),
 ])
 def test_selection_ties(name, shape, top_k, src_of):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     print(f"\n[case] ties {name}: {shape}", flush=True)
-    assert P().decode_kernel(dims_of(shape, top_k=top_k)) == ("absorb" if name.startswith("absorb") else "chain")
+    assert P().decode_kernel(dims_of(shape, top_k=top_k)) == {"absorb": "absorb", "valu": "valu"}.get(
+        name.split("-")[0], "chain")
     out, sel, ref, rsel, host, inp = _roundtrip(shape, top_k, edit=_copy_chunks(src_of))
     lm = host["landmark"][0]
     assert any(np.array_equal(lm[j], lm[src_of(j)]) for j in range(1, lm.shape[0]) if src_of(j) != j)
